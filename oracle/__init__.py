@@ -1,0 +1,6 @@
+"""fp64 CPU oracle for fused softmax cross-entropy.
+
+Test infrastructure only: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``, never by the product path.
+"""
+from .ce_oracle import ce, ce_rows, reduce_loss, rne_bf16_bits, widen_bf16  # noqa: F401
