@@ -1,0 +1,152 @@
+/*
+ * ce.h - C ABI of the MI355X (gfx950) fused softmax cross-entropy library
+ *        (libce_mi355x.so).
+ *
+ * The operation is the fused cross-entropy of the rumus project page,
+ * milestone M7a "Loss Functions & GPU Optimizers" (log-sum-exp with a
+ * per-row max and sum of exponentials, the gradient formed in the forward
+ * pass, the loss reduced to a scalar that stays on the device), whose kernel
+ * is shown in the rumus 0.1.1 source view of cross_entropy.wgsl: pass 1
+ * (steps 1-4: row max, sum of exp(z - max), per-row loss scaled by 1/B,
+ * gradient softmax - one-hot scaled by 1/B) and pass 2 (sum of the per-row
+ * losses).  For a [B, C] logit matrix z and int32 targets t:
+ *
+ *     loss_rows[b] = (log(sum_c exp(z[b,c])) - z[b, t_b]) / B
+ *     grad[b, c]   = (softmax(z[b,:])[c] - [c == t_b]) / B
+ *     loss         = sum_b loss_rows[b]                     (the batch mean)
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller.  The
+ *    library allocates nothing and keeps no mutable state (apart from the
+ *    test-only path override below).
+ *  - Calls are asynchronous and ordered on `stream` (a hipStream_t passed as
+ *    void*; NULL means the default stream).  No call synchronises the
+ *    device or copies data to the host.
+ *  - Arguments are validated on the host before any HIP call; a negative
+ *    ce_status is returned and nothing is launched.  A failed launch returns
+ *    CE_ERR_LAUNCH.  Faults of earlier asynchronous work surface at the
+ *    caller's next synchronisation, as for any HIP call.
+ *  - Outputs are overwritten, never accumulated.
+ *  - The calls are thread-safe.
+ */
+#ifndef CE_MI355X_H
+#define CE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of the logits and of the gradient (they always match).
+ * Accumulation is float32 in both cases; per-row losses are float32. */
+typedef enum {
+    CE_F32 = 0,  /* IEEE binary32 */
+    CE_BF16 = 1  /* bfloat16; the gradient is rounded to nearest, ties to even */
+} ce_dtype;
+
+typedef enum {
+    CE_OK = 0,
+    CE_ERR_NULL = -1,      /* a required pointer is NULL */
+    CE_ERR_SHAPE = -2,     /* B <= 0, C <= 0, or a size beyond the limits below */
+    CE_ERR_DTYPE = -3,     /* dtype is not a ce_dtype */
+    CE_ERR_WORKSPACE = -4, /* workspace NULL or smaller than ce_reduce_workspace_bytes(B) */
+    CE_ERR_LAUNCH = -5,    /* the HIP runtime rejected a kernel launch */
+    CE_ERR_ALIGN = -6,     /* a pointer is not aligned as required */
+    CE_ERR_ALIAS = -7,     /* grad_out overlaps logits */
+    CE_ERR_PATH = -8       /* the forced path (ce_debug_force_path) cannot take this shape */
+} ce_status;
+
+/* Largest number of classes accepted: a row must stay below 2^31 bytes. */
+#define CE_MAX_C ((int64_t)1 << 28)
+
+/*
+ * ce_fwd_grad - per-row loss and gradient of softmax cross-entropy, one pass.
+ *
+ * Defined by: rumus 0.1.1 cross_entropy.wgsl, pass 1, steps 1-4; rumus
+ * project page, milestone M7a (gradient pre-computed during the forward).
+ *
+ *   logits    [B, C] row-major, contiguous, dtype elements.  Read once.
+ *             Must be aligned to the element size.
+ *   targets   [B] int32 class indices.  A target outside [0, C) is not an
+ *             error: that row's loss and its whole gradient row are NaN.
+ *   B, C      1 <= B <= 2^31 - 1, 1 <= C <= CE_MAX_C.
+ *   dtype     CE_F32 or CE_BF16.
+ *   grad_out  [B, C] dtype, fully overwritten with (softmax - onehot) / B.
+ *             Must not overlap logits, must be aligned to the element size,
+ *             and (grad_out - logits) must be a multiple of 16 bytes
+ *             (true for any two allocations from the HIP or torch
+ *             allocators).
+ *   loss_out  [B] float32, overwritten with the per-row losses, already
+ *             scaled by 1/B; ce_reduce_loss sums them to the batch mean.
+ *   stream    hipStream_t or NULL.
+ *
+ * Returns CE_OK or a negative ce_status.  Results are bitwise reproducible
+ * for the same inputs, shape and dtype on the same device.
+ */
+int ce_fwd_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C,
+                int dtype, void* grad_out, float* loss_out, void* stream);
+
+/*
+ * ce_reduce_workspace_bytes - device scratch that ce_reduce_loss needs for
+ * B per-row losses (0 when one workgroup sums them directly).
+ */
+size_t ce_reduce_workspace_bytes(int64_t B);
+
+/*
+ * ce_reduce_loss - the batch-mean loss as one float32 on the device.
+ *
+ * Defined by: rumus 0.1.1 cross_entropy.wgsl, pass 2 (the per-row losses
+ * summed into one scalar); rumus project page, milestone M7b (the loss is
+ * read back as 4 bytes only when the caller wants it).
+ *
+ *   loss_rows        [B] float32 (the loss_out of ce_fwd_grad).
+ *   B                number of rows, >= 1.
+ *   loss_scalar_out  [1] float32, overwritten with sum_b loss_rows[b].
+ *   workspace        device scratch of at least ce_reduce_workspace_bytes(B)
+ *                    bytes (may be NULL when that is 0); contents on entry
+ *                    are ignored.
+ *
+ * The sum uses a fixed two-level tree whose shape depends only on B, with
+ * no atomics, so the result is bitwise reproducible.
+ */
+int ce_reduce_loss(const float* loss_rows, int64_t B, float* loss_scalar_out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a ce_status value. */
+const char* ce_status_string(int status);
+
+/* Library version string. */
+const char* ce_version(void);
+
+/*
+ * Kernel paths:
+ *   1 short rows  - many rows per 64-lane wavefront, cross-lane DPP
+ *                   reductions, no LDS (C <= 256);
+ *   2 resident    - one workgroup per row, the row held on chip in
+ *                   registers between the reduction and the gradient write,
+ *                   so it is read from HBM once and written once;
+ *   3 long rows   - as 2, with the part of the row beyond the on-chip
+ *                   capacity streamed with online max/sum-exp partials and
+ *                   re-read for the gradient.
+ *
+ * ce_select_path returns the path ce_fwd_grad takes for (C, dtype) with
+ * 16-byte aligned base pointers, or a negative ce_status.
+ */
+int ce_select_path(int64_t C, int dtype);
+
+/*
+ * Test hook: force every later ce_fwd_grad onto one path (0 = automatic,
+ * 1, 2 or 3 as above; path 3 is then run with a small on-chip part so that
+ * the streamed part is exercised).  A shape the forced path cannot take
+ * returns CE_ERR_PATH.  Returns the previous setting, or CE_ERR_PATH for an
+ * unknown value.  Process-wide; not meant for production use.
+ */
+int ce_debug_force_path(int path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CE_MI355X_H */

@@ -1,0 +1,196 @@
+"""Fused softmax cross-entropy for MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libce_mi355x.so`` (C ABI in ``include/ce.h``).
+It checks tensor dtypes, devices and contiguity, allocates outputs with
+torch and passes raw device pointers plus torch's current HIP stream; every
+step of the computation runs in the library's HIP kernels.  There is no CPU
+or PyTorch fallback: if the library is missing, importing the binding's
+functions raises.
+
+The operation (rumus project page, milestone M7a; rumus 0.1.1
+``cross_entropy.wgsl`` pass 1 and pass 2): for logits ``z`` of shape
+``[B, C]`` and int32 targets ``t``::
+
+    loss_rows[b] = (logsumexp(z[b]) - z[b, t[b]]) / B
+    grad[b, c]   = (softmax(z[b])[c] - [c == t[b]]) / B
+    loss         = sum_b loss_rows[b]
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "CEError", "lib", "fwd_grad", "fwd_grad_into", "reduce_loss", "reduce_loss_into",
+    "cross_entropy", "reduce_workspace_bytes", "select_path", "force_path", "version",
+    "PATH_NAMES", "F32", "BF16",
+]
+
+F32 = 0
+BF16 = 1
+PATH_NAMES = {1: "short", 2: "resident", 3: "long"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libce_mi355x.so")
+
+
+class CEError(RuntimeError):
+    """A negative status from the C library."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing; build it with "
+            "`python -m softmax_cross_entropy_ce_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.ce_fwd_grad.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp]
+    L.ce_fwd_grad.restype = i32
+    L.ce_reduce_workspace_bytes.argtypes = [i64]
+    L.ce_reduce_workspace_bytes.restype = sz
+    L.ce_reduce_loss.argtypes = [vp, i64, vp, vp, sz, vp]
+    L.ce_reduce_loss.restype = i32
+    L.ce_status_string.argtypes = [i32]
+    L.ce_status_string.restype = ctypes.c_char_p
+    L.ce_version.argtypes = []
+    L.ce_version.restype = ctypes.c_char_p
+    L.ce_select_path.argtypes = [i64, i32]
+    L.ce_select_path.restype = i32
+    L.ce_debug_force_path.argtypes = [i32]
+    L.ce_debug_force_path.restype = i32
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().ce_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().ce_version().decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise CEError(status, what)
+
+
+def select_path(C: int, dtype: int) -> int:
+    r = lib().ce_select_path(int(C), int(dtype))
+    _check(0 if r > 0 else r, "ce_select_path")
+    return r
+
+
+def force_path(path: int) -> int:
+    """Test hook: force a kernel path (0 = automatic).  Returns the previous."""
+    r = lib().ce_debug_force_path(int(path))
+    if r < 0:
+        raise CEError(r, "ce_debug_force_path")
+    return r
+
+
+def reduce_workspace_bytes(B: int) -> int:
+    return int(lib().ce_reduce_workspace_bytes(int(B)))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream_ptr(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_cuda(*ts) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on a HIP device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    dev = ts[0].device
+    if any(t.device != dev for t in ts):
+        raise ValueError("tensors must be on one device")
+
+
+def fwd_grad_into(logits, targets, grad, loss_rows) -> None:
+    """Write the gradient and the per-row losses into preallocated tensors."""
+    torch = _torch()
+    _check_cuda(logits, targets, grad, loss_rows)
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, C]")
+    B, C = logits.shape
+    if targets.dtype != torch.int32 or targets.shape != (B,):
+        raise TypeError("targets must be int32 of shape [B]")
+    if grad.dtype != logits.dtype or grad.shape != logits.shape:
+        raise TypeError("grad must match logits in dtype and shape")
+    if loss_rows.dtype != torch.float32 or loss_rows.shape != (B,):
+        raise TypeError("loss_rows must be float32 of shape [B]")
+    st = lib().ce_fwd_grad(logits.data_ptr(), targets.data_ptr(), B, C, _dtype_code(logits),
+                           grad.data_ptr(), loss_rows.data_ptr(), _stream_ptr(logits.device))
+    _check(st, "ce_fwd_grad")
+
+
+def fwd_grad(logits, targets):
+    """Return ``(grad, loss_rows)`` for ``[B, C]`` logits and int32 targets."""
+    torch = _torch()
+    grad = torch.empty_like(logits)
+    loss_rows = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device)
+    fwd_grad_into(logits, targets, grad, loss_rows)
+    return grad, loss_rows
+
+
+def reduce_loss_into(loss_rows, out, workspace=None) -> None:
+    torch = _torch()
+    _check_cuda(loss_rows, out)
+    if loss_rows.dtype != torch.float32 or loss_rows.dim() != 1:
+        raise TypeError("loss_rows must be a float32 vector")
+    if out.dtype != torch.float32 or out.numel() != 1:
+        raise TypeError("out must be one float32")
+    B = loss_rows.shape[0]
+    need = reduce_workspace_bytes(B)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=loss_rows.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().ce_reduce_loss(loss_rows.data_ptr(), B, out.data_ptr(), wptr, wbytes,
+                              _stream_ptr(loss_rows.device))
+    _check(st, "ce_reduce_loss")
+
+
+def reduce_loss(loss_rows):
+    """The batch-mean loss as a 0-d float32 device tensor."""
+    torch = _torch()
+    out = torch.empty((), dtype=torch.float32, device=loss_rows.device)
+    reduce_loss_into(loss_rows, out)
+    return out
+
+
+def cross_entropy(logits, targets):
+    """Return ``(loss, grad)``: the batch-mean loss (0-d device tensor) and
+    the gradient with respect to the logits."""
+    grad, loss_rows = fwd_grad(logits, targets)
+    return reduce_loss(loss_rows), grad

@@ -1,0 +1,267 @@
+// Host side of libce_mi355x.so: argument validation, path selection, launch
+// geometry and the C ABI declared in include/ce.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <stdint.h>
+
+#include "ce.h"
+#include "ce_kernels.h"
+
+namespace {
+
+std::atomic<int> g_force_path{0};
+
+constexpr int kPathShort = 1;
+constexpr int kPathResident = 2;
+constexpr int kPathLong = 3;
+
+// Per-row configurations of paths 2 and 3: NT threads, NV 16-byte vectors
+// per thread, so NT*NV*16 bytes of the row stay in registers.  Ordered by
+// capacity; the first that holds the row is taken.
+struct RowCfg {
+  int nt, nv;
+};
+constexpr RowCfg kRowCfgs[] = {{64, 1},   {64, 2},   {64, 4},    {256, 2},  {256, 4},
+                               {1024, 2}, {1024, 4}, {1024, 8},  {1024, 16}};
+constexpr RowCfg kLongCfg = {1024, 16};     // automatic path 3
+constexpr RowCfg kLongTestCfg = {256, 1};   // forced path 3: small on-chip part
+
+constexpr int kShortMaxC = 256;
+
+int elem_size(int dtype) { return dtype == CE_F32 ? 4 : 2; }
+
+// 16-byte vectors a row may touch: the aligned body plus a head and a tail.
+int64_t row_vectors(int64_t C, int es) { return (C * es + 15) / 16 + 1; }
+
+int auto_path(int64_t C, int es) {
+  if (C <= kShortMaxC) return kPathShort;
+  const RowCfg& big = kRowCfgs[sizeof(kRowCfgs) / sizeof(kRowCfgs[0]) - 1];
+  if (row_vectors(C, es) <= (int64_t)big.nt * big.nv) return kPathResident;
+  return kPathLong;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int launched() { return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_LAUNCH; }
+
+// ------------------------------------------------------------------ path 1
+template <typename T, int S, int EPL, int VW>
+int launch_short_cfg(const T* z, const int32_t* t, int64_t B, int C, float invB, T* g, float* l,
+                     hipStream_t st) {
+  constexpr int rpb = ce::kShortThreads / S;
+  const int64_t blocks = (B + rpb - 1) / rpb;
+  if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
+  hipLaunchKernelGGL((ce::ce_short_kernel<T, S, EPL, VW>), dim3((unsigned)blocks),
+                     dim3(ce::kShortThreads), 0, st, z, t, B, C, invB, g, l);
+  return launched();
+}
+
+template <typename T, int S, int EPL>
+int launch_short_vw(int vw, const T* z, const int32_t* t, int64_t B, int C, float invB, T* g,
+                    float* l, hipStream_t st) {
+  switch (vw) {
+    case 1: return launch_short_cfg<T, S, EPL, 1>(z, t, B, C, invB, g, l, st);
+    case 2: return launch_short_cfg<T, S, EPL, 2>(z, t, B, C, invB, g, l, st);
+    case 4: return launch_short_cfg<T, S, EPL, 4>(z, t, B, C, invB, g, l, st);
+    case 8:
+      if constexpr (sizeof(T) == 2 && EPL >= 8)
+        return launch_short_cfg<T, S, EPL, 8>(z, t, B, C, invB, g, l, st);
+      return CE_ERR_PATH;
+    default: return CE_ERR_PATH;
+  }
+}
+
+// Vector width (elements) of the short path: the widest load of at most 16
+// bytes that every row start of both arrays is aligned to.
+int short_vw(int64_t C, int es, uintptr_t zaddr, uintptr_t gaddr, int epl) {
+  for (int vw = 16 / es; vw > 1; vw /= 2) {
+    const uintptr_t a = (uintptr_t)vw * es;
+    if (vw <= epl && C % vw == 0 && zaddr % a == 0 && gaddr % a == 0) return vw;
+  }
+  return 1;
+}
+
+template <typename T>
+int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g, float* l,
+                 hipStream_t st) {
+  if (C > kShortMaxC) return CE_ERR_PATH;
+  const int es = sizeof(T);
+  const int c = (int)C;
+  auto vw = [&](int epl) {
+    return short_vw(C, es, (uintptr_t)z, (uintptr_t)g, epl);
+  };
+  if (C <= 4) return launch_short_vw<T, 1, 4>(vw(4), z, t, B, c, invB, g, l, st);
+  if (C <= 8) return launch_short_vw<T, 1, 8>(vw(8), z, t, B, c, invB, g, l, st);
+  if (C <= 16) return launch_short_vw<T, 1, 16>(vw(16), z, t, B, c, invB, g, l, st);
+  if (C <= 32) return launch_short_vw<T, 2, 16>(vw(16), z, t, B, c, invB, g, l, st);
+  if (C <= 64) return launch_short_vw<T, 4, 16>(vw(16), z, t, B, c, invB, g, l, st);
+  if (C <= 128) return launch_short_vw<T, 8, 16>(vw(16), z, t, B, c, invB, g, l, st);
+  return launch_short_vw<T, 16, 16>(vw(16), z, t, B, c, invB, g, l, st);
+}
+
+// -------------------------------------------------------------- paths 2, 3
+template <typename T, int NT, int NV>
+int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g,
+                   float* l, hipStream_t st) {
+  hipLaunchKernelGGL((ce::ce_row_kernel<T, NT, NV>), dim3((unsigned)B), dim3(NT), 0, st, z, t, C,
+                     invB, g, l);
+  return launched();
+}
+
+template <typename T>
+int launch_row(RowCfg cfg, const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g,
+               float* l, hipStream_t st) {
+#define CE_ROW_CASE(NT_, NV_) \
+  if (cfg.nt == NT_ && cfg.nv == NV_) return launch_row_cfg<T, NT_, NV_>(z, t, B, C, invB, g, l, st);
+  CE_ROW_CASE(64, 1)
+  CE_ROW_CASE(64, 2)
+  CE_ROW_CASE(64, 4)
+  CE_ROW_CASE(256, 1)
+  CE_ROW_CASE(256, 2)
+  CE_ROW_CASE(256, 4)
+  CE_ROW_CASE(1024, 2)
+  CE_ROW_CASE(1024, 4)
+  CE_ROW_CASE(1024, 8)
+  CE_ROW_CASE(1024, 16)
+#undef CE_ROW_CASE
+  return CE_ERR_PATH;
+}
+
+RowCfg resident_cfg(int64_t C, int es, bool* ok) {
+  const int64_t need = row_vectors(C, es);
+  for (const RowCfg& r : kRowCfgs)
+    if ((int64_t)r.nt * r.nv >= need) {
+      *ok = true;
+      return r;
+    }
+  *ok = false;
+  return kLongCfg;
+}
+
+template <typename T>
+int fwd_grad_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g, float* l,
+                   hipStream_t st) {
+  const float invB = 1.0f / (float)B;
+  switch (path) {
+    case kPathShort:
+      return launch_short<T>(z, t, B, C, invB, g, l, st);
+    case kPathResident: {
+      bool ok = false;
+      const RowCfg cfg = resident_cfg(C, sizeof(T), &ok);
+      if (!ok) return CE_ERR_PATH;
+      return launch_row<T>(cfg, z, t, B, C, invB, g, l, st);
+    }
+    case kPathLong: {
+      const bool forced = g_force_path.load(std::memory_order_relaxed) == kPathLong;
+      return launch_row<T>(forced ? kLongTestCfg : kLongCfg, z, t, B, C, invB, g, l, st);
+    }
+    default:
+      return CE_ERR_PATH;
+  }
+}
+
+bool overlaps(uintptr_t a, uintptr_t an, uintptr_t b, uintptr_t bn) {
+  return a < b + bn && b < a + an;
+}
+
+// ------------------------------------------------------------ reduction
+constexpr int64_t kReduceMinChunk = 2048;
+constexpr int64_t kReduceMaxBlocks = 1024;
+
+int64_t reduce_chunk(int64_t B) {
+  const int64_t step = 4 * ce::kReduceThreads;
+  int64_t chunk = (B + kReduceMaxBlocks - 1) / kReduceMaxBlocks;
+  chunk = (chunk + step - 1) / step * step;
+  return chunk < kReduceMinChunk ? kReduceMinChunk : chunk;
+}
+
+int64_t reduce_blocks(int64_t B) { return (B + reduce_chunk(B) - 1) / reduce_chunk(B); }
+
+}  // namespace
+
+extern "C" {
+
+int ce_fwd_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
+                void* grad_out, float* loss_out, void* stream) {
+  if (!logits || !targets || !grad_out || !loss_out) return CE_ERR_NULL;
+  if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
+  if (B <= 0 || C <= 0 || B > 0x7fffffffLL || C > CE_MAX_C) return CE_ERR_SHAPE;
+  const int es = elem_size(dtype);
+  const uintptr_t z = (uintptr_t)logits, g = (uintptr_t)grad_out;
+  if (z % es || g % es || (uintptr_t)targets % 4 || (uintptr_t)loss_out % 4) return CE_ERR_ALIGN;
+  if ((z > g ? z - g : g - z) % 16) return CE_ERR_ALIGN;
+  if ((uint64_t)B > UINT64_MAX / ((uint64_t)C * es)) return CE_ERR_SHAPE;
+  const uintptr_t nbytes = (uintptr_t)B * (uintptr_t)C * es;
+  if (overlaps(z, nbytes, g, nbytes)) return CE_ERR_ALIAS;
+
+  const int forced = g_force_path.load(std::memory_order_relaxed);
+  const int path = forced ? forced : auto_path(C, es);
+  const hipStream_t st = as_stream(stream);
+  if (dtype == CE_F32)
+    return fwd_grad_typed<float>(path, (const float*)logits, targets, B, C, (float*)grad_out,
+                                 loss_out, st);
+  return fwd_grad_typed<__bf16>(path, (const __bf16*)logits, targets, B, C, (__bf16*)grad_out,
+                                loss_out, st);
+}
+
+size_t ce_reduce_workspace_bytes(int64_t B) {
+  if (B <= 0) return 0;
+  const int64_t blocks = reduce_blocks(B);
+  return blocks > 1 ? (size_t)blocks * sizeof(float) : 0;
+}
+
+int ce_reduce_loss(const float* loss_rows, int64_t B, float* loss_scalar_out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!loss_rows || !loss_scalar_out) return CE_ERR_NULL;
+  if (B <= 0) return CE_ERR_SHAPE;
+  if ((uintptr_t)loss_rows % 4 || (uintptr_t)loss_scalar_out % 4) return CE_ERR_ALIGN;
+  const size_t need = ce_reduce_workspace_bytes(B);
+  if (need && (!workspace || workspace_bytes < need)) return CE_ERR_WORKSPACE;
+  if (need && (uintptr_t)workspace % 4) return CE_ERR_ALIGN;
+  const hipStream_t st = as_stream(stream);
+  const int64_t blocks = reduce_blocks(B);
+  if (blocks == 1) {
+    hipLaunchKernelGGL(ce::ce_reduce_kernel, dim3(1), dim3(ce::kReduceThreads), 0, st, loss_rows,
+                       B, B, loss_scalar_out);
+    return launched();
+  }
+  float* part = (float*)workspace;
+  hipLaunchKernelGGL(ce::ce_reduce_kernel, dim3((unsigned)blocks), dim3(ce::kReduceThreads), 0, st,
+                     loss_rows, B, reduce_chunk(B), part);
+  if (launched() != CE_OK) return CE_ERR_LAUNCH;
+  hipLaunchKernelGGL(ce::ce_reduce_kernel, dim3(1), dim3(ce::kReduceThreads), 0, st,
+                     (const float*)part, blocks, blocks, loss_scalar_out);
+  return launched();
+}
+
+const char* ce_status_string(int status) {
+  switch (status) {
+    case CE_OK: return "ok";
+    case CE_ERR_NULL: return "a required pointer is NULL";
+    case CE_ERR_SHAPE: return "invalid shape (B and C must be positive and within limits)";
+    case CE_ERR_DTYPE: return "unknown dtype";
+    case CE_ERR_WORKSPACE: return "workspace missing or too small";
+    case CE_ERR_LAUNCH: return "kernel launch failed";
+    case CE_ERR_ALIGN: return "pointer alignment not supported";
+    case CE_ERR_ALIAS: return "grad_out overlaps logits";
+    case CE_ERR_PATH: return "the forced kernel path cannot take this shape";
+    default: return "unknown status";
+  }
+}
+
+const char* ce_version(void) { return "ce_mi355x 0.1.0 gfx950"; }
+
+int ce_select_path(int64_t C, int dtype) {
+  if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
+  if (C <= 0 || C > CE_MAX_C) return CE_ERR_SHAPE;
+  const int forced = g_force_path.load(std::memory_order_relaxed);
+  return forced ? forced : auto_path(C, elem_size(dtype));
+}
+
+int ce_debug_force_path(int path) {
+  if (path < 0 || path > 3) return CE_ERR_PATH;
+  return g_force_path.exchange(path);
+}
+
+}  // extern "C"

@@ -1,0 +1,417 @@
+// gfx950 kernels of the fused softmax cross-entropy path.
+//
+// The method (rumus project page, milestone M7a; rumus 0.1.1
+// cross_entropy.wgsl pass 1 steps 1-4 and pass 2): per row, the max and the
+// sum of exponentials give the log-sum-exp, the per-row loss is
+// (lse - z_t) / B and the gradient is (softmax - onehot) / B; the per-row
+// losses are then summed.  The WGSL kernel reads each row three times with
+// one 64-lane workgroup per row and two shared-memory trees; the kernels
+// here read each row from HBM once and write each gradient element once.
+//
+// Per row they compute, in float32 and the log2 domain:
+//   cg     = round(max_c z_c * log2 e)
+//   Sx     = sum_{c != t} 2^(z_c log2e - cg)      (target left out of the sum)
+//   a_t    = z_t log2e - cg,  E_t = 2^a_t,  S = Sx + E_t
+//   g_c    = 2^(z_c log2e - cg) / (S B)           (c != t)
+//   g_t    = -Sx / (S B)                           (= (softmax_t - 1)/B without cancellation)
+//   loss*B = log1p(Sx / E_t)                       when a_t > -60
+//          = ln2 * (log2 S - a_t)                  otherwise
+// Both forms equal ln(S / E_t) = lse - z_t; the first keeps full relative
+// accuracy when the target holds almost all of the mass.
+#pragma once
+
+#include "ce_device.h"
+
+namespace ce {
+
+// Per-row epilogue shared by both kernels: from the row's (cg, Sx) and the
+// target logit, the gradient scale 1/(S B), the target's gradient and the
+// per-row loss.
+struct RowResult {
+  float scale;   // multiply 2^(z log2e - cg) by this to get the gradient
+  float gt;      // gradient of the target element
+  float loss;    // per-row loss, already scaled by 1/B
+};
+
+__device__ __forceinline__ RowResult row_epilogue(float cg, float sx, float zt, bool valid,
+                                                  float invB) {
+  RowResult r;
+  const float at = __builtin_fmaf(zt, kLog2e, -cg);
+  const float et = exp2_hw(at);
+  const float S = sx + et;
+  const float scale = invB / S;
+  float lossB;
+  if (at > -60.f)
+    lossB = log1pf(sx * exp2_hw(-at));
+  else
+    lossB = kLn2 * (log2_hw(S) - at);
+  const float qnan = __builtin_nanf("");
+  r.scale = valid ? scale : qnan;
+  r.gt = valid ? -sx * scale : qnan;
+  r.loss = valid ? lossB * invB : qnan;
+  return r;
+}
+
+// ===========================================================================
+// Path 1: short rows.  S lanes per row (S = 1..16), 256/S rows per
+// 256-thread workgroup.  Lane q of a segment holds the vectors q, q+S, ...
+// of its row (VW elements each, EPL elements in all), so the lanes of a
+// segment read consecutive addresses.  Max and sum are reduced across the
+// segment with DPP; nothing goes through LDS.
+// ===========================================================================
+template <typename T, int VW>
+struct VecIO;
+
+template <int VW>
+struct VecIO<float, VW> {
+  static_assert(VW == 1 || VW == 2 || VW == 4, "fp32 vector width");
+  __device__ static __forceinline__ void load(rsrc_t r, uint32_t off, float (&f)[VW]) {
+    if constexpr (VW == 1) {
+      const unsigned d = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kPolicyStream);
+      f[0] = __builtin_bit_cast(float, d);
+    } else if constexpr (VW == 2) {
+      const f32x2 v = as_f32(__builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kPolicyStream));
+      f[0] = v.x;
+      f[1] = v.y;
+    } else {
+      const f32x4 v = as_f32(__builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kPolicyStream));
+      f[0] = v.x;
+      f[1] = v.y;
+      f[2] = v.z;
+      f[3] = v.w;
+    }
+  }
+  __device__ static __forceinline__ void store(rsrc_t r, uint32_t off, const float (&g)[VW]) {
+    if constexpr (VW == 1) {
+      const float x = g[0];
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, (int)off, 0,
+                                            kPolicyStream);
+    } else if constexpr (VW == 2) {
+      __builtin_amdgcn_raw_buffer_store_b64(as_u32(f32x2{g[0], g[1]}), r, (int)off, 0,
+                                            kPolicyStream);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b128(as_u32(f32x4{g[0], g[1], g[2], g[3]}), r, (int)off,
+                                             0, kPolicyStream);
+    }
+  }
+};
+
+template <int VW>
+struct VecIO<__bf16, VW> {
+  static_assert(VW == 1 || VW == 2 || VW == 4 || VW == 8, "bf16 vector width");
+  __device__ static __forceinline__ void load(rsrc_t r, uint32_t off, float (&f)[VW]) {
+    if constexpr (VW == 1) {
+      unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, kPolicyStream);
+      f[0] = __builtin_bit_cast(float, (unsigned)h << 16);
+    } else if constexpr (VW == 2) {
+      unsigned d = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kPolicyStream);
+      f[0] = bf16lo(d);
+      f[1] = bf16hi(d);
+    } else if constexpr (VW == 4) {
+      u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kPolicyStream);
+      f[0] = bf16lo(v.x); f[1] = bf16hi(v.x);
+      f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
+    } else {
+      u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kPolicyStream);
+      float t[8];
+      Elem<__bf16>::unpack(v, t);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = t[i];
+    }
+  }
+  __device__ static __forceinline__ void store(rsrc_t r, uint32_t off, const float (&g)[VW]) {
+    if constexpr (VW == 1) {
+      unsigned d = pack_bf16x2(g[0], 0.f);
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(d & 0xffffu), r, (int)off, 0,
+                                            kPolicyStream);
+    } else if constexpr (VW == 2) {
+      __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(g[0], g[1]), r, (int)off, 0,
+                                            kPolicyStream);
+    } else if constexpr (VW == 4) {
+      u32x2 v = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+      __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kPolicyStream);
+    } else {
+      u32x4 v = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
+                 pack_bf16x2(g[6], g[7])};
+      __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kPolicyStream);
+    }
+  }
+};
+
+constexpr int kShortThreads = 256;
+
+template <typename T, int S, int EPL, int VW>
+__global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
+    const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B, int C,
+    float invB, T* __restrict__ grad, float* __restrict__ loss_rows) {
+  constexpr int RPB = kShortThreads / S;  // rows per workgroup
+  constexpr int NVEC = EPL / VW;          // vector slots per lane
+  static_assert(EPL % VW == 0, "EPL must be a multiple of VW");
+  constexpr uint32_t ES = sizeof(T);
+
+  const int tid = threadIdx.x;
+  const int q = tid % S;
+  const int64_t row0 = (int64_t)blockIdx.x * RPB;
+  const int64_t row = row0 + tid / S;
+  const bool live = row < B;
+  const int64_t nrows = (B - row0) < RPB ? (B - row0) : RPB;
+  const uint32_t bytes = (uint32_t)(nrows * C * ES);
+  const rsrc_t rin = make_rsrc(logits + row0 * C, bytes);
+  const rsrc_t rout = make_rsrc(grad + row0 * C, bytes);
+  const uint32_t rowoff = (uint32_t)(tid / S) * (uint32_t)C * ES;
+
+  const int32_t t = live ? targets[row] : 0;
+  const bool valid = live && t >= 0 && t < C;
+  // slot of the target in its owner lane: element c sits in vector c/VW,
+  // lane (c/VW) % S, slot ((c/VW)/S)*VW + c%VW
+  const int tq = valid ? (t / VW) % S : -1;
+  const int tslot = valid ? ((t / VW) / S) * VW + t % VW : -1;
+  const bool owner = (q == tq);
+
+  float f[EPL];
+#pragma unroll
+  for (int j = 0; j < NVEC; ++j) {
+    const int c0 = (j * S + q) * VW;
+    float v[VW];
+    if (c0 < C) {
+      VecIO<T, VW>::load(rin, rowoff + (uint32_t)c0 * ES, v);
+    } else {
+#pragma unroll
+      for (int w = 0; w < VW; ++w) v[w] = kNegInf;
+    }
+#pragma unroll
+    for (int w = 0; w < VW; ++w) f[j * VW + w] = v[w];
+  }
+  const float zt = valid ? Elem<T>::load1(logits + row * C + t) : 0.f;
+
+  // row max across the segment, then the sum with the target left out
+  const float m = seg_allreduce<S>(max_of(f), OpMax{});
+  const float cg = m * kLog2e;
+  float e[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const float x = (owner && i == tslot) ? kNegInf : f[i];
+    e[i] = exp2_hw(__builtin_fmaf(x, kLog2e, -cg));
+  }
+  const float sx = seg_allreduce<S>(tree_sum(e), OpAdd{});
+  const RowResult rr = row_epilogue(cg, sx, zt, valid, invB);
+  if (live && q == 0) loss_rows[row] = rr.loss;
+
+#pragma unroll
+  for (int j = 0; j < NVEC; ++j) {
+    const int c0 = (j * S + q) * VW;
+    if (c0 < C) {
+      float g[VW];
+#pragma unroll
+      for (int w = 0; w < VW; ++w) {
+        const int i = j * VW + w;
+        g[w] = (owner && i == tslot) ? rr.gt : exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
+      }
+      VecIO<T, VW>::store(rout, rowoff + (uint32_t)c0 * ES, g);
+    }
+  }
+}
+
+// ===========================================================================
+// Paths 2 and 3: one workgroup of NT threads per row.  The row's aligned
+// body is split into 16-byte vectors; thread i holds vectors i, i+NT, ...,
+// i+(NV-1)NT in registers (NV*16 bytes per thread).  Vectors beyond NT*NV
+// (path 3) are streamed: folded into the online state on the first read and
+// read again for the gradient.  The up to 2*(VE-1) elements before the first
+// 16-byte boundary and after the last one are handled one per thread.
+//
+// Phase A: every load of the row is issued at once.
+// Phase B: each thread folds its vectors into an online (c, s) state as they
+//          arrive, with the target element left out of s.
+// Combine: (c, s) is reduced over the wave with DPP, the waves' pairs go
+//          through LDS, and every wave combines them in the same fixed order.
+// Phase C: the gradient is formed from the registers and written with
+//          streaming stores.
+// ===========================================================================
+template <typename T, int NT, int NV>
+__global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits,
+                                                    const int32_t* __restrict__ targets,
+                                                    int64_t C, float invB, T* __restrict__ grad,
+                                                    float* __restrict__ loss_rows) {
+  using E = Elem<T>;
+  constexpr int VE = E::VE;
+  constexpr int NW = NT / 64;
+  static_assert(NT % 64 == 0 && NW <= 16, "1 to 16 waves");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int64_t row = blockIdx.x;
+  const T* rp = logits + row * C;
+  T* gp = grad + row * C;
+
+  const uint32_t mis = (uint32_t)((uintptr_t)rp & 15u);
+  int64_t h = mis ? (int64_t)((16u - mis) / sizeof(T)) : 0;  // head elements
+  if (h > C) h = C;
+  const int64_t nb = (C - h) / VE;                              // aligned vectors
+  const int64_t tail0 = h + nb * VE;
+  const int64_t ntail = C - tail0;
+  const rsrc_t rin = make_rsrc(rp + h, (uint32_t)(nb * 16));
+  const rsrc_t rout = make_rsrc(gp + h, (uint32_t)(nb * 16));
+
+  const int32_t t = targets[row];
+  const bool valid = t >= 0 && (int64_t)t < C;
+  // where the target lives: body vector tv (element tj), or an edge element
+  const int64_t tb = (int64_t)t - h;
+  const bool t_in_body = valid && tb >= 0 && tb < nb * VE;
+  const int64_t tv = t_in_body ? tb / VE : -1;
+  const int tj = t_in_body ? (int)(tb % VE) : -1;
+  const int own_k = (t_in_body && tv < (int64_t)NT * NV) ? (int)(tv / NT) : -1;  // uniform
+  const bool own_thread = t_in_body && (tv % NT) == tid;
+
+  // Phase A: issue every load
+  const uint32_t voff = (uint32_t)tid * 16u;
+  u32x4 v[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+    v[k] = bload128<kPolicyStream>(rin, voff, (uint32_t)k * NT * 16u);
+
+  int64_t xe = -1;  // this thread's edge element, if any
+  if (tid < h)
+    xe = tid;
+  else if (tid - h < ntail)
+    xe = tail0 + (tid - h);
+  const float xs = xe >= 0 ? E::load1(rp + xe) : kNegInf;
+  const float zt = valid ? E::load1(rp + t) : 0.f;
+
+  // Phase B: online max / sum-exp over the thread's elements
+  float c = kLowest, s = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int64_t base = (int64_t)k * NT;
+    if (base >= nb) continue;  // uniform: no vector of this slot is in the row
+    float f[VE];
+    E::unpack(v[k], f);
+    if (base + NT > nb) {
+      const bool ok = base + tid < nb;
+#pragma unroll
+      for (int i = 0; i < VE; ++i) f[i] = ok ? f[i] : kNegInf;
+    }
+    const float vm = max_of(f);
+    if (k == own_k && own_thread) {
+#pragma unroll
+      for (int i = 0; i < VE; ++i) f[i] = (i == tj) ? kNegInf : f[i];
+    }
+    online_fold(c, s, vm, f);
+  }
+  // path 3: the part of the row beyond the registers, streamed
+  for (int64_t vi = (int64_t)NT * NV + tid; vi < nb; vi += NT) {
+    const u32x4 w = bload128<kPolicyDefault>(rin, (uint32_t)(vi * 16), 0u);
+    float f[VE];
+    E::unpack(w, f);
+    const float vm = max_of(f);
+    if (vi == tv) {
+#pragma unroll
+      for (int i = 0; i < VE; ++i) f[i] = (i == tj) ? kNegInf : f[i];
+    }
+    online_fold(c, s, vm, f);
+  }
+  if (xe >= 0) {
+    const float one[1] = {(xe == (int64_t)t) ? kNegInf : xs};
+    online_fold(c, s, xs, one);
+  }
+
+  // Combine: wave, then workgroup, in a fixed order
+  const float cw = wave_allreduce(c, OpMax{});
+  const float sw = wave_allreduce(s * exp2_hw(c - cw), OpAdd{});
+  float cg, sx;
+  if constexpr (NW == 1) {
+    cg = cw;
+    sx = sw;
+  } else {
+    __shared__ float red_c[NW], red_s[NW];
+    const int wv = tid >> 6;
+    if (lane == 0) {
+      red_c[wv] = cw;
+      red_s[wv] = sw;
+    }
+    __syncthreads();
+    const float ci = lane < NW ? red_c[lane] : kLowest;
+    const float si = lane < NW ? red_s[lane] : 0.f;
+    cg = wave_uniform(seg_allreduce<16>(ci, OpMax{}));
+    sx = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
+  }
+  const RowResult rr = row_epilogue(cg, sx, zt, valid, invB);
+  if (tid == 0) loss_rows[row] = rr.loss;
+
+  // Phase C: gradient from the registers.  The empty asm makes each packed
+  // vector opaque here, so the compiler widens it again instead of keeping
+  // phase B's widened copy alive (twice the registers for bf16).
+#pragma unroll
+  for (int k = 0; k < NV; ++k) asm volatile("" : "+v"(v[k]));
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int64_t base = (int64_t)k * NT;
+    if (base >= nb) continue;
+    float f[VE], g[VE];
+    E::unpack(v[k], f);
+#pragma unroll
+    for (int i = 0; i < VE; ++i) g[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
+    if (k == own_k && own_thread) {
+#pragma unroll
+      for (int i = 0; i < VE; ++i) g[i] = (i == tj) ? rr.gt : g[i];
+    }
+    bstore128<kPolicyStream>(E::pack(g), rout, voff, (uint32_t)k * NT * 16u);
+  }
+  for (int64_t vi = (int64_t)NT * NV + tid; vi < nb; vi += NT) {
+    const u32x4 w = bload128<kPolicyStream>(rin, (uint32_t)(vi * 16), 0u);
+    float f[VE], g[VE];
+    E::unpack(w, f);
+#pragma unroll
+    for (int i = 0; i < VE; ++i) g[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
+    if (vi == tv) {
+#pragma unroll
+      for (int i = 0; i < VE; ++i) g[i] = (i == tj) ? rr.gt : g[i];
+    }
+    bstore128<kPolicyStream>(E::pack(g), rout, (uint32_t)(vi * 16), 0u);
+  }
+  if (xe >= 0) {
+    const float g = (xe == (int64_t)t) ? rr.gt : exp2_hw(__builtin_fmaf(xs, kLog2e, -cg)) * rr.scale;
+    E::store1(gp + xe, g);
+  }
+}
+
+// ===========================================================================
+// Loss reduction: a fixed two-level tree.  Workgroup g of the first level
+// sums the contiguous range [g*chunk, (g+1)*chunk) of the input; each
+// thread adds its elements i, i+256, ... in order into four interleaved
+// accumulators, and the workgroup combines its threads with DPP/ds_swizzle
+// and four LDS slots in a fixed order.  The second level is the same code
+// over the first level's partial sums.  Nothing depends on timing, so the
+// result is reproducible bit for bit.
+// ===========================================================================
+constexpr int kReduceThreads = 256;
+
+__device__ __forceinline__ float block_sum_256(float v) {
+  __shared__ float part[kReduceThreads / 64];
+  const float w = wave_allreduce(v, OpAdd{});
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = w;
+  __syncthreads();
+  return (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+__global__ __launch_bounds__(kReduceThreads) void ce_reduce_kernel(const float* __restrict__ in,
+                                                                   int64_t n, int64_t chunk,
+                                                                   float* __restrict__ out) {
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  const int64_t hi = (lo + chunk) < n ? (lo + chunk) : n;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int64_t i = lo + threadIdx.x;
+  for (; i + 3 * kReduceThreads < hi; i += 4 * kReduceThreads) {
+    a0 += in[i];
+    a1 += in[i + kReduceThreads];
+    a2 += in[i + 2 * kReduceThreads];
+    a3 += in[i + 3 * kReduceThreads];
+  }
+  if (i < hi) a0 += in[i];
+  if (i + kReduceThreads < hi) a1 += in[i + kReduceThreads];
+  if (i + 2 * kReduceThreads < hi) a2 += in[i + 2 * kReduceThreads];
+  const float tot = block_sum_256((a0 + a1) + (a2 + a3));
+  if (threadIdx.x == 0) out[blockIdx.x] = tot;
+}
+
+}  // namespace ce

@@ -1,0 +1,139 @@
+"""The C-ABI library on the CPU: it loads, exports every function that
+include/ce.h declares, and rejects invalid arguments with the documented
+status before any HIP call (so none of these calls reaches a device)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import softmax_cross_entropy_ce_amd as ce
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ce.h")
+
+OK, NULL, SHAPE, DTYPE, WORKSPACE, LAUNCH, ALIGN, ALIAS, PATH = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+# Fake, never-dereferenced device addresses: every call below fails
+# validation first.
+Z = 0x10000000
+G = 0x20000000
+T = 0x30000000
+L = 0x40000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ce_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L_ = ce.lib()
+    names = declared_functions()
+    assert names == sorted(["ce_fwd_grad", "ce_reduce_workspace_bytes", "ce_reduce_loss",
+                            "ce_status_string", "ce_version", "ce_select_path",
+                            "ce_debug_force_path"])
+    for n in names:
+        assert hasattr(L_, n), n
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in ce.version()
+    for s in (OK, NULL, SHAPE, DTYPE, WORKSPACE, LAUNCH, ALIGN, ALIAS, PATH):
+        assert ce.status_string(s) and ce.status_string(s) != "unknown status"
+    assert ce.status_string(-99) == "unknown status"
+
+
+def fwd(z=Z, t=T, B=8, C=10, dtype=0, g=G, l=L):
+    return ce.lib().ce_fwd_grad(z, t, B, C, dtype, g, l, None)
+
+
+def test_fwd_grad_null_pointers():
+    assert fwd(z=None) == NULL
+    assert fwd(t=None) == NULL
+    assert fwd(g=None) == NULL
+    assert fwd(l=None) == NULL
+
+
+def test_fwd_grad_shapes():
+    assert fwd(B=0) == SHAPE
+    assert fwd(B=-3) == SHAPE
+    assert fwd(C=0) == SHAPE
+    assert fwd(C=-1) == SHAPE
+    assert fwd(C=(1 << 28) + 1) == SHAPE
+    assert fwd(B=1 << 31) == SHAPE
+
+
+def test_fwd_grad_dtype():
+    assert fwd(dtype=2) == DTYPE
+    assert fwd(dtype=-1) == DTYPE
+
+
+def test_fwd_grad_alignment():
+    assert fwd(z=Z + 2, dtype=0) == ALIGN          # fp32 needs 4-byte alignment
+    assert fwd(z=Z + 1, dtype=1) == ALIGN          # bf16 needs 2-byte alignment
+    assert fwd(z=Z + 4, g=G, dtype=0) == ALIGN     # logits and grad 16-byte congruent
+    assert fwd(t=T + 2) == ALIGN
+    assert fwd(l=L + 1) == ALIGN
+
+
+def test_fwd_grad_alias():
+    # grad overlapping logits is refused: same start, and a partial overlap
+    assert fwd(z=Z, g=Z) == ALIAS
+    assert fwd(z=Z, g=Z + 16, B=8, C=10) == ALIAS
+
+
+def test_reduce_workspace_sizes():
+    f = ce.reduce_workspace_bytes
+    assert f(0) == 0 and f(-5) == 0
+    assert f(1) == 0 and f(8) == 0 and f(2048) == 0
+    assert f(2049) == 2 * 4
+    # 2M rows: at most 1024 first-level partial sums
+    assert 0 < f(2_097_152) <= 1024 * 4
+
+
+def red(x=L, B=8, out=G, ws=None, wsb=0):
+    return ce.lib().ce_reduce_loss(x, B, out, ws, wsb, None)
+
+
+def test_reduce_loss_validation():
+    assert red(x=None) == NULL
+    assert red(out=None) == NULL
+    assert red(B=0) == SHAPE
+    assert red(x=L + 2) == ALIGN
+    assert red(B=1 << 20) == WORKSPACE                      # workspace needed, none given
+    need = ce.reduce_workspace_bytes(1 << 20)
+    assert red(B=1 << 20, ws=T, wsb=need - 1) == WORKSPACE  # too small
+    assert red(B=1 << 20, ws=T + 2, wsb=need) == ALIGN
+
+
+@pytest.mark.parametrize("name,C,dtype,path", [
+    ("tiny", 10, 0, 1),
+    ("classifier", 1000, 0, 2),
+    ("skinny", 10, 0, 1),
+    ("lmhead50k", 50257, 0, 2),
+    ("lmhead128k", 128256, 1, 2),
+    ("beyond-registers-bf16", 200_000, 1, 3),
+    ("beyond-registers-f32", 100_000, 0, 3),
+    ("short-limit", 256, 0, 1),
+    ("just-over-short", 257, 1, 2),
+])
+def test_path_selection(name, C, dtype, path):
+    assert ce.select_path(C, dtype) == path
+
+
+def test_force_path_round_trip():
+    prev = ce.force_path(3)
+    try:
+        assert ce.select_path(10, 0) == 3
+        assert ce.force_path(1) == 3
+        # a row too long for the short path is refused, before any launch
+        assert fwd(C=1000) == PATH
+    finally:
+        ce.force_path(prev)
+    assert ce.select_path(10, 0) == 1
+    assert ce.lib().ce_debug_force_path(7) == PATH

@@ -1,0 +1,166 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs, element by element, on every kernel path."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import ce_rows, reduce_loss
+
+from _parity import (compare_block, compare_scalar, full_parity, grad_to_host, run_gpu,
+                     to_device, widen_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _reset_path():
+    import softmax_cross_entropy_ce_amd as ce
+    prev = ce.force_path(0)
+    yield
+    ce.force_path(prev)
+
+
+def _force(path):
+    import softmax_cross_entropy_ce_amd as ce
+    ce.force_path(path)
+
+
+def _log(name, worst):
+    print(f"[parity] {name}: " + ", ".join(f"{k}={v:.3g}" for k, v in worst.items()), flush=True)
+
+
+# (B, C, dtype, sigma) — several tiles and a ragged tail on every path;
+# odd C makes fp32 rows 4-byte aligned and bf16 rows 2-byte aligned.
+SMALL = [
+    (8, 10, "f32", 1.0),
+    (37, 1, "f32", 3.0),
+    (5, 3, "bf16", 2.0),
+    (300, 7, "f32", 20.0),
+    (513, 16, "bf16", 4.0),
+    (70, 33, "f32", 5.0),
+    (129, 100, "bf16", 4.0),
+    (257, 256, "f32", 2.0),
+    (64, 257, "bf16", 3.0),
+    (1024, 1000, "f32", 2.0),
+    (33, 4099, "f32", 3.0),
+    (17, 12345, "bf16", 4.0),
+    (9, 50257, "f32", 3.0),
+    (6, 128256, "bf16", 4.0),
+]
+
+
+def _legal(path, C):
+    return path != 1 or C <= 256
+
+
+@pytest.mark.parametrize("path", [0, 1, 2, 3], ids=["auto", "short", "resident", "long"])
+@pytest.mark.parametrize("B,C,dtype,sigma", SMALL, ids=[f"{b}x{c}-{d}" for b, c, d, _ in SMALL])
+def test_parity_small(path, B, C, dtype, sigma):
+    if not _legal(path, C):
+        pytest.skip("short path takes C <= 256")
+    z, t = synth.make_inputs(B, C, dtype, sigma, seed=B * 1000 + C)
+    _force(path)
+    _log(f"{B}x{C} {dtype} path={path}", full_parity(z, t, dtype, where=f"{B}x{C} {dtype} p{path}"))
+
+
+@pytest.mark.parametrize("path", [0, 2, 3], ids=["auto", "resident", "long"])
+def test_parity_spike_rows(path):
+    """Rows with one +1e4 entry (the LM-head stability case) on a ragged
+    shape, including rows whose target is the spike."""
+    B, C = 40, 50257
+    z, t = synth.make_inputs(B, C, "f32", 3.0, spike=1e4, seed=11)
+    spikes = synth.spike_columns(B, C, seed=11)
+    t[:5] = spikes[:5].astype(np.int32)
+    _force(path)
+    _log(f"spike path={path}", full_parity(z, t, "f32", where=f"spike p{path}"))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("path", [0, 1, 2, 3], ids=["auto", "short", "resident", "long"])
+def test_parity_edge_values(path, dtype):
+    """Uniform rows (loss ln C), rows of +-1e4, rows where the target holds
+    nearly all the mass, and invalid targets (NaN rows)."""
+    C = 200
+    rng = np.random.Generator(np.random.PCG64(5))
+    z = (rng.standard_normal((12, C)) * 3).astype(np.float32)
+    t = rng.integers(0, C, 12).astype(np.int32)
+    z[0] = 0.0
+    z[1] = 1e4
+    z[2] = -1e4
+    z[3, ::2] = 1e4
+    z[3, 1::2] = -1e4
+    z[4, t[4]] = z[4].max() + 30.0       # target dominates: softmax_t ~ 1 - 1e-11
+    z[5, t[5]] = z[5].max() + 12.0
+    t[6] = -1                            # invalid targets
+    t[7] = C
+    z[8] = np.float32(2.5)
+    if dtype == "bf16":
+        z = synth.bf16_bits_from_f32(z)
+    _force(path)
+    if not _legal(path, C):
+        pytest.skip("short path takes C <= 256")
+    _log(f"edges {dtype} path={path}", full_parity(z, t, dtype, where=f"edges {dtype} p{path}"))
+
+
+def test_parity_tiny_workload():
+    z, t = synth.make_workload("tiny")
+    _log("tiny", full_parity(z, t, "f32", where="tiny"))
+
+
+def test_parity_classifier_workload():
+    z, t = synth.make_workload("classifier")
+    _log("classifier", full_parity(z, t, "f32", where="classifier"))
+
+
+def test_parity_skinny_workload():
+    """2,097,152 rows of 10 classes, sigma 20: every row compared, and the
+    2M-term loss reduction."""
+    z, t = synth.make_workload("skinny")
+    _log("skinny", full_parity(z, t, "f32", block_elems=1 << 22, where="skinny"))
+
+
+def test_parity_lmhead50k_workload():
+    """4096 x 50257 fp32 with a +1e4 spike per row: every row compared."""
+    z, t = synth.make_workload("lmhead50k")
+    _log("lmhead50k", full_parity(z, t, "f32", block_elems=1 << 24, where="lmhead50k"))
+
+
+def test_parity_lmhead128k_workload_sampled():
+    """8192 x 128256 bf16 at full size in the launch configuration the
+    benchmark times: 96 seeded-random rows plus the first and last rows are
+    compared with the oracle element by element; the scalar is compared with
+    the oracle's sum over all rows, computed in row blocks."""
+    import torch
+    z, t = synth.make_workload("lmhead128k")
+    B, C = z.shape
+    z_dev, t_dev = to_device(z, t, "bf16")
+    grad, loss_rows, loss = run_gpu(z_dev, t_dev)
+    rng = np.random.Generator(np.random.PCG64(123))
+    rows = np.unique(np.concatenate([[0, B - 1], rng.choice(B, 96, replace=False)]))
+    lr = loss_rows.cpu().numpy()
+    idx = torch.from_numpy(rows).to(grad.device)
+    g = grad_to_host(grad.index_select(0, idx), "bf16")
+    worst, _ = compare_block(g, lr[rows], z[rows], t[rows], B, "bf16", where="lmhead128k")
+    from concurrent.futures import ThreadPoolExecutor
+    step = 128
+
+    def block(lo):
+        zb = widen_rows(z[lo:lo + step], "bf16")
+        l, _ = ce_rows(zb, t[lo:lo + step], B)
+        return l, 1e-5 * (np.abs(zb.max(axis=1)) + math.log(C) + 1.0) / B
+
+    with ThreadPoolExecutor(8) as ex:
+        parts = list(ex.map(block, range(0, B, step)))
+    ora = np.concatenate([p[0] for p in parts])
+    tol = np.concatenate([p[1] for p in parts])
+    worst["loss_rel"] = compare_scalar(float(loss.item()), reduce_loss(ora), "bf16", "lmhead128k")
+    # every per-row loss, not just the sampled rows
+    err = np.abs(lr.astype(np.float64) - ora)
+    worst["loss_rows_all_abs"] = float(err.max())
+    assert (err <= tol).all(), f"row {int(np.argmax(err - tol))}"
+    _log("lmhead128k sampled", worst)
