@@ -101,11 +101,28 @@ int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, float invB,
 }
 
 // -------------------------------------------------------------- paths 2, 3
+// Workgroups of a kernel that the current device holds at once: compute
+// units times the occupancy of that kernel.  The row kernels are persistent,
+// so their grid is this number (or B when that is smaller).
+int resident_blocks(const void* kernel, int nt) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nt, 0) != hipSuccess)
+    return -1;
+  if (per_cu < 1) per_cu = 1;
+  return cus * per_cu;
+}
+
 template <typename T, int NT, int NV>
 int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g,
                    float* l, hipStream_t st) {
-  hipLaunchKernelGGL((ce::ce_row_kernel<T, NT, NV>), dim3((unsigned)B), dim3(NT), 0, st, z, t, C,
-                     invB, g, l);
+  auto kern = ce::ce_row_kernel<T, NT, NV>;
+  const int res = resident_blocks(reinterpret_cast<const void*>(kern), NT);
+  if (res < 1) return CE_ERR_LAUNCH;
+  const int64_t grid = B < res ? B : res;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), 0, st, z, t, B, (int)C, invB, g, l);
   return launched();
 }
 

@@ -213,165 +213,219 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
 }
 
 // ===========================================================================
-// Paths 2 and 3: one workgroup of NT threads per row.  The row's aligned
-// body is split into 16-byte vectors; thread i holds vectors i, i+NT, ...,
-// i+(NV-1)NT in registers (NV*16 bytes per thread).  Vectors beyond NT*NV
-// (path 3) are streamed: folded into the online state on the first read and
-// read again for the gradient.  The up to 2*(VE-1) elements before the first
-// 16-byte boundary and after the last one are handled one per thread.
+// Paths 2 and 3: one workgroup of NT threads per row at a time.  The row's
+// aligned body is split into 16-byte vectors; thread i holds vectors i,
+// i+NT, ..., i+(NV-1)NT in registers (NV*16 bytes per thread).  Vectors
+// beyond NT*NV (path 3) are streamed: folded into the online state on the
+// first read and read again for the gradient.  The up to 2*(VE-1) elements
+// before the first 16-byte boundary and after the last one are handled one
+// per thread.
 //
-// Phase A: every load of the row is issued at once.
-// Phase B: each thread folds its vectors into an online (c, s) state as they
-//          arrive, with the target element left out of s.
-// Combine: (c, s) is reduced over the wave with DPP, the waves' pairs go
-//          through LDS, and every wave combines them in the same fixed order.
-// Phase C: the gradient is formed from the registers and written with
-//          streaming stores.
+// The workgroups are persistent: workgroup w takes rows w, w+G, w+2G, ...
+// (G = gridDim.x, sized to the resident capacity of the GPU) and the
+// per-row work is software-pipelined across rows:
+//   Phase B: each thread folds its vectors of row r into an online (c, s)
+//            state as they arrive, with the target element left out of s.
+//   Combine: (c, s) is reduced over the wave with DPP, the waves' pairs go
+//            through LDS (double-buffered by row parity, so one barrier per
+//            row suffices), and every wave combines them in the same order.
+//   Phase C: for each register slot, the vector of row r is widened, the
+//            slot is immediately refilled with the load of the same slot of
+//            row r+G, and the gradient of row r is written with streaming
+//            stores.  The loads of the next row are in flight while this
+//            row's gradient is formed and written.
 // ===========================================================================
+struct RowGeom {
+  int h;       // elements before the first 16-byte boundary
+  int nb;      // aligned 16-byte vectors
+  int tail0;   // first element after the aligned body
+  int ntail;   // elements after the aligned body
+};
+
+// Row-relative indices fit in 32 bits: C <= 2^28.
+template <typename T>
+__device__ __forceinline__ RowGeom row_geom(const T* rp, int C) {
+  constexpr int VE = Elem<T>::VE;
+  RowGeom g;
+  const uint32_t mis = (uint32_t)((uintptr_t)rp & 15u);
+  g.h = mis ? (int)((16u - mis) / sizeof(T)) : 0;
+  if (g.h > C) g.h = C;
+  g.nb = (C - g.h) / VE;
+  g.tail0 = g.h + g.nb * VE;
+  g.ntail = C - g.tail0;
+  return g;
+}
+
 template <typename T, int NT, int NV>
 __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits,
                                                     const int32_t* __restrict__ targets,
-                                                    int64_t C, float invB, T* __restrict__ grad,
+                                                    int64_t B, int C, float invB,
+                                                    T* __restrict__ grad,
                                                     float* __restrict__ loss_rows) {
   using E = Elem<T>;
   constexpr int VE = E::VE;
   constexpr int NW = NT / 64;
   static_assert(NT % 64 == 0 && NW <= 16, "1 to 16 waves");
+  __shared__ float red_c[2][NW], red_s[2][NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int64_t row = blockIdx.x;
-  const T* rp = logits + row * C;
-  T* gp = grad + row * C;
-
-  const uint32_t mis = (uint32_t)((uintptr_t)rp & 15u);
-  int64_t h = mis ? (int64_t)((16u - mis) / sizeof(T)) : 0;  // head elements
-  if (h > C) h = C;
-  const int64_t nb = (C - h) / VE;                              // aligned vectors
-  const int64_t tail0 = h + nb * VE;
-  const int64_t ntail = C - tail0;
-  const rsrc_t rin = make_rsrc(rp + h, (uint32_t)(nb * 16));
-  const rsrc_t rout = make_rsrc(gp + h, (uint32_t)(nb * 16));
-
-  const int32_t t = targets[row];
-  const bool valid = t >= 0 && (int64_t)t < C;
-  // where the target lives: body vector tv (element tj), or an edge element
-  const int64_t tb = (int64_t)t - h;
-  const bool t_in_body = valid && tb >= 0 && tb < nb * VE;
-  const int64_t tv = t_in_body ? tb / VE : -1;
-  const int tj = t_in_body ? (int)(tb % VE) : -1;
-  const int own_k = (t_in_body && tv < (int64_t)NT * NV) ? (int)(tv / NT) : -1;  // uniform
-  const bool own_thread = t_in_body && (tv % NT) == tid;
-
-  // Phase A: issue every load
   const uint32_t voff = (uint32_t)tid * 16u;
+  const int64_t G = gridDim.x;
+  int64_t row = blockIdx.x;
+  if (row >= B) return;  // whole workgroup
+
+  // Phase A of the first row: issue every register load
   u32x4 v[NV];
+  {
+    const T* rp = logits + row * C;
+    const RowGeom geo = row_geom(rp, C);
+    const rsrc_t rin = make_rsrc(rp + geo.h, (uint32_t)geo.nb * 16u);
 #pragma unroll
-  for (int k = 0; k < NV; ++k)
-    v[k] = bload128<kPolicyStream>(rin, voff, (uint32_t)k * NT * 16u);
-
-  int64_t xe = -1;  // this thread's edge element, if any
-  if (tid < h)
-    xe = tid;
-  else if (tid - h < ntail)
-    xe = tail0 + (tid - h);
-  const float xs = xe >= 0 ? E::load1(rp + xe) : kNegInf;
-  const float zt = valid ? E::load1(rp + t) : 0.f;
-
-  // Phase B: online max / sum-exp over the thread's elements
-  float c = kLowest, s = 0.f;
-#pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    const int64_t base = (int64_t)k * NT;
-    if (base >= nb) continue;  // uniform: no vector of this slot is in the row
-    float f[VE];
-    E::unpack(v[k], f);
-    if (base + NT > nb) {
-      const bool ok = base + tid < nb;
-#pragma unroll
-      for (int i = 0; i < VE; ++i) f[i] = ok ? f[i] : kNegInf;
-    }
-    const float vm = max_of(f);
-    if (k == own_k && own_thread) {
-#pragma unroll
-      for (int i = 0; i < VE; ++i) f[i] = (i == tj) ? kNegInf : f[i];
-    }
-    online_fold(c, s, vm, f);
-  }
-  // path 3: the part of the row beyond the registers, streamed
-  for (int64_t vi = (int64_t)NT * NV + tid; vi < nb; vi += NT) {
-    const u32x4 w = bload128<kPolicyDefault>(rin, (uint32_t)(vi * 16), 0u);
-    float f[VE];
-    E::unpack(w, f);
-    const float vm = max_of(f);
-    if (vi == tv) {
-#pragma unroll
-      for (int i = 0; i < VE; ++i) f[i] = (i == tj) ? kNegInf : f[i];
-    }
-    online_fold(c, s, vm, f);
-  }
-  if (xe >= 0) {
-    const float one[1] = {(xe == (int64_t)t) ? kNegInf : xs};
-    online_fold(c, s, xs, one);
+    for (int k = 0; k < NV; ++k)
+      v[k] = bload128<kPolicyStream>(rin, voff, (uint32_t)k * NT * 16u);
   }
 
-  // Combine: wave, then workgroup, in a fixed order
-  const float cw = wave_allreduce(c, OpMax{});
-  const float sw = wave_allreduce(s * exp2_hw(c - cw), OpAdd{});
-  float cg, sx;
-  if constexpr (NW == 1) {
-    cg = cw;
-    sx = sw;
-  } else {
-    __shared__ float red_c[NW], red_s[NW];
-    const int wv = tid >> 6;
-    if (lane == 0) {
-      red_c[wv] = cw;
-      red_s[wv] = sw;
-    }
-    __syncthreads();
-    const float ci = lane < NW ? red_c[lane] : kLowest;
-    const float si = lane < NW ? red_s[lane] : 0.f;
-    cg = wave_uniform(seg_allreduce<16>(ci, OpMax{}));
-    sx = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
-  }
-  const RowResult rr = row_epilogue(cg, sx, zt, valid, invB);
-  if (tid == 0) loss_rows[row] = rr.loss;
+  for (int parity = 0;; parity ^= 1) {
+    const T* rp = logits + row * C;
+    T* gp = grad + row * C;
+    const RowGeom geo = row_geom(rp, C);
+    const int nb = geo.nb;
+    const rsrc_t rin = make_rsrc(rp + geo.h, (uint32_t)nb * 16u);
+    const rsrc_t rout = make_rsrc(gp + geo.h, (uint32_t)nb * 16u);
 
-  // Phase C: gradient from the registers.  The empty asm makes each packed
-  // vector opaque here, so the compiler widens it again instead of keeping
-  // phase B's widened copy alive (twice the registers for bf16).
+    const int32_t t = targets[row];
+    const bool valid = t >= 0 && t < C;
+    // where the target lives: body vector tv (element tj), or an edge element
+    const int tb = t - geo.h;
+    const bool t_in_body = valid && tb >= 0 && tb < nb * VE;
+    const int tv = t_in_body ? tb / VE : -1;                                  // uniform
+    const int tj = t_in_body ? tb % VE : -1;                                  // uniform
+    const int own_k = (t_in_body && tv < NT * NV) ? tv / NT : -1;             // uniform
+    const bool own_thread = t_in_body && (tv % NT) == tid;
+
+    int xe = -1;  // this thread's edge element, if any
+    if (tid < geo.h)
+      xe = tid;
+    else if (tid - geo.h < geo.ntail)
+      xe = geo.tail0 + (tid - geo.h);
+    const float xs = xe >= 0 ? E::load1(rp + xe) : kNegInf;
+    const float zt = valid ? E::load1(rp + t) : 0.f;
+
+    // Phase B: online max / sum-exp over the thread's elements
+    float c = kLowest, s = 0.f;
 #pragma unroll
-  for (int k = 0; k < NV; ++k) asm volatile("" : "+v"(v[k]));
+    for (int k = 0; k < NV; ++k) {
+      const int base = k * NT;
+      if (base >= nb) continue;  // uniform: no vector of this slot is in the row
+      float f[VE];
+      E::unpack(v[k], f);
+      if (base + NT > nb) {
+        const bool ok = tid < nb - base;
 #pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    const int64_t base = (int64_t)k * NT;
-    if (base >= nb) continue;
-    float f[VE], g[VE];
-    E::unpack(v[k], f);
+        for (int i = 0; i < VE; ++i) f[i] = ok ? f[i] : kNegInf;
+      }
+      const float vm = max_of(f);
+      if (k == own_k && own_thread) {
 #pragma unroll
-    for (int i = 0; i < VE; ++i) g[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
-    if (k == own_k && own_thread) {
-#pragma unroll
-      for (int i = 0; i < VE; ++i) g[i] = (i == tj) ? rr.gt : g[i];
+        for (int i = 0; i < VE; ++i) f[i] = (i == tj) ? kNegInf : f[i];
+      }
+      online_fold(c, s, vm, f);
     }
-    bstore128<kPolicyStream>(E::pack(g), rout, voff, (uint32_t)k * NT * 16u);
-  }
-  for (int64_t vi = (int64_t)NT * NV + tid; vi < nb; vi += NT) {
-    const u32x4 w = bload128<kPolicyStream>(rin, (uint32_t)(vi * 16), 0u);
-    float f[VE], g[VE];
-    E::unpack(w, f);
+    // path 3: the part of the row beyond the registers, streamed
+    for (int vi = NT * NV + tid; vi < nb; vi += NT) {
+      const u32x4 w = bload128<kPolicyDefault>(rin, (uint32_t)vi * 16u, 0u);
+      float f[VE];
+      E::unpack(w, f);
+      const float vm = max_of(f);
+      if (vi == tv) {
 #pragma unroll
-    for (int i = 0; i < VE; ++i) g[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
-    if (vi == tv) {
-#pragma unroll
-      for (int i = 0; i < VE; ++i) g[i] = (i == tj) ? rr.gt : g[i];
+        for (int i = 0; i < VE; ++i) f[i] = (i == tj) ? kNegInf : f[i];
+      }
+      online_fold(c, s, vm, f);
     }
-    bstore128<kPolicyStream>(E::pack(g), rout, (uint32_t)(vi * 16), 0u);
-  }
-  if (xe >= 0) {
-    const float g = (xe == (int64_t)t) ? rr.gt : exp2_hw(__builtin_fmaf(xs, kLog2e, -cg)) * rr.scale;
-    E::store1(gp + xe, g);
+    if (xe >= 0) {
+      const float one[1] = {(xe == t) ? kNegInf : xs};
+      online_fold(c, s, xs, one);
+    }
+
+    // Combine: wave, then workgroup, in a fixed order
+    const float cw = wave_allreduce(c, OpMax{});
+    const float sw = wave_allreduce(s * exp2_hw(c - cw), OpAdd{});
+    float cg, sx;
+    if constexpr (NW == 1) {
+      cg = cw;
+      sx = sw;
+    } else {
+      const int wv = tid >> 6;
+      if (lane == 0) {
+        red_c[parity][wv] = cw;
+        red_s[parity][wv] = sw;
+      }
+      __syncthreads();
+      const float ci = lane < NW ? red_c[parity][lane] : kLowest;
+      const float si = lane < NW ? red_s[parity][lane] : 0.f;
+      cg = wave_uniform(seg_allreduce<16>(ci, OpMax{}));
+      sx = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
+    }
+    const RowResult rr = row_epilogue(cg, sx, zt, valid, invB);
+    if (tid == 0) loss_rows[row] = rr.loss;
+
+    // Phase C: gradient from the registers; each slot is refilled with the
+    // next row's vector as soon as it has been widened.  After the last row
+    // the refill goes through an empty buffer resource: it returns zeros
+    // without a memory access.
+    const int64_t next = row + G;
+    const bool more = next < B;  // uniform
+    const T* rpn = logits + (more ? next : row) * C;
+    const RowGeom geon = row_geom(rpn, C);
+    const rsrc_t rinn = make_rsrc(rpn + geon.h, more ? (uint32_t)geon.nb * 16u : 0u);
+    // The empty asm makes each packed vector opaque here, so the compiler
+    // widens it again instead of keeping phase B's widened copy alive
+    // (twice the registers for bf16).
+#pragma unroll
+    for (int k = 0; k < NV; ++k) asm volatile("" : "+v"(v[k]));
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int base = k * NT;
+      // the gradient of this slot is packed before the slot is refilled, so
+      // the refill can reuse the slot's registers
+      u32x4 packed;
+      if (base < nb) {  // uniform
+        float f[VE], g[VE];
+        E::unpack(v[k], f);
+#pragma unroll
+        for (int i = 0; i < VE; ++i) g[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
+        if (k == own_k && own_thread) {
+#pragma unroll
+          for (int i = 0; i < VE; ++i) g[i] = (i == tj) ? rr.gt : g[i];
+        }
+        packed = E::pack(g);
+      }
+      v[k] = bload128<kPolicyStream>(rinn, voff, (uint32_t)k * NT * 16u);
+      if (base < nb) bstore128<kPolicyStream>(packed, rout, voff, (uint32_t)k * NT * 16u);
+      // keep slot order: a later slot's refill must not be hoisted above
+      // this slot's use of its registers
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int vi = NT * NV + tid; vi < nb; vi += NT) {
+      const u32x4 w = bload128<kPolicyStream>(rin, (uint32_t)vi * 16u, 0u);
+      float f[VE], g[VE];
+      E::unpack(w, f);
+#pragma unroll
+      for (int i = 0; i < VE; ++i) g[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
+      if (vi == tv) {
+#pragma unroll
+        for (int i = 0; i < VE; ++i) g[i] = (i == tj) ? rr.gt : g[i];
+      }
+      bstore128<kPolicyStream>(E::pack(g), rout, (uint32_t)vi * 16u, 0u);
+    }
+    if (xe >= 0) {
+      const float g = (xe == t) ? rr.gt : exp2_hw(__builtin_fmaf(xs, kLog2e, -cg)) * rr.scale;
+      E::store1(gp + xe, g);
+    }
+    if (!more) break;
+    row = next;
   }
 }
 
