@@ -33,7 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "ce_fwd_grad_{workload}_traffic.json")
 CSRC = os.path.join(ROOT, "softmax_cross_entropy_ce_amd", "csrc")
 
 
@@ -54,7 +54,7 @@ def traffic_for(workload: str):
     """Measured HBM bytes per ce_fwd_grad launch, if counters were taken on
     the current kernel source (else None)."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_GLOB.format(workload=workload)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None

@@ -126,6 +126,21 @@ int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, float inv
   return launched();
 }
 
+// Rows that need the largest register configuration run the variant with
+// the next row's prefix prefetched into LDS.
+constexpr int kLdsPrefetchSlots = 9;  // 9 x 16 KB of the 160 KB of LDS
+
+template <typename T>
+int launch_row_lds(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g,
+                   float* l, hipStream_t st) {
+  auto kern = ce::ce_row_lds_kernel<T, 16, kLdsPrefetchSlots>;
+  const int res = resident_blocks(reinterpret_cast<const void*>(kern), 1024);
+  if (res < 1) return CE_ERR_LAUNCH;
+  const int64_t grid = B < res ? B : res;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(1024), 0, st, z, t, B, (int)C, invB, g, l);
+  return launched();
+}
+
 template <typename T>
 int launch_row(RowCfg cfg, const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g,
                float* l, hipStream_t st) {
@@ -167,6 +182,7 @@ int fwd_grad_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C,
       bool ok = false;
       const RowCfg cfg = resident_cfg(C, sizeof(T), &ok);
       if (!ok) return CE_ERR_PATH;
+      if (cfg.nt == 1024 && cfg.nv == 16) return launch_row_lds<T>(z, t, B, C, invB, g, l, st);
       return launch_row<T>(cfg, z, t, B, C, invB, g, l, st);
     }
     case kPathLong: {

@@ -58,9 +58,21 @@ template <int POLICY>
 __device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, POLICY);
 }
+// A store wider than 8 bytes reads its data registers after it issues; a
+// VALU write to those registers in the next two wait states corrupts the
+// stored data.  The compiler inserts those wait states only when soffset is
+// not a register, so every 16-byte store here is followed by them
+// explicitly, with nothing scheduled in between.
+__device__ __forceinline__ void wide_store_guard() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 1");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int POLICY>
 __device__ __forceinline__ void bstore128(u32x4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, POLICY);
+  wide_store_guard();
 }
 
 // ---------------------------------------------------------------------------

@@ -92,6 +92,7 @@ struct VecIO<float, VW> {
     } else {
       __builtin_amdgcn_raw_buffer_store_b128(as_u32(f32x4{g[0], g[1], g[2], g[3]}), r, (int)off,
                                              0, kPolicyStream);
+      wide_store_guard();
     }
   }
 };
@@ -134,6 +135,7 @@ struct VecIO<__bf16, VW> {
       u32x4 v = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
                  pack_bf16x2(g[6], g[7])};
       __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kPolicyStream);
+      wide_store_guard();
     }
   }
 };
@@ -428,6 +430,226 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
     row = next;
   }
 }
+
+// ===========================================================================
+// Path 2 for rows of more than 8192 16-byte vectors (bf16 C > 65528, fp32
+// C > 32764): the row kernel above with the next row's first PF slots
+// (PF*16 KB) prefetched into LDS by direct-to-LDS buffer loads.
+//
+// Loads and stores retire in order on this GPU, so a wait for a load also
+// waits for every store issued before it.  The prefix of row r+1 is issued
+// right after row r's prefix has been copied out of LDS, before any store of
+// row r, so waiting for it never waits for stores; only the NV-PF register
+// slots are still refilled during phase C.  The copy of the prefix into the
+// registers costs one LDS read per element.
+//
+// Every wait below is a fixed vmcnt, so every load and store in the loop is
+// issued unconditionally (buffer-resource bounds make the ones outside the
+// row no-ops), and the first row is preceded by the same number of
+// operations as a steady-state row.  Wave 0 also stores the per-row loss and
+// the edge elements; those are left out of the count, which only makes wave
+// 0 wait slightly longer.
+// ===========================================================================
+template <typename T>
+__device__ __forceinline__ float bload_elem(rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ float bload_elem<float>(rsrc_t r, uint32_t off) {
+  const unsigned d = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kPolicyDefault);
+  return __builtin_bit_cast(float, d);
+}
+template <>
+__device__ __forceinline__ float bload_elem<__bf16>(rsrc_t r, uint32_t off) {
+  const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, kPolicyDefault);
+  return __builtin_bit_cast(float, (unsigned)h << 16);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt vmcnt(N) only (expcnt, lgkmcnt left at their maxima), as asm
+// with a memory clobber so no memory access moves across it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <typename T, int NV, int PF>
+__global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ logits,
+                                                          const int32_t* __restrict__ targets,
+                                                          int64_t B, int C, float invB,
+                                                          T* __restrict__ grad,
+                                                          float* __restrict__ loss_rows) {
+  using E = Elem<T>;
+  constexpr int NT = 1024, NW = 16, VE = E::VE, ES = sizeof(T);
+  static_assert(PF >= 1 && PF < NV, "prefetch slots");
+  // VMEM operations one wave issues after a row's prefix DMA and before the
+  // wait for it: the previous row's phase C (refill load + store per
+  // register slot, store per prefetched slot) and this row's two edge loads.
+  constexpr int kAfterDma = 2 * (NV - PF) + PF + 2;
+  __shared__ u32x4 stage[PF * NT];
+  __shared__ float red_c[2][NW], red_s[2][NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t voff = (uint32_t)tid * 16u;
+  const int64_t G = gridDim.x;
+  int64_t row = blockIdx.x;
+  if (row >= B) return;
+
+  auto body_rsrc = [&](int64_t r, bool exists) {
+    const T* rp = logits + r * C;
+    const RowGeom g = row_geom(rp, C);
+    return make_rsrc(rp + g.h, exists ? (uint32_t)g.nb * 16u : 0u);
+  };
+  auto dma_prefix = [&](rsrc_t rs) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)&stage[p * NT + wv * 64], 16, voff,
+                                               (uint32_t)p * NT * 16u, 0, kPolicyStream);
+  };
+
+  u32x4 v[NV];
+  // prologue: the same VMEM sequence as a steady-state row, so the wait
+  // counts below hold for the first row too
+  {
+    dma_prefix(body_rsrc(row, true));
+    const rsrc_t rin = body_rsrc(row, true);
+    const rsrc_t none = make_rsrc(grad, 0u);
+    // distinct (out-of-range) offsets keep the compiler from merging them
+#pragma unroll
+    for (int k = PF; k < NV; ++k) {
+      v[k] = bload128<kPolicyStream>(rin, voff, (uint32_t)k * NT * 16u);
+      bstore128<kPolicyStream>(u32x4{0, 0, 0, 0}, none, voff, (uint32_t)k * NT * 16u);
+    }
+#pragma unroll
+    for (int k = 0; k < PF; ++k)
+      bstore128<kPolicyStream>(u32x4{0, 0, 0, 0}, none, voff, (uint32_t)k * NT * 16u);
+  }
+
+  for (int parity = 0;; parity ^= 1) {
+    const T* rp = logits + row * C;
+    T* gp = grad + row * C;
+    const RowGeom geo = row_geom(rp, C);
+    const int nb = geo.nb;
+    const rsrc_t rout = make_rsrc(gp + geo.h, (uint32_t)nb * 16u);
+    const rsrc_t rrow = make_rsrc(rp, (uint32_t)C * ES);
+
+    const int32_t t = targets[row];
+    const bool valid = t >= 0 && t < C;
+    const int tb = t - geo.h;
+    const bool t_in_body = valid && tb >= 0 && tb < nb * VE;
+    const int tv = t_in_body ? tb / VE : -1;
+    const int tj = t_in_body ? tb % VE : -1;
+    const int own_k = (t_in_body && tv < NT * NV) ? tv / NT : -1;
+    const bool own_thread = t_in_body && (tv % NT) == tid;
+
+    int xe = -1;
+    if (tid < geo.h)
+      xe = tid;
+    else if (tid - geo.h < geo.ntail)
+      xe = geo.tail0 + (tid - geo.h);
+    // step 1: edge loads, unconditional (an absent element reads past the row: 0)
+    const float xs_raw = bload_elem<T>(rrow, (uint32_t)(xe >= 0 ? xe : C) * ES);
+    const float zt_raw = bload_elem<T>(rrow, (uint32_t)(valid ? t : C) * ES);
+
+    // step 2: this row's prefix is in LDS once everything issued before the
+    // DMA has completed
+    wait_vmcnt<kAfterDma>();
+    // step 3: prefix slots LDS -> registers
+#pragma unroll
+    for (int p = 0; p < PF; ++p) v[p] = stage[p * NT + tid];
+    wait_lgkm0();
+    // step 4: prefetch the next row's prefix (issued before this row's stores)
+    const int64_t next = row + G;
+    const bool more = next < B;
+    const int64_t nrow = more ? next : row;
+    const rsrc_t rinn = body_rsrc(nrow, more);
+    dma_prefix(rinn);
+
+    const float xs = xe >= 0 ? xs_raw : kNegInf;
+    const float zt = valid ? zt_raw : 0.f;
+
+    // step 5: phase B
+    float c = kLowest, s = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int base = k * NT;
+      if (base >= nb) continue;
+      float f[VE];
+      E::unpack(v[k], f);
+      if (base + NT > nb) {
+        const bool ok = tid < nb - base;
+#pragma unroll
+        for (int i = 0; i < VE; ++i) f[i] = ok ? f[i] : kNegInf;
+      }
+      const float vm = max_of(f);
+      if (k == own_k && own_thread) {
+#pragma unroll
+        for (int i = 0; i < VE; ++i) f[i] = (i == tj) ? kNegInf : f[i];
+      }
+      online_fold(c, s, vm, f);
+    }
+    if (xe >= 0) {
+      const float one[1] = {(xe == t) ? kNegInf : xs};
+      online_fold(c, s, xs, one);
+    }
+
+    // step 6: combine
+    const float cw = wave_allreduce(c, OpMax{});
+    const float sw = wave_allreduce(s * exp2_hw(c - cw), OpAdd{});
+    if (lane == 0) {
+      red_c[parity][wv] = cw;
+      red_s[parity][wv] = sw;
+    }
+    // LDS-only barrier: the exchange goes through LDS, so only LDS traffic
+    // has to complete first (a full __syncthreads would also wait for the
+    // next row's prefetch)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const float ci = lane < NW ? red_c[parity][lane] : kLowest;
+    const float si = lane < NW ? red_s[parity][lane] : 0.f;
+    const float cg = wave_uniform(seg_allreduce<16>(ci, OpMax{}));
+    const float sx = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
+    const RowResult rr = row_epilogue(cg, sx, zt, valid, invB);
+
+    // step 7: phase C; register-only slots first (each refilled with the
+    // next row), then the prefetched slots
+#pragma unroll
+    for (int k = 0; k < NV; ++k) asm volatile("" : "+v"(v[k]));
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int k = (j + PF) % NV;
+      float f[VE], g[VE];
+      E::unpack(v[k], f);
+#pragma unroll
+      for (int i = 0; i < VE; ++i) g[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
+      if (k == own_k && own_thread) {
+#pragma unroll
+        for (int i = 0; i < VE; ++i) g[i] = (i == tj) ? rr.gt : g[i];
+      }
+      const u32x4 packed = E::pack(g);
+      if (k >= PF) v[k] = bload128<kPolicyStream>(rinn, voff, (uint32_t)k * NT * 16u);
+      // the scheduling barrier sits before the store: placed right after a
+      // store wider than 8 bytes it hides the store from the compiler's
+      // hazard check, and a following write to the store's data registers
+      // then lands without the wait states the hardware needs
+      __builtin_amdgcn_sched_barrier(0);
+      bstore128<kPolicyStream>(packed, rout, voff, (uint32_t)k * NT * 16u);
+    }
+    if (tid == 0) loss_rows[row] = rr.loss;
+    if (xe >= 0) {
+      const float g = (xe == t) ? rr.gt : exp2_hw(__builtin_fmaf(xs, kLog2e, -cg)) * rr.scale;
+      E::store1(gp + xe, g);
+    }
+    if (!more) {
+      // no LDS write may still be in flight when the workgroup's LDS is
+      // handed to the next workgroup
+      wait_vmcnt<0>();
+      break;
+    }
+    row = next;
+  }
+}
+
 
 // ===========================================================================
 // Loss reduction: a fixed two-level tree.  Workgroup g of the first level

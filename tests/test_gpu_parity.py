@@ -51,6 +51,14 @@ SMALL = [
     (17, 12345, "bf16", 4.0),
     (9, 50257, "f32", 3.0),
     (6, 128256, "bf16", 4.0),
+    # rows on the LDS-prefetch kernel: partial prefetched slot with 2-byte
+    # aligned rows, partial register slot, the largest resident rows, one
+    # row, and more rows than the persistent grid holds
+    (300, 70001, "bf16", 4.0),
+    (257, 40000, "f32", 3.0),
+    (3, 65531, "f32", 3.0),
+    (5, 131064, "bf16", 4.0),
+    (1, 128256, "bf16", 4.0),
 ]
 
 

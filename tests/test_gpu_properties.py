@@ -21,7 +21,8 @@ CASES = [
     (16, 10, "f32", 20.0),      # short path
     (64, 1000, "f32", 2.0),     # resident, one wave
     (8, 50257, "f32", 3.0),     # resident, 1024 threads, misaligned rows
-    (4, 128256, "bf16", 4.0),   # resident, 1024 threads
+    (4, 128256, "bf16", 4.0),   # resident, 1024 threads, LDS prefetch
+    (300, 70001, "bf16", 4.0),  # LDS prefetch, several rows per workgroup
     (3, 200_000, "bf16", 4.0),  # long rows: streamed part
     (2, 100_003, "f32", 3.0),   # long rows, misaligned
 ]
