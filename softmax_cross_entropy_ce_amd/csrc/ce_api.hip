@@ -82,22 +82,30 @@ int short_vw(int64_t C, int es, uintptr_t zaddr, uintptr_t gaddr, int epl) {
   return 1;
 }
 
+// Short-row layout: about 16 bytes per lane.  S lanes per row is the power
+// of two that covers the row with EPL elements per lane (EPL = 16 bytes of
+// elements, more only at S = 16).  Lanes of a row read adjacent vectors,
+// so a load instruction covers 64/S consecutive rows.
 template <typename T>
 int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g, float* l,
                  hipStream_t st) {
   if (C > kShortMaxC) return CE_ERR_PATH;
-  const int es = sizeof(T);
+  constexpr int es = sizeof(T);
+  constexpr int E16 = 16 / es;  // elements in 16 bytes
   const int c = (int)C;
-  auto vw = [&](int epl) {
-    return short_vw(C, es, (uintptr_t)z, (uintptr_t)g, epl);
-  };
-  if (C <= 4) return launch_short_vw<T, 1, 4>(vw(4), z, t, B, c, invB, g, l, st);
-  if (C <= 8) return launch_short_vw<T, 1, 8>(vw(8), z, t, B, c, invB, g, l, st);
-  if (C <= 16) return launch_short_vw<T, 1, 16>(vw(16), z, t, B, c, invB, g, l, st);
-  if (C <= 32) return launch_short_vw<T, 2, 16>(vw(16), z, t, B, c, invB, g, l, st);
-  if (C <= 64) return launch_short_vw<T, 4, 16>(vw(16), z, t, B, c, invB, g, l, st);
-  if (C <= 128) return launch_short_vw<T, 8, 16>(vw(16), z, t, B, c, invB, g, l, st);
-  return launch_short_vw<T, 16, 16>(vw(16), z, t, B, c, invB, g, l, st);
+  auto vw = [&](int epl) { return short_vw(C, es, (uintptr_t)z, (uintptr_t)g, epl); };
+  if (C <= E16) return launch_short_vw<T, 1, E16>(vw(E16), z, t, B, c, invB, g, l, st);
+  if (C <= 2 * E16) return launch_short_vw<T, 2, E16>(vw(E16), z, t, B, c, invB, g, l, st);
+  if (C <= 4 * E16) return launch_short_vw<T, 4, E16>(vw(E16), z, t, B, c, invB, g, l, st);
+  if (C <= 8 * E16) return launch_short_vw<T, 8, E16>(vw(E16), z, t, B, c, invB, g, l, st);
+  if (C <= 16 * E16) return launch_short_vw<T, 16, E16>(vw(E16), z, t, B, c, invB, g, l, st);
+  if constexpr (E16 < 16) {
+    if (C <= 32 * E16) return launch_short_vw<T, 16, 2 * E16>(vw(2 * E16), z, t, B, c, invB, g, l, st);
+  }
+  if constexpr (E16 < 8) {
+    if (C <= 64 * E16) return launch_short_vw<T, 16, 4 * E16>(vw(4 * E16), z, t, B, c, invB, g, l, st);
+  }
+  return CE_ERR_PATH;
 }
 
 // -------------------------------------------------------------- paths 2, 3

@@ -203,17 +203,24 @@ __device__ __forceinline__ float wave_uniform(float v) {
 // removed from the loss by working with c directly.  When c grows, s is
 // rescaled by 2^(c_old - c_new).
 // ---------------------------------------------------------------------------
+// Pairwise sum of N values in a fixed order: element i is added to element
+// i + ceil(W/2) while W > 1 (an odd middle element waits one level).
+template <int W, int N>
+__device__ __forceinline__ void tree_level(float (&t)[N]) {
+  if constexpr (W > 1) {
+    constexpr int H = (W + 1) / 2;
+#pragma unroll
+    for (int i = 0; i < W / 2; ++i) t[i] = t[i] + t[i + H];
+    tree_level<H, N>(t);
+  }
+}
+
 template <int N>
 __device__ __forceinline__ float tree_sum(const float (&a)[N]) {
-  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "tree size");
   float t[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) t[i] = a[i];
-#pragma unroll
-  for (int w = N / 2; w >= 1; w /= 2) {
-#pragma unroll
-    for (int i = 0; i < w; ++i) t[i] = t[i] + t[i + w];
-  }
+  tree_level<N, N>(t);
   return t[0];
 }
 

@@ -184,7 +184,12 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
 #pragma unroll
     for (int w = 0; w < VW; ++w) f[j * VW + w] = v[w];
   }
-  const float zt = valid ? Elem<T>::load1(logits + row * C + t) : 0.f;
+  // the target logit, from the owner lane's registers: a segment sum of the
+  // owner's value and zeros is exact
+  float own_zt = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) own_zt = (owner && i == tslot) ? f[i] : own_zt;
+  const float zt = seg_allreduce<S>(own_zt, OpAdd{});
 
   // row max across the segment, then the sum with the target left out
   const float m = seg_allreduce<S>(max_of(f), OpMax{});
