@@ -18,7 +18,7 @@
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers owned by the caller.  The
  *    library allocates nothing and keeps no mutable state (apart from the
- *    test-only path override below).
+ *    test-only hooks at the end).
  *  - Calls are asynchronous and ordered on `stream` (a hipStream_t passed as
  *    void*; NULL means the default stream).  No call synchronises the
  *    device or copies data to the host.
@@ -74,6 +74,9 @@ typedef enum {
  *   B, C      1 <= B <= 2^31 - 1, 1 <= C <= CE_MAX_C.
  *   dtype     CE_F32 or CE_BF16.
  *   grad_out  [B, C] dtype, fully overwritten with (softmax - onehot) / B.
+ *             Contents on entry are ignored; on path 4 with two parts per
+ *             row the call also uses 16 bytes of each part's own gradient
+ *             as a mailbox before the gradient is written there.
  *             Must not overlap logits, must be aligned to the element size,
  *             and (grad_out - logits) must be a multiple of 16 bytes
  *             (true for any two allocations from the HIP or torch
@@ -129,7 +132,17 @@ const char* ce_version(void);
  *                   so it is read from HBM once and written once;
  *   3 long rows   - as 2, with the part of the row beyond the on-chip
  *                   capacity streamed with online max/sum-exp partials and
- *                   re-read for the gradient.
+ *                   re-read for the gradient;
+ *   4 row parts   - the row cut into one or two parts of up to 12 x 16 KB,
+ *                   one 1024-thread workgroup each and two per CU; each part
+ *                   is read once into registers and LDS and reduced to an
+ *                   online max/sum-exp pair, the parts trade their pairs
+ *                   and combine them in a fixed order, and each writes its
+ *                   share of the gradient from on chip.  A part that does
+ *                   not receive its partner's pair in time recomputes it
+ *                   with the same code, so the bits do not depend on timing.
+ *                   Rows of 16 KB to 384 KB (bf16 C up to 196608, fp32 C up
+ *                   to 98304).
  *
  * ce_select_path returns the path ce_fwd_grad takes for (C, dtype) with
  * 16-byte aligned base pointers, or a negative ce_status.
@@ -138,12 +151,30 @@ int ce_select_path(int64_t C, int dtype);
 
 /*
  * Test hook: force every later ce_fwd_grad onto one path (0 = automatic,
- * 1, 2 or 3 as above; path 3 is then run with a small on-chip part so that
+ * 1 to 4 as above; path 3 is then run with a small on-chip part so that
  * the streamed part is exercised).  A shape the forced path cannot take
  * returns CE_ERR_PATH.  Returns the previous setting, or CE_ERR_PATH for an
  * unknown value.  Process-wide; not meant for production use.
  */
 int ce_debug_force_path(int path);
+
+/*
+ * Test hook: how many times a path-4 row part polls for its partner's
+ * max/sum-exp pair before it recomputes the pair itself (default 64; 0 makes
+ * every part of a two-part row recompute).  Results are bitwise the same
+ * for any value.  Returns the previous value, or CE_ERR_PATH if polls < 0.
+ * Process-wide; not meant for production use.
+ */
+int ce_debug_part_polls(int polls);
+
+/*
+ * Test hook: a DEVICE pointer to a uint32 that every path-4 part which
+ * recomputes its partner's pair increments atomically (NULL turns the count
+ * off, the default).  The caller owns the counter and must keep it alive
+ * while calls that were made with it set can still run.  Returns CE_OK.
+ * Process-wide; not meant for production use.
+ */
+int ce_debug_part_counter(uint32_t* device_counter);
 
 #ifdef __cplusplus
 }

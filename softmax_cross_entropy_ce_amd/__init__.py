@@ -23,13 +23,13 @@ import os
 
 __all__ = [
     "CEError", "lib", "fwd_grad", "fwd_grad_into", "reduce_loss", "reduce_loss_into",
-    "cross_entropy", "reduce_workspace_bytes", "select_path", "force_path", "version",
-    "PATH_NAMES", "F32", "BF16",
+    "cross_entropy", "reduce_workspace_bytes", "select_path", "force_path", "part_polls",
+    "part_counter", "version", "PATH_NAMES", "F32", "BF16",
 ]
 
 F32 = 0
 BF16 = 1
-PATH_NAMES = {1: "short", 2: "resident", 3: "long"}
+PATH_NAMES = {1: "short", 2: "resident", 3: "long", 4: "parts"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libce_mi355x.so")
@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
     L.ce_select_path.restype = i32
     L.ce_debug_force_path.argtypes = [i32]
     L.ce_debug_force_path.restype = i32
+    L.ce_debug_part_polls.argtypes = [i32]
+    L.ce_debug_part_polls.restype = i32
+    L.ce_debug_part_counter.argtypes = [vp]
+    L.ce_debug_part_counter.restype = i32
     _lib = L
     return L
 
@@ -100,6 +104,29 @@ def force_path(path: int) -> int:
     if r < 0:
         raise CEError(r, "ce_debug_force_path")
     return r
+
+
+def part_polls(polls: int) -> int:
+    """Test hook: polls of a path-4 row part for its partner's pair before it
+    recomputes the pair (0: always recompute).  Returns the previous value."""
+    r = lib().ce_debug_part_polls(int(polls))
+    if r < 0:
+        raise CEError(r, "ce_debug_part_polls")
+    return r
+
+
+def part_counter(counter=None) -> None:
+    """Test hook: a one-element int32/uint32 device tensor that counts path-4
+    parts which recomputed their partner's pair (None turns counting off).
+    The tensor must stay alive until the calls made with it have run."""
+    if counter is None:
+        ptr = None
+    else:
+        _check_cuda(counter)
+        if counter.numel() < 1 or counter.element_size() != 4 or not counter.is_contiguous():
+            raise ValueError("counter must be a contiguous 4-byte integer tensor")
+        ptr = counter.data_ptr()
+    _check(lib().ce_debug_part_counter(ptr), "ce_debug_part_counter")
 
 
 def reduce_workspace_bytes(B: int) -> int:

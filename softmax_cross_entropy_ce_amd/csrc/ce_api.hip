@@ -6,7 +6,7 @@
 #include <stdint.h>
 
 #include "ce.h"
-#include "ce_kernels.h"
+#include "ce_parts.h"
 
 namespace {
 
@@ -15,6 +15,14 @@ std::atomic<int> g_force_path{0};
 constexpr int kPathShort = 1;
 constexpr int kPathResident = 2;
 constexpr int kPathLong = 3;
+constexpr int kPathParts = 4;
+
+// Polls of a row part for its partner's pair before it recomputes the pair
+// itself, and the optional device counter of such recomputations (test
+// hooks; see ce_debug_part_polls / ce_debug_part_counter).
+constexpr int kPartPollsDefault = 64;
+std::atomic<int> g_part_polls{kPartPollsDefault};
+std::atomic<uint32_t*> g_part_counter{nullptr};
 
 // Per-row configurations of paths 2 and 3: NT threads, NV 16-byte vectors
 // per thread, so NT*NV*16 bytes of the row stay in registers.  Ordered by
@@ -28,16 +36,30 @@ constexpr RowCfg kLongCfg = {1024, 16};     // automatic path 3
 constexpr RowCfg kLongTestCfg = {256, 1};   // forced path 3: small on-chip part
 
 constexpr int kShortMaxC = 256;
+// Automatic path 2 takes rows of up to this many 16-byte vectors (the
+// configurations up to 256 threads x 4); longer rows go to path 4 while
+// their aligned body fits its largest configuration, then to path 3.
+constexpr int64_t kResidentAutoMaxVectors = 1024;
 
 int elem_size(int dtype) { return dtype == CE_F32 ? 4 : 2; }
 
 // 16-byte vectors a row may touch: the aligned body plus a head and a tail.
 int64_t row_vectors(int64_t C, int es) { return (C * es + 15) / 16 + 1; }
 
+// Path 4 configurations by the largest aligned body a row can have,
+// floor(C / elements per vector): one part of 4 register slots, one part of
+// 8 register and 2 LDS slots, two parts of 8 register and 4 LDS slots each
+// (a slot is 1024 vectors).
+constexpr int64_t kPartsOneSmall = 4 * 1024;
+constexpr int64_t kPartsOne = 10 * 1024;
+constexpr int64_t kPartsTwo = 2 * 12 * 1024;
+
+int64_t body_vectors_max(int64_t C, int es) { return C / (16 / es); }
+
 int auto_path(int64_t C, int es) {
   if (C <= kShortMaxC) return kPathShort;
-  const RowCfg& big = kRowCfgs[sizeof(kRowCfgs) / sizeof(kRowCfgs[0]) - 1];
-  if (row_vectors(C, es) <= (int64_t)big.nt * big.nv) return kPathResident;
+  if (row_vectors(C, es) <= kResidentAutoMaxVectors) return kPathResident;
+  if (body_vectors_max(C, es) <= kPartsTwo) return kPathParts;
   return kPathLong;
 }
 
@@ -179,6 +201,35 @@ RowCfg resident_cfg(int64_t C, int es, bool* ok) {
   return kLongCfg;
 }
 
+// ---------------------------------------------------------------- path 4
+template <typename T, int P, int NR, int NL>
+int launch_parts_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g,
+                     float* l, hipStream_t st) {
+  const int64_t blocks = P * ((B + 7) / 8 * 8);
+  if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
+  if constexpr (P > 1) {
+    const int64_t cb = (B * P + 255) / 256;
+    hipLaunchKernelGGL(ce::ce_mailbox_clear_kernel<T>, dim3((unsigned)cb), dim3(256), 0, st, g, B,
+                       (int)C, P);
+    if (launched() != CE_OK) return CE_ERR_LAUNCH;
+  }
+  hipLaunchKernelGGL((ce::ce_part_kernel<T, P, NR, NL>), dim3((unsigned)blocks),
+                     dim3(ce::kPartThreads), 0, st, z, t, B, (int)C, invB, g, l,
+                     g_part_polls.load(std::memory_order_relaxed),
+                     g_part_counter.load(std::memory_order_relaxed));
+  return launched();
+}
+
+template <typename T>
+int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g, float* l,
+                 hipStream_t st) {
+  const int64_t nb = body_vectors_max(C, sizeof(T));
+  if (nb <= kPartsOneSmall) return launch_parts_cfg<T, 1, 4, 0>(z, t, B, C, invB, g, l, st);
+  if (nb <= kPartsOne) return launch_parts_cfg<T, 1, 8, 2>(z, t, B, C, invB, g, l, st);
+  if (nb <= kPartsTwo) return launch_parts_cfg<T, 2, 8, 4>(z, t, B, C, invB, g, l, st);
+  return CE_ERR_PATH;
+}
+
 template <typename T>
 int fwd_grad_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g, float* l,
                    hipStream_t st) {
@@ -197,6 +248,8 @@ int fwd_grad_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C,
       const bool forced = g_force_path.load(std::memory_order_relaxed) == kPathLong;
       return launch_row<T>(forced ? kLongTestCfg : kLongCfg, z, t, B, C, invB, g, l, st);
     }
+    case kPathParts:
+      return launch_parts<T>(z, t, B, C, invB, g, l, st);
     default:
       return CE_ERR_PATH;
   }
@@ -301,8 +354,18 @@ int ce_select_path(int64_t C, int dtype) {
 }
 
 int ce_debug_force_path(int path) {
-  if (path < 0 || path > 3) return CE_ERR_PATH;
+  if (path < 0 || path > 4) return CE_ERR_PATH;
   return g_force_path.exchange(path);
+}
+
+int ce_debug_part_polls(int polls) {
+  if (polls < 0) return CE_ERR_PATH;
+  return g_part_polls.exchange(polls);
+}
+
+int ce_debug_part_counter(uint32_t* device_counter) {
+  g_part_counter.store(device_counter);
+  return CE_OK;
 }
 
 }  // extern "C"

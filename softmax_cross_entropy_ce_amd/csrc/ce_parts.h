@@ -1,0 +1,301 @@
+// Path 4: rows cut into parts, one 1024-thread workgroup per part and two
+// workgroups per CU.
+//
+// The method's per-row steps (rumus 0.1.1 cross_entropy.wgsl, pass 1 steps
+// 1-4 and pass 2) need the row's max and sum of exponentials before any
+// gradient element can be written.  With one workgroup per row, a row of
+// 128256 bf16 values (256 KB) fills a CU's registers and LDS, so only one
+// row is in flight per CU.  Here a row of nb 16-byte vectors is cut into P
+// parts of at most NT*(NR+NL) vectors.  Each part is read once into
+// registers (NR slots) and LDS (NL slots), reduced to its own online
+// (c, s) pair, and the parts then trade their pairs, so that every part
+// combines the same P pairs in the same order (part 0 first) and writes
+// its share of the gradient from on-chip data.  The combine is the
+// online-softmax merge of (max, sum) partials.
+//
+// Trading pairs between workgroups.  Each part has a mailbox: two 64-bit
+// words at the start of its own last body vector in grad.  Its partner
+// publishes (c, s) there, one value per word in the low half with kMailTag
+// in the high half; the owner polls it, and its own gradient store
+// overwrites it only after the poll has ended.  Before the parts run,
+// ce_mailbox_clear_kernel sets every mailbox word to kMailEmpty.  The
+// partner publishes with compare-and-swap from kMailEmpty, so a publish
+// that arrives after the owner has given up and written its gradient
+// changes nothing.  Both tags are signalling NaNs, both as one float32 and
+// as two bf16 values.  No arithmetic result is a signalling NaN, so no
+// gradient value can look like a mailbox word, and a word with kMailTag was
+// written by the partner in this launch.  The owner polls a bounded number
+// of times.  If the pair has not come by then (the partner is not resident
+// yet), it recomputes the pair from the logits with the same code, slots
+// and order that the partner uses, so the result is bitwise the same
+// whichever way the pair arrived.  No wait is unbounded and no result
+// depends on timing.
+//
+// Workgroup g runs on XCD g % 8 (round-robin dispatch); the parts of a row
+// are given workgroups g, g + 8, ..., so they share an XCD and start next to
+// each other in its dispatch order.
+#pragma once
+
+#include "ce_kernels.h"
+
+namespace ce {
+
+constexpr uint32_t kMailTag = 0x7FA57FA5u;
+constexpr uint32_t kMailEmpty = 0x7FA17FA1u;
+constexpr int kPartThreads = 1024;
+
+// Body-vector range [v0, v0 + len) of part q when nb vectors are cut into P
+// parts of ceil(nb / P).
+struct PartRange {
+  int v0, len;
+};
+__device__ __forceinline__ PartRange part_range(int nb, int P, int q) {
+  const int L = (nb + P - 1) / P;
+  const int a = q * L < nb ? q * L : nb;
+  const int b = a + L < nb ? a + L : nb;
+  return PartRange{a, b - a};
+}
+
+// Workgroup index -> (row, part): parts of one row on one XCD, consecutive
+// in its dispatch order.
+template <int P>
+__device__ __forceinline__ void part_of_block(uint32_t g, int64_t& row, int& part) {
+  const uint32_t xcd = g & 7u, local = g >> 3;
+  row = (int64_t)(local / P) * 8 + xcd;
+  part = (int)(local % P);
+}
+
+// Empty the mailbox of every part of every row (P > 1): both words become
+// kMailEmpty in the high half and zero in the low half.  One thread per
+// (row, part); a 16-byte store into the part's last body vector of grad.
+template <typename T>
+__global__ __launch_bounds__(256) void ce_mailbox_clear_kernel(T* __restrict__ grad, int64_t B,
+                                                               int C, int P) {
+  constexpr int VE = Elem<T>::VE;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= B * P) return;
+  const int64_t row = i / P;
+  const int q = (int)(i % P);
+  T* gp = grad + row * C;
+  const RowGeom geo = row_geom(gp, C);
+  const PartRange pr = part_range(geo.nb, P, q);
+  if (pr.len <= 0) return;
+  u32x4* mb = reinterpret_cast<u32x4*>(gp + geo.h + (int64_t)(pr.v0 + pr.len - 1) * VE);
+  *mb = u32x4{0u, kMailEmpty, 0u, kMailEmpty};
+}
+
+// Max / sum pair of the whole workgroup, from each thread's (c, s).  Every
+// thread gets the same result; the order of operations is fixed.  Contains
+// one barrier; the caller separates two uses by another.
+template <int NW>
+__device__ __forceinline__ void wg_pair(float c, float s, float* red_c, float* red_s, int lane,
+                                        int wv, float& cg, float& sg) {
+  const float cw = wave_allreduce(c, OpMax{});
+  const float sw = wave_allreduce(s * exp2_hw(c - cw), OpAdd{});
+  if (lane == 0) {
+    red_c[wv] = cw;
+    red_s[wv] = sw;
+  }
+  __syncthreads();
+  const float ci = lane < NW ? red_c[lane] : kLowest;
+  const float si = lane < NW ? red_s[lane] : 0.f;
+  cg = wave_uniform(seg_allreduce<16>(ci, OpMax{}));
+  sg = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
+}
+
+// fallbacks (may be null): a device counter, incremented once by every part
+// that recomputed its partner's pair instead of receiving it.  spin: polls
+// before that happens (0: every part recomputes).
+template <typename T, int P, int NR, int NL>
+__global__ __launch_bounds__(kPartThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B,
+                    int C, float invB, T* __restrict__ grad, float* __restrict__ loss_rows,
+                    int spin, uint32_t* __restrict__ fallbacks) {
+  using E = Elem<T>;
+  constexpr int NT = kPartThreads, NW = NT / 64, VE = E::VE, ES = sizeof(T);
+  constexpr int NS = NR + NL;  // slots per part
+  static_assert(P == 1 || P == 2, "one or two parts per row");
+  __shared__ u32x4 stage[NL > 0 ? NL * NT : 1];
+  __shared__ float red_c[NW], red_s[NW];
+  __shared__ float mail_c, mail_s;
+  __shared__ int mail_ok;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t voff = (uint32_t)tid * 16u;
+  int64_t row;
+  int part;
+  part_of_block<P>(blockIdx.x, row, part);
+  if (row >= B) return;  // whole workgroup (and every part of the row)
+
+  const T* rp = logits + row * C;
+  T* gp = grad + row * C;
+  const RowGeom geo = row_geom(rp, C);
+  const PartRange own = part_range(geo.nb, P, part);
+  const rsrc_t rrow = make_rsrc(rp, (uint32_t)C * ES);
+  const rsrc_t rin = make_rsrc(rp + geo.h + own.v0 * VE, (uint32_t)own.len * 16u);
+  const rsrc_t rout = make_rsrc(gp + geo.h + own.v0 * VE, (uint32_t)own.len * 16u);
+
+  // Phase A: every load of this part, register slots first.
+  u32x4 v[NR];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) v[k] = bload128<kPolicyStream>(rin, voff, (uint32_t)k * NT * 16u);
+#pragma unroll
+  for (int p = 0; p < NL; ++p)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rin, (lds_ptr_t)&stage[p * NT + wv * 64], 16, voff,
+                                             (uint32_t)(NR + p) * NT * 16u, 0, kPolicyStream);
+
+  const int32_t t = targets[row];
+  const bool valid = t >= 0 && t < C;
+  const int tb = valid ? t - geo.h : -1;
+  const bool t_body = tb >= 0 && tb < geo.nb * VE;
+  const int tvec = t_body ? tb / VE : -1;  // target's body vector (row-relative)
+  const int tj = t_body ? tb % VE : -1;
+
+  // Edge elements of part q: the head (before the first 16-byte boundary)
+  // belongs to part 0 and the tail to part P-1; edge i goes to thread i.
+  auto edge_elem = [&](int q) -> int {
+    const int nh = q == 0 ? geo.h : 0;
+    const int nt = q == P - 1 ? geo.ntail : 0;
+    if (tid < nh) return tid;
+    if (tid - nh < nt) return geo.tail0 + (tid - nh);
+    return -1;
+  };
+  const int xe = edge_elem(part);
+  const float xs_raw = bload_elem<T>(rrow, (uint32_t)(xe >= 0 ? xe : C) * ES);
+  const float zt_raw = bload_elem<T>(rrow, (uint32_t)(valid ? t : C) * ES);
+
+  // Fold slot k of part q (this thread's vector k*NT + tid of the part).
+  // Slots past the part's end are skipped as a whole (uniform); lanes past
+  // it hold -inf.  The target element is left out of the sum.
+  auto fold_slot = [&](const PartRange& pr, int k, u32x4 w, float& c, float& s) {
+    const int base = k * NT;
+    if (base >= pr.len) return;
+    float f[VE];
+    E::unpack(w, f);
+    if (base + NT > pr.len) {
+      const bool ok = tid < pr.len - base;
+#pragma unroll
+      for (int i = 0; i < VE; ++i) f[i] = ok ? f[i] : kNegInf;
+    }
+    const float vm = max_of(f);
+    if (pr.v0 + base + tid == tvec) {
+#pragma unroll
+      for (int i = 0; i < VE; ++i) f[i] = (i == tj) ? kNegInf : f[i];
+    }
+    online_fold(c, s, vm, f);
+  };
+  auto fold_edge = [&](int e, float x, float& c, float& s) {
+    if (e >= 0) {
+      const float one[1] = {(e == t) ? kNegInf : x};
+      online_fold(c, s, x, one);
+    }
+  };
+
+  // Phase B: this part's pair.
+  float c = kLowest, s = 0.f;
+#pragma unroll
+  for (int k = 0; k < NR; ++k) fold_slot(own, k, v[k], c, s);
+  wait_vmcnt<0>();  // LDS slots, edge and target loads
+#pragma unroll
+  for (int p = 0; p < NL; ++p) fold_slot(own, NR + p, stage[p * NT + tid], c, s);
+  const float xs = xe >= 0 ? xs_raw : kNegInf;
+  const float zt = valid ? zt_raw : 0.f;
+  fold_edge(xe, xs, c, s);
+  float c_own, s_own;
+  wg_pair<NW>(c, s, red_c, red_s, lane, wv, c_own, s_own);
+
+  float c_oth = kLowest, s_oth = 0.f;
+  if constexpr (P == 2) {
+    const int q = 1 - part;
+    if (tid == 0) {
+      const PartRange pq = part_range(geo.nb, P, q);
+      uint64_t* mine = reinterpret_cast<uint64_t*>(gp + geo.h + (int64_t)(own.v0 + own.len - 1) * VE);
+      uint64_t* theirs = reinterpret_cast<uint64_t*>(gp + geo.h + (int64_t)(pq.v0 + pq.len - 1) * VE);
+      const uint64_t tag = (uint64_t)kMailTag << 32;
+      uint64_t e0 = (uint64_t)kMailEmpty << 32, e1 = e0;
+      if (__hip_atomic_compare_exchange_strong(&theirs[0], &e0, tag | __builtin_bit_cast(uint32_t, c_own),
+                                               __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        __hip_atomic_compare_exchange_strong(&theirs[1], &e1, tag | __builtin_bit_cast(uint32_t, s_own),
+                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      int ok = 0;
+      uint64_t a = 0, b = 0;
+      for (int it = 0; it < spin; ++it) {
+        a = __hip_atomic_load(&mine[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        b = __hip_atomic_load(&mine[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(a >> 32) == kMailTag && (uint32_t)(b >> 32) == kMailTag) {
+          ok = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+      mail_c = __builtin_bit_cast(float, (uint32_t)a);
+      mail_s = __builtin_bit_cast(float, (uint32_t)b);
+      mail_ok = ok;
+      if (!ok && fallbacks != nullptr) atomicAdd(fallbacks, 1u);
+    }
+    __syncthreads();
+    if (mail_ok) {
+      c_oth = mail_c;
+      s_oth = mail_s;
+    } else {
+      // Recompute part q's pair: the same slots, fold order, edges and
+      // workgroup reduction as part q runs itself.
+      const PartRange pq = part_range(geo.nb, P, q);
+      const rsrc_t rq = make_rsrc(rp + geo.h + pq.v0 * VE, (uint32_t)pq.len * 16u);
+      float cq = kLowest, sq = 0.f;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const u32x4 w = bload128<kPolicyStream>(rq, voff, (uint32_t)k * NT * 16u);
+        fold_slot(pq, k, w, cq, sq);
+      }
+      const int xq = edge_elem(q);
+      const float xqv = bload_elem<T>(rrow, (uint32_t)(xq >= 0 ? xq : C) * ES);
+      fold_edge(xq, xq >= 0 ? xqv : kNegInf, cq, sq);
+      wg_pair<NW>(cq, sq, red_c, red_s, lane, wv, c_oth, s_oth);
+    }
+  }
+
+  // Combine the parts' pairs in part order.
+  float cg, sx;
+  if constexpr (P == 1) {
+    cg = c_own;
+    sx = s_own;
+  } else {
+    const float c0 = part == 0 ? c_own : c_oth, s0 = part == 0 ? s_own : s_oth;
+    const float c1 = part == 0 ? c_oth : c_own, s1 = part == 0 ? s_oth : s_own;
+    cg = __builtin_fmaxf(c0, c1);
+    sx = s0 * exp2_hw(c0 - cg);
+    sx = sx + s1 * exp2_hw(c1 - cg);
+  }
+  const RowResult rr = row_epilogue(cg, sx, zt, valid, invB);
+  if (part == 0 && tid == 0) loss_rows[row] = rr.loss;
+
+  // Phase C: the gradient of this part from registers and LDS.
+  auto write_slot = [&](int k, u32x4 w) {
+    const int base = k * NT;
+    if (base >= own.len) return;
+    float f[VE], g[VE];
+    E::unpack(w, f);
+#pragma unroll
+    for (int i = 0; i < VE; ++i) g[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
+    if (own.v0 + base + tid == tvec) {
+#pragma unroll
+      for (int i = 0; i < VE; ++i) g[i] = (i == tj) ? rr.gt : g[i];
+    }
+    bstore128<kPolicyStream>(E::pack(g), rout, voff, (uint32_t)k * NT * 16u);
+  };
+#pragma unroll
+  for (int k = 0; k < NR; ++k) asm volatile("" : "+v"(v[k]));
+#pragma unroll
+  for (int k = 0; k < NR; ++k) write_slot(k, v[k]);
+#pragma unroll
+  for (int p = 0; p < NL; ++p) write_slot(NR + p, stage[p * NT + tid]);
+  if (xe >= 0) {
+    const float g = (xe == t) ? rr.gt : exp2_hw(__builtin_fmaf(xs, kLog2e, -cg)) * rr.scale;
+    E::store1(gp + xe, g);
+  }
+}
+
+}  // namespace ce

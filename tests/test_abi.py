@@ -36,7 +36,8 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert names == sorted(["ce_fwd_grad", "ce_reduce_workspace_bytes", "ce_reduce_loss",
                             "ce_status_string", "ce_version", "ce_select_path",
-                            "ce_debug_force_path"])
+                            "ce_debug_force_path", "ce_debug_part_polls",
+                            "ce_debug_part_counter"])
     for n in names:
         assert hasattr(L_, n), n
 
@@ -115,12 +116,22 @@ def test_reduce_loss_validation():
     ("tiny", 10, 0, 1),
     ("classifier", 1000, 0, 2),
     ("skinny", 10, 0, 1),
-    ("lmhead50k", 50257, 0, 2),
-    ("lmhead128k", 128256, 1, 2),
+    ("lmhead50k", 50257, 0, 4),
+    ("lmhead128k", 128256, 1, 4),
     ("beyond-registers-bf16", 200_000, 1, 3),
     ("beyond-registers-f32", 100_000, 0, 3),
     ("short-limit", 256, 0, 1),
     ("just-over-short", 257, 1, 2),
+    # 16-byte vectors per row (body + head/tail) up to 1024 stay resident
+    ("resident-limit-f32", 4080, 0, 2),
+    ("over-resident-f32", 4096, 0, 4),
+    ("resident-limit-bf16", 8176, 1, 2),
+    ("over-resident-bf16", 8192, 1, 4),
+    # two parts of 12 x 1024 vectors: aligned body of at most 24576 vectors
+    ("parts-limit-bf16", 196_608, 1, 4),
+    ("over-parts-bf16", 196_616, 1, 3),
+    ("parts-limit-f32", 98_304, 0, 4),
+    ("over-parts-f32", 98_308, 0, 3),
 ])
 def test_path_selection(name, C, dtype, path):
     assert ce.select_path(C, dtype) == path
@@ -137,3 +148,20 @@ def test_force_path_round_trip():
         ce.force_path(prev)
     assert ce.select_path(10, 0) == 1
     assert ce.lib().ce_debug_force_path(7) == PATH
+    assert ce.lib().ce_debug_force_path(5) == PATH
+    prev = ce.force_path(4)
+    try:
+        assert ce.select_path(10, 1) == 4
+    finally:
+        ce.force_path(prev)
+
+
+def test_part_hooks_round_trip():
+    prev = ce.part_polls(0)
+    try:
+        assert ce.part_polls(5) == 0
+    finally:
+        ce.part_polls(prev)
+    assert prev == 64
+    assert ce.lib().ce_debug_part_polls(-1) == PATH
+    ce.part_counter(None)

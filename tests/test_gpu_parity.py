@@ -59,24 +59,45 @@ SMALL = [
     (3, 65531, "f32", 3.0),
     (5, 131064, "bf16", 4.0),
     (1, 128256, "bf16", 4.0),
+    # row parts (path 4): the one-part configurations at their capacity,
+    # two parts with 2-byte aligned bf16 rows, and two parts filling every
+    # register and LDS slot
+    (21, 32767, "bf16", 4.0),
+    (13, 81919, "bf16", 4.0),
+    (7, 99999, "bf16", 4.0),
+    (11, 196607, "bf16", 4.0),
+    (4, 98303, "f32", 3.0),
 ]
 
+PATHS = [0, 1, 2, 3, 4]
+PATH_IDS = ["auto", "short", "resident", "long", "parts"]
 
-def _legal(path, C):
-    return path != 1 or C <= 256
+
+def _legal(path, C, dtype):
+    """Whether a forced path takes rows of C elements (short: C <= 256;
+    resident: at most 16384 16-byte vectors; parts: an aligned body of at
+    most 24576 vectors)."""
+    es = 4 if dtype == "f32" else 2
+    if path == 1:
+        return C <= 256
+    if path == 2:
+        return (C * es + 15) // 16 + 1 <= 16384
+    if path == 4:
+        return C // (16 // es) <= 24576
+    return True
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3], ids=["auto", "short", "resident", "long"])
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("B,C,dtype,sigma", SMALL, ids=[f"{b}x{c}-{d}" for b, c, d, _ in SMALL])
 def test_parity_small(path, B, C, dtype, sigma):
-    if not _legal(path, C):
-        pytest.skip("short path takes C <= 256")
+    if not _legal(path, C, dtype):
+        pytest.skip("the forced path does not take this row length")
     z, t = synth.make_inputs(B, C, dtype, sigma, seed=B * 1000 + C)
     _force(path)
     _log(f"{B}x{C} {dtype} path={path}", full_parity(z, t, dtype, where=f"{B}x{C} {dtype} p{path}"))
 
 
-@pytest.mark.parametrize("path", [0, 2, 3], ids=["auto", "resident", "long"])
+@pytest.mark.parametrize("path", [0, 2, 3, 4], ids=["auto", "resident", "long", "parts"])
 def test_parity_spike_rows(path):
     """Rows with one +1e4 entry (the LM-head stability case) on a ragged
     shape, including rows whose target is the spike."""
@@ -89,7 +110,7 @@ def test_parity_spike_rows(path):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("path", [0, 1, 2, 3], ids=["auto", "short", "resident", "long"])
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 def test_parity_edge_values(path, dtype):
     """Uniform rows (loss ln C), rows of +-1e4, rows where the target holds
     nearly all the mass, and invalid targets (NaN rows)."""
@@ -110,8 +131,8 @@ def test_parity_edge_values(path, dtype):
     if dtype == "bf16":
         z = synth.bf16_bits_from_f32(z)
     _force(path)
-    if not _legal(path, C):
-        pytest.skip("short path takes C <= 256")
+    if not _legal(path, C, dtype):
+        pytest.skip("the forced path does not take this row length")
     _log(f"edges {dtype} path={path}", full_parity(z, t, dtype, where=f"edges {dtype} p{path}"))
 
 

@@ -1,0 +1,150 @@
+"""Row parts (path 4): the trade of max/sum-exp pairs between the
+workgroups of a row.
+
+A part that does not receive its partner's pair in time recomputes it with
+the same code.  These tests force that (zero polls) and check that the
+outputs are bitwise those of the exchange, that the device counter sees
+every part of every two-part row recompute, that mailbox-like bit patterns
+left in grad_out on entry change nothing, that the forced fallback matches
+the oracle, and that calls on two streams at once do not disturb each
+other."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synth
+
+from _parity import full_parity, to_device
+
+pytestmark = pytest.mark.gpu
+
+# (B, C, dtype, sigma): two parts per row (aligned, 2-byte aligned, 4-byte
+# aligned fp32, every slot filled) and one one-part shape as a control.
+SHAPES = [
+    (64, 128256, "bf16", 4.0),
+    (9, 99999, "bf16", 4.0),
+    (33, 50257, "f32", 3.0),
+    (5, 196607, "bf16", 4.0),
+    (40, 40000, "f32", 3.0),
+]
+IDS = [f"{b}x{c}-{d}" for b, c, d, _ in SHAPES]
+
+MAIL_TAG = 0x7FA57FA5
+MAIL_EMPTY = 0x7FA17FA1
+
+
+def _ce():
+    import softmax_cross_entropy_ce_amd as ce
+    return ce
+
+
+@pytest.fixture(autouse=True)
+def _reset_hooks():
+    ce = _ce()
+    prev_path = ce.force_path(4)
+    prev_polls = ce.part_polls(64)
+    yield
+    ce.part_counter(None)
+    ce.part_polls(prev_polls)
+    ce.force_path(prev_path)
+
+
+def _two_parts(C, dtype):
+    return C // (4 if dtype == "f32" else 8) > 10 * 1024
+
+
+def _bits(x):
+    import torch
+    return x.view(torch.int16 if x.element_size() == 2 else torch.int32)
+
+
+def _run(z_dev, t_dev):
+    import torch
+    grad, loss_rows = _ce().fwd_grad(z_dev, t_dev)
+    torch.cuda.synchronize()
+    return grad, loss_rows
+
+
+@pytest.mark.parametrize("B,C,dtype,sigma", SHAPES, ids=IDS)
+def test_fallback_is_bitwise_and_counted(B, C, dtype, sigma):
+    import torch
+    ce = _ce()
+    z, t = synth.make_inputs(B, C, dtype, sigma, seed=B + C)
+    z_dev, t_dev = to_device(z, t, dtype)
+    counter = torch.zeros(1, dtype=torch.int32, device=z_dev.device)
+    ce.part_counter(counter)
+    g1, l1 = _run(z_dev, t_dev)
+    n_default = int(counter.item())
+    ce.part_polls(0)
+    counter.zero_()
+    g2, l2 = _run(z_dev, t_dev)
+    n_forced = int(counter.item())
+    print(f"[parts] {B}x{C} {dtype}: recomputed pairs {n_default} (64 polls), "
+          f"{n_forced} (0 polls)", flush=True)
+    assert n_forced == (2 * B if _two_parts(C, dtype) else 0)
+    assert torch.equal(_bits(g1), _bits(g2))
+    assert torch.equal(_bits(l1), _bits(l2))
+
+
+@pytest.mark.parametrize("pattern", [MAIL_TAG, MAIL_EMPTY, 0], ids=["tag", "empty", "zero"])
+def test_stale_grad_content_is_ignored(pattern):
+    """grad_out filled with the mailbox tag (or the empty tag) before the
+    call: the clear step makes the parts ignore it."""
+    import torch
+    ce = _ce()
+    B, C, dtype = 24, 99999, "bf16"
+    z, t = synth.make_inputs(B, C, dtype, 4.0, seed=77)
+    z_dev, t_dev = to_device(z, t, dtype)
+    g_ref, l_ref = _run(z_dev, t_dev)
+    words = torch.full((B * C // 2,), pattern - (1 << 32) if pattern >= 1 << 31 else pattern,
+                       dtype=torch.int32, device=z_dev.device)
+    grad = torch.empty_like(z_dev)
+    grad.view(-1)[: 2 * words.numel()].view(torch.int32).copy_(words)
+    loss_rows = torch.full((B,), float("nan"), dtype=torch.float32, device=z_dev.device)
+    ce.fwd_grad_into(z_dev, t_dev, grad, loss_rows)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(grad), _bits(g_ref))
+    assert torch.equal(_bits(loss_rows), _bits(l_ref))
+
+
+@pytest.mark.parametrize("B,C,dtype,sigma", SHAPES[:4], ids=IDS[:4])
+def test_forced_fallback_matches_oracle(B, C, dtype, sigma):
+    _ce().part_polls(0)
+    z, t = synth.make_inputs(B, C, dtype, sigma, seed=3 * B + C)
+    full_parity(z, t, dtype, where=f"{B}x{C} {dtype} fallback")
+
+
+def test_spike_rows_forced_fallback():
+    """+1e4 spikes, some on the target, with every pair recomputed."""
+    _ce().part_polls(0)
+    B, C = 33, 50257
+    z, t = synth.make_inputs(B, C, "f32", 3.0, spike=1e4, seed=12)
+    t[:6] = synth.spike_columns(B, C, seed=12)[:6].astype(np.int32)
+    full_parity(z, t, "f32", where="spike fallback")
+
+
+def test_two_streams_at_once():
+    """Two calls on two streams with their own outputs, queued together:
+    each matches a call made alone."""
+    import torch
+    ce = _ce()
+    B, C, dtype = 48, 128256, "bf16"
+    z, t = synth.make_inputs(B, C, dtype, 4.0, seed=5)
+    z_dev, t_dev = to_device(z, t, dtype)
+    g_ref, l_ref = _run(z_dev, t_dev)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    torch.cuda.synchronize()
+    for s in (s1, s2):
+        g = torch.empty_like(z_dev)
+        lr = torch.empty(B, dtype=torch.float32, device=z_dev.device)
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                ce.fwd_grad_into(z_dev, t_dev, g, lr)
+        outs.append((g, lr))
+    torch.cuda.synchronize()
+    for g, lr in outs:
+        assert torch.equal(_bits(g), _bits(g_ref))
+        assert torch.equal(_bits(lr), _bits(l_ref))

@@ -17,16 +17,20 @@ from _parity import F32_GRAD_ATOL, grad_to_host, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
+# (B, C, dtype, sigma, path): path 0 is the automatic choice
 CASES = [
-    (16, 10, "f32", 20.0),      # short path
-    (64, 1000, "f32", 2.0),     # resident, one wave
-    (8, 50257, "f32", 3.0),     # resident, 1024 threads, misaligned rows
-    (4, 128256, "bf16", 4.0),   # resident, 1024 threads, LDS prefetch
-    (300, 70001, "bf16", 4.0),  # LDS prefetch, several rows per workgroup
-    (3, 200_000, "bf16", 4.0),  # long rows: streamed part
-    (2, 100_003, "f32", 3.0),   # long rows, misaligned
+    (16, 10, "f32", 20.0, 0),       # short path
+    (64, 1000, "f32", 2.0, 0),      # resident, 256 threads
+    (8, 50257, "f32", 3.0, 0),      # two row parts, misaligned rows
+    (4, 128256, "bf16", 4.0, 0),    # two row parts
+    (300, 70001, "bf16", 4.0, 0),   # one row part with LDS slots, 2-byte aligned rows
+    (8, 50257, "f32", 3.0, 2),      # resident, 1024 threads, misaligned rows
+    (4, 128256, "bf16", 4.0, 2),    # resident with LDS prefetch
+    (300, 70001, "bf16", 4.0, 2),   # LDS prefetch, several rows per workgroup
+    (3, 200_000, "bf16", 4.0, 0),   # long rows: streamed part
+    (2, 100_003, "f32", 3.0, 0),    # long rows, misaligned
 ]
-IDS = [f"{b}x{c}-{d}" for b, c, d, _ in CASES]
+IDS = [f"{b}x{c}-{d}-p{p}" for b, c, d, _, p in CASES]
 
 
 @pytest.fixture(autouse=True)
@@ -37,9 +41,15 @@ def _reset_path():
     ce.force_path(prev)
 
 
-@pytest.mark.parametrize("B,C,dtype,sigma", CASES, ids=IDS)
-def test_bitwise_determinism(B, C, dtype, sigma):
+def _force(path):
+    import softmax_cross_entropy_ce_amd as ce
+    ce.force_path(path)
+
+
+@pytest.mark.parametrize("B,C,dtype,sigma,path", CASES, ids=IDS)
+def test_bitwise_determinism(B, C, dtype, sigma, path):
     import torch
+    _force(path)
     z, t = synth.make_inputs(B, C, dtype, sigma, seed=7)
     zd, td = to_device(z, t, dtype)
     ref = run_gpu(zd, td)
@@ -51,13 +61,14 @@ def test_bitwise_determinism(B, C, dtype, sigma):
         assert torch.equal(out[2].view(torch.int32), ref[2].view(torch.int32))
 
 
-@pytest.mark.parametrize("B,C,dtype,sigma", CASES, ids=IDS)
-def test_full_coverage_and_guard_bands(B, C, dtype, sigma):
+@pytest.mark.parametrize("B,C,dtype,sigma,path", CASES, ids=IDS)
+def test_full_coverage_and_guard_bands(B, C, dtype, sigma, path):
     """Outputs pre-filled with NaN come back NaN-free (every element
     written), and the guard bands around them keep their sentinel (nothing
     written outside)."""
     import torch
     import softmax_cross_entropy_ce_amd as ce
+    _force(path)
     z, t = synth.make_inputs(B, C, dtype, sigma, seed=8)
     zd, td = to_device(z, t, dtype)
     pad = 4096
@@ -75,12 +86,13 @@ def test_full_coverage_and_guard_bands(B, C, dtype, sigma):
     assert torch.isnan(lbuf[:pad]).all() and torch.isnan(lbuf[pad + B:]).all()
 
 
-@pytest.mark.parametrize("B,C,dtype,sigma", CASES, ids=IDS)
-def test_shift_invariance(B, C, dtype, sigma):
+@pytest.mark.parametrize("B,C,dtype,sigma,path", CASES, ids=IDS)
+def test_shift_invariance(B, C, dtype, sigma, path):
     """Adding a constant to every logit of a row leaves loss and gradient
     unchanged (within the parity bars).  Logits sit on a grid (fp32:
     multiples of 2^-8 within +-64, shift 37; bf16: multiples of 2^-2 within
     +-8, shift 4) so that the shifted inputs are exact."""
+    _force(path)
     if dtype == "f32":
         z = synth.grid_logits(B, C, 2.0 ** -8, 64.0, seed=9)
         z2 = z + np.float32(37.0)

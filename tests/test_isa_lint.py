@@ -10,7 +10,13 @@ cross-compiles).
   states when the store's soffset is a register.  A silent corruption of
   exactly this kind was seen on the GPU; the kernels guard every 16-byte
   store, and this test keeps it that way.
-* Every kernel fits in the 160 KB of LDS of a compute unit.
+* Every kernel fits in the 160 KB of LDS of a compute unit; the row-part
+  kernels, which run two 1024-thread workgroups per compute unit, fit in
+  64 VGPRs and half the LDS.
+* No kernel writes through the scalar data cache (scalar stores, scalar
+  atomics, scalar cache write-back or invalidate of written data): every
+  store, including the mailbox words the row parts trade, is a vector
+  memory instruction.
 """
 
 from __future__ import annotations
@@ -25,6 +31,8 @@ import pytest
 from softmax_cross_entropy_ce_amd import build as B
 
 PACKED_FP32 = re.compile(r"\bv_pk_(add|mul|fma|mov)_f32\b")
+SCALAR_WRITE = re.compile(r"^\s+s_(store|buffer_store|scratch_store|atomic|buffer_atomic|"
+                          r"dcache_wb|dcache_discard)\w*", re.M)
 
 
 def _vregs(tok: str) -> set[int]:
@@ -101,7 +109,8 @@ def _kernel_meta(asm: str) -> dict[str, dict[str, int]]:
 def test_kernels_present(device_asm):
     meta = _kernel_meta(device_asm)
     names = " ".join(meta)
-    for k in ("ce_short_kernel", "ce_row_kernel", "ce_row_lds_kernel", "ce_reduce_kernel"):
+    for k in ("ce_short_kernel", "ce_row_kernel", "ce_row_lds_kernel", "ce_reduce_kernel",
+              "ce_part_kernel", "ce_mailbox_clear_kernel"):
         assert k in names, k
 
 
@@ -123,6 +132,28 @@ def test_1024_thread_kernels_fit_registers(device_asm):
     for k, v in meta.items():
         if "Li1024E" in k or "ce_row_lds_kernel" in k:
             assert v["next_free_vgpr"] <= 128, (k, v["next_free_vgpr"])
+
+
+def test_part_kernels_fit_two_per_cu(device_asm):
+    meta = _kernel_meta(device_asm)
+    parts = {k: v for k, v in meta.items() if "ce_part_kernel" in k}
+    assert parts
+    for k, v in parts.items():
+        assert v["next_free_vgpr"] <= 64, (k, v["next_free_vgpr"])
+        assert v.get("group_segment_fixed_size", 0) <= 80 * 1024, k
+
+
+def test_no_scalar_memory_writes(device_asm):
+    hits = SCALAR_WRITE.findall(device_asm)
+    assert not hits, hits[:5]
+
+
+def test_scalar_write_pattern_matches():
+    assert SCALAR_WRITE.search("\ts_store_dword s0, s[2:3], 0x0\n")
+    assert SCALAR_WRITE.search("\ts_atomic_add s0, s[2:3], 0x0\n")
+    assert SCALAR_WRITE.search("\ts_dcache_wb\n")
+    assert not SCALAR_WRITE.search("\ts_load_dwordx2 s[0:1], s[4:5], 0x0\n")
+    assert not SCALAR_WRITE.search("\tglobal_atomic_cmpswap_x2 v1, v[2:5], s[0:1]\n")
 
 
 def test_no_packed_fp32(device_asm):
