@@ -104,8 +104,12 @@ def run_copy(args) -> None:
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU's clocks take about 40 back-to-back lmhead128k steps (~30 ms)
+    # to settle after idle: a step runs fast, then up to 30 % slower, then
+    # settles.  The default warm-up covers that; the timed steps are the
+    # steady state.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="lmhead128k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -46,12 +46,14 @@ int elem_size(int dtype) { return dtype == CE_F32 ? 4 : 2; }
 // 16-byte vectors a row may touch: the aligned body plus a head and a tail.
 int64_t row_vectors(int64_t C, int es) { return (C * es + 15) / 16 + 1; }
 
-// Path 4 configurations by the largest aligned body a row can have,
-// floor(C / elements per vector): one part of 4 register slots, one part of
-// 8 register and 2 LDS slots, two parts of 8 register and 4 LDS slots each
-// (a slot is 1024 vectors).
+// Path 4 configurations by the largest body a row can have, floor(C /
+// elements per vector) 16-byte vectors: one part of 4 register slots; one
+// part of 8 register and 2 LDS slots; two parts of 8 register slots; two
+// parts of 8 register and 4 LDS slots (a slot is 1024 vectors, and a part
+// of a two-part row is half the body rounded up to 8 vectors).
 constexpr int64_t kPartsOneSmall = 4 * 1024;
 constexpr int64_t kPartsOne = 10 * 1024;
+constexpr int64_t kPartsTwoRegs = 2 * 8 * 1024;
 constexpr int64_t kPartsTwo = 2 * 12 * 1024;
 
 int64_t body_vectors_max(int64_t C, int es) { return C / (16 / es); }
@@ -202,19 +204,19 @@ RowCfg resident_cfg(int64_t C, int es, bool* ok) {
 }
 
 // ---------------------------------------------------------------- path 4
-template <typename T, int P, int NR, int NL>
+template <typename T, int P, int NT, int NR, int NL, int NXW>
 int launch_parts_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g,
                      float* l, hipStream_t st) {
   const int64_t blocks = P * ((B + 7) / 8 * 8);
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
   if constexpr (P > 1) {
     const int64_t cb = (B * P + 255) / 256;
-    hipLaunchKernelGGL(ce::ce_mailbox_clear_kernel<T>, dim3((unsigned)cb), dim3(256), 0, st, g, B,
-                       (int)C, P);
+    hipLaunchKernelGGL(ce::ce_mailbox_clear_kernel<T>, dim3((unsigned)cb), dim3(256), 0, st, z, g,
+                       B, (int)C, P);
     if (launched() != CE_OK) return CE_ERR_LAUNCH;
   }
-  hipLaunchKernelGGL((ce::ce_part_kernel<T, P, NR, NL>), dim3((unsigned)blocks),
-                     dim3(ce::kPartThreads), 0, st, z, t, B, (int)C, invB, g, l,
+  hipLaunchKernelGGL((ce::ce_part_kernel<T, P, NT, NR, NL, NXW>), dim3((unsigned)blocks), dim3(NT),
+                     0, st, z, t, B, (int)C, invB, g, l,
                      g_part_polls.load(std::memory_order_relaxed),
                      g_part_counter.load(std::memory_order_relaxed));
   return launched();
@@ -224,9 +226,10 @@ template <typename T>
 int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g, float* l,
                  hipStream_t st) {
   const int64_t nb = body_vectors_max(C, sizeof(T));
-  if (nb <= kPartsOneSmall) return launch_parts_cfg<T, 1, 4, 0>(z, t, B, C, invB, g, l, st);
-  if (nb <= kPartsOne) return launch_parts_cfg<T, 1, 8, 2>(z, t, B, C, invB, g, l, st);
-  if (nb <= kPartsTwo) return launch_parts_cfg<T, 2, 8, 4>(z, t, B, C, invB, g, l, st);
+  if (nb <= kPartsOneSmall) return launch_parts_cfg<T, 1, 1024, 4, 0, 0>(z, t, B, C, invB, g, l, st);
+  if (nb <= kPartsOne) return launch_parts_cfg<T, 1, 1024, 8, 2, 0>(z, t, B, C, invB, g, l, st);
+  if (nb <= kPartsTwoRegs) return launch_parts_cfg<T, 2, 1024, 8, 0, 0>(z, t, B, C, invB, g, l, st);
+  if (nb <= kPartsTwo) return launch_parts_cfg<T, 2, 1024, 8, 4, 0>(z, t, B, C, invB, g, l, st);
   return CE_ERR_PATH;
 }
 

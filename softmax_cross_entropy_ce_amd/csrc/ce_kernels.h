@@ -243,19 +243,21 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
 //            row's gradient is formed and written.
 // ===========================================================================
 struct RowGeom {
-  int h;       // elements before the first 16-byte boundary
-  int nb;      // aligned 16-byte vectors
-  int tail0;   // first element after the aligned body
-  int ntail;   // elements after the aligned body
+  int h;       // elements before the first ALIGN-byte boundary
+  int nb;      // 16-byte vectors from there on
+  int tail0;   // first element after them
+  int ntail;   // elements after them
 };
 
-// Row-relative indices fit in 32 bits: C <= 2^28.
-template <typename T>
+// Row-relative indices fit in 32 bits: C <= 2^28.  The body starts at the
+// first ALIGN-byte boundary of the row (ALIGN a power of two >= 16).
+template <typename T, int ALIGN = 16>
 __device__ __forceinline__ RowGeom row_geom(const T* rp, int C) {
   constexpr int VE = Elem<T>::VE;
+  static_assert(ALIGN >= 16 && (ALIGN & (ALIGN - 1)) == 0, "alignment");
   RowGeom g;
-  const uint32_t mis = (uint32_t)((uintptr_t)rp & 15u);
-  g.h = mis ? (int)((16u - mis) / sizeof(T)) : 0;
+  const uint32_t mis = (uint32_t)((uintptr_t)rp & (uint32_t)(ALIGN - 1));
+  g.h = mis ? (int)((ALIGN - mis) / sizeof(T)) : 0;
   if (g.h > C) g.h = C;
   g.nb = (C - g.h) / VE;
   g.tail0 = g.h + g.nb * VE;

@@ -1,4 +1,4 @@
-// Path 4: rows cut into parts, one 1024-thread workgroup per part and two
+// Path 4: rows cut into parts, one workgroup per part and several
 // workgroups per CU.
 //
 // The method's per-row steps (rumus 0.1.1 cross_entropy.wgsl, pass 1 steps
@@ -6,8 +6,10 @@
 // gradient element can be written.  With one workgroup per row, a row of
 // 128256 bf16 values (256 KB) fills a CU's registers and LDS, so only one
 // row is in flight per CU.  Here a row of nb 16-byte vectors is cut into P
-// parts of at most NT*(NR+NL) vectors.  Each part is read once into
-// registers (NR slots) and LDS (NL slots), reduced to its own online
+// parts.  A part is read once into registers (NR slots of NT vectors) and
+// LDS (NL slots of NT vectors, then a partial slot of NXW waves), so that
+// two or three workgroups of at most 64 VGPRs fill a CU's 32 wave slots
+// and its LDS.  Each part is reduced to its own online
 // (c, s) pair, and the parts then trade their pairs, so that every part
 // combines the same P pairs in the same order (part 0 first) and writes
 // its share of the gradient from on-chip data.  The combine is the
@@ -42,15 +44,21 @@ namespace ce {
 
 constexpr uint32_t kMailTag = 0x7FA57FA5u;
 constexpr uint32_t kMailEmpty = 0x7FA17FA1u;
-constexpr int kPartThreads = 1024;
+
+// A part's body starts at a 128-byte boundary of the logits row (one cache
+// line), and parts are whole multiples of 8 vectors, so every wave's 1 KB
+// access covers whole lines; the up to 128/size - 1 elements before the
+// boundary are head elements handled one per thread.
+constexpr int kPartAlign = 128;
+constexpr int kPartQuantum = kPartAlign / 16;
 
 // Body-vector range [v0, v0 + len) of part q when nb vectors are cut into P
-// parts of ceil(nb / P).
+// parts of ceil(nb / P) rounded up to whole cache lines.
 struct PartRange {
   int v0, len;
 };
 __device__ __forceinline__ PartRange part_range(int nb, int P, int q) {
-  const int L = (nb + P - 1) / P;
+  const int L = ((nb + P - 1) / P + kPartQuantum - 1) / kPartQuantum * kPartQuantum;
   const int a = q * L < nb ? q * L : nb;
   const int b = a + L < nb ? a + L : nb;
   return PartRange{a, b - a};
@@ -68,8 +76,10 @@ __device__ __forceinline__ void part_of_block(uint32_t g, int64_t& row, int& par
 // Empty the mailbox of every part of every row (P > 1): both words become
 // kMailEmpty in the high half and zero in the low half.  One thread per
 // (row, part); a 16-byte store into the part's last body vector of grad.
+// The geometry is that of the logits row, as in ce_part_kernel.
 template <typename T>
-__global__ __launch_bounds__(256) void ce_mailbox_clear_kernel(T* __restrict__ grad, int64_t B,
+__global__ __launch_bounds__(256) void ce_mailbox_clear_kernel(const T* __restrict__ logits,
+                                                               T* __restrict__ grad, int64_t B,
                                                                int C, int P) {
   constexpr int VE = Elem<T>::VE;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -77,7 +87,7 @@ __global__ __launch_bounds__(256) void ce_mailbox_clear_kernel(T* __restrict__ g
   const int64_t row = i / P;
   const int q = (int)(i % P);
   T* gp = grad + row * C;
-  const RowGeom geo = row_geom(gp, C);
+  const RowGeom geo = row_geom<T, kPartAlign>(logits + row * C, C);
   const PartRange pr = part_range(geo.nb, P, q);
   if (pr.len <= 0) return;
   u32x4* mb = reinterpret_cast<u32x4*>(gp + geo.h + (int64_t)(pr.v0 + pr.len - 1) * VE);
@@ -103,19 +113,27 @@ __device__ __forceinline__ void wg_pair(float c, float s, float* red_c, float* r
   sg = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
 }
 
+// Vectors a part of ce_part_kernel<T, P, NT, NR, NL, NXW> holds.
+constexpr int part_capacity(int NT, int NR, int NL, int NXW) { return (NR + NL) * NT + NXW * 64; }
+
 // fallbacks (may be null): a device counter, incremented once by every part
 // that recomputed its partner's pair instead of receiving it.  spin: polls
-// before that happens (0: every part recomputes).
-template <typename T, int P, int NR, int NL>
-__global__ __launch_bounds__(kPartThreads) __attribute__((amdgpu_waves_per_eu(8)))
+// before that happens (0: every part recomputes).  At most 64 VGPRs (eight
+// waves per SIMD), so 32 / (NT / 64) workgroups fit a CU by waves.
+template <typename T, int P, int NT, int NR, int NL, int NXW>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8)))
 void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B,
                     int C, float invB, T* __restrict__ grad, float* __restrict__ loss_rows,
                     int spin, uint32_t* __restrict__ fallbacks) {
   using E = Elem<T>;
-  constexpr int NT = kPartThreads, NW = NT / 64, VE = E::VE, ES = sizeof(T);
-  constexpr int NS = NR + NL;  // slots per part
+  constexpr int NW = NT / 64, VE = E::VE, ES = sizeof(T);
+  constexpr int NLS = NL + (NXW > 0 ? 1 : 0);  // LDS slots, the last maybe partial
+  constexpr int NS = NR + NLS;                 // slots per part
+  constexpr int NX = NXW * 64;                 // threads with a vector in the partial slot
   static_assert(P == 1 || P == 2, "one or two parts per row");
-  __shared__ u32x4 stage[NL > 0 ? NL * NT : 1];
+  static_assert(NT % 64 == 0 && NW >= 1 && NW <= 16, "1 to 16 waves");
+  static_assert(NXW >= 0 && NXW < NW, "partial LDS slot smaller than a slot");
+  __shared__ u32x4 stage[NL * NT + NX > 0 ? NL * NT + NX : 1];
   __shared__ float red_c[NW], red_s[NW];
   __shared__ float mail_c, mail_s;
   __shared__ int mail_ok;
@@ -129,7 +147,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
 
   const T* rp = logits + row * C;
   T* gp = grad + row * C;
-  const RowGeom geo = row_geom(rp, C);
+  const RowGeom geo = row_geom<T, kPartAlign>(rp, C);
   const PartRange own = part_range(geo.nb, P, part);
   const rsrc_t rrow = make_rsrc(rp, (uint32_t)C * ES);
   const rsrc_t rin = make_rsrc(rp + geo.h + own.v0 * VE, (uint32_t)own.len * 16u);
@@ -143,6 +161,17 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   for (int p = 0; p < NL; ++p)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rin, (lds_ptr_t)&stage[p * NT + wv * 64], 16, voff,
                                              (uint32_t)(NR + p) * NT * 16u, 0, kPolicyStream);
+  if constexpr (NXW > 0) {
+    if (wv < NXW)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rin, (lds_ptr_t)&stage[NL * NT + wv * 64], 16, voff,
+                                               (uint32_t)(NR + NL) * NT * 16u, 0, kPolicyStream);
+  }
+  // LDS slot p of this thread (the partial slot holds nothing for threads
+  // at or past NX: their vectors lie past every part's end).
+  auto lds_slot = [&](int p) -> u32x4 {
+    if (p < NL || tid < NX) return stage[p * NT + tid];
+    return u32x4{0u, 0u, 0u, 0u};
+  };
 
   const int32_t t = targets[row];
   const bool valid = t >= 0 && t < C;
@@ -151,7 +180,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   const int tvec = t_body ? tb / VE : -1;  // target's body vector (row-relative)
   const int tj = t_body ? tb % VE : -1;
 
-  // Edge elements of part q: the head (before the first 16-byte boundary)
+  // Edge elements of part q: the head (before the first 128-byte boundary)
   // belongs to part 0 and the tail to part P-1; edge i goes to thread i.
   auto edge_elem = [&](int q) -> int {
     const int nh = q == 0 ? geo.h : 0;
@@ -197,7 +226,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   for (int k = 0; k < NR; ++k) fold_slot(own, k, v[k], c, s);
   wait_vmcnt<0>();  // LDS slots, edge and target loads
 #pragma unroll
-  for (int p = 0; p < NL; ++p) fold_slot(own, NR + p, stage[p * NT + tid], c, s);
+  for (int p = 0; p < NLS; ++p) fold_slot(own, NR + p, lds_slot(p), c, s);
   const float xs = xe >= 0 ? xs_raw : kNegInf;
   const float zt = valid ? zt_raw : 0.f;
   fold_edge(xe, xs, c, s);
@@ -212,13 +241,16 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       uint64_t* mine = reinterpret_cast<uint64_t*>(gp + geo.h + (int64_t)(own.v0 + own.len - 1) * VE);
       uint64_t* theirs = reinterpret_cast<uint64_t*>(gp + geo.h + (int64_t)(pq.v0 + pq.len - 1) * VE);
       const uint64_t tag = (uint64_t)kMailTag << 32;
+      // Both publishes are issued without waiting for their results (each
+      // fails harmlessly if the owner has already written its gradient), so
+      // the first poll follows them at once.
       uint64_t e0 = (uint64_t)kMailEmpty << 32, e1 = e0;
-      if (__hip_atomic_compare_exchange_strong(&theirs[0], &e0, tag | __builtin_bit_cast(uint32_t, c_own),
-                                               __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT))
-        __hip_atomic_compare_exchange_strong(&theirs[1], &e1, tag | __builtin_bit_cast(uint32_t, s_own),
-                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_compare_exchange_strong(&theirs[0], &e0, tag | __builtin_bit_cast(uint32_t, c_own),
+                                           __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_compare_exchange_strong(&theirs[1], &e1, tag | __builtin_bit_cast(uint32_t, s_own),
+                                           __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
       int ok = 0;
       uint64_t a = 0, b = 0;
       for (int it = 0; it < spin; ++it) {
@@ -291,7 +323,9 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
 #pragma unroll
   for (int k = 0; k < NR; ++k) write_slot(k, v[k]);
 #pragma unroll
-  for (int p = 0; p < NL; ++p) write_slot(NR + p, stage[p * NT + tid]);
+  for (int p = 0; p < NLS; ++p) {
+    if (p < NL || tid < NX) write_slot(NR + p, lds_slot(p));
+  }
   if (xe >= 0) {
     const float g = (xe == t) ? rr.gt : exp2_hw(__builtin_fmaf(xs, kLog2e, -cg)) * rr.scale;
     E::store1(gp + xe, g);

@@ -4,8 +4,8 @@ cross-compiles).
 * No kernel uses scratch memory (a register spill in a hot loop).
 * No packed fp32 VALU instruction is emitted (the library is built with that
   feature disabled).
-* No store wider than 8 bytes has its data registers overwritten by a VALU
-  instruction less than two wait states later: such a store reads its data
+* No store (or 16-byte compare-and-swap) wider than 8 bytes has its data
+  registers overwritten by a VALU instruction less than two wait states later: such a store reads its data
   registers after it issues, and the compiler does not insert the wait
   states when the store's soffset is a register.  A silent corruption of
   exactly this kind was seen on the GPU; the kernels guard every 16-byte
@@ -50,11 +50,15 @@ def wide_store_hazards(asm: str, wait_states: int = 2) -> list[str]:
     for i, line in enumerate(lines):
         if re.match(r"^[_A-Za-z][\w.]*:", line):
             func = line.split(":")[0]
-        m = re.match(r"\s+(buffer|global|flat)_store_dwordx[34]\s+(.*)", line)
+        m = re.match(r"\s+(buffer|global|flat)_(store_dwordx[34]|atomic_cmpswap_x2)\s+(.*)", line)
         if not m:
             continue
-        ops = m.group(2).split()
-        data = _vregs(ops[1] if m.group(1) == "global" else ops[0])
+        ops = m.group(3).split()
+        if m.group(2).startswith("atomic"):
+            # the 16-byte data operand (new value and compare value)
+            data = next((r for r in map(_vregs, ops) if len(r) == 4), set())
+        else:
+            data = _vregs(ops[1] if m.group(1) == "global" else ops[0])
         ws, j = 0, i + 1
         while j < len(lines) and ws < wait_states:
             t = lines[j].strip()
@@ -173,3 +177,6 @@ def test_hazard_scanner_catches_the_pattern():
            "\t; sched_barrier mask(0x00000000)\n\tv_mov_b32_e32 v58, s15\n")
     good = bad.replace("\t; sched_barrier", "\ts_nop 1\n\t; sched_barrier")
     assert wide_store_hazards(bad) and not wide_store_hazards(good)
+    cas = "k:\n\tglobal_atomic_cmpswap_x2 v36, v[34:37], s[0:1] offset:-16\n\tv_mov_b32_e32 v34, s62\n"
+    cas_ok = cas.replace("\tv_mov", "\ts_mov_b32 s48, s33\n\ts_mov_b32 s49, s33\n\tv_mov")
+    assert wide_store_hazards(cas) and not wide_store_hazards(cas_ok)
