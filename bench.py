@@ -159,22 +159,31 @@ def main() -> None:
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Two events per step, around ce_fwd_grad only (each event adds a few
+    # microseconds between kernels); the step time is the wall time.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     log(f"[bench] path {ce.PATH_NAMES[path]}; timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1, e2 in evs:
+    for e0, e1 in evs:
         e0.record(stream)
         ce.fwd_grad_into(zd, td, grad, loss_rows)
         e1.record(stream)
         ce.reduce_loss_into(loss_rows, loss, ws)
-        e2.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = [a.elapsed_time(b) for a, b, _ in evs]
-    red_ms = [b.elapsed_time(c) for _, b, c in evs]
+    fwd_ms = [a.elapsed_time(b) for a, b in evs]
     ms_per_step = wall * 1e3 / args.steps
+    # ce_reduce_loss alone, after the timed region
+    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(20)]
+    for a, b in rev:
+        a.record(stream)
+        ce.reduce_loss_into(loss_rows, loss, ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    red_ms = [a.elapsed_time(b) for a, b in rev]
     log(f"[bench] loss {loss.item():.6f}; fwd_grad median {statistics.median(fwd_ms):.4f} ms, "
         f"reduce median {statistics.median(red_ms):.4f} ms, step {ms_per_step:.4f} ms")
 

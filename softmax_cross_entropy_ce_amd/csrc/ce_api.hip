@@ -209,12 +209,6 @@ int launch_parts_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, float i
                      float* l, hipStream_t st) {
   const int64_t blocks = P * ((B + 7) / 8 * 8);
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  if constexpr (P > 1) {
-    const int64_t cb = (B * P + 255) / 256;
-    hipLaunchKernelGGL(ce::ce_mailbox_clear_kernel<T>, dim3((unsigned)cb), dim3(256), 0, st, z, g,
-                       B, (int)C, P);
-    if (launched() != CE_OK) return CE_ERR_LAUNCH;
-  }
   hipLaunchKernelGGL((ce::ce_part_kernel<T, P, NT, NR, NL, NXW>), dim3((unsigned)blocks), dim3(NT),
                      0, st, z, t, B, (int)C, invB, g, l,
                      g_part_polls.load(std::memory_order_relaxed),
@@ -263,7 +257,7 @@ bool overlaps(uintptr_t a, uintptr_t an, uintptr_t b, uintptr_t bn) {
 }
 
 // ------------------------------------------------------------ reduction
-constexpr int64_t kReduceMinChunk = 2048;
+constexpr int64_t kReduceMinChunk = 16384;  // one workgroup, one launch, up to here
 constexpr int64_t kReduceMaxBlocks = 1024;
 
 int64_t reduce_chunk(int64_t B) {

@@ -684,6 +684,9 @@ __global__ __launch_bounds__(kReduceThreads) void ce_reduce_kernel(const float* 
   const int64_t hi = (lo + chunk) < n ? (lo + chunk) : n;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   int64_t i = lo + threadIdx.x;
+  // unrolled so that 16 loads per thread are in flight; each accumulator
+  // still adds its elements in index order
+#pragma unroll 4
   for (; i + 3 * kReduceThreads < hi; i += 4 * kReduceThreads) {
     a0 += in[i];
     a1 += in[i + kReduceThreads];

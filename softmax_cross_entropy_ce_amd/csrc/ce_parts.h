@@ -19,19 +19,28 @@
 // words at the start of its own last body vector in grad.  Its partner
 // publishes (c, s) there, one value per word in the low half with kMailTag
 // in the high half; the owner polls it, and its own gradient store
-// overwrites it only after the poll has ended.  Before the parts run,
-// ce_mailbox_clear_kernel sets every mailbox word to kMailEmpty.  The
-// partner publishes with compare-and-swap from kMailEmpty, so a publish
-// that arrives after the owner has given up and written its gradient
-// changes nothing.  Both tags are signalling NaNs, both as one float32 and
-// as two bf16 values.  No arithmetic result is a signalling NaN, so no
-// gradient value can look like a mailbox word, and a word with kMailTag was
-// written by the partner in this launch.  The owner polls a bounded number
-// of times.  If the pair has not come by then (the partner is not resident
-// yet), it recomputes the pair from the logits with the same code, slots
-// and order that the partner uses, so the result is bitwise the same
-// whichever way the pair arrived.  No wait is unbounded and no result
-// depends on timing.
+// overwrites it only after the poll has ended.
+//  - First thing, the owner sets both words to kMailEmpty.  Its own later
+//    polls are ordered after that store, so whatever grad held before the
+//    call can never be read as a partner's value.
+//  - The partner publishes with compare-and-swap from kMailEmpty, so a
+//    publish that meets anything else (data from before the owner's
+//    emptying, or the owner's gradient once the owner has given up) changes
+//    nothing.  It repeats the publish on every poll of its own mailbox, so
+//    a publish that an owner starting late has emptied again is made
+//    again.  (One more publish after the partner's own pair has arrived
+//    was measured to cost about 1 % and is not made: the rare publish it
+//    would save ends in the recompute below.)
+//  - Both tags are signalling NaNs, both as one float32 and as two bf16
+//    values.  No arithmetic result is a signalling NaN, so no gradient
+//    value can look like a mailbox word, and a word with kMailTag that the
+//    owner reads was written by the partner in this launch.
+//  - The owner polls a bounded number of times.  If the pair has not come
+//    by then (the partner is not resident yet, or its publish was erased),
+//    it recomputes the pair from the logits with the same code, slots and
+//    order that the partner uses.  The result is bitwise the same whichever
+//    way the pair arrived.  No wait is unbounded and no result depends on
+//    timing.
 //
 // Workgroup g runs on XCD g % 8 (round-robin dispatch); the parts of a row
 // are given workgroups g, g + 8, ..., so they share an XCD and start next to
@@ -71,27 +80,6 @@ __device__ __forceinline__ void part_of_block(uint32_t g, int64_t& row, int& par
   const uint32_t xcd = g & 7u, local = g >> 3;
   row = (int64_t)(local / P) * 8 + xcd;
   part = (int)(local % P);
-}
-
-// Empty the mailbox of every part of every row (P > 1): both words become
-// kMailEmpty in the high half and zero in the low half.  One thread per
-// (row, part); a 16-byte store into the part's last body vector of grad.
-// The geometry is that of the logits row, as in ce_part_kernel.
-template <typename T>
-__global__ __launch_bounds__(256) void ce_mailbox_clear_kernel(const T* __restrict__ logits,
-                                                               T* __restrict__ grad, int64_t B,
-                                                               int C, int P) {
-  constexpr int VE = Elem<T>::VE;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= B * P) return;
-  const int64_t row = i / P;
-  const int q = (int)(i % P);
-  T* gp = grad + row * C;
-  const RowGeom geo = row_geom<T, kPartAlign>(logits + row * C, C);
-  const PartRange pr = part_range(geo.nb, P, q);
-  if (pr.len <= 0) return;
-  u32x4* mb = reinterpret_cast<u32x4*>(gp + geo.h + (int64_t)(pr.v0 + pr.len - 1) * VE);
-  *mb = u32x4{0u, kMailEmpty, 0u, kMailEmpty};
 }
 
 // Max / sum pair of the whole workgroup, from each thread's (c, s).  Every
@@ -166,6 +154,18 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rin, (lds_ptr_t)&stage[NL * NT + wv * 64], 16, voff,
                                                (uint32_t)(NR + NL) * NT * 16u, 0, kPolicyStream);
   }
+  // Empty this part's mailbox (two-part rows) before anything can be
+  // published into it.
+  uint64_t* const mine =
+      P == 2 ? reinterpret_cast<uint64_t*>(gp + geo.h + (int64_t)(own.v0 + own.len - 1) * VE)
+             : nullptr;
+  constexpr uint64_t kEmptyWord = (uint64_t)kMailEmpty << 32;
+  if constexpr (P == 2) {
+    if (tid == 0) {
+      __hip_atomic_store(&mine[0], kEmptyWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&mine[1], kEmptyWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   // LDS slot p of this thread (the partial slot holds nothing for threads
   // at or past NX: their vectors lie past every part's end).
   auto lds_slot = [&](int p) -> u32x4 {
@@ -238,19 +238,20 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
     const int q = 1 - part;
     if (tid == 0) {
       const PartRange pq = part_range(geo.nb, P, q);
-      uint64_t* mine = reinterpret_cast<uint64_t*>(gp + geo.h + (int64_t)(own.v0 + own.len - 1) * VE);
       uint64_t* theirs = reinterpret_cast<uint64_t*>(gp + geo.h + (int64_t)(pq.v0 + pq.len - 1) * VE);
       const uint64_t tag = (uint64_t)kMailTag << 32;
-      // Both publishes are issued without waiting for their results (each
-      // fails harmlessly if the owner has already written its gradient), so
-      // the first poll follows them at once.
-      uint64_t e0 = (uint64_t)kMailEmpty << 32, e1 = e0;
-      __hip_atomic_compare_exchange_strong(&theirs[0], &e0, tag | __builtin_bit_cast(uint32_t, c_own),
-                                           __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_compare_exchange_strong(&theirs[1], &e1, tag | __builtin_bit_cast(uint32_t, s_own),
-                                           __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t w0 = tag | __builtin_bit_cast(uint32_t, c_own);
+      const uint64_t w1 = tag | __builtin_bit_cast(uint32_t, s_own);
+      // The publishes are issued without waiting for their results, so the
+      // next poll follows them at once.
+      auto publish = [&] {
+        uint64_t e0 = kEmptyWord, e1 = kEmptyWord;
+        __hip_atomic_compare_exchange_strong(&theirs[0], &e0, w0, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_compare_exchange_strong(&theirs[1], &e1, w1, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      };
+      publish();
       int ok = 0;
       uint64_t a = 0, b = 0;
       for (int it = 0; it < spin; ++it) {
@@ -260,6 +261,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
           ok = 1;
           break;
         }
+        publish();
         __builtin_amdgcn_s_sleep(8);
       }
       mail_c = __builtin_bit_cast(float, (uint32_t)a);

@@ -125,7 +125,7 @@ def test_batch_independence():
     assert torch.equal(a[1][:8] * 32, b[1] * 8)
 
 
-@pytest.mark.parametrize("B", [1, 7, 2048, 2049, 100_000, 2_097_152, 3_000_001])
+@pytest.mark.parametrize("B", [1, 7, 2048, 2049, 8192, 16384, 16385, 100_000, 2_097_152, 3_000_001])
 def test_reduce_matches_exact_sum_of_gpu_rows(B):
     """The scalar equals the exactly rounded sum of the GPU's own per-row
     values to fp32 summation accuracy, and is bitwise reproducible."""

@@ -114,7 +114,7 @@ def test_kernels_present(device_asm):
     meta = _kernel_meta(device_asm)
     names = " ".join(meta)
     for k in ("ce_short_kernel", "ce_row_kernel", "ce_row_lds_kernel", "ce_reduce_kernel",
-              "ce_part_kernel", "ce_mailbox_clear_kernel"):
+              "ce_part_kernel"):
         assert k in names, k
 
 
