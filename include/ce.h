@@ -124,6 +124,17 @@ const char* ce_status_string(int status);
 const char* ce_version(void);
 
 /*
+ * ce_stream_copy - measurement reference, not part of the method: copies
+ * `bytes` bytes from src to dst (device pointers, 16-byte aligned, bytes a
+ * positive multiple of 16, no overlap) with the memory pattern of the
+ * row-part kernel (1024-thread workgroups, 128 KiB each as 8 slots of
+ * 16-byte non-temporal loads issued before the stores).  The benchmark
+ * reports the cross-entropy kernel's bandwidth as a share of this copy's.
+ * Stream-ordered; returns CE_OK or a negative ce_status.
+ */
+int ce_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/*
  * Kernel paths:
  *   1 short rows  - many rows per 64-lane wavefront, cross-lane DPP
  *                   reductions, no LDS (C <= 256);

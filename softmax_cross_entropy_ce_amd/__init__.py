@@ -24,7 +24,7 @@ import os
 __all__ = [
     "CEError", "lib", "fwd_grad", "fwd_grad_into", "reduce_loss", "reduce_loss_into",
     "cross_entropy", "reduce_workspace_bytes", "select_path", "force_path", "part_polls",
-    "part_counter", "version", "PATH_NAMES", "F32", "BF16",
+    "part_counter", "stream_copy", "version", "PATH_NAMES", "F32", "BF16",
 ]
 
 F32 = 0
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.ce_debug_part_polls.restype = i32
     L.ce_debug_part_counter.argtypes = [vp]
     L.ce_debug_part_counter.restype = i32
+    L.ce_stream_copy.argtypes = [vp, vp, i64, vp]
+    L.ce_stream_copy.restype = i32
     _lib = L
     return L
 
@@ -127,6 +129,18 @@ def part_counter(counter=None) -> None:
             raise ValueError("counter must be a contiguous 4-byte integer tensor")
         ptr = counter.data_ptr()
     _check(lib().ce_debug_part_counter(ptr), "ce_debug_part_counter")
+
+
+def stream_copy(src, dst) -> None:
+    """Measurement reference: copy src's bytes into dst with the library's
+    streaming copy kernel (both contiguous device tensors of equal byte
+    size, a multiple of 16)."""
+    _check_cuda(src, dst)
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst differ in size")
+    _check(lib().ce_stream_copy(src.data_ptr(), dst.data_ptr(), n, _stream_ptr(src.device)),
+           "ce_stream_copy")
 
 
 def reduce_workspace_bytes(B: int) -> int:

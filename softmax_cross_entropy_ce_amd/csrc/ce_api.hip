@@ -343,6 +343,18 @@ const char* ce_status_string(int status) {
 
 const char* ce_version(void) { return "ce_mi355x 0.1.0 gfx950"; }
 
+int ce_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (!src || !dst) return CE_ERR_NULL;
+  if (bytes <= 0 || bytes % 16) return CE_ERR_SHAPE;
+  if ((uintptr_t)src % 16 || (uintptr_t)dst % 16) return CE_ERR_ALIGN;
+  if (overlaps((uintptr_t)src, (uintptr_t)bytes, (uintptr_t)dst, (uintptr_t)bytes)) return CE_ERR_ALIAS;
+  const int64_t blocks = (bytes + ce::kCopyChunk - 1) / ce::kCopyChunk;
+  if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
+  hipLaunchKernelGGL(ce::ce_copy_kernel, dim3((unsigned)blocks), dim3(ce::kCopyThreads), 0,
+                     as_stream(stream), (const char*)src, (char*)dst, bytes);
+  return launched();
+}
+
 int ce_select_path(int64_t C, int dtype) {
   if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
   if (C <= 0 || C > CE_MAX_C) return CE_ERR_SHAPE;

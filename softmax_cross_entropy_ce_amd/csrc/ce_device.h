@@ -100,6 +100,12 @@ struct Elem<float> {
   __device__ static __forceinline__ void store1(float* p, float g) {
     __builtin_nontemporal_store(g, p);
   }
+  // the vector with element j (0..3) replaced by -inf
+  __device__ static __forceinline__ u32x4 kill(u32x4 v, int j) {
+    constexpr unsigned kNinf = 0xFF800000u;
+    return u32x4{j == 0 ? kNinf : v.x, j == 1 ? kNinf : v.y, j == 2 ? kNinf : v.z,
+                 j == 3 ? kNinf : v.w};
+  }
 };
 
 __device__ __forceinline__ float bf16lo(unsigned d) { return __builtin_bit_cast(float, d << 16); }
@@ -132,6 +138,14 @@ struct Elem<__bf16> {
     unsigned d = pack_bf16x2(g, 0.f);
     __builtin_nontemporal_store((unsigned short)(d & 0xffffu),
                                 reinterpret_cast<unsigned short*>(p));
+  }
+  // the vector with element j (0..7) replaced by -inf (bf16 0xFF80)
+  __device__ static __forceinline__ u32x4 kill(u32x4 v, int j) {
+    const int d = j >> 1;
+    const unsigned keep = (j & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    const unsigned ninf = (j & 1) ? 0xFF800000u : 0x0000FF80u;
+    return u32x4{d == 0 ? (v.x & keep) | ninf : v.x, d == 1 ? (v.y & keep) | ninf : v.y,
+                 d == 2 ? (v.z & keep) | ninf : v.z, d == 3 ? (v.w & keep) | ninf : v.w};
   }
 };
 
@@ -236,15 +250,22 @@ __device__ __forceinline__ float max_of(const float (&a)[N]) {
 }
 
 // Fold N new elements into (c, s).  vmax is their maximum (taken before any
-// element was masked out of the sum); masked elements hold -inf.
+// element was masked out of the sum); masked elements hold -inf.  e
+// receives each element's term 2^(f log2e - c_new).
 template <int N>
-__device__ __forceinline__ void online_fold(float& c, float& s, float vmax, const float (&f)[N]) {
+__device__ __forceinline__ void online_fold_e(float& c, float& s, float vmax, const float (&f)[N],
+                                              float (&e)[N]) {
   const float cn = __builtin_fmaxf(c, vmax * kLog2e);
-  float e[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) e[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cn));
   s = s * exp2_hw(c - cn) + tree_sum(e);
   c = cn;
+}
+
+template <int N>
+__device__ __forceinline__ void online_fold(float& c, float& s, float vmax, const float (&f)[N]) {
+  float e[N];
+  online_fold_e(c, s, vmax, f, e);
 }
 
 }  // namespace ce

@@ -700,4 +700,34 @@ __global__ __launch_bounds__(kReduceThreads) void ce_reduce_kernel(const float* 
   if (threadIdx.x == 0) out[blockIdx.x] = tot;
 }
 
+// ===========================================================================
+// Streaming copy with the memory pattern of the row-part kernel (1024
+// threads, 8 slots of 16-byte non-temporal loads issued before the stores,
+// 128 KiB per workgroup): the achievable-bandwidth reference that the
+// benchmark reports beside the cross-entropy kernel.  Not part of the
+// method.
+// ===========================================================================
+constexpr int kCopyThreads = 1024;
+constexpr int kCopySlots = 8;
+constexpr int64_t kCopyChunk = (int64_t)kCopyThreads * kCopySlots * 16;
+
+__global__ __launch_bounds__(kCopyThreads) void ce_copy_kernel(const char* __restrict__ src,
+                                                               char* __restrict__ dst,
+                                                               int64_t bytes) {
+  const int64_t base = (int64_t)blockIdx.x * kCopyChunk;
+  if (base >= bytes) return;
+  const uint32_t n = (uint32_t)(bytes - base < kCopyChunk ? bytes - base : kCopyChunk);
+  const rsrc_t ri = make_rsrc(src + base, n), ro = make_rsrc(dst + base, n);
+  const uint32_t voff = threadIdx.x * 16u;
+  u32x4 v[kCopySlots];
+#pragma unroll
+  for (int k = 0; k < kCopySlots; ++k)
+    v[k] = bload128<kPolicyStream>(ri, voff, (uint32_t)k * kCopyThreads * 16u);
+#pragma unroll
+  for (int k = 0; k < kCopySlots; ++k) asm volatile("" : "+v"(v[k]));
+#pragma unroll
+  for (int k = 0; k < kCopySlots; ++k)
+    bstore128<kPolicyStream>(v[k], ro, voff, (uint32_t)k * kCopyThreads * 16u);
+}
+
 }  // namespace ce

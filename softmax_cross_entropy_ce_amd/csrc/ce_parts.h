@@ -193,25 +193,42 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   const float xs_raw = bload_elem<T>(rrow, (uint32_t)(xe >= 0 ? xe : C) * ES);
   const float zt_raw = bload_elem<T>(rrow, (uint32_t)(valid ? t : C) * ES);
 
-  // Fold slot k of part q (this thread's vector k*NT + tid of the part).
-  // Slots past the part's end are skipped as a whole (uniform); lanes past
-  // it hold -inf.  The target element is left out of the sum.
-  auto fold_slot = [&](const PartRange& pr, int k, u32x4 w, float& c, float& s) {
-    const int base = k * NT;
-    if (base >= pr.len) return;
-    float f[VE];
+  // The target element.  The thread whose vectors hold it sets it to -inf
+  // in the loaded data, once, so no slot needs per-element target code; the
+  // part folds z_t into its running max after its slots (the target stays
+  // out of the sum), and the owning thread stores g_t after its vector
+  // stores.  Per part q: whether this wave holds the target's vector, and
+  // the slot that holds it for the owning thread (-1 for the others).
+  struct TargetIn {
+    bool wave;
+    int k;
+  };
+  auto target_in = [&](const PartRange& pr) -> TargetIn {
+    const bool in = t_body && tvec >= pr.v0 && tvec < pr.v0 + pr.len;
+    const bool mine = in && (tvec - pr.v0) % NT == tid;
+    return TargetIn{__builtin_amdgcn_ballot_w64(mine) != 0, mine ? (tvec - pr.v0) / NT : -1};
+  };
+  const TargetIn tin = target_in(own);
+
+  // Slot k of part q (this thread's vector k*NT + tid of the part) as
+  // floats.  Slots past the part's end are skipped as a whole (uniform);
+  // lanes past it hold -inf.
+  auto slot_values = [&](const PartRange& pr, const TargetIn& ti, int k, u32x4 w,
+                         float (&f)[VE]) {
+    if (ti.wave && ti.k == k) w = E::kill(w, tj);
     E::unpack(w, f);
-    if (base + NT > pr.len) {
-      const bool ok = tid < pr.len - base;
+    if (k * NT + NT > pr.len) {
+      const bool ok = tid < pr.len - k * NT;
 #pragma unroll
       for (int i = 0; i < VE; ++i) f[i] = ok ? f[i] : kNegInf;
     }
-    const float vm = max_of(f);
-    if (pr.v0 + base + tid == tvec) {
-#pragma unroll
-      for (int i = 0; i < VE; ++i) f[i] = (i == tj) ? kNegInf : f[i];
-    }
-    online_fold(c, s, vm, f);
+  };
+  auto fold_slot = [&](const PartRange& pr, const TargetIn& ti, int k, u32x4 w, float& c,
+                       float& s) {
+    if (k * NT >= pr.len) return;
+    float f[VE];
+    slot_values(pr, ti, k, w, f);
+    online_fold(c, s, max_of(f), f);
   };
   auto fold_edge = [&](int e, float x, float& c, float& s) {
     if (e >= 0) {
@@ -219,17 +236,42 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       online_fold(c, s, x, one);
     }
   };
+  // z_t into the running max of the part whose body holds it (max only)
+  auto fold_target_max = [&](const PartRange& pr, float zt_, float& c, float& s) {
+    if (t_body && tvec >= pr.v0 && tvec < pr.v0 + pr.len) {
+      const float none[1] = {kNegInf};
+      online_fold(c, s, zt_, none);
+    }
+  };
 
-  // Phase B: this part's pair.
+  // Phase B: this part's pair.  For fp32, the register slots keep each
+  // element's term 2^(z log2e - c_k) in place of z, with c_k the running max
+  // after slot k, so that the gradient needs one multiply per element.
+  constexpr bool kKeepTerms = sizeof(T) == 4;
+  float ck[NR];
   float c = kLowest, s = 0.f;
 #pragma unroll
-  for (int k = 0; k < NR; ++k) fold_slot(own, k, v[k], c, s);
+  for (int k = 0; k < NR; ++k) {
+    ck[k] = c;
+    if (k * NT >= own.len) continue;
+    float f[VE];
+    slot_values(own, tin, k, v[k], f);
+    if constexpr (kKeepTerms) {
+      float e[VE];
+      online_fold_e(c, s, max_of(f), f, e);
+      ck[k] = c;
+      v[k] = as_u32(f32x4{e[0], e[1], e[2], e[3]});
+    } else {
+      online_fold(c, s, max_of(f), f);
+    }
+  }
   wait_vmcnt<0>();  // LDS slots, edge and target loads
 #pragma unroll
-  for (int p = 0; p < NLS; ++p) fold_slot(own, NR + p, lds_slot(p), c, s);
+  for (int p = 0; p < NLS; ++p) fold_slot(own, tin, NR + p, lds_slot(p), c, s);
   const float xs = xe >= 0 ? xs_raw : kNegInf;
   const float zt = valid ? zt_raw : 0.f;
   fold_edge(xe, xs, c, s);
+  fold_target_max(own, zt, c, s);
   float c_own, s_own;
   wg_pair<NW>(c, s, red_c, red_s, lane, wv, c_own, s_own);
 
@@ -278,15 +320,17 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       // workgroup reduction as part q runs itself.
       const PartRange pq = part_range(geo.nb, P, q);
       const rsrc_t rq = make_rsrc(rp + geo.h + pq.v0 * VE, (uint32_t)pq.len * 16u);
+      const TargetIn tq = target_in(pq);
       float cq = kLowest, sq = 0.f;
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
         const u32x4 w = bload128<kPolicyStream>(rq, voff, (uint32_t)k * NT * 16u);
-        fold_slot(pq, k, w, cq, sq);
+        fold_slot(pq, tq, k, w, cq, sq);
       }
       const int xq = edge_elem(q);
       const float xqv = bload_elem<T>(rrow, (uint32_t)(xq >= 0 ? xq : C) * ES);
       fold_edge(xq, xq >= 0 ? xqv : kNegInf, cq, sq);
+      fold_target_max(pq, zt, cq, sq);
       wg_pair<NW>(cq, sq, red_c, red_s, lane, wv, c_oth, s_oth);
     }
   }
@@ -308,22 +352,27 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
 
   // Phase C: the gradient of this part from registers and LDS.
   auto write_slot = [&](int k, u32x4 w) {
-    const int base = k * NT;
-    if (base >= own.len) return;
+    if (k * NT >= own.len) return;
     float f[VE], g[VE];
     E::unpack(w, f);
 #pragma unroll
     for (int i = 0; i < VE; ++i) g[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
-    if (own.v0 + base + tid == tvec) {
-#pragma unroll
-      for (int i = 0; i < VE; ++i) g[i] = (i == tj) ? rr.gt : g[i];
-    }
     bstore128<kPolicyStream>(E::pack(g), rout, voff, (uint32_t)k * NT * 16u);
   };
 #pragma unroll
   for (int k = 0; k < NR; ++k) asm volatile("" : "+v"(v[k]));
 #pragma unroll
-  for (int k = 0; k < NR; ++k) write_slot(k, v[k]);
+  for (int k = 0; k < NR; ++k) {
+    if constexpr (kKeepTerms) {
+      if (k * NT >= own.len) continue;
+      const float factor = exp2_hw(ck[k] - cg) * rr.scale;
+      const f32x4 e = as_f32(v[k]);
+      const f32x4 g = {e.x * factor, e.y * factor, e.z * factor, e.w * factor};
+      bstore128<kPolicyStream>(as_u32(g), rout, voff, (uint32_t)k * NT * 16u);
+    } else {
+      write_slot(k, v[k]);
+    }
+  }
 #pragma unroll
   for (int p = 0; p < NLS; ++p) {
     if (p < NL || tid < NX) write_slot(NR + p, lds_slot(p));
@@ -332,6 +381,9 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
     const float g = (xe == t) ? rr.gt : exp2_hw(__builtin_fmaf(xs, kLog2e, -cg)) * rr.scale;
     E::store1(gp + xe, g);
   }
+  // the target's gradient, over the value its vector store wrote there (the
+  // same thread, the same address, later in program order)
+  if (tin.k >= 0) E::store1(gp + geo.h + (int64_t)tvec * VE + tj, rr.gt);
 }
 
 }  // namespace ce

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
     assert names == sorted(["ce_fwd_grad", "ce_reduce_workspace_bytes", "ce_reduce_loss",
                             "ce_status_string", "ce_version", "ce_select_path",
                             "ce_debug_force_path", "ce_debug_part_polls",
-                            "ce_debug_part_counter"])
+                            "ce_debug_part_counter", "ce_stream_copy"])
     for n in names:
         assert hasattr(L_, n), n
 
@@ -166,3 +166,13 @@ def test_part_hooks_round_trip():
     assert prev == 64
     assert ce.lib().ce_debug_part_polls(-1) == PATH
     ce.part_counter(None)
+
+
+def test_stream_copy_validation():
+    cp = ce.lib().ce_stream_copy
+    assert cp(None, G, 16, None) == NULL
+    assert cp(Z, None, 16, None) == NULL
+    assert cp(Z, G, 0, None) == SHAPE
+    assert cp(Z, G, 24, None) == SHAPE      # not a multiple of 16
+    assert cp(Z + 8, G, 16, None) == ALIGN
+    assert cp(Z, Z + 16, 64, None) == ALIAS

@@ -171,3 +171,18 @@ def test_invalid_target_does_not_disturb_other_rows():
     assert torch.equal(a[0][keep], b[0][keep])
     assert torch.isnan(b[0][5]).all() and torch.isnan(b[0][6]).all()
     assert math.isnan(b[2].item())
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 131072, 131088, (1 << 20) + 48, 3 * 131072 - 16])
+def test_stream_copy_is_exact(nbytes):
+    """The measurement reference copy moves every byte and nothing else."""
+    import torch
+    import softmax_cross_entropy_ce_amd as ce
+    g = torch.Generator().manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g).cuda()
+    buf = torch.full((nbytes + 4096,), 0xA5, dtype=torch.uint8, device=src.device)
+    dst = buf[2048:2048 + nbytes]
+    ce.stream_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    assert (buf[:2048] == 0xA5).all() and (buf[2048 + nbytes:] == 0xA5).all()
