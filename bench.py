@@ -140,6 +140,40 @@ def copy_calibration(zd, grad, reps: int = 20) -> dict:
             "runtime_copy_GBps": round(nbytes / (ms_rt * 1e-3) / 1e9, 2)}
 
 
+def backward_scale(zd, td, grad, loss_rows, reps: int = 20) -> dict:
+    """The backward of the fused loss on the workload's gradient: the
+    broadcast scale ce_scale_grad by a device scalar (0.5: every element
+    read and written; 1: the no-op early exit), and the forward with the
+    scale folded in (ce_fwd_grad_scaled)."""
+    import torch
+    import softmax_cross_entropy_ce_amd as ce
+    stream = torch.cuda.current_stream(zd.device)
+    half = torch.tensor([0.5], dtype=torch.float32, device=zd.device)
+    one = torch.tensor([1.0], dtype=torch.float32, device=zd.device)
+
+    def timed(fn):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return statistics.median([a.elapsed_time(b) for a, b in evs])
+
+    nbytes = 2 * grad.numel() * grad.element_size()
+    ms_half = timed(lambda: ce.scale_grad_(grad, half))
+    ms_one = timed(lambda: ce.scale_grad_(grad, one))
+    ms_fused = timed(lambda: ce.fwd_grad_scaled_into(zd, td, grad, loss_rows, half))
+    return {"scale_grad_ms": round(ms_half, 5),
+            "scale_grad_GBps": round(nbytes / (ms_half * 1e-3) / 1e9, 2),
+            "scale_grad_one_ms": round(ms_one, 5),
+            "fwd_grad_scaled_ms": round(ms_fused, 5)}
+
+
 def run_copy(args) -> None:
     """Plain device-to-device copy of a known size (counter calibration)."""
     import torch
@@ -251,6 +285,7 @@ def main() -> None:
     qs = statistics.quantiles(fwd_ms, n=10)
     achieved = fwd_bytes / (fwd_avg * 1e-3) / 1e9
     cal = copy_calibration(zd, grad)
+    bwd = backward_scale(zd, td, grad, loss_rows)
     cal["fwd_grad_pct_of_copy"] = round(100 * achieved / cal["GBps"], 2)
     rec = {
         "metric": "fused CE fwd+grad: achieved HBM GB/s (% of peak) and rows/sec at C=128256 bf16"
@@ -281,6 +316,7 @@ def main() -> None:
                      "algorithmic_bytes_per_launch": fwd_bytes,
                      "traffic": traffic_for(w.name)},
         "copy_calibration": cal,
+        "backward_scale": bwd,
     }
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f} s")

@@ -92,6 +92,42 @@ int ce_fwd_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C
                 int dtype, void* grad_out, float* loss_out, void* stream);
 
 /*
+ * ce_fwd_grad_scaled - ce_fwd_grad with the gradient multiplied by an
+ * upstream gradient of the loss that is known before the forward pass
+ * (for example a loss-scaling factor): grad_out = (softmax - onehot) / B *
+ * (*grad_scale), at no extra memory traffic.  loss_out is not scaled.
+ *
+ * Defined by: rumus project page, milestone M7a (the backward of the fused
+ * loss is a broadcast scale of the gradient formed in the forward).
+ *
+ *   grad_scale  DEVICE pointer to one float32, read by the kernels in
+ *               stream order; 4-byte aligned; must not be NULL.
+ *   other arguments, layout and errors as ce_fwd_grad.
+ */
+int ce_fwd_grad_scaled(const void* logits, const int32_t* targets, int64_t B, int64_t C,
+                       int dtype, void* grad_out, float* loss_out, const float* grad_scale,
+                       void* stream);
+
+/*
+ * ce_scale_grad - the backward of the fused loss: grad *= *scale in place,
+ * for the n elements of a gradient that ce_fwd_grad produced and the
+ * upstream gradient `scale` of the loss (a DEVICE float32 scalar, read in
+ * stream order, so the host never reads it).  When *scale is exactly 1 the
+ * kernel returns without touching grad (the broadcast scale of the common
+ * `loss.backward()` moves no gradient bytes).  bf16 values are scaled in
+ * float32 and rounded to nearest even.
+ *
+ * Defined by: rumus project page, milestone M7a (the backward of the fused
+ * loss is a zero-copy broadcast scale of the gradient formed in the
+ * forward).
+ *
+ *   grad   [n] dtype, element-aligned, DEVICE pointer, scaled in place.
+ *   n      >= 1 elements.
+ *   scale  DEVICE pointer to one float32, 4-byte aligned, not inside grad.
+ */
+int ce_scale_grad(void* grad, int64_t n, int dtype, const float* scale, void* stream);
+
+/*
  * ce_reduce_workspace_bytes - device scratch that ce_reduce_loss needs for
  * B per-row losses (0 when one workgroup sums them directly).
  */

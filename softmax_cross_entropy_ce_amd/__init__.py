@@ -23,8 +23,9 @@ import os
 
 __all__ = [
     "CEError", "lib", "fwd_grad", "fwd_grad_into", "reduce_loss", "reduce_loss_into",
-    "cross_entropy", "reduce_workspace_bytes", "select_path", "force_path", "part_polls",
-    "part_counter", "stream_copy", "version", "PATH_NAMES", "F32", "BF16",
+    "cross_entropy", "cross_entropy_loss", "fwd_grad_scaled_into", "scale_grad_",
+    "reduce_workspace_bytes", "select_path", "force_path", "part_polls", "part_counter",
+    "stream_copy", "version", "PATH_NAMES", "F32", "BF16",
 ]
 
 F32 = 0
@@ -77,6 +78,10 @@ def lib() -> ctypes.CDLL:
     L.ce_debug_part_counter.restype = i32
     L.ce_stream_copy.argtypes = [vp, vp, i64, vp]
     L.ce_stream_copy.restype = i32
+    L.ce_fwd_grad_scaled.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp, vp]
+    L.ce_fwd_grad_scaled.restype = i32
+    L.ce_scale_grad.argtypes = [vp, i64, i32, vp, vp]
+    L.ce_scale_grad.restype = i32
     _lib = L
     return L
 
@@ -177,8 +182,7 @@ def _check_cuda(*ts) -> None:
         raise ValueError("tensors must be on one device")
 
 
-def fwd_grad_into(logits, targets, grad, loss_rows) -> None:
-    """Write the gradient and the per-row losses into preallocated tensors."""
+def _check_fwd_args(logits, targets, grad, loss_rows):
     torch = _torch()
     _check_cuda(logits, targets, grad, loss_rows)
     if logits.dim() != 2:
@@ -190,9 +194,44 @@ def fwd_grad_into(logits, targets, grad, loss_rows) -> None:
         raise TypeError("grad must match logits in dtype and shape")
     if loss_rows.dtype != torch.float32 or loss_rows.shape != (B,):
         raise TypeError("loss_rows must be float32 of shape [B]")
+    return B, C
+
+
+def _check_scalar(x, what: str):
+    torch = _torch()
+    _check_cuda(x)
+    if x.dtype != torch.float32 or x.numel() != 1:
+        raise TypeError(f"{what} must be one float32 on the device")
+
+
+def fwd_grad_into(logits, targets, grad, loss_rows) -> None:
+    """Write the gradient and the per-row losses into preallocated tensors."""
+    B, C = _check_fwd_args(logits, targets, grad, loss_rows)
     st = lib().ce_fwd_grad(logits.data_ptr(), targets.data_ptr(), B, C, _dtype_code(logits),
                            grad.data_ptr(), loss_rows.data_ptr(), _stream_ptr(logits.device))
     _check(st, "ce_fwd_grad")
+
+
+def fwd_grad_scaled_into(logits, targets, grad, loss_rows, grad_scale) -> None:
+    """As fwd_grad_into, with the gradient multiplied by the device scalar
+    grad_scale (one float32) in the same pass; loss_rows are not scaled."""
+    B, C = _check_fwd_args(logits, targets, grad, loss_rows)
+    _check_scalar(grad_scale, "grad_scale")
+    st = lib().ce_fwd_grad_scaled(logits.data_ptr(), targets.data_ptr(), B, C,
+                                  _dtype_code(logits), grad.data_ptr(), loss_rows.data_ptr(),
+                                  grad_scale.data_ptr(), _stream_ptr(logits.device))
+    _check(st, "ce_fwd_grad_scaled")
+
+
+def scale_grad_(grad, scale) -> None:
+    """The backward broadcast-scale: grad *= scale in place, scale a device
+    float32 scalar (nothing is read back to the host; a scale of exactly 1
+    leaves grad untouched without moving its bytes)."""
+    _check_cuda(grad)
+    _check_scalar(scale, "scale")
+    st = lib().ce_scale_grad(grad.data_ptr(), grad.numel(), _dtype_code(grad), scale.data_ptr(),
+                             _stream_ptr(grad.device))
+    _check(st, "ce_scale_grad")
 
 
 def fwd_grad(logits, targets):
@@ -235,3 +274,44 @@ def cross_entropy(logits, targets):
     the gradient with respect to the logits."""
     grad, loss_rows = fwd_grad(logits, targets)
     return reduce_loss(loss_rows), grad
+
+
+_autograd_fn = None
+
+
+def _function():
+    global _autograd_fn
+    if _autograd_fn is not None:
+        return _autograd_fn
+    torch = _torch()
+
+    class CrossEntropyFunction(torch.autograd.Function):
+        """Forward: the batch-mean loss and, in the same pass, its gradient
+        (ce_fwd_grad + ce_reduce_loss).  Backward: that gradient scaled in
+        place by the upstream gradient (ce_scale_grad), a device scalar, so
+        there is no host synchronisation; one backward per forward."""
+
+        @staticmethod
+        def forward(ctx, logits, targets):
+            grad, loss_rows = fwd_grad(logits.detach(), targets)
+            ctx.grad = grad
+            return reduce_loss(loss_rows)
+
+        @staticmethod
+        def backward(ctx, grad_output):
+            grad = ctx.grad
+            if grad is None:
+                raise RuntimeError("cross_entropy_loss: backward can run once per forward")
+            ctx.grad = None
+            scale_grad_(grad, grad_output.detach().to(torch.float32).reshape(1).contiguous())
+            return grad, None
+
+    _autograd_fn = CrossEntropyFunction
+    return _autograd_fn
+
+
+def cross_entropy_loss(logits, targets):
+    """The batch-mean fused cross-entropy as a differentiable 0-d tensor:
+    ``loss.backward()`` gives ``logits.grad = (softmax - onehot) / B`` times
+    the upstream gradient, from the gradient formed in the forward pass."""
+    return _function().apply(logits, targets)

@@ -71,26 +71,26 @@ int launched() { return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_LAUNCH;
 
 // ------------------------------------------------------------------ path 1
 template <typename T, int S, int EPL, int VW>
-int launch_short_cfg(const T* z, const int32_t* t, int64_t B, int C, float invB, T* g, float* l,
+int launch_short_cfg(const T* z, const int32_t* t, int64_t B, int C, ce::RowScale rs, T* g, float* l,
                      hipStream_t st) {
   constexpr int rpb = ce::kShortThreads / S;
   const int64_t blocks = (B + rpb - 1) / rpb;
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
   hipLaunchKernelGGL((ce::ce_short_kernel<T, S, EPL, VW>), dim3((unsigned)blocks),
-                     dim3(ce::kShortThreads), 0, st, z, t, B, C, invB, g, l);
+                     dim3(ce::kShortThreads), 0, st, z, t, B, C, rs, g, l);
   return launched();
 }
 
 template <typename T, int S, int EPL>
-int launch_short_vw(int vw, const T* z, const int32_t* t, int64_t B, int C, float invB, T* g,
+int launch_short_vw(int vw, const T* z, const int32_t* t, int64_t B, int C, ce::RowScale rs, T* g,
                     float* l, hipStream_t st) {
   switch (vw) {
-    case 1: return launch_short_cfg<T, S, EPL, 1>(z, t, B, C, invB, g, l, st);
-    case 2: return launch_short_cfg<T, S, EPL, 2>(z, t, B, C, invB, g, l, st);
-    case 4: return launch_short_cfg<T, S, EPL, 4>(z, t, B, C, invB, g, l, st);
+    case 1: return launch_short_cfg<T, S, EPL, 1>(z, t, B, C, rs, g, l, st);
+    case 2: return launch_short_cfg<T, S, EPL, 2>(z, t, B, C, rs, g, l, st);
+    case 4: return launch_short_cfg<T, S, EPL, 4>(z, t, B, C, rs, g, l, st);
     case 8:
       if constexpr (sizeof(T) == 2 && EPL >= 8)
-        return launch_short_cfg<T, S, EPL, 8>(z, t, B, C, invB, g, l, st);
+        return launch_short_cfg<T, S, EPL, 8>(z, t, B, C, rs, g, l, st);
       return CE_ERR_PATH;
     default: return CE_ERR_PATH;
   }
@@ -111,23 +111,23 @@ int short_vw(int64_t C, int es, uintptr_t zaddr, uintptr_t gaddr, int epl) {
 // elements, more only at S = 16).  Lanes of a row read adjacent vectors,
 // so a load instruction covers 64/S consecutive rows.
 template <typename T>
-int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g, float* l,
+int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g, float* l,
                  hipStream_t st) {
   if (C > kShortMaxC) return CE_ERR_PATH;
   constexpr int es = sizeof(T);
   constexpr int E16 = 16 / es;  // elements in 16 bytes
   const int c = (int)C;
   auto vw = [&](int epl) { return short_vw(C, es, (uintptr_t)z, (uintptr_t)g, epl); };
-  if (C <= E16) return launch_short_vw<T, 1, E16>(vw(E16), z, t, B, c, invB, g, l, st);
-  if (C <= 2 * E16) return launch_short_vw<T, 2, E16>(vw(E16), z, t, B, c, invB, g, l, st);
-  if (C <= 4 * E16) return launch_short_vw<T, 4, E16>(vw(E16), z, t, B, c, invB, g, l, st);
-  if (C <= 8 * E16) return launch_short_vw<T, 8, E16>(vw(E16), z, t, B, c, invB, g, l, st);
-  if (C <= 16 * E16) return launch_short_vw<T, 16, E16>(vw(E16), z, t, B, c, invB, g, l, st);
+  if (C <= E16) return launch_short_vw<T, 1, E16>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= 2 * E16) return launch_short_vw<T, 2, E16>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= 4 * E16) return launch_short_vw<T, 4, E16>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= 8 * E16) return launch_short_vw<T, 8, E16>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= 16 * E16) return launch_short_vw<T, 16, E16>(vw(E16), z, t, B, c, rs, g, l, st);
   if constexpr (E16 < 16) {
-    if (C <= 32 * E16) return launch_short_vw<T, 16, 2 * E16>(vw(2 * E16), z, t, B, c, invB, g, l, st);
+    if (C <= 32 * E16) return launch_short_vw<T, 16, 2 * E16>(vw(2 * E16), z, t, B, c, rs, g, l, st);
   }
   if constexpr (E16 < 8) {
-    if (C <= 64 * E16) return launch_short_vw<T, 16, 4 * E16>(vw(4 * E16), z, t, B, c, invB, g, l, st);
+    if (C <= 64 * E16) return launch_short_vw<T, 16, 4 * E16>(vw(4 * E16), z, t, B, c, rs, g, l, st);
   }
   return CE_ERR_PATH;
 }
@@ -148,13 +148,13 @@ int resident_blocks(const void* kernel, int nt) {
 }
 
 template <typename T, int NT, int NV>
-int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g,
+int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
                    float* l, hipStream_t st) {
   auto kern = ce::ce_row_kernel<T, NT, NV>;
   const int res = resident_blocks(reinterpret_cast<const void*>(kern), NT);
   if (res < 1) return CE_ERR_LAUNCH;
   const int64_t grid = B < res ? B : res;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), 0, st, z, t, B, (int)C, invB, g, l);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), 0, st, z, t, B, (int)C, rs, g, l);
   return launched();
 }
 
@@ -163,21 +163,21 @@ int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, float inv
 constexpr int kLdsPrefetchSlots = 9;  // 9 x 16 KB of the 160 KB of LDS
 
 template <typename T>
-int launch_row_lds(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g,
+int launch_row_lds(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
                    float* l, hipStream_t st) {
   auto kern = ce::ce_row_lds_kernel<T, 16, kLdsPrefetchSlots>;
   const int res = resident_blocks(reinterpret_cast<const void*>(kern), 1024);
   if (res < 1) return CE_ERR_LAUNCH;
   const int64_t grid = B < res ? B : res;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(1024), 0, st, z, t, B, (int)C, invB, g, l);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(1024), 0, st, z, t, B, (int)C, rs, g, l);
   return launched();
 }
 
 template <typename T>
-int launch_row(RowCfg cfg, const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g,
+int launch_row(RowCfg cfg, const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
                float* l, hipStream_t st) {
 #define CE_ROW_CASE(NT_, NV_) \
-  if (cfg.nt == NT_ && cfg.nv == NV_) return launch_row_cfg<T, NT_, NV_>(z, t, B, C, invB, g, l, st);
+  if (cfg.nt == NT_ && cfg.nv == NV_) return launch_row_cfg<T, NT_, NV_>(z, t, B, C, rs, g, l, st);
   CE_ROW_CASE(64, 1)
   CE_ROW_CASE(64, 2)
   CE_ROW_CASE(64, 4)
@@ -205,48 +205,48 @@ RowCfg resident_cfg(int64_t C, int es, bool* ok) {
 
 // ---------------------------------------------------------------- path 4
 template <typename T, int P, int NT, int NR, int NL, int NXW>
-int launch_parts_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g,
+int launch_parts_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
                      float* l, hipStream_t st) {
   const int64_t blocks = P * ((B + 7) / 8 * 8);
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
   hipLaunchKernelGGL((ce::ce_part_kernel<T, P, NT, NR, NL, NXW>), dim3((unsigned)blocks), dim3(NT),
-                     0, st, z, t, B, (int)C, invB, g, l,
+                     0, st, z, t, B, (int)C, rs, g, l,
                      g_part_polls.load(std::memory_order_relaxed),
                      g_part_counter.load(std::memory_order_relaxed));
   return launched();
 }
 
 template <typename T>
-int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, float invB, T* g, float* l,
+int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g, float* l,
                  hipStream_t st) {
   const int64_t nb = body_vectors_max(C, sizeof(T));
-  if (nb <= kPartsOneSmall) return launch_parts_cfg<T, 1, 1024, 4, 0, 0>(z, t, B, C, invB, g, l, st);
-  if (nb <= kPartsOne) return launch_parts_cfg<T, 1, 1024, 8, 2, 0>(z, t, B, C, invB, g, l, st);
-  if (nb <= kPartsTwoRegs) return launch_parts_cfg<T, 2, 1024, 8, 0, 0>(z, t, B, C, invB, g, l, st);
-  if (nb <= kPartsTwo) return launch_parts_cfg<T, 2, 1024, 8, 4, 0>(z, t, B, C, invB, g, l, st);
+  if (nb <= kPartsOneSmall) return launch_parts_cfg<T, 1, 1024, 4, 0, 0>(z, t, B, C, rs, g, l, st);
+  if (nb <= kPartsOne) return launch_parts_cfg<T, 1, 1024, 8, 2, 0>(z, t, B, C, rs, g, l, st);
+  if (nb <= kPartsTwoRegs) return launch_parts_cfg<T, 2, 1024, 8, 0, 0>(z, t, B, C, rs, g, l, st);
+  if (nb <= kPartsTwo) return launch_parts_cfg<T, 2, 1024, 8, 4, 0>(z, t, B, C, rs, g, l, st);
   return CE_ERR_PATH;
 }
 
 template <typename T>
 int fwd_grad_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g, float* l,
-                   hipStream_t st) {
-  const float invB = 1.0f / (float)B;
+                   const float* gmul, hipStream_t st) {
+  const ce::RowScale rs{1.0f / (float)B, gmul};
   switch (path) {
     case kPathShort:
-      return launch_short<T>(z, t, B, C, invB, g, l, st);
+      return launch_short<T>(z, t, B, C, rs, g, l, st);
     case kPathResident: {
       bool ok = false;
       const RowCfg cfg = resident_cfg(C, sizeof(T), &ok);
       if (!ok) return CE_ERR_PATH;
-      if (cfg.nt == 1024 && cfg.nv == 16) return launch_row_lds<T>(z, t, B, C, invB, g, l, st);
-      return launch_row<T>(cfg, z, t, B, C, invB, g, l, st);
+      if (cfg.nt == 1024 && cfg.nv == 16) return launch_row_lds<T>(z, t, B, C, rs, g, l, st);
+      return launch_row<T>(cfg, z, t, B, C, rs, g, l, st);
     }
     case kPathLong: {
       const bool forced = g_force_path.load(std::memory_order_relaxed) == kPathLong;
-      return launch_row<T>(forced ? kLongTestCfg : kLongCfg, z, t, B, C, invB, g, l, st);
+      return launch_row<T>(forced ? kLongTestCfg : kLongCfg, z, t, B, C, rs, g, l, st);
     }
     case kPathParts:
-      return launch_parts<T>(z, t, B, C, invB, g, l, st);
+      return launch_parts<T>(z, t, B, C, rs, g, l, st);
     default:
       return CE_ERR_PATH;
   }
@@ -273,14 +273,19 @@ int64_t reduce_blocks(int64_t B) { return (B + reduce_chunk(B) - 1) / reduce_chu
 
 extern "C" {
 
-int ce_fwd_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
-                void* grad_out, float* loss_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int fwd_grad_impl(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
+                  void* grad_out, float* loss_out, const float* gmul, void* stream) {
   if (!logits || !targets || !grad_out || !loss_out) return CE_ERR_NULL;
   if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
   if (B <= 0 || C <= 0 || B > 0x7fffffffLL || C > CE_MAX_C) return CE_ERR_SHAPE;
   const int es = elem_size(dtype);
   const uintptr_t z = (uintptr_t)logits, g = (uintptr_t)grad_out;
   if (z % es || g % es || (uintptr_t)targets % 4 || (uintptr_t)loss_out % 4) return CE_ERR_ALIGN;
+  if (gmul && (uintptr_t)gmul % 4) return CE_ERR_ALIGN;
   if ((z > g ? z - g : g - z) % 16) return CE_ERR_ALIGN;
   if ((uint64_t)B > UINT64_MAX / ((uint64_t)C * es)) return CE_ERR_SHAPE;
   const uintptr_t nbytes = (uintptr_t)B * (uintptr_t)C * es;
@@ -291,9 +296,49 @@ int ce_fwd_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C
   const hipStream_t st = as_stream(stream);
   if (dtype == CE_F32)
     return fwd_grad_typed<float>(path, (const float*)logits, targets, B, C, (float*)grad_out,
-                                 loss_out, st);
+                                 loss_out, gmul, st);
   return fwd_grad_typed<__bf16>(path, (const __bf16*)logits, targets, B, C, (__bf16*)grad_out,
-                                loss_out, st);
+                                loss_out, gmul, st);
+}
+
+template <typename T>
+int launch_scale(T* g, int64_t n, const float* scale, hipStream_t st) {
+  constexpr int64_t chunk = (int64_t)ce::kScaleThreads * ce::kScaleSlots;
+  const int64_t nb = n / (16 / (int64_t)sizeof(T)) + 1;
+  const int64_t blocks = (nb + chunk - 1) / chunk;
+  if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
+  hipLaunchKernelGGL(ce::ce_scale_kernel<T>, dim3((unsigned)blocks), dim3(ce::kScaleThreads), 0, st,
+                     g, n, scale);
+  return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ce_fwd_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
+                void* grad_out, float* loss_out, void* stream) {
+  return fwd_grad_impl(logits, targets, B, C, dtype, grad_out, loss_out, nullptr, stream);
+}
+
+int ce_fwd_grad_scaled(const void* logits, const int32_t* targets, int64_t B, int64_t C,
+                       int dtype, void* grad_out, float* loss_out, const float* grad_scale,
+                       void* stream) {
+  if (!grad_scale) return CE_ERR_NULL;
+  return fwd_grad_impl(logits, targets, B, C, dtype, grad_out, loss_out, grad_scale, stream);
+}
+
+int ce_scale_grad(void* grad, int64_t n, int dtype, const float* scale, void* stream) {
+  if (!grad || !scale) return CE_ERR_NULL;
+  if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
+  if (n <= 0) return CE_ERR_SHAPE;
+  const int es = elem_size(dtype);
+  if ((uintptr_t)grad % es || (uintptr_t)scale % 4) return CE_ERR_ALIGN;
+  if ((uint64_t)n > UINT64_MAX / 2 / (uint64_t)es) return CE_ERR_SHAPE;
+  if (overlaps((uintptr_t)grad, (uintptr_t)n * es, (uintptr_t)scale, 4)) return CE_ERR_ALIAS;
+  const hipStream_t st = as_stream(stream);
+  if (dtype == CE_F32) return launch_scale<float>((float*)grad, n, scale, st);
+  return launch_scale<__bf16>((__bf16*)grad, n, scale, st);
 }
 
 size_t ce_reduce_workspace_bytes(int64_t B) {

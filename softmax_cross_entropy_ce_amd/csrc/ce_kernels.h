@@ -24,9 +24,20 @@
 
 namespace ce {
 
-// Per-row epilogue shared by both kernels: from the row's (cg, Sx) and the
-// target logit, the gradient scale 1/(S B), the target's gradient and the
-// per-row loss.
+// Scales of a call: 1/B for the loss, and for the gradient 1/B times the
+// upstream gradient of the loss, a device scalar (gmul; null means 1).
+struct RowScale {
+  float invB;
+  const float* gmul;
+};
+
+__device__ __forceinline__ float grad_mul(const RowScale& rs) {
+  return rs.gmul != nullptr ? *rs.gmul : 1.0f;
+}
+
+// Per-row epilogue shared by all kernels: from the row's (cg, Sx) and the
+// target logit, the gradient scale gmul/(S B), the target's gradient and
+// the per-row loss.
 struct RowResult {
   float scale;   // multiply 2^(z log2e - cg) by this to get the gradient
   float gt;      // gradient of the target element
@@ -34,12 +45,12 @@ struct RowResult {
 };
 
 __device__ __forceinline__ RowResult row_epilogue(float cg, float sx, float zt, bool valid,
-                                                  float invB) {
+                                                  float invB, float gmul) {
   RowResult r;
   const float at = __builtin_fmaf(zt, kLog2e, -cg);
   const float et = exp2_hw(at);
   const float S = sx + et;
-  const float scale = invB / S;
+  const float scale = invB / S * gmul;
   float lossB;
   if (at > -60.f)
     lossB = log1pf(sx * exp2_hw(-at));
@@ -145,7 +156,8 @@ constexpr int kShortThreads = 256;
 template <typename T, int S, int EPL, int VW>
 __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
     const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B, int C,
-    float invB, T* __restrict__ grad, float* __restrict__ loss_rows) {
+    RowScale rs, T* __restrict__ grad, float* __restrict__ loss_rows) {
+  const float invB = rs.invB, gmul = grad_mul(rs);
   constexpr int RPB = kShortThreads / S;  // rows per workgroup
   constexpr int NVEC = EPL / VW;          // vector slots per lane
   static_assert(EPL % VW == 0, "EPL must be a multiple of VW");
@@ -201,7 +213,7 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
     e[i] = exp2_hw(__builtin_fmaf(x, kLog2e, -cg));
   }
   const float sx = seg_allreduce<S>(tree_sum(e), OpAdd{});
-  const RowResult rr = row_epilogue(cg, sx, zt, valid, invB);
+  const RowResult rr = row_epilogue(cg, sx, zt, valid, invB, gmul);
   if (live && q == 0) loss_rows[row] = rr.loss;
 
 #pragma unroll
@@ -268,9 +280,10 @@ __device__ __forceinline__ RowGeom row_geom(const T* rp, int C) {
 template <typename T, int NT, int NV>
 __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits,
                                                     const int32_t* __restrict__ targets,
-                                                    int64_t B, int C, float invB,
+                                                    int64_t B, int C, RowScale rs,
                                                     T* __restrict__ grad,
                                                     float* __restrict__ loss_rows) {
+  const float invB = rs.invB, gmul = grad_mul(rs);
   using E = Elem<T>;
   constexpr int VE = E::VE;
   constexpr int NW = NT / 64;
@@ -377,7 +390,7 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
       cg = wave_uniform(seg_allreduce<16>(ci, OpMax{}));
       sx = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
     }
-    const RowResult rr = row_epilogue(cg, sx, zt, valid, invB);
+    const RowResult rr = row_epilogue(cg, sx, zt, valid, invB, gmul);
     if (tid == 0) loss_rows[row] = rr.loss;
 
     // Phase C: gradient from the registers; each slot is refilled with the
@@ -484,9 +497,10 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 template <typename T, int NV, int PF>
 __global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ logits,
                                                           const int32_t* __restrict__ targets,
-                                                          int64_t B, int C, float invB,
+                                                          int64_t B, int C, RowScale rs,
                                                           T* __restrict__ grad,
                                                           float* __restrict__ loss_rows) {
+  const float invB = rs.invB, gmul = grad_mul(rs);
   using E = Elem<T>;
   constexpr int NT = 1024, NW = 16, VE = E::VE, ES = sizeof(T);
   static_assert(PF >= 1 && PF < NV, "prefetch slots");
@@ -616,7 +630,7 @@ __global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ 
     const float si = lane < NW ? red_s[parity][lane] : 0.f;
     const float cg = wave_uniform(seg_allreduce<16>(ci, OpMax{}));
     const float sx = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
-    const RowResult rr = row_epilogue(cg, sx, zt, valid, invB);
+    const RowResult rr = row_epilogue(cg, sx, zt, valid, invB, gmul);
 
     // step 7: phase C; register-only slots first (each refilled with the
     // next row), then the prefetched slots
@@ -698,6 +712,60 @@ __global__ __launch_bounds__(kReduceThreads) void ce_reduce_kernel(const float* 
   if (i + 2 * kReduceThreads < hi) a2 += in[i + 2 * kReduceThreads];
   const float tot = block_sum_256((a0 + a1) + (a2 + a3));
   if (threadIdx.x == 0) out[blockIdx.x] = tot;
+}
+
+// ===========================================================================
+// Backward broadcast-scale: g *= *scale in place over n elements (the
+// gradient was formed in the forward pass; the backward multiplies it by
+// the upstream gradient of the loss, a device scalar).  Every workgroup
+// first reads the scalar and returns at once when it is exactly 1, so the
+// common case moves no gradient bytes (about 16 us of launches at 2 GB of
+// bf16).  The grid has one workgroup per chunk of 8192 16-byte vectors of
+// the aligned body, the fastest streaming pattern measured (a grid capped
+// at 2048 workgroups halved the no-op time and cost 3.5 % on a full pass);
+// workgroup 0 also takes the elements before the first 16-byte boundary
+// and after the last.
+// ===========================================================================
+constexpr int kScaleThreads = 1024;
+constexpr int kScaleSlots = 8;
+
+template <typename T>
+__global__ __launch_bounds__(kScaleThreads) void ce_scale_kernel(T* __restrict__ g, int64_t n,
+                                                                 const float* __restrict__ scale) {
+  using E = Elem<T>;
+  constexpr int VE = E::VE, ES = sizeof(T);
+  const float sc = *scale;
+  if (sc == 1.0f) return;
+  const uint32_t mis = (uint32_t)((uintptr_t)g & 15u);
+  int64_t h = mis ? (int64_t)((16u - mis) / ES) : 0;
+  if (h > n) h = n;
+  const int64_t nb = (n - h) / VE;
+  const int64_t tail0 = h + nb * VE;
+  constexpr int64_t chunk = (int64_t)kScaleThreads * kScaleSlots;
+  const uint32_t voff = threadIdx.x * 16u;
+  for (int64_t v0 = (int64_t)blockIdx.x * chunk; v0 < nb; v0 += (int64_t)gridDim.x * chunk) {
+    const int64_t cnt = nb - v0 < chunk ? nb - v0 : chunk;
+    const rsrc_t r = make_rsrc(g + h + v0 * VE, (uint32_t)(cnt * 16));
+    u32x4 v[kScaleSlots];
+#pragma unroll
+    for (int k = 0; k < kScaleSlots; ++k)
+      v[k] = bload128<kPolicyStream>(r, voff, (uint32_t)k * kScaleThreads * 16u);
+#pragma unroll
+    for (int k = 0; k < kScaleSlots; ++k) {
+      float f[VE];
+      E::unpack(v[k], f);
+#pragma unroll
+      for (int i = 0; i < VE; ++i) f[i] *= sc;
+      bstore128<kPolicyStream>(E::pack(f), r, voff, (uint32_t)k * kScaleThreads * 16u);
+    }
+  }
+  if (blockIdx.x == 0) {
+    const int64_t i = threadIdx.x;
+    int64_t e = -1;
+    if (i < h) e = i;
+    else if (i - h < n - tail0) e = tail0 + (i - h);
+    if (e >= 0) E::store1(g + e, E::load1(g + e) * sc);
+  }
 }
 
 // ===========================================================================

@@ -111,8 +111,9 @@ constexpr int part_capacity(int NT, int NR, int NL, int NXW) { return (NR + NL) 
 template <typename T, int P, int NT, int NR, int NL, int NXW>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8)))
 void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B,
-                    int C, float invB, T* __restrict__ grad, float* __restrict__ loss_rows,
+                    int C, RowScale rs, T* __restrict__ grad, float* __restrict__ loss_rows,
                     int spin, uint32_t* __restrict__ fallbacks) {
+  const float invB = rs.invB, gmul = grad_mul(rs);
   using E = Elem<T>;
   constexpr int NW = NT / 64, VE = E::VE, ES = sizeof(T);
   constexpr int NLS = NL + (NXW > 0 ? 1 : 0);  // LDS slots, the last maybe partial
@@ -347,7 +348,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
     sx = s0 * exp2_hw(c0 - cg);
     sx = sx + s1 * exp2_hw(c1 - cg);
   }
-  const RowResult rr = row_epilogue(cg, sx, zt, valid, invB);
+  const RowResult rr = row_epilogue(cg, sx, zt, valid, invB, gmul);
   if (part == 0 && tid == 0) loss_rows[row] = rr.loss;
 
   // Phase C: the gradient of this part from registers and LDS.

@@ -37,7 +37,8 @@ def test_library_exports_every_declared_function():
     assert names == sorted(["ce_fwd_grad", "ce_reduce_workspace_bytes", "ce_reduce_loss",
                             "ce_status_string", "ce_version", "ce_select_path",
                             "ce_debug_force_path", "ce_debug_part_polls",
-                            "ce_debug_part_counter", "ce_stream_copy"])
+                            "ce_debug_part_counter", "ce_stream_copy",
+                            "ce_fwd_grad_scaled", "ce_scale_grad"])
     for n in names:
         assert hasattr(L_, n), n
 
@@ -176,3 +177,23 @@ def test_stream_copy_validation():
     assert cp(Z, G, 24, None) == SHAPE      # not a multiple of 16
     assert cp(Z + 8, G, 16, None) == ALIGN
     assert cp(Z, Z + 16, 64, None) == ALIAS
+
+
+def test_fwd_grad_scaled_validation():
+    f = ce.lib().ce_fwd_grad_scaled
+    assert f(Z, T, 8, 10, 0, G, L, None, None) == NULL          # grad_scale required
+    assert f(Z, T, 8, 10, 0, G, L, L + 2, None) == ALIGN
+    assert f(None, T, 8, 10, 0, G, L, L, None) == NULL
+    assert f(Z, T, 0, 10, 0, G, L, L, None) == SHAPE
+    assert f(Z, T, 8, 10, 5, G, L, L, None) == DTYPE
+
+
+def test_scale_grad_validation():
+    f = ce.lib().ce_scale_grad
+    assert f(None, 16, 0, L, None) == NULL
+    assert f(G, 16, 0, None, None) == NULL
+    assert f(G, 0, 0, L, None) == SHAPE
+    assert f(G, 16, 7, L, None) == DTYPE
+    assert f(G + 2, 16, 0, L, None) == ALIGN      # fp32 grad 2-byte aligned
+    assert f(G, 16, 0, L + 1, None) == ALIGN
+    assert f(G, 16, 0, G + 8, None) == ALIAS      # scale inside grad
