@@ -174,6 +174,39 @@ def backward_scale(zd, td, grad, loss_rows, reps: int = 20) -> dict:
             "fwd_grad_scaled_ms": round(ms_fused, 5)}
 
 
+def loss_only_and_in_place(zd, td, grad, loss_rows, reps: int = 20) -> dict:
+    """ce_fwd_loss (logits read once, per-row losses written) and
+    ce_fwd_grad in place of the logits (on a copy of them; each call then
+    reads the previous call's gradient, a valid input of the same size)."""
+    import torch
+    import softmax_cross_entropy_ce_amd as ce
+    stream = torch.cuda.current_stream(zd.device)
+
+    def timed(fn):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return statistics.median([a.elapsed_time(b) for a, b in evs])
+
+    in_bytes = zd.numel() * zd.element_size()
+    ms_loss = timed(lambda: ce.fwd_loss_into(zd, td, loss_rows))
+    grad.copy_(zd)
+    ms_inpl = timed(lambda: ce.fwd_grad_into(grad, td, grad, loss_rows))
+    gbs_loss = (in_bytes + 8 * zd.shape[0]) / (ms_loss * 1e-3) / 1e9
+    gbs_inpl = (2 * in_bytes + 8 * zd.shape[0]) / (ms_inpl * 1e-3) / 1e9
+    return {"loss_only_ms": round(ms_loss, 5), "loss_only_GBps": round(gbs_loss, 2),
+            "loss_only_frac": round(gbs_loss / PEAK_HBM_GBS, 4),
+            "in_place_ms": round(ms_inpl, 5), "in_place_GBps": round(gbs_inpl, 2),
+            "in_place_frac": round(gbs_inpl / PEAK_HBM_GBS, 4)}
+
+
 def run_copy(args) -> None:
     """Plain device-to-device copy of a known size (counter calibration)."""
     import torch
@@ -286,6 +319,7 @@ def main() -> None:
     achieved = fwd_bytes / (fwd_avg * 1e-3) / 1e9
     cal = copy_calibration(zd, grad)
     bwd = backward_scale(zd, td, grad, loss_rows)
+    variants = loss_only_and_in_place(zd, td, grad, loss_rows)
     cal["fwd_grad_pct_of_copy"] = round(100 * achieved / cal["GBps"], 2)
     rec = {
         "metric": "fused CE fwd+grad: achieved HBM GB/s (% of peak) and rows/sec at C=128256 bf16"
@@ -317,6 +351,7 @@ def main() -> None:
                      "traffic": traffic_for(w.name)},
         "copy_calibration": cal,
         "backward_scale": bwd,
+        "loss_only_and_in_place": variants,
     }
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f} s")

@@ -77,10 +77,14 @@ typedef enum {
  *             Contents on entry are ignored; on path 4 with two parts per
  *             row the call also uses 16 bytes of each part's own gradient
  *             as a mailbox before the gradient is written there.
- *             Must not overlap logits, must be aligned to the element size,
- *             and (grad_out - logits) must be a multiple of 16 bytes
- *             (true for any two allocations from the HIP or torch
- *             allocators).
+ *             grad_out == logits computes the gradient in place of the
+ *             logits (every kernel holds a row's data on chip, or reads it
+ *             again from the same thread, before writing it; rows that
+ *             path 4 would cut into two parts run on path 2 or 3 instead).
+ *             Any other overlap with logits is refused.  Must be aligned
+ *             to the element size, and (grad_out - logits) must be a
+ *             multiple of 16 bytes (true for any two allocations from the
+ *             HIP or torch allocators).
  *   loss_out  [B] float32, overwritten with the per-row losses, already
  *             scaled by 1/B; ce_reduce_loss sums them to the batch mean.
  *   stream    hipStream_t or NULL.
@@ -90,6 +94,19 @@ typedef enum {
  */
 int ce_fwd_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C,
                 int dtype, void* grad_out, float* loss_out, void* stream);
+
+/*
+ * ce_fwd_loss - per-row losses only, for evaluation: the logits are read
+ * once and only loss_out is written.  Arguments, layout and errors as
+ * ce_fwd_grad without grad_out; runs on paths 1 to 3 (no row parts are
+ * needed when nothing has to stay on chip for a gradient), so forcing path
+ * 4 returns CE_ERR_PATH.
+ *
+ * Defined by: rumus 0.1.1 cross_entropy.wgsl, pass 1 steps 1-3 (row max,
+ * sum of exponentials, per-row loss scaled by 1/B).
+ */
+int ce_fwd_loss(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
+                float* loss_out, void* stream);
 
 /*
  * ce_fwd_grad_scaled - ce_fwd_grad with the gradient multiplied by an

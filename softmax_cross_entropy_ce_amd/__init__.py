@@ -24,6 +24,7 @@ import os
 __all__ = [
     "CEError", "lib", "fwd_grad", "fwd_grad_into", "reduce_loss", "reduce_loss_into",
     "cross_entropy", "cross_entropy_loss", "fwd_grad_scaled_into", "scale_grad_",
+    "fwd_loss", "fwd_loss_into", "fwd_grad_inplace_",
     "reduce_workspace_bytes", "select_path", "force_path", "part_polls", "part_counter",
     "stream_copy", "version", "PATH_NAMES", "F32", "BF16",
 ]
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
     L.ce_fwd_grad_scaled.restype = i32
     L.ce_scale_grad.argtypes = [vp, i64, i32, vp, vp]
     L.ce_scale_grad.restype = i32
+    L.ce_fwd_loss.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+    L.ce_fwd_loss.restype = i32
     _lib = L
     return L
 
@@ -210,6 +213,39 @@ def fwd_grad_into(logits, targets, grad, loss_rows) -> None:
     st = lib().ce_fwd_grad(logits.data_ptr(), targets.data_ptr(), B, C, _dtype_code(logits),
                            grad.data_ptr(), loss_rows.data_ptr(), _stream_ptr(logits.device))
     _check(st, "ce_fwd_grad")
+
+
+def fwd_grad_inplace_(logits, targets):
+    """Overwrite logits with the gradient (softmax - onehot) / B and return
+    the per-row losses."""
+    torch = _torch()
+    loss_rows = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device)
+    fwd_grad_into(logits, targets, logits, loss_rows)
+    return loss_rows
+
+
+def fwd_loss_into(logits, targets, loss_rows) -> None:
+    """Per-row losses only (the logits are read once, no gradient)."""
+    torch = _torch()
+    _check_cuda(logits, targets, loss_rows)
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, C]")
+    B, C = logits.shape
+    if targets.dtype != torch.int32 or targets.shape != (B,):
+        raise TypeError("targets must be int32 of shape [B]")
+    if loss_rows.dtype != torch.float32 or loss_rows.shape != (B,):
+        raise TypeError("loss_rows must be float32 of shape [B]")
+    st = lib().ce_fwd_loss(logits.data_ptr(), targets.data_ptr(), B, C, _dtype_code(logits),
+                           loss_rows.data_ptr(), _stream_ptr(logits.device))
+    _check(st, "ce_fwd_loss")
+
+
+def fwd_loss(logits, targets):
+    """The per-row losses (already scaled by 1/B) of ``[B, C]`` logits."""
+    torch = _torch()
+    loss_rows = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device)
+    fwd_loss_into(logits, targets, loss_rows)
+    return loss_rows
 
 
 def fwd_grad_scaled_into(logits, targets, grad, loss_rows, grad_scale) -> None:

@@ -70,27 +70,27 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 int launched() { return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_LAUNCH; }
 
 // ------------------------------------------------------------------ path 1
-template <typename T, int S, int EPL, int VW>
+template <typename T, int S, int EPL, int VW, bool GRAD>
 int launch_short_cfg(const T* z, const int32_t* t, int64_t B, int C, ce::RowScale rs, T* g, float* l,
                      hipStream_t st) {
   constexpr int rpb = ce::kShortThreads / S;
   const int64_t blocks = (B + rpb - 1) / rpb;
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL((ce::ce_short_kernel<T, S, EPL, VW>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((ce::ce_short_kernel<T, S, EPL, VW, GRAD>), dim3((unsigned)blocks),
                      dim3(ce::kShortThreads), 0, st, z, t, B, C, rs, g, l);
   return launched();
 }
 
-template <typename T, int S, int EPL>
+template <typename T, int S, int EPL, bool GRAD>
 int launch_short_vw(int vw, const T* z, const int32_t* t, int64_t B, int C, ce::RowScale rs, T* g,
                     float* l, hipStream_t st) {
   switch (vw) {
-    case 1: return launch_short_cfg<T, S, EPL, 1>(z, t, B, C, rs, g, l, st);
-    case 2: return launch_short_cfg<T, S, EPL, 2>(z, t, B, C, rs, g, l, st);
-    case 4: return launch_short_cfg<T, S, EPL, 4>(z, t, B, C, rs, g, l, st);
+    case 1: return launch_short_cfg<T, S, EPL, 1, GRAD>(z, t, B, C, rs, g, l, st);
+    case 2: return launch_short_cfg<T, S, EPL, 2, GRAD>(z, t, B, C, rs, g, l, st);
+    case 4: return launch_short_cfg<T, S, EPL, 4, GRAD>(z, t, B, C, rs, g, l, st);
     case 8:
       if constexpr (sizeof(T) == 2 && EPL >= 8)
-        return launch_short_cfg<T, S, EPL, 8>(z, t, B, C, rs, g, l, st);
+        return launch_short_cfg<T, S, EPL, 8, GRAD>(z, t, B, C, rs, g, l, st);
       return CE_ERR_PATH;
     default: return CE_ERR_PATH;
   }
@@ -110,7 +110,7 @@ int short_vw(int64_t C, int es, uintptr_t zaddr, uintptr_t gaddr, int epl) {
 // of two that covers the row with EPL elements per lane (EPL = 16 bytes of
 // elements, more only at S = 16).  Lanes of a row read adjacent vectors,
 // so a load instruction covers 64/S consecutive rows.
-template <typename T>
+template <typename T, bool GRAD>
 int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g, float* l,
                  hipStream_t st) {
   if (C > kShortMaxC) return CE_ERR_PATH;
@@ -118,16 +118,16 @@ int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScal
   constexpr int E16 = 16 / es;  // elements in 16 bytes
   const int c = (int)C;
   auto vw = [&](int epl) { return short_vw(C, es, (uintptr_t)z, (uintptr_t)g, epl); };
-  if (C <= E16) return launch_short_vw<T, 1, E16>(vw(E16), z, t, B, c, rs, g, l, st);
-  if (C <= 2 * E16) return launch_short_vw<T, 2, E16>(vw(E16), z, t, B, c, rs, g, l, st);
-  if (C <= 4 * E16) return launch_short_vw<T, 4, E16>(vw(E16), z, t, B, c, rs, g, l, st);
-  if (C <= 8 * E16) return launch_short_vw<T, 8, E16>(vw(E16), z, t, B, c, rs, g, l, st);
-  if (C <= 16 * E16) return launch_short_vw<T, 16, E16>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= E16) return launch_short_vw<T, 1, E16, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= 2 * E16) return launch_short_vw<T, 2, E16, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= 4 * E16) return launch_short_vw<T, 4, E16, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= 8 * E16) return launch_short_vw<T, 8, E16, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= 16 * E16) return launch_short_vw<T, 16, E16, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
   if constexpr (E16 < 16) {
-    if (C <= 32 * E16) return launch_short_vw<T, 16, 2 * E16>(vw(2 * E16), z, t, B, c, rs, g, l, st);
+    if (C <= 32 * E16) return launch_short_vw<T, 16, 2 * E16, GRAD>(vw(2 * E16), z, t, B, c, rs, g, l, st);
   }
   if constexpr (E16 < 8) {
-    if (C <= 64 * E16) return launch_short_vw<T, 16, 4 * E16>(vw(4 * E16), z, t, B, c, rs, g, l, st);
+    if (C <= 64 * E16) return launch_short_vw<T, 16, 4 * E16, GRAD>(vw(4 * E16), z, t, B, c, rs, g, l, st);
   }
   return CE_ERR_PATH;
 }
@@ -147,10 +147,10 @@ int resident_blocks(const void* kernel, int nt) {
   return cus * per_cu;
 }
 
-template <typename T, int NT, int NV>
+template <typename T, int NT, int NV, bool GRAD>
 int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
                    float* l, hipStream_t st) {
-  auto kern = ce::ce_row_kernel<T, NT, NV>;
+  auto kern = ce::ce_row_kernel<T, NT, NV, GRAD>;
   const int res = resident_blocks(reinterpret_cast<const void*>(kern), NT);
   if (res < 1) return CE_ERR_LAUNCH;
   const int64_t grid = B < res ? B : res;
@@ -173,11 +173,11 @@ int launch_row_lds(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowSc
   return launched();
 }
 
-template <typename T>
+template <typename T, bool GRAD>
 int launch_row(RowCfg cfg, const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
                float* l, hipStream_t st) {
 #define CE_ROW_CASE(NT_, NV_) \
-  if (cfg.nt == NT_ && cfg.nv == NV_) return launch_row_cfg<T, NT_, NV_>(z, t, B, C, rs, g, l, st);
+  if (cfg.nt == NT_ && cfg.nv == NV_) return launch_row_cfg<T, NT_, NV_, GRAD>(z, t, B, C, rs, g, l, st);
   CE_ROW_CASE(64, 1)
   CE_ROW_CASE(64, 2)
   CE_ROW_CASE(64, 4)
@@ -227,29 +227,42 @@ int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScal
   return CE_ERR_PATH;
 }
 
-template <typename T>
-int fwd_grad_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g, float* l,
-                   const float* gmul, hipStream_t st) {
+// GRAD false: the loss only, on the short, resident or long path (nothing
+// has to stay on chip for a gradient, so no row parts).
+template <typename T, bool GRAD>
+int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g, float* l,
+              const float* gmul, hipStream_t st) {
   const ce::RowScale rs{1.0f / (float)B, gmul};
   switch (path) {
     case kPathShort:
-      return launch_short<T>(z, t, B, C, rs, g, l, st);
+      return launch_short<T, GRAD>(z, t, B, C, rs, g, l, st);
     case kPathResident: {
       bool ok = false;
       const RowCfg cfg = resident_cfg(C, sizeof(T), &ok);
       if (!ok) return CE_ERR_PATH;
-      if (cfg.nt == 1024 && cfg.nv == 16) return launch_row_lds<T>(z, t, B, C, rs, g, l, st);
-      return launch_row<T>(cfg, z, t, B, C, rs, g, l, st);
+      if (GRAD && cfg.nt == 1024 && cfg.nv == 16) return launch_row_lds<T>(z, t, B, C, rs, g, l, st);
+      return launch_row<T, GRAD>(cfg, z, t, B, C, rs, g, l, st);
     }
     case kPathLong: {
       const bool forced = g_force_path.load(std::memory_order_relaxed) == kPathLong;
-      return launch_row<T>(forced ? kLongTestCfg : kLongCfg, z, t, B, C, rs, g, l, st);
+      return launch_row<T, GRAD>(forced ? kLongTestCfg : kLongCfg, z, t, B, C, rs, g, l, st);
     }
     case kPathParts:
-      return launch_parts<T>(z, t, B, C, rs, g, l, st);
+      if constexpr (GRAD) return launch_parts<T>(z, t, B, C, rs, g, l, st);
+      return CE_ERR_PATH;
     default:
       return CE_ERR_PATH;
   }
+}
+
+// Rows that path 4 cuts into two parts: their parts may read each other's
+// logits (the recompute) and keep mailboxes in grad, so they cannot run
+// in place.
+bool two_part_row(int64_t C, int es) { return body_vectors_max(C, es) > kPartsOne; }
+
+int path_without_parts(int64_t C, int es) {
+  if (C <= kShortMaxC) return kPathShort;
+  return row_vectors(C, es) <= (int64_t)kLongCfg.nt * kLongCfg.nv ? kPathResident : kPathLong;
 }
 
 bool overlaps(uintptr_t a, uintptr_t an, uintptr_t b, uintptr_t bn) {
@@ -277,28 +290,44 @@ extern "C" {
 
 namespace {
 
-int fwd_grad_impl(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
-                  void* grad_out, float* loss_out, const float* gmul, void* stream) {
-  if (!logits || !targets || !grad_out || !loss_out) return CE_ERR_NULL;
+// grad_out == nullptr: the loss only.  grad_out == logits: the gradient in
+// place of the logits.
+int fwd_impl(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
+             void* grad_out, float* loss_out, const float* gmul, void* stream) {
+  if (!logits || !targets || !loss_out) return CE_ERR_NULL;
   if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
   if (B <= 0 || C <= 0 || B > 0x7fffffffLL || C > CE_MAX_C) return CE_ERR_SHAPE;
   const int es = elem_size(dtype);
   const uintptr_t z = (uintptr_t)logits, g = (uintptr_t)grad_out;
   if (z % es || g % es || (uintptr_t)targets % 4 || (uintptr_t)loss_out % 4) return CE_ERR_ALIGN;
   if (gmul && (uintptr_t)gmul % 4) return CE_ERR_ALIGN;
-  if ((z > g ? z - g : g - z) % 16) return CE_ERR_ALIGN;
+  if (grad_out && (z > g ? z - g : g - z) % 16) return CE_ERR_ALIGN;
   if ((uint64_t)B > UINT64_MAX / ((uint64_t)C * es)) return CE_ERR_SHAPE;
   const uintptr_t nbytes = (uintptr_t)B * (uintptr_t)C * es;
-  if (overlaps(z, nbytes, g, nbytes)) return CE_ERR_ALIAS;
+  const bool in_place = grad_out && g == z;
+  if (grad_out && !in_place && overlaps(z, nbytes, g, nbytes)) return CE_ERR_ALIAS;
 
   const int forced = g_force_path.load(std::memory_order_relaxed);
-  const int path = forced ? forced : auto_path(C, es);
+  int path = forced ? forced : auto_path(C, es);
+  if (!grad_out || in_place) {
+    if (path == kPathParts && (!grad_out || two_part_row(C, es))) {
+      if (forced) return CE_ERR_PATH;
+      path = path_without_parts(C, es);
+    }
+  }
   const hipStream_t st = as_stream(stream);
-  if (dtype == CE_F32)
-    return fwd_grad_typed<float>(path, (const float*)logits, targets, B, C, (float*)grad_out,
+  if (dtype == CE_F32) {
+    if (!grad_out)
+      return fwd_typed<float, false>(path, (const float*)logits, targets, B, C, nullptr, loss_out,
+                                     gmul, st);
+    return fwd_typed<float, true>(path, (const float*)logits, targets, B, C, (float*)grad_out,
+                                  loss_out, gmul, st);
+  }
+  if (!grad_out)
+    return fwd_typed<__bf16, false>(path, (const __bf16*)logits, targets, B, C, nullptr, loss_out,
+                                    gmul, st);
+  return fwd_typed<__bf16, true>(path, (const __bf16*)logits, targets, B, C, (__bf16*)grad_out,
                                  loss_out, gmul, st);
-  return fwd_grad_typed<__bf16>(path, (const __bf16*)logits, targets, B, C, (__bf16*)grad_out,
-                                loss_out, gmul, st);
 }
 
 template <typename T>
@@ -318,14 +347,20 @@ extern "C" {
 
 int ce_fwd_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
                 void* grad_out, float* loss_out, void* stream) {
-  return fwd_grad_impl(logits, targets, B, C, dtype, grad_out, loss_out, nullptr, stream);
+  if (!grad_out) return CE_ERR_NULL;
+  return fwd_impl(logits, targets, B, C, dtype, grad_out, loss_out, nullptr, stream);
+}
+
+int ce_fwd_loss(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
+                float* loss_out, void* stream) {
+  return fwd_impl(logits, targets, B, C, dtype, nullptr, loss_out, nullptr, stream);
 }
 
 int ce_fwd_grad_scaled(const void* logits, const int32_t* targets, int64_t B, int64_t C,
                        int dtype, void* grad_out, float* loss_out, const float* grad_scale,
                        void* stream) {
-  if (!grad_scale) return CE_ERR_NULL;
-  return fwd_grad_impl(logits, targets, B, C, dtype, grad_out, loss_out, grad_scale, stream);
+  if (!grad_scale || !grad_out) return CE_ERR_NULL;
+  return fwd_impl(logits, targets, B, C, dtype, grad_out, loss_out, grad_scale, stream);
 }
 
 int ce_scale_grad(void* grad, int64_t n, int dtype, const float* scale, void* stream) {

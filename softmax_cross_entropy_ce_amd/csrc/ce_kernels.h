@@ -153,7 +153,8 @@ struct VecIO<__bf16, VW> {
 
 constexpr int kShortThreads = 256;
 
-template <typename T, int S, int EPL, int VW>
+// GRAD false: the loss only; grad is not written (and may be null).
+template <typename T, int S, int EPL, int VW, bool GRAD>
 __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
     const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B, int C,
     RowScale rs, T* __restrict__ grad, float* __restrict__ loss_rows) {
@@ -215,6 +216,7 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
   const float sx = seg_allreduce<S>(tree_sum(e), OpAdd{});
   const RowResult rr = row_epilogue(cg, sx, zt, valid, invB, gmul);
   if (live && q == 0) loss_rows[row] = rr.loss;
+  if constexpr (!GRAD) return;
 
 #pragma unroll
   for (int j = 0; j < NVEC; ++j) {
@@ -277,7 +279,9 @@ __device__ __forceinline__ RowGeom row_geom(const T* rp, int C) {
   return g;
 }
 
-template <typename T, int NT, int NV>
+// GRAD false: the loss only; grad is not written (and may be null), and the
+// streamed part of a long row is read once.
+template <typename T, int NT, int NV, bool GRAD>
 __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits,
                                                     const int32_t* __restrict__ targets,
                                                     int64_t B, int C, RowScale rs,
@@ -407,6 +411,13 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
     // (twice the registers for bf16).
 #pragma unroll
     for (int k = 0; k < NV; ++k) asm volatile("" : "+v"(v[k]));
+    if constexpr (!GRAD) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) v[k] = bload128<kPolicyStream>(rinn, voff, (uint32_t)k * NT * 16u);
+      if (!more) break;
+      row = next;
+      continue;
+    }
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int base = k * NT;

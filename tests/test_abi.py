@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
                             "ce_status_string", "ce_version", "ce_select_path",
                             "ce_debug_force_path", "ce_debug_part_polls",
                             "ce_debug_part_counter", "ce_stream_copy",
-                            "ce_fwd_grad_scaled", "ce_scale_grad"])
+                            "ce_fwd_grad_scaled", "ce_scale_grad", "ce_fwd_loss"])
     for n in names:
         assert hasattr(L_, n), n
 
@@ -84,9 +84,10 @@ def test_fwd_grad_alignment():
 
 
 def test_fwd_grad_alias():
-    # grad overlapping logits is refused: same start, and a partial overlap
-    assert fwd(z=Z, g=Z) == ALIAS
+    # a partial overlap of grad and logits is refused (grad == logits is the
+    # in-place call, accepted)
     assert fwd(z=Z, g=Z + 16, B=8, C=10) == ALIAS
+    assert fwd(z=Z + 16, g=Z, B=8, C=10) == ALIAS
 
 
 def test_reduce_workspace_sizes():
@@ -197,3 +198,27 @@ def test_scale_grad_validation():
     assert f(G + 2, 16, 0, L, None) == ALIGN      # fp32 grad 2-byte aligned
     assert f(G, 16, 0, L + 1, None) == ALIGN
     assert f(G, 16, 0, G + 8, None) == ALIAS      # scale inside grad
+
+
+def test_fwd_loss_validation():
+    f = ce.lib().ce_fwd_loss
+    assert f(None, T, 8, 10, 0, L, None) == NULL
+    assert f(Z, None, 8, 10, 0, L, None) == NULL
+    assert f(Z, T, 8, 10, 0, None, None) == NULL
+    assert f(Z, T, 0, 10, 0, L, None) == SHAPE
+    assert f(Z, T, 8, 0, 0, L, None) == SHAPE
+    assert f(Z, T, 8, 10, 9, L, None) == DTYPE
+    assert f(Z + 2, T, 8, 10, 0, L, None) == ALIGN
+    prev = ce.force_path(4)
+    try:
+        assert f(Z, T, 8, 10, 0, L, None) == PATH   # no row parts for the loss alone
+    finally:
+        ce.force_path(prev)
+
+
+def test_in_place_two_part_rows_refuse_forced_parts():
+    prev = ce.force_path(4)
+    try:
+        assert fwd(z=Z, g=Z, B=8, C=128256, dtype=1) == PATH
+    finally:
+        ce.force_path(prev)
