@@ -207,6 +207,62 @@ def loss_only_and_in_place(zd, td, grad, loss_rows, reps: int = 20) -> dict:
             "in_place_frac": round(gbs_inpl / PEAK_HBM_GBS, 4)}
 
 
+def _event_median_ms(fn, stream, reps: int, warm: int = 10) -> float:
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return statistics.median([a.elapsed_time(b) for a, b in evs])
+
+
+def _rate(nbytes: int, ms: float) -> dict:
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 5), "GBps": round(gbs, 2), "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "bytes": nbytes}
+
+
+def softmax_and_shards(zd, td, grad, loss_rows, reps: int = 20, nshards: int = 8) -> dict:
+    """The row-wise softmax forward (y and the log-sum-exp) and backward on
+    the workload's shape, and the cross-entropy of its vocabulary cut into
+    nshards column shards: one shard's record pass (ce_shard_stats) and
+    gradient pass (ce_shard_grad, from the records of all shards).  Bytes
+    counted: every array element read or written once, plus the per-row
+    values."""
+    import torch
+    import softmax_cross_entropy_ce_amd as ce
+    stream = torch.cuda.current_stream(zd.device)
+    B, C = zd.shape
+    es = zd.element_size()
+    out = {}
+    ms = _event_median_ms(lambda: ce.softmax_fwd_into(zd, grad, loss_rows), stream, reps)
+    out["softmax_fwd"] = _rate(2 * B * C * es + 4 * B, ms)
+    y = grad.clone()          # a softmax output as y; the logits serve as dy
+    dx = torch.empty_like(zd)
+    ms = _event_median_ms(lambda: ce.softmax_bwd_into(y, zd, dx), stream, reps)
+    out["softmax_bwd"] = _rate(3 * B * C * es, ms)
+    del y, dx
+    edges = [C * k // nshards for k in range(nshards + 1)]
+    shards = [zd[:, a:b].contiguous() for a, b in zip(edges[:-1], edges[1:])]
+    recs = torch.stack([ce.shard_stats(s, td, a) for s, a in zip(shards, edges[:-1])])
+    s0 = shards[0]
+    g0 = torch.empty_like(s0)
+    Cs = s0.shape[1]
+    ms = _event_median_ms(lambda: ce.shard_stats_into(s0, td, 0, recs[0]), stream, reps)
+    out["shard_stats"] = _rate(B * Cs * es + 4 * B + 16 * B, ms)
+    ms = _event_median_ms(lambda: ce.shard_grad_into(s0, td, 0, C, recs, g0, loss_rows),
+                          stream, reps)
+    out["shard_grad"] = _rate(2 * B * Cs * es + 4 * B + 16 * nshards * B + 4 * B, ms)
+    out["shard"] = {"shards": nshards, "columns": Cs}
+    return out
+
+
 def run_copy(args) -> None:
     """Plain device-to-device copy of a known size (counter calibration)."""
     import torch
@@ -320,6 +376,7 @@ def main() -> None:
     cal = copy_calibration(zd, grad)
     bwd = backward_scale(zd, td, grad, loss_rows)
     variants = loss_only_and_in_place(zd, td, grad, loss_rows)
+    sm = softmax_and_shards(zd, td, grad, loss_rows)
     cal["fwd_grad_pct_of_copy"] = round(100 * achieved / cal["GBps"], 2)
     rec = {
         "metric": "fused CE fwd+grad: achieved HBM GB/s (% of peak) and rows/sec at C=128256 bf16"
@@ -352,6 +409,7 @@ def main() -> None:
         "copy_calibration": cal,
         "backward_scale": bwd,
         "loss_only_and_in_place": variants,
+        "softmax_and_shards": sm,
     }
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f} s")

@@ -54,7 +54,7 @@ typedef enum {
     CE_ERR_WORKSPACE = -4, /* workspace NULL or smaller than ce_reduce_workspace_bytes(B) */
     CE_ERR_LAUNCH = -5,    /* the HIP runtime rejected a kernel launch */
     CE_ERR_ALIGN = -6,     /* a pointer is not aligned as required */
-    CE_ERR_ALIAS = -7,     /* grad_out overlaps logits */
+    CE_ERR_ALIAS = -7,     /* an output overlaps an input in a way the call refuses */
     CE_ERR_PATH = -8       /* the forced path (ce_debug_force_path) cannot take this shape */
 } ce_status;
 
@@ -170,6 +170,112 @@ size_t ce_reduce_workspace_bytes(int64_t B);
 int ce_reduce_loss(const float* loss_rows, int64_t B, float* loss_scalar_out,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ce_softmax_fwd - row-wise softmax and log-sum-exp.
+ *
+ * Defined by: rumus project page, milestone M8c (row-wise softmax kept
+ * stable with the log-sum-exp trick) and its feature table's Softmax row.
+ * For each row of x:
+ *
+ *     y[b, c]  = exp(x[b,c] - m_b) / sum_j exp(x[b,j] - m_b),  m_b = max_j x[b,j]
+ *     lse[b]   = m_b + ln(sum_j exp(x[b,j] - m_b))
+ *
+ * computed by the kernels of ce_fwd_grad (same paths, same single read of
+ * x and single write of y), in float32, the log-sum-exp in the log2
+ * domain as ln2 * (round(m log2 e) + log2 s).
+ *
+ *   x        [B, C] dtype, row-major, contiguous, element-aligned.
+ *   B, C     as ce_fwd_grad.
+ *   y_out    [B, C] dtype, overwritten; y_out == x computes the softmax in
+ *            place (rows that path 4 would cut into two parts then run on
+ *            path 2 or 3).  Other overlaps are refused; (y_out - x) must be
+ *            a multiple of 16 bytes.  Path 4's two-part rows use 16 bytes of
+ *            each part of y_out as a mailbox before writing it.
+ *   lse_out  [B] float32 (4-byte aligned), or NULL for none.
+ * Returns CE_OK or a negative ce_status.
+ */
+int ce_softmax_fwd(const void* x, int64_t B, int64_t C, int dtype, void* y_out, float* lse_out,
+                   void* stream);
+
+/*
+ * ce_softmax_bwd - backward of the row-wise softmax.
+ *
+ * Defined by: rumus project page, milestone M8c (softmax backward kernel).
+ * The pages give no formula; this is the vector-Jacobian product of the
+ * forward, from its output y and the upstream gradient dy:
+ *
+ *     dx[b, c] = y[b,c] * (dy[b,c] - sum_j dy[b,j] * y[b,j])
+ *
+ * in float32 with a fixed summation order (bitwise reproducible).
+ *
+ *   y, dy    [B, C] dtype, row-major, contiguous, element-aligned; y is the
+ *            softmax (for example ce_softmax_fwd's y_out).
+ *   dx_out   [B, C] dtype, overwritten.  May be y or dy themselves; any
+ *            other overlap is refused.  (dy - y) and (dx_out - y) must be
+ *            multiples of 16 bytes.
+ * Rows of C <= 256 run many to a wave (path 1); longer rows run one
+ * workgroup per row with y and dy held in registers (path 2) up to 8192
+ * 16-byte vectors of each, and beyond that stream the rest of the row a
+ * second time (path 3).  ce_debug_force_path applies; path 4 returns
+ * CE_ERR_PATH.
+ */
+int ce_softmax_bwd(const void* y, const void* dy, int64_t B, int64_t C, int dtype, void* dx_out,
+                   void* stream);
+
+/*
+ * Cross-entropy over a vocabulary split into column shards.
+ *
+ * Defined by: rumus project page, milestone M24 (a column-parallel linear
+ * layer splits its weight along the output features, so each rank holds
+ * the logits of a contiguous range of classes), with the cross-entropy of
+ * rumus 0.1.1 cross_entropy.wgsl pass 1 taken over such ranges: the max and
+ * the sum of exponentials of the whole row are the max of the shards' maxes
+ * and the rescaled sum of their sums.
+ *
+ * Shard k holds columns [col0_k, col0_k + C_k) of every row as its own
+ * [B, C_k] row-major array.  The calls:
+ *   1. ce_shard_stats on every shard writes B records of 4 float32 (c, sx,
+ *      zt, own): c = max_c z * log2(e) rounded to float32; sx = the sum over
+ *      the shard's columns other than the target of 2^(z log2e - c); zt =
+ *      the target logit, and own = 1, where the shard holds the target
+ *      (else zt = own = 0).
+ *   2. The caller gathers the records of all N shards into one array of
+ *      N x B records, shard-major, in shard order (one all-gather of
+ *      16 B bytes per shard on several GPUs).
+ *   3. ce_shard_grad on every shard combines each row's N records in shard
+ *      order (c = max c_k, sx = sum sx_k 2^(c_k - c), zt from the owning
+ *      shard) and writes that shard's columns of (softmax - onehot) / B,
+ *      times *grad_scale when grad_scale is not NULL, and, when loss_out is
+ *      not NULL, the per-row losses (lse - z_t) / B.
+ * A row whose target lies outside [0, C_total), or whose records do not
+ * name exactly one owner, gets a NaN loss and NaN gradient.  All shards
+ * compute identical per-row values, so any one may write the losses.
+ *
+ * ce_shard_stats:
+ *   logits       [B, C] dtype, the shard (C = C_k columns), element-aligned.
+ *   targets      [B] int32, the global class indices.
+ *   col0         the shard's first column, 0 <= col0 <= 2^31 - 1.
+ *   records_out  [B][4] float32, 16-byte aligned, overwritten.
+ * It reads the shard once on paths 1 to 3 (path 4 is refused).
+ *
+ * ce_shard_grad:
+ *   logits, targets, B, C, col0, dtype as ce_shard_stats.
+ *   C_total      the whole row's length: col0 + C <= C_total <= 2^31 - 1.
+ *   records      [n_shards][B][4] float32, 16-byte aligned (step 2).
+ *   n_shards     1 to 1024.
+ *   grad_out     [B, C] dtype, overwritten; may be logits itself (each
+ *                thread reads its elements before writing them); no other
+ *                overlap with logits or records.
+ *   loss_out     [B] float32 or NULL.
+ *   grad_scale   DEVICE float32 scalar or NULL (as ce_fwd_grad_scaled).
+ */
+int ce_shard_stats(const void* logits, const int32_t* targets, int64_t B, int64_t C, int64_t col0,
+                   int dtype, float* records_out, void* stream);
+
+int ce_shard_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C, int64_t col0,
+                  int64_t C_total, int dtype, const float* records, int n_shards, void* grad_out,
+                  float* loss_out, const float* grad_scale, void* stream);
+
 /* Static text for a ce_status value. */
 const char* ce_status_string(int status);
 
@@ -214,9 +320,10 @@ int ce_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 int ce_select_path(int64_t C, int dtype);
 
 /*
- * Test hook: force every later ce_fwd_grad onto one path (0 = automatic,
- * 1 to 4 as above; path 3 is then run with a small on-chip part so that
- * the streamed part is exercised).  A shape the forced path cannot take
+ * Test hook: force every later call of ce_fwd_grad, ce_fwd_grad_scaled,
+ * ce_fwd_loss, ce_softmax_fwd, ce_softmax_bwd and ce_shard_stats onto one
+ * path (0 = automatic, 1 to 4 as above; path 3 is then run with a small
+ * on-chip part so that the streamed part is exercised).  A shape the forced path cannot take
  * returns CE_ERR_PATH.  Returns the previous setting, or CE_ERR_PATH for an
  * unknown value.  Process-wide; not meant for production use.
  */

@@ -14,6 +14,11 @@ The operation (rumus project page, milestone M7a; rumus 0.1.1
     loss_rows[b] = (logsumexp(z[b]) - z[b, t[b]]) / B
     grad[b, c]   = (softmax(z[b])[c] - [c == t[b]]) / B
     loss         = sum_b loss_rows[b]
+
+Beside it, on the same kernels: the row-wise softmax forward and backward
+(rumus project page, milestone M8c) and the cross-entropy of a vocabulary
+split into column shards (per-shard records, then a combine that writes
+each shard's gradient).
 """
 
 from __future__ import annotations
@@ -25,6 +30,8 @@ __all__ = [
     "CEError", "lib", "fwd_grad", "fwd_grad_into", "reduce_loss", "reduce_loss_into",
     "cross_entropy", "cross_entropy_loss", "fwd_grad_scaled_into", "scale_grad_",
     "fwd_loss", "fwd_loss_into", "fwd_grad_inplace_",
+    "softmax_fwd", "softmax_fwd_into", "softmax_bwd", "softmax_bwd_into", "softmax",
+    "shard_stats", "shard_stats_into", "shard_grad", "shard_grad_into",
     "reduce_workspace_bytes", "select_path", "force_path", "part_polls", "part_counter",
     "stream_copy", "version", "PATH_NAMES", "F32", "BF16",
 ]
@@ -85,6 +92,14 @@ def lib() -> ctypes.CDLL:
     L.ce_scale_grad.restype = i32
     L.ce_fwd_loss.argtypes = [vp, vp, i64, i64, i32, vp, vp]
     L.ce_fwd_loss.restype = i32
+    L.ce_softmax_fwd.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    L.ce_softmax_fwd.restype = i32
+    L.ce_softmax_bwd.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+    L.ce_softmax_bwd.restype = i32
+    L.ce_shard_stats.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp]
+    L.ce_shard_stats.restype = i32
+    L.ce_shard_grad.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp, i32, vp, vp, vp, vp]
+    L.ce_shard_grad.restype = i32
     _lib = L
     return L
 
@@ -351,3 +366,147 @@ def cross_entropy_loss(logits, targets):
     ``loss.backward()`` gives ``logits.grad = (softmax - onehot) / B`` times
     the upstream gradient, from the gradient formed in the forward pass."""
     return _function().apply(logits, targets)
+
+
+# ---------------------------------------------------------------- softmax
+
+def _check_pair(a, b, what: str):
+    if b.dtype != a.dtype or b.shape != a.shape:
+        raise TypeError(f"{what} must match in dtype and shape")
+
+
+def softmax_fwd_into(x, y, lse=None) -> None:
+    """Row-wise softmax of ``[B, C]`` x into y (y may be x itself), and the
+    rows' log-sum-exp into lse (float32 [B]) when it is given."""
+    torch = _torch()
+    _check_cuda(x, y, *([lse] if lse is not None else []))
+    if x.dim() != 2:
+        raise ValueError("x must be [B, C]")
+    _check_pair(x, y, "x and y")
+    B, C = x.shape
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (B,)):
+        raise TypeError("lse must be float32 of shape [B]")
+    st = lib().ce_softmax_fwd(x.data_ptr(), B, C, _dtype_code(x), y.data_ptr(),
+                              lse.data_ptr() if lse is not None else None,
+                              _stream_ptr(x.device))
+    _check(st, "ce_softmax_fwd")
+
+
+def softmax_fwd(x, with_lse: bool = False):
+    """The row-wise softmax of ``[B, C]`` x; with ``with_lse`` also the rows'
+    log-sum-exp (float32 [B])."""
+    torch = _torch()
+    y = torch.empty_like(x)
+    lse = torch.empty(x.shape[0], dtype=torch.float32, device=x.device) if with_lse else None
+    softmax_fwd_into(x, y, lse)
+    return (y, lse) if with_lse else y
+
+
+def softmax_bwd_into(y, dy, dx) -> None:
+    """dx = y * (dy - rowsum(dy * y)), the backward of the row-wise softmax
+    from its output y and the upstream gradient dy (dx may be y or dy)."""
+    _check_cuda(y, dy, dx)
+    if y.dim() != 2:
+        raise ValueError("y must be [B, C]")
+    _check_pair(y, dy, "y and dy")
+    _check_pair(y, dx, "y and dx")
+    B, C = y.shape
+    st = lib().ce_softmax_bwd(y.data_ptr(), dy.data_ptr(), B, C, _dtype_code(y), dx.data_ptr(),
+                              _stream_ptr(y.device))
+    _check(st, "ce_softmax_bwd")
+
+
+def softmax_bwd(y, dy):
+    torch = _torch()
+    dx = torch.empty_like(y)
+    softmax_bwd_into(y, dy, dx)
+    return dx
+
+
+_softmax_fn = None
+
+
+def softmax(x):
+    """Differentiable row-wise softmax of ``[B, C]`` x: the forward keeps its
+    output for the backward (ce_softmax_fwd, then ce_softmax_bwd)."""
+    global _softmax_fn
+    if _softmax_fn is None:
+        torch = _torch()
+
+        class SoftmaxFunction(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, x):
+                y = softmax_fwd(x.detach().contiguous())
+                ctx.save_for_backward(y)
+                return y
+
+            @staticmethod
+            def backward(ctx, dy):
+                (y,) = ctx.saved_tensors
+                return softmax_bwd(y, dy.contiguous())
+
+        _softmax_fn = SoftmaxFunction
+    return _softmax_fn.apply(x)
+
+
+# ------------------------------------------------------ vocabulary shards
+
+def shard_stats_into(logits, targets, col0: int, records) -> None:
+    """Per-row record (c, sx, zt, own) of one vocabulary shard: the columns
+    [col0, col0 + C) of the rows, as a contiguous ``[B, C]`` tensor, with
+    the rows' global int32 targets.  records: float32 ``[B, 4]``."""
+    torch = _torch()
+    _check_cuda(logits, targets, records)
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, C]")
+    B, C = logits.shape
+    if targets.dtype != torch.int32 or targets.shape != (B,):
+        raise TypeError("targets must be int32 of shape [B]")
+    if records.dtype != torch.float32 or records.shape != (B, 4):
+        raise TypeError("records must be float32 of shape [B, 4]")
+    st = lib().ce_shard_stats(logits.data_ptr(), targets.data_ptr(), B, C, int(col0),
+                              _dtype_code(logits), records.data_ptr(), _stream_ptr(logits.device))
+    _check(st, "ce_shard_stats")
+
+
+def shard_stats(logits, targets, col0: int):
+    torch = _torch()
+    rec = torch.empty((logits.shape[0], 4), dtype=torch.float32, device=logits.device)
+    shard_stats_into(logits, targets, col0, rec)
+    return rec
+
+
+def shard_grad_into(logits, targets, col0: int, C_total: int, records, grad, loss_rows=None,
+                    grad_scale=None) -> None:
+    """One shard's gradient (and, when loss_rows is given, the rows' losses)
+    from the records of all shards, float32 ``[N, B, 4]`` in shard order."""
+    torch = _torch()
+    extra = [t for t in (loss_rows, grad_scale) if t is not None]
+    _check_cuda(logits, targets, records, grad, *extra)
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, C]")
+    B, C = logits.shape
+    if targets.dtype != torch.int32 or targets.shape != (B,):
+        raise TypeError("targets must be int32 of shape [B]")
+    if records.dtype != torch.float32 or records.dim() != 3 or records.shape[1:] != (B, 4):
+        raise TypeError("records must be float32 of shape [N, B, 4]")
+    _check_pair(logits, grad, "logits and grad")
+    if loss_rows is not None and (loss_rows.dtype != torch.float32 or loss_rows.shape != (B,)):
+        raise TypeError("loss_rows must be float32 of shape [B]")
+    if grad_scale is not None:
+        _check_scalar(grad_scale, "grad_scale")
+    st = lib().ce_shard_grad(logits.data_ptr(), targets.data_ptr(), B, C, int(col0), int(C_total),
+                             _dtype_code(logits), records.data_ptr(), records.shape[0],
+                             grad.data_ptr(),
+                             loss_rows.data_ptr() if loss_rows is not None else None,
+                             grad_scale.data_ptr() if grad_scale is not None else None,
+                             _stream_ptr(logits.device))
+    _check(st, "ce_shard_grad")
+
+
+def shard_grad(logits, targets, col0: int, C_total: int, records, with_loss: bool = False):
+    torch = _torch()
+    grad = torch.empty_like(logits)
+    lr = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device) if with_loss else None
+    shard_grad_into(logits, targets, col0, C_total, records, grad, lr)
+    return (grad, lr) if with_loss else grad

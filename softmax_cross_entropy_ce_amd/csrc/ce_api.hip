@@ -7,6 +7,8 @@
 
 #include "ce.h"
 #include "ce_parts.h"
+#include "ce_shard.h"
+#include "softmax_bwd.h"
 
 namespace {
 
@@ -70,27 +72,27 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 int launched() { return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_LAUNCH; }
 
 // ------------------------------------------------------------------ path 1
-template <typename T, int S, int EPL, int VW, bool GRAD>
+template <typename T, int S, int EPL, int VW, int OP, bool GRAD>
 int launch_short_cfg(const T* z, const int32_t* t, int64_t B, int C, ce::RowScale rs, T* g, float* l,
                      hipStream_t st) {
   constexpr int rpb = ce::kShortThreads / S;
   const int64_t blocks = (B + rpb - 1) / rpb;
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL((ce::ce_short_kernel<T, S, EPL, VW, GRAD>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((ce::ce_short_kernel<T, S, EPL, VW, GRAD, OP>), dim3((unsigned)blocks),
                      dim3(ce::kShortThreads), 0, st, z, t, B, C, rs, g, l);
   return launched();
 }
 
-template <typename T, int S, int EPL, bool GRAD>
+template <typename T, int S, int EPL, int OP, bool GRAD>
 int launch_short_vw(int vw, const T* z, const int32_t* t, int64_t B, int C, ce::RowScale rs, T* g,
                     float* l, hipStream_t st) {
   switch (vw) {
-    case 1: return launch_short_cfg<T, S, EPL, 1, GRAD>(z, t, B, C, rs, g, l, st);
-    case 2: return launch_short_cfg<T, S, EPL, 2, GRAD>(z, t, B, C, rs, g, l, st);
-    case 4: return launch_short_cfg<T, S, EPL, 4, GRAD>(z, t, B, C, rs, g, l, st);
+    case 1: return launch_short_cfg<T, S, EPL, 1, OP, GRAD>(z, t, B, C, rs, g, l, st);
+    case 2: return launch_short_cfg<T, S, EPL, 2, OP, GRAD>(z, t, B, C, rs, g, l, st);
+    case 4: return launch_short_cfg<T, S, EPL, 4, OP, GRAD>(z, t, B, C, rs, g, l, st);
     case 8:
       if constexpr (sizeof(T) == 2 && EPL >= 8)
-        return launch_short_cfg<T, S, EPL, 8, GRAD>(z, t, B, C, rs, g, l, st);
+        return launch_short_cfg<T, S, EPL, 8, OP, GRAD>(z, t, B, C, rs, g, l, st);
       return CE_ERR_PATH;
     default: return CE_ERR_PATH;
   }
@@ -110,7 +112,7 @@ int short_vw(int64_t C, int es, uintptr_t zaddr, uintptr_t gaddr, int epl) {
 // of two that covers the row with EPL elements per lane (EPL = 16 bytes of
 // elements, more only at S = 16).  Lanes of a row read adjacent vectors,
 // so a load instruction covers 64/S consecutive rows.
-template <typename T, bool GRAD>
+template <typename T, int OP, bool GRAD>
 int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g, float* l,
                  hipStream_t st) {
   if (C > kShortMaxC) return CE_ERR_PATH;
@@ -118,16 +120,18 @@ int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScal
   constexpr int E16 = 16 / es;  // elements in 16 bytes
   const int c = (int)C;
   auto vw = [&](int epl) { return short_vw(C, es, (uintptr_t)z, (uintptr_t)g, epl); };
-  if (C <= E16) return launch_short_vw<T, 1, E16, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
-  if (C <= 2 * E16) return launch_short_vw<T, 2, E16, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
-  if (C <= 4 * E16) return launch_short_vw<T, 4, E16, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
-  if (C <= 8 * E16) return launch_short_vw<T, 8, E16, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
-  if (C <= 16 * E16) return launch_short_vw<T, 16, E16, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= E16) return launch_short_vw<T, 1, E16, OP, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= 2 * E16) return launch_short_vw<T, 2, E16, OP, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= 4 * E16) return launch_short_vw<T, 4, E16, OP, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= 8 * E16) return launch_short_vw<T, 8, E16, OP, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
+  if (C <= 16 * E16) return launch_short_vw<T, 16, E16, OP, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
   if constexpr (E16 < 16) {
-    if (C <= 32 * E16) return launch_short_vw<T, 16, 2 * E16, GRAD>(vw(2 * E16), z, t, B, c, rs, g, l, st);
+    if (C <= 32 * E16)
+      return launch_short_vw<T, 16, 2 * E16, OP, GRAD>(vw(2 * E16), z, t, B, c, rs, g, l, st);
   }
   if constexpr (E16 < 8) {
-    if (C <= 64 * E16) return launch_short_vw<T, 16, 4 * E16, GRAD>(vw(4 * E16), z, t, B, c, rs, g, l, st);
+    if (C <= 64 * E16)
+      return launch_short_vw<T, 16, 4 * E16, OP, GRAD>(vw(4 * E16), z, t, B, c, rs, g, l, st);
   }
   return CE_ERR_PATH;
 }
@@ -147,10 +151,10 @@ int resident_blocks(const void* kernel, int nt) {
   return cus * per_cu;
 }
 
-template <typename T, int NT, int NV, bool GRAD>
+template <typename T, int NT, int NV, int OP, bool GRAD>
 int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
                    float* l, hipStream_t st) {
-  auto kern = ce::ce_row_kernel<T, NT, NV, GRAD>;
+  auto kern = ce::ce_row_kernel<T, NT, NV, GRAD, OP>;
   const int res = resident_blocks(reinterpret_cast<const void*>(kern), NT);
   if (res < 1) return CE_ERR_LAUNCH;
   const int64_t grid = B < res ? B : res;
@@ -162,10 +166,10 @@ int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowSc
 // the next row's prefix prefetched into LDS.
 constexpr int kLdsPrefetchSlots = 9;  // 9 x 16 KB of the 160 KB of LDS
 
-template <typename T>
+template <typename T, int OP>
 int launch_row_lds(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
                    float* l, hipStream_t st) {
-  auto kern = ce::ce_row_lds_kernel<T, 16, kLdsPrefetchSlots>;
+  auto kern = ce::ce_row_lds_kernel<T, 16, kLdsPrefetchSlots, OP>;
   const int res = resident_blocks(reinterpret_cast<const void*>(kern), 1024);
   if (res < 1) return CE_ERR_LAUNCH;
   const int64_t grid = B < res ? B : res;
@@ -173,11 +177,12 @@ int launch_row_lds(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowSc
   return launched();
 }
 
-template <typename T, bool GRAD>
+template <typename T, int OP, bool GRAD>
 int launch_row(RowCfg cfg, const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
                float* l, hipStream_t st) {
-#define CE_ROW_CASE(NT_, NV_) \
-  if (cfg.nt == NT_ && cfg.nv == NV_) return launch_row_cfg<T, NT_, NV_, GRAD>(z, t, B, C, rs, g, l, st);
+#define CE_ROW_CASE(NT_, NV_)                                                           \
+  if (cfg.nt == NT_ && cfg.nv == NV_)                                                   \
+    return launch_row_cfg<T, NT_, NV_, OP, GRAD>(z, t, B, C, rs, g, l, st);
   CE_ROW_CASE(64, 1)
   CE_ROW_CASE(64, 2)
   CE_ROW_CASE(64, 4)
@@ -204,51 +209,52 @@ RowCfg resident_cfg(int64_t C, int es, bool* ok) {
 }
 
 // ---------------------------------------------------------------- path 4
-template <typename T, int P, int NT, int NR, int NL, int NXW>
+template <typename T, int P, int NT, int NR, int NL, int NXW, int OP>
 int launch_parts_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
                      float* l, hipStream_t st) {
   const int64_t blocks = P * ((B + 7) / 8 * 8);
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL((ce::ce_part_kernel<T, P, NT, NR, NL, NXW>), dim3((unsigned)blocks), dim3(NT),
+  hipLaunchKernelGGL((ce::ce_part_kernel<T, P, NT, NR, NL, NXW, OP>), dim3((unsigned)blocks), dim3(NT),
                      0, st, z, t, B, (int)C, rs, g, l,
                      g_part_polls.load(std::memory_order_relaxed),
                      g_part_counter.load(std::memory_order_relaxed));
   return launched();
 }
 
-template <typename T>
+template <typename T, int OP>
 int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g, float* l,
                  hipStream_t st) {
   const int64_t nb = body_vectors_max(C, sizeof(T));
-  if (nb <= kPartsOneSmall) return launch_parts_cfg<T, 1, 1024, 4, 0, 0>(z, t, B, C, rs, g, l, st);
-  if (nb <= kPartsOne) return launch_parts_cfg<T, 1, 1024, 8, 2, 0>(z, t, B, C, rs, g, l, st);
-  if (nb <= kPartsTwoRegs) return launch_parts_cfg<T, 2, 1024, 8, 0, 0>(z, t, B, C, rs, g, l, st);
-  if (nb <= kPartsTwo) return launch_parts_cfg<T, 2, 1024, 8, 4, 0>(z, t, B, C, rs, g, l, st);
+  if (nb <= kPartsOneSmall) return launch_parts_cfg<T, 1, 1024, 4, 0, 0, OP>(z, t, B, C, rs, g, l, st);
+  if (nb <= kPartsOne) return launch_parts_cfg<T, 1, 1024, 8, 2, 0, OP>(z, t, B, C, rs, g, l, st);
+  if (nb <= kPartsTwoRegs) return launch_parts_cfg<T, 2, 1024, 8, 0, 0, OP>(z, t, B, C, rs, g, l, st);
+  if (nb <= kPartsTwo) return launch_parts_cfg<T, 2, 1024, 8, 4, 0, OP>(z, t, B, C, rs, g, l, st);
   return CE_ERR_PATH;
 }
 
-// GRAD false: the loss only, on the short, resident or long path (nothing
-// has to stay on chip for a gradient, so no row parts).
-template <typename T, bool GRAD>
+// GRAD false: the per-row output only, on the short, resident or long path
+// (nothing has to stay on chip for a gradient, so no row parts).
+template <typename T, int OP, bool GRAD>
 int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g, float* l,
-              const float* gmul, hipStream_t st) {
-  const ce::RowScale rs{1.0f / (float)B, gmul};
+              ce::RowScale rs, hipStream_t st) {
   switch (path) {
     case kPathShort:
-      return launch_short<T, GRAD>(z, t, B, C, rs, g, l, st);
+      return launch_short<T, OP, GRAD>(z, t, B, C, rs, g, l, st);
     case kPathResident: {
       bool ok = false;
       const RowCfg cfg = resident_cfg(C, sizeof(T), &ok);
       if (!ok) return CE_ERR_PATH;
-      if (GRAD && cfg.nt == 1024 && cfg.nv == 16) return launch_row_lds<T>(z, t, B, C, rs, g, l, st);
-      return launch_row<T, GRAD>(cfg, z, t, B, C, rs, g, l, st);
+      if constexpr (GRAD) {
+        if (cfg.nt == 1024 && cfg.nv == 16) return launch_row_lds<T, OP>(z, t, B, C, rs, g, l, st);
+      }
+      return launch_row<T, OP, GRAD>(cfg, z, t, B, C, rs, g, l, st);
     }
     case kPathLong: {
       const bool forced = g_force_path.load(std::memory_order_relaxed) == kPathLong;
-      return launch_row<T, GRAD>(forced ? kLongTestCfg : kLongCfg, z, t, B, C, rs, g, l, st);
+      return launch_row<T, OP, GRAD>(forced ? kLongTestCfg : kLongCfg, z, t, B, C, rs, g, l, st);
     }
     case kPathParts:
-      if constexpr (GRAD) return launch_parts<T>(z, t, B, C, rs, g, l, st);
+      if constexpr (GRAD) return launch_parts<T, OP>(z, t, B, C, rs, g, l, st);
       return CE_ERR_PATH;
     default:
       return CE_ERR_PATH;
@@ -290,16 +296,41 @@ extern "C" {
 
 namespace {
 
-// grad_out == nullptr: the loss only.  grad_out == logits: the gradient in
-// place of the logits.
-int fwd_impl(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
-             void* grad_out, float* loss_out, const float* gmul, void* stream) {
-  if (!logits || !targets || !loss_out) return CE_ERR_NULL;
+template <typename T>
+int fwd_dispatch(int op, int path, const void* z, const int32_t* t, int64_t B, int64_t C, void* g,
+                 float* l, ce::RowScale rs, hipStream_t st) {
+  const T* zz = (const T*)z;
+  T* gg = (T*)g;
+  switch (op) {
+    case ce::kOpCE:
+      if (!g) return fwd_typed<T, ce::kOpCE, false>(path, zz, t, B, C, nullptr, l, rs, st);
+      return fwd_typed<T, ce::kOpCE, true>(path, zz, t, B, C, gg, l, rs, st);
+    case ce::kOpSoftmax:
+      return fwd_typed<T, ce::kOpSoftmax, true>(path, zz, t, B, C, gg, l, rs, st);
+    case ce::kOpShard:
+      return fwd_typed<T, ce::kOpShard, false>(path, zz, t, B, C, nullptr, l, rs, st);
+    default:
+      return CE_ERR_PATH;
+  }
+}
+
+// The row kernels' entry.  op kOpCE: targets and loss_out required;
+// grad_out null gives the loss only, grad_out == logits the gradient in
+// place.  op kOpSoftmax: targets unused; grad_out (the softmax) required,
+// or the logits themselves; loss_out (the log-sum-exp) may be null.  op
+// kOpShard: targets and loss_out (B records of 4 floats, 16-byte aligned)
+// required, grad_out null; col0 is the shard's first column.
+int fwd_impl(int op, const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
+             void* grad_out, float* loss_out, const float* gmul, int64_t col0, void* stream) {
+  if (!logits) return CE_ERR_NULL;
+  if (op != ce::kOpSoftmax && (!targets || !loss_out)) return CE_ERR_NULL;
+  if (op == ce::kOpSoftmax && !grad_out) return CE_ERR_NULL;
   if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
   if (B <= 0 || C <= 0 || B > 0x7fffffffLL || C > CE_MAX_C) return CE_ERR_SHAPE;
   const int es = elem_size(dtype);
   const uintptr_t z = (uintptr_t)logits, g = (uintptr_t)grad_out;
-  if (z % es || g % es || (uintptr_t)targets % 4 || (uintptr_t)loss_out % 4) return CE_ERR_ALIGN;
+  if (z % es || g % es || (uintptr_t)targets % 4) return CE_ERR_ALIGN;
+  if ((uintptr_t)loss_out % (op == ce::kOpShard ? 16 : 4)) return CE_ERR_ALIGN;
   if (gmul && (uintptr_t)gmul % 4) return CE_ERR_ALIGN;
   if (grad_out && (z > g ? z - g : g - z) % 16) return CE_ERR_ALIGN;
   if ((uint64_t)B > UINT64_MAX / ((uint64_t)C * es)) return CE_ERR_SHAPE;
@@ -315,19 +346,11 @@ int fwd_impl(const void* logits, const int32_t* targets, int64_t B, int64_t C, i
       path = path_without_parts(C, es);
     }
   }
+  const ce::RowScale rs{1.0f / (float)B, gmul, col0};
   const hipStream_t st = as_stream(stream);
-  if (dtype == CE_F32) {
-    if (!grad_out)
-      return fwd_typed<float, false>(path, (const float*)logits, targets, B, C, nullptr, loss_out,
-                                     gmul, st);
-    return fwd_typed<float, true>(path, (const float*)logits, targets, B, C, (float*)grad_out,
-                                  loss_out, gmul, st);
-  }
-  if (!grad_out)
-    return fwd_typed<__bf16, false>(path, (const __bf16*)logits, targets, B, C, nullptr, loss_out,
-                                    gmul, st);
-  return fwd_typed<__bf16, true>(path, (const __bf16*)logits, targets, B, C, (__bf16*)grad_out,
-                                 loss_out, gmul, st);
+  if (dtype == CE_F32)
+    return fwd_dispatch<float>(op, path, logits, targets, B, C, grad_out, loss_out, rs, st);
+  return fwd_dispatch<__bf16>(op, path, logits, targets, B, C, grad_out, loss_out, rs, st);
 }
 
 template <typename T>
@@ -341,6 +364,130 @@ int launch_scale(T* g, int64_t n, const float* scale, hipStream_t st) {
   return launched();
 }
 
+// ------------------------------------------------------- softmax backward
+// Row configurations that hold both y and dy of a row in registers (NT
+// threads x NV 16-byte vectors of each); longer rows stream the rest.
+constexpr RowCfg kBwdCfgs[] = {{64, 1},   {64, 2},   {64, 4},   {256, 2},
+                               {256, 4},  {1024, 2}, {1024, 4}, {1024, 8}};
+constexpr RowCfg kBwdLongCfg = {1024, 8};
+constexpr RowCfg kBwdLongTestCfg = {256, 1};
+
+template <typename T, int S, int EPL, int VW>
+int launch_bwd_short_cfg(const T* y, const T* dy, int64_t B, int C, T* dx, hipStream_t st) {
+  constexpr int rpb = ce::kShortThreads / S;
+  const int64_t blocks = (B + rpb - 1) / rpb;
+  if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
+  hipLaunchKernelGGL((ce::sm_bwd_short_kernel<T, S, EPL, VW>), dim3((unsigned)blocks),
+                     dim3(ce::kShortThreads), 0, st, y, dy, B, C, dx);
+  return launched();
+}
+
+template <typename T, int S, int EPL>
+int launch_bwd_short_vw(int vw, const T* y, const T* dy, int64_t B, int C, T* dx, hipStream_t st) {
+  switch (vw) {
+    case 1: return launch_bwd_short_cfg<T, S, EPL, 1>(y, dy, B, C, dx, st);
+    case 2: return launch_bwd_short_cfg<T, S, EPL, 2>(y, dy, B, C, dx, st);
+    case 4: return launch_bwd_short_cfg<T, S, EPL, 4>(y, dy, B, C, dx, st);
+    case 8:
+      if constexpr (sizeof(T) == 2 && EPL >= 8) return launch_bwd_short_cfg<T, S, EPL, 8>(y, dy, B, C, dx, st);
+      return CE_ERR_PATH;
+    default: return CE_ERR_PATH;
+  }
+}
+
+// The short layout of the loss (S lanes per row, about 16 bytes of each
+// array per lane), with a vector width that all three arrays' rows allow.
+template <typename T>
+int launch_bwd_short(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipStream_t st) {
+  if (C > kShortMaxC) return CE_ERR_PATH;
+  constexpr int es = sizeof(T);
+  constexpr int E16 = 16 / es;
+  const int c = (int)C;
+  const uintptr_t other = (uintptr_t)dy | (uintptr_t)dx;  // aligned iff both are
+  auto vw = [&](int epl) { return short_vw(C, es, (uintptr_t)y, other, epl); };
+  if (C <= E16) return launch_bwd_short_vw<T, 1, E16>(vw(E16), y, dy, B, c, dx, st);
+  if (C <= 2 * E16) return launch_bwd_short_vw<T, 2, E16>(vw(E16), y, dy, B, c, dx, st);
+  if (C <= 4 * E16) return launch_bwd_short_vw<T, 4, E16>(vw(E16), y, dy, B, c, dx, st);
+  if (C <= 8 * E16) return launch_bwd_short_vw<T, 8, E16>(vw(E16), y, dy, B, c, dx, st);
+  if (C <= 16 * E16) return launch_bwd_short_vw<T, 16, E16>(vw(E16), y, dy, B, c, dx, st);
+  if constexpr (E16 < 16) {
+    if (C <= 32 * E16) return launch_bwd_short_vw<T, 16, 2 * E16>(vw(2 * E16), y, dy, B, c, dx, st);
+  }
+  if constexpr (E16 < 8) {
+    if (C <= 64 * E16) return launch_bwd_short_vw<T, 16, 4 * E16>(vw(4 * E16), y, dy, B, c, dx, st);
+  }
+  return CE_ERR_PATH;
+}
+
+template <typename T, int NT, int NV>
+int launch_bwd_row_cfg(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipStream_t st) {
+  auto kern = ce::sm_bwd_row_kernel<T, NT, NV>;
+  const int res = resident_blocks(reinterpret_cast<const void*>(kern), NT);
+  if (res < 1) return CE_ERR_LAUNCH;
+  const int64_t grid = B < res ? B : res;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), 0, st, y, dy, B, (int)C, dx);
+  return launched();
+}
+
+template <typename T>
+int launch_bwd_row(RowCfg cfg, const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipStream_t st) {
+#define CE_BWD_CASE(NT_, NV_) \
+  if (cfg.nt == NT_ && cfg.nv == NV_) return launch_bwd_row_cfg<T, NT_, NV_>(y, dy, B, C, dx, st);
+  CE_BWD_CASE(64, 1)
+  CE_BWD_CASE(64, 2)
+  CE_BWD_CASE(64, 4)
+  CE_BWD_CASE(256, 1)
+  CE_BWD_CASE(256, 2)
+  CE_BWD_CASE(256, 4)
+  CE_BWD_CASE(1024, 2)
+  CE_BWD_CASE(1024, 4)
+  CE_BWD_CASE(1024, 8)
+#undef CE_BWD_CASE
+  return CE_ERR_PATH;
+}
+
+int bwd_auto_path(int64_t C, int es) {
+  if (C <= kShortMaxC) return kPathShort;
+  return row_vectors(C, es) <= (int64_t)kBwdLongCfg.nt * kBwdLongCfg.nv ? kPathResident : kPathLong;
+}
+
+template <typename T>
+int softmax_bwd_typed(int path, const T* y, const T* dy, int64_t B, int64_t C, T* dx,
+                      hipStream_t st) {
+  switch (path) {
+    case kPathShort:
+      return launch_bwd_short<T>(y, dy, B, C, dx, st);
+    case kPathResident: {
+      const int64_t need = row_vectors(C, sizeof(T));
+      for (const RowCfg& r : kBwdCfgs)
+        if ((int64_t)r.nt * r.nv >= need) return launch_bwd_row<T>(r, y, dy, B, C, dx, st);
+      return CE_ERR_PATH;
+    }
+    case kPathLong: {
+      const bool forced = g_force_path.load(std::memory_order_relaxed) == kPathLong;
+      return launch_bwd_row<T>(forced ? kBwdLongTestCfg : kBwdLongCfg, y, dy, B, C, dx, st);
+    }
+    default:
+      return CE_ERR_PATH;
+  }
+}
+
+// --------------------------------------------------------- vocabulary shards
+constexpr int kMaxShards = 1024;
+
+template <typename T>
+int launch_shard_grad(const T* z, const int32_t* t, int64_t B, int64_t C, int64_t col0,
+                      int64_t Ctot, const float* recs, int nshards, ce::RowScale rs, T* g,
+                      float* l, hipStream_t st) {
+  const int64_t nb = body_vectors_max(C, sizeof(T));
+  const int64_t chunks = nb > 0 ? (nb + ce::kShardChunk - 1) / ce::kShardChunk : 1;
+  if (B * chunks > 0x7fffffffLL) return CE_ERR_SHAPE;
+  hipLaunchKernelGGL(ce::ce_shard_grad_kernel<T>, dim3((unsigned)(B * chunks)),
+                     dim3(ce::kShardThreads), 0, st, z, t, B, (int)C, col0, Ctot,
+                     reinterpret_cast<const ce::f32x4*>(recs), nshards, rs, g, l, (int)chunks);
+  return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -348,19 +495,20 @@ extern "C" {
 int ce_fwd_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
                 void* grad_out, float* loss_out, void* stream) {
   if (!grad_out) return CE_ERR_NULL;
-  return fwd_impl(logits, targets, B, C, dtype, grad_out, loss_out, nullptr, stream);
+  return fwd_impl(ce::kOpCE, logits, targets, B, C, dtype, grad_out, loss_out, nullptr, 0, stream);
 }
 
 int ce_fwd_loss(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
                 float* loss_out, void* stream) {
-  return fwd_impl(logits, targets, B, C, dtype, nullptr, loss_out, nullptr, stream);
+  return fwd_impl(ce::kOpCE, logits, targets, B, C, dtype, nullptr, loss_out, nullptr, 0, stream);
 }
 
 int ce_fwd_grad_scaled(const void* logits, const int32_t* targets, int64_t B, int64_t C,
                        int dtype, void* grad_out, float* loss_out, const float* grad_scale,
                        void* stream) {
   if (!grad_scale || !grad_out) return CE_ERR_NULL;
-  return fwd_impl(logits, targets, B, C, dtype, grad_out, loss_out, grad_scale, stream);
+  return fwd_impl(ce::kOpCE, logits, targets, B, C, dtype, grad_out, loss_out, grad_scale, 0,
+                  stream);
 }
 
 int ce_scale_grad(void* grad, int64_t n, int dtype, const float* scale, void* stream) {
@@ -374,6 +522,68 @@ int ce_scale_grad(void* grad, int64_t n, int dtype, const float* scale, void* st
   const hipStream_t st = as_stream(stream);
   if (dtype == CE_F32) return launch_scale<float>((float*)grad, n, scale, st);
   return launch_scale<__bf16>((__bf16*)grad, n, scale, st);
+}
+
+int ce_softmax_fwd(const void* x, int64_t B, int64_t C, int dtype, void* y_out, float* lse_out,
+                   void* stream) {
+  return fwd_impl(ce::kOpSoftmax, x, nullptr, B, C, dtype, y_out, lse_out, nullptr, 0, stream);
+}
+
+int ce_softmax_bwd(const void* y, const void* dy, int64_t B, int64_t C, int dtype, void* dx_out,
+                   void* stream) {
+  if (!y || !dy || !dx_out) return CE_ERR_NULL;
+  if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
+  if (B <= 0 || C <= 0 || B > 0x7fffffffLL || C > CE_MAX_C) return CE_ERR_SHAPE;
+  const int es = elem_size(dtype);
+  const uintptr_t a = (uintptr_t)y, b = (uintptr_t)dy, o = (uintptr_t)dx_out;
+  if (a % es || b % es || o % es) return CE_ERR_ALIGN;
+  if ((a > b ? a - b : b - a) % 16 || (a > o ? a - o : o - a) % 16) return CE_ERR_ALIGN;
+  if ((uint64_t)B > UINT64_MAX / ((uint64_t)C * es)) return CE_ERR_SHAPE;
+  const uintptr_t n = (uintptr_t)B * (uintptr_t)C * es;
+  // dx may be y or dy themselves (every element is read before the thread
+  // that reads it writes it), but no other overlap
+  if (o != a && overlaps(o, n, a, n)) return CE_ERR_ALIAS;
+  if (o != b && overlaps(o, n, b, n)) return CE_ERR_ALIAS;
+  const int forced = g_force_path.load(std::memory_order_relaxed);
+  const int path = forced ? forced : bwd_auto_path(C, es);
+  const hipStream_t st = as_stream(stream);
+  if (dtype == CE_F32)
+    return softmax_bwd_typed<float>(path, (const float*)y, (const float*)dy, B, C, (float*)dx_out, st);
+  return softmax_bwd_typed<__bf16>(path, (const __bf16*)y, (const __bf16*)dy, B, C,
+                                   (__bf16*)dx_out, st);
+}
+
+int ce_shard_stats(const void* logits, const int32_t* targets, int64_t B, int64_t C, int64_t col0,
+                   int dtype, float* records_out, void* stream) {
+  if (col0 < 0 || col0 > 0x7fffffffLL) return CE_ERR_SHAPE;
+  return fwd_impl(ce::kOpShard, logits, targets, B, C, dtype, nullptr, records_out, nullptr, col0,
+                  stream);
+}
+
+int ce_shard_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C, int64_t col0,
+                  int64_t C_total, int dtype, const float* records, int n_shards, void* grad_out,
+                  float* loss_out, const float* grad_scale, void* stream) {
+  if (!logits || !targets || !records || !grad_out) return CE_ERR_NULL;
+  if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
+  if (B <= 0 || C <= 0 || B > 0x7fffffffLL || C > CE_MAX_C) return CE_ERR_SHAPE;
+  if (n_shards < 1 || n_shards > kMaxShards) return CE_ERR_SHAPE;
+  if (col0 < 0 || C_total < C || col0 > C_total - C || C_total > 0x7fffffffLL) return CE_ERR_SHAPE;
+  const int es = elem_size(dtype);
+  const uintptr_t z = (uintptr_t)logits, g = (uintptr_t)grad_out;
+  if (z % es || g % es || (uintptr_t)targets % 4 || (uintptr_t)records % 16) return CE_ERR_ALIGN;
+  if ((uintptr_t)loss_out % 4 || (uintptr_t)grad_scale % 4) return CE_ERR_ALIGN;
+  if ((z > g ? z - g : g - z) % 16) return CE_ERR_ALIGN;
+  if ((uint64_t)B > UINT64_MAX / ((uint64_t)C * es)) return CE_ERR_SHAPE;
+  const uintptr_t n = (uintptr_t)B * (uintptr_t)C * es;
+  if (g != z && overlaps(z, n, g, n)) return CE_ERR_ALIAS;
+  if (overlaps(g, n, (uintptr_t)records, (uintptr_t)n_shards * (uintptr_t)B * 16)) return CE_ERR_ALIAS;
+  const ce::RowScale rs{1.0f / (float)B, grad_scale, col0};
+  const hipStream_t st = as_stream(stream);
+  if (dtype == CE_F32)
+    return launch_shard_grad<float>((const float*)logits, targets, B, C, col0, C_total, records,
+                                    n_shards, rs, (float*)grad_out, loss_out, st);
+  return launch_shard_grad<__bf16>((const __bf16*)logits, targets, B, C, col0, C_total, records,
+                                   n_shards, rs, (__bf16*)grad_out, loss_out, st);
 }
 
 size_t ce_reduce_workspace_bytes(int64_t B) {
@@ -415,7 +625,7 @@ const char* ce_status_string(int status) {
     case CE_ERR_WORKSPACE: return "workspace missing or too small";
     case CE_ERR_LAUNCH: return "kernel launch failed";
     case CE_ERR_ALIGN: return "pointer alignment not supported";
-    case CE_ERR_ALIAS: return "grad_out overlaps logits";
+    case CE_ERR_ALIAS: return "an output overlaps an input in a way the call refuses";
     case CE_ERR_PATH: return "the forced kernel path cannot take this shape";
     default: return "unknown status";
   }

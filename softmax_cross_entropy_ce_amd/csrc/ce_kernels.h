@@ -24,12 +24,53 @@
 
 namespace ce {
 
+// What a row kernel computes from a row's max and sum of exponentials.
+//   kOpCE       the fused cross-entropy: per-row loss and gradient
+//               (softmax - onehot) / B.
+//   kOpSoftmax  the row-wise softmax (rumus project page, milestone M8c) and,
+//               where loss_rows is not null, the row's log-sum-exp.  No
+//               targets are read.
+//   kOpShard    the record of one vocabulary shard per row (the columns
+//               [col0, col0 + C) of a longer row): its max, its sum of
+//               exponentials without the target and the target logit where
+//               the shard holds it.  No per-element output.
+enum RowOp : int { kOpCE = 0, kOpSoftmax = 1, kOpShard = 2 };
+
 // Scales of a call: 1/B for the loss, and for the gradient 1/B times the
 // upstream gradient of the loss, a device scalar (gmul; null means 1).
+// col0: kOpShard's first column in the whole row.
 struct RowScale {
   float invB;
   const float* gmul;
+  int64_t col0;
 };
+
+// The target of a row as one call sees it: its column in the row (-1 when
+// the row has none here) and whether the row has a result.  A CE row has a
+// result when its target lies in [0, C); a shard row always has a record
+// (whether the target is valid at all is decided when the records are
+// combined).
+struct RowTarget {
+  int t;
+  bool valid;
+};
+
+template <int OP>
+__device__ __forceinline__ RowTarget row_target(const int32_t* targets, int64_t row, int C,
+                                                const RowScale& rs) {
+  if constexpr (OP == kOpSoftmax) {
+    return RowTarget{-1, true};
+  } else {
+    const int64_t t = (int64_t)targets[row] - (OP == kOpShard ? rs.col0 : 0);
+    const bool in = t >= 0 && t < C;
+    return RowTarget{in ? (int)t : -1, OP == kOpShard || in};
+  }
+}
+
+// A shard's per-row record, four floats (c, sx, zt, own): c = max z * log2(e)
+// rounded to float32, sx = the sum over the shard's non-target columns of
+// 2^(z log2e - c), zt = the target logit (0 where the shard does not hold
+// the target), own = 1 where it does, else 0.
 
 __device__ __forceinline__ float grad_mul(const RowScale& rs) {
   return rs.gmul != nullptr ? *rs.gmul : 1.0f;
@@ -61,6 +102,39 @@ __device__ __forceinline__ RowResult row_epilogue(float cg, float sx, float zt, 
   r.gt = valid ? -sx * scale : qnan;
   r.loss = valid ? lossB * invB : qnan;
   return r;
+}
+
+// The epilogue of each operation.  Softmax: scale = 1 / S (the target
+// fields are unused, S = sx) and loss = lse = ln2 * (cg + log2 S).  Shard
+// records need no epilogue.
+template <int OP>
+__device__ __forceinline__ RowResult row_finish(float cg, float sx, float zt, bool valid,
+                                                float invB, float gmul) {
+  if constexpr (OP == kOpCE) {
+    return row_epilogue(cg, sx, zt, valid, invB, gmul);
+  } else {
+    RowResult r;
+    r.scale = OP == kOpSoftmax ? 1.0f / sx : 0.f;
+    r.gt = 0.f;
+    r.loss = OP == kOpSoftmax ? kLn2 * (cg + log2_hw(sx)) : 0.f;
+    return r;
+  }
+}
+
+// The per-row output of each operation: CE the loss, softmax the
+// log-sum-exp (when out is not null), a shard its record (out holds
+// ShardRecords).
+template <int OP>
+__device__ __forceinline__ void store_row(float* out, int64_t row, const RowResult& rr, float cg,
+                                          float sx, float zt, bool has_t) {
+  if constexpr (OP == kOpCE) {
+    out[row] = rr.loss;
+  } else if constexpr (OP == kOpSoftmax) {
+    if (out != nullptr) out[row] = rr.loss;
+  } else {
+    const f32x4 rec = {cg, sx, has_t ? zt : 0.f, has_t ? 1.f : 0.f};
+    *reinterpret_cast<f32x4*>(out + 4 * row) = rec;
+  }
 }
 
 // ===========================================================================
@@ -153,8 +227,9 @@ struct VecIO<__bf16, VW> {
 
 constexpr int kShortThreads = 256;
 
-// GRAD false: the loss only; grad is not written (and may be null).
-template <typename T, int S, int EPL, int VW, bool GRAD>
+// GRAD false: the loss (or record) only; grad is not written (and may be
+// null).
+template <typename T, int S, int EPL, int VW, bool GRAD, int OP = kOpCE>
 __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
     const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B, int C,
     RowScale rs, T* __restrict__ grad, float* __restrict__ loss_rows) {
@@ -175,12 +250,13 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
   const rsrc_t rout = make_rsrc(grad + row0 * C, bytes);
   const uint32_t rowoff = (uint32_t)(tid / S) * (uint32_t)C * ES;
 
-  const int32_t t = live ? targets[row] : 0;
-  const bool valid = live && t >= 0 && t < C;
+  const RowTarget rt = live ? row_target<OP>(targets, row, C, rs) : RowTarget{-1, false};
+  const int t = rt.t;
+  const bool valid = live && rt.valid;
   // slot of the target in its owner lane: element c sits in vector c/VW,
   // lane (c/VW) % S, slot ((c/VW)/S)*VW + c%VW
-  const int tq = valid ? (t / VW) % S : -1;
-  const int tslot = valid ? ((t / VW) / S) * VW + t % VW : -1;
+  const int tq = t >= 0 ? (t / VW) % S : -1;
+  const int tslot = t >= 0 ? ((t / VW) / S) * VW + t % VW : -1;
   const bool owner = (q == tq);
 
   float f[EPL];
@@ -214,8 +290,8 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
     e[i] = exp2_hw(__builtin_fmaf(x, kLog2e, -cg));
   }
   const float sx = seg_allreduce<S>(tree_sum(e), OpAdd{});
-  const RowResult rr = row_epilogue(cg, sx, zt, valid, invB, gmul);
-  if (live && q == 0) loss_rows[row] = rr.loss;
+  const RowResult rr = row_finish<OP>(cg, sx, zt, valid, invB, gmul);
+  if (live && q == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
   if constexpr (!GRAD) return;
 
 #pragma unroll
@@ -279,9 +355,9 @@ __device__ __forceinline__ RowGeom row_geom(const T* rp, int C) {
   return g;
 }
 
-// GRAD false: the loss only; grad is not written (and may be null), and the
-// streamed part of a long row is read once.
-template <typename T, int NT, int NV, bool GRAD>
+// GRAD false: the loss (or record) only; grad is not written (and may be
+// null), and the streamed part of a long row is read once.
+template <typename T, int NT, int NV, bool GRAD, int OP = kOpCE>
 __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits,
                                                     const int32_t* __restrict__ targets,
                                                     int64_t B, int C, RowScale rs,
@@ -320,11 +396,12 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
     const rsrc_t rin = make_rsrc(rp + geo.h, (uint32_t)nb * 16u);
     const rsrc_t rout = make_rsrc(gp + geo.h, (uint32_t)nb * 16u);
 
-    const int32_t t = targets[row];
-    const bool valid = t >= 0 && t < C;
+    const RowTarget rt = row_target<OP>(targets, row, C, rs);
+    const int t = rt.t;
+    const bool valid = rt.valid;
     // where the target lives: body vector tv (element tj), or an edge element
     const int tb = t - geo.h;
-    const bool t_in_body = valid && tb >= 0 && tb < nb * VE;
+    const bool t_in_body = t >= 0 && tb >= 0 && tb < nb * VE;
     const int tv = t_in_body ? tb / VE : -1;                                  // uniform
     const int tj = t_in_body ? tb % VE : -1;                                  // uniform
     const int own_k = (t_in_body && tv < NT * NV) ? tv / NT : -1;             // uniform
@@ -336,7 +413,7 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
     else if (tid - geo.h < geo.ntail)
       xe = geo.tail0 + (tid - geo.h);
     const float xs = xe >= 0 ? E::load1(rp + xe) : kNegInf;
-    const float zt = valid ? E::load1(rp + t) : 0.f;
+    const float zt = t >= 0 ? E::load1(rp + t) : 0.f;
 
     // Phase B: online max / sum-exp over the thread's elements
     float c = kLowest, s = 0.f;
@@ -394,8 +471,8 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
       cg = wave_uniform(seg_allreduce<16>(ci, OpMax{}));
       sx = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
     }
-    const RowResult rr = row_epilogue(cg, sx, zt, valid, invB, gmul);
-    if (tid == 0) loss_rows[row] = rr.loss;
+    const RowResult rr = row_finish<OP>(cg, sx, zt, valid, invB, gmul);
+    if (tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
 
     // Phase C: gradient from the registers; each slot is refilled with the
     // next row's vector as soon as it has been widened.  After the last row
@@ -505,7 +582,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <typename T, int NV, int PF>
+template <typename T, int NV, int PF, int OP = kOpCE>
 __global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ logits,
                                                           const int32_t* __restrict__ targets,
                                                           int64_t B, int C, RowScale rs,
@@ -566,10 +643,11 @@ __global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ 
     const rsrc_t rout = make_rsrc(gp + geo.h, (uint32_t)nb * 16u);
     const rsrc_t rrow = make_rsrc(rp, (uint32_t)C * ES);
 
-    const int32_t t = targets[row];
-    const bool valid = t >= 0 && t < C;
+    const RowTarget rt = row_target<OP>(targets, row, C, rs);
+    const int t = rt.t;
+    const bool valid = rt.valid;
     const int tb = t - geo.h;
-    const bool t_in_body = valid && tb >= 0 && tb < nb * VE;
+    const bool t_in_body = t >= 0 && tb >= 0 && tb < nb * VE;
     const int tv = t_in_body ? tb / VE : -1;
     const int tj = t_in_body ? tb % VE : -1;
     const int own_k = (t_in_body && tv < NT * NV) ? tv / NT : -1;
@@ -582,7 +660,7 @@ __global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ 
       xe = geo.tail0 + (tid - geo.h);
     // step 1: edge loads, unconditional (an absent element reads past the row: 0)
     const float xs_raw = bload_elem<T>(rrow, (uint32_t)(xe >= 0 ? xe : C) * ES);
-    const float zt_raw = bload_elem<T>(rrow, (uint32_t)(valid ? t : C) * ES);
+    const float zt_raw = bload_elem<T>(rrow, (uint32_t)(t >= 0 ? t : C) * ES);
 
     // step 2: this row's prefix is in LDS once everything issued before the
     // DMA has completed
@@ -599,7 +677,7 @@ __global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ 
     dma_prefix(rinn);
 
     const float xs = xe >= 0 ? xs_raw : kNegInf;
-    const float zt = valid ? zt_raw : 0.f;
+    const float zt = t >= 0 ? zt_raw : 0.f;
 
     // step 5: phase B
     float c = kLowest, s = 0.f;
@@ -641,7 +719,7 @@ __global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ 
     const float si = lane < NW ? red_s[parity][lane] : 0.f;
     const float cg = wave_uniform(seg_allreduce<16>(ci, OpMax{}));
     const float sx = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
-    const RowResult rr = row_epilogue(cg, sx, zt, valid, invB, gmul);
+    const RowResult rr = row_finish<OP>(cg, sx, zt, valid, invB, gmul);
 
     // step 7: phase C; register-only slots first (each refilled with the
     // next row), then the prefetched slots
@@ -667,7 +745,7 @@ __global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ 
       __builtin_amdgcn_sched_barrier(0);
       bstore128<kPolicyStream>(packed, rout, voff, (uint32_t)k * NT * 16u);
     }
-    if (tid == 0) loss_rows[row] = rr.loss;
+    if (tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
     if (xe >= 0) {
       const float g = (xe == t) ? rr.gt : exp2_hw(__builtin_fmaf(xs, kLog2e, -cg)) * rr.scale;
       E::store1(gp + xe, g);

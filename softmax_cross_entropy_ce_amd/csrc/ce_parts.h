@@ -108,7 +108,7 @@ constexpr int part_capacity(int NT, int NR, int NL, int NXW) { return (NR + NL) 
 // that recomputed its partner's pair instead of receiving it.  spin: polls
 // before that happens (0: every part recomputes).  At most 64 VGPRs (eight
 // waves per SIMD), so 32 / (NT / 64) workgroups fit a CU by waves.
-template <typename T, int P, int NT, int NR, int NL, int NXW>
+template <typename T, int P, int NT, int NR, int NL, int NXW, int OP = kOpCE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8)))
 void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B,
                     int C, RowScale rs, T* __restrict__ grad, float* __restrict__ loss_rows,
@@ -174,9 +174,11 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
     return u32x4{0u, 0u, 0u, 0u};
   };
 
-  const int32_t t = targets[row];
-  const bool valid = t >= 0 && t < C;
-  const int tb = valid ? t - geo.h : -1;
+  static_assert(OP != kOpShard, "shard records come from the row kernels");
+  const RowTarget rt = row_target<OP>(targets, row, C, rs);
+  const int t = rt.t;
+  const bool valid = rt.valid;
+  const int tb = t >= 0 ? t - geo.h : -1;
   const bool t_body = tb >= 0 && tb < geo.nb * VE;
   const int tvec = t_body ? tb / VE : -1;  // target's body vector (row-relative)
   const int tj = t_body ? tb % VE : -1;
@@ -192,7 +194,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   };
   const int xe = edge_elem(part);
   const float xs_raw = bload_elem<T>(rrow, (uint32_t)(xe >= 0 ? xe : C) * ES);
-  const float zt_raw = bload_elem<T>(rrow, (uint32_t)(valid ? t : C) * ES);
+  const float zt_raw = bload_elem<T>(rrow, (uint32_t)(t >= 0 ? t : C) * ES);
 
   // The target element.  The thread whose vectors hold it sets it to -inf
   // in the loaded data, once, so no slot needs per-element target code; the
@@ -270,7 +272,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
 #pragma unroll
   for (int p = 0; p < NLS; ++p) fold_slot(own, tin, NR + p, lds_slot(p), c, s);
   const float xs = xe >= 0 ? xs_raw : kNegInf;
-  const float zt = valid ? zt_raw : 0.f;
+  const float zt = t >= 0 ? zt_raw : 0.f;
   fold_edge(xe, xs, c, s);
   fold_target_max(own, zt, c, s);
   float c_own, s_own;
@@ -348,8 +350,8 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
     sx = s0 * exp2_hw(c0 - cg);
     sx = sx + s1 * exp2_hw(c1 - cg);
   }
-  const RowResult rr = row_epilogue(cg, sx, zt, valid, invB, gmul);
-  if (part == 0 && tid == 0) loss_rows[row] = rr.loss;
+  const RowResult rr = row_finish<OP>(cg, sx, zt, valid, invB, gmul);
+  if (part == 0 && tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
 
   // Phase C: the gradient of this part from registers and LDS.
   auto write_slot = [&](int k, u32x4 w) {

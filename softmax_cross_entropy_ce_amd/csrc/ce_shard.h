@@ -1,0 +1,113 @@
+// Cross-entropy over a vocabulary split into column shards.
+//
+// An LM head split along its output features (rumus project page, milestone
+// M24: a column-parallel linear layer) leaves each rank the logits of a
+// contiguous range of classes.  The cross-entropy of the whole row then
+// takes two passes over a shard, with one exchange between them:
+//   1. every shard reduces each row to a record (the row kernels with
+//      kOpShard: c, sx, zt, own; one read of the shard);
+//   2. the records of all shards are gathered (on several GPUs an
+//      all-gather of B x 16 bytes per shard; here the caller stacks them);
+//   3. every shard combines the records of a row in shard order and writes
+//      its columns of the gradient (this kernel: one more read of the shard
+//      and one write).
+// The combine is the merge of (max, sum) partials that the row-part kernel
+// applies to its parts: c = max_k c_k, sx = sum_k sx_k 2^(c_k - c) in shard
+// order, zt from the shard that holds the target; row_epilogue then gives
+// the loss, the gradient scale and the target's gradient.  Every shard does
+// the same arithmetic on the same records, so all shards agree bit for bit
+// on each row's values, whichever shard computes them.
+#pragma once
+
+#include "ce_kernels.h"
+
+namespace ce {
+
+constexpr int kShardThreads = 256;
+constexpr int kShardSlots = 8;                              // 16-byte vectors per thread
+constexpr int kShardChunk = kShardThreads * kShardSlots;    // body vectors per workgroup
+
+// Workgroup g handles body vectors [j * kShardChunk, (j + 1) * kShardChunk)
+// of row g / chunks (j = g % chunks), and chunk 0 also the row's elements
+// before its first 16-byte boundary and after its last.  recs holds
+// nshards x B records, shard-major.  A row whose target lies outside
+// [0, Ctot), or is held by other than exactly one shard's record, gets NaN
+// loss and gradient.
+template <typename T>
+__global__ __launch_bounds__(kShardThreads) void ce_shard_grad_kernel(
+    const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B, int C,
+    int64_t col0, int64_t Ctot, const f32x4* __restrict__ recs, int nshards, RowScale rs,
+    T* __restrict__ grad, float* __restrict__ loss_rows, int chunks) {
+  using E = Elem<T>;
+  constexpr int VE = E::VE, NT = kShardThreads;
+  const int64_t row = (int64_t)(blockIdx.x / (uint32_t)chunks);
+  const int chunk = (int)(blockIdx.x % (uint32_t)chunks);
+  const int tid = threadIdx.x;
+  const uint32_t voff = (uint32_t)tid * 16u;
+
+  const T* rp = logits + row * C;
+  T* gp = grad + row * C;
+  const RowGeom geo = row_geom(rp, C);
+  const int v0 = chunk * kShardChunk;
+  const int nv = geo.nb - v0 < kShardChunk ? geo.nb - v0 : kShardChunk;
+  const uint32_t bytes = nv > 0 ? (uint32_t)nv * 16u : 0u;
+  const rsrc_t rin = make_rsrc(rp + geo.h + (int64_t)v0 * VE, bytes);
+  const rsrc_t rout = make_rsrc(gp + geo.h + (int64_t)v0 * VE, bytes);
+  u32x4 v[kShardSlots];
+#pragma unroll
+  for (int k = 0; k < kShardSlots; ++k)
+    v[k] = bload128<kPolicyStream>(rin, voff, (uint32_t)k * NT * 16u);
+  int xe = -1;  // chunk 0: this thread's edge element, if any
+  if (chunk == 0) {
+    if (tid < geo.h)
+      xe = tid;
+    else if (tid - geo.h < geo.ntail)
+      xe = geo.tail0 + (tid - geo.h);
+  }
+  const float xs = xe >= 0 ? E::load1(rp + xe) : 0.f;
+
+  // combine the shards' records in shard order
+  float c = kLowest;
+  for (int k = 0; k < nshards; ++k) c = __builtin_fmaxf(c, recs[(int64_t)k * B + row].x);
+  float sx = 0.f, zt = 0.f, own = 0.f;
+  for (int k = 0; k < nshards; ++k) {
+    const f32x4 r = recs[(int64_t)k * B + row];
+    sx = sx + r.y * exp2_hw(r.x - c);
+    zt = zt + r.z;
+    own = own + r.w;
+  }
+  const int64_t tg = targets[row];
+  const bool valid = tg >= 0 && tg < Ctot && own == 1.f;
+  const RowResult rr = row_epilogue(c, sx, zt, valid, rs.invB, grad_mul(rs));
+  if (loss_rows != nullptr && chunk == 0 && tid == 0) loss_rows[row] = rr.loss;
+
+  // the target's column in this shard, if it is here: body vector tvec
+  // (element tj) or an edge element
+  const int64_t tl = tg - col0;
+  const int t = (tl >= 0 && tl < C) ? (int)tl : -1;
+  const int tb = t - geo.h;
+  const bool t_body = t >= 0 && tb >= 0 && tb < geo.nb * VE;
+  const int tvec = t_body ? tb / VE - v0 : -1;  // chunk-relative
+  const int tk = (tvec >= 0 && tvec < nv && tvec % NT == tid) ? tvec / NT : -1;
+  const int tj = t_body ? tb % VE : 0;
+
+#pragma unroll
+  for (int k = 0; k < kShardSlots; ++k) {
+    if (k * NT >= nv) break;  // uniform
+    float f[VE], g[VE];
+    E::unpack(v[k], f);
+#pragma unroll
+    for (int i = 0; i < VE; ++i) g[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -c)) * rr.scale;
+    if (k == tk) {
+#pragma unroll
+      for (int i = 0; i < VE; ++i) g[i] = (i == tj) ? rr.gt : g[i];
+    }
+    bstore128<kPolicyStream>(E::pack(g), rout, voff, (uint32_t)k * NT * 16u);
+  }
+  if (xe >= 0) {
+    const float g = (xe == t) ? rr.gt : exp2_hw(__builtin_fmaf(xs, kLog2e, -c)) * rr.scale;
+    E::store1(gp + xe, g);
+  }
+}
+
+}  // namespace ce

@@ -36,7 +36,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "make_inputs", "make_workload",
-           "spike_columns", "bf16_bits_from_f32", "grid_logits"]
+           "spike_columns", "bf16_bits_from_f32", "grid_logits", "simplex_rows"]
 
 _BLOCK_ELEMS = 1 << 23  # about 8M logits per independently seeded block
 
@@ -155,3 +155,29 @@ def grid_logits(B: int, C: int, step: float, lim: float, seed: int = 0) -> np.nd
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
     k = g.integers(-int(lim / step), int(lim / step) + 1, size=(B, C))
     return (k * step).astype(np.float32)
+
+
+def simplex_rows(B: int, C: int, dtype: str = "f32", seed: int = 0) -> np.ndarray:
+    """Rows on the probability simplex, to stand in for a softmax's output:
+    one Dirichlet(1, ..., 1) draw per row (independent standard exponentials
+    divided by their row sum in float64), then rounded to float32 or to
+    bfloat16 (returned as uint16 bit patterns).  Drawn in independently
+    seeded row blocks, like ``make_inputs``."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rows_per = max(1, _BLOCK_ELEMS // max(C, 1))
+    nblocks = max(1, -(-B // rows_per))
+    children = np.random.SeedSequence(seed).spawn(nblocks)
+    out = np.empty((B, C), dtype=np.float32 if dtype == "f32" else np.uint16)
+
+    def fill(i: int) -> None:
+        lo, hi = i * rows_per, min(B, (i + 1) * rows_per)
+        if hi <= lo:
+            return
+        w = np.random.Generator(np.random.PCG64(children[i])).standard_exponential((hi - lo, C))
+        y = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+        out[lo:hi] = y if dtype == "f32" else bf16_bits_from_f32(y)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(nblocks)))
+    return out

@@ -38,7 +38,9 @@ def test_library_exports_every_declared_function():
                             "ce_status_string", "ce_version", "ce_select_path",
                             "ce_debug_force_path", "ce_debug_part_polls",
                             "ce_debug_part_counter", "ce_stream_copy",
-                            "ce_fwd_grad_scaled", "ce_scale_grad", "ce_fwd_loss"])
+                            "ce_fwd_grad_scaled", "ce_scale_grad", "ce_fwd_loss",
+                            "ce_softmax_fwd", "ce_softmax_bwd", "ce_shard_stats",
+                            "ce_shard_grad"])
     for n in names:
         assert hasattr(L_, n), n
 
@@ -222,3 +224,83 @@ def test_in_place_two_part_rows_refuse_forced_parts():
         assert fwd(z=Z, g=Z, B=8, C=128256, dtype=1) == PATH
     finally:
         ce.force_path(prev)
+
+
+def smf(x=Z, B=8, C=10, dtype=0, y=G, lse=L):
+    return ce.lib().ce_softmax_fwd(x, B, C, dtype, y, lse, None)
+
+
+def test_softmax_fwd_validation():
+    assert smf(x=None) == NULL
+    assert smf(y=None) == NULL
+    assert smf(dtype=5) == DTYPE
+    assert smf(B=0) == SHAPE and smf(C=0) == SHAPE and smf(C=(1 << 28) + 1) == SHAPE
+    assert smf(x=Z + 2) == ALIGN
+    assert smf(y=G + 4) == ALIGN                 # x and y 16-byte congruent
+    assert smf(lse=L + 2) == ALIGN
+    assert smf(x=Z, y=Z + 16) == ALIAS           # partial overlap
+    prev = ce.force_path(4)
+    try:
+        assert smf(x=Z, y=Z, C=128256, dtype=1) == PATH   # in place, two-part rows
+    finally:
+        ce.force_path(prev)
+
+
+def smb(y=Z, dy=T, B=8, C=10, dtype=0, dx=G):
+    return ce.lib().ce_softmax_bwd(y, dy, B, C, dtype, dx, None)
+
+
+def test_softmax_bwd_validation():
+    assert smb(y=None) == NULL and smb(dy=None) == NULL and smb(dx=None) == NULL
+    assert smb(dtype=2) == DTYPE
+    assert smb(B=0) == SHAPE and smb(C=-1) == SHAPE and smb(B=1 << 31) == SHAPE
+    assert smb(y=Z + 2) == ALIGN
+    assert smb(dy=T + 4) == ALIGN                # y and dy 16-byte congruent
+    assert smb(dx=G + 8) == ALIGN                # y and dx 16-byte congruent
+    assert smb(y=Z, dx=Z + 16) == ALIAS          # dx partly over y
+    assert smb(dy=T, dx=T - 16) == ALIAS         # dx partly over dy
+    prev = ce.force_path(4)
+    try:
+        assert smb() == PATH                     # no row parts for the backward
+        ce.force_path(1)
+        assert smb(C=300) == PATH                # short path: C <= 256
+    finally:
+        ce.force_path(prev)
+
+
+def sst(z=Z, t=T, B=8, C=10, col0=0, dtype=0, rec=L):
+    return ce.lib().ce_shard_stats(z, t, B, C, col0, dtype, rec, None)
+
+
+def test_shard_stats_validation():
+    assert sst(z=None) == NULL and sst(t=None) == NULL and sst(rec=None) == NULL
+    assert sst(dtype=3) == DTYPE
+    assert sst(B=0) == SHAPE and sst(col0=-1) == SHAPE and sst(col0=1 << 31) == SHAPE
+    assert sst(rec=L + 4) == ALIGN               # records are 16-byte aligned
+    assert sst(t=T + 2) == ALIGN
+    prev = ce.force_path(4)
+    try:
+        assert sst() == PATH                     # records need no row parts
+    finally:
+        ce.force_path(prev)
+
+
+def sgr(z=Z, t=T, B=8, C=10, col0=0, ctot=10, dtype=0, rec=L, n=1, g=G, lo=None, sc=None):
+    return ce.lib().ce_shard_grad(z, t, B, C, col0, ctot, dtype, rec, n, g, lo, sc, None)
+
+
+def test_shard_grad_validation():
+    assert sgr(z=None) == NULL and sgr(t=None) == NULL
+    assert sgr(rec=None) == NULL and sgr(g=None) == NULL
+    assert sgr(dtype=4) == DTYPE
+    assert sgr(B=0) == SHAPE and sgr(C=0) == SHAPE
+    assert sgr(n=0) == SHAPE and sgr(n=1025) == SHAPE
+    assert sgr(col0=-1) == SHAPE
+    assert sgr(col0=5, ctot=14) == SHAPE         # col0 + C beyond the row
+    assert sgr(ctot=9) == SHAPE                  # the row shorter than the shard
+    assert sgr(ctot=1 << 31) == SHAPE
+    assert sgr(rec=L + 8) == ALIGN
+    assert sgr(g=G + 4) == ALIGN
+    assert sgr(lo=L + 2) == ALIGN and sgr(sc=T + 1) == ALIGN
+    assert sgr(z=Z, g=Z + 16) == ALIAS           # grad partly over the logits
+    assert sgr(g=L - 64) == ALIAS                # grad over the records
