@@ -37,7 +37,14 @@ Readings where the pages are silent (each is listed in the design doc):
   bf16 gradient is the fp64 gradient rounded once to bf16, nearest, ties to
   even (the Haelixe page's "BF16 storage, F32 compute" boundary);
 * the scalar is the exactly rounded sum (``math.fsum``), so it carries no
-  summation-order error of its own.
+  summation-order error of its own;
+* fp16 logits (the pages' F16 data type, rumus project page milestone M11)
+  are widened exactly and the expected fp16 gradient is the fp64 gradient
+  rounded once to fp16, nearest, ties to even, with fp16's subnormals;
+* ``ignore_index`` (not on the pages) follows the common mean-reduction
+  convention: a row whose target equals it has loss 0 and a zero gradient
+  row, and the other rows are scaled by 1 / (number of rows not ignored)
+  instead of 1 / B.
 
 Pinned by ``tests/test_oracle_pins.py`` (closed forms, special cases,
 invariants, finite differences, library cross-checks, planted-mistake
@@ -54,7 +61,10 @@ import numpy as np
 __all__ = [
     "widen_bf16",
     "rne_bf16_bits",
+    "widen_f16",
+    "rne_f16_bits",
     "ce_rows",
+    "ce_rows_ignore",
     "ce",
     "reduce_loss",
 ]
@@ -95,6 +105,52 @@ def rne_bf16_bits(x: np.ndarray) -> np.ndarray:
     return (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+def widen_f16(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) -> exact float64 values: sign,
+    5-bit exponent (bias 15) and 10-bit fraction decoded by hand;
+    exponent 0 holds the subnormals f * 2^-24, exponent 31 the infinities
+    and NaNs."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where(b & 0x8000, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    normal = np.ldexp(1024.0 + f, np.maximum(e, 1) - 25)      # (1 + f/1024) 2^(e-15)
+    val = np.where(e == 0, np.ldexp(f, -24), normal)
+    val = np.where(e == 31, np.where(f == 0, np.inf, np.nan), val)
+    return sign * val
+
+
+def rne_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values once to IEEE binary16 (nearest, ties to even),
+    returning uint16 bit patterns.
+
+    binary16 keeps 11 significant bits; for |x| with binary exponent e
+    (x = f 2^e, 0.5 <= |f| < 1) the spacing is 2^(e - 11), never finer than
+    the subnormal spacing 2^-24.  The quotient by the spacing is an exact
+    fp64 scaling and ``np.rint`` rounds half to even.  Results of 65536 or
+    more in magnitude (past the largest finite value 65504) become
+    infinities.  The rounded value is then encoded by hand."""
+    x = np.asarray(x, dtype=np.float64)
+    finite = np.isfinite(x)
+    xf = np.where(finite, x, 0.0)
+    _, e = np.frexp(xf)
+    q = np.maximum(e - 11, -24)
+    r = np.ldexp(np.rint(np.ldexp(xf, -q)), q)
+    a = np.abs(r)
+    out = np.zeros(x.shape, dtype=np.int64)
+    sub = a < 2.0 ** -14
+    out = np.where(sub, np.rint(np.ldexp(a, 24)).astype(np.int64), out)
+    _, en = np.frexp(np.where(sub | (a == 0), 1.0, a))          # a = fn 2^en, 0.5 <= fn < 1
+    frac = np.rint(np.ldexp(np.where(sub, 1.0, a), 11 - en)).astype(np.int64) - 1024
+    out = np.where(~sub, ((en - 1 + 15) << 10) | frac, out)
+    out = np.where(a >= 65536.0, 0x7C00, out)
+    out = np.where(np.isinf(x), 0x7C00, out)
+    out = np.where(np.isnan(x), 0x7E00, out)
+    neg = np.signbit(np.where(finite, r, x))
+    out = np.where(neg, out | 0x8000, out)
+    return out.astype(np.uint16)
+
+
 def ce_rows(z: np.ndarray, t: np.ndarray, B: int):
     """Per-row loss and gradient for a block of rows, in float64.
 
@@ -126,19 +182,39 @@ def ce_rows(z: np.ndarray, t: np.ndarray, B: int):
     return loss, grad
 
 
+def ce_rows_ignore(z: np.ndarray, t: np.ndarray, ignore_index: int):
+    """Per-row loss and gradient of a whole [B, C] problem with rows whose
+    target equals ``ignore_index`` left out of the mean: those rows get
+    loss 0 and a zero gradient row; every other row is the cross-entropy of
+    ``ce_rows`` scaled by 1 / N, N the number of rows not ignored (when
+    N = 0 every row is ignored and every output is 0)."""
+    z = np.asarray(z, dtype=np.float64)
+    t = np.asarray(t, dtype=np.int64)
+    ign = t == ignore_index
+    N = int((~ign).sum())
+    loss = np.zeros(z.shape[0])
+    grad = np.zeros(z.shape)
+    if N:
+        l, g = ce_rows(z[~ign], t[~ign], N)
+        loss[~ign] = l
+        grad[~ign] = g
+    return loss, grad
+
+
 def ce(logits: np.ndarray, targets: np.ndarray, dtype: str = "f32", rows=None,
        block_elems: int = 1 << 22):
     """Oracle for a whole [B, C] problem, or for the rows listed in ``rows``.
 
     ``logits`` is float32 [B, C] (dtype "f32") or the uint16 bit patterns of
-    bfloat16 [B, C] (dtype "bf16").  Rows are processed in blocks of about
-    ``block_elems`` elements to bound memory.  Returns fp64
-    ``(loss_rows, grad)`` for the selected rows.
+    bfloat16 or float16 [B, C] (dtype "bf16" or "f16").  Rows are processed
+    in blocks of about ``block_elems`` elements to bound memory.  Returns
+    fp64 ``(loss_rows, grad)`` for the selected rows.
     """
     B, C = logits.shape
     idx = np.arange(B) if rows is None else np.asarray(rows, dtype=np.int64)
-    widen = (lambda a: np.asarray(a, dtype=np.float64)) if dtype == "f32" else widen_bf16
-    if dtype not in ("f32", "bf16"):
+    widen = {"f32": lambda a: np.asarray(a, dtype=np.float64), "bf16": widen_bf16,
+             "f16": widen_f16}.get(dtype)
+    if widen is None:
         raise ValueError(f"unknown dtype {dtype!r}")
     loss = np.empty(idx.size, dtype=np.float64)
     grad = np.empty((idx.size, C), dtype=np.float64)

@@ -462,3 +462,132 @@ def test_row_selection_matches_full():
     ls, gs = ce(z, t, "f32", rows=rows)
     np.testing.assert_array_equal(ls, lf[rows])
     np.testing.assert_array_equal(gs, gf[rows])
+
+
+# --------------------------------------------------------------------------
+# fp16 conversions and ignore_index
+# --------------------------------------------------------------------------
+
+def test_widen_f16_every_pattern():
+    """All 65536 binary16 patterns decode to numpy's float16 values."""
+    from oracle import widen_f16
+    b = np.arange(1 << 16, dtype=np.uint16)
+    got, want = widen_f16(b), b.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+
+
+def test_rne_f16_hand_cases():
+    """Ties to even at 1, in the subnormal range and at the overflow edge."""
+    from oracle import rne_f16_bits
+    cases = {
+        1.0: 0x3C00, 1.0 + 2.0 ** -11: 0x3C00,            # tie: down to even
+        1.0 + 3 * 2.0 ** -11: 0x3C02,                       # tie: up to even
+        2.0 ** -24: 0x0001, 2.0 ** -25: 0x0000,             # smallest subnormal; tie to 0
+        1.5 * 2.0 ** -24: 0x0002, 2.0 ** -14: 0x0400,       # tie up to even; smallest normal
+        65504.0: 0x7BFF, 65519.99: 0x7BFF, 65520.0: 0x7C00,  # largest finite; tie to inf
+        -2.0: 0xC000, -0.0: 0x8000, float("inf"): 0x7C00, -1e6: 0xFC00,
+    }
+    x = np.array(list(cases))
+    np.testing.assert_array_equal(rne_f16_bits(x), np.array(list(cases.values()), np.uint16))
+    assert np.isnan(np.array([0]).astype(np.uint16).view(np.float16)).sum() == 0
+    assert rne_f16_bits(np.array([np.nan]))[0] & 0x7C00 == 0x7C00
+
+
+def test_rne_f16_matches_numpy_and_torch():
+    """Random magnitudes from 2^-30 to 2^17: numpy's float64 -> float16
+    conversion (one rounding to nearest even) agrees bit for bit, and so
+    does torch's float32 -> float16 on float32 inputs (torch's float64 ->
+    float16 goes through float32 and rounds twice, so it is not the
+    reference for float64 inputs)."""
+    import torch
+    from oracle import rne_f16_bits
+    rng = _rng(60)
+    x = rng.standard_normal(300_000) * np.exp2(rng.uniform(-30, 17, 300_000))
+    got = rne_f16_bits(x)
+    with np.errstate(over="ignore"):
+        assert np.array_equal(got, x.astype(np.float16).view(np.uint16))
+    x32 = x.astype(np.float32)
+    tt = torch.from_numpy(x32).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(rne_f16_bits(x32.astype(np.float64)), tt)
+
+
+def test_f16_oracle_widens_exactly():
+    from oracle import rne_f16_bits, widen_f16
+    rng = _rng(61)
+    z = rne_f16_bits(rng.standard_normal((6, 300)) * 4)
+    t = rng.integers(0, 300, 6)
+    l1, g1 = ce(z, t, "f16")
+    l2, g2 = ce_rows(widen_f16(z), t, 6)
+    np.testing.assert_array_equal(l1, l2)
+    np.testing.assert_array_equal(g1, g2)
+
+
+def test_ignore_index_matches_torch():
+    """Library cross-check: torch.nn.functional.cross_entropy with
+    ignore_index and the mean reduction, in float64 on the CPU, gives the
+    sum of the per-row losses and, by autograd, the gradient."""
+    import torch
+    from oracle import ce_rows_ignore
+    rng = _rng(62)
+    for B, C, ii in ((16, 9, -100), (40, 300, 7), (5, 2, 0)):
+        z = rng.standard_normal((B, C)) * 3
+        t = rng.integers(0, C, B)
+        t[rng.random(B) < 0.4] = ii
+        t[0] = ii
+        if (t == ii).all():
+            t[1] = (ii + 1) % C
+        loss, grad = ce_rows_ignore(z, t, ii)
+        zt = torch.from_numpy(z).requires_grad_(True)
+        L = torch.nn.functional.cross_entropy(zt, torch.from_numpy(t), ignore_index=ii)
+        L.backward()
+        assert math.isclose(math.fsum(loss), L.item(), rel_tol=1e-13)
+        np.testing.assert_allclose(grad, zt.grad.numpy(), rtol=1e-12, atol=1e-17)
+
+
+def test_ignore_index_reductions():
+    """No row ignored: ce_rows with B; every row ignored: zeros; the logits of
+    an ignored row change nothing; each kept row equals ce_rows of the kept
+    rows with B = their count."""
+    from oracle import ce_rows_ignore
+    rng = _rng(63)
+    B, C = 12, 20
+    z = rng.standard_normal((B, C)) * 2
+    t = rng.integers(0, C, B)
+    l0, g0 = ce_rows(z, t, B)
+    l1, g1 = ce_rows_ignore(z, t, -1)
+    np.testing.assert_array_equal(l0, l1)
+    np.testing.assert_array_equal(g0, g1)
+    l2, g2 = ce_rows_ignore(z, np.full(B, 3), 3)
+    assert (l2 == 0).all() and (g2 == 0).all()
+    t2 = t.copy()
+    t2[[1, 4, 5]] = -100
+    l3, g3 = ce_rows_ignore(z, t2, -100)
+    z2 = z.copy()
+    z2[[1, 4, 5]] = 1e4
+    l4, g4 = ce_rows_ignore(z2, t2, -100)
+    np.testing.assert_array_equal(l3, l4)
+    np.testing.assert_array_equal(g3, g4)
+    keep = t2 != -100
+    l5, g5 = ce_rows(z[keep], t2[keep], int(keep.sum()))
+    np.testing.assert_array_equal(l3[keep], l5)
+    np.testing.assert_array_equal(g3[keep], g5)
+    assert (l3[~keep] == 0).all() and (g3[~keep] == 0).all()
+
+
+def test_ignore_index_mutant_scaled_by_batch_is_caught():
+    """A planted mistake (kept rows scaled by 1/B instead of 1/N) fails the
+    torch cross-check."""
+    import torch
+    rng = _rng(64)
+    B, C = 16, 9
+    z = rng.standard_normal((B, C))
+    t = rng.integers(0, C, B)
+    t[:5] = -100
+    keep = t != -100
+    l_bad, _ = ce_rows(z[keep], t[keep], B)
+    L = torch.nn.functional.cross_entropy(torch.from_numpy(z), torch.from_numpy(t),
+                                          ignore_index=-100)
+    assert not math.isclose(math.fsum(l_bad), L.item(), rel_tol=1e-6)
