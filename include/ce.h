@@ -40,10 +40,13 @@ extern "C" {
 #endif
 
 /* Element type of the logits and of the gradient (they always match).
- * Accumulation is float32 in both cases; per-row losses are float32. */
+ * Accumulation is float32 in every case; per-row losses are float32. */
 typedef enum {
     CE_F32 = 0,  /* IEEE binary32 */
-    CE_BF16 = 1  /* bfloat16; the gradient is rounded to nearest, ties to even */
+    CE_BF16 = 1, /* bfloat16; the gradient is rounded to nearest, ties to even */
+    CE_F16 = 2   /* IEEE binary16 (the pages' F16 data type, rumus project page
+                    milestone M11); widened exactly, the gradient rounded to
+                    nearest, ties to even, with binary16 subnormals */
 } ce_dtype;
 
 typedef enum {
@@ -60,6 +63,9 @@ typedef enum {
 
 /* Largest number of classes accepted: a row must stay below 2^31 bytes. */
 #define CE_MAX_C ((int64_t)1 << 28)
+
+/* ignore_index value of ce_fwd_grad_ex that ignores no row. */
+#define CE_NO_IGNORE ((int32_t)(-2147483647 - 1))
 
 /*
  * ce_fwd_grad - per-row loss and gradient of softmax cross-entropy, one pass.
@@ -124,6 +130,46 @@ int ce_fwd_loss(const void* logits, const int32_t* targets, int64_t B, int64_t C
 int ce_fwd_grad_scaled(const void* logits, const int32_t* targets, int64_t B, int64_t C,
                        int dtype, void* grad_out, float* loss_out, const float* grad_scale,
                        void* stream);
+
+/*
+ * ce_fwd_grad_ex - ce_fwd_grad with row strides, an optional device
+ * gradient scale, the loss-only mode and ignore_index in one call.
+ *
+ * Defined by: as ce_fwd_grad.  Row strides: a tensor's Layout holds its
+ * shape, strides and offset, and views share storage with other layouts
+ * (rumus project page, core-types table); ignore_index is not on the pages
+ * and follows the common mean-reduction convention.
+ *
+ *   logits        row b starts at logits + b * ld_logits elements;
+ *                 ld_logits >= C.
+ *   grad_out      NULL for the per-row losses only (ld_grad is then
+ *                 unused), else row b starts at grad_out + b * ld_grad,
+ *                 ld_grad >= C.  In place when grad_out == logits and
+ *                 ld_grad == ld_logits; otherwise the two spans (first
+ *                 element of row 0 to the last of row B-1) must not
+ *                 overlap.  Every row of grad must start at the same
+ *                 address modulo 16 as its row of logits: (grad_out -
+ *                 logits) and (ld_grad - ld_logits) * element size are
+ *                 multiples of 16 bytes.
+ *   grad_scale    DEVICE float32 scalar multiplying the gradient, or NULL.
+ *   ignore_index  CE_NO_IGNORE, or a class value: rows whose target equals
+ *                 it get loss 0 and a zero gradient row, and the other rows
+ *                 are scaled by 1/N instead of 1/B, N the number of rows
+ *                 not ignored, counted on the device (no host
+ *                 synchronisation).  Other targets outside [0, C) still
+ *                 give NaN rows (and count in N).
+ *   workspace     device scratch of ce_fwd_workspace_bytes(ignore_index)
+ *                 bytes (4-byte aligned), or NULL when that is 0; it holds
+ *                 the count N while the call's kernels run.
+ *   other arguments and errors as ce_fwd_grad; CE_ERR_WORKSPACE when the
+ *   workspace is missing or too small.
+ */
+size_t ce_fwd_workspace_bytes(int32_t ignore_index);
+
+int ce_fwd_grad_ex(const void* logits, int64_t ld_logits, const int32_t* targets, int64_t B,
+                   int64_t C, int dtype, void* grad_out, int64_t ld_grad, float* loss_out,
+                   const float* grad_scale, int32_t ignore_index, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /*
  * ce_scale_grad - the backward of the fused loss: grad *= *scale in place,

@@ -33,11 +33,14 @@ __all__ = [
     "softmax_fwd", "softmax_fwd_into", "softmax_bwd", "softmax_bwd_into", "softmax",
     "shard_stats", "shard_stats_into", "shard_grad", "shard_grad_into",
     "reduce_workspace_bytes", "select_path", "force_path", "part_polls", "part_counter",
-    "stream_copy", "version", "PATH_NAMES", "F32", "BF16",
+    "stream_copy", "version", "PATH_NAMES", "F32", "BF16", "F16", "NO_IGNORE",
+    "fwd_grad_ex_into", "fwd_grad_ex", "fwd_workspace_bytes",
 ]
 
 F32 = 0
 BF16 = 1
+F16 = 2
+NO_IGNORE = -(1 << 31)
 PATH_NAMES = {1: "short", 2: "resident", 3: "long", 4: "parts"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -100,6 +103,11 @@ def lib() -> ctypes.CDLL:
     L.ce_shard_stats.restype = i32
     L.ce_shard_grad.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp, i32, vp, vp, vp, vp]
     L.ce_shard_grad.restype = i32
+    L.ce_fwd_workspace_bytes.argtypes = [ctypes.c_int32]
+    L.ce_fwd_workspace_bytes.restype = sz
+    L.ce_fwd_grad_ex.argtypes = [vp, i64, vp, i64, i64, i32, vp, i64, vp, vp, ctypes.c_int32, vp,
+                                 sz, vp]
+    L.ce_fwd_grad_ex.restype = i32
     _lib = L
     return L
 
@@ -181,7 +189,9 @@ def _dtype_code(t) -> int:
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
-    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+    if t.dtype == torch.float16:
+        return F16
+    raise TypeError(f"logits must be float32, bfloat16 or float16, got {t.dtype}")
 
 
 def _stream_ptr(device) -> int:
@@ -285,6 +295,67 @@ def scale_grad_(grad, scale) -> None:
     _check(st, "ce_scale_grad")
 
 
+def fwd_workspace_bytes(ignore_index=None) -> int:
+    return int(lib().ce_fwd_workspace_bytes(NO_IGNORE if ignore_index is None else int(ignore_index)))
+
+
+def _rows_view(x, what: str):
+    """A [B, C] device tensor whose rows are contiguous (column stride 1);
+    returns its row stride in elements."""
+    if not x.is_cuda:
+        raise ValueError("tensors must live on a HIP device")
+    if x.dim() != 2:
+        raise ValueError(f"{what} must be [B, C]")
+    if x.stride(1) != 1 and x.shape[1] > 1:
+        raise ValueError(f"{what} must have contiguous rows (column stride 1)")
+    return x.stride(0) if x.shape[0] > 1 else max(x.shape[1], x.stride(0))
+
+
+def fwd_grad_ex_into(logits, targets, grad, loss_rows, grad_scale=None, ignore_index=None,
+                     workspace=None) -> None:
+    """ce_fwd_grad_ex: logits and grad may be row-strided views (rows
+    contiguous); grad None gives the losses only; grad_scale is an optional
+    device scalar; rows whose target equals ignore_index give loss 0 and a
+    zero gradient row, and the rest are averaged over the rows kept."""
+    torch = _torch()
+    ldz = _rows_view(logits, "logits")
+    B, C = logits.shape
+    _check_cuda(targets, loss_rows)
+    if targets.dtype != torch.int32 or targets.shape != (B,):
+        raise TypeError("targets must be int32 of shape [B]")
+    if loss_rows.dtype != torch.float32 or loss_rows.shape != (B,):
+        raise TypeError("loss_rows must be float32 of shape [B]")
+    ldg = 0
+    if grad is not None:
+        ldg = _rows_view(grad, "grad")
+        if grad.dtype != logits.dtype or grad.shape != logits.shape:
+            raise TypeError("grad must match logits in dtype and shape")
+    if grad_scale is not None:
+        _check_scalar(grad_scale, "grad_scale")
+    ii = NO_IGNORE if ignore_index is None else int(ignore_index)
+    need = fwd_workspace_bytes(ignore_index)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    st = lib().ce_fwd_grad_ex(
+        logits.data_ptr(), ldz, targets.data_ptr(), B, C, _dtype_code(logits),
+        grad.data_ptr() if grad is not None else None, ldg, loss_rows.data_ptr(),
+        grad_scale.data_ptr() if grad_scale is not None else None, ii,
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream_ptr(logits.device))
+    _check(st, "ce_fwd_grad_ex")
+
+
+def fwd_grad_ex(logits, targets, ignore_index=None, grad_scale=None, with_grad: bool = True):
+    """Return ``(grad, loss_rows)`` (grad None when with_grad is False) for
+    row-strided logits, with the options of fwd_grad_ex_into."""
+    torch = _torch()
+    grad = torch.empty(logits.shape, dtype=logits.dtype, device=logits.device) if with_grad else None
+    loss_rows = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device)
+    fwd_grad_ex_into(logits, targets, grad, loss_rows, grad_scale, ignore_index)
+    return grad, loss_rows
+
+
 def fwd_grad(logits, targets):
     """Return ``(grad, loss_rows)`` for ``[B, C]`` logits and int32 targets."""
     torch = _torch()
@@ -343,8 +414,11 @@ def _function():
         there is no host synchronisation; one backward per forward."""
 
         @staticmethod
-        def forward(ctx, logits, targets):
-            grad, loss_rows = fwd_grad(logits.detach(), targets)
+        def forward(ctx, logits, targets, ignore_index=None):
+            if ignore_index is None:
+                grad, loss_rows = fwd_grad(logits.detach(), targets)
+            else:
+                grad, loss_rows = fwd_grad_ex(logits.detach(), targets, ignore_index=ignore_index)
             ctx.grad = grad
             return reduce_loss(loss_rows)
 
@@ -355,17 +429,19 @@ def _function():
                 raise RuntimeError("cross_entropy_loss: backward can run once per forward")
             ctx.grad = None
             scale_grad_(grad, grad_output.detach().to(torch.float32).reshape(1).contiguous())
-            return grad, None
+            return grad, None, None
 
     _autograd_fn = CrossEntropyFunction
     return _autograd_fn
 
 
-def cross_entropy_loss(logits, targets):
+def cross_entropy_loss(logits, targets, ignore_index=None):
     """The batch-mean fused cross-entropy as a differentiable 0-d tensor:
     ``loss.backward()`` gives ``logits.grad = (softmax - onehot) / B`` times
-    the upstream gradient, from the gradient formed in the forward pass."""
-    return _function().apply(logits, targets)
+    the upstream gradient, from the gradient formed in the forward pass.
+    With ignore_index, rows whose target equals it are left out of the
+    mean (the mean is over the other rows)."""
+    return _function().apply(logits, targets, ignore_index)
 
 
 # ---------------------------------------------------------------- softmax

@@ -73,7 +73,7 @@ int launched() { return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_LAUNCH;
 
 // ------------------------------------------------------------------ path 1
 template <typename T, int S, int EPL, int VW, int OP, bool GRAD>
-int launch_short_cfg(const T* z, const int32_t* t, int64_t B, int C, ce::RowScale rs, T* g, float* l,
+int launch_short_cfg(const T* z, const int32_t* t, int64_t B, int C, ce::RowArgs rs, T* g, float* l,
                      hipStream_t st) {
   constexpr int rpb = ce::kShortThreads / S;
   const int64_t blocks = (B + rpb - 1) / rpb;
@@ -84,7 +84,7 @@ int launch_short_cfg(const T* z, const int32_t* t, int64_t B, int C, ce::RowScal
 }
 
 template <typename T, int S, int EPL, int OP, bool GRAD>
-int launch_short_vw(int vw, const T* z, const int32_t* t, int64_t B, int C, ce::RowScale rs, T* g,
+int launch_short_vw(int vw, const T* z, const int32_t* t, int64_t B, int C, ce::RowArgs rs, T* g,
                     float* l, hipStream_t st) {
   switch (vw) {
     case 1: return launch_short_cfg<T, S, EPL, 1, OP, GRAD>(z, t, B, C, rs, g, l, st);
@@ -99,13 +99,20 @@ int launch_short_vw(int vw, const T* z, const int32_t* t, int64_t B, int C, ce::
 }
 
 // Vector width (elements) of the short path: the widest load of at most 16
-// bytes that every row start of both arrays is aligned to.
-int short_vw(int64_t C, int es, uintptr_t zaddr, uintptr_t gaddr, int epl) {
+// bytes that every row start of both arrays is aligned to (lens: the row
+// length and both row strides, each a multiple of the width).
+int short_vw(int64_t lens, int es, uintptr_t zaddr, uintptr_t gaddr, int epl) {
   for (int vw = 16 / es; vw > 1; vw /= 2) {
     const uintptr_t a = (uintptr_t)vw * es;
-    if (vw <= epl && C % vw == 0 && zaddr % a == 0 && gaddr % a == 0) return vw;
+    if (vw <= epl && lens % vw == 0 && zaddr % a == 0 && gaddr % a == 0) return vw;
   }
   return 1;
+}
+
+// The short path addresses a workgroup's up to 256 rows through one buffer
+// resource per array: their span must stay below 2^31 bytes.
+bool short_span_ok(int64_t C, int64_t ld, int es) {
+  return C <= kShortMaxC && (255 * ld + C) * es < ((int64_t)1 << 31);
 }
 
 // Short-row layout: about 16 bytes per lane.  S lanes per row is the power
@@ -113,13 +120,15 @@ int short_vw(int64_t C, int es, uintptr_t zaddr, uintptr_t gaddr, int epl) {
 // elements, more only at S = 16).  Lanes of a row read adjacent vectors,
 // so a load instruction covers 64/S consecutive rows.
 template <typename T, int OP, bool GRAD>
-int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g, float* l,
+int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g, float* l,
                  hipStream_t st) {
-  if (C > kShortMaxC) return CE_ERR_PATH;
+  if (!short_span_ok(C, rs.ldz, sizeof(T)) || (GRAD && !short_span_ok(C, rs.ldg, sizeof(T))))
+    return CE_ERR_PATH;
   constexpr int es = sizeof(T);
   constexpr int E16 = 16 / es;  // elements in 16 bytes
   const int c = (int)C;
-  auto vw = [&](int epl) { return short_vw(C, es, (uintptr_t)z, (uintptr_t)g, epl); };
+  const int64_t lens = C | rs.ldz | (GRAD ? rs.ldg : 0);
+  auto vw = [&](int epl) { return short_vw(lens, es, (uintptr_t)z, (uintptr_t)g, epl); };
   if (C <= E16) return launch_short_vw<T, 1, E16, OP, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
   if (C <= 2 * E16) return launch_short_vw<T, 2, E16, OP, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
   if (C <= 4 * E16) return launch_short_vw<T, 4, E16, OP, GRAD>(vw(E16), z, t, B, c, rs, g, l, st);
@@ -152,7 +161,7 @@ int resident_blocks(const void* kernel, int nt) {
 }
 
 template <typename T, int NT, int NV, int OP, bool GRAD>
-int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
+int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
                    float* l, hipStream_t st) {
   auto kern = ce::ce_row_kernel<T, NT, NV, GRAD, OP>;
   const int res = resident_blocks(reinterpret_cast<const void*>(kern), NT);
@@ -167,7 +176,7 @@ int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowSc
 constexpr int kLdsPrefetchSlots = 9;  // 9 x 16 KB of the 160 KB of LDS
 
 template <typename T, int OP>
-int launch_row_lds(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
+int launch_row_lds(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
                    float* l, hipStream_t st) {
   auto kern = ce::ce_row_lds_kernel<T, 16, kLdsPrefetchSlots, OP>;
   const int res = resident_blocks(reinterpret_cast<const void*>(kern), 1024);
@@ -178,7 +187,7 @@ int launch_row_lds(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowSc
 }
 
 template <typename T, int OP, bool GRAD>
-int launch_row(RowCfg cfg, const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
+int launch_row(RowCfg cfg, const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
                float* l, hipStream_t st) {
 #define CE_ROW_CASE(NT_, NV_)                                                           \
   if (cfg.nt == NT_ && cfg.nv == NV_)                                                   \
@@ -210,7 +219,7 @@ RowCfg resident_cfg(int64_t C, int es, bool* ok) {
 
 // ---------------------------------------------------------------- path 4
 template <typename T, int P, int NT, int NR, int NL, int NXW, int OP>
-int launch_parts_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g,
+int launch_parts_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
                      float* l, hipStream_t st) {
   const int64_t blocks = P * ((B + 7) / 8 * 8);
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
@@ -222,7 +231,7 @@ int launch_parts_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::Row
 }
 
 template <typename T, int OP>
-int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScale rs, T* g, float* l,
+int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g, float* l,
                  hipStream_t st) {
   const int64_t nb = body_vectors_max(C, sizeof(T));
   if (nb <= kPartsOneSmall) return launch_parts_cfg<T, 1, 1024, 4, 0, 0, OP>(z, t, B, C, rs, g, l, st);
@@ -236,7 +245,7 @@ int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowScal
 // (nothing has to stay on chip for a gradient, so no row parts).
 template <typename T, int OP, bool GRAD>
 int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g, float* l,
-              ce::RowScale rs, hipStream_t st) {
+              ce::RowArgs rs, hipStream_t st) {
   switch (path) {
     case kPathShort:
       return launch_short<T, OP, GRAD>(z, t, B, C, rs, g, l, st);
@@ -296,9 +305,36 @@ extern "C" {
 
 namespace {
 
+// The row kernels' entry.  op kOpCE: targets and loss_out required;
+// grad_out null gives the loss only, grad_out == logits (with equal row
+// strides) the gradient in place.  op kOpSoftmax: targets unused; grad_out
+// (the softmax) required, or the logits themselves; loss_out (the
+// log-sum-exp) may be null.  op kOpShard: targets and loss_out (B records
+// of 4 floats, 16-byte aligned) required, grad_out null; col0 is the
+// shard's first column.  ldz, ldg: row strides in elements (>= C).  With
+// has_ignore (kOpCE only), rows whose target equals ignore are left out of
+// the mean: ws (>= 4 bytes, 4-aligned) receives the count of kept rows.
+struct FwdArgs {
+  int op = ce::kOpCE;
+  const void* logits = nullptr;
+  int64_t ldz = 0;
+  const int32_t* targets = nullptr;
+  int64_t B = 0, C = 0;
+  int dtype = CE_F32;
+  void* grad = nullptr;
+  int64_t ldg = 0;
+  float* loss = nullptr;
+  const float* gmul = nullptr;
+  int64_t col0 = 0;
+  bool has_ignore = false;
+  int32_t ignore = 0;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+};
+
 template <typename T>
 int fwd_dispatch(int op, int path, const void* z, const int32_t* t, int64_t B, int64_t C, void* g,
-                 float* l, ce::RowScale rs, hipStream_t st) {
+                 float* l, ce::RowArgs rs, hipStream_t st) {
   const T* zz = (const T*)z;
   T* gg = (T*)g;
   switch (op) {
@@ -314,43 +350,98 @@ int fwd_dispatch(int op, int path, const void* z, const int32_t* t, int64_t B, i
   }
 }
 
-// The row kernels' entry.  op kOpCE: targets and loss_out required;
-// grad_out null gives the loss only, grad_out == logits the gradient in
-// place.  op kOpSoftmax: targets unused; grad_out (the softmax) required,
-// or the logits themselves; loss_out (the log-sum-exp) may be null.  op
-// kOpShard: targets and loss_out (B records of 4 floats, 16-byte aligned)
-// required, grad_out null; col0 is the shard's first column.
-int fwd_impl(int op, const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
-             void* grad_out, float* loss_out, const float* gmul, int64_t col0, void* stream) {
-  if (!logits) return CE_ERR_NULL;
-  if (op != ce::kOpSoftmax && (!targets || !loss_out)) return CE_ERR_NULL;
-  if (op == ce::kOpSoftmax && !grad_out) return CE_ERR_NULL;
-  if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
+bool known_dtype(int dtype) { return dtype == CE_F32 || dtype == CE_BF16 || dtype == CE_F16; }
+
+// Bytes from the first element of row 0 to the end of row B-1.
+uintptr_t span_bytes(int64_t B, int64_t C, int64_t ld, int es) {
+  return ((uintptr_t)(B - 1) * (uintptr_t)ld + (uintptr_t)C) * (uintptr_t)es;
+}
+
+int fwd_impl(const FwdArgs& a, void* stream) {
+  if (!a.logits) return CE_ERR_NULL;
+  if (a.op != ce::kOpSoftmax && (!a.targets || !a.loss)) return CE_ERR_NULL;
+  if (a.op == ce::kOpSoftmax && !a.grad) return CE_ERR_NULL;
+  if (a.has_ignore && !a.ws) return CE_ERR_WORKSPACE;
+  if (!known_dtype(a.dtype)) return CE_ERR_DTYPE;
+  const int64_t B = a.B, C = a.C;
   if (B <= 0 || C <= 0 || B > 0x7fffffffLL || C > CE_MAX_C) return CE_ERR_SHAPE;
-  const int es = elem_size(dtype);
-  const uintptr_t z = (uintptr_t)logits, g = (uintptr_t)grad_out;
-  if (z % es || g % es || (uintptr_t)targets % 4) return CE_ERR_ALIGN;
-  if ((uintptr_t)loss_out % (op == ce::kOpShard ? 16 : 4)) return CE_ERR_ALIGN;
-  if (gmul && (uintptr_t)gmul % 4) return CE_ERR_ALIGN;
-  if (grad_out && (z > g ? z - g : g - z) % 16) return CE_ERR_ALIGN;
-  if ((uint64_t)B > UINT64_MAX / ((uint64_t)C * es)) return CE_ERR_SHAPE;
-  const uintptr_t nbytes = (uintptr_t)B * (uintptr_t)C * es;
-  const bool in_place = grad_out && g == z;
-  if (grad_out && !in_place && overlaps(z, nbytes, g, nbytes)) return CE_ERR_ALIAS;
+  if (a.ldz < C || (a.grad && a.ldg < C)) return CE_ERR_SHAPE;
+  const int es = elem_size(a.dtype);
+  const int64_t ldg = a.grad ? a.ldg : a.ldz;
+  if ((uint64_t)B > UINT64_MAX / 4 / ((uint64_t)(a.ldz > ldg ? a.ldz : ldg) * es)) return CE_ERR_SHAPE;
+  if (a.has_ignore && a.ws_bytes < 4) return CE_ERR_WORKSPACE;
+  const uintptr_t z = (uintptr_t)a.logits, g = (uintptr_t)a.grad;
+  if (z % es || g % es || (uintptr_t)a.targets % 4) return CE_ERR_ALIGN;
+  if ((uintptr_t)a.loss % (a.op == ce::kOpShard ? 16 : 4)) return CE_ERR_ALIGN;
+  if (a.gmul && (uintptr_t)a.gmul % 4) return CE_ERR_ALIGN;
+  if (a.has_ignore && (uintptr_t)a.ws % 4) return CE_ERR_ALIGN;
+  // every row of grad must start at the same offset modulo 16 as its row of
+  // logits
+  if (a.grad && ((z > g ? z - g : g - z) % 16 || ((a.ldz - ldg) * es) % 16)) return CE_ERR_ALIGN;
+  const uintptr_t zspan = span_bytes(B, C, a.ldz, es);
+  const bool in_place = a.grad && g == z && ldg == a.ldz;
+  if (a.grad && !in_place && overlaps(z, zspan, g, span_bytes(B, C, ldg, es))) return CE_ERR_ALIAS;
 
   const int forced = g_force_path.load(std::memory_order_relaxed);
   int path = forced ? forced : auto_path(C, es);
-  if (!grad_out || in_place) {
-    if (path == kPathParts && (!grad_out || two_part_row(C, es))) {
+  if (!a.grad || in_place) {
+    if (path == kPathParts && (!a.grad || two_part_row(C, es))) {
       if (forced) return CE_ERR_PATH;
       path = path_without_parts(C, es);
     }
   }
-  const ce::RowScale rs{1.0f / (float)B, gmul, col0};
+  const bool short_ok = short_span_ok(C, a.ldz, es) && (!a.grad || short_span_ok(C, ldg, es));
+  if (path == kPathShort && !forced && !short_ok) path = kPathResident;
+  // a forced path that cannot take the shape is refused before any launch
+  bool takes = false;
+  switch (path) {
+    case kPathShort: takes = short_ok; break;
+    case kPathResident: resident_cfg(C, es, &takes); break;
+    case kPathLong: takes = true; break;
+    case kPathParts: takes = a.grad && body_vectors_max(C, es) <= kPartsTwo; break;
+    default: break;
+  }
+  if (!takes) return CE_ERR_PATH;
   const hipStream_t st = as_stream(stream);
-  if (dtype == CE_F32)
-    return fwd_dispatch<float>(op, path, logits, targets, B, C, grad_out, loss_out, rs, st);
-  return fwd_dispatch<__bf16>(op, path, logits, targets, B, C, grad_out, loss_out, rs, st);
+  ce::RowArgs rs{1.0f / (float)B, a.gmul, a.col0, a.ldz, ldg, nullptr, a.ignore,
+                 a.has_ignore ? 1 : 0};
+  if (a.has_ignore) {
+    uint32_t* kept = (uint32_t*)a.ws;
+    hipLaunchKernelGGL(ce::ce_set_u32_kernel, dim3(1), dim3(64), 0, st, kept, 0u);
+    if (launched() != CE_OK) return CE_ERR_LAUNCH;
+    const int64_t blocks = (B + ce::kCountThreads - 1) / ce::kCountThreads;
+    hipLaunchKernelGGL(ce::ce_count_kept_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)),
+                       dim3(ce::kCountThreads), 0, st, a.targets, B, a.ignore, kept);
+    if (launched() != CE_OK) return CE_ERR_LAUNCH;
+    rs.kept = kept;
+  }
+  switch (a.dtype) {
+    case CE_F32:
+      return fwd_dispatch<float>(a.op, path, a.logits, a.targets, B, C, a.grad, a.loss, rs, st);
+    case CE_BF16:
+      return fwd_dispatch<__bf16>(a.op, path, a.logits, a.targets, B, C, a.grad, a.loss, rs, st);
+    default:
+      return fwd_dispatch<_Float16>(a.op, path, a.logits, a.targets, B, C, a.grad, a.loss, rs, st);
+  }
+}
+
+// The contiguous calls.
+int fwd_plain(int op, const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
+              void* grad_out, float* loss_out, const float* gmul, int64_t col0, void* stream) {
+  FwdArgs a;
+  a.op = op;
+  a.logits = logits;
+  a.ldz = C;
+  a.targets = targets;
+  a.B = B;
+  a.C = C;
+  a.dtype = dtype;
+  a.grad = grad_out;
+  a.ldg = C;
+  a.loss = loss_out;
+  a.gmul = gmul;
+  a.col0 = col0;
+  return fwd_impl(a, stream);
 }
 
 template <typename T>
@@ -477,7 +568,7 @@ constexpr int kMaxShards = 1024;
 
 template <typename T>
 int launch_shard_grad(const T* z, const int32_t* t, int64_t B, int64_t C, int64_t col0,
-                      int64_t Ctot, const float* recs, int nshards, ce::RowScale rs, T* g,
+                      int64_t Ctot, const float* recs, int nshards, ce::RowArgs rs, T* g,
                       float* l, hipStream_t st) {
   const int64_t nb = body_vectors_max(C, sizeof(T));
   const int64_t chunks = nb > 0 ? (nb + ce::kShardChunk - 1) / ce::kShardChunk : 1;
@@ -495,25 +586,51 @@ extern "C" {
 int ce_fwd_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
                 void* grad_out, float* loss_out, void* stream) {
   if (!grad_out) return CE_ERR_NULL;
-  return fwd_impl(ce::kOpCE, logits, targets, B, C, dtype, grad_out, loss_out, nullptr, 0, stream);
+  return fwd_plain(ce::kOpCE, logits, targets, B, C, dtype, grad_out, loss_out, nullptr, 0, stream);
 }
 
 int ce_fwd_loss(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
                 float* loss_out, void* stream) {
-  return fwd_impl(ce::kOpCE, logits, targets, B, C, dtype, nullptr, loss_out, nullptr, 0, stream);
+  return fwd_plain(ce::kOpCE, logits, targets, B, C, dtype, nullptr, loss_out, nullptr, 0, stream);
 }
 
 int ce_fwd_grad_scaled(const void* logits, const int32_t* targets, int64_t B, int64_t C,
                        int dtype, void* grad_out, float* loss_out, const float* grad_scale,
                        void* stream) {
   if (!grad_scale || !grad_out) return CE_ERR_NULL;
-  return fwd_impl(ce::kOpCE, logits, targets, B, C, dtype, grad_out, loss_out, grad_scale, 0,
-                  stream);
+  return fwd_plain(ce::kOpCE, logits, targets, B, C, dtype, grad_out, loss_out, grad_scale, 0,
+                   stream);
+}
+
+size_t ce_fwd_workspace_bytes(int32_t ignore_index) {
+  return ignore_index == CE_NO_IGNORE ? 0 : 4;
+}
+
+int ce_fwd_grad_ex(const void* logits, int64_t ld_logits, const int32_t* targets, int64_t B,
+                   int64_t C, int dtype, void* grad_out, int64_t ld_grad, float* loss_out,
+                   const float* grad_scale, int32_t ignore_index, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  FwdArgs a;
+  a.logits = logits;
+  a.ldz = ld_logits;
+  a.targets = targets;
+  a.B = B;
+  a.C = C;
+  a.dtype = dtype;
+  a.grad = grad_out;
+  a.ldg = ld_grad;
+  a.loss = loss_out;
+  a.gmul = grad_scale;
+  a.has_ignore = ignore_index != CE_NO_IGNORE;
+  a.ignore = ignore_index;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  return fwd_impl(a, stream);
 }
 
 int ce_scale_grad(void* grad, int64_t n, int dtype, const float* scale, void* stream) {
   if (!grad || !scale) return CE_ERR_NULL;
-  if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
+  if (!known_dtype(dtype)) return CE_ERR_DTYPE;
   if (n <= 0) return CE_ERR_SHAPE;
   const int es = elem_size(dtype);
   if ((uintptr_t)grad % es || (uintptr_t)scale % 4) return CE_ERR_ALIGN;
@@ -521,18 +638,19 @@ int ce_scale_grad(void* grad, int64_t n, int dtype, const float* scale, void* st
   if (overlaps((uintptr_t)grad, (uintptr_t)n * es, (uintptr_t)scale, 4)) return CE_ERR_ALIAS;
   const hipStream_t st = as_stream(stream);
   if (dtype == CE_F32) return launch_scale<float>((float*)grad, n, scale, st);
-  return launch_scale<__bf16>((__bf16*)grad, n, scale, st);
+  if (dtype == CE_BF16) return launch_scale<__bf16>((__bf16*)grad, n, scale, st);
+  return launch_scale<_Float16>((_Float16*)grad, n, scale, st);
 }
 
 int ce_softmax_fwd(const void* x, int64_t B, int64_t C, int dtype, void* y_out, float* lse_out,
                    void* stream) {
-  return fwd_impl(ce::kOpSoftmax, x, nullptr, B, C, dtype, y_out, lse_out, nullptr, 0, stream);
+  return fwd_plain(ce::kOpSoftmax, x, nullptr, B, C, dtype, y_out, lse_out, nullptr, 0, stream);
 }
 
 int ce_softmax_bwd(const void* y, const void* dy, int64_t B, int64_t C, int dtype, void* dx_out,
                    void* stream) {
   if (!y || !dy || !dx_out) return CE_ERR_NULL;
-  if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
+  if (!known_dtype(dtype)) return CE_ERR_DTYPE;
   if (B <= 0 || C <= 0 || B > 0x7fffffffLL || C > CE_MAX_C) return CE_ERR_SHAPE;
   const int es = elem_size(dtype);
   const uintptr_t a = (uintptr_t)y, b = (uintptr_t)dy, o = (uintptr_t)dx_out;
@@ -549,22 +667,25 @@ int ce_softmax_bwd(const void* y, const void* dy, int64_t B, int64_t C, int dtyp
   const hipStream_t st = as_stream(stream);
   if (dtype == CE_F32)
     return softmax_bwd_typed<float>(path, (const float*)y, (const float*)dy, B, C, (float*)dx_out, st);
-  return softmax_bwd_typed<__bf16>(path, (const __bf16*)y, (const __bf16*)dy, B, C,
-                                   (__bf16*)dx_out, st);
+  if (dtype == CE_BF16)
+    return softmax_bwd_typed<__bf16>(path, (const __bf16*)y, (const __bf16*)dy, B, C,
+                                     (__bf16*)dx_out, st);
+  return softmax_bwd_typed<_Float16>(path, (const _Float16*)y, (const _Float16*)dy, B, C,
+                                     (_Float16*)dx_out, st);
 }
 
 int ce_shard_stats(const void* logits, const int32_t* targets, int64_t B, int64_t C, int64_t col0,
                    int dtype, float* records_out, void* stream) {
   if (col0 < 0 || col0 > 0x7fffffffLL) return CE_ERR_SHAPE;
-  return fwd_impl(ce::kOpShard, logits, targets, B, C, dtype, nullptr, records_out, nullptr, col0,
-                  stream);
+  return fwd_plain(ce::kOpShard, logits, targets, B, C, dtype, nullptr, records_out, nullptr, col0,
+                   stream);
 }
 
 int ce_shard_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C, int64_t col0,
                   int64_t C_total, int dtype, const float* records, int n_shards, void* grad_out,
                   float* loss_out, const float* grad_scale, void* stream) {
   if (!logits || !targets || !records || !grad_out) return CE_ERR_NULL;
-  if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
+  if (!known_dtype(dtype)) return CE_ERR_DTYPE;
   if (B <= 0 || C <= 0 || B > 0x7fffffffLL || C > CE_MAX_C) return CE_ERR_SHAPE;
   if (n_shards < 1 || n_shards > kMaxShards) return CE_ERR_SHAPE;
   if (col0 < 0 || C_total < C || col0 > C_total - C || C_total > 0x7fffffffLL) return CE_ERR_SHAPE;
@@ -577,13 +698,16 @@ int ce_shard_grad(const void* logits, const int32_t* targets, int64_t B, int64_t
   const uintptr_t n = (uintptr_t)B * (uintptr_t)C * es;
   if (g != z && overlaps(z, n, g, n)) return CE_ERR_ALIAS;
   if (overlaps(g, n, (uintptr_t)records, (uintptr_t)n_shards * (uintptr_t)B * 16)) return CE_ERR_ALIAS;
-  const ce::RowScale rs{1.0f / (float)B, grad_scale, col0};
+  const ce::RowArgs rs{1.0f / (float)B, grad_scale, col0, C, C, nullptr, 0, 0};
   const hipStream_t st = as_stream(stream);
   if (dtype == CE_F32)
     return launch_shard_grad<float>((const float*)logits, targets, B, C, col0, C_total, records,
                                     n_shards, rs, (float*)grad_out, loss_out, st);
-  return launch_shard_grad<__bf16>((const __bf16*)logits, targets, B, C, col0, C_total, records,
-                                   n_shards, rs, (__bf16*)grad_out, loss_out, st);
+  if (dtype == CE_BF16)
+    return launch_shard_grad<__bf16>((const __bf16*)logits, targets, B, C, col0, C_total, records,
+                                     n_shards, rs, (__bf16*)grad_out, loss_out, st);
+  return launch_shard_grad<_Float16>((const _Float16*)logits, targets, B, C, col0, C_total,
+                                     records, n_shards, rs, (_Float16*)grad_out, loss_out, st);
 }
 
 size_t ce_reduce_workspace_bytes(int64_t B) {
@@ -646,7 +770,7 @@ int ce_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
 }
 
 int ce_select_path(int64_t C, int dtype) {
-  if (dtype != CE_F32 && dtype != CE_BF16) return CE_ERR_DTYPE;
+  if (!known_dtype(dtype)) return CE_ERR_DTYPE;
   if (C <= 0 || C > CE_MAX_C) return CE_ERR_SHAPE;
   const int forced = g_force_path.load(std::memory_order_relaxed);
   return forced ? forced : auto_path(C, elem_size(dtype));

@@ -77,8 +77,9 @@ __device__ __forceinline__ void bstore128(u32x4 v, rsrc_t r, uint32_t voff, uint
 
 // ---------------------------------------------------------------------------
 // Element traits.  A 16-byte vector holds VE elements; unpack widens them
-// to float32 (bf16 -> f32 is exact: the bf16 bits become the high half),
-// pack rounds float32 back (bf16: v_cvt_pk_bf16_f32, nearest-even).
+// to float32 (bf16 -> f32 is exact: the bf16 bits become the high half;
+// f16 -> f32 is exact too), pack rounds float32 back (bf16:
+// v_cvt_pk_bf16_f32, f16: v_cvt_f16_f32; both nearest-even).
 // ---------------------------------------------------------------------------
 template <typename T>
 struct Elem;
@@ -144,6 +145,55 @@ struct Elem<__bf16> {
     const int d = j >> 1;
     const unsigned keep = (j & 1) ? 0x0000FFFFu : 0xFFFF0000u;
     const unsigned ninf = (j & 1) ? 0xFF800000u : 0x0000FF80u;
+    return u32x4{d == 0 ? (v.x & keep) | ninf : v.x, d == 1 ? (v.y & keep) | ninf : v.y,
+                 d == 2 ? (v.z & keep) | ninf : v.z, d == 3 ? (v.w & keep) | ninf : v.w};
+  }
+};
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float f16lo(unsigned d) {
+  return (float)__builtin_bit_cast(f16x2, d).x;
+}
+__device__ __forceinline__ float f16hi(unsigned d) {
+  return (float)__builtin_bit_cast(f16x2, d).y;
+}
+// float32 -> two float16, each rounded to nearest even (fp16 subnormals
+// kept), packed low then high
+__device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
+}
+
+// IEEE binary16: widening to float32 is exact; narrowing rounds to nearest
+// even.
+template <>
+struct Elem<_Float16> {
+  static constexpr int VE = 8;
+  __device__ static __forceinline__ void unpack(u32x4 v, float (&f)[8]) {
+    f[0] = f16lo(v.x); f[1] = f16hi(v.x);
+    f[2] = f16lo(v.y); f[3] = f16hi(v.y);
+    f[4] = f16lo(v.z); f[5] = f16hi(v.z);
+    f[6] = f16lo(v.w); f[7] = f16hi(v.w);
+  }
+  __device__ static __forceinline__ u32x4 pack(const float (&g)[8]) {
+    return u32x4{pack_f16x2(g[0], g[1]), pack_f16x2(g[2], g[3]), pack_f16x2(g[4], g[5]),
+                 pack_f16x2(g[6], g[7])};
+  }
+  __device__ static __forceinline__ float load1(const _Float16* p) {
+    const unsigned short h = *reinterpret_cast<const unsigned short*>(p);
+    return f16lo((unsigned)h);
+  }
+  __device__ static __forceinline__ void store1(_Float16* p, float g) {
+    const unsigned d = pack_f16x2(g, 0.f);
+    __builtin_nontemporal_store((unsigned short)(d & 0xffffu),
+                                reinterpret_cast<unsigned short*>(p));
+  }
+  // the vector with element j (0..7) replaced by -inf (fp16 0xFC00)
+  __device__ static __forceinline__ u32x4 kill(u32x4 v, int j) {
+    const int d = j >> 1;
+    const unsigned keep = (j & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    const unsigned ninf = (j & 1) ? 0xFC000000u : 0x0000FC00u;
     return u32x4{d == 0 ? (v.x & keep) | ninf : v.x, d == 1 ? (v.y & keep) | ninf : v.y,
                  d == 2 ? (v.z & keep) | ninf : v.z, d == 3 ? (v.w & keep) | ninf : v.w};
   }

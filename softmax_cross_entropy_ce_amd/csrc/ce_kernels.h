@@ -36,34 +36,53 @@ namespace ce {
 //               the shard holds it.  No per-element output.
 enum RowOp : int { kOpCE = 0, kOpSoftmax = 1, kOpShard = 2 };
 
-// Scales of a call: 1/B for the loss, and for the gradient 1/B times the
-// upstream gradient of the loss, a device scalar (gmul; null means 1).
-// col0: kOpShard's first column in the whole row.
-struct RowScale {
+// Per-call arguments of the row kernels.
+//   invB        1/B, the scale of the batch mean (unless kept is set).
+//   gmul        the upstream gradient of the loss, a device scalar that
+//               multiplies the gradient (null: 1).
+//   col0        kOpShard: the shard's first column in the whole row.
+//   ldz, ldg    row strides of the logits and of the output, in elements
+//               (>= C; equal to C for contiguous rows).
+//   kept        device count of the rows that are not ignored; when set,
+//               the mean is over those rows: the scale is 1/kept.
+//   ignore      with has_ignore, rows whose target equals it are ignored
+//               (kOpCE): loss 0 and a zero gradient row.
+struct RowArgs {
   float invB;
   const float* gmul;
   int64_t col0;
+  int64_t ldz, ldg;
+  const uint32_t* kept;
+  int32_t ignore;
+  int32_t has_ignore;
 };
 
+__device__ __forceinline__ float row_invB(const RowArgs& rs) {
+  return rs.kept != nullptr ? 1.0f / (float)*rs.kept : rs.invB;
+}
+
 // The target of a row as one call sees it: its column in the row (-1 when
-// the row has none here) and whether the row has a result.  A CE row has a
-// result when its target lies in [0, C); a shard row always has a record
-// (whether the target is valid at all is decided when the records are
-// combined).
+// the row has none here), whether the row has a result and whether it is
+// ignored.  A CE row has a result when its target lies in [0, C) or is the
+// ignored value; a shard row always has a record (whether the target is
+// valid at all is decided when the records are combined).
 struct RowTarget {
   int t;
   bool valid;
+  bool ignored;
 };
 
 template <int OP>
 __device__ __forceinline__ RowTarget row_target(const int32_t* targets, int64_t row, int C,
-                                                const RowScale& rs) {
+                                                const RowArgs& rs) {
   if constexpr (OP == kOpSoftmax) {
-    return RowTarget{-1, true};
+    return RowTarget{-1, true, false};
   } else {
-    const int64_t t = (int64_t)targets[row] - (OP == kOpShard ? rs.col0 : 0);
+    const int32_t raw = targets[row];
+    if (OP == kOpCE && rs.has_ignore && raw == rs.ignore) return RowTarget{-1, true, true};
+    const int64_t t = (int64_t)raw - (OP == kOpShard ? rs.col0 : 0);
     const bool in = t >= 0 && t < C;
-    return RowTarget{in ? (int)t : -1, OP == kOpShard || in};
+    return RowTarget{in ? (int)t : -1, OP == kOpShard || in, false};
   }
 }
 
@@ -72,7 +91,7 @@ __device__ __forceinline__ RowTarget row_target(const int32_t* targets, int64_t 
 // 2^(z log2e - c), zt = the target logit (0 where the shard does not hold
 // the target), own = 1 where it does, else 0.
 
-__device__ __forceinline__ float grad_mul(const RowScale& rs) {
+__device__ __forceinline__ float grad_mul(const RowArgs& rs) {
   return rs.gmul != nullptr ? *rs.gmul : 1.0f;
 }
 
@@ -104,14 +123,17 @@ __device__ __forceinline__ RowResult row_epilogue(float cg, float sx, float zt, 
   return r;
 }
 
-// The epilogue of each operation.  Softmax: scale = 1 / S (the target
-// fields are unused, S = sx) and loss = lse = ln2 * (cg + log2 S).  Shard
-// records need no epilogue.
+// The epilogue of each operation.  CE: row_epilogue, and an ignored row
+// gets scale, target gradient and loss 0.  Softmax: scale = 1 / S (the
+// target fields are unused, S = sx) and loss = lse = ln2 * (cg + log2 S).
+// Shard records need no epilogue.
 template <int OP>
 __device__ __forceinline__ RowResult row_finish(float cg, float sx, float zt, bool valid,
-                                                float invB, float gmul) {
+                                                bool ignored, float invB, float gmul) {
   if constexpr (OP == kOpCE) {
-    return row_epilogue(cg, sx, zt, valid, invB, gmul);
+    RowResult r = row_epilogue(cg, sx, zt, valid, invB, gmul);
+    if (ignored) r.scale = r.gt = r.loss = 0.f;
+    return r;
   } else {
     RowResult r;
     r.scale = OP == kOpSoftmax ? 1.0f / sx : 0.f;
@@ -183,6 +205,49 @@ struct VecIO<float, VW> {
 };
 
 template <int VW>
+struct VecIO<_Float16, VW> {
+  static_assert(VW == 1 || VW == 2 || VW == 4 || VW == 8, "fp16 vector width");
+  __device__ static __forceinline__ void load(rsrc_t r, uint32_t off, float (&f)[VW]) {
+    if constexpr (VW == 1) {
+      unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, kPolicyStream);
+      f[0] = f16lo((unsigned)h);
+    } else if constexpr (VW == 2) {
+      unsigned d = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kPolicyStream);
+      f[0] = f16lo(d);
+      f[1] = f16hi(d);
+    } else if constexpr (VW == 4) {
+      u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kPolicyStream);
+      f[0] = f16lo(v.x); f[1] = f16hi(v.x);
+      f[2] = f16lo(v.y); f[3] = f16hi(v.y);
+    } else {
+      u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kPolicyStream);
+      float t[8];
+      Elem<_Float16>::unpack(v, t);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = t[i];
+    }
+  }
+  __device__ static __forceinline__ void store(rsrc_t r, uint32_t off, const float (&g)[VW]) {
+    if constexpr (VW == 1) {
+      unsigned d = pack_f16x2(g[0], 0.f);
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(d & 0xffffu), r, (int)off, 0,
+                                            kPolicyStream);
+    } else if constexpr (VW == 2) {
+      __builtin_amdgcn_raw_buffer_store_b32(pack_f16x2(g[0], g[1]), r, (int)off, 0,
+                                            kPolicyStream);
+    } else if constexpr (VW == 4) {
+      u32x2 v = {pack_f16x2(g[0], g[1]), pack_f16x2(g[2], g[3])};
+      __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kPolicyStream);
+    } else {
+      u32x4 v = {pack_f16x2(g[0], g[1]), pack_f16x2(g[2], g[3]), pack_f16x2(g[4], g[5]),
+                 pack_f16x2(g[6], g[7])};
+      __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kPolicyStream);
+      wide_store_guard();
+    }
+  }
+};
+
+template <int VW>
 struct VecIO<__bf16, VW> {
   static_assert(VW == 1 || VW == 2 || VW == 4 || VW == 8, "bf16 vector width");
   __device__ static __forceinline__ void load(rsrc_t r, uint32_t off, float (&f)[VW]) {
@@ -232,8 +297,8 @@ constexpr int kShortThreads = 256;
 template <typename T, int S, int EPL, int VW, bool GRAD, int OP = kOpCE>
 __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
     const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B, int C,
-    RowScale rs, T* __restrict__ grad, float* __restrict__ loss_rows) {
-  const float invB = rs.invB, gmul = grad_mul(rs);
+    RowArgs rs, T* __restrict__ grad, float* __restrict__ loss_rows) {
+  const float invB = row_invB(rs), gmul = grad_mul(rs);
   constexpr int RPB = kShortThreads / S;  // rows per workgroup
   constexpr int NVEC = EPL / VW;          // vector slots per lane
   static_assert(EPL % VW == 0, "EPL must be a multiple of VW");
@@ -245,12 +310,14 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
   const int64_t row = row0 + tid / S;
   const bool live = row < B;
   const int64_t nrows = (B - row0) < RPB ? (B - row0) : RPB;
-  const uint32_t bytes = (uint32_t)(nrows * C * ES);
-  const rsrc_t rin = make_rsrc(logits + row0 * C, bytes);
-  const rsrc_t rout = make_rsrc(grad + row0 * C, bytes);
-  const uint32_t rowoff = (uint32_t)(tid / S) * (uint32_t)C * ES;
+  // the workgroup's rows, with the row strides (the host keeps these spans
+  // below 2^31 bytes); lanes of rows past B read zeros and store nothing
+  const rsrc_t rin = make_rsrc(logits + row0 * rs.ldz, (uint32_t)(((nrows - 1) * rs.ldz + C) * ES));
+  const rsrc_t rout = make_rsrc(grad + row0 * rs.ldg, (uint32_t)(((nrows - 1) * rs.ldg + C) * ES));
+  const uint32_t rowoff = (uint32_t)(tid / S) * (uint32_t)rs.ldz * ES;
+  const uint32_t rowoff_g = (uint32_t)(tid / S) * (uint32_t)rs.ldg * ES;
 
-  const RowTarget rt = live ? row_target<OP>(targets, row, C, rs) : RowTarget{-1, false};
+  const RowTarget rt = live ? row_target<OP>(targets, row, C, rs) : RowTarget{-1, false, false};
   const int t = rt.t;
   const bool valid = live && rt.valid;
   // slot of the target in its owner lane: element c sits in vector c/VW,
@@ -290,7 +357,7 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
     e[i] = exp2_hw(__builtin_fmaf(x, kLog2e, -cg));
   }
   const float sx = seg_allreduce<S>(tree_sum(e), OpAdd{});
-  const RowResult rr = row_finish<OP>(cg, sx, zt, valid, invB, gmul);
+  const RowResult rr = row_finish<OP>(cg, sx, zt, valid, rt.ignored, invB, gmul);
   if (live && q == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
   if constexpr (!GRAD) return;
 
@@ -304,7 +371,7 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
         const int i = j * VW + w;
         g[w] = (owner && i == tslot) ? rr.gt : exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
       }
-      VecIO<T, VW>::store(rout, rowoff + (uint32_t)c0 * ES, g);
+      VecIO<T, VW>::store(rout, rowoff_g + (uint32_t)c0 * ES, g);
     }
   }
 }
@@ -360,10 +427,10 @@ __device__ __forceinline__ RowGeom row_geom(const T* rp, int C) {
 template <typename T, int NT, int NV, bool GRAD, int OP = kOpCE>
 __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits,
                                                     const int32_t* __restrict__ targets,
-                                                    int64_t B, int C, RowScale rs,
+                                                    int64_t B, int C, RowArgs rs,
                                                     T* __restrict__ grad,
                                                     float* __restrict__ loss_rows) {
-  const float invB = rs.invB, gmul = grad_mul(rs);
+  const float invB = row_invB(rs), gmul = grad_mul(rs);
   using E = Elem<T>;
   constexpr int VE = E::VE;
   constexpr int NW = NT / 64;
@@ -380,7 +447,7 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
   // Phase A of the first row: issue every register load
   u32x4 v[NV];
   {
-    const T* rp = logits + row * C;
+    const T* rp = logits + row * rs.ldz;
     const RowGeom geo = row_geom(rp, C);
     const rsrc_t rin = make_rsrc(rp + geo.h, (uint32_t)geo.nb * 16u);
 #pragma unroll
@@ -389,8 +456,8 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
   }
 
   for (int parity = 0;; parity ^= 1) {
-    const T* rp = logits + row * C;
-    T* gp = grad + row * C;
+    const T* rp = logits + row * rs.ldz;
+    T* gp = grad + row * rs.ldg;
     const RowGeom geo = row_geom(rp, C);
     const int nb = geo.nb;
     const rsrc_t rin = make_rsrc(rp + geo.h, (uint32_t)nb * 16u);
@@ -471,7 +538,7 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
       cg = wave_uniform(seg_allreduce<16>(ci, OpMax{}));
       sx = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
     }
-    const RowResult rr = row_finish<OP>(cg, sx, zt, valid, invB, gmul);
+    const RowResult rr = row_finish<OP>(cg, sx, zt, valid, rt.ignored, invB, gmul);
     if (tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
 
     // Phase C: gradient from the registers; each slot is refilled with the
@@ -480,7 +547,7 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
     // without a memory access.
     const int64_t next = row + G;
     const bool more = next < B;  // uniform
-    const T* rpn = logits + (more ? next : row) * C;
+    const T* rpn = logits + (more ? next : row) * rs.ldz;
     const RowGeom geon = row_geom(rpn, C);
     const rsrc_t rinn = make_rsrc(rpn + geon.h, more ? (uint32_t)geon.nb * 16u : 0u);
     // The empty asm makes each packed vector opaque here, so the compiler
@@ -570,6 +637,11 @@ __device__ __forceinline__ float bload_elem<__bf16>(rsrc_t r, uint32_t off) {
   const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, kPolicyDefault);
   return __builtin_bit_cast(float, (unsigned)h << 16);
 }
+template <>
+__device__ __forceinline__ float bload_elem<_Float16>(rsrc_t r, uint32_t off) {
+  const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, kPolicyDefault);
+  return f16lo((unsigned)h);
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -585,10 +657,10 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 template <typename T, int NV, int PF, int OP = kOpCE>
 __global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ logits,
                                                           const int32_t* __restrict__ targets,
-                                                          int64_t B, int C, RowScale rs,
+                                                          int64_t B, int C, RowArgs rs,
                                                           T* __restrict__ grad,
                                                           float* __restrict__ loss_rows) {
-  const float invB = rs.invB, gmul = grad_mul(rs);
+  const float invB = row_invB(rs), gmul = grad_mul(rs);
   using E = Elem<T>;
   constexpr int NT = 1024, NW = 16, VE = E::VE, ES = sizeof(T);
   static_assert(PF >= 1 && PF < NV, "prefetch slots");
@@ -606,7 +678,7 @@ __global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ 
   if (row >= B) return;
 
   auto body_rsrc = [&](int64_t r, bool exists) {
-    const T* rp = logits + r * C;
+    const T* rp = logits + r * rs.ldz;
     const RowGeom g = row_geom(rp, C);
     return make_rsrc(rp + g.h, exists ? (uint32_t)g.nb * 16u : 0u);
   };
@@ -636,8 +708,8 @@ __global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ 
   }
 
   for (int parity = 0;; parity ^= 1) {
-    const T* rp = logits + row * C;
-    T* gp = grad + row * C;
+    const T* rp = logits + row * rs.ldz;
+    T* gp = grad + row * rs.ldg;
     const RowGeom geo = row_geom(rp, C);
     const int nb = geo.nb;
     const rsrc_t rout = make_rsrc(gp + geo.h, (uint32_t)nb * 16u);
@@ -719,7 +791,7 @@ __global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ 
     const float si = lane < NW ? red_s[parity][lane] : 0.f;
     const float cg = wave_uniform(seg_allreduce<16>(ci, OpMax{}));
     const float sx = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
-    const RowResult rr = row_finish<OP>(cg, sx, zt, valid, invB, gmul);
+    const RowResult rr = row_finish<OP>(cg, sx, zt, valid, rt.ignored, invB, gmul);
 
     // step 7: phase C; register-only slots first (each refilled with the
     // next row), then the prefetched slots
@@ -801,6 +873,29 @@ __global__ __launch_bounds__(kReduceThreads) void ce_reduce_kernel(const float* 
   if (i + 2 * kReduceThreads < hi) a2 += in[i + 2 * kReduceThreads];
   const float tot = block_sum_256((a0 + a1) + (a2 + a3));
   if (threadIdx.x == 0) out[blockIdx.x] = tot;
+}
+
+// ===========================================================================
+// Rows kept by ignore_index: the number of targets that differ from it,
+// added into *count with one integer atomic per wave (an integer total does
+// not depend on the order of the additions).  The count is zeroed first by
+// ce_set_u32_kernel on the same stream.
+// ===========================================================================
+constexpr int kCountThreads = 256;
+
+__global__ __launch_bounds__(kCountThreads) void ce_count_kept_kernel(
+    const int32_t* __restrict__ targets, int64_t B, int32_t ignore, uint32_t* __restrict__ count) {
+  uint32_t n = 0;
+  const int64_t stride = (int64_t)gridDim.x * kCountThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kCountThreads + threadIdx.x; i < B; i += stride)
+    n += targets[i] != ignore ? 1u : 0u;
+  // a wave's total is at most 64 * ceil(B / stride) < 2^24: exact in float32
+  const float w = wave_allreduce((float)n, OpAdd{});
+  if ((threadIdx.x & 63) == 0 && w != 0.f) atomicAdd(count, (uint32_t)w);
+}
+
+__global__ __launch_bounds__(64) void ce_set_u32_kernel(uint32_t* __restrict__ p, uint32_t v) {
+  if (threadIdx.x == 0) *p = v;
 }
 
 // ===========================================================================

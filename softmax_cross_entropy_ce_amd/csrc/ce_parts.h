@@ -111,9 +111,9 @@ constexpr int part_capacity(int NT, int NR, int NL, int NXW) { return (NR + NL) 
 template <typename T, int P, int NT, int NR, int NL, int NXW, int OP = kOpCE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8)))
 void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B,
-                    int C, RowScale rs, T* __restrict__ grad, float* __restrict__ loss_rows,
+                    int C, RowArgs rs, T* __restrict__ grad, float* __restrict__ loss_rows,
                     int spin, uint32_t* __restrict__ fallbacks) {
-  const float invB = rs.invB, gmul = grad_mul(rs);
+  const float invB = row_invB(rs), gmul = grad_mul(rs);
   using E = Elem<T>;
   constexpr int NW = NT / 64, VE = E::VE, ES = sizeof(T);
   constexpr int NLS = NL + (NXW > 0 ? 1 : 0);  // LDS slots, the last maybe partial
@@ -134,8 +134,8 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   part_of_block<P>(blockIdx.x, row, part);
   if (row >= B) return;  // whole workgroup (and every part of the row)
 
-  const T* rp = logits + row * C;
-  T* gp = grad + row * C;
+  const T* rp = logits + row * rs.ldz;
+  T* gp = grad + row * rs.ldg;
   const RowGeom geo = row_geom<T, kPartAlign>(rp, C);
   const PartRange own = part_range(geo.nb, P, part);
   const rsrc_t rrow = make_rsrc(rp, (uint32_t)C * ES);
@@ -350,7 +350,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
     sx = s0 * exp2_hw(c0 - cg);
     sx = sx + s1 * exp2_hw(c1 - cg);
   }
-  const RowResult rr = row_finish<OP>(cg, sx, zt, valid, invB, gmul);
+  const RowResult rr = row_finish<OP>(cg, sx, zt, valid, rt.ignored, invB, gmul);
   if (part == 0 && tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
 
   // Phase C: the gradient of this part from registers and LDS.

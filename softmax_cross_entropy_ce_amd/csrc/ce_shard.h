@@ -36,7 +36,7 @@ constexpr int kShardChunk = kShardThreads * kShardSlots;    // body vectors per 
 template <typename T>
 __global__ __launch_bounds__(kShardThreads) void ce_shard_grad_kernel(
     const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B, int C,
-    int64_t col0, int64_t Ctot, const f32x4* __restrict__ recs, int nshards, RowScale rs,
+    int64_t col0, int64_t Ctot, const f32x4* __restrict__ recs, int nshards, RowArgs rs,
     T* __restrict__ grad, float* __restrict__ loss_rows, int chunks) {
   using E = Elem<T>;
   constexpr int VE = E::VE, NT = kShardThreads;
@@ -45,8 +45,8 @@ __global__ __launch_bounds__(kShardThreads) void ce_shard_grad_kernel(
   const int tid = threadIdx.x;
   const uint32_t voff = (uint32_t)tid * 16u;
 
-  const T* rp = logits + row * C;
-  T* gp = grad + row * C;
+  const T* rp = logits + row * rs.ldz;
+  T* gp = grad + row * rs.ldg;
   const RowGeom geo = row_geom(rp, C);
   const int v0 = chunk * kShardChunk;
   const int nv = geo.nb - v0 < kShardChunk ? geo.nb - v0 : kShardChunk;

@@ -36,7 +36,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "make_inputs", "make_workload",
-           "spike_columns", "bf16_bits_from_f32", "grid_logits", "simplex_rows"]
+           "spike_columns", "bf16_bits_from_f32", "f16_bits_from_f32", "grid_logits",
+           "simplex_rows"]
 
 _BLOCK_ELEMS = 1 << 23  # about 8M logits per independently seeded block
 
@@ -86,6 +87,17 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+def f16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to IEEE binary16 (nearest, ties to even, with
+    subnormals) and return the 16-bit patterns as uint16."""
+    with np.errstate(over="ignore"):
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def _to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_bits_from_f32(x) if dtype == "bf16" else f16_bits_from_f32(x)
+
+
 def _threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
@@ -95,10 +107,11 @@ def make_inputs(B: int, C: int, dtype: str = "f32", sigma: float = 1.0,
     """Draw ``(logits, targets)`` for a ``[B, C]`` problem.
 
     ``logits`` is float32 ``[B, C]`` for dtype "f32" and the uint16 bit
-    pattern of bfloat16 values ``[B, C]`` for dtype "bf16"; ``targets`` is
-    int32 ``[B]`` uniform in ``[0, C)``.
+    pattern of bfloat16 or float16 values ``[B, C]`` for dtype "bf16" or
+    "f16" (the float32 draw rounded to nearest even); ``targets`` is int32
+    ``[B]`` uniform in ``[0, C)``.
     """
-    if dtype not in ("f32", "bf16"):
+    if dtype not in ("f32", "bf16", "f16"):
         raise ValueError(f"unknown dtype {dtype!r}")
     ss_t, ss_z, ss_s = np.random.SeedSequence(seed).spawn(3)
     targets = np.random.Generator(np.random.PCG64(ss_t)).integers(
@@ -121,8 +134,8 @@ def make_inputs(B: int, C: int, dtype: str = "f32", sigma: float = 1.0,
         seg *= np.float32(sigma)
         if spike is not None:
             pass  # spikes are placed after all blocks are drawn
-        if dtype == "bf16" and spike is None:
-            out[lo:hi] = bf16_bits_from_f32(seg)
+        if dtype != "f32" and spike is None:
+            out[lo:hi] = _to_bits(seg, dtype)
 
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(fill, range(nblocks)))
@@ -131,8 +144,8 @@ def make_inputs(B: int, C: int, dtype: str = "f32", sigma: float = 1.0,
         cols = np.random.Generator(np.random.PCG64(ss_s)).integers(
             0, C, size=B, dtype=np.int64)
         flat32.reshape(B, C)[np.arange(B), cols] = np.float32(spike)
-        if dtype == "bf16":
-            out[:] = bf16_bits_from_f32(flat32)
+        if dtype != "f32":
+            out[:] = _to_bits(flat32, dtype)
     logits = out.reshape(B, C)
     return logits, targets
 
@@ -163,7 +176,7 @@ def simplex_rows(B: int, C: int, dtype: str = "f32", seed: int = 0) -> np.ndarra
     divided by their row sum in float64), then rounded to float32 or to
     bfloat16 (returned as uint16 bit patterns).  Drawn in independently
     seeded row blocks, like ``make_inputs``."""
-    if dtype not in ("f32", "bf16"):
+    if dtype not in ("f32", "bf16", "f16"):
         raise ValueError(f"unknown dtype {dtype!r}")
     rows_per = max(1, _BLOCK_ELEMS // max(C, 1))
     nblocks = max(1, -(-B // rows_per))
@@ -176,7 +189,7 @@ def simplex_rows(B: int, C: int, dtype: str = "f32", seed: int = 0) -> np.ndarra
             return
         w = np.random.Generator(np.random.PCG64(children[i])).standard_exponential((hi - lo, C))
         y = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
-        out[lo:hi] = y if dtype == "f32" else bf16_bits_from_f32(y)
+        out[lo:hi] = y if dtype == "f32" else _to_bits(y, dtype)
 
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(fill, range(nblocks)))

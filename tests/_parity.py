@@ -11,6 +11,11 @@ Tolerances (from the definition of the bars):
   counting as zero, plus an absolute slack of 2^-50 / B that covers the
   oracle's own rounding of softmax_t - 1 in fp64; scalar loss relative
   error <= 2e-3.
+* fp16 logits: gradient within 1 fp16 ulp of the oracle's fp64 value
+  rounded once to fp16 (nearest even, with fp16's subnormals, whose
+  spacing 2^-24 is then the ulp), plus the same 2^-50 / B slack; the
+  arithmetic is float32 on exactly widened inputs, as for fp32, so the
+  scalar loss is held to fp32's 1e-5.
 """
 
 from __future__ import annotations
@@ -19,7 +24,7 @@ import math
 
 import numpy as np
 
-from oracle import ce_rows, reduce_loss, rne_bf16_bits, widen_bf16
+from oracle import ce_rows, reduce_loss, rne_bf16_bits, rne_f16_bits, widen_bf16, widen_f16
 
 F32_GRAD_ATOL = 1e-6
 F32_LOSS_RTOL = 1e-5
@@ -39,17 +44,18 @@ def to_device(logits: np.ndarray, targets: np.ndarray, dtype: str, device="cuda:
         z = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).to(device)
     else:
         z = torch.from_numpy(np.ascontiguousarray(logits).view(np.int16)).to(device).view(
-            torch.bfloat16)
+            torch.bfloat16 if dtype == "bf16" else torch.float16)
     t = torch.from_numpy(np.ascontiguousarray(targets, dtype=np.int32)).to(device)
     return z, t
 
 
 def grad_to_host(grad, dtype: str) -> np.ndarray:
-    """fp32 gradient as float32 numpy; bf16 gradient as uint16 bit patterns."""
+    """fp32 gradient as float32 numpy; bf16 / fp16 gradient as uint16 bit
+    patterns."""
     torch = torch_mod()
     if dtype == "f32":
         return grad.cpu().numpy()
-    return grad.view(torch.int16).cpu().numpy().view(np.uint16)
+    return grad.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 def run_gpu(z_dev, t_dev):
@@ -71,9 +77,18 @@ def bf16_order(bits: np.ndarray) -> np.ndarray:
     return np.where(b & 0x8000, -mag, mag)
 
 
+def f16_order(bits: np.ndarray) -> np.ndarray:
+    """Map fp16 bit patterns to integers that count ulps monotonically,
+    subnormals included (their spacing 2^-24 is fp16's ulp there)."""
+    b = bits.astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
 def widen_rows(logits_block: np.ndarray, dtype: str) -> np.ndarray:
-    return (np.asarray(logits_block, dtype=np.float64) if dtype == "f32"
-            else widen_bf16(logits_block))
+    if dtype == "f32":
+        return np.asarray(logits_block, dtype=np.float64)
+    return widen_bf16(logits_block) if dtype == "bf16" else widen_f16(logits_block)
 
 
 def compare_block(g_gpu: np.ndarray, l_gpu: np.ndarray, z: np.ndarray, t: np.ndarray, B: int,
@@ -89,8 +104,7 @@ def compare_block(g_gpu: np.ndarray, l_gpu: np.ndarray, z: np.ndarray, t: np.nda
     # invalid targets: NaN loss and an all-NaN gradient row
     if (~valid).any():
         assert np.isnan(l_gpu[~valid]).all(), f"{where}: invalid-target loss not NaN"
-        gi = g_gpu[~valid]
-        gi = widen_bf16(gi) if dtype == "bf16" else gi
+        gi = widen_rows(g_gpu[~valid], dtype)
         assert np.isnan(gi).all(), f"{where}: invalid-target gradient not NaN"
     g_gpu, l_gpu, g_ora, l_ora, z64 = (g_gpu[valid], l_gpu[valid], g_ora[valid], l_ora[valid],
                                       z64[valid])
@@ -106,14 +120,15 @@ def compare_block(g_gpu: np.ndarray, l_gpu: np.ndarray, z: np.ndarray, t: np.nda
                                  f"{F32_GRAD_ATOL} at row {r} col {c}: gpu {g_gpu[r, c]!r} "
                                  f"oracle {g_ora[r, c]!r}")
     else:
-        want = rne_bf16_bits(g_ora)
-        ulp = np.abs(bf16_order(g_gpu) - bf16_order(want))
-        slack = np.abs(widen_bf16(g_gpu) - g_ora) <= 2.0 ** -50 / B
+        rne, order = (rne_bf16_bits, bf16_order) if dtype == "bf16" else (rne_f16_bits, f16_order)
+        want = rne(g_ora)
+        ulp = np.abs(order(g_gpu) - order(want))
+        slack = np.abs(widen_rows(g_gpu, dtype) - g_ora) <= 2.0 ** -50 / B
         bad = (ulp > BF16_MAX_ULP) & ~slack
         out["grad_ulp"] = int(ulp.max())
         if bad.any():
             r, c = np.argwhere(bad)[0]
-            raise AssertionError(f"{where}: bf16 gradient {ulp[r, c]} ulp from RNE(oracle) at "
+            raise AssertionError(f"{where}: {dtype} gradient {ulp[r, c]} ulp from RNE(oracle) at "
                                  f"row {r} col {c}: gpu bits {g_gpu[r, c]:#06x} want "
                                  f"{want[r, c]:#06x} (oracle {g_ora[r, c]!r})")
     # per-row loss diagnostic
@@ -130,7 +145,7 @@ def compare_block(g_gpu: np.ndarray, l_gpu: np.ndarray, z: np.ndarray, t: np.nda
 
 
 def compare_scalar(loss_gpu: float, loss_rows_oracle_sum: float, dtype: str, where: str = ""):
-    rtol = F32_LOSS_RTOL if dtype == "f32" else BF16_LOSS_RTOL
+    rtol = BF16_LOSS_RTOL if dtype == "bf16" else F32_LOSS_RTOL
     denom = max(abs(loss_rows_oracle_sum), 1e-30)
     rel = abs(loss_gpu - loss_rows_oracle_sum) / denom
     assert rel <= rtol or abs(loss_gpu - loss_rows_oracle_sum) <= 1e-30, (

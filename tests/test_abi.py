@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function():
                             "ce_debug_part_counter", "ce_stream_copy",
                             "ce_fwd_grad_scaled", "ce_scale_grad", "ce_fwd_loss",
                             "ce_softmax_fwd", "ce_softmax_bwd", "ce_shard_stats",
-                            "ce_shard_grad"])
+                            "ce_shard_grad", "ce_fwd_grad_ex", "ce_fwd_workspace_bytes"])
     for n in names:
         assert hasattr(L_, n), n
 
@@ -73,7 +73,7 @@ def test_fwd_grad_shapes():
 
 
 def test_fwd_grad_dtype():
-    assert fwd(dtype=2) == DTYPE
+    assert fwd(dtype=3) == DTYPE
     assert fwd(dtype=-1) == DTYPE
 
 
@@ -252,7 +252,7 @@ def smb(y=Z, dy=T, B=8, C=10, dtype=0, dx=G):
 
 def test_softmax_bwd_validation():
     assert smb(y=None) == NULL and smb(dy=None) == NULL and smb(dx=None) == NULL
-    assert smb(dtype=2) == DTYPE
+    assert smb(dtype=3) == DTYPE
     assert smb(B=0) == SHAPE and smb(C=-1) == SHAPE and smb(B=1 << 31) == SHAPE
     assert smb(y=Z + 2) == ALIGN
     assert smb(dy=T + 4) == ALIGN                # y and dy 16-byte congruent
@@ -304,3 +304,40 @@ def test_shard_grad_validation():
     assert sgr(lo=L + 2) == ALIGN and sgr(sc=T + 1) == ALIGN
     assert sgr(z=Z, g=Z + 16) == ALIAS           # grad partly over the logits
     assert sgr(g=L - 64) == ALIAS                # grad over the records
+
+
+NO_IGNORE = -(1 << 31)
+WS = 0x50000000
+
+
+def fex(z=Z, ldz=10, t=T, B=8, C=10, dtype=0, g=G, ldg=10, l=L, sc=None, ii=NO_IGNORE, ws=None,
+        wsb=0):
+    return ce.lib().ce_fwd_grad_ex(z, ldz, t, B, C, dtype, g, ldg, l, sc, ii, ws, wsb, None)
+
+
+def test_fwd_workspace_bytes():
+    assert ce.fwd_workspace_bytes() == 0 and ce.fwd_workspace_bytes(-100) == 4
+    assert ce.fwd_workspace_bytes(0) == 4
+
+
+def test_fwd_grad_ex_validation():
+    assert fex(z=None) == NULL and fex(t=None) == NULL and fex(l=None) == NULL
+    assert fex(dtype=3) == DTYPE
+    assert fex(B=0) == SHAPE and fex(C=0) == SHAPE
+    assert fex(ldz=9) == SHAPE                     # row stride below C
+    assert fex(ldg=9) == SHAPE
+    assert fex(ldz=12, ldg=10) == ALIGN            # rows 8 bytes apart modulo 16
+    assert fex(g=G + 4) == ALIGN
+    assert fex(sc=L + 2) == ALIGN
+    assert fex(ii=-100) == WORKSPACE               # ignore_index needs the count's workspace
+    assert fex(ii=-100, ws=WS, wsb=3) == WORKSPACE
+    assert fex(ii=-100, ws=WS + 2, wsb=4) == ALIGN
+    # grad overlapping logits with another stride, or partly
+    assert fex(z=Z, g=Z + 16 * 4, ldz=14, ldg=10) == ALIAS
+    assert fex(z=Z, g=Z, ldz=14, ldg=10) == ALIAS  # same base, other stride: not in place
+    prev = ce.force_path(4)
+    try:
+        assert fex(g=None) == PATH                 # loss only: no row parts
+        assert fex(z=Z, g=Z, ldz=128256, ldg=128256, C=128256, dtype=1) == PATH
+    finally:
+        ce.force_path(prev)
