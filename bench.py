@@ -260,6 +260,22 @@ def softmax_and_shards(zd, td, grad, loss_rows, reps: int = 20, nshards: int = 8
                           stream, reps)
     out["shard_grad"] = _rate(2 * B * Cs * es + 4 * B + 16 * nshards * B + 4 * B, ms)
     out["shard"] = {"shards": nshards, "columns": Cs}
+    del shards, recs, g0
+    # attention-shaped rows (the softmax of scaled dot products: batch 4 x
+    # 32 heads x 2048 queries, 2048 keys), bf16, values from torch's device
+    # generator (timing only)
+    Ba, Ca = 4 * 32 * 2048, 2048
+    gen = torch.Generator(device=zd.device).manual_seed(0)
+    xa = torch.randn((Ba, Ca), generator=gen, device=zd.device).mul_(3).to(torch.bfloat16)
+    ya = torch.empty_like(xa)
+    ms = _event_median_ms(lambda: ce.softmax_fwd_into(xa, ya), stream, reps)
+    att = {"rows": Ba, "columns": Ca, "dtype": "bf16",
+           "softmax_fwd": _rate(2 * Ba * Ca * 2, ms)}
+    dya = torch.randn((Ba, Ca), generator=gen, device=zd.device).to(torch.bfloat16)
+    dxa = torch.empty_like(xa)
+    ms = _event_median_ms(lambda: ce.softmax_bwd_into(ya, dya, dxa), stream, reps)
+    att["softmax_bwd"] = _rate(3 * Ba * Ca * 2, ms)
+    out["attention_rows"] = att
     return out
 
 

@@ -34,6 +34,12 @@ struct RowCfg {
 };
 constexpr RowCfg kRowCfgs[] = {{64, 1},   {64, 2},   {64, 4},    {256, 2},  {256, 4},
                                {1024, 2}, {1024, 4}, {1024, 8},  {1024, 16}};
+// Rows read for a per-row value only (the loss alone, shard records) run on
+// these: 256-thread workgroups hold up to 4096 vectors, so several rows
+// are in flight on each compute unit (no gradient has to wait in
+// registers for the row's reduction).
+constexpr RowCfg kReadCfgs[] = {{64, 1},   {64, 2},   {64, 4},    {256, 2},  {256, 4},
+                                {256, 8},  {256, 16}, {1024, 8},  {1024, 16}};
 constexpr RowCfg kLongCfg = {1024, 16};     // automatic path 3
 constexpr RowCfg kLongTestCfg = {256, 1};   // forced path 3: small on-chip part
 
@@ -198,6 +204,10 @@ int launch_row(RowCfg cfg, const T* z, const int32_t* t, int64_t B, int64_t C, c
   CE_ROW_CASE(256, 1)
   CE_ROW_CASE(256, 2)
   CE_ROW_CASE(256, 4)
+  if constexpr (!GRAD) {
+    CE_ROW_CASE(256, 8)
+    CE_ROW_CASE(256, 16)
+  }
   CE_ROW_CASE(1024, 2)
   CE_ROW_CASE(1024, 4)
   CE_ROW_CASE(1024, 8)
@@ -206,9 +216,16 @@ int launch_row(RowCfg cfg, const T* z, const int32_t* t, int64_t B, int64_t C, c
   return CE_ERR_PATH;
 }
 
-RowCfg resident_cfg(int64_t C, int es, bool* ok) {
-  const int64_t need = row_vectors(C, es);
-  for (const RowCfg& r : kRowCfgs)
+// 16-byte vectors of a row's body: exactly floor(C * es / 16) when every
+// row of every array starts on a 16-byte boundary, else at most
+// row_vectors.
+int64_t row_need(int64_t C, int es, bool aligned) {
+  return aligned ? C * es / 16 : row_vectors(C, es);
+}
+
+RowCfg resident_cfg(int64_t C, int es, bool* ok, bool grad = true, bool aligned = false) {
+  const int64_t need = row_need(C, es, aligned);
+  for (const RowCfg& r : (grad ? kRowCfgs : kReadCfgs))
     if ((int64_t)r.nt * r.nv >= need) {
       *ok = true;
       return r;
@@ -246,12 +263,15 @@ int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs
 template <typename T, int OP, bool GRAD>
 int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g, float* l,
               ce::RowArgs rs, hipStream_t st) {
+  constexpr int es = sizeof(T);
+  const bool aligned = (uintptr_t)z % 16 == 0 && (rs.ldz * es) % 16 == 0 &&
+                       (!GRAD || ((uintptr_t)g % 16 == 0 && (rs.ldg * es) % 16 == 0));
   switch (path) {
     case kPathShort:
       return launch_short<T, OP, GRAD>(z, t, B, C, rs, g, l, st);
     case kPathResident: {
       bool ok = false;
-      const RowCfg cfg = resident_cfg(C, sizeof(T), &ok);
+      const RowCfg cfg = resident_cfg(C, es, &ok, GRAD, aligned);
       if (!ok) return CE_ERR_PATH;
       if constexpr (GRAD) {
         if (cfg.nt == 1024 && cfg.nv == 16) return launch_row_lds<T, OP>(z, t, B, C, rs, g, l, st);
@@ -549,7 +569,8 @@ int softmax_bwd_typed(int path, const T* y, const T* dy, int64_t B, int64_t C, T
     case kPathShort:
       return launch_bwd_short<T>(y, dy, B, C, dx, st);
     case kPathResident: {
-      const int64_t need = row_vectors(C, sizeof(T));
+      const bool aligned = (uintptr_t)y % 16 == 0 && (C * sizeof(T)) % 16 == 0;  // dy, dx: congruent
+      const int64_t need = row_need(C, sizeof(T), aligned);
       for (const RowCfg& r : kBwdCfgs)
         if ((int64_t)r.nt * r.nv >= need) return launch_bwd_row<T>(r, y, dy, B, C, dx, st);
       return CE_ERR_PATH;
@@ -572,8 +593,9 @@ int launch_shard_grad(const T* z, const int32_t* t, int64_t B, int64_t C, int64_
                       float* l, hipStream_t st) {
   const int64_t nb = body_vectors_max(C, sizeof(T));
   const int64_t chunks = nb > 0 ? (nb + ce::kShardChunk - 1) / ce::kShardChunk : 1;
-  if (B * chunks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL(ce::ce_shard_grad_kernel<T>, dim3((unsigned)(B * chunks)),
+  const int64_t blocks = (B * chunks + ce::kShardUnits - 1) / ce::kShardUnits;
+  if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
+  hipLaunchKernelGGL(ce::ce_shard_grad_kernel<T>, dim3((unsigned)blocks),
                      dim3(ce::kShardThreads), 0, st, z, t, B, (int)C, col0, Ctot,
                      reinterpret_cast<const ce::f32x4*>(recs), nshards, rs, g, l, (int)chunks);
   return launched();

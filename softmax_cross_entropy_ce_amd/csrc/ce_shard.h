@@ -23,14 +23,21 @@
 
 namespace ce {
 
-constexpr int kShardThreads = 256;
+// A unit of work is 256 threads x 8 slots: 2048 body vectors of one row.
+// Four units share a 1024-thread workgroup (large workgroups stream
+// faster than small ones on this GPU); they need no barrier, since every
+// thread combines the records of its row by itself.
+constexpr int kShardThreads = 1024;
+constexpr int kShardUnit = 256;                             // threads per unit
+constexpr int kShardUnits = kShardThreads / kShardUnit;     // units per workgroup
 constexpr int kShardSlots = 8;                              // 16-byte vectors per thread
-constexpr int kShardChunk = kShardThreads * kShardSlots;    // body vectors per workgroup
+constexpr int kShardChunk = kShardUnit * kShardSlots;       // body vectors per unit
 
-// Workgroup g handles body vectors [j * kShardChunk, (j + 1) * kShardChunk)
-// of row g / chunks (j = g % chunks), and chunk 0 also the row's elements
-// before its first 16-byte boundary and after its last.  recs holds
-// nshards x B records, shard-major.  A row whose target lies outside
+// Unit u (= 4 * workgroup + threadIdx.x / 256) handles body vectors
+// [j * kShardChunk, (j + 1) * kShardChunk) of row u / chunks (j = u %
+// chunks), and chunk 0 also the row's elements before its first 16-byte
+// boundary and after its last; units past B * chunks do nothing.  recs
+// holds nshards x B records, shard-major.  A row whose target lies outside
 // [0, Ctot), or is held by other than exactly one shard's record, gets NaN
 // loss and gradient.
 template <typename T>
@@ -39,10 +46,15 @@ __global__ __launch_bounds__(kShardThreads) void ce_shard_grad_kernel(
     int64_t col0, int64_t Ctot, const f32x4* __restrict__ recs, int nshards, RowArgs rs,
     T* __restrict__ grad, float* __restrict__ loss_rows, int chunks) {
   using E = Elem<T>;
-  constexpr int VE = E::VE, NT = kShardThreads;
-  const int64_t row = (int64_t)(blockIdx.x / (uint32_t)chunks);
-  const int chunk = (int)(blockIdx.x % (uint32_t)chunks);
-  const int tid = threadIdx.x;
+  constexpr int VE = E::VE, NT = kShardUnit;
+  // wave-uniform (a unit is four whole waves): readfirstlane lets the
+  // compiler load the row's records and target with scalar loads
+  const int64_t unit = (int64_t)blockIdx.x * kShardUnits +
+                       __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kShardUnit));
+  const int64_t row = unit / chunks;
+  if (row >= B) return;  // whole waves: a unit is four waves
+  const int chunk = (int)(unit % chunks);
+  const int tid = threadIdx.x % kShardUnit;
   const uint32_t voff = (uint32_t)tid * 16u;
 
   const T* rp = logits + row * rs.ldz;
