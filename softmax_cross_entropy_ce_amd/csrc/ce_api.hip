@@ -125,9 +125,34 @@ bool short_span_ok(int64_t C, int64_t ld, int es) {
 // of two that covers the row with EPL elements per lane (EPL = 16 bytes of
 // elements, more only at S = 16).  Lanes of a row read adjacent vectors,
 // so a load instruction covers 64/S consecutive rows.
+int resident_blocks(const void* kernel, int nt);
+
+// Rows of at most 64 bytes, contiguous, in 16-byte aligned arrays: the
+// LDS-staged kernel with one row per thread, persistent over chunks of 256
+// rows.
+template <typename T, int OP, bool GRAD>
+int launch_tiny(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g, float* l,
+                hipStream_t st) {
+  auto kern = ce::ce_tiny_kernel<T, GRAD, OP>;
+  const int res = resident_blocks(reinterpret_cast<const void*>(kern), ce::kTinyRows);
+  if (res < 1) return CE_ERR_LAUNCH;
+  const int64_t chunks = (B + ce::kTinyRows - 1) / ce::kTinyRows;
+  const int64_t grid = chunks < res ? chunks : res;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(ce::kTinyRows), 0, st, z, t, B, (int)C, rs, g,
+                     l);
+  return launched();
+}
+
+template <typename T>
+bool tiny_rows(const T* z, int64_t C, const ce::RowArgs& rs, const T* g, bool grad) {
+  return C * (int64_t)sizeof(T) <= ce::kTinyRowBytes && rs.ldz == C && (uintptr_t)z % 16 == 0 &&
+         (!grad || (rs.ldg == C && (uintptr_t)g % 16 == 0));
+}
+
 template <typename T, int OP, bool GRAD>
 int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g, float* l,
                  hipStream_t st) {
+  if (tiny_rows(z, C, rs, g, GRAD)) return launch_tiny<T, OP, GRAD>(z, t, B, C, rs, g, l, st);
   if (!short_span_ok(C, rs.ldz, sizeof(T)) || (GRAD && !short_span_ok(C, rs.ldg, sizeof(T))))
     return CE_ERR_PATH;
   constexpr int es = sizeof(T);
@@ -305,10 +330,16 @@ bool overlaps(uintptr_t a, uintptr_t an, uintptr_t b, uintptr_t bn) {
 }
 
 // ------------------------------------------------------------ reduction
-constexpr int64_t kReduceMinChunk = 16384;  // one workgroup, one launch, up to here
+// Up to kReduceOneLaunch rows one workgroup sums them in a single launch.
+// Above, the first level has up to kReduceMaxBlocks workgroups with chunks
+// of at least kReduceMinChunk rows (2048: 8 per thread), so that the whole
+// GPU reads the rows, then one workgroup sums the partials.
+constexpr int64_t kReduceOneLaunch = 16384;
+constexpr int64_t kReduceMinChunk = 2048;
 constexpr int64_t kReduceMaxBlocks = 1024;
 
 int64_t reduce_chunk(int64_t B) {
+  if (B <= kReduceOneLaunch) return kReduceOneLaunch;
   const int64_t step = 4 * ce::kReduceThreads;
   int64_t chunk = (B + kReduceMaxBlocks - 1) / kReduceMaxBlocks;
   chunk = (chunk + step - 1) / step * step;

@@ -377,6 +377,145 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
 }
 
 // ===========================================================================
+// Path 1, rows of at most 64 bytes (fp32 C <= 16, bf16/fp16 C <= 32) with
+// contiguous rows and 16-byte aligned arrays.  A chunk of 256 rows is at
+// most 16 KB and starts on a 16-byte boundary (256 * C * size is a multiple
+// of 16), so the workgroup reads it with whole 16-byte loads into LDS, each
+// thread reduces one row from LDS without any cross-lane step, writes its
+// gradient back into LDS, and the chunk leaves with whole 16-byte stores.
+// The workgroups are persistent; the next chunk's loads are issued before
+// this chunk's stores.  The last, partial chunk of a call is moved one
+// element per thread instead.
+// ===========================================================================
+constexpr int kTinyRows = 256;      // rows per chunk, one per thread
+constexpr int kTinyRowBytes = 64;   // largest row
+constexpr int kTinyVecs = kTinyRows * kTinyRowBytes / 16 / kTinyRows;  // 16-byte loads per thread
+
+template <typename T>
+struct LdsElem;
+template <>
+struct LdsElem<float> {
+  __device__ static __forceinline__ float get(const u32x4* st, int i) {
+    return reinterpret_cast<const float*>(st)[i];
+  }
+  __device__ static __forceinline__ void put(u32x4* st, int i, float g) {
+    reinterpret_cast<float*>(st)[i] = g;
+  }
+};
+template <>
+struct LdsElem<__bf16> {
+  __device__ static __forceinline__ float get(const u32x4* st, int i) {
+    return __builtin_bit_cast(float, (unsigned)reinterpret_cast<const unsigned short*>(st)[i] << 16);
+  }
+  __device__ static __forceinline__ void put(u32x4* st, int i, float g) {
+    reinterpret_cast<unsigned short*>(st)[i] = (unsigned short)(pack_bf16x2(g, 0.f) & 0xffffu);
+  }
+};
+template <>
+struct LdsElem<_Float16> {
+  __device__ static __forceinline__ float get(const u32x4* st, int i) {
+    return f16lo((unsigned)reinterpret_cast<const unsigned short*>(st)[i]);
+  }
+  __device__ static __forceinline__ void put(u32x4* st, int i, float g) {
+    reinterpret_cast<unsigned short*>(st)[i] = (unsigned short)(pack_f16x2(g, 0.f) & 0xffffu);
+  }
+};
+
+template <typename T, bool GRAD, int OP = kOpCE>
+__global__ __launch_bounds__(kTinyRows) void ce_tiny_kernel(const T* __restrict__ logits,
+                                                            const int32_t* __restrict__ targets,
+                                                            int64_t B, int C, RowArgs rs,
+                                                            T* __restrict__ grad,
+                                                            float* __restrict__ loss_rows) {
+  using E = Elem<T>;
+  constexpr int ES = sizeof(T), CMAX = kTinyRowBytes / ES, NT = kTinyRows, K = kTinyVecs;
+  __shared__ u32x4 stage[NT * K];
+  const float invB = row_invB(rs), gmul = grad_mul(rs);
+  const int tid = threadIdx.x;
+  const uint32_t voff = (uint32_t)tid * 16u;
+  const int64_t nchunks = (B + NT - 1) / NT;
+  const int64_t nfull = B / NT;              // chunks of exactly NT rows
+  const uint32_t full_bytes = (uint32_t)(NT * C * ES);
+  const int nvec = (int)(full_bytes / 16);   // 16-byte vectors of a full chunk
+  int64_t chunk = blockIdx.x;
+  if (chunk >= nchunks) return;
+
+  auto load_full = [&](int64_t ch, u32x4 (&v)[K]) {
+    const rsrc_t r = make_rsrc(logits + ch * NT * C, full_bytes);
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = bload128<kPolicyStream>(r, voff, (uint32_t)k * NT * 16u);
+  };
+  u32x4 v[K];
+  if (chunk < nfull) load_full(chunk, v);
+
+  for (;;) {
+    const int64_t row0 = chunk * NT;
+    const bool full = chunk < nfull;
+    const int nrows = full ? NT : (int)(B - row0);
+    // the chunk into LDS
+    if (full) {
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if (tid + k * NT < nvec) stage[tid + k * NT] = v[k];
+    } else {
+      for (int i = tid; i < nrows * C; i += NT)
+        LdsElem<T>::put(stage, i, E::load1(logits + row0 * C + i));
+    }
+    __syncthreads();
+    // the next chunk's loads, before this chunk's stores
+    const int64_t next = chunk + gridDim.x;
+    if (next < nfull) load_full(next, v);
+
+    // one row per thread
+    if (tid < nrows) {
+      const int64_t row = row0 + tid;
+      const RowTarget rt = row_target<OP>(targets, row, C, rs);
+      const int t = rt.t;
+      float f[CMAX];
+      float m = kNegInf;
+#pragma unroll
+      for (int c = 0; c < CMAX; ++c) {
+        f[c] = c < C ? LdsElem<T>::get(stage, tid * C + c) : kNegInf;
+        m = __builtin_fmaxf(m, f[c]);
+      }
+      const float cg = m * kLog2e;
+      float e[CMAX];
+      float zt = 0.f;
+#pragma unroll
+      for (int c = 0; c < CMAX; ++c) {
+        zt = (c == t) ? f[c] : zt;
+        e[c] = (c == t) ? 0.f : exp2_hw(__builtin_fmaf(f[c], kLog2e, -cg));
+      }
+      const float sx = tree_sum(e);
+      const RowResult rr = row_finish<OP>(cg, sx, zt, rt.valid, rt.ignored, invB, gmul);
+      store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
+      if constexpr (GRAD) {
+#pragma unroll
+        for (int c = 0; c < CMAX; ++c)
+          if (c < C)
+            LdsElem<T>::put(stage, tid * C + c,
+                            c == t ? rr.gt : exp2_hw(__builtin_fmaf(f[c], kLog2e, -cg)) * rr.scale);
+      }
+    }
+    if constexpr (GRAD) {
+      __syncthreads();
+      if (full) {
+        const rsrc_t r = make_rsrc(grad + row0 * C, full_bytes);
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+          if (tid + k * NT < nvec)
+            bstore128<kPolicyStream>(stage[tid + k * NT], r, voff, (uint32_t)k * NT * 16u);
+      } else {
+        for (int i = tid; i < nrows * C; i += NT) E::store1(grad + row0 * C + i, LdsElem<T>::get(stage, i));
+      }
+    }
+    if (next >= nchunks) break;
+    chunk = next;
+    __syncthreads();  // the stage is refilled next
+  }
+}
+
+// ===========================================================================
 // Paths 2 and 3: one workgroup of NT threads per row at a time.  The row's
 // aligned body is split into 16-byte vectors; thread i holds vectors i,
 // i+NT, ..., i+(NV-1)NT in registers (NV*16 bytes per thread).  Vectors

@@ -97,7 +97,7 @@ def test_reduce_workspace_sizes():
     assert f(0) == 0 and f(-5) == 0
     # up to 16384 rows one workgroup sums them in a single launch
     assert f(1) == 0 and f(8) == 0 and f(2048) == 0 and f(16384) == 0
-    assert f(16385) == 2 * 4
+    assert f(16385) == 9 * 4                                # chunks of 2048 rows
     # 2M rows: at most 1024 first-level partial sums
     assert 0 < f(2_097_152) <= 1024 * 4
 
