@@ -9,6 +9,7 @@
 #include "ce_parts.h"
 #include "ce_shard.h"
 #include "softmax_bwd.h"
+#include "softmax_bwd_parts.h"
 
 namespace {
 
@@ -588,15 +589,45 @@ int launch_bwd_row(RowCfg cfg, const T* y, const T* dy, int64_t B, int64_t C, T*
   return CE_ERR_PATH;
 }
 
-int bwd_auto_path(int64_t C, int es) {
+// Row parts of the backward: four parts of four register slots of y and of
+// dy (1024 threads): bodies of up to 16384 16-byte vectors per array (bf16
+// C up to 131072, fp32 C up to 65536), out of place only (a part's mailbox
+// is in dx and a recompute reads its partner's y and dy).
+constexpr int kBwdParts = 4;
+constexpr int kBwdPartSlots = 4;
+constexpr int64_t kBwdPartsMax = (int64_t)kBwdParts * kBwdPartSlots * 1024;
+constexpr int64_t kBwdPartsMin = 128;  // every part keeps at least its two mailbox vectors
+
+bool bwd_parts_take(int64_t C, int es, bool in_place) {
+  const int64_t nb = body_vectors_max(C, es);
+  return !in_place && nb >= kBwdPartsMin && nb <= kBwdPartsMax;
+}
+
+int bwd_auto_path(int64_t C, int es, bool in_place) {
   if (C <= kShortMaxC) return kPathShort;
-  return row_vectors(C, es) <= (int64_t)kBwdLongCfg.nt * kBwdLongCfg.nv ? kPathResident : kPathLong;
+  if (row_vectors(C, es) <= (int64_t)kBwdLongCfg.nt * kBwdLongCfg.nv) return kPathResident;
+  if (bwd_parts_take(C, es, in_place)) return kPathParts;
+  return kPathLong;
+}
+
+template <typename T>
+int launch_bwd_parts(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipStream_t st) {
+  const int64_t blocks = kBwdParts * ((B + 7) / 8 * 8);
+  if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
+  hipLaunchKernelGGL((ce::sm_bwd_part_kernel<T, kBwdParts, 1024, kBwdPartSlots>),
+                     dim3((unsigned)blocks), dim3(1024), 0, st, y, dy, B, (int)C, dx,
+                     g_part_polls.load(std::memory_order_relaxed),
+                     g_part_counter.load(std::memory_order_relaxed));
+  return launched();
 }
 
 template <typename T>
 int softmax_bwd_typed(int path, const T* y, const T* dy, int64_t B, int64_t C, T* dx,
-                      hipStream_t st) {
+                      bool in_place, hipStream_t st) {
   switch (path) {
+    case kPathParts:
+      if (!bwd_parts_take(C, sizeof(T), in_place)) return CE_ERR_PATH;
+      return launch_bwd_parts<T>(y, dy, B, C, dx, st);
     case kPathShort:
       return launch_bwd_short<T>(y, dy, B, C, dx, st);
     case kPathResident: {
@@ -715,16 +746,18 @@ int ce_softmax_bwd(const void* y, const void* dy, int64_t B, int64_t C, int dtyp
   // that reads it writes it), but no other overlap
   if (o != a && overlaps(o, n, a, n)) return CE_ERR_ALIAS;
   if (o != b && overlaps(o, n, b, n)) return CE_ERR_ALIAS;
+  const bool in_place = o == a || o == b;
   const int forced = g_force_path.load(std::memory_order_relaxed);
-  const int path = forced ? forced : bwd_auto_path(C, es);
+  const int path = forced ? forced : bwd_auto_path(C, es, in_place);
   const hipStream_t st = as_stream(stream);
   if (dtype == CE_F32)
-    return softmax_bwd_typed<float>(path, (const float*)y, (const float*)dy, B, C, (float*)dx_out, st);
+    return softmax_bwd_typed<float>(path, (const float*)y, (const float*)dy, B, C, (float*)dx_out,
+                                    in_place, st);
   if (dtype == CE_BF16)
     return softmax_bwd_typed<__bf16>(path, (const __bf16*)y, (const __bf16*)dy, B, C,
-                                     (__bf16*)dx_out, st);
+                                     (__bf16*)dx_out, in_place, st);
   return softmax_bwd_typed<_Float16>(path, (const _Float16*)y, (const _Float16*)dy, B, C,
-                                     (_Float16*)dx_out, st);
+                                     (_Float16*)dx_out, in_place, st);
 }
 
 int ce_shard_stats(const void* logits, const int32_t* targets, int64_t B, int64_t C, int64_t col0,

@@ -221,12 +221,14 @@ BWD_SHAPES = [
 BWD_IDS = [f"{b}x{c}-{d}" for b, c, d in BWD_SHAPES]
 
 
-def _bwd_legal(path, C, dtype):
+def _bwd_legal(path, C, dtype, in_place=False):
     es = 4 if dtype == "f32" else 2
     if path == 1:
         return C <= 256
     if path == 2:
         return (C * es + 15) // 16 + 1 <= 8192
+    if path == 4:
+        return not in_place and 128 <= C // (16 // es) <= 16384
     return path in (0, 3)
 
 
@@ -252,7 +254,7 @@ def check_dx(dx_host, y64, dy64, dtype, where):
     return float((err / np.maximum(tol, 1e-300)).max())
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3], ids=["auto", "short", "resident", "long"])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4], ids=["auto", "short", "resident", "long", "parts"])
 @pytest.mark.parametrize("B,C,dtype", BWD_SHAPES, ids=BWD_IDS)
 def test_softmax_bwd_matches_oracle(B, C, dtype, path):
     import torch
@@ -269,7 +271,7 @@ def test_softmax_bwd_matches_oracle(B, C, dtype, path):
     print(f"[softmax] bwd {B}x{C} {dtype} p{path}: worst error / bar {r:.3g}", flush=True)
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3], ids=["auto", "short", "resident", "long"])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4], ids=["auto", "short", "resident", "long", "parts"])
 @pytest.mark.parametrize("B,C,dtype", [(64, 200, "f32"), (40, 50257, "f32"), (9, 128256, "bf16")])
 def test_softmax_bwd_chain_to_cross_entropy(B, C, dtype, path):
     """The softmax of logits (from the oracle; a quarter of the rows with a
@@ -305,25 +307,41 @@ def test_softmax_bwd_chain_to_cross_entropy(B, C, dtype, path):
         assert np.abs(got[keep] - g[keep]).max() <= 1e-6
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3], ids=["auto", "short", "resident", "long"])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4], ids=["auto", "short", "resident", "long", "parts"])
 @pytest.mark.parametrize("B,C,dtype", [(64, 200, "bf16"), (33, 4099, "f32"), (9, 128256, "bf16")])
 def test_softmax_bwd_in_place(B, C, dtype, path):
-    """dx == dy and dx == y give the bits of the out-of-place call."""
+    """dx == dy and dx == y give the bits of the out-of-place call on the
+    same path; forced row parts refuse to run in place, and automatic
+    selection runs long rows in place on path 3."""
     import torch
     ce = _ce()
+    if path == 4 and _bwd_legal(4, C, dtype):
+        ce.force_path(4)
+        y = _dev(synth.simplex_rows(B, C, dtype, seed=C), dtype)
+        a = _dev(synth.make_inputs(B, C, dtype, 1.0, seed=C + 1)[0], dtype)
+        with pytest.raises(ce.CEError):
+            ce.softmax_bwd_into(y, a, a)
+        return
     if not _bwd_legal(path, C, dtype):
         pytest.skip("the forced path does not take this row length")
     ce.force_path(path)
-    y = _dev(synth.simplex_rows(B, C, dtype, seed=C), dtype)
-    dy = _dev(synth.make_inputs(B, C, dtype, 1.0, seed=C + 1)[0], dtype)
+    yh = synth.simplex_rows(B, C, dtype, seed=C)
+    dyh = synth.make_inputs(B, C, dtype, 1.0, seed=C + 1)[0]
+    y, dy = _dev(yh, dtype), _dev(dyh, dtype)
     ref = ce.softmax_bwd(y, dy)
     a = dy.clone()
     ce.softmax_bwd_into(y, a, a)
     b = y.clone()
     ce.softmax_bwd_into(b, dy, b)
     torch.cuda.synchronize()
+    assert torch.equal(_bits(a), _bits(b))
+    if path == 0 and _bwd_legal(4, C, dtype) and not _bwd_legal(2, C, dtype):
+        # out of place these rows run as row parts, in place on path 3: both
+        # against the oracle
+        check_dx(grad_to_host(a, dtype), widen_rows(yh, dtype), widen_rows(dyh, dtype), dtype,
+                 f"in place {B}x{C}")
+        return
     assert torch.equal(_bits(a), _bits(ref))
-    assert torch.equal(_bits(b), _bits(ref))
 
 
 def test_softmax_bwd_full_lmhead128k_sampled():
@@ -359,3 +377,36 @@ def test_softmax_autograd(B, C, dtype):
     check_y(y_host, y_ora, dtype, "autograd fwd")
     check_dx(grad_to_host(x.grad, dtype), widen_rows(y_host, dtype), widen_rows(dy, dtype), dtype,
              "autograd bwd")
+
+
+@pytest.mark.parametrize("B,C,dtype", [(16, 128256, "bf16"), (9, 50257, "f32"), (5, 99999, "f16"),
+                                       (33, 70001, "bf16")])
+def test_softmax_bwd_parts_fallback_is_bitwise(B, C, dtype):
+    """Row parts of the backward with no polls: every part recomputes the
+    other parts' partial dots; the bits equal those of the exchange, and the
+    device counter sees every missing partial."""
+    import torch
+    ce = _ce()
+    if dtype == "f16":
+        y = _dev(synth.simplex_rows(B, C, "f16", seed=C), "f16")
+        dy = _dev(synth.make_inputs(B, C, "f16", 1.0, seed=C + 1)[0], "f16")
+    else:
+        y = _dev(synth.simplex_rows(B, C, dtype, seed=C), dtype)
+        dy = _dev(synth.make_inputs(B, C, dtype, 1.0, seed=C + 1)[0], dtype)
+    ce.force_path(4)
+    prev = ce.part_polls(64)
+    counter = torch.zeros(1, dtype=torch.int32, device=y.device)
+    ce.part_counter(counter)
+    try:
+        dx1 = ce.softmax_bwd(y, dy)
+        torch.cuda.synchronize()
+        ce.part_polls(0)
+        counter.zero_()
+        dx2 = ce.softmax_bwd(y, dy)
+        torch.cuda.synchronize()
+        n = int(counter.item())
+    finally:
+        ce.part_counter(None)
+        ce.part_polls(prev)
+    assert n == B * 4 * 3
+    assert torch.equal(_bits(dx1), _bits(dx2))
