@@ -131,17 +131,32 @@ int resident_blocks(const void* kernel, int nt);
 // Rows of at most 64 bytes, contiguous, in 16-byte aligned arrays: the
 // LDS-staged kernel with one row per thread, persistent over chunks of 256
 // rows.
+// One row per thread: chunks of 256 rows (two rows per thread, with half as
+// many workgroups resident, measured slower).
+constexpr int kTinyRowsPerThread = 1;
+
+template <typename T, int CMAX, int OP, bool GRAD>
+int launch_tiny_w(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
+                  float* l, hipStream_t st) {
+  constexpr int R = kTinyRowsPerThread;
+  auto kern = ce::ce_tiny_kernel<T, CMAX, R, GRAD, OP>;
+  const int res = resident_blocks(reinterpret_cast<const void*>(kern), ce::kTinyThreads);
+  if (res < 1) return CE_ERR_LAUNCH;
+  const int64_t rows = (int64_t)ce::kTinyThreads * R;
+  const int64_t chunks = (B + rows - 1) / rows;
+  const int64_t grid = chunks < res ? chunks : res;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(ce::kTinyThreads), 0, st, z, t, B, (int)C, rs,
+                     g, l);
+  return launched();
+}
+
 template <typename T, int OP, bool GRAD>
 int launch_tiny(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g, float* l,
                 hipStream_t st) {
-  auto kern = ce::ce_tiny_kernel<T, GRAD, OP>;
-  const int res = resident_blocks(reinterpret_cast<const void*>(kern), ce::kTinyRows);
-  if (res < 1) return CE_ERR_LAUNCH;
-  const int64_t chunks = (B + ce::kTinyRows - 1) / ce::kTinyRows;
-  const int64_t grid = chunks < res ? chunks : res;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(ce::kTinyRows), 0, st, z, t, B, (int)C, rs, g,
-                     l);
-  return launched();
+  if (C <= 8) return launch_tiny_w<T, 8, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 16) return launch_tiny_w<T, 16, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if constexpr (sizeof(T) == 2) return launch_tiny_w<T, 32, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  return CE_ERR_PATH;
 }
 
 template <typename T>

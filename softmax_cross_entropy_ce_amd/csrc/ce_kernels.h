@@ -378,18 +378,17 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
 
 // ===========================================================================
 // Path 1, rows of at most 64 bytes (fp32 C <= 16, bf16/fp16 C <= 32) with
-// contiguous rows and 16-byte aligned arrays.  A chunk of 256 rows is at
-// most 16 KB and starts on a 16-byte boundary (256 * C * size is a multiple
-// of 16), so the workgroup reads it with whole 16-byte loads into LDS, each
-// thread reduces one row from LDS without any cross-lane step, writes its
-// gradient back into LDS, and the chunk leaves with whole 16-byte stores.
-// The workgroups are persistent; the next chunk's loads are issued before
-// this chunk's stores.  The last, partial chunk of a call is moved one
-// element per thread instead.
+// contiguous rows and 16-byte aligned arrays.  A chunk of 256 * R rows is
+// at most R * 16 KB and starts on a 16-byte boundary (256 * C * size is a
+// multiple of 16), so the workgroup reads it with whole 16-byte loads into
+// LDS; each thread reduces R rows from LDS without any cross-lane step and
+// writes their gradients back into LDS, and the chunk leaves with whole
+// 16-byte stores.  The workgroups are persistent; the next chunk's loads
+// are issued before this chunk's stores.  The last, partial chunk of a call
+// is moved one element per thread instead.
 // ===========================================================================
-constexpr int kTinyRows = 256;      // rows per chunk, one per thread
+constexpr int kTinyThreads = 256;
 constexpr int kTinyRowBytes = 64;   // largest row
-constexpr int kTinyVecs = kTinyRows * kTinyRowBytes / 16 / kTinyRows;  // 16-byte loads per thread
 
 template <typename T>
 struct LdsElem;
@@ -421,27 +420,31 @@ struct LdsElem<_Float16> {
   }
 };
 
-template <typename T, bool GRAD, int OP = kOpCE>
-__global__ __launch_bounds__(kTinyRows) void ce_tiny_kernel(const T* __restrict__ logits,
-                                                            const int32_t* __restrict__ targets,
-                                                            int64_t B, int C, RowArgs rs,
-                                                            T* __restrict__ grad,
-                                                            float* __restrict__ loss_rows) {
+// CMAX: the row length rounded up to 8, 16 or 32 elements (at most 64
+// bytes), the width of each thread's per-row arrays.  R: rows per thread.
+template <typename T, int CMAX, int R, bool GRAD, int OP = kOpCE>
+__global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restrict__ logits,
+                                                               const int32_t* __restrict__ targets,
+                                                               int64_t B, int C, RowArgs rs,
+                                                               T* __restrict__ grad,
+                                                               float* __restrict__ loss_rows) {
   using E = Elem<T>;
-  constexpr int ES = sizeof(T), CMAX = kTinyRowBytes / ES, NT = kTinyRows, K = kTinyVecs;
+  constexpr int ES = sizeof(T), NT = kTinyThreads, ROWS = NT * R;
+  constexpr int K = (ROWS * CMAX * ES + 16 * NT - 1) / (16 * NT);  // 16-byte loads per thread
+  static_assert(CMAX * ES <= kTinyRowBytes, "row width");
   __shared__ u32x4 stage[NT * K];
   const float invB = row_invB(rs), gmul = grad_mul(rs);
   const int tid = threadIdx.x;
   const uint32_t voff = (uint32_t)tid * 16u;
-  const int64_t nchunks = (B + NT - 1) / NT;
-  const int64_t nfull = B / NT;              // chunks of exactly NT rows
-  const uint32_t full_bytes = (uint32_t)(NT * C * ES);
-  const int nvec = (int)(full_bytes / 16);   // 16-byte vectors of a full chunk
+  const int64_t nchunks = (B + ROWS - 1) / ROWS;
+  const int64_t nfull = B / ROWS;             // chunks of exactly ROWS rows
+  const uint32_t full_bytes = (uint32_t)(ROWS * C * ES);
+  const int nvec = (int)(full_bytes / 16);    // 16-byte vectors of a full chunk
   int64_t chunk = blockIdx.x;
   if (chunk >= nchunks) return;
 
   auto load_full = [&](int64_t ch, u32x4 (&v)[K]) {
-    const rsrc_t r = make_rsrc(logits + ch * NT * C, full_bytes);
+    const rsrc_t r = make_rsrc(logits + ch * ROWS * C, full_bytes);
 #pragma unroll
     for (int k = 0; k < K; ++k) v[k] = bload128<kPolicyStream>(r, voff, (uint32_t)k * NT * 16u);
   };
@@ -449,9 +452,9 @@ __global__ __launch_bounds__(kTinyRows) void ce_tiny_kernel(const T* __restrict_
   if (chunk < nfull) load_full(chunk, v);
 
   for (;;) {
-    const int64_t row0 = chunk * NT;
+    const int64_t row0 = chunk * ROWS;
     const bool full = chunk < nfull;
-    const int nrows = full ? NT : (int)(B - row0);
+    const int nrows = full ? ROWS : (int)(B - row0);
     // the chunk into LDS
     if (full) {
 #pragma unroll
@@ -466,16 +469,19 @@ __global__ __launch_bounds__(kTinyRows) void ce_tiny_kernel(const T* __restrict_
     const int64_t next = chunk + gridDim.x;
     if (next < nfull) load_full(next, v);
 
-    // one row per thread
-    if (tid < nrows) {
-      const int64_t row = row0 + tid;
+    // rows tid, tid + NT, ... of the chunk
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int lr = tid + j * NT;
+      if (lr >= nrows) break;
+      const int64_t row = row0 + lr;
       const RowTarget rt = row_target<OP>(targets, row, C, rs);
       const int t = rt.t;
       float f[CMAX];
       float m = kNegInf;
 #pragma unroll
       for (int c = 0; c < CMAX; ++c) {
-        f[c] = c < C ? LdsElem<T>::get(stage, tid * C + c) : kNegInf;
+        f[c] = c < C ? LdsElem<T>::get(stage, lr * C + c) : kNegInf;
         m = __builtin_fmaxf(m, f[c]);
       }
       const float cg = m * kLog2e;
@@ -490,11 +496,11 @@ __global__ __launch_bounds__(kTinyRows) void ce_tiny_kernel(const T* __restrict_
       const RowResult rr = row_finish<OP>(cg, sx, zt, rt.valid, rt.ignored, invB, gmul);
       store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
       if constexpr (GRAD) {
+        // the terms of the sum are the unnormalised softmax: scaled, they
+        // are the gradient (the target's term was left out of the sum)
 #pragma unroll
         for (int c = 0; c < CMAX; ++c)
-          if (c < C)
-            LdsElem<T>::put(stage, tid * C + c,
-                            c == t ? rr.gt : exp2_hw(__builtin_fmaf(f[c], kLog2e, -cg)) * rr.scale);
+          if (c < C) LdsElem<T>::put(stage, lr * C + c, c == t ? rr.gt : e[c] * rr.scale);
       }
     }
     if constexpr (GRAD) {
