@@ -210,6 +210,35 @@ def _check_cuda(*ts) -> None:
         raise ValueError("tensors must be on one device")
 
 
+def _empty_congruent(x):
+    """A new contiguous tensor of x's shape and dtype whose address has the
+    same offset modulo 16 bytes as x's (the kernels read and write matching
+    rows with the same 16-byte vector split, so the library requires it)."""
+    torch = _torch()
+    mis = x.data_ptr() % 16
+    if mis == 0:
+        return torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    es = x.element_size()
+    n = x.numel()
+    flat = torch.empty(n + 16 // es, dtype=x.dtype, device=x.device)
+    off = ((mis - flat.data_ptr() % 16) % 16) // es
+    return flat[off:off + n].view(x.shape)
+
+
+def _empty_rows_congruent(x, ld: int):
+    """As _empty_congruent for a [B, C] view with row stride ld: a [B, C]
+    view of a new buffer with the same row stride and offset modulo 16."""
+    torch = _torch()
+    B, C = x.shape
+    if ld == C:
+        return _empty_congruent(x)
+    es = x.element_size()
+    mis = x.data_ptr() % 16
+    flat = torch.empty(B * ld + 16 // es, dtype=x.dtype, device=x.device)
+    off = ((mis - flat.data_ptr() % 16) % 16) // es
+    return flat[off:off + B * ld].view(B, ld)[:, :C]
+
+
 def _check_fwd_args(logits, targets, grad, loss_rows):
     torch = _torch()
     _check_cuda(logits, targets, grad, loss_rows)
@@ -348,9 +377,10 @@ def fwd_grad_ex_into(logits, targets, grad, loss_rows, grad_scale=None, ignore_i
 
 def fwd_grad_ex(logits, targets, ignore_index=None, grad_scale=None, with_grad: bool = True):
     """Return ``(grad, loss_rows)`` (grad None when with_grad is False) for
-    row-strided logits, with the options of fwd_grad_ex_into."""
+    row-strided logits, with the options of fwd_grad_ex_into.  grad has the
+    logits' row stride."""
     torch = _torch()
-    grad = torch.empty(logits.shape, dtype=logits.dtype, device=logits.device) if with_grad else None
+    grad = _empty_rows_congruent(logits, _rows_view(logits, "logits")) if with_grad else None
     loss_rows = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device)
     fwd_grad_ex_into(logits, targets, grad, loss_rows, grad_scale, ignore_index)
     return grad, loss_rows
@@ -359,7 +389,7 @@ def fwd_grad_ex(logits, targets, ignore_index=None, grad_scale=None, with_grad: 
 def fwd_grad(logits, targets):
     """Return ``(grad, loss_rows)`` for ``[B, C]`` logits and int32 targets."""
     torch = _torch()
-    grad = torch.empty_like(logits)
+    grad = _empty_congruent(logits)
     loss_rows = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device)
     fwd_grad_into(logits, targets, grad, loss_rows)
     return grad, loss_rows
@@ -472,7 +502,7 @@ def softmax_fwd(x, with_lse: bool = False):
     """The row-wise softmax of ``[B, C]`` x; with ``with_lse`` also the rows'
     log-sum-exp (float32 [B])."""
     torch = _torch()
-    y = torch.empty_like(x)
+    y = _empty_congruent(x)
     lse = torch.empty(x.shape[0], dtype=torch.float32, device=x.device) if with_lse else None
     softmax_fwd_into(x, y, lse)
     return (y, lse) if with_lse else y
@@ -493,8 +523,13 @@ def softmax_bwd_into(y, dy, dx) -> None:
 
 
 def softmax_bwd(y, dy):
-    torch = _torch()
-    dx = torch.empty_like(y)
+    """dx for y and dy; dy is first copied to an address congruent to y's
+    modulo 16 bytes if it is not (the library requires it)."""
+    if (dy.data_ptr() - y.data_ptr()) % 16:
+        t = _empty_congruent(y)
+        t.copy_(dy)
+        dy = t
+    dx = _empty_congruent(y)
     softmax_bwd_into(y, dy, dx)
     return dx
 
@@ -582,7 +617,7 @@ def shard_grad_into(logits, targets, col0: int, C_total: int, records, grad, los
 
 def shard_grad(logits, targets, col0: int, C_total: int, records, with_loss: bool = False):
     torch = _torch()
-    grad = torch.empty_like(logits)
+    grad = _empty_congruent(logits)
     lr = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device) if with_loss else None
     shard_grad_into(logits, targets, col0, C_total, records, grad, lr)
     return (grad, lr) if with_loss else grad

@@ -341,3 +341,46 @@ def test_fwd_grad_ex_validation():
         assert fex(z=Z, g=Z, ldz=128256, ldg=128256, C=128256, dtype=1) == PATH
     finally:
         ce.force_path(prev)
+
+
+C_CLIENT = r"""
+#include "ce.h"
+#include <stdio.h>
+/* A plain C client: every call below fails validation (or is host-only),
+   so nothing reaches a device. */
+int main(void) {
+  if (ce_fwd_grad(0, 0, 8, 10, CE_F32, 0, 0, 0) != CE_ERR_NULL) return 1;
+  if (ce_softmax_fwd(0, 8, 10, CE_F16, 0, 0, 0) != CE_ERR_NULL) return 2;
+  if (ce_softmax_bwd(0, 0, 8, 10, CE_BF16, 0, 0) != CE_ERR_NULL) return 3;
+  if (ce_shard_grad(0, 0, 8, 10, 0, 10, CE_F32, 0, 1, 0, 0, 0, 0) != CE_ERR_NULL) return 4;
+  if (ce_fwd_workspace_bytes(CE_NO_IGNORE) != 0 || ce_fwd_workspace_bytes(-100) != 4) return 5;
+  if (ce_reduce_workspace_bytes(16384) != 0) return 6;
+  if (ce_select_path(128256, CE_BF16) != 4) return 7;
+  printf("%s\n", ce_version());
+  return 0;
+}
+"""
+
+
+@pytest.mark.parametrize("compiler,std", [("gcc", "-std=c99"), ("g++", "-std=c++11")])
+def test_header_builds_a_plain_client(tmp_path, compiler, std):
+    """include/ce.h compiles as strict C99 (and as C++11) with every warning
+    an error, and a client links against the library and runs."""
+    import shutil
+    import subprocess
+    cc = shutil.which(compiler)
+    if cc is None:
+        pytest.skip(f"{compiler} not available")
+    src = tmp_path / ("client.c" if compiler == "gcc" else "client.cpp")
+    src.write_text(C_CLIENT)
+    libdir = os.path.dirname(ce._LIB_PATH)
+    exe = tmp_path / "client"
+    lang = ["-x", "c++"] if compiler == "g++" else []
+    res = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror",
+                          f"-I{os.path.join(ROOT, 'include')}", *lang, str(src), "-x", "none",
+                          f"-L{libdir}", "-lce_mi355x", f"-Wl,-rpath,{libdir}", "-o", str(exe)],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, (run.returncode, run.stderr[-2000:])
+    assert "gfx950" in run.stdout
