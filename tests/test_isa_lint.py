@@ -113,8 +113,10 @@ def _kernel_meta(asm: str) -> dict[str, dict[str, int]]:
 def test_kernels_present(device_asm):
     meta = _kernel_meta(device_asm)
     names = " ".join(meta)
-    for k in ("ce_short_kernel", "ce_row_kernel", "ce_row_lds_kernel", "ce_reduce_kernel",
-              "ce_part_kernel"):
+    for k in ("ce_short_kernel", "ce_tiny_kernel", "ce_row_kernel", "ce_row_lds_kernel",
+              "ce_reduce_kernel", "ce_part_kernel", "ce_shard_grad_kernel", "ce_scale_kernel",
+              "ce_count_kept_kernel", "sm_bwd_short_kernel", "sm_bwd_row_kernel",
+              "sm_bwd_part_kernel"):
         assert k in names, k
 
 
@@ -139,9 +141,12 @@ def test_1024_thread_kernels_fit_registers(device_asm):
 
 
 def test_part_kernels_fit_two_per_cu(device_asm):
+    """The row-part kernels of the loss and softmax (ce_part_kernel) and of
+    the softmax backward (sm_bwd_part_kernel) run two 1024-thread
+    workgroups per CU: at most 64 VGPRs and half the LDS each."""
     meta = _kernel_meta(device_asm)
-    parts = {k: v for k, v in meta.items() if "ce_part_kernel" in k}
-    assert parts
+    parts = {k: v for k, v in meta.items() if "ce_part_kernel" in k or "sm_bwd_part_kernel" in k}
+    assert any("sm_bwd_part_kernel" in k for k in parts)
     for k, v in parts.items():
         assert v["next_free_vgpr"] <= 64, (k, v["next_free_vgpr"])
         assert v.get("group_segment_fixed_size", 0) <= 80 * 1024, k
