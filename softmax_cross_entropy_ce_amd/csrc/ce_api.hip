@@ -154,6 +154,7 @@ template <typename T, int OP, bool GRAD>
 int launch_tiny(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g, float* l,
                 hipStream_t st) {
   if (C <= 8) return launch_tiny_w<T, 8, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 12) return launch_tiny_w<T, 12, OP, GRAD>(z, t, B, C, rs, g, l, st);
   if (C <= 16) return launch_tiny_w<T, 16, OP, GRAD>(z, t, B, C, rs, g, l, st);
   if constexpr (sizeof(T) == 2) return launch_tiny_w<T, 32, OP, GRAD>(z, t, B, C, rs, g, l, st);
   return CE_ERR_PATH;

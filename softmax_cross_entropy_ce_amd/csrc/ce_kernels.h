@@ -383,9 +383,11 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
 // multiple of 16), so the workgroup reads it with whole 16-byte loads into
 // LDS; each thread reduces R rows from LDS without any cross-lane step and
 // writes their gradients back into LDS, and the chunk leaves with whole
-// 16-byte stores.  The workgroups are persistent; the next chunk's loads
-// are issued before this chunk's stores.  The last, partial chunk of a call
-// is moved one element per thread instead.
+// 16-byte stores.  The workgroups are persistent and keep the loads of the
+// next two chunks in flight, in two register sets used in turn (each set
+// is refilled as soon as its chunk is in LDS, before this chunk's stores).
+// The last, partial chunk of a call is moved one element per thread
+// instead.
 // ===========================================================================
 constexpr int kTinyThreads = 256;
 constexpr int kTinyRowBytes = 64;   // largest row
@@ -448,26 +450,24 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
 #pragma unroll
     for (int k = 0; k < K; ++k) v[k] = bload128<kPolicyStream>(r, voff, (uint32_t)k * NT * 16u);
   };
-  u32x4 v[K];
-  if (chunk < nfull) load_full(chunk, v);
-
-  for (;;) {
-    const int64_t row0 = chunk * ROWS;
-    const bool full = chunk < nfull;
+  const int64_t G = gridDim.x;
+  // one chunk: into LDS from its register set, which is then refilled with
+  // the chunk two steps ahead, so two chunks' loads are in flight while
+  // this one is reduced and stored
+  auto step = [&](u32x4 (&r)[K], int64_t ch) {
+    const int64_t row0 = ch * ROWS;
+    const bool full = ch < nfull;
     const int nrows = full ? ROWS : (int)(B - row0);
-    // the chunk into LDS
     if (full) {
 #pragma unroll
       for (int k = 0; k < K; ++k)
-        if (tid + k * NT < nvec) stage[tid + k * NT] = v[k];
+        if (tid + k * NT < nvec) stage[tid + k * NT] = r[k];
     } else {
       for (int i = tid; i < nrows * C; i += NT)
         LdsElem<T>::put(stage, i, E::load1(logits + row0 * C + i));
     }
     __syncthreads();
-    // the next chunk's loads, before this chunk's stores
-    const int64_t next = chunk + gridDim.x;
-    if (next < nfull) load_full(next, v);
+    if (ch + 2 * G < nfull) load_full(ch + 2 * G, r);
 
     // rows tid, tid + NT, ... of the chunk
 #pragma unroll
@@ -506,18 +506,28 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
     if constexpr (GRAD) {
       __syncthreads();
       if (full) {
-        const rsrc_t r = make_rsrc(grad + row0 * C, full_bytes);
+        const rsrc_t ro = make_rsrc(grad + row0 * C, full_bytes);
 #pragma unroll
         for (int k = 0; k < K; ++k)
           if (tid + k * NT < nvec)
-            bstore128<kPolicyStream>(stage[tid + k * NT], r, voff, (uint32_t)k * NT * 16u);
+            bstore128<kPolicyStream>(stage[tid + k * NT], ro, voff, (uint32_t)k * NT * 16u);
       } else {
         for (int i = tid; i < nrows * C; i += NT) E::store1(grad + row0 * C + i, LdsElem<T>::get(stage, i));
       }
     }
-    if (next >= nchunks) break;
-    chunk = next;
-    __syncthreads();  // the stage is refilled next
+    __syncthreads();  // the stage is refilled by the next step
+  };
+
+  u32x4 v[K], u[K];
+  if (chunk < nfull) load_full(chunk, v);
+  if (chunk + G < nfull) load_full(chunk + G, u);
+  for (;;) {
+    step(v, chunk);
+    chunk += G;
+    if (chunk >= nchunks) break;
+    step(u, chunk);
+    chunk += G;
+    if (chunk >= nchunks) break;
   }
 }
 
