@@ -92,7 +92,7 @@ def cpu_baseline(z, t, dtype: str, C: int, in_bytes: int, budget_s: float) -> di
     t0 = time.perf_counter()
     oracle_ce(z[:rows], t[:rows], dtype)
     dt1 = time.perf_counter() - t0
-    # the GPU machine grants 16 host cores to a run; never more than the host has
+    # at most 16 threads (the host share of a benchmark run), never more than the host has
     workers = max(1, min(16, os.cpu_count() or 1))
     step = max(1, min(rows, (1 << 22) // C))
     blocks = [(lo, min(rows, lo + step)) for lo in range(0, rows, step)]
