@@ -591,6 +591,11 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
   constexpr int NW = NT / 64;
   static_assert(NT % 64 == 0 && NW <= 16, "1 to 16 waves");
   __shared__ float red_c[2][NW], red_s[2][NW];
+  // fp32: keep the register slots' terms for the gradient in place of z
+  // (no extra registers).  Keeping them for 16-bit types needs a float copy
+  // of every slot; on 2048-wide bf16 rows it cost as much occupancy as it
+  // saved arithmetic, so they recompute.
+  constexpr bool kKeep = sizeof(T) == 4;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -637,11 +642,16 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
     const float xs = xe >= 0 ? E::load1(rp + xe) : kNegInf;
     const float zt = t >= 0 ? E::load1(rp + t) : 0.f;
 
-    // Phase B: online max / sum-exp over the thread's elements
+    // Phase B: online max / sum-exp over the thread's elements.  With kKeep,
+    // each register slot's terms 2^(z log2e - ck[k]) replace z (ck[k] the
+    // running max after slot k); the gradient is then one multiply per
+    // element.
     float c = kLowest, s = 0.f;
+    float ck[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int base = k * NT;
+      ck[k] = c;
       if (base >= nb) continue;  // uniform: no vector of this slot is in the row
       float f[VE];
       E::unpack(v[k], f);
@@ -655,7 +665,14 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
 #pragma unroll
         for (int i = 0; i < VE; ++i) f[i] = (i == tj) ? kNegInf : f[i];
       }
-      online_fold(c, s, vm, f);
+      if constexpr (GRAD && kKeep) {
+        float e[VE];
+        online_fold_e(c, s, vm, f, e);
+        ck[k] = c;
+        v[k] = as_u32(f32x4{e[0], e[1], e[2], e[3]});
+      } else {
+        online_fold(c, s, vm, f);
+      }
     }
     // path 3: the part of the row beyond the registers, streamed
     for (int vi = NT * NV + tid; vi < nb; vi += NT) {
@@ -724,10 +741,20 @@ __global__ __launch_bounds__(NT) void ce_row_kernel(const T* __restrict__ logits
       // the refill can reuse the slot's registers
       u32x4 packed;
       if (base < nb) {  // uniform
-        float f[VE], g[VE];
-        E::unpack(v[k], f);
+        float g[VE];
+        if constexpr (kKeep) {
+          const float factor = exp2_hw(ck[k] - cg) * rr.scale;
+          const f32x4 e = as_f32(v[k]);
+          g[0] = e.x * factor;
+          g[1] = e.y * factor;
+          g[2] = e.z * factor;
+          g[3] = e.w * factor;
+        } else {
+          float f[VE];
+          E::unpack(v[k], f);
 #pragma unroll
-        for (int i = 0; i < VE; ++i) g[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
+          for (int i = 0; i < VE; ++i) g[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
+        }
         if (k == own_k && own_thread) {
 #pragma unroll
           for (int i = 0; i < VE; ++i) g[i] = (i == tj) ? rr.gt : g[i];
