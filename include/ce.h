@@ -104,9 +104,9 @@ int ce_fwd_grad(const void* logits, const int32_t* targets, int64_t B, int64_t C
 /*
  * ce_fwd_loss - per-row losses only, for evaluation: the logits are read
  * once and only loss_out is written.  Arguments, layout and errors as
- * ce_fwd_grad without grad_out; runs on paths 1 to 3 (no row parts are
- * needed when nothing has to stay on chip for a gradient), so forcing path
- * 4 returns CE_ERR_PATH.
+ * ce_fwd_grad without grad_out; runs on paths 1, 2, 3 and 5 (no row parts
+ * are needed when nothing has to stay on chip for a gradient), so forcing
+ * path 4 returns CE_ERR_PATH.
  *
  * Defined by: rumus 0.1.1 cross_entropy.wgsl, pass 1 steps 1-3 (row max,
  * sum of exponentials, per-row loss scaled by 1/B).
@@ -302,7 +302,7 @@ int ce_softmax_bwd(const void* y, const void* dy, int64_t B, int64_t C, int dtyp
  *   targets      [B] int32, the global class indices.
  *   col0         the shard's first column, 0 <= col0 <= 2^31 - 1.
  *   records_out  [B][4] float32, 16-byte aligned, overwritten.
- * It reads the shard once on paths 1 to 3 (path 4 is refused).
+ * It reads the shard once on paths 1, 2, 3 and 5 (path 4 is refused).
  *
  * ce_shard_grad:
  *   logits, targets, B, C, col0, dtype as ce_shard_stats.
@@ -359,16 +359,24 @@ int ce_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
  *                   with the same code, so the bits do not depend on timing.
  *                   Rows of 16 KB to 384 KB (bf16 C up to 196608, fp32 C up
  *                   to 98304).
+ *   5 wave rows   - rows of up to 16 KB (automatic above 256 elements)
+ *                   whose starts, lengths and strides allow 16-, 8- or
+ *                   4-byte vectors (4-byte ones up to 8 KB; 16-bit rows of
+ *                   odd length have none): each 64-lane wavefront holds one
+ *                   to eight whole rows in registers, reduces them with DPP
+ *                   and writes their outputs from there.  Automatic
+ *                   selection runs other such rows on path 2.
  *
  * ce_select_path returns the path ce_fwd_grad takes for (C, dtype) with
- * 16-byte aligned base pointers, or a negative ce_status.
+ * contiguous rows and 16-byte aligned base pointers, or a negative
+ * ce_status.
  */
 int ce_select_path(int64_t C, int dtype);
 
 /*
  * Test hook: force every later call of ce_fwd_grad, ce_fwd_grad_scaled,
  * ce_fwd_loss, ce_softmax_fwd, ce_softmax_bwd and ce_shard_stats onto one
- * path (0 = automatic, 1 to 4 as above; path 3 is then run with a small
+ * path (0 = automatic, 1 to 5 as above; path 3 is then run with a small
  * on-chip part so that the streamed part is exercised).  A shape the forced path cannot take
  * returns CE_ERR_PATH.  Returns the previous setting, or CE_ERR_PATH for an
  * unknown value.  Process-wide; not meant for production use.

@@ -41,7 +41,7 @@ F32 = 0
 BF16 = 1
 F16 = 2
 NO_IGNORE = -(1 << 31)
-PATH_NAMES = {1: "short", 2: "resident", 3: "long", 4: "parts"}
+PATH_NAMES = {1: "short", 2: "resident", 3: "long", 4: "parts", 5: "wave"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libce_mi355x.so")

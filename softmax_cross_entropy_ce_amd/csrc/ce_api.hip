@@ -10,6 +10,7 @@
 #include "ce_shard.h"
 #include "softmax_bwd.h"
 #include "softmax_bwd_parts.h"
+#include "ce_wave_host.h"
 
 namespace {
 
@@ -19,6 +20,7 @@ constexpr int kPathShort = 1;
 constexpr int kPathResident = 2;
 constexpr int kPathLong = 3;
 constexpr int kPathParts = 4;
+constexpr int kPathWave = 5;
 
 // Polls of a row part for its partner's pair before it recomputes the pair
 // itself, and the optional device counter of such recomputations (test
@@ -67,8 +69,17 @@ constexpr int64_t kPartsTwo = 2 * 12 * 1024;
 
 int64_t body_vectors_max(int64_t C, int es) { return C / (16 / es); }
 
+// Vector bytes of path 5 for contiguous rows from 16-byte aligned bases:
+// the widest of 16, 8 and 4 that divides the row's bytes (0 if none).
+int wave_vb_contiguous(int64_t C, int es) {
+  for (int vb = 16; vb >= 4; vb /= 2)
+    if ((C * es) % vb == 0) return vb;
+  return 0;
+}
+
 int auto_path(int64_t C, int es) {
   if (C <= kShortMaxC) return kPathShort;
+  if (ce_wave::lane_bytes(C, es, wave_vb_contiguous(C, es)) != 0) return kPathWave;
   if (row_vectors(C, es) <= kResidentAutoMaxVectors) return kPathResident;
   if (body_vectors_max(C, es) <= kPartsTwo) return kPathParts;
   return kPathLong;
@@ -460,6 +471,18 @@ int fwd_impl(const FwdArgs& a, void* stream) {
   }
   const bool short_ok = short_span_ok(C, a.ldz, es) && (!a.grad || short_span_ok(C, ldg, es));
   if (path == kPathShort && !forced && !short_ok) path = kPathResident;
+  // path 5 loads vectors that every row start of both arrays is aligned to
+  // and that divide the row length and strides; rows it has no
+  // configuration for run on path 2
+  int wave_vb = 0;
+  if (path == kPathWave) {
+    const int64_t lens = C | a.ldz | (a.grad ? ldg : 0);
+    wave_vb = short_vw(lens, es, z, a.grad ? g : 0, 16 / es) * es;
+    if (ce_wave::lane_bytes(C, es, wave_vb) == 0) {
+      if (forced) return CE_ERR_PATH;
+      path = kPathResident;
+    }
+  }
   // a forced path that cannot take the shape is refused before any launch
   bool takes = false;
   switch (path) {
@@ -467,6 +490,7 @@ int fwd_impl(const FwdArgs& a, void* stream) {
     case kPathResident: resident_cfg(C, es, &takes); break;
     case kPathLong: takes = true; break;
     case kPathParts: takes = a.grad && body_vectors_max(C, es) <= kPartsTwo; break;
+    case kPathWave: takes = true; break;
     default: break;
   }
   if (!takes) return CE_ERR_PATH;
@@ -483,6 +507,9 @@ int fwd_impl(const FwdArgs& a, void* stream) {
     if (launched() != CE_OK) return CE_ERR_LAUNCH;
     rs.kept = kept;
   }
+  if (path == kPathWave)
+    return ce_wave::launch(a.dtype, a.op, a.grad != nullptr, wave_vb, a.logits, a.targets, B,
+                           (int)C, rs, a.grad, a.loss, st);
   switch (a.dtype) {
     case CE_F32:
       return fwd_dispatch<float>(a.op, path, a.logits, a.targets, B, C, a.grad, a.loss, rs, st);
@@ -621,6 +648,7 @@ bool bwd_parts_take(int64_t C, int es, bool in_place) {
 
 int bwd_auto_path(int64_t C, int es, bool in_place) {
   if (C <= kShortMaxC) return kPathShort;
+  if (ce_wave::bwd_lane_bytes(C, es, wave_vb_contiguous(C, es)) != 0) return kPathWave;
   if (row_vectors(C, es) <= (int64_t)kBwdLongCfg.nt * kBwdLongCfg.nv) return kPathResident;
   if (bwd_parts_take(C, es, in_place)) return kPathParts;
   return kPathLong;
@@ -764,8 +792,16 @@ int ce_softmax_bwd(const void* y, const void* dy, int64_t B, int64_t C, int dtyp
   if (o != b && overlaps(o, n, b, n)) return CE_ERR_ALIAS;
   const bool in_place = o == a || o == b;
   const int forced = g_force_path.load(std::memory_order_relaxed);
-  const int path = forced ? forced : bwd_auto_path(C, es, in_place);
+  int path = forced ? forced : bwd_auto_path(C, es, in_place);
   const hipStream_t st = as_stream(stream);
+  if (path == kPathWave) {
+    // y, dy and dx are congruent modulo 16 bytes: y's alignment serves all
+    const int vb = short_vw(C, es, a, 0, 16 / es) * es;
+    if (ce_wave::bwd_lane_bytes(C, es, vb) != 0)
+      return ce_wave::launch_bwd(dtype, vb, y, dy, B, (int)C, dx_out, st);
+    if (forced) return CE_ERR_PATH;
+    path = kPathResident;
+  }
   if (dtype == CE_F32)
     return softmax_bwd_typed<float>(path, (const float*)y, (const float*)dy, B, C, (float*)dx_out,
                                     in_place, st);
@@ -879,7 +915,7 @@ int ce_select_path(int64_t C, int dtype) {
 }
 
 int ce_debug_force_path(int path) {
-  if (path < 0 || path > 4) return CE_ERR_PATH;
+  if (path < 0 || path > kPathWave) return CE_ERR_PATH;
   return g_force_path.exchange(path);
 }
 

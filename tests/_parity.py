@@ -180,3 +180,49 @@ def full_parity(logits: np.ndarray, targets: np.ndarray, dtype: str, block_elems
     else:
         assert math.isnan(float(loss.item()))
     return worst
+
+
+# ---------------------------------------------------------------- path 5
+def wave_vector_bytes(es: int, lens, addrs=()) -> int:
+    """The vector bytes path 5 loads rows with: the widest of 16, 8 and 4
+    that divides every row length and stride (lens, in elements) and every
+    array base (addrs), else 0."""
+    for vb in (16, 8, 4):
+        if vb >= es and all(n % (vb // es) == 0 for n in lens) and all(a % vb == 0 for a in addrs):
+            return vb
+    return 0
+
+
+def wave_takes(C: int, es: int, lens=None, addrs=()) -> bool:
+    """Whether path 5 has a configuration for rows of C elements (rows of at
+    most 64 lanes x 256 bytes, 128 bytes with 4-byte vectors)."""
+    vb = wave_vector_bytes(es, lens if lens is not None else (C,), addrs)
+    if vb == 0:
+        return False
+    for lb in (16, 32, 64, 128, 256):
+        if lb >= vb and 64 * lb >= C * es:
+            return not (vb == 4 and lb > 128)
+    return False
+
+
+def path_takes(path: int, C: int, dtype: str) -> bool:
+    """Whether a forced path takes contiguous rows of C elements from
+    16-byte aligned arrays (short: C <= 256; resident: at most 16384
+    16-byte vectors; parts: an aligned body of at most 24576 vectors;
+    wave: wave_takes)."""
+    es = 4 if dtype == "f32" else 2
+    if path == 1:
+        return C <= 256
+    if path == 2:
+        return (C * es + 15) // 16 + 1 <= 16384
+    if path == 4:
+        return C // (16 // es) <= 24576
+    if path == 5:
+        return wave_takes(C, es)
+    return True
+
+
+def wave_bwd_takes(C: int, es: int, addrs=()) -> bool:
+    """Whether path 5's softmax backward takes contiguous rows of C elements
+    (as wave_takes, rows of at most 8 KB)."""
+    return C * es <= 8192 and wave_takes(C, es, (C,), addrs)

@@ -119,19 +119,29 @@ def test_reduce_loss_validation():
 
 @pytest.mark.parametrize("name,C,dtype,path", [
     ("tiny", 10, 0, 1),
-    ("classifier", 1000, 0, 2),
+    ("classifier", 1000, 0, 5),
     ("skinny", 10, 0, 1),
     ("lmhead50k", 50257, 0, 4),
     ("lmhead128k", 128256, 1, 4),
     ("beyond-registers-bf16", 200_000, 1, 3),
     ("beyond-registers-f32", 100_000, 0, 3),
     ("short-limit", 256, 0, 1),
-    ("just-over-short", 257, 1, 2),
-    # 16-byte vectors per row (body + head/tail) up to 1024 stay resident
-    ("resident-limit-f32", 4080, 0, 2),
-    ("over-resident-f32", 4096, 0, 4),
-    ("resident-limit-bf16", 8176, 1, 2),
-    ("over-resident-bf16", 8192, 1, 4),
+    ("just-over-short", 258, 1, 5),
+    # path 5: rows of at most 16 KB loaded in vectors of 4 to 16 bytes
+    # (4-byte vectors up to 8 KB); 16-bit rows of odd length have none
+    ("wave-limit-f32", 4096, 0, 5),
+    ("over-wave-f32", 4100, 0, 4),
+    ("wave-limit-bf16", 8192, 1, 5),
+    ("over-wave-bf16", 8200, 1, 4),
+    ("wave-4-byte-vectors", 2047, 0, 5),
+    ("over-wave-4-byte-vectors", 2049, 0, 2),
+    ("odd-bf16", 257, 1, 2),
+    # other rows of up to 1024 16-byte vectors (body + head/tail) stay
+    # resident
+    ("resident-limit-f32", 4079, 0, 2),
+    ("over-resident-f32", 4093, 0, 4),
+    ("resident-limit-bf16", 8175, 1, 2),
+    ("over-resident-bf16", 8185, 1, 4),
     # two parts of 12 x 1024 vectors: aligned body of at most 24576 vectors
     ("parts-limit-bf16", 196_608, 1, 4),
     ("over-parts-bf16", 196_616, 1, 3),
@@ -153,7 +163,7 @@ def test_force_path_round_trip():
         ce.force_path(prev)
     assert ce.select_path(10, 0) == 1
     assert ce.lib().ce_debug_force_path(7) == PATH
-    assert ce.lib().ce_debug_force_path(5) == PATH
+    assert ce.lib().ce_debug_force_path(6) == PATH
     prev = ce.force_path(4)
     try:
         assert ce.select_path(10, 1) == 4

@@ -23,13 +23,13 @@ import pytest
 import synth
 from oracle import ce_rows, ce_rows_ignore, reduce_loss, rne_f16_bits, softmax_bwd_rows, softmax_rows
 
-from _parity import (compare_block, compare_scalar, f16_order, full_parity, grad_to_host,
+from _parity import (path_takes, wave_bwd_takes, wave_takes, compare_block, compare_scalar, f16_order, full_parity, grad_to_host,
                      to_device, widen_rows)
 
 pytestmark = pytest.mark.gpu
 
-PATHS = [0, 1, 2, 3, 4]
-PATH_IDS = ["auto", "short", "resident", "long", "parts"]
+PATHS = [0, 1, 2, 3, 4, 5]
+PATH_IDS = ["auto", "short", "resident", "long", "parts", "wave"]
 
 
 def _ce():
@@ -50,14 +50,7 @@ def _es(dtype):
 
 
 def _legal(path, C, dtype):
-    es = _es(dtype)
-    if path == 1:
-        return C <= 256
-    if path == 2:
-        return (C * es + 15) // 16 + 1 <= 16384
-    if path == 4:
-        return C // (16 // es) <= 24576
-    return True
+    return path_takes(path, C, dtype)
 
 
 def _bits(x):
@@ -121,7 +114,7 @@ def test_f16_loss_only_in_place_and_scale(B, C):
     assert np.abs(f16_order(grad_to_host(g, "f16")) - f16_order(want)).max() <= 1
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3, 4], ids=PATH_IDS)
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("B,C", [(64, 200), (33, 4099), (9, 128256)])
 def test_f16_softmax(B, C, path):
     """Softmax forward (1 fp16 ulp) and backward (the backward's bar with an
@@ -141,8 +134,9 @@ def test_f16_softmax(B, C, path):
     assert np.abs(f16_order(yh) - f16_order(rne_f16_bits(y_ora))).max() <= 1
     tol = 2.0 ** -20 * (np.abs(z64.max(axis=1)) + math.log(C) + 1.0)
     assert (np.abs(lse.cpu().numpy() - lse_ora) <= tol).all()
-    if path == 4 or (path == 2 and (C * 2 + 15) // 16 + 1 > 8192):
-        return  # the backward has no row parts, and holds at most 8192 vectors on path 2
+    if path == 4 or (path == 5 and not wave_bwd_takes(C, 2)) or \
+            (path == 2 and (C * 2 + 15) // 16 + 1 > 8192):
+        return  # no backward for these rows on the forced path
     dy, _ = synth.make_inputs(B, C, "f16", 1.0, seed=C + 5)
     dyd, _ = to_device(dy, np.zeros(B, np.int32), "f16")
     dx = ce.softmax_bwd(y, dyd)
@@ -238,6 +232,9 @@ def test_row_stride_matches_oracle(B, C, dtype, padz, padg, path):
     _, td = to_device(z, t, dtype)
     zbuf, zv = _wide(z, dtype, padz)
     gbuf, gv = _wide(np.zeros_like(z), dtype, padg)
+    if path == 5 and not wave_takes(C, _es(dtype), (C, C + padz, C + padg),
+                                    (zv.data_ptr(), gv.data_ptr())):
+        pytest.skip("rows that path 5 does not take at these strides")
     zsnap = zbuf.clone()
     gsnap = gbuf.clone()
     lr = torch.empty(B, dtype=torch.float32, device=zv.device)

@@ -12,7 +12,7 @@ import pytest
 import synth
 from oracle import ce_rows, reduce_loss
 
-from _parity import compare_block, compare_scalar, grad_to_host, to_device, widen_rows
+from _parity import path_takes, compare_block, compare_scalar, grad_to_host, to_device, widen_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -46,14 +46,7 @@ def _reset_path():
 
 
 def _legal(path, C, dtype):
-    es = 4 if dtype == "f32" else 2
-    if path == 1:
-        return C <= 256
-    if path == 2:
-        return (C * es + 15) // 16 + 1 <= 16384
-    if path == 4:
-        return C // (16 // es) <= 24576
-    return True
+    return path_takes(path, C, dtype)
 
 
 def _two_part(C, dtype):
@@ -75,7 +68,7 @@ def _check_losses(lr_gpu, z, t, dtype, where, B=None):
     return l_ora
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3], ids=["auto", "short", "resident", "long"])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 5], ids=["auto", "short", "resident", "long", "wave"])
 @pytest.mark.parametrize("B,C,dtype,sigma", SHAPES, ids=IDS)
 def test_loss_only_matches_oracle(B, C, dtype, sigma, path):
     import torch
@@ -92,9 +85,10 @@ def test_loss_only_matches_oracle(B, C, dtype, sigma, path):
     compare_scalar(float(loss.item()), reduce_loss(l_ora), dtype, f"loss-only {B}x{C}")
     # where the loss alone runs the kernel configuration of the full call,
     # the same bits (path 2 picks wider workgroups for the loss alone
-    # between 1024 and 4096 vectors, and no LDS prefetch above 8192)
+    # between 1024 and 4096 vectors, and no LDS prefetch above 8192; path 5
+    # runs one kernel for both)
     nv = (C * (4 if dtype == "f32" else 2) + 15) // 16 + 1
-    if path in (1, 3) or (path == 2 and (nv <= 1024 or 4096 < nv <= 8192)):
+    if path in (1, 3, 5) or (path == 2 and (nv <= 1024 or 4096 < nv <= 8192)):
         _, lr_full = ce.fwd_grad(zd, td)
         torch.cuda.synchronize()
         assert torch.equal(lr.view(torch.int32), lr_full.view(torch.int32))
@@ -124,7 +118,7 @@ def test_loss_only_invalid_targets_and_spikes():
     _check_losses(lr[keep], z[keep], t[keep], "f32", "spikes", B=B)
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3, 4], ids=["auto", "short", "resident", "long", "parts"])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4, 5], ids=["auto", "short", "resident", "long", "parts", "wave"])
 @pytest.mark.parametrize("B,C,dtype,sigma", SHAPES, ids=IDS)
 def test_in_place_matches_oracle(B, C, dtype, sigma, path):
     import torch

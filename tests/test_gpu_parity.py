@@ -11,7 +11,7 @@ import pytest
 import synth
 from oracle import ce_rows, reduce_loss
 
-from _parity import (compare_block, compare_scalar, full_parity, grad_to_host, run_gpu,
+from _parity import (path_takes, compare_block, compare_scalar, full_parity, grad_to_host, run_gpu,
                      to_device, widen_rows)
 
 pytestmark = pytest.mark.gpu
@@ -69,22 +69,12 @@ SMALL = [
     (4, 98303, "f32", 3.0),
 ]
 
-PATHS = [0, 1, 2, 3, 4]
-PATH_IDS = ["auto", "short", "resident", "long", "parts"]
+PATHS = [0, 1, 2, 3, 4, 5]
+PATH_IDS = ["auto", "short", "resident", "long", "parts", "wave"]
 
 
 def _legal(path, C, dtype):
-    """Whether a forced path takes rows of C elements (short: C <= 256;
-    resident: at most 16384 16-byte vectors; parts: an aligned body of at
-    most 24576 vectors)."""
-    es = 4 if dtype == "f32" else 2
-    if path == 1:
-        return C <= 256
-    if path == 2:
-        return (C * es + 15) // 16 + 1 <= 16384
-    if path == 4:
-        return C // (16 // es) <= 24576
-    return True
+    return path_takes(path, C, dtype)
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)

@@ -23,7 +23,7 @@ import pytest
 import synth
 from oracle import ce_rows, rne_bf16_bits, widen_bf16
 
-from _parity import BF16_MAX_ULP, F32_GRAD_ATOL, bf16_order, grad_to_host, to_device, widen_rows
+from _parity import path_takes, BF16_MAX_ULP, F32_GRAD_ATOL, bf16_order, grad_to_host, to_device, widen_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +72,7 @@ def _check_scaled(g_host, z, t, dtype, s, where):
 
 
 @pytest.mark.parametrize("s", [0.5, 3.0, -1.25, 0.0])
-@pytest.mark.parametrize("path", [0, 2, 3, 4], ids=["auto", "resident", "long", "parts"])
+@pytest.mark.parametrize("path", [0, 2, 3, 4, 5], ids=["auto", "resident", "long", "parts", "wave"])
 @pytest.mark.parametrize("B,C,dtype,sigma", SHAPES, ids=IDS)
 def test_fused_scale_matches_oracle(B, C, dtype, sigma, path, s):
     import torch
@@ -81,6 +81,8 @@ def test_fused_scale_matches_oracle(B, C, dtype, sigma, path, s):
         pytest.skip("row too long for the row parts")
     if path == 2 and (C * (4 if dtype == "f32" else 2) + 15) // 16 + 1 > 16384:
         pytest.skip("row too long for the resident path")
+    if path == 5 and not path_takes(5, C, dtype):
+        pytest.skip("rows that path 5 does not take")
     ce.force_path(path)
     z, t = synth.make_inputs(B, C, dtype, sigma, seed=B + C + 7)
     zd, td = to_device(z, t, dtype)

@@ -25,7 +25,7 @@ import pytest
 import synth
 from oracle import reduce_loss, shard_partials
 
-from _parity import compare_block, compare_scalar, grad_to_host, to_device, widen_rows
+from _parity import wave_takes, compare_block, compare_scalar, grad_to_host, to_device, widen_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -95,7 +95,7 @@ def run_sharded(zd, td, edges, dtype, loss_from=0, grad_scale=None, in_place=Fal
     return recs, torch.cat(grads, dim=1), loss_rows
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3], ids=["auto", "short", "resident", "long"])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 5], ids=["auto", "short", "resident", "long", "wave"])
 @pytest.mark.parametrize("B,C,dtype,sigma,spike,edges", CASES, ids=IDS)
 def test_sharded_matches_whole_row_oracle(B, C, dtype, sigma, spike, edges, path):
     import torch
@@ -106,6 +106,8 @@ def test_sharded_matches_whole_row_oracle(B, C, dtype, sigma, spike, edges, path
     es = 4 if dtype == "f32" else 2
     if path == 2 and (int(widths.max()) * es + 15) // 16 + 1 > 16384:
         pytest.skip("a shard longer than the resident path takes")
+    if path == 5 and not all(wave_takes(int(w), es) for w in widths):
+        pytest.skip("a shard that path 5 does not take")
     ce.force_path(path)
     z, t = synth.make_inputs(B, C, dtype, sigma, spike=spike, seed=B + C + len(edges))
     if spike is not None:

@@ -27,7 +27,7 @@ import pytest
 import synth
 from oracle import ce_rows, rne_bf16_bits, softmax_bwd_rows, softmax_rows, widen_bf16
 
-from _parity import bf16_order, grad_to_host, widen_rows
+from _parity import path_takes, wave_bwd_takes, bf16_order, grad_to_host, widen_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -63,14 +63,7 @@ def _reset_path():
 
 
 def _legal(path, C, dtype):
-    es = 4 if dtype == "f32" else 2
-    if path == 1:
-        return C <= 256
-    if path == 2:
-        return (C * es + 15) // 16 + 1 <= 16384
-    if path == 4:
-        return C // (16 // es) <= 24576
-    return True
+    return path_takes(path, C, dtype)
 
 
 def _dev(a, dtype):
@@ -102,7 +95,7 @@ def check_lse(lse_host, z64, lse_ora, where):
     assert (err <= tol).all(), (where, float(err.max()), float(tol[np.argmax(err - tol)]))
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3, 4], ids=["auto", "short", "resident", "long", "parts"])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4, 5], ids=["auto", "short", "resident", "long", "parts", "wave"])
 @pytest.mark.parametrize("B,C,dtype,sigma,spike", FWD_SHAPES, ids=FWD_IDS)
 def test_softmax_fwd_matches_oracle(B, C, dtype, sigma, spike, path):
     import torch
@@ -125,7 +118,7 @@ def test_softmax_fwd_matches_oracle(B, C, dtype, sigma, spike, path):
     assert torch.equal(_bits(y2), _bits(y))
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3, 4], ids=["auto", "short", "resident", "long", "parts"])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4, 5], ids=["auto", "short", "resident", "long", "parts", "wave"])
 @pytest.mark.parametrize("B,C,dtype", [(64, 200, "bf16"), (33, 4099, "f32"), (9, 50257, "f32"),
                                        (6, 128256, "bf16"), (3, 200_000, "bf16")])
 def test_softmax_fwd_in_place(B, C, dtype, path):
@@ -223,6 +216,12 @@ BWD_SHAPES = [
     (20, 50257, "f32"),
     (9, 128256, "bf16"),
     (3, 200_000, "bf16"),
+    # path 5: attention-shaped rows, 8- and 4-byte vectors, 8 KB rows
+    (77, 2048, "bf16"),
+    (45, 300, "bf16"),
+    (31, 1002, "bf16"),
+    (19, 2047, "f32"),
+    (11, 4096, "bf16"),
 ]
 BWD_IDS = [f"{b}x{c}-{d}" for b, c, d in BWD_SHAPES]
 
@@ -235,6 +234,8 @@ def _bwd_legal(path, C, dtype, in_place=False):
         return (C * es + 15) // 16 + 1 <= 8192
     if path == 4:
         return not in_place and 128 <= C // (16 // es) <= 16384
+    if path == 5:
+        return wave_bwd_takes(C, es)
     return path in (0, 3)
 
 
@@ -260,7 +261,7 @@ def check_dx(dx_host, y64, dy64, dtype, where):
     return float((err / np.maximum(tol, 1e-300)).max())
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3, 4], ids=["auto", "short", "resident", "long", "parts"])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4, 5], ids=["auto", "short", "resident", "long", "parts", "wave"])
 @pytest.mark.parametrize("B,C,dtype", BWD_SHAPES, ids=BWD_IDS)
 def test_softmax_bwd_matches_oracle(B, C, dtype, path):
     import torch
@@ -277,7 +278,7 @@ def test_softmax_bwd_matches_oracle(B, C, dtype, path):
     print(f"[softmax] bwd {B}x{C} {dtype} p{path}: worst error / bar {r:.3g}", flush=True)
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3, 4], ids=["auto", "short", "resident", "long", "parts"])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4, 5], ids=["auto", "short", "resident", "long", "parts", "wave"])
 @pytest.mark.parametrize("B,C,dtype", [(64, 200, "f32"), (40, 50257, "f32"), (9, 128256, "bf16")])
 def test_softmax_bwd_chain_to_cross_entropy(B, C, dtype, path):
     """The softmax of logits (from the oracle; a quarter of the rows with a
@@ -313,7 +314,7 @@ def test_softmax_bwd_chain_to_cross_entropy(B, C, dtype, path):
         assert np.abs(got[keep] - g[keep]).max() <= 1e-6
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3, 4], ids=["auto", "short", "resident", "long", "parts"])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4, 5], ids=["auto", "short", "resident", "long", "parts", "wave"])
 @pytest.mark.parametrize("B,C,dtype", [(64, 200, "bf16"), (33, 4099, "f32"), (9, 128256, "bf16")])
 def test_softmax_bwd_in_place(B, C, dtype, path):
     """dx == dy and dx == y give the bits of the out-of-place call on the

@@ -82,13 +82,19 @@ def device_asm(tmp_path_factory):
         hipcc = B.hipcc()
     except RuntimeError:
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("isa") / "ce.s"
+    work = tmp_path_factory.mktemp("isa")
     flags = [f for f in B.HIP_FLAGS if f not in ("-shared", "-fPIC")]
-    cmd = [hipcc, *flags, "--cuda-device-only", "-S", f"-I{B.INCLUDE}", f"-I{B.CSRC}",
-           *[os.path.join(B.CSRC, s) for s in B.SOURCES], "-o", str(out)]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    assert res.returncode == 0, res.stderr[-4000:]
-    return out.read_text()
+    procs = []
+    for src in B.SOURCES:
+        out = work / (os.path.splitext(src)[0] + ".s")
+        cmd = [hipcc, *flags, "--cuda-device-only", "-S", f"-I{B.INCLUDE}", f"-I{B.CSRC}",
+               os.path.join(B.CSRC, src), "-o", str(out)]
+        procs.append((out, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                             stderr=subprocess.STDOUT, text=True)))
+    for out, proc in procs:
+        log = proc.communicate()[0]
+        assert proc.returncode == 0, log[-4000:]
+    return "\n".join(out.read_text() for out, _ in procs)
 
 
 def _kernel_meta(asm: str) -> dict[str, dict[str, int]]:
@@ -116,7 +122,7 @@ def test_kernels_present(device_asm):
     for k in ("ce_short_kernel", "ce_tiny_kernel", "ce_row_kernel", "ce_row_lds_kernel",
               "ce_reduce_kernel", "ce_part_kernel", "ce_shard_grad_kernel", "ce_scale_kernel",
               "ce_count_kept_kernel", "sm_bwd_short_kernel", "sm_bwd_row_kernel",
-              "sm_bwd_part_kernel"):
+              "sm_bwd_part_kernel", "ce_wave_kernel"):
         assert k in names, k
 
 
