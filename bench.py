@@ -16,6 +16,7 @@ sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
     python bench.py --mode copy --copy-mib 1024   # plain device copy, for counter calibration
+    python bench.py --mode sweep                  # rates across row lengths, against a copy
 """
 
 from __future__ import annotations
@@ -387,6 +388,51 @@ def run_copy(args) -> None:
                       "GBps": round(2 * n / dt / 1e9, 1), "ms": round(dt * 1e3, 4)}), flush=True)
 
 
+SWEEP_C = (64, 256, 300, 512, 1000, 2048, 3000, 4096, 8192, 12000, 16032, 32000, 50257, 65536,
+           128256, 200000)
+
+
+def run_sweep(args) -> None:
+    """Rates across row lengths: for each dtype and C, rows filling 1 GiB of
+    logits; ce_stream_copy of the logits' bytes into the gradient buffer
+    (the achievable rate), ce_fwd_grad, ce_fwd_loss, the softmax forward and
+    backward, each the median of HIP-event times over 30 calls after 40.
+    One JSON line per shape; rates in GB/s of the bytes each call must move
+    (copy and fwd_grad 2 arrays, the loss 1, softmax forward 2, backward 3)."""
+    import torch
+    import softmax_cross_entropy_ce_amd as ce
+    stream = torch.cuda.current_stream()
+    for dt in ("bf16", "f32"):
+        tdt = torch.float32 if dt == "f32" else torch.bfloat16
+        es = 4 if dt == "f32" else 2
+        for C in SWEEP_C:
+            B = max(16, (1 << 30) // (C * es) // 16 * 16)
+            gen = torch.Generator(device="cuda:0").manual_seed(C)
+            z = (torch.randn(B, C, device="cuda:0", generator=gen) * 3).to(tdt)
+            t = torch.randint(0, C, (B,), device="cuda:0", dtype=torch.int32, generator=gen)
+            g, lr = torch.empty_like(z), torch.empty(B, device="cuda:0")
+            dy = torch.randn(B, C, device="cuda:0", generator=gen).to(tdt)
+            dx = torch.empty_like(z)
+            n = B * C * es
+            src, dst = z.view(-1).view(torch.uint8), g.view(-1).view(torch.uint8)
+
+            def rate(fn, arrays):
+                ms = _event_median_ms(fn, stream, 30, warm=40)
+                return {"us": round(ms * 1e3, 1), "GBps": round(arrays * n / (ms * 1e-3) / 1e9, 1)}
+
+            rec = {"mode": "sweep", "dtype": dt, "C": C, "B": B,
+                   "path": ce.PATH_NAMES[ce.select_path(C, ce.F32 if dt == "f32" else ce.BF16)],
+                   "copy": rate(lambda: ce.stream_copy(src, dst), 2),
+                   "fwd_grad": rate(lambda: ce.fwd_grad_into(z, t, g, lr), 2),
+                   "fwd_loss": rate(lambda: ce.fwd_loss_into(z, t, lr), 1),
+                   "softmax_fwd": rate(lambda: ce.softmax_fwd_into(z, g, lr), 2),
+                   "softmax_bwd": rate(lambda: ce.softmax_bwd_into(g, dy, dx), 3)}
+            rec["fwd_grad_pct_of_copy"] = round(100 * rec["fwd_grad"]["GBps"] / rec["copy"]["GBps"], 1)
+            print(json.dumps(rec), flush=True)
+            del z, t, g, lr, dy, dx, src, dst
+            torch.cuda.empty_cache()
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -399,7 +445,7 @@ def main() -> None:
     ap.add_argument("--workload", default="lmhead128k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["ce", "copy"], default="ce")
+    ap.add_argument("--mode", choices=["ce", "copy", "sweep"], default="ce")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
 
@@ -410,6 +456,9 @@ def main() -> None:
         sys.exit(2)
     if args.mode == "copy":
         run_copy(args)
+        return
+    if args.mode == "sweep":
+        run_sweep(args)
         return
 
     import numpy as np

@@ -47,10 +47,15 @@ constexpr RowCfg kLongCfg = {1024, 16};     // automatic path 3
 constexpr RowCfg kLongTestCfg = {256, 1};   // forced path 3: small on-chip part
 
 constexpr int kShortMaxC = 256;
-// Automatic path 2 takes rows of up to this many 16-byte vectors (the
-// configurations up to 256 threads x 4); longer rows go to path 4 while
-// their aligned body fits its largest configuration, then to path 3.
-constexpr int64_t kResidentAutoMaxVectors = 1024;
+// Automatic selection (measured on rows filling 1 GiB): path 5 takes rows
+// of up to 8 KB of 16-bit elements or 4 KB of float32 (above that the
+// one-part, 256-thread configuration of path 4 moves more bytes per second;
+// float32 rows reach it sooner, their gradient needing no second exp).
+// Rows path 5 has no configuration for stay on path 2 up to that size;
+// longer rows go to path 4 while their aligned body fits its largest
+// configuration, then to path 3.
+constexpr int64_t kWaveAutoMaxBytes16 = 8192;
+constexpr int64_t kWaveAutoMaxBytes32 = 4096;
 
 int elem_size(int dtype) { return dtype == CE_F32 ? 4 : 2; }
 
@@ -58,10 +63,13 @@ int elem_size(int dtype) { return dtype == CE_F32 ? 4 : 2; }
 int64_t row_vectors(int64_t C, int es) { return (C * es + 15) / 16 + 1; }
 
 // Path 4 configurations by the largest body a row can have, floor(C /
-// elements per vector) 16-byte vectors: one part of 4 register slots; one
-// part of 8 register and 2 LDS slots; two parts of 8 register slots; two
-// parts of 8 register and 4 LDS slots (a slot is 1024 vectors, and a part
-// of a two-part row is half the body rounded up to 8 vectors).
+// elements per vector) 16-byte vectors: one part of 256 threads and 8
+// register slots (eight such workgroups fit a CU); one part of 1024
+// threads and 4 register slots; one part of 8 register and 2 LDS slots;
+// two parts of 8 register slots; two parts of 8 register and 4 LDS slots
+// (a 1024-thread slot is 1024 vectors, and a part of a two-part row is half
+// the body rounded up to 8 vectors).
+constexpr int64_t kPartsOneQuarter = 8 * 256;
 constexpr int64_t kPartsOneSmall = 4 * 1024;
 constexpr int64_t kPartsOne = 10 * 1024;
 constexpr int64_t kPartsTwoRegs = 2 * 8 * 1024;
@@ -79,8 +87,10 @@ int wave_vb_contiguous(int64_t C, int es) {
 
 int auto_path(int64_t C, int es) {
   if (C <= kShortMaxC) return kPathShort;
-  if (ce_wave::lane_bytes(C, es, wave_vb_contiguous(C, es)) != 0) return kPathWave;
-  if (row_vectors(C, es) <= kResidentAutoMaxVectors) return kPathResident;
+  if (C * es <= (es == 4 ? kWaveAutoMaxBytes32 : kWaveAutoMaxBytes16)) {
+    return ce_wave::lane_bytes(C, es, wave_vb_contiguous(C, es)) != 0 ? kPathWave
+                                                                       : kPathResident;
+  }
   if (body_vectors_max(C, es) <= kPartsTwo) return kPathParts;
   return kPathLong;
 }
@@ -304,6 +314,7 @@ template <typename T, int OP>
 int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g, float* l,
                  hipStream_t st) {
   const int64_t nb = body_vectors_max(C, sizeof(T));
+  if (nb <= kPartsOneQuarter) return launch_parts_cfg<T, 1, 256, 8, 0, 0, OP>(z, t, B, C, rs, g, l, st);
   if (nb <= kPartsOneSmall) return launch_parts_cfg<T, 1, 1024, 4, 0, 0, OP>(z, t, B, C, rs, g, l, st);
   if (nb <= kPartsOne) return launch_parts_cfg<T, 1, 1024, 8, 2, 0, OP>(z, t, B, C, rs, g, l, st);
   if (nb <= kPartsTwoRegs) return launch_parts_cfg<T, 2, 1024, 8, 0, 0, OP>(z, t, B, C, rs, g, l, st);
@@ -348,8 +359,13 @@ int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g
 // in place.
 bool two_part_row(int64_t C, int es) { return body_vectors_max(C, es) > kPartsOne; }
 
+// Rows that do not run as row parts (the loss alone, two-part rows in
+// place): path 5 where it has a configuration for contiguous rows (it falls
+// back to path 2 at launch when the arrays do not allow it), else path 2 or
+// 3 by length.
 int path_without_parts(int64_t C, int es) {
   if (C <= kShortMaxC) return kPathShort;
+  if (ce_wave::lane_bytes(C, es, wave_vb_contiguous(C, es)) != 0) return kPathWave;
   return row_vectors(C, es) <= (int64_t)kLongCfg.nt * kLongCfg.nv ? kPathResident : kPathLong;
 }
 

@@ -127,21 +127,17 @@ def test_reduce_loss_validation():
     ("beyond-registers-f32", 100_000, 0, 3),
     ("short-limit", 256, 0, 1),
     ("just-over-short", 258, 1, 5),
-    # path 5: rows of at most 16 KB loaded in vectors of 4 to 16 bytes
-    # (4-byte vectors up to 8 KB); 16-bit rows of odd length have none
-    ("wave-limit-f32", 4096, 0, 5),
-    ("over-wave-f32", 4100, 0, 4),
-    ("wave-limit-bf16", 8192, 1, 5),
-    ("over-wave-bf16", 8200, 1, 4),
-    ("wave-4-byte-vectors", 2047, 0, 5),
-    ("over-wave-4-byte-vectors", 2049, 0, 2),
+    # path 5 up to 8 KB of 16-bit or 4 KB of fp32 elements, where the row
+    # allows 16-, 8- or 4-byte vectors (16-bit rows of odd length do not);
+    # those stay on path 2, longer rows go to the row parts
+    ("wave-limit-f32", 1024, 0, 5),
+    ("over-wave-f32", 1025, 0, 4),
+    ("wave-limit-bf16", 4096, 1, 5),
+    ("over-wave-bf16", 4100, 1, 4),
+    ("wave-4-byte-vectors", 1023, 0, 5),
     ("odd-bf16", 257, 1, 2),
-    # other rows of up to 1024 16-byte vectors (body + head/tail) stay
-    # resident
-    ("resident-limit-f32", 4079, 0, 2),
-    ("over-resident-f32", 4093, 0, 4),
-    ("resident-limit-bf16", 8175, 1, 2),
-    ("over-resident-bf16", 8185, 1, 4),
+    ("odd-bf16-limit", 4095, 1, 2),
+    ("over-odd-bf16-limit", 4097, 1, 4),
     # two parts of 12 x 1024 vectors: aligned body of at most 24576 vectors
     ("parts-limit-bf16", 196_608, 1, 4),
     ("over-parts-bf16", 196_616, 1, 3),
