@@ -80,13 +80,15 @@ typedef enum {
  *   B, C      1 <= B <= 2^31 - 1, 1 <= C <= CE_MAX_C.
  *   dtype     CE_F32 or CE_BF16.
  *   grad_out  [B, C] dtype, fully overwritten with (softmax - onehot) / B.
- *             Contents on entry are ignored; on path 4 with two parts per
- *             row the call also uses 16 bytes of each part's own gradient
- *             as a mailbox before the gradient is written there.
+ *             Contents on entry are ignored; on path 4 with two or four
+ *             parts per row the call also uses 16 bytes per other part of
+ *             each part's own gradient as a mailbox before the gradient is
+ *             written there.
  *             grad_out == logits computes the gradient in place of the
  *             logits (every kernel holds a row's data on chip, or reads it
  *             again from the same thread, before writing it; rows that
- *             path 4 would cut into two parts run on path 2 or 3 instead).
+ *             path 4 would cut into several parts run on path 2 or 3
+ *             instead).
  *             Any other overlap with logits is refused.  Must be aligned
  *             to the element size, and (grad_out - logits) must be a
  *             multiple of 16 bytes (true for any two allocations from the
@@ -233,10 +235,11 @@ int ce_reduce_loss(const float* loss_rows, int64_t B, float* loss_scalar_out,
  *   x        [B, C] dtype, row-major, contiguous, element-aligned.
  *   B, C     as ce_fwd_grad.
  *   y_out    [B, C] dtype, overwritten; y_out == x computes the softmax in
- *            place (rows that path 4 would cut into two parts then run on
- *            path 2 or 3).  Other overlaps are refused; (y_out - x) must be
- *            a multiple of 16 bytes.  Path 4's two-part rows use 16 bytes of
- *            each part of y_out as a mailbox before writing it.
+ *            place (rows that path 4 would cut into several parts then run
+ *            on path 2 or 3).  Other overlaps are refused; (y_out - x) must
+ *            be a multiple of 16 bytes.  Path 4's rows of several parts use
+ *            16 bytes per other part of each part of y_out as a mailbox
+ *            before writing it.
  *   lse_out  [B] float32 (4-byte aligned), or NULL for none.
  * Returns CE_OK or a negative ce_status.
  */
@@ -349,16 +352,18 @@ int ce_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
  *   3 long rows   - as 2, with the part of the row beyond the on-chip
  *                   capacity streamed with online max/sum-exp partials and
  *                   re-read for the gradient;
- *   4 row parts   - the row cut into one or two parts of up to 12 x 16 KB,
- *                   one 1024-thread workgroup each and two per CU; each part
- *                   is read once into registers and LDS and reduced to an
- *                   online max/sum-exp pair, the parts trade their pairs
- *                   and combine them in a fixed order, and each writes its
- *                   share of the gradient from on chip.  A part that does
- *                   not receive its partner's pair in time recomputes it
- *                   with the same code, so the bits do not depend on timing.
- *                   Rows of 16 KB to 384 KB (bf16 C up to 196608, fp32 C up
- *                   to 98304).
+ *   4 row parts   - the row cut into one, two or four parts (one
+ *                   256-thread workgroup for rows up to 32 KB, else
+ *                   1024-thread workgroups of up to 12 x 16 KB, two per
+ *                   CU); each part is read once into registers and LDS and
+ *                   reduced to an online max/sum-exp pair, the parts trade
+ *                   their pairs and combine them in a fixed order, and each
+ *                   writes its share of the gradient from on chip.  A part
+ *                   that does not receive a partner's pair in time
+ *                   recomputes it with the same code, so the bits do not
+ *                   depend on timing.  Automatic above 8 KB of 16-bit or
+ *                   4 KB of fp32 elements, up to 768 KB (16-bit C up to
+ *                   393216) or 512 KB (fp32 C up to 131072).
  *   5 wave rows   - rows of up to 16 KB (automatic above 256 elements)
  *                   whose starts, lengths and strides allow 16-, 8- or
  *                   4-byte vectors (4-byte ones up to 8 KB; 16-bit rows of
@@ -384,18 +389,19 @@ int ce_select_path(int64_t C, int dtype);
 int ce_debug_force_path(int path);
 
 /*
- * Test hook: how many times a path-4 row part polls for its partner's
- * max/sum-exp pair before it recomputes the pair itself (default 64; 0 makes
- * every part of a two-part row recompute).  Results are bitwise the same
- * for any value.  Returns the previous value, or CE_ERR_PATH if polls < 0.
+ * Test hook: how many times a path-4 row part polls for its partners'
+ * max/sum-exp pairs before it recomputes the missing ones itself (default
+ * 64; 0 makes every part of a row of several parts recompute every other
+ * part's pair), and likewise for the parts of the softmax backward.
+ * Results are bitwise the same for any value.  Returns the previous value, or CE_ERR_PATH if polls < 0.
  * Process-wide; not meant for production use.
  */
 int ce_debug_part_polls(int polls);
 
 /*
- * Test hook: a DEVICE pointer to a uint32 that every path-4 part which
- * recomputes its partner's pair increments atomically (NULL turns the count
- * off, the default).  The caller owns the counter and must keep it alive
+ * Test hook: a DEVICE pointer to a uint32 to which every path-4 part adds
+ * the number of partner pairs it recomputed, atomically (NULL turns the
+ * count off, the default).  The caller owns the counter and must keep it alive
  * while calls that were made with it set can still run.  Returns CE_OK.
  * Process-wide; not meant for production use.
  */

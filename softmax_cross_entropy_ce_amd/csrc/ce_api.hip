@@ -66,14 +66,22 @@ int64_t row_vectors(int64_t C, int es) { return (C * es + 15) / 16 + 1; }
 // elements per vector) 16-byte vectors: one part of 256 threads and 8
 // register slots (eight such workgroups fit a CU); one part of 1024
 // threads and 4 register slots; one part of 8 register and 2 LDS slots;
-// two parts of 8 register slots; two parts of 8 register and 4 LDS slots
-// (a 1024-thread slot is 1024 vectors, and a part of a two-part row is half
+// two parts of 8 register slots; two parts of 8 register and 4 LDS slots;
+// four parts of 8 register slots; four parts of 8 register and 4 LDS slots
+// (a 1024-thread slot is 1024 vectors, and a part of a P-part row is 1/P of
 // the body rounded up to 8 vectors).
 constexpr int64_t kPartsOneQuarter = 8 * 256;
 constexpr int64_t kPartsOneSmall = 4 * 1024;
 constexpr int64_t kPartsOne = 10 * 1024;
 constexpr int64_t kPartsTwoRegs = 2 * 8 * 1024;
 constexpr int64_t kPartsTwo = 2 * 12 * 1024;
+constexpr int64_t kPartsFourRegs = 4 * 8 * 1024;
+constexpr int64_t kPartsFour = 4 * 12 * 1024;
+// The largest body path 4 takes: four parts with LDS slots for 16-bit
+// types; for float32 (whose register slots keep the terms of the sum) that
+// configuration would exceed 64 VGPRs, so it stops at four register-only
+// parts.
+int64_t parts_max(int es) { return es == 4 ? kPartsFourRegs : kPartsFour; }
 
 int64_t body_vectors_max(int64_t C, int es) { return C / (16 / es); }
 
@@ -91,7 +99,7 @@ int auto_path(int64_t C, int es) {
     return ce_wave::lane_bytes(C, es, wave_vb_contiguous(C, es)) != 0 ? kPathWave
                                                                        : kPathResident;
   }
-  if (body_vectors_max(C, es) <= kPartsTwo) return kPathParts;
+  if (body_vectors_max(C, es) <= parts_max(es)) return kPathParts;
   return kPathLong;
 }
 
@@ -319,6 +327,10 @@ int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs
   if (nb <= kPartsOne) return launch_parts_cfg<T, 1, 1024, 8, 2, 0, OP>(z, t, B, C, rs, g, l, st);
   if (nb <= kPartsTwoRegs) return launch_parts_cfg<T, 2, 1024, 8, 0, 0, OP>(z, t, B, C, rs, g, l, st);
   if (nb <= kPartsTwo) return launch_parts_cfg<T, 2, 1024, 8, 4, 0, OP>(z, t, B, C, rs, g, l, st);
+  if (nb <= kPartsFourRegs) return launch_parts_cfg<T, 4, 1024, 8, 0, 0, OP>(z, t, B, C, rs, g, l, st);
+  if constexpr (sizeof(T) == 2) {
+    if (nb <= kPartsFour) return launch_parts_cfg<T, 4, 1024, 8, 4, 0, OP>(z, t, B, C, rs, g, l, st);
+  }
   return CE_ERR_PATH;
 }
 
@@ -354,13 +366,13 @@ int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g
   }
 }
 
-// Rows that path 4 cuts into two parts: their parts may read each other's
-// logits (the recompute) and keep mailboxes in grad, so they cannot run
-// in place.
-bool two_part_row(int64_t C, int es) { return body_vectors_max(C, es) > kPartsOne; }
+// Rows that path 4 cuts into two or four parts: their parts may read each
+// other's logits (the recompute) and keep mailboxes in grad, so they cannot
+// run in place.
+bool multi_part_row(int64_t C, int es) { return body_vectors_max(C, es) > kPartsOne; }
 
-// Rows that do not run as row parts (the loss alone, two-part rows in
-// place): path 5 where it has a configuration for contiguous rows (it falls
+// Rows that do not run as row parts (the loss alone, rows of several parts
+// in place): path 5 where it has a configuration for contiguous rows (it falls
 // back to path 2 at launch when the arrays do not allow it), else path 2 or
 // 3 by length.
 int path_without_parts(int64_t C, int es) {
@@ -480,7 +492,7 @@ int fwd_impl(const FwdArgs& a, void* stream) {
   const int forced = g_force_path.load(std::memory_order_relaxed);
   int path = forced ? forced : auto_path(C, es);
   if (!a.grad || in_place) {
-    if (path == kPathParts && (!a.grad || two_part_row(C, es))) {
+    if (path == kPathParts && (!a.grad || multi_part_row(C, es))) {
       if (forced) return CE_ERR_PATH;
       path = path_without_parts(C, es);
     }
@@ -505,7 +517,7 @@ int fwd_impl(const FwdArgs& a, void* stream) {
     case kPathShort: takes = short_ok; break;
     case kPathResident: resident_cfg(C, es, &takes); break;
     case kPathLong: takes = true; break;
-    case kPathParts: takes = a.grad && body_vectors_max(C, es) <= kPartsTwo; break;
+    case kPathParts: takes = a.grad && body_vectors_max(C, es) <= parts_max(es); break;
     case kPathWave: takes = true; break;
     default: break;
   }

@@ -15,12 +15,13 @@
 // its share of the gradient from on-chip data.  The combine is the
 // online-softmax merge of (max, sum) partials.
 //
-// Trading pairs between workgroups.  Each part has a mailbox: two 64-bit
-// words at the start of its own last body vector in grad.  Its partner
-// publishes (c, s) there, one value per word in the low half with kMailTag
-// in the high half; the owner polls it, and its own gradient store
-// overwrites it only after the poll has ended.
-//  - First thing, the owner sets both words to kMailEmpty.  Its own later
+// Trading pairs between workgroups.  Each part has a mailbox in grad: a
+// pair of 64-bit words for each other part of its row, at the start of its
+// own last P - 1 body vectors.  Every other part publishes its (c, s) into
+// its pair of words, one value per word in the low half with kMailTag in
+// the high half; the owner polls them, and its own gradient store
+// overwrites them only after the poll has ended.
+//  - First thing, the owner sets its words to kMailEmpty.  Its own later
 //    polls are ordered after that store, so whatever grad held before the
 //    call can never be read as a partner's value.
 //  - The partner publishes with compare-and-swap from kMailEmpty, so a
@@ -44,7 +45,8 @@
 //
 // Workgroup g runs on XCD g % 8 (round-robin dispatch); the parts of a row
 // are given workgroups g, g + 8, ..., so they share an XCD and start next to
-// each other in its dispatch order.
+// each other in its dispatch order.  Rows are cut into one, two or four
+// parts.
 #pragma once
 
 #include "ce_kernels.h"
@@ -119,13 +121,13 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   constexpr int NLS = NL + (NXW > 0 ? 1 : 0);  // LDS slots, the last maybe partial
   constexpr int NS = NR + NLS;                 // slots per part
   constexpr int NX = NXW * 64;                 // threads with a vector in the partial slot
-  static_assert(P == 1 || P == 2, "one or two parts per row");
+  static_assert(P >= 1 && P <= 4, "one to four parts per row");
   static_assert(NT % 64 == 0 && NW >= 1 && NW <= 16, "1 to 16 waves");
   static_assert(NXW >= 0 && NXW < NW, "partial LDS slot smaller than a slot");
   __shared__ u32x4 stage[NL * NT + NX > 0 ? NL * NT + NX : 1];
   __shared__ float red_c[NW], red_s[NW];
-  __shared__ float mail_c, mail_s;
-  __shared__ int mail_ok;
+  __shared__ float mail_c[P], mail_s[P];
+  __shared__ int mail_ok[P];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t voff = (uint32_t)tid * 16u;
@@ -155,16 +157,22 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rin, (lds_ptr_t)&stage[NL * NT + wv * 64], 16, voff,
                                                (uint32_t)(NR + NL) * NT * 16u, 0, kPolicyStream);
   }
-  // Empty this part's mailbox (two-part rows) before anything can be
-  // published into it.
-  uint64_t* const mine =
-      P == 2 ? reinterpret_cast<uint64_t*>(gp + geo.h + (int64_t)(own.v0 + own.len - 1) * VE)
-             : nullptr;
+  // Empty this part's mailbox (rows of several parts) before anything can
+  // be published into it: P - 1 pairs of words, one pair per other part,
+  // at the start of the part's last P - 1 body vectors.
+  constexpr int NM = P - 1;
+  auto mailbox = [&](const PartRange& pr) {
+    return reinterpret_cast<uint64_t*>(gp + geo.h + (int64_t)(pr.v0 + pr.len - NM) * VE);
+  };
+  // the pair of words that part `from` publishes into part `to`'s mailbox
+  auto mail_index = [](int from, int to) { return 2 * (from < to ? from : from - 1); };
+  uint64_t* const mine = P > 1 ? mailbox(own) : nullptr;
   constexpr uint64_t kEmptyWord = (uint64_t)kMailEmpty << 32;
-  if constexpr (P == 2) {
+  if constexpr (P > 1) {
     if (tid == 0) {
-      __hip_atomic_store(&mine[0], kEmptyWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&mine[1], kEmptyWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int w = 0; w < 2 * NM; ++w)
+        __hip_atomic_store(&mine[w], kEmptyWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   // LDS slot p of this thread (the partial slot holds nothing for threads
@@ -278,47 +286,61 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   float c_own, s_own;
   wg_pair<NW>(c, s, red_c, red_s, lane, wv, c_own, s_own);
 
-  float c_oth = kLowest, s_oth = 0.f;
-  if constexpr (P == 2) {
-    const int q = 1 - part;
+  // The pairs of all parts, in LDS: this part's own, the others' as
+  // received, or recomputed where a partner's did not arrive in time.
+  float cg = c_own, sx = s_own;
+  if constexpr (P > 1) {
     if (tid == 0) {
-      const PartRange pq = part_range(geo.nb, P, q);
-      uint64_t* theirs = reinterpret_cast<uint64_t*>(gp + geo.h + (int64_t)(pq.v0 + pq.len - 1) * VE);
+      mail_c[part] = c_own;
+      mail_s[part] = s_own;
       const uint64_t tag = (uint64_t)kMailTag << 32;
       const uint64_t w0 = tag | __builtin_bit_cast(uint32_t, c_own);
       const uint64_t w1 = tag | __builtin_bit_cast(uint32_t, s_own);
       // The publishes are issued without waiting for their results, so the
       // next poll follows them at once.
       auto publish = [&] {
-        uint64_t e0 = kEmptyWord, e1 = kEmptyWord;
-        __hip_atomic_compare_exchange_strong(&theirs[0], &e0, w0, __ATOMIC_RELAXED,
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_compare_exchange_strong(&theirs[1], &e1, w1, __ATOMIC_RELAXED,
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+          if (q == part) continue;
+          uint64_t* m = mailbox(part_range(geo.nb, P, q)) + mail_index(part, q);
+          uint64_t e0 = kEmptyWord, e1 = kEmptyWord;
+          __hip_atomic_compare_exchange_strong(&m[0], &e0, w0, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_compare_exchange_strong(&m[1], &e1, w1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        }
       };
       publish();
-      int ok = 0;
-      uint64_t a = 0, b = 0;
-      for (int it = 0; it < spin; ++it) {
-        a = __hip_atomic_load(&mine[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        b = __hip_atomic_load(&mine[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((uint32_t)(a >> 32) == kMailTag && (uint32_t)(b >> 32) == kMailTag) {
-          ok = 1;
-          break;
+      // a bit per part whose pair is here; received pairs go straight to LDS
+      constexpr unsigned kAll = (1u << P) - 1u;
+      unsigned got = 1u << part;
+      for (int it = 0; it < spin && got != kAll; ++it) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+          if ((got >> q) & 1u) continue;
+          const uint64_t* m = mine + mail_index(q, part);
+          const uint64_t a = __hip_atomic_load(&m[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t b = __hip_atomic_load(&m[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((uint32_t)(a >> 32) == kMailTag && (uint32_t)(b >> 32) == kMailTag) {
+            mail_c[q] = __builtin_bit_cast(float, (uint32_t)a);
+            mail_s[q] = __builtin_bit_cast(float, (uint32_t)b);
+            got |= 1u << q;
+          }
         }
-        publish();
-        __builtin_amdgcn_s_sleep(8);
+        if (got != kAll) {
+          publish();
+          __builtin_amdgcn_s_sleep(8);
+        }
       }
-      mail_c = __builtin_bit_cast(float, (uint32_t)a);
-      mail_s = __builtin_bit_cast(float, (uint32_t)b);
-      mail_ok = ok;
-      if (!ok && fallbacks != nullptr) atomicAdd(fallbacks, 1u);
+#pragma unroll
+      for (int q = 0; q < P; ++q) mail_ok[q] = (int)((got >> q) & 1u);
+      if (got != kAll && fallbacks != nullptr)
+        atomicAdd(fallbacks, (uint32_t)(P - __builtin_popcount(got)));
     }
     __syncthreads();
-    if (mail_ok) {
-      c_oth = mail_c;
-      s_oth = mail_s;
-    } else {
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      if (q == part || mail_ok[q]) continue;  // uniform (LDS, after the barrier)
       // Recompute part q's pair: the same slots, fold order, edges and
       // workgroup reduction as part q runs itself.
       const PartRange pq = part_range(geo.nb, P, q);
@@ -334,21 +356,21 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       const float xqv = bload_elem<T>(rrow, (uint32_t)(xq >= 0 ? xq : C) * ES);
       fold_edge(xq, xq >= 0 ? xqv : kNegInf, cq, sq);
       fold_target_max(pq, zt, cq, sq);
-      wg_pair<NW>(cq, sq, red_c, red_s, lane, wv, c_oth, s_oth);
+      float cr, sr;
+      wg_pair<NW>(cq, sq, red_c, red_s, lane, wv, cr, sr);
+      if (tid == 0) {
+        mail_c[q] = cr;
+        mail_s[q] = sr;
+      }
+      __syncthreads();  // the pair is in LDS; red_c / red_s may be used again
     }
-  }
-
-  // Combine the parts' pairs in part order.
-  float cg, sx;
-  if constexpr (P == 1) {
-    cg = c_own;
-    sx = s_own;
-  } else {
-    const float c0 = part == 0 ? c_own : c_oth, s0 = part == 0 ? s_own : s_oth;
-    const float c1 = part == 0 ? c_oth : c_own, s1 = part == 0 ? s_oth : s_own;
-    cg = __builtin_fmaxf(c0, c1);
-    sx = s0 * exp2_hw(c0 - cg);
-    sx = sx + s1 * exp2_hw(c1 - cg);
+    // Combine the parts' pairs in part order.
+    cg = mail_c[0];
+#pragma unroll
+    for (int q = 1; q < P; ++q) cg = __builtin_fmaxf(cg, mail_c[q]);
+    sx = mail_s[0] * exp2_hw(mail_c[0] - cg);
+#pragma unroll
+    for (int q = 1; q < P; ++q) sx = sx + mail_s[q] * exp2_hw(mail_c[q] - cg);
   }
   const RowResult rr = row_finish<OP>(cg, sx, zt, valid, rt.ignored, invB, gmul);
   if (part == 0 && tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);

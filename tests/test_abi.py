@@ -123,8 +123,8 @@ def test_reduce_loss_validation():
     ("skinny", 10, 0, 1),
     ("lmhead50k", 50257, 0, 4),
     ("lmhead128k", 128256, 1, 4),
-    ("beyond-registers-bf16", 200_000, 1, 3),
-    ("beyond-registers-f32", 100_000, 0, 3),
+    ("four-parts-bf16", 200_000, 1, 4),
+    ("four-parts-f32", 100_000, 0, 4),
     ("short-limit", 256, 0, 1),
     ("just-over-short", 258, 1, 5),
     # path 5 up to 8 KB of 16-bit or 4 KB of fp32 elements, where the row
@@ -138,11 +138,12 @@ def test_reduce_loss_validation():
     ("odd-bf16", 257, 1, 2),
     ("odd-bf16-limit", 4095, 1, 2),
     ("over-odd-bf16-limit", 4097, 1, 4),
-    # two parts of 12 x 1024 vectors: aligned body of at most 24576 vectors
-    ("parts-limit-bf16", 196_608, 1, 4),
-    ("over-parts-bf16", 196_616, 1, 3),
-    ("parts-limit-f32", 98_304, 0, 4),
-    ("over-parts-f32", 98_308, 0, 3),
+    # four parts of 12 x 1024 vectors (16-bit) or 8 x 1024 (fp32): aligned
+    # body of at most 49152 or 32768 vectors
+    ("parts-limit-bf16", 393_216, 1, 4),
+    ("over-parts-bf16", 393_224, 1, 3),
+    ("parts-limit-f32", 131_072, 0, 4),
+    ("over-parts-f32", 131_076, 0, 3),
 ])
 def test_path_selection(name, C, dtype, path):
     assert ce.select_path(C, dtype) == path

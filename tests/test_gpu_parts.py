@@ -4,7 +4,8 @@ workgroups of a row.
 A part that does not receive its partner's pair in time recomputes it with
 the same code.  These tests force that (zero polls) and check that the
 outputs are bitwise those of the exchange, that the device counter sees
-every part of every two-part row recompute, that mailbox-like bit patterns
+every part of every row of two or four parts recompute every other part's
+pair, that mailbox-like bit patterns
 left in grad_out on entry change nothing, that the forced fallback matches
 the oracle, and that calls on two streams at once do not disturb each
 other."""
@@ -21,12 +22,18 @@ from _parity import full_parity, to_device
 pytestmark = pytest.mark.gpu
 
 # (B, C, dtype, sigma): two parts per row (aligned, 2-byte aligned, 4-byte
-# aligned fp32, every slot filled) and one one-part shape as a control.
+# aligned fp32, every slot filled), four parts per row (registers only,
+# fp32 at its largest, 2-byte aligned with LDS slots, every slot filled)
+# and one one-part shape as a control.
 SHAPES = [
     (64, 128256, "bf16", 4.0),
     (9, 99999, "bf16", 4.0),
     (33, 50257, "f32", 3.0),
     (5, 196607, "bf16", 4.0),
+    (11, 256000, "bf16", 4.0),
+    (6, 131071, "f32", 3.0),
+    (5, 300001, "bf16", 4.0),
+    (3, 393216, "bf16", 4.0),
     (40, 40000, "f32", 3.0),
 ]
 IDS = [f"{b}x{c}-{d}" for b, c, d, _ in SHAPES]
@@ -51,8 +58,11 @@ def _reset_hooks():
     ce.force_path(prev_path)
 
 
-def _two_parts(C, dtype):
-    return C // (4 if dtype == "f32" else 8) > 10 * 1024
+def _parts(C, dtype):
+    """Parts per row: one up to an aligned body of 10240 vectors, two up to
+    24576, then four."""
+    nb = C // (4 if dtype == "f32" else 8)
+    return 1 if nb <= 10 * 1024 else 2 if nb <= 24 * 1024 else 4
 
 
 def _bits(x):
@@ -83,7 +93,8 @@ def test_fallback_is_bitwise_and_counted(B, C, dtype, sigma):
     n_forced = int(counter.item())
     print(f"[parts] {B}x{C} {dtype}: recomputed pairs {n_default} (64 polls), "
           f"{n_forced} (0 polls)", flush=True)
-    assert n_forced == (2 * B if _two_parts(C, dtype) else 0)
+    P = _parts(C, dtype)
+    assert n_forced == B * P * (P - 1)      # every part recomputes every other part's pair
     assert torch.equal(_bits(g1), _bits(g2))
     assert torch.equal(_bits(l1), _bits(l2))
 
@@ -109,7 +120,7 @@ def test_stale_grad_content_is_ignored(pattern):
     assert torch.equal(_bits(loss_rows), _bits(l_ref))
 
 
-@pytest.mark.parametrize("B,C,dtype,sigma", SHAPES[:4], ids=IDS[:4])
+@pytest.mark.parametrize("B,C,dtype,sigma", SHAPES[:-1], ids=IDS[:-1])
 def test_forced_fallback_matches_oracle(B, C, dtype, sigma):
     _ce().part_polls(0)
     z, t = synth.make_inputs(B, C, dtype, sigma, seed=3 * B + C)

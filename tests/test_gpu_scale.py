@@ -77,7 +77,7 @@ def _check_scaled(g_host, z, t, dtype, s, where):
 def test_fused_scale_matches_oracle(B, C, dtype, sigma, path, s):
     import torch
     ce = _ce()
-    if path == 4 and C // (16 // (4 if dtype == "f32" else 2)) > 24576:
+    if path == 4 and not path_takes(4, C, dtype):
         pytest.skip("row too long for the row parts")
     if path == 2 and (C * (4 if dtype == "f32" else 2) + 15) // 16 + 1 > 16384:
         pytest.skip("row too long for the resident path")
