@@ -725,13 +725,30 @@ template <typename T>
 int launch_shard_grad(const T* z, const int32_t* t, int64_t B, int64_t C, int64_t col0,
                       int64_t Ctot, const float* recs, int nshards, ce::RowArgs rs, T* g,
                       float* l, hipStream_t st) {
+  const ce::f32x4* r4 = reinterpret_cast<const ce::f32x4*>(recs);
+  if (C <= ce::kShardTinyC) {
+    const int64_t blocks = (B + 255) / 256;
+    if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
+    hipLaunchKernelGGL(ce::ce_shard_grad_tiny_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       z, t, B, (int)C, col0, Ctot, r4, nshards, rs, g, l);
+    return launched();
+  }
+  // units of one wave for rows of at most 512 vectors, else of four waves
   const int64_t nb = body_vectors_max(C, sizeof(T));
-  const int64_t chunks = nb > 0 ? (nb + ce::kShardChunk - 1) / ce::kShardChunk : 1;
-  const int64_t blocks = (B * chunks + ce::kShardUnits - 1) / ce::kShardUnits;
+  const bool wave_units = nb <= 64 * ce::kShardSlots;
+  const int64_t chunk = (wave_units ? 64 : 256) * ce::kShardSlots;
+  const int64_t units = ce::kShardThreads / (wave_units ? 64 : 256);
+  const int64_t chunks = nb > 0 ? (nb + chunk - 1) / chunk : 1;
+  const int64_t blocks = (B * chunks + units - 1) / units;
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL(ce::ce_shard_grad_kernel<T>, dim3((unsigned)blocks),
-                     dim3(ce::kShardThreads), 0, st, z, t, B, (int)C, col0, Ctot,
-                     reinterpret_cast<const ce::f32x4*>(recs), nshards, rs, g, l, (int)chunks);
+  if (wave_units)
+    hipLaunchKernelGGL((ce::ce_shard_grad_kernel<T, 64>), dim3((unsigned)blocks),
+                       dim3(ce::kShardThreads), 0, st, z, t, B, (int)C, col0, Ctot, r4, nshards, rs,
+                       g, l, (int)chunks);
+  else
+    hipLaunchKernelGGL((ce::ce_shard_grad_kernel<T, 256>), dim3((unsigned)blocks),
+                       dim3(ce::kShardThreads), 0, st, z, t, B, (int)C, col0, Ctot, r4, nshards, rs,
+                       g, l, (int)chunks);
   return launched();
 }
 

@@ -23,45 +23,66 @@
 
 namespace ce {
 
-// A unit of work is 256 threads x 8 slots: 2048 body vectors of one row.
-// Four units share a 1024-thread workgroup (large workgroups stream
-// faster than small ones on this GPU); they need no barrier, since every
-// thread combines the records of its row by itself.
-constexpr int kShardThreads = 1024;
-constexpr int kShardUnit = 256;                             // threads per unit
-constexpr int kShardUnits = kShardThreads / kShardUnit;     // units per workgroup
-constexpr int kShardSlots = 8;                              // 16-byte vectors per thread
-constexpr int kShardChunk = kShardUnit * kShardSlots;       // body vectors per unit
+// The combine of a row's records, shard by shard in shard order: every
+// kernel below runs exactly this code, so all shards of a row, whichever
+// kernel serves them, compute the same bits.
+struct ShardRow {
+  float c, sx, zt, own;
+};
+__device__ __forceinline__ ShardRow shard_combine(const f32x4* __restrict__ recs, int nshards,
+                                                  int64_t B, int64_t row) {
+  ShardRow r{kLowest, 0.f, 0.f, 0.f};
+  for (int k = 0; k < nshards; ++k) r.c = __builtin_fmaxf(r.c, recs[(int64_t)k * B + row].x);
+  for (int k = 0; k < nshards; ++k) {
+    const f32x4 q = recs[(int64_t)k * B + row];
+    r.sx = r.sx + q.y * exp2_hw(q.x - r.c);
+    r.zt = r.zt + q.z;
+    r.own = r.own + q.w;
+  }
+  return r;
+}
 
-// Unit u (= 4 * workgroup + threadIdx.x / 256) handles body vectors
-// [j * kShardChunk, (j + 1) * kShardChunk) of row u / chunks (j = u %
-// chunks), and chunk 0 also the row's elements before its first 16-byte
-// boundary and after its last; units past B * chunks do nothing.  recs
-// holds nshards x B records, shard-major.  A row whose target lies outside
-// [0, Ctot), or is held by other than exactly one shard's record, gets NaN
-// loss and gradient.
-template <typename T>
+// A unit of work is U threads x 8 slots: U * 8 body vectors of one row
+// (U = 256, or one wave for rows of at most 512 vectors).  1024 / U units
+// share a 1024-thread workgroup (large workgroups stream faster than small
+// ones on this GPU); they need no barrier, since every thread combines the
+// records of its row by itself.
+constexpr int kShardThreads = 1024;
+constexpr int kShardSlots = 8;                              // 16-byte vectors per thread
+constexpr int kShardTinyC = 16;                             // rows one thread handles
+
+// Unit u (= 1024/U * workgroup + threadIdx.x / U) handles body vectors
+// [j * U * 8, (j + 1) * U * 8) of row u / chunks (j = u % chunks), and
+// chunk 0 also the row's elements before its first 16-byte boundary and
+// after its last; units past B * chunks do nothing.  recs holds nshards x B
+// records, shard-major.  A row whose target lies outside [0, Ctot), or is
+// held by other than exactly one shard's record, gets NaN loss and
+// gradient.
+template <typename T, int U>
 __global__ __launch_bounds__(kShardThreads) void ce_shard_grad_kernel(
     const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B, int C,
     int64_t col0, int64_t Ctot, const f32x4* __restrict__ recs, int nshards, RowArgs rs,
     T* __restrict__ grad, float* __restrict__ loss_rows, int chunks) {
+  static_assert(U == 64 || U == 256, "a unit is one or four waves");
+  constexpr int kUnits = kShardThreads / U;
+  constexpr int kChunk = U * kShardSlots;
   using E = Elem<T>;
-  constexpr int VE = E::VE, NT = kShardUnit;
-  // wave-uniform (a unit is four whole waves): readfirstlane lets the
-  // compiler load the row's records and target with scalar loads
-  const int64_t unit = (int64_t)blockIdx.x * kShardUnits +
-                       __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kShardUnit));
+  constexpr int VE = E::VE, NT = U;
+  // wave-uniform (a unit is whole waves): readfirstlane lets the compiler
+  // load the row's records and target with scalar loads
+  const int64_t unit = (int64_t)blockIdx.x * kUnits +
+                       __builtin_amdgcn_readfirstlane((int)(threadIdx.x / U));
   const int64_t row = unit / chunks;
-  if (row >= B) return;  // whole waves: a unit is four waves
+  if (row >= B) return;  // whole waves
   const int chunk = (int)(unit % chunks);
-  const int tid = threadIdx.x % kShardUnit;
+  const int tid = threadIdx.x % U;
   const uint32_t voff = (uint32_t)tid * 16u;
 
   const T* rp = logits + row * rs.ldz;
   T* gp = grad + row * rs.ldg;
   const RowGeom geo = row_geom(rp, C);
-  const int v0 = chunk * kShardChunk;
-  const int nv = geo.nb - v0 < kShardChunk ? geo.nb - v0 : kShardChunk;
+  const int v0 = chunk * kChunk;
+  const int nv = geo.nb - v0 < kChunk ? geo.nb - v0 : kChunk;
   const uint32_t bytes = nv > 0 ? (uint32_t)nv * 16u : 0u;
   const rsrc_t rin = make_rsrc(rp + geo.h + (int64_t)v0 * VE, bytes);
   const rsrc_t rout = make_rsrc(gp + geo.h + (int64_t)v0 * VE, bytes);
@@ -78,19 +99,11 @@ __global__ __launch_bounds__(kShardThreads) void ce_shard_grad_kernel(
   }
   const float xs = xe >= 0 ? E::load1(rp + xe) : 0.f;
 
-  // combine the shards' records in shard order
-  float c = kLowest;
-  for (int k = 0; k < nshards; ++k) c = __builtin_fmaxf(c, recs[(int64_t)k * B + row].x);
-  float sx = 0.f, zt = 0.f, own = 0.f;
-  for (int k = 0; k < nshards; ++k) {
-    const f32x4 r = recs[(int64_t)k * B + row];
-    sx = sx + r.y * exp2_hw(r.x - c);
-    zt = zt + r.z;
-    own = own + r.w;
-  }
+  const ShardRow sr = shard_combine(recs, nshards, B, row);
+  const float c = sr.c;
   const int64_t tg = targets[row];
-  const bool valid = tg >= 0 && tg < Ctot && own == 1.f;
-  const RowResult rr = row_epilogue(c, sx, zt, valid, rs.invB, grad_mul(rs));
+  const bool valid = tg >= 0 && tg < Ctot && sr.own == 1.f;
+  const RowResult rr = row_epilogue(c, sr.sx, sr.zt, valid, rs.invB, grad_mul(rs));
   if (loss_rows != nullptr && chunk == 0 && tid == 0) loss_rows[row] = rr.loss;
 
   // the target's column in this shard, if it is here: body vector tvec
@@ -119,6 +132,33 @@ __global__ __launch_bounds__(kShardThreads) void ce_shard_grad_kernel(
   if (xe >= 0) {
     const float g = (xe == t) ? rr.gt : exp2_hw(__builtin_fmaf(xs, kLog2e, -c)) * rr.scale;
     E::store1(gp + xe, g);
+  }
+}
+
+// Shards of at most kShardTinyC columns (a vocabulary cut into more shards
+// than it has many columns): one thread per row, elements loaded and stored
+// one by one.  The records of a row then outweigh its elements, and a unit
+// of whole waves per row would leave almost every lane idle.
+template <typename T>
+__global__ __launch_bounds__(256) void ce_shard_grad_tiny_kernel(
+    const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B, int C,
+    int64_t col0, int64_t Ctot, const f32x4* __restrict__ recs, int nshards, RowArgs rs,
+    T* __restrict__ grad, float* __restrict__ loss_rows) {
+  using E = Elem<T>;
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= B) return;  // no barrier follows
+  const ShardRow sr = shard_combine(recs, nshards, B, row);
+  const int64_t tg = targets[row];
+  const bool valid = tg >= 0 && tg < Ctot && sr.own == 1.f;
+  const RowResult rr = row_epilogue(sr.c, sr.sx, sr.zt, valid, rs.invB, grad_mul(rs));
+  if (loss_rows != nullptr) loss_rows[row] = rr.loss;
+  const T* rp = logits + row * rs.ldz;
+  T* gp = grad + row * rs.ldg;
+  const int64_t tl = tg - col0;
+  for (int j = 0; j < C; ++j) {
+    const float x = E::load1(rp + j);
+    const float g = j == tl ? rr.gt : exp2_hw(__builtin_fmaf(x, kLog2e, -sr.c)) * rr.scale;
+    E::store1(gp + j, g);
   }
 }
 
