@@ -199,6 +199,38 @@ struct Elem<_Float16> {
   }
 };
 
+// Element `half` of a 32-bit word, widened: float32 is the word itself;
+// 16-bit types hold element 0 in the low half.  pack_word is the inverse
+// (each element rounded to nearest even).
+template <typename T>
+__device__ __forceinline__ float widen_half(unsigned d, int half);
+template <>
+__device__ __forceinline__ float widen_half<float>(unsigned d, int) {
+  return __builtin_bit_cast(float, d);
+}
+template <>
+__device__ __forceinline__ float widen_half<__bf16>(unsigned d, int half) {
+  return half ? bf16hi(d) : bf16lo(d);
+}
+template <>
+__device__ __forceinline__ float widen_half<_Float16>(unsigned d, int half) {
+  return half ? f16hi(d) : f16lo(d);
+}
+template <typename T>
+__device__ __forceinline__ unsigned pack_word(const float* g);
+template <>
+__device__ __forceinline__ unsigned pack_word<float>(const float* g) {
+  return __builtin_bit_cast(unsigned, g[0]);
+}
+template <>
+__device__ __forceinline__ unsigned pack_word<__bf16>(const float* g) {
+  return pack_bf16x2(g[0], g[1]);
+}
+template <>
+__device__ __forceinline__ unsigned pack_word<_Float16>(const float* g) {
+  return pack_f16x2(g[0], g[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane reductions.  DPP moves inside rows of 16 lanes (quad
 // permutations, half-row and row mirrors) are plain VALU operands; the step

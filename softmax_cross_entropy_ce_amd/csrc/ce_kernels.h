@@ -150,7 +150,7 @@ struct LdsElem<_Float16> {
 
 // CMAX: the row length rounded up to 8, 16 or 32 elements (at most 64
 // bytes), the width of each thread's per-row arrays.  R: rows per thread.
-template <typename T, int CMAX, int R, bool GRAD, int OP = kOpCE>
+template <typename T, int CMAX, int R, bool GRAD, int OP = kOpCE, bool PAD = false>
 __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restrict__ logits,
                                                                const int32_t* __restrict__ targets,
                                                                int64_t B, int C, RowArgs rs,
@@ -160,7 +160,16 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
   constexpr int ES = sizeof(T), NT = kTinyThreads, ROWS = NT * R;
   constexpr int K = (ROWS * CMAX * ES + 16 * NT - 1) / (16 * NT);  // 16-byte loads per thread
   static_assert(CMAX * ES <= kTinyRowBytes, "row width");
-  __shared__ u32x4 stage[NT * K];
+  // PAD: rows of whole 32-bit words (C * size a multiple of 4) sit in LDS at
+  // an odd stride of RS words, so that the threads of a wave, each reading
+  // its own row, hit different banks (at the row's own stride of 4, 8, 12
+  // or 16 words they would share a few).
+  constexpr int EPW = 4 / ES;                 // elements per word
+  constexpr int RDMAX = CMAX / EPW;           // words of the widest row
+  constexpr int STAGE = PAD ? (ROWS * (RDMAX | 1) + 3) / 4 : NT * K;
+  static_assert(!PAD || CMAX % EPW == 0, "whole words");
+  __shared__ u32x4 stage[STAGE];
+  unsigned* const sw = reinterpret_cast<unsigned*>(stage);
   const float invB = row_invB(rs), gmul = grad_mul(rs);
   const int tid = threadIdx.x;
   const uint32_t voff = (uint32_t)tid * 16u;
@@ -168,6 +177,29 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
   const int64_t nfull = B / ROWS;             // chunks of exactly ROWS rows
   const uint32_t full_bytes = (uint32_t)(ROWS * C * ES);
   const int nvec = (int)(full_bytes / 16);    // 16-byte vectors of a full chunk
+  // PAD: words per row (4, 8, 12 or 16: the host pads rows of a multiple of
+  // 16 bytes) and the padded stride; word d of a chunk is word d - RD * (d /
+  // RD) of row d / RD, with d / RD = high half of d * ceil(2^32 / RD),
+  // exact since d * (ceil(2^32 / RD) * RD - 2^32) < 2^32 for d < ROWS * RD
+  // <= 2^14
+  const int RD = PAD ? C / EPW : 1;
+  const int RS = RD | 1;
+  const uint32_t magic =
+      PAD ? (uint32_t)((0x100000000ull + (uint64_t)RD - 1u) / (uint64_t)RD) : 0u;
+  static_assert(ROWS * RDMAX <= (1 << 14), "exact word division");
+  auto word_slot = [&](int d) -> int {
+    const int row = (int)(((uint64_t)(uint32_t)d * magic) >> 32);
+    return row * RS + (d - row * RD);
+  };
+  // LDS index of element i of the chunk (rows of C elements)
+  auto elem_slot = [&](int i) -> int {
+    if constexpr (PAD) {
+      const int row = i / C;
+      return row * RS * EPW + (i - row * C);
+    } else {
+      return i;
+    }
+  };
   int64_t chunk = blockIdx.x;
   if (chunk >= nchunks) return;
 
@@ -186,11 +218,21 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
     const int nrows = full ? ROWS : (int)(B - row0);
     if (full) {
 #pragma unroll
-      for (int k = 0; k < K; ++k)
-        if (tid + k * NT < nvec) stage[tid + k * NT] = r[k];
+      for (int k = 0; k < K; ++k) {
+        const int gv = tid + k * NT;
+        if (gv >= nvec) continue;
+        if constexpr (PAD) {
+          sw[word_slot(4 * gv + 0)] = r[k].x;
+          sw[word_slot(4 * gv + 1)] = r[k].y;
+          sw[word_slot(4 * gv + 2)] = r[k].z;
+          sw[word_slot(4 * gv + 3)] = r[k].w;
+        } else {
+          stage[gv] = r[k];
+        }
+      }
     } else {
       for (int i = tid; i < nrows * C; i += NT)
-        LdsElem<T>::put(stage, i, E::load1(logits + row0 * C + i));
+        LdsElem<T>::put(stage, elem_slot(i), E::load1(logits + row0 * C + i));
     }
     __syncthreads();
     if (ch + 2 * G < nfull) load_full(ch + 2 * G, r);
@@ -205,11 +247,22 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
       const int t = rt.t;
       float f[CMAX];
       float m = kNegInf;
+      if constexpr (PAD) {
 #pragma unroll
-      for (int c = 0; c < CMAX; ++c) {
-        f[c] = c < C ? LdsElem<T>::get(stage, lr * C + c) : kNegInf;
-        m = __builtin_fmaxf(m, f[c]);
+        for (int k = 0; k < RDMAX; ++k) {
+          const unsigned w = k < RD ? sw[lr * RS + k] : 0u;
+#pragma unroll
+          for (int q = 0; q < EPW; ++q) {
+            const int c = k * EPW + q;
+            f[c] = c < C ? widen_half<T>(w, q) : kNegInf;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < CMAX; ++c) f[c] = c < C ? LdsElem<T>::get(stage, lr * C + c) : kNegInf;
       }
+#pragma unroll
+      for (int c = 0; c < CMAX; ++c) m = __builtin_fmaxf(m, f[c]);
       const float cg = m * kLog2e;
       float e[CMAX];
       float zt = 0.f;
@@ -224,9 +277,18 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
       if constexpr (GRAD) {
         // the terms of the sum are the unnormalised softmax: scaled, they
         // are the gradient (the target's term was left out of the sum)
+        float g[CMAX];
 #pragma unroll
-        for (int c = 0; c < CMAX; ++c)
-          if (c < C) LdsElem<T>::put(stage, lr * C + c, c == t ? rr.gt : e[c] * rr.scale);
+        for (int c = 0; c < CMAX; ++c) g[c] = c == t ? rr.gt : e[c] * rr.scale;
+        if constexpr (PAD) {
+#pragma unroll
+          for (int k = 0; k < RDMAX; ++k)
+            if (k < RD) sw[lr * RS + k] = pack_word<T>(&g[k * EPW]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < CMAX; ++c)
+            if (c < C) LdsElem<T>::put(stage, lr * C + c, g[c]);
+        }
       }
     }
     if constexpr (GRAD) {
@@ -234,11 +296,21 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
       if (full) {
         const rsrc_t ro = make_rsrc(grad + row0 * C, full_bytes);
 #pragma unroll
-        for (int k = 0; k < K; ++k)
-          if (tid + k * NT < nvec)
-            bstore128<kPolicyStream>(stage[tid + k * NT], ro, voff, (uint32_t)k * NT * 16u);
+        for (int k = 0; k < K; ++k) {
+          const int gv = tid + k * NT;
+          if (gv >= nvec) continue;
+          u32x4 w;
+          if constexpr (PAD) {
+            w = u32x4{sw[word_slot(4 * gv + 0)], sw[word_slot(4 * gv + 1)],
+                      sw[word_slot(4 * gv + 2)], sw[word_slot(4 * gv + 3)]};
+          } else {
+            w = stage[gv];
+          }
+          bstore128<kPolicyStream>(w, ro, voff, (uint32_t)k * NT * 16u);
+        }
       } else {
-        for (int i = tid; i < nrows * C; i += NT) E::store1(grad + row0 * C + i, LdsElem<T>::get(stage, i));
+        for (int i = tid; i < nrows * C; i += NT)
+          E::store1(grad + row0 * C + i, LdsElem<T>::get(stage, elem_slot(i)));
       }
     }
     __syncthreads();  // the stage is refilled by the next step

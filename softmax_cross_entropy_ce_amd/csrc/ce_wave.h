@@ -72,23 +72,6 @@ struct RawVec<16> {
   }
 };
 
-// Element i of a 32-bit word: float32 is the word itself; 16-bit types hold
-// element 0 in the low half.
-template <typename T>
-__device__ __forceinline__ float widen_half(unsigned d, int half);
-template <>
-__device__ __forceinline__ float widen_half<float>(unsigned d, int) {
-  return __builtin_bit_cast(float, d);
-}
-template <>
-__device__ __forceinline__ float widen_half<__bf16>(unsigned d, int half) {
-  return half ? bf16hi(d) : bf16lo(d);
-}
-template <>
-__device__ __forceinline__ float widen_half<_Float16>(unsigned d, int half) {
-  return half ? f16hi(d) : f16lo(d);
-}
-
 template <typename T, int VB>
 __device__ __forceinline__ void widen_vec(typename RawVec<VB>::W w, float (&f)[VB / sizeof(T)]) {
   constexpr int PER = 4 / (int)sizeof(T);  // elements per word
