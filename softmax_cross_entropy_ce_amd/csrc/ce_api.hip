@@ -108,13 +108,21 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 int launched() { return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_LAUNCH; }
 
 // ------------------------------------------------------------------ path 1
+// Row groups per workgroup: lanes holding 16 bytes of a row take four rows
+// each (their loads all issued first), 32 bytes two, more one.
+template <typename T, int EPL>
+constexpr int short_groups() {
+  return EPL * (int)sizeof(T) <= 16 ? 4 : EPL * (int)sizeof(T) <= 32 ? 2 : 1;
+}
+
 template <typename T, int S, int EPL, int VW, int OP, bool GRAD>
 int launch_short_cfg(const T* z, const int32_t* t, int64_t B, int C, ce::RowArgs rs, T* g, float* l,
                      hipStream_t st) {
-  constexpr int rpb = ce::kShortThreads / S;
+  constexpr int R = short_groups<T, EPL>();
+  constexpr int rpb = ce::kShortThreads / S * R;
   const int64_t blocks = (B + rpb - 1) / rpb;
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL((ce::ce_short_kernel<T, S, EPL, VW, GRAD, OP>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((ce::ce_short_kernel<T, S, EPL, VW, GRAD, OP, R>), dim3((unsigned)blocks),
                      dim3(ce::kShortThreads), 0, st, z, t, B, C, rs, g, l);
   return launched();
 }
@@ -145,10 +153,11 @@ int short_vw(int64_t lens, int es, uintptr_t zaddr, uintptr_t gaddr, int epl) {
   return 1;
 }
 
-// The short path addresses a workgroup's up to 256 rows through one buffer
-// resource per array: their span must stay below 2^31 bytes.
+// The short path addresses a workgroup's up to 1024 rows (256 segments of
+// one lane, four groups) through one buffer resource per array: their span
+// must stay below 2^31 bytes.
 bool short_span_ok(int64_t C, int64_t ld, int es) {
-  return C <= kShortMaxC && (255 * ld + C) * es < ((int64_t)1 << 31);
+  return C <= kShortMaxC && (1023 * ld + C) * es < ((int64_t)1 << 31);
 }
 
 // Short-row layout: about 16 bytes per lane.  S lanes per row is the power

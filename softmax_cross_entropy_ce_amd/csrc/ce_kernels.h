@@ -9,9 +9,10 @@
 namespace ce {
 
 // ===========================================================================
-// Path 1: short rows.  S lanes per row (S = 1..16), 256/S rows per
-// 256-thread workgroup.  Lane q of a segment holds the vectors q, q+S, ...
-// of its row (VW elements each, EPL elements in all), so the lanes of a
+// Path 1: short rows.  S lanes per row (S = 1..16), 256/S rows per group
+// of a 256-thread workgroup and R groups per workgroup, all of whose loads
+// are issued first.  Lane q of a segment holds the vectors q, q+S, ... of
+// its row (VW elements each, EPL elements in all), so the lanes of a
 // segment read consecutive addresses.  Max and sum are reduced across the
 // segment with DPP; nothing goes through LDS.
 // ===========================================================================
@@ -20,84 +21,93 @@ constexpr int kShortThreads = 256;
 
 // GRAD false: the loss (or record) only; grad is not written (and may be
 // null).
-template <typename T, int S, int EPL, int VW, bool GRAD, int OP = kOpCE>
+template <typename T, int S, int EPL, int VW, bool GRAD, int OP = kOpCE, int R = 1>
 __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
     const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B, int C,
     RowArgs rs, T* __restrict__ grad, float* __restrict__ loss_rows) {
   const float invB = row_invB(rs), gmul = grad_mul(rs);
-  constexpr int RPB = kShortThreads / S;  // rows per workgroup
+  constexpr int RPG = kShortThreads / S;  // rows per group: one per segment
+  constexpr int RPB = RPG * R;            // rows per workgroup: R groups
   constexpr int NVEC = EPL / VW;          // vector slots per lane
   static_assert(EPL % VW == 0, "EPL must be a multiple of VW");
   constexpr uint32_t ES = sizeof(T);
 
   const int tid = threadIdx.x;
-  const int q = tid % S;
+  const int q = tid % S, seg = tid / S;
   const int64_t row0 = (int64_t)blockIdx.x * RPB;
-  const int64_t row = row0 + tid / S;
-  const bool live = row < B;
   const int64_t nrows = (B - row0) < RPB ? (B - row0) : RPB;
   // the workgroup's rows, with the row strides (the host keeps these spans
   // below 2^31 bytes); lanes of rows past B read zeros and store nothing
   const rsrc_t rin = make_rsrc(logits + row0 * rs.ldz, (uint32_t)(((nrows - 1) * rs.ldz + C) * ES));
   const rsrc_t rout = make_rsrc(grad + row0 * rs.ldg, (uint32_t)(((nrows - 1) * rs.ldg + C) * ES));
-  const uint32_t rowoff = (uint32_t)(tid / S) * (uint32_t)rs.ldz * ES;
-  const uint32_t rowoff_g = (uint32_t)(tid / S) * (uint32_t)rs.ldg * ES;
 
-  const RowTarget rt = live ? row_target<OP>(targets, row, C, rs) : RowTarget{-1, false, false};
-  const int t = rt.t;
-  const bool valid = live && rt.valid;
-  // slot of the target in its owner lane: element c sits in vector c/VW,
-  // lane (c/VW) % S, slot ((c/VW)/S)*VW + c%VW
-  const int tq = t >= 0 ? (t / VW) % S : -1;
-  const int tslot = t >= 0 ? ((t / VW) / S) * VW + t % VW : -1;
-  const bool owner = (q == tq);
-
-  float f[EPL];
+  // every load of the R groups first: R rows' vectors in flight per lane
+  float f[R][EPL];
 #pragma unroll
-  for (int j = 0; j < NVEC; ++j) {
-    const int c0 = (j * S + q) * VW;
-    float v[VW];
-    if (c0 < C) {
-      VecIO<T, VW>::load(rin, rowoff + (uint32_t)c0 * ES, v);
-    } else {
+  for (int r = 0; r < R; ++r) {
+    const uint32_t rowoff = (uint32_t)(r * RPG + seg) * (uint32_t)rs.ldz * ES;
 #pragma unroll
-      for (int w = 0; w < VW; ++w) v[w] = kNegInf;
-    }
+    for (int j = 0; j < NVEC; ++j) {
+      const int c0 = (j * S + q) * VW;
+      float v[VW];
+      if (c0 < C) {
+        VecIO<T, VW>::load(rin, rowoff + (uint32_t)c0 * ES, v);
+      } else {
 #pragma unroll
-    for (int w = 0; w < VW; ++w) f[j * VW + w] = v[w];
-  }
-  // the target logit, from the owner lane's registers: a segment sum of the
-  // owner's value and zeros is exact
-  float own_zt = 0.f;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) own_zt = (owner && i == tslot) ? f[i] : own_zt;
-  const float zt = seg_allreduce<S>(own_zt, OpAdd{});
-
-  // row max across the segment, then the sum with the target left out
-  const float m = seg_allreduce<S>(max_of(f), OpMax{});
-  const float cg = m * kLog2e;
-  float e[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const float x = (owner && i == tslot) ? kNegInf : f[i];
-    e[i] = exp2_hw(__builtin_fmaf(x, kLog2e, -cg));
-  }
-  const float sx = seg_allreduce<S>(tree_sum(e), OpAdd{});
-  const RowResult rr = row_finish<OP>(cg, sx, zt, valid, rt.ignored, invB, gmul);
-  if (live && q == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
-  if constexpr (!GRAD) return;
-
-#pragma unroll
-  for (int j = 0; j < NVEC; ++j) {
-    const int c0 = (j * S + q) * VW;
-    if (c0 < C) {
-      float g[VW];
-#pragma unroll
-      for (int w = 0; w < VW; ++w) {
-        const int i = j * VW + w;
-        g[w] = (owner && i == tslot) ? rr.gt : exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
+        for (int w = 0; w < VW; ++w) v[w] = kNegInf;
       }
-      VecIO<T, VW>::store(rout, rowoff_g + (uint32_t)c0 * ES, g);
+#pragma unroll
+      for (int w = 0; w < VW; ++w) f[r][j * VW + w] = v[w];
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r * RPG + seg;
+    const bool live = row < B;
+    const RowTarget rt = live ? row_target<OP>(targets, row, C, rs) : RowTarget{-1, false, false};
+    const int t = rt.t;
+    const bool valid = live && rt.valid;
+    // slot of the target in its owner lane: element c sits in vector c/VW,
+    // lane (c/VW) % S, slot ((c/VW)/S)*VW + c%VW
+    const int tq = t >= 0 ? (t / VW) % S : -1;
+    const int tslot = t >= 0 ? ((t / VW) / S) * VW + t % VW : -1;
+    const bool owner = (q == tq);
+    // the target logit, from the owner lane's registers: a segment sum of
+    // the owner's value and zeros is exact
+    float own_zt = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) own_zt = (owner && i == tslot) ? f[r][i] : own_zt;
+    const float zt = seg_allreduce<S>(own_zt, OpAdd{});
+
+    // row max across the segment, then the sum with the target left out;
+    // the terms are kept: scaled, they are the gradient
+    const float m = seg_allreduce<S>(max_of(f[r]), OpMax{});
+    const float cg = m * kLog2e;
+    float e[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const float x = (owner && i == tslot) ? kNegInf : f[r][i];
+      e[i] = exp2_hw(__builtin_fmaf(x, kLog2e, -cg));
+    }
+    const float sx = seg_allreduce<S>(tree_sum(e), OpAdd{});
+    const RowResult rr = row_finish<OP>(cg, sx, zt, valid, rt.ignored, invB, gmul);
+    if (live && q == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
+    if constexpr (GRAD) {
+      const uint32_t rowoff_g = (uint32_t)(r * RPG + seg) * (uint32_t)rs.ldg * ES;
+#pragma unroll
+      for (int j = 0; j < NVEC; ++j) {
+        const int c0 = (j * S + q) * VW;
+        if (c0 < C) {
+          float g[VW];
+#pragma unroll
+          for (int w = 0; w < VW; ++w) {
+            const int i = j * VW + w;
+            g[w] = (owner && i == tslot) ? rr.gt : e[i] * rr.scale;
+          }
+          VecIO<T, VW>::store(rout, rowoff_g + (uint32_t)c0 * ES, g);
+        }
+      }
     }
   }
 }
