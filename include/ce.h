@@ -262,11 +262,14 @@ int ce_softmax_fwd(const void* x, int64_t B, int64_t C, int dtype, void* y_out, 
  *   dx_out   [B, C] dtype, overwritten.  May be y or dy themselves; any
  *            other overlap is refused.  (dy - y) and (dx_out - y) must be
  *            multiples of 16 bytes.
- * Rows of C <= 256 run many to a wave (path 1); longer rows run one
- * workgroup per row with y and dy held in registers (path 2) up to 8192
- * 16-byte vectors of each, and beyond that stream the rest of the row a
- * second time (path 3).  ce_debug_force_path applies; path 4 returns
- * CE_ERR_PATH.
+ * Rows of C <= 256 run many to a wave (path 1); rows of up to 8 KB whose
+ * length and alignment allow 4-byte or wider vectors run whole in one
+ * wavefront's registers, one to four rows per wave (path 5); other rows of
+ * up to 8192 16-byte vectors run one workgroup per row with y and dy held
+ * in registers (path 2); longer rows of up to 16384 body vectors, out of
+ * place, run in four parts that trade their partial dot products (path 4),
+ * and beyond that, or in place, stream the rest of the row a second time
+ * (path 3).  ce_debug_force_path applies.
  */
 int ce_softmax_bwd(const void* y, const void* dy, int64_t B, int64_t C, int dtype, void* dx_out,
                    void* stream);

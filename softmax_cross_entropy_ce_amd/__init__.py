@@ -140,8 +140,9 @@ def force_path(path: int) -> int:
 
 
 def part_polls(polls: int) -> int:
-    """Test hook: polls of a path-4 row part for its partner's pair before it
-    recomputes the pair (0: always recompute).  Returns the previous value."""
+    """Test hook: polls of a path-4 row part for its partners' pairs before
+    it recomputes the missing ones (0: always recompute).  Returns the
+    previous value."""
     r = lib().ce_debug_part_polls(int(polls))
     if r < 0:
         raise CEError(r, "ce_debug_part_polls")
@@ -149,8 +150,9 @@ def part_polls(polls: int) -> int:
 
 
 def part_counter(counter=None) -> None:
-    """Test hook: a one-element int32/uint32 device tensor that counts path-4
-    parts which recomputed their partner's pair (None turns counting off).
+    """Test hook: a one-element int32/uint32 device tensor to which every
+    path-4 part adds the number of partner pairs it recomputed (None turns
+    counting off).
     The tensor must stay alive until the calls made with it have run."""
     if counter is None:
         ptr = None

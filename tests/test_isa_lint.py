@@ -122,7 +122,8 @@ def test_kernels_present(device_asm):
     for k in ("ce_short_kernel", "ce_tiny_kernel", "ce_row_kernel", "ce_row_lds_kernel",
               "ce_reduce_kernel", "ce_part_kernel", "ce_shard_grad_kernel", "ce_scale_kernel",
               "ce_count_kept_kernel", "sm_bwd_short_kernel", "sm_bwd_row_kernel",
-              "sm_bwd_part_kernel", "ce_wave_kernel"):
+              "sm_bwd_part_kernel", "ce_wave_kernel", "sm_bwd_wave_kernel",
+              "ce_shard_grad_tiny_kernel"):
         assert k in names, k
 
 
