@@ -213,16 +213,22 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
   int64_t chunk = blockIdx.x;
   if (chunk >= nchunks) return;
 
-  auto load_full = [&](int64_t ch, u32x4 (&v)[K]) {
+  // a chunk's loads: its data, and the targets of this thread's rows (so
+  // that no target load waits on the chunk's critical path)
+  auto load_full = [&](int64_t ch, u32x4 (&v)[K], int32_t (&tg)[R]) {
     const rsrc_t r = make_rsrc(logits + ch * ROWS * C, full_bytes);
 #pragma unroll
     for (int k = 0; k < K; ++k) v[k] = bload128<kPolicyStream>(r, voff, (uint32_t)k * NT * 16u);
+    if constexpr (OP != kOpSoftmax) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) tg[j] = targets[ch * ROWS + tid + j * NT];
+    }
   };
   const int64_t G = gridDim.x;
   // one chunk: into LDS from its register set, which is then refilled with
   // the chunk two steps ahead, so two chunks' loads are in flight while
   // this one is reduced and stored
-  auto step = [&](u32x4 (&r)[K], int64_t ch) {
+  auto step = [&](u32x4 (&r)[K], int32_t (&tg)[R], int64_t ch) {
     const int64_t row0 = ch * ROWS;
     const bool full = ch < nfull;
     const int nrows = full ? ROWS : (int)(B - row0);
@@ -244,8 +250,16 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
       for (int i = tid; i < nrows * C; i += NT)
         LdsElem<T>::put(stage, elem_slot(i), E::load1(logits + row0 * C + i));
     }
+    // this chunk's targets, before the register set is refilled
+    RowTarget rts[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int lr = tid + j * NT;
+      rts[j] = !full && lr < nrows ? row_target<OP>(targets, row0 + lr, C, rs)
+                                   : row_target_of<OP>(full ? tg[j] : -1, C, rs);
+    }
     __syncthreads();
-    if (ch + 2 * G < nfull) load_full(ch + 2 * G, r);
+    if (ch + 2 * G < nfull) load_full(ch + 2 * G, r, tg);
 
     // rows tid, tid + NT, ... of the chunk
 #pragma unroll
@@ -253,7 +267,7 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
       const int lr = tid + j * NT;
       if (lr >= nrows) break;
       const int64_t row = row0 + lr;
-      const RowTarget rt = row_target<OP>(targets, row, C, rs);
+      const RowTarget rt = rts[j];
       const int t = rt.t;
       float f[CMAX];
       float m = kNegInf;
@@ -327,13 +341,14 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
   };
 
   u32x4 v[K], u[K];
-  if (chunk < nfull) load_full(chunk, v);
-  if (chunk + G < nfull) load_full(chunk + G, u);
+  int32_t tv[R], tu[R];
+  if (chunk < nfull) load_full(chunk, v, tv);
+  if (chunk + G < nfull) load_full(chunk + G, u, tu);
   for (;;) {
-    step(v, chunk);
+    step(v, tv, chunk);
     chunk += G;
     if (chunk >= nchunks) break;
-    step(u, chunk);
+    step(u, tu, chunk);
     chunk += G;
     if (chunk >= nchunks) break;
   }

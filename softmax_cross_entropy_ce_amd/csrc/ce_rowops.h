@@ -73,17 +73,27 @@ struct RowTarget {
   bool ignored;
 };
 
+// The same from the row's target value itself (raw: targets[row], loaded by
+// the caller; unused for the softmax).
+template <int OP>
+__device__ __forceinline__ RowTarget row_target_of(int32_t raw, int C, const RowArgs& rs) {
+  if constexpr (OP == kOpSoftmax) {
+    return RowTarget{-1, true, false};
+  } else {
+    if (OP == kOpCE && rs.has_ignore && raw == rs.ignore) return RowTarget{-1, true, true};
+    const int64_t t = (int64_t)raw - (OP == kOpShard ? rs.col0 : 0);
+    const bool in = t >= 0 && t < C;
+    return RowTarget{in ? (int)t : -1, OP == kOpShard || in, false};
+  }
+}
+
 template <int OP>
 __device__ __forceinline__ RowTarget row_target(const int32_t* targets, int64_t row, int C,
                                                 const RowArgs& rs) {
   if constexpr (OP == kOpSoftmax) {
     return RowTarget{-1, true, false};
   } else {
-    const int32_t raw = targets[row];
-    if (OP == kOpCE && rs.has_ignore && raw == rs.ignore) return RowTarget{-1, true, true};
-    const int64_t t = (int64_t)raw - (OP == kOpShard ? rs.col0 : 0);
-    const bool in = t >= 0 && t < C;
-    return RowTarget{in ? (int)t : -1, OP == kOpShard || in, false};
+    return row_target_of<OP>(targets[row], C, rs);
   }
 }
 
