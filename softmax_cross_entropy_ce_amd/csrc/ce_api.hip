@@ -48,9 +48,10 @@ constexpr RowCfg kLongTestCfg = {256, 1};   // forced path 3: small on-chip part
 
 constexpr int kShortMaxC = 256;
 // Automatic selection (measured on rows filling 1 GiB): path 5 takes rows
-// of up to 8 KB of 16-bit elements or 4 KB of float32 (above that the
-// one-part, 256-thread configuration of path 4 moves more bytes per second;
-// float32 rows reach it sooner, their gradient needing no second exp).
+// of up to 8 KB of 16-bit elements or 4 KB of float32; above that the
+// one-part, 256-thread configuration of path 4 moved more bytes per second
+// (the two crossed between 8 and 12 KB for bf16 rows, between 4 and 8 KB
+// for fp32 rows).
 // Rows path 5 has no configuration for stay on path 2 up to that size;
 // longer rows go to path 4 while their aligned body fits its largest
 // configuration, then to path 3.
@@ -160,24 +161,20 @@ bool short_span_ok(int64_t C, int64_t ld, int es) {
   return C <= kShortMaxC && (1023 * ld + C) * es < ((int64_t)1 << 31);
 }
 
-// Short-row layout: about 16 bytes per lane.  S lanes per row is the power
-// of two that covers the row with EPL elements per lane (EPL = 16 bytes of
-// elements, more only at S = 16).  Lanes of a row read adjacent vectors,
-// so a load instruction covers 64/S consecutive rows.
-int resident_blocks(const void* kernel, int nt);
+int resident_blocks(const void* kernel, int nt, std::atomic<int>& per_cu_cache);
 
 // Rows of at most 64 bytes, contiguous, in 16-byte aligned arrays: the
-// LDS-staged kernel with one row per thread, persistent over chunks of 256
-// rows.
-// One row per thread: chunks of 256 rows (two rows per thread, with half as
-// many workgroups resident, measured slower).
+// LDS-staged kernel, persistent over chunks of 256 * R rows (R rows per
+// thread, below).  Rows of more than 32 bytes take one per thread (two,
+// with half as many workgroups resident, measured slower on 40-byte rows).
 constexpr int kTinyRowsPerThread = 1;
 
 template <typename T, int CMAX, int R, int OP, bool GRAD, bool PAD>
 int launch_tiny_w(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
                   float* l, hipStream_t st) {
   auto kern = ce::ce_tiny_kernel<T, CMAX, R, GRAD, OP, PAD>;
-  const int res = resident_blocks(reinterpret_cast<const void*>(kern), ce::kTinyThreads);
+  static std::atomic<int> occupancy{0};
+  const int res = resident_blocks(reinterpret_cast<const void*>(kern), ce::kTinyThreads, occupancy);
   if (res < 1) return CE_ERR_LAUNCH;
   const int64_t rows = (int64_t)ce::kTinyThreads * R;
   const int64_t chunks = (B + rows - 1) / rows;
@@ -235,6 +232,10 @@ bool tiny_rows(const T* z, int64_t C, const ce::RowArgs& rs, const T* g, bool gr
          (!grad || (rs.ldg == C && (uintptr_t)g % 16 == 0));
 }
 
+// Short-row layout: about 16 bytes per lane.  S lanes per row is the power
+// of two that covers the row with EPL elements per lane (EPL = 16 bytes of
+// elements, more only at S = 16).  Lanes of a row read adjacent vectors,
+// so a load instruction covers 64/S consecutive rows.
 template <typename T, int OP, bool GRAD>
 int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g, float* l,
                  hipStream_t st) {
@@ -266,14 +267,33 @@ int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs
 // Workgroups of a kernel that the current device holds at once: compute
 // units times the occupancy of that kernel.  The row kernels are persistent,
 // so their grid is this number (or B when that is smaller).
-int resident_blocks(const void* kernel, int nt) {
-  int dev = 0, cus = 0, per_cu = 0;
+// The compute-unit count is cached per device (a partitioned GPU exposes
+// devices of fewer units) and the occupancy per kernel by the caller, so a
+// launch queries the runtime only the first time.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_cus[kMaxDevices];
+
+int device_cus() {
+  int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached && (cus = g_device_cus[dev].load(std::memory_order_relaxed)) > 0) return cus;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return -1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nt, 0) != hipSuccess)
-    return -1;
-  if (per_cu < 1) per_cu = 1;
+  if (cached) g_device_cus[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+int resident_blocks(const void* kernel, int nt, std::atomic<int>& per_cu_cache) {
+  const int cus = device_cus();
+  if (cus < 1) return -1;
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
+  if (per_cu < 1) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nt, 0) != hipSuccess)
+      return -1;
+    if (per_cu < 1) per_cu = 1;
+    per_cu_cache.store(per_cu, std::memory_order_relaxed);
+  }
   return cus * per_cu;
 }
 
@@ -281,7 +301,8 @@ template <typename T, int NT, int NV, int OP, bool GRAD>
 int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
                    float* l, hipStream_t st) {
   auto kern = ce::ce_row_kernel<T, NT, NV, GRAD, OP>;
-  const int res = resident_blocks(reinterpret_cast<const void*>(kern), NT);
+  static std::atomic<int> occupancy{0};
+  const int res = resident_blocks(reinterpret_cast<const void*>(kern), NT, occupancy);
   if (res < 1) return CE_ERR_LAUNCH;
   const int64_t grid = B < res ? B : res;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), 0, st, z, t, B, (int)C, rs, g, l);
@@ -296,7 +317,8 @@ template <typename T, int OP>
 int launch_row_lds(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
                    float* l, hipStream_t st) {
   auto kern = ce::ce_row_lds_kernel<T, 16, kLdsPrefetchSlots, OP>;
-  const int res = resident_blocks(reinterpret_cast<const void*>(kern), 1024);
+  static std::atomic<int> occupancy{0};
+  const int res = resident_blocks(reinterpret_cast<const void*>(kern), 1024, occupancy);
   if (res < 1) return CE_ERR_LAUNCH;
   const int64_t grid = B < res ? B : res;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(1024), 0, st, z, t, B, (int)C, rs, g, l);
@@ -676,7 +698,8 @@ int launch_bwd_short(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipSt
 template <typename T, int NT, int NV>
 int launch_bwd_row_cfg(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipStream_t st) {
   auto kern = ce::sm_bwd_row_kernel<T, NT, NV>;
-  const int res = resident_blocks(reinterpret_cast<const void*>(kern), NT);
+  static std::atomic<int> occupancy{0};
+  const int res = resident_blocks(reinterpret_cast<const void*>(kern), NT, occupancy);
   if (res < 1) return CE_ERR_LAUNCH;
   const int64_t grid = B < res ? B : res;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), 0, st, y, dy, B, (int)C, dx);
