@@ -43,7 +43,7 @@ constexpr RowCfg kRowCfgs[] = {{64, 1},   {64, 2},   {64, 4},    {256, 2},  {256
 // registers for the row's reduction).
 constexpr RowCfg kReadCfgs[] = {{64, 1},   {64, 2},   {64, 4},    {256, 2},  {256, 4},
                                 {256, 8},  {256, 16}, {1024, 8},  {1024, 16}};
-constexpr RowCfg kLongCfg = {1024, 16};     // automatic path 3
+constexpr RowCfg kLongCfg = {1024, 16};     // automatic path 3 with a gradient
 constexpr RowCfg kLongTestCfg = {256, 1};   // forced path 3: small on-chip part
 
 constexpr int kShortMaxC = 256;
@@ -338,8 +338,10 @@ int launch_row(RowCfg cfg, const T* z, const int32_t* t, int64_t B, int64_t C, c
   CE_ROW_CASE(256, 2)
   CE_ROW_CASE(256, 4)
   if constexpr (!GRAD) {
+    CE_ROW_CASE(128, 16)
     CE_ROW_CASE(256, 8)
     CE_ROW_CASE(256, 16)
+    CE_ROW_CASE(512, 8)
   }
   CE_ROW_CASE(1024, 2)
   CE_ROW_CASE(1024, 4)
@@ -364,6 +366,28 @@ RowCfg resident_cfg(int64_t C, int es, bool* ok, bool grad = true, bool aligned 
       return r;
     }
   *ok = false;
+  return kLongCfg;
+}
+
+// Automatic configuration of a row read for its per-row value only, by the
+// 16-byte vectors it needs.  Up to 4096 vectors (16-bit types) or 1024
+// (float32) the first of kReadCfgs that holds the row; longer rows keep a
+// part of the row on chip and stream the rest, in the configuration that
+// moved the most bytes per second on rows filling 1 GiB: 16-bit rows with
+// 256 threads x 8 slots up to 12288 vectors and 512 x 8 beyond (the
+// 1024-thread configurations that hold such rows whole fit one workgroup
+// per compute unit and left it idle while a row is reduced); float32 rows
+// with 128 x 16 up to 6144 vectors and 1024 x 4 beyond.
+RowCfg read_cfg(int64_t need, int es) {
+  if (es == 2) {
+    if (need > 12288) return {512, 8};
+    if (need > 4096) return {256, 8};
+  } else {
+    if (need > 6144) return {1024, 4};
+    if (need > 1024) return {128, 16};
+  }
+  for (const RowCfg& r : kReadCfgs)
+    if ((int64_t)r.nt * r.nv >= need) return r;
   return kLongCfg;
 }
 
@@ -404,6 +428,7 @@ int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g
   constexpr int es = sizeof(T);
   const bool aligned = (uintptr_t)z % 16 == 0 && (rs.ldz * es) % 16 == 0 &&
                        (!GRAD || ((uintptr_t)g % 16 == 0 && (rs.ldg * es) % 16 == 0));
+  const bool forced = g_force_path.load(std::memory_order_relaxed) != 0;
   switch (path) {
     case kPathShort:
       return launch_short<T, OP, GRAD>(z, t, B, C, rs, g, l, st);
@@ -413,12 +438,16 @@ int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g
       if (!ok) return CE_ERR_PATH;
       if constexpr (GRAD) {
         if (cfg.nt == 1024 && cfg.nv == 16) return launch_row_lds<T, OP>(z, t, B, C, rs, g, l, st);
+      } else {
+        if (!forced) return launch_row<T, OP, GRAD>(read_cfg(row_need(C, es, aligned), es), z, t, B,
+                                                    C, rs, g, l, st);
       }
       return launch_row<T, OP, GRAD>(cfg, z, t, B, C, rs, g, l, st);
     }
     case kPathLong: {
-      const bool forced = g_force_path.load(std::memory_order_relaxed) == kPathLong;
-      return launch_row<T, OP, GRAD>(forced ? kLongTestCfg : kLongCfg, z, t, B, C, rs, g, l, st);
+      if (forced) return launch_row<T, OP, GRAD>(kLongTestCfg, z, t, B, C, rs, g, l, st);
+      return launch_row<T, OP, GRAD>(GRAD ? kLongCfg : read_cfg(row_need(C, es, aligned), es), z, t,
+                                     B, C, rs, g, l, st);
     }
     case kPathParts:
       if constexpr (GRAD) return launch_parts<T, OP>(z, t, B, C, rs, g, l, st);
@@ -437,10 +466,12 @@ bool multi_part_row(int64_t C, int es) { return body_vectors_max(C, es) > kParts
 // in place): path 5 where it has a configuration for contiguous rows (it falls
 // back to path 2 at launch when the arrays do not allow it), else path 2 or
 // 3 by length.
-int path_without_parts(int64_t C, int es) {
+int path_without_parts(int64_t C, int es, bool grad) {
   if (C <= kShortMaxC) return kPathShort;
   if (ce_wave::lane_bytes(C, es, wave_vb_contiguous(C, es)) != 0) return kPathWave;
-  return row_vectors(C, es) <= (int64_t)kLongCfg.nt * kLongCfg.nv ? kPathResident : kPathLong;
+  const int64_t need = row_vectors(C, es);
+  const RowCfg cap = grad ? kLongCfg : read_cfg(need, es);
+  return need <= (int64_t)cap.nt * cap.nv ? kPathResident : kPathLong;
 }
 
 bool overlaps(uintptr_t a, uintptr_t an, uintptr_t b, uintptr_t bn) {
@@ -556,7 +587,7 @@ int fwd_impl(const FwdArgs& a, void* stream) {
   if (!a.grad || in_place) {
     if (path == kPathParts && (!a.grad || multi_part_row(C, es))) {
       if (forced) return CE_ERR_PATH;
-      path = path_without_parts(C, es);
+      path = path_without_parts(C, es, a.grad != nullptr);
     }
   }
   const bool short_ok = short_span_ok(C, a.ldz, es) && (!a.grad || short_span_ok(C, ldg, es));
