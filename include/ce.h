@@ -80,7 +80,7 @@ typedef enum {
  *   B, C      1 <= B <= 2^31 - 1, 1 <= C <= CE_MAX_C.
  *   dtype     CE_F32 or CE_BF16.
  *   grad_out  [B, C] dtype, fully overwritten with (softmax - onehot) / B.
- *             Contents on entry are ignored; on path 4 with two or four
+ *             Contents on entry are ignored; on path 4 with several
  *             parts per row the call also uses 16 bytes per other part of
  *             each part's own gradient as a mailbox before the gradient is
  *             written there.
@@ -355,7 +355,7 @@ int ce_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
  *   3 long rows   - as 2, with the part of the row beyond the on-chip
  *                   capacity streamed with online max/sum-exp partials and
  *                   re-read for the gradient;
- *   4 row parts   - the row cut into one, two or four parts (one
+ *   4 row parts   - the row cut into one, two, four or eight parts (one
  *                   256-thread workgroup for rows up to 32 KB, else
  *                   1024-thread workgroups of up to 12 x 16 KB, two per
  *                   CU); each part is read once into registers and LDS and
@@ -365,8 +365,8 @@ int ce_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
  *                   that does not receive a partner's pair in time
  *                   recomputes it with the same code, so the bits do not
  *                   depend on timing.  Automatic above 8 KB of 16-bit or
- *                   4 KB of fp32 elements, up to 768 KB (16-bit C up to
- *                   393216) or 512 KB (fp32 C up to 131072).
+ *                   4 KB of fp32 elements, up to 1 MB (16-bit C up to
+ *                   524288, fp32 C up to 262144).
  *   5 wave rows   - rows of up to 16 KB (automatic above 256 elements)
  *                   whose starts, lengths and strides allow 16-, 8- or
  *                   4-byte vectors (4-byte ones up to 8 KB; 16-bit rows of

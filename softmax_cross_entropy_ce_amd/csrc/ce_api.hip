@@ -68,7 +68,8 @@ int64_t row_vectors(int64_t C, int es) { return (C * es + 15) / 16 + 1; }
 // register slots (eight such workgroups fit a CU); one part of 1024
 // threads and 4 register slots; one part of 8 register and 2 LDS slots;
 // two parts of 8 register slots; two parts of 8 register and 4 LDS slots;
-// four parts of 8 register slots; four parts of 8 register and 4 LDS slots
+// four parts of 8 register slots; four parts of 8 register and 4 LDS slots;
+// eight parts of 8 register slots
 // (a 1024-thread slot is 1024 vectors, and a part of a P-part row is 1/P of
 // the body rounded up to 8 vectors).
 constexpr int64_t kPartsOneQuarter = 8 * 256;
@@ -78,11 +79,12 @@ constexpr int64_t kPartsTwoRegs = 2 * 8 * 1024;
 constexpr int64_t kPartsTwo = 2 * 12 * 1024;
 constexpr int64_t kPartsFourRegs = 4 * 8 * 1024;
 constexpr int64_t kPartsFour = 4 * 12 * 1024;
-// The largest body path 4 takes: four parts with LDS slots for 16-bit
-// types; for float32 (whose register slots keep the terms of the sum) that
-// configuration would exceed 64 VGPRs, so it stops at four register-only
-// parts.
-int64_t parts_max(int es) { return es == 4 ? kPartsFourRegs : kPartsFour; }
+constexpr int64_t kPartsEightRegs = 8 * 8 * 1024;
+// The largest body path 4 takes: eight register-only parts.  (Four parts
+// with LDS slots serve 16-bit rows up to kPartsFour; for float32, whose
+// register slots keep the terms of the sum, that configuration would exceed
+// 64 VGPRs, so fp32 rows go from four register-only parts to eight.)
+int64_t parts_max(int) { return kPartsEightRegs; }
 
 int64_t body_vectors_max(int64_t C, int es) { return C / (16 / es); }
 
@@ -417,6 +419,7 @@ int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs
   if constexpr (sizeof(T) == 2) {
     if (nb <= kPartsFour) return launch_parts_cfg<T, 4, 1024, 8, 4, 0, OP>(z, t, B, C, rs, g, l, st);
   }
+  if (nb <= kPartsEightRegs) return launch_parts_cfg<T, 8, 1024, 8, 0, 0, OP>(z, t, B, C, rs, g, l, st);
   return CE_ERR_PATH;
 }
 
@@ -457,7 +460,7 @@ int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g
   }
 }
 
-// Rows that path 4 cuts into two or four parts: their parts may read each
+// Rows that path 4 cuts into several parts: their parts may read each
 // other's logits (the recompute) and keep mailboxes in grad, so they cannot
 // run in place.
 bool multi_part_row(int64_t C, int es) { return body_vectors_max(C, es) > kPartsOne; }

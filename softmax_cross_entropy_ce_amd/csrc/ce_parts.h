@@ -45,8 +45,8 @@
 //
 // Workgroup g runs on XCD g % 8 (round-robin dispatch); the parts of a row
 // are given workgroups g, g + 8, ..., so they share an XCD and start next to
-// each other in its dispatch order.  Rows are cut into one, two or four
-// parts.
+// each other in its dispatch order.  Rows are cut into one, two, four or
+// eight parts.
 #pragma once
 
 #include "ce_kernels.h"
@@ -121,7 +121,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   constexpr int NLS = NL + (NXW > 0 ? 1 : 0);  // LDS slots, the last maybe partial
   constexpr int NS = NR + NLS;                 // slots per part
   constexpr int NX = NXW * 64;                 // threads with a vector in the partial slot
-  static_assert(P >= 1 && P <= 4, "one to four parts per row");
+  static_assert(P == 1 || P == 2 || P == 4 || P == 8, "one, two, four or eight parts per row");
   static_assert(NT % 64 == 0 && NW >= 1 && NW <= 16, "1 to 16 waves");
   static_assert(NXW >= 0 && NXW < NW, "partial LDS slot smaller than a slot");
   __shared__ u32x4 stage[NL * NT + NX > 0 ? NL * NT + NX : 1];
@@ -258,7 +258,9 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   // Phase B: this part's pair.  For fp32, the register slots keep each
   // element's term 2^(z log2e - c_k) in place of z, with c_k the running max
   // after slot k, so that the gradient needs one multiply per element.
-  constexpr bool kKeepTerms = sizeof(T) == 4;
+  // Eight parts recompute the terms instead: the running maxima, with the
+  // code that trades eight pairs, would not fit the 64 VGPRs.
+  constexpr bool kKeepTerms = sizeof(T) == 4 && P <= 4;
   float ck[NR];
   float c = kLowest, s = 0.f;
 #pragma unroll
@@ -290,6 +292,10 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   // received, or recomputed where a partner's did not arrive in time.
   float cg = c_own, sx = s_own;
   if constexpr (P > 1) {
+    // Eight parts keep the loops over partners rolled (less code, and no
+    // partner's address or pair held beyond its iteration: the kernel is
+    // capped at 64 VGPRs).
+    constexpr int kUnrollPartners = P <= 4 ? P : 1;
     if (tid == 0) {
       mail_c[part] = c_own;
       mail_s[part] = s_own;
@@ -299,15 +305,19 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       // The publishes are issued without waiting for their results, so the
       // next poll follows them at once.
       auto publish = [&] {
-#pragma unroll
+#pragma unroll kUnrollPartners
         for (int q = 0; q < P; ++q) {
           if (q == part) continue;
           uint64_t* m = mailbox(part_range(geo.nb, P, q)) + mail_index(part, q);
           uint64_t e0 = kEmptyWord, e1 = kEmptyWord;
+          // a 64-bit compare-and-swap sends 16 bytes of data: the same
+          // wait states as a wide store follow it
           __hip_atomic_compare_exchange_strong(&m[0], &e0, w0, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
+          wide_store_guard();
           __hip_atomic_compare_exchange_strong(&m[1], &e1, w1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
+          wide_store_guard();
         }
       };
       publish();
@@ -315,7 +325,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       constexpr unsigned kAll = (1u << P) - 1u;
       unsigned got = 1u << part;
       for (int it = 0; it < spin && got != kAll; ++it) {
-#pragma unroll
+#pragma unroll kUnrollPartners
         for (int q = 0; q < P; ++q) {
           if ((got >> q) & 1u) continue;
           const uint64_t* m = mine + mail_index(q, part);
@@ -338,7 +348,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
         atomicAdd(fallbacks, (uint32_t)(P - __builtin_popcount(got)));
     }
     __syncthreads();
-#pragma unroll
+#pragma unroll kUnrollPartners
     for (int q = 0; q < P; ++q) {
       if (q == part || mail_ok[q]) continue;  // uniform (LDS, after the barrier)
       // Recompute part q's pair: the same slots, fold order, edges and
@@ -368,6 +378,8 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
     cg = mail_c[0];
 #pragma unroll
     for (int q = 1; q < P; ++q) cg = __builtin_fmaxf(cg, mail_c[q]);
+    // the maxima are read from LDS again rather than kept in registers
+    if constexpr (P > 4) asm volatile("" ::: "memory");
     sx = mail_s[0] * exp2_hw(mail_c[0] - cg);
 #pragma unroll
     for (int q = 1; q < P; ++q) sx = sx + mail_s[q] * exp2_hw(mail_c[q] - cg);

@@ -208,8 +208,7 @@ def wave_takes(C: int, es: int, lens=None, addrs=()) -> bool:
 def path_takes(path: int, C: int, dtype: str) -> bool:
     """Whether a forced path takes contiguous rows of C elements from
     16-byte aligned arrays (short: C <= 256; resident: at most 16384
-    16-byte vectors; parts: an aligned body of at most 49152 vectors for
-    16-bit types, 32768 for fp32;
+    16-byte vectors; parts: an aligned body of at most 65536 vectors;
     wave: wave_takes)."""
     es = 4 if dtype == "f32" else 2
     if path == 1:
@@ -217,7 +216,7 @@ def path_takes(path: int, C: int, dtype: str) -> bool:
     if path == 2:
         return (C * es + 15) // 16 + 1 <= 16384
     if path == 4:
-        return C // (16 // es) <= (32768 if es == 4 else 49152)
+        return C // (16 // es) <= 65536
     if path == 5:
         return wave_takes(C, es)
     return True

@@ -138,12 +138,16 @@ def test_reduce_loss_validation():
     ("odd-bf16", 257, 1, 2),
     ("odd-bf16-limit", 4095, 1, 2),
     ("over-odd-bf16-limit", 4097, 1, 4),
-    # four parts of 12 x 1024 vectors (16-bit) or 8 x 1024 (fp32): aligned
-    # body of at most 49152 or 32768 vectors
-    ("parts-limit-bf16", 393_216, 1, 4),
-    ("over-parts-bf16", 393_224, 1, 3),
-    ("parts-limit-f32", 131_072, 0, 4),
-    ("over-parts-f32", 131_076, 0, 3),
+    # four parts of 12 x 1024 vectors (16-bit) or 8 x 1024 (fp32), then
+    # eight parts of 8 x 1024 vectors: aligned body of at most 65536 vectors
+    ("four-parts-limit-bf16", 393_216, 1, 4),
+    ("eight-parts-bf16", 393_224, 1, 4),
+    ("parts-limit-bf16", 524_288, 1, 4),
+    ("over-parts-bf16", 524_296, 1, 3),
+    ("four-parts-limit-f32", 131_072, 0, 4),
+    ("eight-parts-f32", 131_076, 0, 4),
+    ("parts-limit-f32", 262_144, 0, 4),
+    ("over-parts-f32", 262_148, 0, 3),
 ])
 def test_path_selection(name, C, dtype, path):
     assert ce.select_path(C, dtype) == path

@@ -50,10 +50,10 @@ def _legal(path, C, dtype):
 
 
 def _two_part(C, dtype):
-    """Rows that path 4 cuts into two or four parts (an aligned body of
-    10241 to 49152 16-byte vectors, 32768 for fp32)."""
+    """Rows that path 4 cuts into several parts (an aligned body of 10241
+    to 65536 16-byte vectors)."""
     nb = C // (4 if dtype == "f32" else 8)
-    return 10 * 1024 < nb <= (32 if dtype == "f32" else 48) * 1024
+    return 10 * 1024 < nb <= 64 * 1024
 
 
 def _check_losses(lr_gpu, z, t, dtype, where, B=None):

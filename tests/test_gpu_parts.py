@@ -4,8 +4,8 @@ workgroups of a row.
 A part that does not receive its partner's pair in time recomputes it with
 the same code.  These tests force that (zero polls) and check that the
 outputs are bitwise those of the exchange, that the device counter sees
-every part of every row of two or four parts recompute every other part's
-pair, that mailbox-like bit patterns
+every part of every row of two, four or eight parts recompute every other
+part's pair, that mailbox-like bit patterns
 left in grad_out on entry change nothing, that the forced fallback matches
 the oracle, and that calls on two streams at once do not disturb each
 other."""
@@ -23,8 +23,10 @@ pytestmark = pytest.mark.gpu
 
 # (B, C, dtype, sigma): two parts per row (aligned, 2-byte aligned, 4-byte
 # aligned fp32, every slot filled), four parts per row (registers only,
-# fp32 at its largest, 2-byte aligned with LDS slots, every slot filled)
-# and one one-part shape as a control.
+# fp32 at its largest, 2-byte aligned with LDS slots, every slot filled),
+# eight parts per row (fp32 just past four parts, a 256000-wide fp32 row,
+# both types at their largest, 2-byte aligned bf16) and one one-part shape
+# as a control.
 SHAPES = [
     (64, 128256, "bf16", 4.0),
     (9, 99999, "bf16", 4.0),
@@ -34,6 +36,11 @@ SHAPES = [
     (6, 131071, "f32", 3.0),
     (5, 300001, "bf16", 4.0),
     (3, 393216, "bf16", 4.0),
+    (7, 131077, "f32", 3.0),
+    (9, 256000, "f32", 3.0),
+    (3, 262144, "f32", 3.0),
+    (3, 524288, "bf16", 4.0),
+    (4, 400001, "bf16", 4.0),
     (40, 40000, "f32", 3.0),
 ]
 IDS = [f"{b}x{c}-{d}" for b, c, d, _ in SHAPES]
@@ -60,9 +67,13 @@ def _reset_hooks():
 
 def _parts(C, dtype):
     """Parts per row: one up to an aligned body of 10240 vectors, two up to
-    24576, then four."""
+    24576, four up to 49152 (16-bit) or 32768 (fp32), then eight."""
     nb = C // (4 if dtype == "f32" else 8)
-    return 1 if nb <= 10 * 1024 else 2 if nb <= 24 * 1024 else 4
+    if nb <= 10 * 1024:
+        return 1
+    if nb <= 24 * 1024:
+        return 2
+    return 4 if nb <= (32 if dtype == "f32" else 48) * 1024 else 8
 
 
 def _bits(x):

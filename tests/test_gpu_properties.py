@@ -27,8 +27,9 @@ CASES = [
     (8, 50257, "f32", 3.0, 2),      # resident, 1024 threads, misaligned rows
     (4, 128256, "bf16", 4.0, 2),    # resident with LDS prefetch
     (300, 70001, "bf16", 4.0, 2),   # LDS prefetch, several rows per workgroup
-    (3, 200_000, "bf16", 4.0, 0),   # long rows: streamed part
+    (3, 200_000, "bf16", 4.0, 0),   # long rows: four parts
     (2, 100_003, "f32", 3.0, 0),    # long rows, misaligned
+    (2, 300_001, "f32", 3.0, 0),    # past eight parts: streamed part (path 3)
 ]
 IDS = [f"{b}x{c}-{d}-p{p}" for b, c, d, _, p in CASES]
 
