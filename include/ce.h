@@ -266,10 +266,10 @@ int ce_softmax_fwd(const void* x, int64_t B, int64_t C, int dtype, void* y_out, 
  * length and alignment allow 4-byte or wider vectors run whole in one
  * wavefront's registers, one to four rows per wave (path 5); other rows of
  * up to 8192 16-byte vectors run one workgroup per row with y and dy held
- * in registers (path 2); longer rows of up to 16384 body vectors, out of
- * place, run in four parts that trade their partial dot products (path 4),
- * and beyond that, or in place, stream the rest of the row a second time
- * (path 3).  ce_debug_force_path applies.
+ * in registers (path 2); longer rows of up to 32768 body vectors, out of
+ * place, run in four parts (up to 16384 vectors) or eight that trade their
+ * partial dot products (path 4), and beyond that, or in place, stream the
+ * rest of the row a second time (path 3).  ce_debug_force_path applies.
  */
 int ce_softmax_bwd(const void* y, const void* dy, int64_t B, int64_t C, int dtype, void* dx_out,
                    void* stream);

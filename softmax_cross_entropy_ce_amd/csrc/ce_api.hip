@@ -758,12 +758,13 @@ int launch_bwd_row(RowCfg cfg, const T* y, const T* dy, int64_t B, int64_t C, T*
 }
 
 // Row parts of the backward: four parts of four register slots of y and of
-// dy (1024 threads): bodies of up to 16384 16-byte vectors per array (bf16
-// C up to 131072, fp32 C up to 65536), out of place only (a part's mailbox
-// is in dx and a recompute reads its partner's y and dy).
-constexpr int kBwdParts = 4;
+// dy (1024 threads) for bodies of up to 16384 16-byte vectors per array
+// (bf16 C up to 131072, fp32 C up to 65536), eight such parts up to 32768
+// (bf16 C up to 262144, fp32 C up to 131072); out of place only (a part's
+// mailbox is in dx and a recompute reads its partner's y and dy).
 constexpr int kBwdPartSlots = 4;
-constexpr int64_t kBwdPartsMax = (int64_t)kBwdParts * kBwdPartSlots * 1024;
+constexpr int64_t kBwdPartsFour = (int64_t)4 * kBwdPartSlots * 1024;
+constexpr int64_t kBwdPartsMax = (int64_t)8 * kBwdPartSlots * 1024;
 constexpr int64_t kBwdPartsMin = 128;  // every part keeps at least its two mailbox vectors
 
 bool bwd_parts_take(int64_t C, int es, bool in_place) {
@@ -779,15 +780,22 @@ int bwd_auto_path(int64_t C, int es, bool in_place) {
   return kPathLong;
 }
 
-template <typename T>
-int launch_bwd_parts(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipStream_t st) {
-  const int64_t blocks = kBwdParts * ((B + 7) / 8 * 8);
+template <typename T, int P>
+int launch_bwd_parts_p(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipStream_t st) {
+  const int64_t blocks = P * ((B + 7) / 8 * 8);
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL((ce::sm_bwd_part_kernel<T, kBwdParts, 1024, kBwdPartSlots>),
-                     dim3((unsigned)blocks), dim3(1024), 0, st, y, dy, B, (int)C, dx,
+  hipLaunchKernelGGL((ce::sm_bwd_part_kernel<T, P, 1024, kBwdPartSlots>), dim3((unsigned)blocks),
+                     dim3(1024), 0, st, y, dy, B, (int)C, dx,
                      g_part_polls.load(std::memory_order_relaxed),
                      g_part_counter.load(std::memory_order_relaxed));
   return launched();
+}
+
+template <typename T>
+int launch_bwd_parts(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipStream_t st) {
+  if (body_vectors_max(C, sizeof(T)) <= kBwdPartsFour)
+    return launch_bwd_parts_p<T, 4>(y, dy, B, C, dx, st);
+  return launch_bwd_parts_p<T, 8>(y, dy, B, C, dx, st);
 }
 
 template <typename T>

@@ -13,7 +13,8 @@
 // The trade follows the row-part protocol of the cross-entropy kernel
 // (ce_parts.h), with one float per part instead of a (max, sum) pair:
 //  - part p's mailbox is P 64-bit words at the start of its own last two
-//    body vectors in dx; word q receives d_q as [kMailTag | bits(d_q)];
+//    body vectors in dx (four for eight parts); word q receives d_q as
+//    [kMailTag | bits(d_q)];
 //  - first thing, p sets its words to the empty tag; partners publish with
 //    compare-and-swap from the empty tag, repeat the publish on every poll
 //    of their own mailbox, and never wait for a publish's result;
@@ -48,7 +49,13 @@ void sm_bwd_part_kernel(const T* __restrict__ y, const T* __restrict__ dy, int64
                         T* __restrict__ dx, int spin, uint32_t* __restrict__ fallbacks) {
   using E = Elem<T>;
   constexpr int NW = NT / 64, VE = E::VE;
-  static_assert(P >= 2 && P <= 4, "two to four parts per row");
+  static_assert(P == 2 || P == 4 || P == 8, "two, four or eight parts per row");
+  // mailbox vectors at the end of each part: P 64-bit words
+  constexpr int MV = P <= 4 ? 2 : P / 2;
+  // eight parts keep the loops over partners rolled (less code, and no
+  // partner's address held beyond its iteration: the kernel is capped at
+  // 64 VGPRs)
+  constexpr int kUnrollPartners = P <= 4 ? P : 1;
   static_assert(NT % 64 == 0 && NW >= 1 && NW <= 16, "1 to 16 waves");
   __shared__ float red[NW];
   __shared__ float mail[P];
@@ -79,9 +86,11 @@ void sm_bwd_part_kernel(const T* __restrict__ y, const T* __restrict__ dy, int64
     vy[k] = bload128<kPolicyStream>(ry, voff, (uint32_t)k * NT * 16u);
     vd[k] = bload128<kPolicyStream>(rd, voff, (uint32_t)k * NT * 16u);
   }
-  // this part's mailbox: P words at the start of its last two body vectors
-  uint64_t* const mine =
-      reinterpret_cast<uint64_t*>(op + geo.h + (int64_t)(own.v0 + own.len - 2) * VE);
+  // this part's mailbox: P words at the start of its last MV body vectors
+  auto mailbox = [&](const PartRange& pr) {
+    return reinterpret_cast<uint64_t*>(op + geo.h + (int64_t)(pr.v0 + pr.len - MV) * VE);
+  };
+  uint64_t* const mine = mailbox(own);
   constexpr uint64_t kEmptyWord = (uint64_t)kMailEmpty << 32;
   if (tid == 0) {
 #pragma unroll
@@ -118,25 +127,21 @@ void sm_bwd_part_kernel(const T* __restrict__ y, const T* __restrict__ dy, int64
   if (tid == 0) {
     mail[part] = d_own;
     const uint64_t word = ((uint64_t)kMailTag << 32) | __builtin_bit_cast(uint32_t, d_own);
-    uint64_t* theirs[P];
-#pragma unroll
-    for (int q = 0; q < P; ++q) {
-      const PartRange pq = part_range(geo.nb, P, q);
-      theirs[q] = reinterpret_cast<uint64_t*>(op + geo.h + (int64_t)(pq.v0 + pq.len - 2) * VE);
-    }
     auto publish = [&] {
-#pragma unroll
+#pragma unroll kUnrollPartners
       for (int q = 0; q < P; ++q) {
         if (q == part) continue;
         uint64_t e = kEmptyWord;
-        __hip_atomic_compare_exchange_strong(&theirs[q][part], &e, word, __ATOMIC_RELAXED,
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_compare_exchange_strong(&mailbox(part_range(geo.nb, P, q))[part], &e, word,
+                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        wide_store_guard();  // 16 bytes of data, as a wide store
       }
     };
     publish();
     int have = 1;
     for (int it = 0; it < spin && have < P; ++it) {
-#pragma unroll
+#pragma unroll kUnrollPartners
       for (int q = 0; q < P; ++q) {
         if (q == part || got[q]) continue;
         const uint64_t w = __hip_atomic_load(&mine[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -155,7 +160,7 @@ void sm_bwd_part_kernel(const T* __restrict__ y, const T* __restrict__ dy, int64
   }
   __syncthreads();
   // recompute what did not arrive, with the part's own slots and order
-#pragma unroll
+#pragma unroll kUnrollPartners
   for (int q = 0; q < P; ++q) {
     if (got[q]) continue;  // uniform (LDS, after the barrier)
     const PartRange pq = part_range(geo.nb, P, q);

@@ -216,6 +216,8 @@ BWD_SHAPES = [
     (20, 50257, "f32"),
     (9, 128256, "bf16"),
     (3, 200_000, "bf16"),
+    (5, 128256, "f32"),
+    (2, 262_144, "bf16"),
     # path 5: attention-shaped rows, 8- and 4-byte vectors, 8 KB rows
     (77, 2048, "bf16"),
     (45, 300, "bf16"),
@@ -233,7 +235,7 @@ def _bwd_legal(path, C, dtype, in_place=False):
     if path == 2:
         return (C * es + 15) // 16 + 1 <= 8192
     if path == 4:
-        return not in_place and 128 <= C // (16 // es) <= 16384
+        return not in_place and 128 <= C // (16 // es) <= 32768
     if path == 5:
         return wave_bwd_takes(C, es)
     return path in (0, 3)
@@ -387,11 +389,13 @@ def test_softmax_autograd(B, C, dtype):
 
 
 @pytest.mark.parametrize("B,C,dtype", [(16, 128256, "bf16"), (9, 50257, "f32"), (5, 99999, "f16"),
-                                       (33, 70001, "bf16")])
+                                       (33, 70001, "bf16"), (5, 128256, "f32"), (3, 200_000, "bf16"),
+                                       (2, 262_144, "f16")])
 def test_softmax_bwd_parts_fallback_is_bitwise(B, C, dtype):
     """Row parts of the backward with no polls: every part recomputes the
     other parts' partial dots; the bits equal those of the exchange, and the
-    device counter sees every missing partial."""
+    device counter sees every missing partial (four parts up to a body of
+    16384 vectors, eight beyond)."""
     import torch
     ce = _ce()
     if dtype == "f16":
@@ -415,5 +419,6 @@ def test_softmax_bwd_parts_fallback_is_bitwise(B, C, dtype):
     finally:
         ce.part_counter(None)
         ce.part_polls(prev)
-    assert n == B * 4 * 3
+    P = 4 if C // (4 if dtype == "f32" else 8) <= 16384 else 8
+    assert n == B * P * (P - 1)
     assert torch.equal(_bits(dx1), _bits(dx2))
