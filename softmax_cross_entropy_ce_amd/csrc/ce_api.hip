@@ -234,6 +234,53 @@ bool tiny_rows(const T* z, int64_t C, const ce::RowArgs& rs, const T* g, bool gr
          (!grad || (rs.ldg == C && (uintptr_t)g % 16 == 0));
 }
 
+// Contiguous rows in 16-byte aligned arrays whose byte length 16 does not
+// divide (the short kernel would read them with narrower loads): the
+// LDS-staged kernel, persistent over chunks of rows, with the short
+// kernel's segment layout.
+template <typename T>
+bool staged_rows(const T* z, int64_t C, const ce::RowArgs& rs, const T* g, bool grad) {
+  return C * (int64_t)sizeof(T) > ce::kTinyRowBytes && (C * (int64_t)sizeof(T)) % 16 != 0 &&
+         rs.ldz == C && (uintptr_t)z % 16 == 0 &&
+         (!grad || (rs.ldg == C && (uintptr_t)g % 16 == 0));
+}
+
+template <typename T, int S, int EPL, int OP, bool GRAD>
+int launch_staged_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
+                      float* l, hipStream_t st) {
+  auto kern = ce::ce_staged_kernel<T, S, EPL, GRAD, OP>;
+  static std::atomic<int> occupancy{0};
+  const int res = resident_blocks(reinterpret_cast<const void*>(kern), ce::kStagedThreads, occupancy);
+  if (res < 1) return CE_ERR_LAUNCH;
+  const int64_t rows = ce::staged_rows_per_chunk((int)C, (int)sizeof(T), ce::kStagedThreads / S);
+  if (rows < 1 || C > S * EPL) return CE_ERR_PATH;  // a chunk pass and the slots hold a row
+  const int64_t chunks = (B + rows - 1) / rows;
+  const int64_t grid = chunks < res ? chunks : res;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(ce::kStagedThreads), 0, st, z, t, B, (int)C,
+                     rs, g, l);
+  return launched();
+}
+
+// Eight lanes per row up to 128 elements (eight rows per wave share each
+// reduction step), sixteen up to 256; slots per lane in steps of two, so
+// that at most a fifth of them lie past the row's end (rows of more than
+// 64 bytes: C > 16 for fp32, C > 32 for 16-bit types).
+template <typename T, int OP, bool GRAD>
+int launch_staged(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
+                  float* l, hipStream_t st) {
+  if (C <= 48) return launch_staged_cfg<T, 8, 6, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 64) return launch_staged_cfg<T, 8, 8, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 80) return launch_staged_cfg<T, 8, 10, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 96) return launch_staged_cfg<T, 8, 12, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 112) return launch_staged_cfg<T, 8, 14, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 128) return launch_staged_cfg<T, 8, 16, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 160) return launch_staged_cfg<T, 16, 10, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 192) return launch_staged_cfg<T, 16, 12, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 224) return launch_staged_cfg<T, 16, 14, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 256) return launch_staged_cfg<T, 16, 16, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  return CE_ERR_PATH;
+}
+
 // Short-row layout: about 16 bytes per lane.  S lanes per row is the power
 // of two that covers the row with EPL elements per lane (EPL = 16 bytes of
 // elements, more only at S = 16).  Lanes of a row read adjacent vectors,
@@ -242,6 +289,7 @@ template <typename T, int OP, bool GRAD>
 int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g, float* l,
                  hipStream_t st) {
   if (tiny_rows(z, C, rs, g, GRAD)) return launch_tiny<T, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (staged_rows(z, C, rs, g, GRAD)) return launch_staged<T, OP, GRAD>(z, t, B, C, rs, g, l, st);
   if (!short_span_ok(C, rs.ldz, sizeof(T)) || (GRAD && !short_span_ok(C, rs.ldg, sizeof(T))))
     return CE_ERR_PATH;
   constexpr int es = sizeof(T);

@@ -355,6 +355,164 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
 }
 
 // ===========================================================================
+// Path 1, contiguous rows of more than 64 bytes and up to 256 elements whose
+// length in bytes is not a multiple of 16 (odd lengths, for example): the
+// short kernel would read them with 8-, 4- or 2-byte loads.  Here a chunk
+// of rows, which starts on a 16-byte boundary, is staged through LDS with
+// whole 16-byte loads and stores as in the tiny kernel, and each row is
+// reduced by a segment of S lanes as in the short kernel, lane q taking
+// elements q, q+S, ... of its row from LDS.  A chunk holds as many whole
+// passes of 256/S rows as fit kStagedChunkBytes (the count is set at run
+// time from C, so short rows fill the chunk too); with rows of more than 64
+// bytes that is fewer than 256 rows, so each thread loads at most one
+// target per chunk, with the chunk's data.  The workgroups are persistent
+// and keep the loads of the next two chunks in flight in two register sets;
+// the last, partial chunk of a call moves one element per thread.
+// ===========================================================================
+constexpr int kStagedThreads = 256;
+constexpr int kStagedChunkBytes = 16384;  // K = 4 loads per thread and register set
+
+// Rows per chunk for rows of C elements of es bytes: whole passes of rpp
+// rows that fit kStagedChunkBytes (a multiple of 8 rows, since rpp >= 16).
+__host__ __device__ constexpr int staged_rows_per_chunk(int C, int es, int rpp) {
+  return kStagedChunkBytes / (rpp * C * es) * rpp;
+}
+
+// EPL: elements per lane, slots k = 0..EPL-1 at row offsets q + k*S
+// (C <= S * EPL).  Every slot is read unconditionally (the stage has EPL * S
+// elements of slack past the chunk, so a slot past its row's end reads the
+// next row or the slack) and taken as -inf unless q + k*S < C; only the
+// gradient's stores are predicated.  The target's LDS element is replaced
+// by -inf once its value is read, so the terms leave it out of the sum with
+// no test per element (the max takes z_t back in), and its gradient is
+// written over the term's zero afterwards by the segment's first lane.
+template <typename T, int S, int EPL, bool GRAD, int OP = kOpCE>
+__global__ __launch_bounds__(kStagedThreads) void ce_staged_kernel(
+    const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B, int C,
+    RowArgs rs, T* __restrict__ grad, float* __restrict__ loss_rows) {
+  using E = Elem<T>;
+  constexpr int ES = sizeof(T), NT = kStagedThreads;
+  constexpr int RPP = NT / S;  // rows per pass: one per segment
+  constexpr int K = kStagedChunkBytes / (16 * NT);
+  constexpr int SLACK = (S * EPL * ES + 15) / 16;  // vectors past the chunk
+  static_assert(S == 8 || S == 16, "segment size");
+  static_assert(RPP % 8 == 0, "whole passes keep a chunk on a 16-byte boundary");
+  __shared__ u32x4 stage[NT * K + SLACK];
+  __shared__ int32_t stage_t[NT];
+  const float invB = row_invB(rs), gmul = grad_mul(rs);
+  const int tid = threadIdx.x, q = tid % S, seg = tid / S;
+  const uint32_t voff = (uint32_t)tid * 16u;
+  // C * size > 64 bytes: fewer than 256 rows per chunk, at least one pass
+  const int ROWS = staged_rows_per_chunk(C, ES, RPP);
+  const int64_t nchunks = (B + ROWS - 1) / ROWS;
+  const int64_t nfull = B / ROWS;
+  const uint32_t full_bytes = (uint32_t)(ROWS * C * ES);
+  const int nvec = (int)(full_bytes / 16);
+  const int lim = C - q;  // slot k of this lane lies in the row iff k * S < lim
+  int64_t chunk = blockIdx.x;
+  if (chunk >= nchunks) return;  // whole workgroup
+
+  // a full chunk's loads, and the target of its row tid (if any)
+  auto load_full = [&](int64_t ch, u32x4 (&v)[K], int32_t& tg) {
+    const rsrc_t r = make_rsrc(logits + ch * ROWS * C, full_bytes);
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = bload128<kPolicyStream>(r, voff, (uint32_t)k * NT * 16u);
+    if constexpr (OP != kOpSoftmax) {
+      if (tid < ROWS) tg = targets[ch * ROWS + tid];
+    }
+  };
+  const int64_t G = gridDim.x;
+  auto step = [&](u32x4 (&r)[K], int32_t& tg, int64_t ch) {
+    const int64_t row0 = ch * ROWS;
+    const bool full = ch < nfull;
+    const int nrows = full ? ROWS : (int)(B - row0);
+    if (full) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int gv = tid + k * NT;
+        if (gv < nvec) stage[gv] = r[k];
+      }
+      if (tid < ROWS) stage_t[tid] = tg;
+    } else {
+      for (int i = tid; i < nrows * C; i += NT)
+        LdsElem<T>::put(stage, i, E::load1(logits + row0 * C + i));
+      if constexpr (OP != kOpSoftmax) {
+        if (tid < nrows) stage_t[tid] = targets[row0 + tid];
+      }
+    }
+    __syncthreads();
+    if (ch + 2 * G < nfull) load_full(ch + 2 * G, r, tg);
+
+#pragma unroll 1
+    for (int lr = seg; lr < nrows; lr += RPP) {  // whole segments
+      const int64_t row = row0 + lr;
+      const RowTarget rt = row_target_of<OP>(OP != kOpSoftmax ? stage_t[lr] : -1, C, rs);
+      const int t = rt.t;
+      const int base = lr * C + q;  // this lane's element of slot k: base + k * S
+      // the target logit (every lane of the segment reads it), then -inf in
+      // its place
+      float zt = 0.f;
+      if (t >= 0) {
+        zt = LdsElem<T>::get(stage, lr * C + t);
+        if (q == 0) LdsElem<T>::put(stage, lr * C + t, kNegInf);
+      }
+      float f[EPL];
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) {
+        const float x = LdsElem<T>::get(stage, base + k * S);
+        f[k] = k * S < lim ? x : kNegInf;
+      }
+      float m = max_of(f);
+      m = seg_allreduce<S>(m, OpMax{});
+      if (t >= 0) m = __builtin_fmaxf(m, zt);
+      const float cg = m * kLog2e;
+      // the terms, in place
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) f[k] = exp2_hw(__builtin_fmaf(f[k], kLog2e, -cg));
+      const float sx = seg_allreduce<S>(tree_sum(f), OpAdd{});
+      const RowResult rr = row_finish<OP>(cg, sx, zt, rt.valid, rt.ignored, invB, gmul);
+      if (q == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
+      if constexpr (GRAD) {
+        // the terms, scaled, are the gradient; the target's (zero) is then
+        // overwritten with g_t, later in the same wave's program order
+#pragma unroll
+        for (int k = 0; k < EPL; ++k)
+          if (k * S < lim) LdsElem<T>::put(stage, base + k * S, f[k] * rr.scale);
+        if (t >= 0 && q == 0) LdsElem<T>::put(stage, lr * C + t, rr.gt);
+      }
+    }
+    if constexpr (GRAD) {
+      __syncthreads();
+      if (full) {
+        const rsrc_t ro = make_rsrc(grad + row0 * C, full_bytes);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int gv = tid + k * NT;
+          if (gv < nvec) bstore128<kPolicyStream>(stage[gv], ro, voff, (uint32_t)k * NT * 16u);
+        }
+      } else {
+        for (int i = tid; i < nrows * C; i += NT)
+          E::store1(grad + row0 * C + i, LdsElem<T>::get(stage, i));
+      }
+    }
+    __syncthreads();  // the stage is refilled by the next step
+  };
+
+  u32x4 v[K], u[K];
+  int32_t tv = -1, tu = -1;
+  if (chunk < nfull) load_full(chunk, v, tv);
+  if (chunk + G < nfull) load_full(chunk + G, u, tu);
+  for (;;) {
+    step(v, tv, chunk);
+    chunk += G;
+    if (chunk >= nchunks) break;
+    step(u, tu, chunk);
+    chunk += G;
+    if (chunk >= nchunks) break;
+  }
+}
+
+// ===========================================================================
 // Paths 2 and 3: one workgroup of NT threads per row at a time.  The row's
 // aligned body is split into 16-byte vectors; thread i holds vectors i,
 // i+NT, ..., i+(NV-1)NT in registers (NV*16 bytes per thread).  Vectors

@@ -1,0 +1,143 @@
+"""Path 1's LDS-staged kernel (contiguous rows of up to 256 elements whose
+length in bytes 16 does not divide: odd lengths, 100 or 250 bf16 elements,
+50 or 130 fp32 elements) on the GPU against the fp64 oracle.
+
+A chunk of rows is moved between HBM and LDS with whole 16-byte vectors and
+each row is reduced by a segment of 8 or 16 lanes reading its elements from
+LDS.  The kernel is persistent and keeps the loads of two chunks in flight
+in two register sets, so the large cases give every workgroup several
+chunks (more rows than the resident grid holds), both register sets and a
+ragged last chunk; the small ones a single partial chunk.  The loss alone
+and the gradient in place run the same arithmetic: the same bits.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import rne_bf16_bits, softmax_rows
+
+from _parity import bf16_order, full_parity, grad_to_host, to_device, widen_rows
+
+pytestmark = pytest.mark.gpu
+
+# (B, C, dtype): every configuration (8 lanes per row with 6 to 16
+# elements each, 16 lanes with 10 to 16), odd and even lengths, full chunks
+# with a ragged last one, and single partial chunks
+CASES = [
+    (300_001, 33, "bf16"),      # 8 lanes x 6
+    (200_003, 81, "bf16"),      # 8 lanes x 12
+    (100_001, 255, "bf16"),     # 16 lanes x 16
+    (150_001, 129, "bf16"),     # 16 lanes x 10
+    (200_001, 100, "bf16"),     # 8 lanes x 14; 200-byte rows (8-byte vectors on the short kernel)
+    (120_001, 250, "bf16"),
+    (250_001, 17, "f32"),       # 8 lanes x 6
+    (100_003, 101, "f32"),      # 8 lanes x 14
+    (60_001, 255, "f32"),       # 16 lanes x 16
+    (100_000, 50, "f32"),       # 8 lanes x 8; 200-byte rows
+    (90_001, 130, "f32"),       # 16 lanes x 10
+    (150_001, 75, "bf16"),      # 8 lanes x 10
+    (100_001, 127, "bf16"),     # 8 lanes x 16
+    (80_001, 191, "bf16"),      # 16 lanes x 12
+    (70_001, 223, "bf16"),      # 16 lanes x 14
+    (100_001, 63, "f32"),       # 8 lanes x 8
+    (60_001, 93, "f32"),        # 8 lanes x 12
+    (50_001, 119, "f32"),       # 8 lanes x 16
+    (40_001, 171, "f32"),       # 16 lanes x 12
+    (40_001, 213, "f32"),       # 16 lanes x 14
+    (60_001, 77, "f16"),
+    (5, 33, "bf16"),            # one partial chunk
+    (37, 101, "f32"),
+    (1, 255, "bf16"),
+]
+IDS = [f"{b}x{c}-{d}" for b, c, d in CASES]
+
+
+def _ce():
+    import softmax_cross_entropy_ce_amd as ce
+    return ce
+
+
+@pytest.fixture(autouse=True)
+def _auto():
+    ce = _ce()
+    prev = ce.force_path(0)
+    yield
+    ce.force_path(prev)
+
+
+def _bits(x):
+    import torch
+    return x.view(torch.int16 if x.element_size() == 2 else torch.int32)
+
+
+@pytest.mark.parametrize("B,C,dtype", CASES, ids=IDS)
+def test_staged_matches_oracle(B, C, dtype):
+    import torch
+    ce = _ce()
+    es = 4 if dtype == "f32" else 2
+    assert (C * es) % 16 != 0 and C * es > 64
+    assert ce.select_path(C, 0 if dtype == "f32" else 1) == 1
+    z, t = synth.make_inputs(B, C, dtype, 3.0, seed=B + 7 * C)
+    # targets on the first and last element of some rows
+    t[: min(B, 3)] = 0
+    t[-min(B, 3):] = C - 1
+    worst = full_parity(z, t, dtype, where=f"staged {B}x{C} {dtype}")
+    print(f"[staged] {B}x{C} {dtype}: {worst}", flush=True)
+    # the loss alone and the gradient in place: the bits of the full call
+    zd, td = to_device(z, t, dtype)
+    g_full, l_full = ce.fwd_grad(zd, td)
+    l_only = ce.fwd_loss(zd, td)
+    buf = zd.clone()
+    l_in = ce.fwd_grad_inplace_(buf, td)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(l_only), _bits(l_full))
+    assert torch.equal(_bits(l_in), _bits(l_full))
+    assert torch.equal(_bits(buf), _bits(g_full))
+
+
+@pytest.mark.parametrize("B,C,dtype", [(200_003, 81, "bf16"), (100_003, 101, "f32"),
+                                       (77, 255, "bf16")])
+def test_staged_softmax_matches_oracle(B, C, dtype):
+    import torch
+    ce = _ce()
+    z, _ = synth.make_inputs(B, C, dtype, 3.0, seed=C + 5)
+    zd, _ = to_device(z, np.zeros(B, np.int32), dtype)
+    y, lse = ce.softmax_fwd(zd, with_lse=True)
+    torch.cuda.synchronize()
+    yh, lh = grad_to_host(y, dtype), lse.cpu().numpy()
+    step = 1 << 16
+    for lo in range(0, B, step):
+        z64 = widen_rows(z[lo:lo + step], dtype)
+        y_ora, lse_ora = softmax_rows(z64)
+        if dtype == "f32":
+            assert np.abs(yh[lo:lo + step].astype(np.float64) - y_ora).max() <= 1e-6
+        else:
+            assert np.abs(bf16_order(yh[lo:lo + step]) - bf16_order(rne_bf16_bits(y_ora))).max() <= 1
+        tol = 2.0 ** -20 * (np.abs(z64.max(axis=1)) + math.log(C) + 1.0)
+        assert (np.abs(lh[lo:lo + step] - lse_ora) <= tol).all()
+
+
+@pytest.mark.parametrize("B,C,dtype", [(100_001, 99, "bf16"), (50_001, 63, "f32")])
+def test_staged_ignore_index(B, C, dtype):
+    """A quarter of the rows ignored: their loss and gradient are zero, the
+    others match the oracle with the mean over the rows kept."""
+    import torch
+    ce = _ce()
+    z, t = synth.make_inputs(B, C, dtype, 3.0, seed=B + C)
+    rng = np.random.Generator(np.random.PCG64(C))
+    ign = rng.random(B) < 0.25
+    t[ign] = -100
+    zd, td = to_device(z, t, dtype)
+    g, lr = ce.fwd_grad_ex(zd, td, ignore_index=-100)
+    torch.cuda.synchronize()
+    gh, lh = grad_to_host(g, dtype), lr.cpu().numpy()
+    assert (lh[ign] == 0).all()
+    assert (gh[ign].view(np.uint32 if dtype == "f32" else np.uint16) == 0).all()
+    from _parity import compare_block
+    N = int((~ign).sum())
+    compare_block(gh[~ign], lh[~ign], z[~ign], t[~ign], N, dtype, where=f"staged ignore {B}x{C}")
