@@ -348,7 +348,10 @@ int ce_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 /*
  * Kernel paths:
  *   1 short rows  - many rows per 64-lane wavefront, cross-lane DPP
- *                   reductions, no LDS (C <= 256);
+ *                   reductions (C <= 256); contiguous rows in 16-byte
+ *                   aligned arrays of at most 64 bytes, or whose byte
+ *                   length is not a multiple of 16, move through LDS in
+ *                   chunks of whole 16-byte vectors;
  *   2 resident    - one workgroup per row, the row held on chip in
  *                   registers between the reduction and the gradient write,
  *                   so it is read from HBM once and written once;
