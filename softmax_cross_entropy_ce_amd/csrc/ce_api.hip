@@ -96,6 +96,13 @@ int wave_vb_contiguous(int64_t C, int es) {
   return 0;
 }
 
+// Longest row the staged kernel takes on path 2 (a chunk of at least
+// eight rows).  Path 2 runs it for the rows path 5 has no vectors for
+// (16-bit rows of odd length); where path 5 can take a row with 8- or
+// 4-byte vectors it was as fast or faster above about 340 elements, and
+// within a few percent below.
+int64_t staged_max_c(int es) { return (int64_t)ce::kStagedChunkBytes / (8 * es); }
+
 int auto_path(int64_t C, int es) {
   if (C <= kShortMaxC) return kPathShort;
   if (C * es <= (es == 4 ? kWaveAutoMaxBytes32 : kWaveAutoMaxBytes16)) {
@@ -278,6 +285,23 @@ int launch_staged(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArg
   if (C <= 192) return launch_staged_cfg<T, 16, 12, OP, GRAD>(z, t, B, C, rs, g, l, st);
   if (C <= 224) return launch_staged_cfg<T, 16, 14, OP, GRAD>(z, t, B, C, rs, g, l, st);
   if (C <= 256) return launch_staged_cfg<T, 16, 16, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  return CE_ERR_PATH;
+}
+
+// 16-bit rows of 257 to 1024 elements on path 2 (a chunk holds at least
+// eight rows): 32 lanes per row, slots in steps that waste at most a fifth
+// of them.
+
+template <typename T, int OP, bool GRAD>
+int launch_staged_long(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
+                       float* l, hipStream_t st) {
+  static_assert(sizeof(T) == 2, "fp32 rows of this length have path 5");
+  if (C <= 320) return launch_staged_cfg<T, 32, 10, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 384) return launch_staged_cfg<T, 32, 12, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 512) return launch_staged_cfg<T, 32, 16, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 640) return launch_staged_cfg<T, 32, 20, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 768) return launch_staged_cfg<T, 32, 24, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (C <= 1024) return launch_staged_cfg<T, 32, 32, OP, GRAD>(z, t, B, C, rs, g, l, st);
   return CE_ERR_PATH;
 }
 
@@ -487,6 +511,10 @@ int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g
       bool ok = false;
       const RowCfg cfg = resident_cfg(C, es, &ok, GRAD, aligned);
       if (!ok) return CE_ERR_PATH;
+      if constexpr (es == 2) {
+        if (!forced && C > kShortMaxC && C <= staged_max_c(es) && staged_rows(z, C, rs, g, GRAD))
+          return launch_staged_long<T, OP, GRAD>(z, t, B, C, rs, g, l, st);
+      }
       if constexpr (GRAD) {
         if (cfg.nt == 1024 && cfg.nv == 16) return launch_row_lds<T, OP>(z, t, B, C, rs, g, l, st);
       } else {

@@ -259,14 +259,18 @@ struct OpAdd {
   __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
 };
 
-// All-reduce over aligned segments of S lanes (S = 1, 2, 4, 8 or 16).
+// All-reduce over aligned segments of S lanes (S = 1, 2, 4, 8, 16 or 32;
+// the last step swaps the halves of each 32 lanes through ds_swizzle).
 template <int S, typename Op>
 __device__ __forceinline__ float seg_allreduce(float v, Op op) {
-  static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16, "segment size");
+  static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16 || S == 32, "segment size");
   if constexpr (S >= 2) v = op(v, dpp<kDppXor1>(v));
   if constexpr (S >= 4) v = op(v, dpp<kDppXor2>(v));
   if constexpr (S >= 8) v = op(v, dpp<kDppHalfMirror>(v));
   if constexpr (S >= 16) v = op(v, dpp<kDppMirror>(v));
+  if constexpr (S >= 32)
+    v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                    kSwizzleXor16)));
   return v;
 }
 

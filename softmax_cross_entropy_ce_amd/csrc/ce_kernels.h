@@ -355,9 +355,10 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
 }
 
 // ===========================================================================
-// Path 1, contiguous rows of more than 64 bytes and up to 256 elements whose
-// length in bytes is not a multiple of 16 (odd lengths, for example): the
-// short kernel would read them with 8-, 4- or 2-byte loads.  Here a chunk
+// Path 1 (and path 2 up to 1024 elements), contiguous rows of more than 64
+// bytes whose length in bytes is not a multiple of 16 (odd lengths, for
+// example): the short kernel would read them with 8-, 4- or 2-byte loads,
+// the row kernel its head and tail element by element.  Here a chunk
 // of rows, which starts on a 16-byte boundary, is staged through LDS with
 // whole 16-byte loads and stores as in the tiny kernel, and each row is
 // reduced by a segment of S lanes as in the short kernel, lane q taking
@@ -365,7 +366,8 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
 // passes of 256/S rows as fit kStagedChunkBytes (the count is set at run
 // time from C, so short rows fill the chunk too); with rows of more than 64
 // bytes that is fewer than 256 rows, so each thread loads at most one
-// target per chunk, with the chunk's data.  The workgroups are persistent
+// target per chunk, with the chunk's data.  16-bit rows of 257 to 1024
+// elements take 32 lanes each.  The workgroups are persistent
 // and keep the loads of the next two chunks in flight in two register sets;
 // the last, partial chunk of a call moves one element per thread.
 // ===========================================================================
@@ -395,7 +397,7 @@ __global__ __launch_bounds__(kStagedThreads) void ce_staged_kernel(
   constexpr int RPP = NT / S;  // rows per pass: one per segment
   constexpr int K = kStagedChunkBytes / (16 * NT);
   constexpr int SLACK = (S * EPL * ES + 15) / 16;  // vectors past the chunk
-  static_assert(S == 8 || S == 16, "segment size");
+  static_assert(S == 8 || S == 16 || S == 32, "segment size");
   static_assert(RPP % 8 == 0, "whole passes keep a chunk on a 16-byte boundary");
   __shared__ u32x4 stage[NT * K + SLACK];
   __shared__ int32_t stage_t[NT];

@@ -1,6 +1,7 @@
-"""Path 1's LDS-staged kernel (contiguous rows of up to 256 elements whose
-length in bytes 16 does not divide: odd lengths, 100 or 250 bf16 elements,
-50 or 130 fp32 elements) on the GPU against the fp64 oracle.
+"""The LDS-staged kernel (contiguous rows of more than 64 bytes whose length
+in bytes 16 does not divide: on path 1 up to 256 elements, odd lengths or
+100 or 250 bf16 elements or 50 or 130 fp32 elements; on path 2 16-bit rows
+of odd length up to 1024 elements) on the GPU against the fp64 oracle.
 
 A chunk of rows is moved between HBM and LDS with whole 16-byte vectors and
 each row is reduced by a segment of 8 or 16 lanes reading its elements from
@@ -100,8 +101,44 @@ def test_staged_matches_oracle(B, C, dtype):
     assert torch.equal(_bits(buf), _bits(g_full))
 
 
+# 16-bit rows of odd length from 257 to 1024 elements run the same kernel
+# on path 2, 32 lanes per row (10 to 32 elements each)
+LONG_CASES = [
+    (40_001, 257, "bf16"),      # 32 lanes x 10
+    (30_001, 383, "bf16"),      # x 12
+    (20_001, 511, "bf16"),      # x 16
+    (20_001, 601, "bf16"),      # x 20
+    (15_001, 767, "bf16"),      # x 24
+    (10_001, 1001, "bf16"),     # x 32
+    (9_001, 1023, "f16"),
+    (3, 999, "bf16"),           # one partial chunk
+]
+LONG_IDS = [f"{b}x{c}-{d}" for b, c, d in LONG_CASES]
+
+
+@pytest.mark.parametrize("B,C,dtype", LONG_CASES, ids=LONG_IDS)
+def test_staged_long_rows_match_oracle(B, C, dtype):
+    import torch
+    ce = _ce()
+    assert ce.select_path(C, 1) == 2
+    z, t = synth.make_inputs(B, C, dtype, 4.0, seed=B + 3 * C)
+    t[: min(B, 2)] = 0
+    t[-min(B, 2):] = C - 1
+    worst = full_parity(z, t, dtype, where=f"staged long {B}x{C} {dtype}")
+    print(f"[staged] {B}x{C} {dtype}: {worst}", flush=True)
+    zd, td = to_device(z, t, dtype)
+    g_full, l_full = ce.fwd_grad(zd, td)
+    l_only = ce.fwd_loss(zd, td)
+    buf = zd.clone()
+    l_in = ce.fwd_grad_inplace_(buf, td)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(l_only), _bits(l_full))
+    assert torch.equal(_bits(l_in), _bits(l_full))
+    assert torch.equal(_bits(buf), _bits(g_full))
+
+
 @pytest.mark.parametrize("B,C,dtype", [(200_003, 81, "bf16"), (100_003, 101, "f32"),
-                                       (77, 255, "bf16")])
+                                       (77, 255, "bf16"), (20_001, 701, "bf16")])
 def test_staged_softmax_matches_oracle(B, C, dtype):
     import torch
     ce = _ce()
