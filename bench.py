@@ -388,8 +388,10 @@ def run_copy(args) -> None:
                       "GBps": round(2 * n / dt / 1e9, 1), "ms": round(dt * 1e3, 4)}), flush=True)
 
 
-SWEEP_C = (64, 256, 300, 512, 1000, 2048, 3000, 4096, 8192, 12000, 16032, 32000, 50257, 65536,
-           128256, 200000)
+# even lengths at each path's boundaries and typical vocabularies, and odd
+# lengths (no whole 16-byte vectors per row) from 33 to 4095
+SWEEP_C = (33, 64, 81, 101, 255, 256, 300, 301, 512, 1000, 1001, 2047, 2048, 3000, 4095, 4096,
+           8192, 12000, 16032, 32000, 50257, 65536, 128256, 200000)
 
 
 def run_sweep(args) -> None:
