@@ -52,9 +52,9 @@ constexpr int kShortMaxC = 256;
 // one-part, 256-thread configuration of path 4 moved more bytes per second
 // (the two crossed between 8 and 12 KB for bf16 rows, between 4 and 8 KB
 // for fp32 rows).
-// Rows path 5 has no configuration for stay on path 2 up to that size;
-// longer rows go to path 4 while their aligned body fits its largest
-// configuration, then to path 3.
+// Rows path 5 has no configuration for stay on path 2 up to 256 vectors and
+// go to path 4 above; longer rows go to path 4 while their aligned body
+// fits its largest configuration, then to path 3.
 constexpr int64_t kWaveAutoMaxBytes16 = 8192;
 constexpr int64_t kWaveAutoMaxBytes32 = 4096;
 
@@ -103,11 +103,24 @@ int wave_vb_contiguous(int64_t C, int es) {
 // within a few percent below.
 int64_t staged_max_c(int es) { return (int64_t)ce::kStagedChunkBytes / (8 * es); }
 
+// Lanes per row of the staged softmax backward for rows of C elements: the
+// smallest S of 8, 16, 32 with C <= 16 * S and a pass of 256 / S rows within
+// half a staged chunk (0: none).
+int staged_bwd_lanes(int64_t C, int es) {
+  for (int S = 8; S <= 32; S *= 2)
+    if (C <= 16 * S && (int64_t)(256 / S) * C * es <= ce::kStagedBwdChunkBytes) return S;
+  return 0;
+}
+
 int auto_path(int64_t C, int es) {
   if (C <= kShortMaxC) return kPathShort;
   if (C * es <= (es == 4 ? kWaveAutoMaxBytes32 : kWaveAutoMaxBytes16)) {
-    return ce_wave::lane_bytes(C, es, wave_vb_contiguous(C, es)) != 0 ? kPathWave
-                                                                       : kPathResident;
+    if (ce_wave::lane_bytes(C, es, wave_vb_contiguous(C, es)) != 0) return kPathWave;
+    // rows path 5 has no vectors for (16-bit, odd length): path 2 up to 256
+    // vectors, one row part beyond (measured on rows filling 1 GiB: 2001
+    // bf16 elements 4.2 TB/s on path 2 against 3.8 as a part; 2047 elements
+    // 2.9 against 3.8, 4095 elements 3.8 against 5.4)
+    return row_vectors(C, es) <= 256 ? kPathResident : kPathParts;
   }
   if (body_vectors_max(C, es) <= parts_max(es)) return kPathParts;
   return kPathLong;
@@ -781,6 +794,48 @@ int launch_bwd_short_vw(int vw, const T* y, const T* dy, int64_t B, int C, T* dx
   }
 }
 
+// Rows of more than 64 bytes that 16-byte vectors do not divide, with y (and
+// so dy and dx, congruent to it) 16-byte aligned: the LDS-staged backward.
+// S is the smallest of 8, 16 and 32 whose 16 slots cover the row and whose
+// pass of 256/S rows fits half a staged chunk; EPL is 8, 12 or 16.
+bool staged_bwd_rows(const void* y, int64_t C, int es) {
+  return C * es > ce::kTinyRowBytes && (C * es) % 16 != 0 && (uintptr_t)y % 16 == 0 &&
+         staged_bwd_lanes(C, es) > 0;
+}
+
+template <typename T, int S, int EPL>
+int launch_bwd_staged_cfg(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipStream_t st) {
+  auto kern = ce::sm_bwd_staged_kernel<T, S, EPL>;
+  static std::atomic<int> occupancy{0};
+  const int res = resident_blocks(reinterpret_cast<const void*>(kern), ce::kStagedThreads, occupancy);
+  if (res < 1) return CE_ERR_LAUNCH;
+  const int64_t rows = ce::staged_rows_per_chunk((int)C, (int)sizeof(T), ce::kStagedThreads / S,
+                                                 ce::kStagedBwdChunkBytes);
+  if (rows < 1 || C > S * EPL) return CE_ERR_PATH;
+  const int64_t chunks = (B + rows - 1) / rows;
+  const int64_t grid = chunks < res ? chunks : res;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(ce::kStagedThreads), 0, st, y, dy, B, (int)C,
+                     dx);
+  return launched();
+}
+
+template <typename T, int S>
+int launch_bwd_staged_s(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipStream_t st) {
+  if (C <= 8 * S) return launch_bwd_staged_cfg<T, S, 8>(y, dy, B, C, dx, st);
+  if (C <= 12 * S) return launch_bwd_staged_cfg<T, S, 12>(y, dy, B, C, dx, st);
+  return launch_bwd_staged_cfg<T, S, 16>(y, dy, B, C, dx, st);
+}
+
+template <typename T>
+int launch_bwd_staged(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipStream_t st) {
+  switch (staged_bwd_lanes(C, sizeof(T))) {
+    case 8: return launch_bwd_staged_s<T, 8>(y, dy, B, C, dx, st);
+    case 16: return launch_bwd_staged_s<T, 16>(y, dy, B, C, dx, st);
+    case 32: return launch_bwd_staged_s<T, 32>(y, dy, B, C, dx, st);
+    default: return CE_ERR_PATH;
+  }
+}
+
 // The short layout of the loss (S lanes per row, about 16 bytes of each
 // array per lane), with a vector width that all three arrays' rows allow.
 template <typename T>
@@ -877,23 +932,28 @@ int launch_bwd_parts(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipSt
 template <typename T>
 int softmax_bwd_typed(int path, const T* y, const T* dy, int64_t B, int64_t C, T* dx,
                       bool in_place, hipStream_t st) {
+  const bool forced = g_force_path.load(std::memory_order_relaxed) != 0;
   switch (path) {
     case kPathParts:
       if (!bwd_parts_take(C, sizeof(T), in_place)) return CE_ERR_PATH;
       return launch_bwd_parts<T>(y, dy, B, C, dx, st);
     case kPathShort:
+      if (!forced && staged_bwd_rows(y, C, sizeof(T)))
+        return launch_bwd_staged<T>(y, dy, B, C, dx, st);
       return launch_bwd_short<T>(y, dy, B, C, dx, st);
     case kPathResident: {
+      if constexpr (sizeof(T) == 2) {
+        if (!forced && staged_bwd_rows(y, C, sizeof(T)))
+          return launch_bwd_staged<T>(y, dy, B, C, dx, st);
+      }
       const bool aligned = (uintptr_t)y % 16 == 0 && (C * sizeof(T)) % 16 == 0;  // dy, dx: congruent
       const int64_t need = row_need(C, sizeof(T), aligned);
       for (const RowCfg& r : kBwdCfgs)
         if ((int64_t)r.nt * r.nv >= need) return launch_bwd_row<T>(r, y, dy, B, C, dx, st);
       return CE_ERR_PATH;
     }
-    case kPathLong: {
-      const bool forced = g_force_path.load(std::memory_order_relaxed) == kPathLong;
+    case kPathLong:
       return launch_bwd_row<T>(forced ? kBwdLongTestCfg : kBwdLongCfg, y, dy, B, C, dx, st);
-    }
     default:
       return CE_ERR_PATH;
   }

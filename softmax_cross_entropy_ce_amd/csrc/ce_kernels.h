@@ -375,9 +375,10 @@ constexpr int kStagedThreads = 256;
 constexpr int kStagedChunkBytes = 16384;  // K = 4 loads per thread and register set
 
 // Rows per chunk for rows of C elements of es bytes: whole passes of rpp
-// rows that fit kStagedChunkBytes (a multiple of 8 rows, since rpp >= 16).
-__host__ __device__ constexpr int staged_rows_per_chunk(int C, int es, int rpp) {
-  return kStagedChunkBytes / (rpp * C * es) * rpp;
+// rows that fit `bytes` (a multiple of 8 rows, since rpp is).
+__host__ __device__ constexpr int staged_rows_per_chunk(int C, int es, int rpp,
+                                                        int bytes = kStagedChunkBytes) {
+  return bytes / (rpp * C * es) * rpp;
 }
 
 // EPL: elements per lane, slots k = 0..EPL-1 at row offsets q + k*S

@@ -8,9 +8,11 @@
 // float32 arithmetic; each row of y and dy is read from HBM once where the
 // kernel holds it on chip, and dx is written once.
 //
-// Two layouts, as for the loss:
+// Layouts, as for the loss:
 //   short rows   S lanes per row inside a wave (S = 1..16), the dot reduced
-//                over the segment with DPP, nothing in LDS;
+//                over the segment with DPP, nothing in LDS; rows that
+//                16-byte vectors do not divide go through LDS in chunks of
+//                whole 16-byte vectors (the staged layout);
 //   other rows   one workgroup per row at a time, persistent over rows:
 //                thread i holds vectors i, i + NT, ... (NV each of y and
 //                dy) in registers, the dot goes through the wave and an
@@ -77,6 +79,115 @@ __global__ __launch_bounds__(kShortThreads) void sm_bwd_short_kernel(
       for (int w = 0; w < VW; ++w) g[w] = fy[j * VW + w] * (fd[j * VW + w] - dot);
       VecIO<T, VW>::store(ro, rowoff + (uint32_t)c0 * ES, g);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rows of more than 64 bytes whose length in bytes is not a multiple of 16
+// (odd lengths, ...), with y, dy and dx 16-byte aligned: the short kernel
+// would read them with 8-, 4- or 2-byte loads.  As in ce_staged_kernel,
+// chunks of whole passes of 256/S rows move between HBM and LDS with whole
+// 16-byte loads and stores (half that kernel's chunk for each of y and
+// dy), each row is reduced by a segment of S lanes reading slots q, q+S,
+// ... of y and dy from LDS (read unconditionally from a stage with slack,
+// their products taken as 0 past the row's end), and dx is formed in place
+// of y in LDS and leaves with the chunk.  Persistent, with the loads of the
+// next two chunks in flight in two register sets.
+// ---------------------------------------------------------------------------
+constexpr int kStagedBwdChunkBytes = kStagedChunkBytes / 2;
+
+template <typename T, int S, int EPL>
+__global__ __launch_bounds__(kStagedThreads) void sm_bwd_staged_kernel(
+    const T* __restrict__ y, const T* __restrict__ dy, int64_t B, int C, T* __restrict__ dx) {
+  using E = Elem<T>;
+  constexpr int ES = sizeof(T), NT = kStagedThreads;
+  constexpr int RPP = NT / S;
+  constexpr int K = kStagedBwdChunkBytes / (16 * NT);
+  constexpr int SLACK = (S * EPL * ES + 15) / 16;
+  static_assert(S == 8 || S == 16 || S == 32, "segment size");
+  __shared__ u32x4 sy[NT * K + SLACK], sd[NT * K + SLACK];
+  const int tid = threadIdx.x, q = tid % S, seg = tid / S;
+  const uint32_t voff = (uint32_t)tid * 16u;
+  const int ROWS = staged_rows_per_chunk(C, ES, RPP, kStagedBwdChunkBytes);
+  const int64_t nchunks = (B + ROWS - 1) / ROWS;
+  const int64_t nfull = B / ROWS;
+  const uint32_t full_bytes = (uint32_t)(ROWS * C * ES);
+  const int nvec = (int)(full_bytes / 16);
+  const int lim = C - q;  // slot k of this lane lies in the row iff k * S < lim
+  int64_t chunk = blockIdx.x;
+  if (chunk >= nchunks) return;  // whole workgroup
+
+  auto load_full = [&](int64_t ch, u32x4 (&a)[K], u32x4 (&b)[K]) {
+    const rsrc_t ra = make_rsrc(y + ch * ROWS * C, full_bytes);
+    const rsrc_t rb = make_rsrc(dy + ch * ROWS * C, full_bytes);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      a[k] = bload128<kPolicyStream>(ra, voff, (uint32_t)k * NT * 16u);
+      b[k] = bload128<kPolicyStream>(rb, voff, (uint32_t)k * NT * 16u);
+    }
+  };
+  const int64_t G = gridDim.x;
+  auto step = [&](u32x4 (&a)[K], u32x4 (&b)[K], int64_t ch) {
+    const int64_t row0 = ch * ROWS;
+    const bool full = ch < nfull;
+    const int nrows = full ? ROWS : (int)(B - row0);
+    if (full) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int gv = tid + k * NT;
+        if (gv < nvec) {
+          sy[gv] = a[k];
+          sd[gv] = b[k];
+        }
+      }
+    } else {
+      for (int i = tid; i < nrows * C; i += NT) {
+        LdsElem<T>::put(sy, i, E::load1(y + row0 * C + i));
+        LdsElem<T>::put(sd, i, E::load1(dy + row0 * C + i));
+      }
+    }
+    __syncthreads();
+    if (ch + 2 * G < nfull) load_full(ch + 2 * G, a, b);
+
+#pragma unroll 1
+    for (int lr = seg; lr < nrows; lr += RPP) {  // whole segments
+      const int base = lr * C + q;
+      float fy[EPL], fd[EPL], p[EPL];
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) {
+        fy[k] = LdsElem<T>::get(sy, base + k * S);
+        fd[k] = LdsElem<T>::get(sd, base + k * S);
+        p[k] = k * S < lim ? fy[k] * fd[k] : 0.f;
+      }
+      const float dot = seg_allreduce<S>(tree_sum(p), OpAdd{});
+#pragma unroll
+      for (int k = 0; k < EPL; ++k)
+        if (k * S < lim) LdsElem<T>::put(sy, base + k * S, fy[k] * (fd[k] - dot));
+    }
+    __syncthreads();
+    if (full) {
+      const rsrc_t ro = make_rsrc(dx + row0 * C, full_bytes);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int gv = tid + k * NT;
+        if (gv < nvec) bstore128<kPolicyStream>(sy[gv], ro, voff, (uint32_t)k * NT * 16u);
+      }
+    } else {
+      for (int i = tid; i < nrows * C; i += NT) E::store1(dx + row0 * C + i, LdsElem<T>::get(sy, i));
+    }
+    __syncthreads();  // the stages are refilled by the next step
+  };
+
+  u32x4 va[K], vb[K], ua[K], ub[K];
+  if (chunk < nfull) load_full(chunk, va, vb);
+  if (chunk + G < nfull) load_full(chunk + G, ua, ub);
+  for (;;) {
+    step(va, vb, chunk);
+    chunk += G;
+    if (chunk >= nchunks) break;
+    step(ua, ub, chunk);
+    chunk += G;
+    if (chunk >= nchunks) break;
   }
 }
 

@@ -128,15 +128,18 @@ def test_reduce_loss_validation():
     ("short-limit", 256, 0, 1),
     ("just-over-short", 258, 1, 5),
     # path 5 up to 8 KB of 16-bit or 4 KB of fp32 elements, where the row
-    # allows 16-, 8- or 4-byte vectors (16-bit rows of odd length do not);
-    # those stay on path 2, longer rows go to the row parts
+    # allows 16-, 8- or 4-byte vectors (16-bit rows of odd length do not:
+    # those stay on path 2 up to 256 16-byte vectors and take one row part
+    # above); longer rows go to the row parts
     ("wave-limit-f32", 1024, 0, 5),
     ("over-wave-f32", 1025, 0, 4),
     ("wave-limit-bf16", 4096, 1, 5),
     ("over-wave-bf16", 4100, 1, 4),
     ("wave-4-byte-vectors", 1023, 0, 5),
     ("odd-bf16", 257, 1, 2),
-    ("odd-bf16-limit", 4095, 1, 2),
+    ("odd-bf16-resident-limit", 2039, 1, 2),
+    ("odd-bf16-one-part", 2041, 1, 4),
+    ("odd-bf16-limit", 4095, 1, 4),
     ("over-odd-bf16-limit", 4097, 1, 4),
     # four parts of 12 x 1024 vectors (16-bit) or 8 x 1024 (fp32), then
     # eight parts of 8 x 1024 vectors: aligned body of at most 65536 vectors

@@ -178,3 +178,43 @@ def test_staged_ignore_index(B, C, dtype):
     from _parity import compare_block
     N = int((~ign).sum())
     compare_block(gh[~ign], lh[~ign], z[~ign], t[~ign], N, dtype, where=f"staged ignore {B}x{C}")
+
+
+# The softmax backward of such rows: y, dy and dx staged through LDS (8, 16
+# or 32 lanes per row), on path 1 and, for 16-bit rows of 257 to 512
+# elements, on path 2
+BWD_CASES = [
+    (200_001, 33, "bf16"),      # 8 lanes
+    (100_003, 81, "bf16"),      # 8 lanes
+    (60_001, 255, "bf16"),      # 16 lanes
+    (30_001, 301, "bf16"),      # 32 lanes, path 2
+    (20_001, 511, "bf16"),      # 32 lanes, path 2
+    (200_001, 17, "f32"),       # 8 lanes
+    (100_001, 101, "f32"),      # 16 lanes
+    (40_001, 255, "f32"),       # 32 lanes
+    (7, 99, "bf16"),            # one partial chunk
+]
+BWD_IDS = [f"{b}x{c}-{d}" for b, c, d in BWD_CASES]
+
+
+@pytest.mark.parametrize("B,C,dtype", BWD_CASES, ids=BWD_IDS)
+def test_staged_softmax_bwd_matches_oracle(B, C, dtype):
+    import torch
+    from test_gpu_softmax import check_dx, _dev
+    ce = _ce()
+    y = synth.simplex_rows(B, C, dtype, seed=B + C)
+    dy, _ = synth.make_inputs(B, C, dtype, 1.0, seed=B + 2 * C)
+    yd, dyd = _dev(y, dtype), _dev(dy, dtype)
+    dx = ce.softmax_bwd(yd, dyd)
+    torch.cuda.synchronize()
+    r = check_dx(grad_to_host(dx, dtype), widen_rows(y, dtype), widen_rows(dy, dtype), dtype,
+                 f"staged bwd {B}x{C} {dtype}")
+    print(f"[staged] bwd {B}x{C} {dtype}: worst error / bar {r:.3g}", flush=True)
+    # in place of dy and of y: the same bits
+    a = dyd.clone()
+    ce.softmax_bwd_into(yd, a, a)
+    b = yd.clone()
+    ce.softmax_bwd_into(b, dyd, b)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(a), _bits(dx))
+    assert torch.equal(_bits(b), _bits(dx))

@@ -123,7 +123,7 @@ def test_kernels_present(device_asm):
               "ce_reduce_kernel", "ce_part_kernel", "ce_shard_grad_kernel", "ce_scale_kernel",
               "ce_count_kept_kernel", "sm_bwd_short_kernel", "sm_bwd_row_kernel",
               "sm_bwd_part_kernel", "ce_wave_kernel", "sm_bwd_wave_kernel",
-              "ce_shard_grad_tiny_kernel", "ce_staged_kernel"):
+              "ce_shard_grad_tiny_kernel", "ce_staged_kernel", "sm_bwd_staged_kernel"):
         assert k in names, k
 
 
