@@ -368,15 +368,19 @@ int ce_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
  *                   that does not receive a partner's pair in time
  *                   recomputes it with the same code, so the bits do not
  *                   depend on timing.  Automatic above 8 KB of 16-bit or
- *                   4 KB of fp32 elements, up to 1 MB (16-bit C up to
- *                   524288, fp32 C up to 262144).
+ *                   4 KB of fp32 elements (above 4 KB for 16-bit rows of
+ *                   odd length), up to 1 MB (16-bit C up to 524288, fp32 C
+ *                   up to 262144).
  *   5 wave rows   - rows of up to 16 KB (automatic above 256 elements)
  *                   whose starts, lengths and strides allow 16-, 8- or
  *                   4-byte vectors (4-byte ones up to 8 KB; 16-bit rows of
  *                   odd length have none): each 64-lane wavefront holds one
  *                   to eight whole rows in registers, reduces them with DPP
  *                   and writes their outputs from there.  Automatic
- *                   selection runs other such rows on path 2.
+ *                   selection runs other such rows on path 2 up to 256
+ *                   16-byte vectors (16-bit rows of odd length up to 1024
+ *                   elements through the LDS-staged kernel) and as one row
+ *                   part (path 4) above.
  *
  * ce_select_path returns the path ce_fwd_grad takes for (C, dtype) with
  * contiguous rows and 16-byte aligned base pointers, or a negative
