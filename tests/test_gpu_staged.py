@@ -26,26 +26,31 @@ from _parity import bf16_order, full_parity, grad_to_host, to_device, widen_rows
 
 pytestmark = pytest.mark.gpu
 
-# (B, C, dtype): every configuration (8 lanes per row with 6 to 16
-# elements each, 16 lanes with 10 to 16), odd and even lengths, full chunks
-# with a ragged last one, and single partial chunks
+# (B, C, dtype): every configuration (4 lanes per row with 10 to 24
+# elements each, 8 lanes with 10 to 16, 16 lanes with 10 to 16), odd and
+# even lengths, full chunks with a ragged last one, and single partial
+# chunks
 CASES = [
-    (300_001, 33, "bf16"),      # 8 lanes x 6
-    (200_003, 81, "bf16"),      # 8 lanes x 12
+    (300_001, 33, "bf16"),      # 4 lanes x 10
+    (200_003, 81, "bf16"),      # 4 lanes x 24
+    (250_001, 45, "bf16"),      # 4 lanes x 12
+    (200_001, 63, "bf16"),      # 4 lanes x 16
     (100_001, 255, "bf16"),     # 16 lanes x 16
     (150_001, 129, "bf16"),     # 16 lanes x 10
     (200_001, 100, "bf16"),     # 8 lanes x 14; 200-byte rows (8-byte vectors on the short kernel)
     (120_001, 250, "bf16"),
-    (250_001, 17, "f32"),       # 8 lanes x 6
+    (250_001, 17, "f32"),       # 4 lanes x 10
+    (150_001, 47, "f32"),       # 4 lanes x 12
     (100_003, 101, "f32"),      # 8 lanes x 14
     (60_001, 255, "f32"),       # 16 lanes x 16
-    (100_000, 50, "f32"),       # 8 lanes x 8; 200-byte rows
+    (100_000, 50, "f32"),       # 4 lanes x 16; 200-byte rows
     (90_001, 130, "f32"),       # 16 lanes x 10
-    (150_001, 75, "bf16"),      # 8 lanes x 10
+    (150_001, 75, "bf16"),      # 4 lanes x 20
     (100_001, 127, "bf16"),     # 8 lanes x 16
     (80_001, 191, "bf16"),      # 16 lanes x 12
     (70_001, 223, "bf16"),      # 16 lanes x 14
-    (100_001, 63, "f32"),       # 8 lanes x 8
+    (100_001, 63, "f32"),       # 4 lanes x 16
+    (100_001, 77, "f32"),       # 8 lanes x 10
     (60_001, 93, "f32"),        # 8 lanes x 12
     (50_001, 119, "f32"),       # 8 lanes x 16
     (40_001, 171, "f32"),       # 16 lanes x 12
