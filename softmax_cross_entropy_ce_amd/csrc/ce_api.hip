@@ -281,16 +281,25 @@ int launch_staged_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::Ro
   return launched();
 }
 
-// Four lanes per row up to 64 elements (96 for 16-bit types; sixteen rows
-// per wave share each reduction step), eight up to 128, sixteen up to 256;
-// slots per lane in steps that leave at most about a fifth of them past the
-// row's end (rows of more than 64 bytes: C > 16 for fp32, C > 32 for
-// 16-bit types).  Four lanes took fp32 rows of 17-49 elements from 50-84 %
-// of a copy's rate to 74-90 %, bf16 rows of 33-91 from 41-72 % to 62-79 %;
-// from 97 bf16 elements on, eight lanes were faster.
+// Two lanes per row up to 32 fp32 or 64 16-bit elements (rows of at most
+// 128 bytes, so that a pass of 128 rows fits a chunk), four up to 64 (96
+// for 16-bit types), eight up to 128, sixteen up to 256: fewer lanes per
+// row let more rows share each reduction step.  Slots per lane in steps
+// that leave at most about a fifth of them past the row's end (rows of
+// more than 64 bytes: C > 16 for fp32, C > 32 for 16-bit types).  With
+// eight lanes, fp32 rows of 17-49 elements ran at 50-84 % of a copy's rate
+// and bf16 rows of 33-91 at 41-72 %; with two or four, 86-94 % and 70-83 %.
+// From 97 bf16 elements on, eight lanes were faster.
 template <typename T, int OP, bool GRAD>
 int launch_staged(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
                   float* l, hipStream_t st) {
+  if (C <= 32) return launch_staged_cfg<T, 2, 16, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if constexpr (sizeof(T) == 2) {
+    if (C <= 40) return launch_staged_cfg<T, 2, 20, OP, GRAD>(z, t, B, C, rs, g, l, st);
+    if (C <= 48) return launch_staged_cfg<T, 2, 24, OP, GRAD>(z, t, B, C, rs, g, l, st);
+    if (C <= 56) return launch_staged_cfg<T, 2, 28, OP, GRAD>(z, t, B, C, rs, g, l, st);
+    if (C <= 64) return launch_staged_cfg<T, 2, 32, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  }
   if (C <= 40) return launch_staged_cfg<T, 4, 10, OP, GRAD>(z, t, B, C, rs, g, l, st);
   if (C <= 48) return launch_staged_cfg<T, 4, 12, OP, GRAD>(z, t, B, C, rs, g, l, st);
   if (C <= 64) return launch_staged_cfg<T, 4, 16, OP, GRAD>(z, t, B, C, rs, g, l, st);

@@ -366,9 +366,9 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
 // passes of 256/S rows as fit kStagedChunkBytes (the count is set at run
 // time from C, so short rows fill the chunk too); with rows of more than 64
 // bytes that is fewer than 256 rows, so each thread loads at most one
-// target per chunk, with the chunk's data.  Rows of up to 64 elements (96
-// for 16-bit types) take 4 lanes each, 16-bit rows of 257 to 1024 elements
-// 32.  The workgroups are persistent
+// target per chunk, with the chunk's data.  Rows of up to 128 bytes take 2
+// lanes each, up to 64 elements (96 for 16-bit types) 4, 16-bit rows of 257
+// to 1024 elements 32.  The workgroups are persistent
 // and keep the loads of the next two chunks in flight in two register sets;
 // the last, partial chunk of a call moves one element per thread.
 // ===========================================================================
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(kStagedThreads) void ce_staged_kernel(
   constexpr int RPP = NT / S;  // rows per pass: one per segment
   constexpr int K = kStagedChunkBytes / (16 * NT);
   constexpr int SLACK = (S * EPL * ES + 15) / 16;  // vectors past the chunk
-  static_assert(S == 4 || S == 8 || S == 16 || S == 32, "segment size");
+  static_assert(S == 2 || S == 4 || S == 8 || S == 16 || S == 32, "segment size");
   static_assert(RPP % 8 == 0, "whole passes keep a chunk on a 16-byte boundary");
   __shared__ u32x4 stage[NT * K + SLACK];
   __shared__ int32_t stage_t[NT];

@@ -26,20 +26,25 @@ from _parity import bf16_order, full_parity, grad_to_host, to_device, widen_rows
 
 pytestmark = pytest.mark.gpu
 
-# (B, C, dtype): every configuration (4 lanes per row with 10 to 24
-# elements each, 8 lanes with 10 to 16, 16 lanes with 10 to 16), odd and
+# (B, C, dtype): every configuration (2 lanes per row with 16 to 32
+# elements each, 4 lanes with 10 to 24, 8 lanes with 10 to 16, 16 lanes
+# with 10 to 16), odd and
 # even lengths, full chunks with a ragged last one, and single partial
 # chunks
 CASES = [
-    (300_001, 33, "bf16"),      # 4 lanes x 10
+    (300_001, 33, "bf16"),      # 2 lanes x 20
     (200_003, 81, "bf16"),      # 4 lanes x 24
-    (250_001, 45, "bf16"),      # 4 lanes x 12
-    (200_001, 63, "bf16"),      # 4 lanes x 16
+    (250_001, 45, "bf16"),      # 2 lanes x 24
+    (200_001, 49, "bf16"),      # 2 lanes x 28
+    (200_001, 63, "bf16"),      # 2 lanes x 32
     (100_001, 255, "bf16"),     # 16 lanes x 16
     (150_001, 129, "bf16"),     # 16 lanes x 10
+    (150_001, 71, "bf16"),      # 4 lanes x 20
     (200_001, 100, "bf16"),     # 8 lanes x 14; 200-byte rows (8-byte vectors on the short kernel)
     (120_001, 250, "bf16"),
-    (250_001, 17, "f32"),       # 4 lanes x 10
+    (250_001, 17, "f32"),       # 2 lanes x 16
+    (200_001, 31, "f32"),       # 2 lanes x 16
+    (150_001, 39, "f32"),       # 4 lanes x 10
     (150_001, 47, "f32"),       # 4 lanes x 12
     (100_003, 101, "f32"),      # 8 lanes x 14
     (60_001, 255, "f32"),       # 16 lanes x 16
