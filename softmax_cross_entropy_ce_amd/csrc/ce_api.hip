@@ -257,10 +257,15 @@ bool tiny_rows(const T* z, int64_t C, const ce::RowArgs& rs, const T* g, bool gr
 // Contiguous rows in 16-byte aligned arrays whose byte length 16 does not
 // divide (the short kernel would read them with narrower loads): the
 // LDS-staged kernel, persistent over chunks of rows, with the short
-// kernel's segment layout.
+// kernel's segment layout.  It takes them from 33 bytes for 16-bit types
+// (two lanes per row beat the tiny kernel's one thread per row from 17
+// elements on) and from 65 bytes for fp32 (the tiny kernel up to 16
+// elements).
+template <typename T>
+constexpr int64_t kStagedMinBytes = sizeof(T) == 2 ? 32 : ce::kTinyRowBytes;
 template <typename T>
 bool staged_rows(const T* z, int64_t C, const ce::RowArgs& rs, const T* g, bool grad) {
-  return C * (int64_t)sizeof(T) > ce::kTinyRowBytes && (C * (int64_t)sizeof(T)) % 16 != 0 &&
+  return C * (int64_t)sizeof(T) > kStagedMinBytes<T> && (C * (int64_t)sizeof(T)) % 16 != 0 &&
          rs.ldz == C && (uintptr_t)z % 16 == 0 &&
          (!grad || (rs.ldg == C && (uintptr_t)g % 16 == 0));
 }
@@ -342,8 +347,8 @@ int launch_staged_long(const T* z, const int32_t* t, int64_t B, int64_t C, ce::R
 template <typename T, int OP, bool GRAD>
 int launch_short(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g, float* l,
                  hipStream_t st) {
-  if (tiny_rows(z, C, rs, g, GRAD)) return launch_tiny<T, OP, GRAD>(z, t, B, C, rs, g, l, st);
   if (staged_rows(z, C, rs, g, GRAD)) return launch_staged<T, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if (tiny_rows(z, C, rs, g, GRAD)) return launch_tiny<T, OP, GRAD>(z, t, B, C, rs, g, l, st);
   if (!short_span_ok(C, rs.ldz, sizeof(T)) || (GRAD && !short_span_ok(C, rs.ldg, sizeof(T))))
     return CE_ERR_PATH;
   constexpr int es = sizeof(T);

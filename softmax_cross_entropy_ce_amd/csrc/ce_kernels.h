@@ -364,9 +364,9 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
 // reduced by a segment of S lanes as in the short kernel, lane q taking
 // elements q, q+S, ... of its row from LDS.  A chunk holds as many whole
 // passes of 256/S rows as fit kStagedChunkBytes (the count is set at run
-// time from C, so short rows fill the chunk too); with rows of more than 64
-// bytes that is fewer than 256 rows, so each thread loads at most one
-// target per chunk, with the chunk's data.  Rows of up to 128 bytes take 2
+// time from C, so short rows fill the chunk too); with rows of more than 32
+// bytes that is fewer than 512 rows, so each thread loads at most two
+// targets per chunk, with the chunk's data.  Rows of up to 128 bytes take 2
 // lanes each, up to 64 elements (96 for 16-bit types) 4, 16-bit rows of 257
 // to 1024 elements 32.  The workgroups are persistent
 // and keep the loads of the next two chunks in flight in two register sets;
@@ -403,14 +403,15 @@ __global__ __launch_bounds__(kStagedThreads) void ce_staged_kernel(
   constexpr int RPP = NT / S;  // rows per pass: one per segment
   constexpr int K = kStagedChunkBytes / (16 * NT);
   constexpr int SLACK = (S * EPL * ES + 15) / 16;  // vectors past the chunk
+  constexpr int TPT = 2;  // targets per thread and chunk: rows of more than 32 bytes
   static_assert(S == 2 || S == 4 || S == 8 || S == 16 || S == 32, "segment size");
   static_assert(RPP % 8 == 0, "whole passes keep a chunk on a 16-byte boundary");
   __shared__ u32x4 stage[NT * K + SLACK];
-  __shared__ int32_t stage_t[NT];
+  __shared__ int32_t stage_t[NT * TPT];
   const float invB = row_invB(rs), gmul = grad_mul(rs);
   const int tid = threadIdx.x, q = tid % S, seg = tid / S;
   const uint32_t voff = (uint32_t)tid * 16u;
-  // C * size > 64 bytes: fewer than 256 rows per chunk, at least one pass
+  // C * size > 32 bytes: fewer than 512 rows per chunk, at least one pass
   const int ROWS = staged_rows_per_chunk(C, ES, RPP);
   const int64_t nchunks = (B + ROWS - 1) / ROWS;
   const int64_t nfull = B / ROWS;
@@ -420,17 +421,20 @@ __global__ __launch_bounds__(kStagedThreads) void ce_staged_kernel(
   int64_t chunk = blockIdx.x;
   if (chunk >= nchunks) return;  // whole workgroup
 
-  // a full chunk's loads, and the target of its row tid (if any)
-  auto load_full = [&](int64_t ch, u32x4 (&v)[K], int32_t& tg) {
+  // a full chunk's loads, and the targets of its rows tid and tid + NT (if
+  // any)
+  auto load_full = [&](int64_t ch, u32x4 (&v)[K], int32_t (&tg)[TPT]) {
     const rsrc_t r = make_rsrc(logits + ch * ROWS * C, full_bytes);
 #pragma unroll
     for (int k = 0; k < K; ++k) v[k] = bload128<kPolicyStream>(r, voff, (uint32_t)k * NT * 16u);
     if constexpr (OP != kOpSoftmax) {
-      if (tid < ROWS) tg = targets[ch * ROWS + tid];
+#pragma unroll
+      for (int j = 0; j < TPT; ++j)
+        if (tid + j * NT < ROWS) tg[j] = targets[ch * ROWS + tid + j * NT];
     }
   };
   const int64_t G = gridDim.x;
-  auto step = [&](u32x4 (&r)[K], int32_t& tg, int64_t ch) {
+  auto step = [&](u32x4 (&r)[K], int32_t (&tg)[TPT], int64_t ch) {
     const int64_t row0 = ch * ROWS;
     const bool full = ch < nfull;
     const int nrows = full ? ROWS : (int)(B - row0);
@@ -440,12 +444,16 @@ __global__ __launch_bounds__(kStagedThreads) void ce_staged_kernel(
         const int gv = tid + k * NT;
         if (gv < nvec) stage[gv] = r[k];
       }
-      if (tid < ROWS) stage_t[tid] = tg;
+#pragma unroll
+      for (int j = 0; j < TPT; ++j)
+        if (tid + j * NT < ROWS) stage_t[tid + j * NT] = tg[j];
     } else {
       for (int i = tid; i < nrows * C; i += NT)
         LdsElem<T>::put(stage, i, E::load1(logits + row0 * C + i));
       if constexpr (OP != kOpSoftmax) {
-        if (tid < nrows) stage_t[tid] = targets[row0 + tid];
+#pragma unroll
+        for (int j = 0; j < TPT; ++j)
+          if (tid + j * NT < nrows) stage_t[tid + j * NT] = targets[row0 + tid + j * NT];
       }
     }
     __syncthreads();
@@ -507,7 +515,7 @@ __global__ __launch_bounds__(kStagedThreads) void ce_staged_kernel(
   };
 
   u32x4 v[K], u[K];
-  int32_t tv = -1, tu = -1;
+  int32_t tv[TPT] = {-1, -1}, tu[TPT] = {-1, -1};
   if (chunk < nfull) load_full(chunk, v, tv);
   if (chunk + G < nfull) load_full(chunk + G, u, tu);
   for (;;) {

@@ -32,6 +32,10 @@ pytestmark = pytest.mark.gpu
 # even lengths, full chunks with a ragged last one, and single partial
 # chunks
 CASES = [
+    (400_001, 17, "bf16"),      # 2 lanes x 16 (16-bit rows from 33 bytes)
+    (300_001, 31, "bf16"),      # 2 lanes x 16
+    (200_001, 25, "f16"),       # 2 lanes x 16
+    (3, 19, "bf16"),            # one partial chunk
     (300_001, 33, "bf16"),      # 2 lanes x 20
     (200_003, 81, "bf16"),      # 4 lanes x 24
     (250_001, 45, "bf16"),      # 2 lanes x 24
@@ -91,7 +95,7 @@ def test_staged_matches_oracle(B, C, dtype):
     import torch
     ce = _ce()
     es = 4 if dtype == "f32" else 2
-    assert (C * es) % 16 != 0 and C * es > 64
+    assert (C * es) % 16 != 0 and C * es > (32 if es == 2 else 64)
     assert ce.select_path(C, 0 if dtype == "f32" else 1) == 1
     z, t = synth.make_inputs(B, C, dtype, 3.0, seed=B + 7 * C)
     # targets on the first and last element of some rows
