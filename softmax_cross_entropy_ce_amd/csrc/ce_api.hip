@@ -479,8 +479,9 @@ RowCfg resident_cfg(int64_t C, int es, bool* ok, bool grad = true, bool aligned 
 }
 
 // Automatic configuration of a row read for its per-row value only, by the
-// 16-byte vectors it needs.  Up to 4096 vectors (16-bit types) or 1024
-// (float32) the first of kReadCfgs that holds the row; longer rows keep a
+// 16-byte vectors it needs.  Up to 4096 vectors (16-bit types, but see the
+// rows of 65 to 1024 vectors below) or 1024 (float32) the first of
+// kReadCfgs that holds the row; longer rows keep a
 // part of the row on chip and stream the rest, in the configuration that
 // moved the most bytes per second on rows filling 1 GiB: 16-bit rows with
 // 256 threads x 8 slots up to 12288 vectors and 512 x 8 beyond (the
@@ -491,6 +492,12 @@ RowCfg read_cfg(int64_t need, int es) {
   if (es == 2) {
     if (need > 12288) return {512, 8};
     if (need > 4096) return {256, 8};
+    // 16-bit rows of up to 16 KB reach here when path 5 has no vectors for
+    // them (odd lengths, strides or bases): one wave per row, streaming past
+    // 4 vectors per lane, moved 3.7-5.6 TB/s on odd rows of 1025-4095 bf16
+    // elements against 1.1-3.6 for the 256-thread configurations that hold
+    // them
+    if (need > 64 && need <= 1024) return {64, 4};
   } else {
     if (need > 6144) return {1024, 4};
     if (need > 1024) return {128, 16};
