@@ -170,3 +170,31 @@ def test_two_streams_at_once():
     for g, lr in outs:
         assert torch.equal(_bits(g), _bits(g_ref))
         assert torch.equal(_bits(lr), _bits(l_ref))
+
+
+@pytest.mark.parametrize("B,C,dtype,sigma", [(1040, 256000, "f32", 3.0), (1024, 524288, "bf16", 4.0)],
+                         ids=["1040x256000-f32", "1024x524288-bf16"])
+def test_eight_parts_full_grid_sampled(B, C, dtype, sigma):
+    """Eight parts per row on a grid of about 1 GB of logits, so that parts
+    of one row may not all be resident at once (the bounded polls, then the
+    recompute): 34 sampled rows, the first and last among them, against the
+    oracle element by element, and the device counter's recomputed pairs
+    reported."""
+    import torch
+    from _parity import compare_block, grad_to_host
+    ce = _ce()
+    ce.force_path(0)
+    assert _parts(C, dtype) == 8
+    z, t = synth.make_inputs(B, C, dtype, sigma, seed=B + C)
+    z_dev, t_dev = to_device(z, t, dtype)
+    counter = torch.zeros(1, dtype=torch.int32, device=z_dev.device)
+    ce.part_counter(counter)
+    grad, loss_rows = _run(z_dev, t_dev)
+    n = int(counter.item())
+    rng = np.random.Generator(np.random.PCG64(B))
+    rows = np.unique(np.concatenate([[0, B - 1], rng.choice(B, 32, replace=False)]))
+    idx = torch.from_numpy(rows).to(grad.device)
+    g = grad_to_host(grad.index_select(0, idx), dtype)
+    worst, _ = compare_block(g, loss_rows.cpu().numpy()[rows], z[rows], t[rows], B, dtype,
+                             where=f"eight parts {B}x{C} {dtype}")
+    print(f"[parts] {B}x{C} {dtype}: {worst}, recomputed pairs {n}", flush=True)
