@@ -407,7 +407,7 @@ def run_sweep(args) -> None:
     for dt in ("bf16", "f32"):
         tdt = torch.float32 if dt == "f32" else torch.bfloat16
         es = 4 if dt == "f32" else 2
-        for C in SWEEP_C:
+        for C in (args.sweep_c or SWEEP_C):
             B = max(16, (1 << 30) // (C * es) // 16 * 16)
             gen = torch.Generator(device="cuda:0").manual_seed(C)
             z = (torch.randn(B, C, device="cuda:0", generator=gen) * 3).to(tdt)
@@ -449,6 +449,8 @@ def main() -> None:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["ce", "copy", "sweep"], default="ce")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--sweep-c", type=lambda v: tuple(int(x) for x in v.split(",")), default=None,
+                    help="row lengths for --mode sweep, comma-separated (default: the built-in list)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
