@@ -78,7 +78,7 @@ typedef enum {
  *   targets   [B] int32 class indices.  A target outside [0, C) is not an
  *             error: that row's loss and its whole gradient row are NaN.
  *   B, C      1 <= B <= 2^31 - 1, 1 <= C <= CE_MAX_C.
- *   dtype     CE_F32 or CE_BF16.
+ *   dtype     CE_F32, CE_BF16 or CE_F16.
  *   grad_out  [B, C] dtype, fully overwritten with (softmax - onehot) / B.
  *             Contents on entry are ignored; on path 4 with several
  *             parts per row the call also uses 16 bytes per other part of

@@ -32,9 +32,13 @@ constexpr float kLowest = -3.402823466e38f;  // finite start value of a running 
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
-__device__ __forceinline__ float fmax3(float a, float b, float c) {
-  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+// Maxima as IEEE maximum (a NaN operand gives NaN; -0 < +0): one
+// v_maximum3_f32, where fmaxf would first quiet each operand that is not
+// the result of arithmetic (a load, a DPP move) with an extra v_max.
+__device__ __forceinline__ float fmax2(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
 }
+__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmax2(fmax2(a, b), c); }
 
 // ---------------------------------------------------------------------------
 // Buffer resources.  A raw buffer access whose byte offset is at or beyond
@@ -87,6 +91,7 @@ struct Elem;
 template <>
 struct Elem<float> {
   static constexpr int VE = 4;
+  static constexpr unsigned kNegInfWord = 0xFF800000u;  // a 32-bit word of -inf elements
   __device__ static __forceinline__ void unpack(u32x4 v, float (&f)[4]) {
     const f32x4 x = as_f32(v);
     f[0] = x.x;
@@ -121,6 +126,7 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 template <>
 struct Elem<__bf16> {
   static constexpr int VE = 8;
+  static constexpr unsigned kNegInfWord = 0xFF80FF80u;
   __device__ static __forceinline__ void unpack(u32x4 v, float (&f)[8]) {
     f[0] = bf16lo(v.x); f[1] = bf16hi(v.x);
     f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
@@ -170,6 +176,7 @@ __device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
 template <>
 struct Elem<_Float16> {
   static constexpr int VE = 8;
+  static constexpr unsigned kNegInfWord = 0xFC00FC00u;
   __device__ static __forceinline__ void unpack(u32x4 v, float (&f)[8]) {
     f[0] = f16lo(v.x); f[1] = f16hi(v.x);
     f[2] = f16lo(v.y); f[3] = f16hi(v.y);
@@ -232,6 +239,34 @@ __device__ __forceinline__ unsigned pack_word<_Float16>(const float* g) {
 }
 
 // ---------------------------------------------------------------------------
+// Maximum of 16-bit floating-point values (bf16 or fp16) on their bit
+// patterns, two per instruction (v_pk_max_i16 / v_pk_min_i16), with no
+// widening.  Both formats are sign and magnitude, so compared as signed
+// 16-bit integers:
+//  - non-negative values order as their numbers do, and every negative
+//    value (sign bit set) lies below every non-negative one: when a set
+//    holds a value >= +0, its integer maximum is its numeric maximum;
+//  - negative values order in reverse: when every value of a set is
+//    negative, its numeric maximum is its integer minimum.
+// The -inf pattern (bf16 0xFF80, fp16 0xFC00) lies above every finite
+// negative pattern as an integer, so it is never the minimum of a set that
+// holds a finite negative value.
+// ---------------------------------------------------------------------------
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ s16x2 pk_max16(u32x4 w) {
+  const s16x8 h = __builtin_bit_cast(s16x8, w);
+  return __builtin_elementwise_max(__builtin_elementwise_max(h.s01, h.s23),
+                                   __builtin_elementwise_max(h.s45, h.s67));
+}
+__device__ __forceinline__ s16x2 pk_min16(u32x4 w) {
+  const s16x8 h = __builtin_bit_cast(s16x8, w);
+  return __builtin_elementwise_min(__builtin_elementwise_min(h.s01, h.s23),
+                                   __builtin_elementwise_min(h.s45, h.s67));
+}
+
+// ---------------------------------------------------------------------------
 // Cross-lane reductions.  DPP moves inside rows of 16 lanes (quad
 // permutations, half-row and row mirrors) are plain VALU operands; the step
 // across the two 16-lane halves of a 32-lane group uses ds_swizzle, and the
@@ -252,7 +287,7 @@ constexpr int kSwizzleXor16 = 0x401F; // bitmask mode: lane ^ 16 within 32
 
 struct OpMax {
   __device__ __forceinline__ float operator()(float a, float b) const {
-    return __builtin_fmaxf(a, b);
+    return fmax2(a, b);
   }
 };
 struct OpAdd {
@@ -331,7 +366,7 @@ __device__ __forceinline__ float max_of(const float (&a)[N]) {
   int i = 1;
 #pragma unroll
   for (; i + 1 < N; i += 2) m = fmax3(m, a[i], a[i + 1]);
-  if (i < N) m = __builtin_fmaxf(m, a[i]);
+  if (i < N) m = fmax2(m, a[i]);
   return m;
 }
 
@@ -341,7 +376,7 @@ __device__ __forceinline__ float max_of(const float (&a)[N]) {
 template <int N>
 __device__ __forceinline__ void online_fold_e(float& c, float& s, float vmax, const float (&f)[N],
                                               float (&e)[N]) {
-  const float cn = __builtin_fmaxf(c, vmax * kLog2e);
+  const float cn = fmax2(c, vmax * kLog2e);
 #pragma unroll
   for (int i = 0; i < N; ++i) e[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cn));
   s = s * exp2_hw(c - cn) + tree_sum(e);

@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
         for (int c = 0; c < CMAX; ++c) f[c] = c < C ? LdsElem<T>::get(stage, lr * C + c) : kNegInf;
       }
 #pragma unroll
-      for (int c = 0; c < CMAX; ++c) m = __builtin_fmaxf(m, f[c]);
+      for (int c = 0; c < CMAX; ++c) m = fmax2(m, f[c]);
       const float cg = m * kLog2e;
       float e[CMAX];
       float zt = 0.f;
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(kStagedThreads) void ce_staged_kernel(
       }
       float m = max_of(f);
       m = seg_allreduce<S>(m, OpMax{});
-      if (t >= 0) m = __builtin_fmaxf(m, zt);
+      if (t >= 0) m = fmax2(m, zt);
       const float cg = m * kLog2e;
       // the terms, in place
 #pragma unroll

@@ -49,6 +49,8 @@
 // eight parts.
 #pragma once
 
+#include <type_traits>
+
 #include "ce_kernels.h"
 
 namespace ce {
@@ -106,6 +108,24 @@ __device__ __forceinline__ void wg_pair(float c, float s, float* red_c, float* r
 // Vectors a part of ce_part_kernel<T, P, NT, NR, NL, NXW> holds.
 constexpr int part_capacity(int NT, int NR, int NL, int NXW) { return (NR + NL) * NT + NXW * 64; }
 
+// The max / sum pair of a part, in two passes over the data it holds:
+//  1. the thread's maximum over its elements (16-bit types on their bit
+//     patterns, pk_max16, with no widening; fp32 with max3);
+//  2. the sum of 2^(z log2e - c) over them, c = that maximum times log2 e,
+//     one fma and one v_exp_f32 per element, one c for all of the thread's
+//     slots (no rescaling between slots).
+// A partner that recomputes the pair runs the same two passes over the
+// same slots in the same order, so the bits agree whichever way a pair
+// arrives.
+//
+// Gradient of 16-bit types (and of fp32 in eight parts): each element's
+// g = 2^(z log2e - c') with c' = cg - log2(1 / (S B)), the row's scale
+// folded into the exponent, so that an element costs an fma, an exp and
+// half a conversion.  A known upstream factor other than 1 multiplies
+// after the exponential (a power of two then commutes with the rounding).
+// fp32 in up to four parts keeps each element's term in its register slot
+// and multiplies it by 2^(c - cg) / (S B).
+//
 // fallbacks (may be null): a device counter, incremented once by every part
 // that recomputed its partner's pair instead of receiving it.  spin: polls
 // before that happens (0: every part recomputes).  At most 64 VGPRs (eight
@@ -118,8 +138,8 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   const float invB = row_invB(rs), gmul = grad_mul(rs);
   using E = Elem<T>;
   constexpr int NW = NT / 64, VE = E::VE, ES = sizeof(T);
+  constexpr bool k16 = sizeof(T) == 2;
   constexpr int NLS = NL + (NXW > 0 ? 1 : 0);  // LDS slots, the last maybe partial
-  constexpr int NS = NR + NLS;                 // slots per part
   constexpr int NX = NXW * 64;                 // threads with a vector in the partial slot
   static_assert(P == 1 || P == 2 || P == 4 || P == 8, "one, two, four or eight parts per row");
   static_assert(NT % 64 == 0 && NW >= 1 && NW <= 16, "1 to 16 waves");
@@ -205,86 +225,147 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   const float zt_raw = bload_elem<T>(rrow, (uint32_t)(t >= 0 ? t : C) * ES);
 
   // The target element.  The thread whose vectors hold it sets it to -inf
-  // in the loaded data, once, so no slot needs per-element target code; the
-  // part folds z_t into its running max after its slots (the target stays
+  // in the loaded data, once, so no slot needs per-element target code; z_t
+  // enters the maximum of the part whose body holds it (the target stays
   // out of the sum), and the owning thread stores g_t after its vector
   // stores.  Per part q: whether this wave holds the target's vector, and
   // the slot that holds it for the owning thread (-1 for the others).
   struct TargetIn {
     bool wave;
     int k;
+    bool part;  // the part's body holds the target
   };
   auto target_in = [&](const PartRange& pr) -> TargetIn {
     const bool in = t_body && tvec >= pr.v0 && tvec < pr.v0 + pr.len;
     const bool mine = in && (tvec - pr.v0) % NT == tid;
-    return TargetIn{__builtin_amdgcn_ballot_w64(mine) != 0, mine ? (tvec - pr.v0) / NT : -1};
+    return TargetIn{__builtin_amdgcn_ballot_w64(mine) != 0, mine ? (tvec - pr.v0) / NT : -1, in};
   };
   const TargetIn tin = target_in(own);
 
-  // Slot k of part q (this thread's vector k*NT + tid of the part) as
-  // floats.  Slots past the part's end are skipped as a whole (uniform);
-  // lanes past it hold -inf.
-  auto slot_values = [&](const PartRange& pr, const TargetIn& ti, int k, u32x4 w,
-                         float (&f)[VE]) {
+  // Slot k of part q as it enters the pair: the target killed, lanes past
+  // the part's end (last slot only; uniform test) set to -inf.  Slots wholly
+  // past the end are skipped (uniform).
+  auto slot_words = [&](const PartRange& pr, const TargetIn& ti, int k, u32x4 w) -> u32x4 {
     if (ti.wave && ti.k == k) w = E::kill(w, tj);
-    E::unpack(w, f);
     if (k * NT + NT > pr.len) {
+      // a branch, not selects on every slot: only a part's last slot can
+      // reach past its end
+      asm volatile("");
+      constexpr unsigned n = E::kNegInfWord;
       const bool ok = tid < pr.len - k * NT;
-#pragma unroll
-      for (int i = 0; i < VE; ++i) f[i] = ok ? f[i] : kNegInf;
+      w = ok ? w : u32x4{n, n, n, n};
+    }
+    return w;
+  };
+  // Pass 1 state: the thread's maximum.  16-bit types keep packed integer
+  // maxima (pk_max16) and fall back to packed minima when every element
+  // is negative; fp32 keeps a float.
+  struct MaxState {
+    s16x2 hi;   // 16-bit: packed integer maximum
+    s16x2 lo;   // 16-bit: packed integer minimum (second pass, all negative)
+    float f;    // fp32
+  };
+  constexpr short kNegInfBits = (short)(E::kNegInfWord & 0xFFFFu);
+  auto max_init = [&]() {
+    return MaxState{s16x2{(short)-32768, (short)-32768}, s16x2{kNegInfBits, kNegInfBits}, kNegInf};
+  };
+  auto max_add = [&](MaxState& m, u32x4 w) {
+    if constexpr (k16) {
+      m.hi = __builtin_elementwise_max(m.hi, pk_max16(w));
+    } else {
+      const f32x4 x = as_f32(w);
+      m.f = fmax3(fmax3(m.f, x.x, x.y), x.z, x.w);
     }
   };
-  auto fold_slot = [&](const PartRange& pr, const TargetIn& ti, int k, u32x4 w, float& c,
-                       float& s) {
-    if (k * NT >= pr.len) return;
+  auto max_add_neg = [&](MaxState& m, u32x4 w) {
+    if constexpr (k16) m.lo = __builtin_elementwise_min(m.lo, pk_min16(w));
+  };
+  // whether the second (all-negative) pass is needed, and the final value
+  auto max_needs_neg = [&](const MaxState& m) -> bool {
+    if constexpr (k16) return (m.hi.x > m.hi.y ? m.hi.x : m.hi.y) < 0;
+    return false;
+  };
+  auto max_value = [&](const MaxState& m) -> float {
+    if constexpr (k16) {
+      const short h = m.hi.x > m.hi.y ? m.hi.x : m.hi.y;
+      const short b = h >= 0 ? h : (m.lo.x < m.lo.y ? m.lo.x : m.lo.y);
+      return widen_half<T>((unsigned)(unsigned short)b, 0);
+    } else {
+      return m.f;
+    }
+  };
+  // c from the maximum over the slots, the edge element and (in the part
+  // holding it) the target
+  auto pair_c = [&](float m, int e, float x, bool has_t, float zt_) -> float {
+    if (e >= 0) m = fmax2(m, x);
+    if (has_t) m = fmax2(m, zt_);
+    return fmax2(m * kLog2e, kLowest);
+  };
+  // Pass 2 of one slot: its terms and their sum (the slot's words as from
+  // slot_words).
+  auto slot_terms = [&](u32x4 w, float c, float (&e)[VE]) -> float {
     float f[VE];
-    slot_values(pr, ti, k, w, f);
-    online_fold(c, s, max_of(f), f);
+    E::unpack(w, f);
+#pragma unroll
+    for (int i = 0; i < VE; ++i) e[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -c));
+    return tree_sum(e);
   };
-  auto fold_edge = [&](int e, float x, float& c, float& s) {
-    if (e >= 0) {
-      const float one[1] = {(e == t) ? kNegInf : x};
-      online_fold(c, s, x, one);
-    }
-  };
-  // z_t into the running max of the part whose body holds it (max only)
-  auto fold_target_max = [&](const PartRange& pr, float zt_, float& c, float& s) {
-    if (t_body && tvec >= pr.v0 && tvec < pr.v0 + pr.len) {
-      const float none[1] = {kNegInf};
-      online_fold(c, s, zt_, none);
-    }
+  auto edge_term = [&](int e, float x, float c) -> float {
+    return (e >= 0 && e != t) ? exp2_hw(__builtin_fmaf(x, kLog2e, -c)) : 0.f;
   };
 
-  // Phase B: this part's pair.  For fp32, the register slots keep each
-  // element's term 2^(z log2e - c_k) in place of z, with c_k the running max
-  // after slot k, so that the gradient needs one multiply per element.
-  // Eight parts recompute the terms instead: the running maxima, with the
-  // code that trades eight pairs, would not fit the 64 VGPRs.
+  // Phase B: this part's pair.
   constexpr bool kKeepTerms = sizeof(T) == 4 && P <= 4;
-  float ck[NR];
-  float c = kLowest, s = 0.f;
+  const float zt = t >= 0 ? zt_raw : 0.f;
+  // Each phase tests the slots against its own opaque copy of the part's
+  // length: conditions shared between phases would stay live in scalar
+  // registers from pass 1 to the gradient, and the compiler spills them.
+  auto opaque = [](int x) {
+    asm volatile("" : "+s"(x));
+    return x;
+  };
+  MaxState ms = max_init();
+  {
+    const int len = opaque(own.len);
 #pragma unroll
-  for (int k = 0; k < NR; ++k) {
-    ck[k] = c;
-    if (k * NT >= own.len) continue;
-    float f[VE];
-    slot_values(own, tin, k, v[k], f);
-    if constexpr (kKeepTerms) {
-      float e[VE];
-      online_fold_e(c, s, max_of(f), f, e);
-      ck[k] = c;
-      v[k] = as_u32(f32x4{e[0], e[1], e[2], e[3]});
-    } else {
-      online_fold(c, s, max_of(f), f);
+    for (int k = 0; k < NR; ++k) {
+      if (k * NT >= len) continue;
+      v[k] = slot_words(own, tin, k, v[k]);
+      max_add(ms, v[k]);
+    }
+    wait_vmcnt<0>();  // LDS slots (each thread reads its own wave's), edge and target loads
+#pragma unroll
+    for (int p = 0; p < NLS; ++p)
+      if ((NR + p) * NT < len) max_add(ms, slot_words(own, tin, NR + p, lds_slot(p)));
+    if (max_needs_neg(ms)) {
+#pragma unroll
+      for (int k = 0; k < NR; ++k)
+        if (k * NT < len) max_add_neg(ms, v[k]);
+#pragma unroll
+      for (int p = 0; p < NLS; ++p)
+        if ((NR + p) * NT < len) max_add_neg(ms, slot_words(own, tin, NR + p, lds_slot(p)));
     }
   }
-  wait_vmcnt<0>();  // LDS slots, edge and target loads
-#pragma unroll
-  for (int p = 0; p < NLS; ++p) fold_slot(own, tin, NR + p, lds_slot(p), c, s);
   const float xs = xe >= 0 ? xs_raw : kNegInf;
-  const float zt = t >= 0 ? zt_raw : 0.f;
-  fold_edge(xe, xs, c, s);
-  fold_target_max(own, zt, c, s);
+  const float c = pair_c(max_value(ms), xe, xs, tin.part, zt);
+  float s = 0.f;
+  {
+    const int len = opaque(own.len);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      if (k * NT >= len) continue;
+      float e[VE];
+      s = s + slot_terms(v[k], c, e);
+      if constexpr (kKeepTerms) v[k] = as_u32(f32x4{e[0], e[1], e[2], e[3]});
+    }
+#pragma unroll
+    for (int p = 0; p < NLS; ++p) {
+      if ((NR + p) * NT >= len) continue;
+      float e[VE];
+      s = s + slot_terms(slot_words(own, tin, NR + p, lds_slot(p)), c, e);
+    }
+  }
+  s = s + edge_term(xe, xs, c);
   float c_own, s_own;
   wg_pair<NW>(c, s, red_c, red_s, lane, wv, c_own, s_own);
 
@@ -351,21 +432,36 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
 #pragma unroll kUnrollPartners
     for (int q = 0; q < P; ++q) {
       if (q == part || mail_ok[q]) continue;  // uniform (LDS, after the barrier)
-      // Recompute part q's pair: the same slots, fold order, edges and
-      // workgroup reduction as part q runs itself.
+      // Recompute part q's pair: the same slots, passes, edge and workgroup
+      // reduction as part q runs itself, reading its logits again for each
+      // pass.
       const PartRange pq = part_range(geo.nb, P, q);
       const rsrc_t rq = make_rsrc(rp + geo.h + pq.v0 * VE, (uint32_t)pq.len * 16u);
       const TargetIn tq = target_in(pq);
-      float cq = kLowest, sq = 0.f;
-#pragma unroll
-      for (int k = 0; k < NS; ++k) {
-        const u32x4 w = bload128<kPolicyStream>(rq, voff, (uint32_t)k * NT * 16u);
-        fold_slot(pq, tq, k, w, cq, sq);
+      auto load_q = [&](int k) {
+        return slot_words(pq, tq, k, bload128<kPolicyStream>(rq, voff, (uint32_t)k * NT * 16u));
+      };
+      // (rolled loops: one slot's load in flight at a time, beside the
+      // part's own slots held for its gradient)
+      const int nq = (pq.len + NT - 1) / NT;  // slots holding part q's vectors
+      MaxState mq = max_init();
+#pragma unroll 1
+      for (int k = 0; k < nq; ++k) max_add(mq, load_q(k));
+      if (max_needs_neg(mq)) {
+#pragma unroll 1
+        for (int k = 0; k < nq; ++k) max_add_neg(mq, load_q(k));
       }
       const int xq = edge_elem(q);
       const float xqv = bload_elem<T>(rrow, (uint32_t)(xq >= 0 ? xq : C) * ES);
-      fold_edge(xq, xq >= 0 ? xqv : kNegInf, cq, sq);
-      fold_target_max(pq, zt, cq, sq);
+      const float xqs = xq >= 0 ? xqv : kNegInf;
+      const float cq = pair_c(max_value(mq), xq, xqs, tq.part, zt);
+      float sq = 0.f;
+#pragma unroll 1
+      for (int k = 0; k < nq; ++k) {
+        float e[VE];
+        sq = sq + slot_terms(load_q(k), cq, e);
+      }
+      sq = sq + edge_term(xq, xqs, cq);
       float cr, sr;
       wg_pair<NW>(cq, sq, red_c, red_s, lane, wv, cr, sr);
       if (tid == 0) {
@@ -377,7 +473,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
     // Combine the parts' pairs in part order.
     cg = mail_c[0];
 #pragma unroll
-    for (int q = 1; q < P; ++q) cg = __builtin_fmaxf(cg, mail_c[q]);
+    for (int q = 1; q < P; ++q) cg = fmax2(cg, mail_c[q]);
     // the maxima are read from LDS again rather than kept in registers
     if constexpr (P > 4) asm volatile("" ::: "memory");
     sx = mail_s[0] * exp2_hw(mail_c[0] - cg);
@@ -388,35 +484,58 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   if (part == 0 && tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
 
   // Phase C: the gradient of this part from registers and LDS.
-  auto write_slot = [&](int k, u32x4 w) {
-    if (k * NT >= own.len) return;
-    float f[VE], g[VE];
-    E::unpack(w, f);
-#pragma unroll
-    for (int i = 0; i < VE; ++i) g[i] = exp2_hw(__builtin_fmaf(f[i], kLog2e, -cg)) * rr.scale;
-    bstore128<kPolicyStream>(E::pack(g), rout, voff, (uint32_t)k * NT * 16u);
-  };
 #pragma unroll
   for (int k = 0; k < NR; ++k) asm volatile("" : "+v"(v[k]));
+  if constexpr (kKeepTerms) {
+    const float factor = exp2_hw(c - cg) * rr.scale;
+    const int len = opaque(own.len);
 #pragma unroll
-  for (int k = 0; k < NR; ++k) {
-    if constexpr (kKeepTerms) {
-      if (k * NT >= own.len) continue;
-      const float factor = exp2_hw(ck[k] - cg) * rr.scale;
+    for (int k = 0; k < NR; ++k) {
+      if (k * NT >= len) continue;
       const f32x4 e = as_f32(v[k]);
       const f32x4 g = {e.x * factor, e.y * factor, e.z * factor, e.w * factor};
       bstore128<kPolicyStream>(as_u32(g), rout, voff, (uint32_t)k * NT * 16u);
-    } else {
-      write_slot(k, v[k]);
     }
-  }
+    // LDS slots: the same terms formed again
 #pragma unroll
-  for (int p = 0; p < NLS; ++p) {
-    if (p < NL || tid < NX) write_slot(NR + p, lds_slot(p));
-  }
-  if (xe >= 0) {
-    const float g = (xe == t) ? rr.gt : exp2_hw(__builtin_fmaf(xs, kLog2e, -cg)) * rr.scale;
-    E::store1(gp + xe, g);
+    for (int p = 0; p < NLS; ++p) {
+      if ((NR + p) * NT >= len) continue;
+      float e[VE];
+      slot_terms(slot_words(own, tin, NR + p, lds_slot(p)), c, e);
+      const f32x4 g = {e[0] * factor, e[1] * factor, e[2] * factor, e[3] * factor};
+      bstore128<kPolicyStream>(as_u32(g), rout, voff, (uint32_t)(NR + p) * NT * 16u);
+    }
+    if (xe >= 0)
+      E::store1(gp + xe, xe == t ? rr.gt : exp2_hw(__builtin_fmaf(xs, kLog2e, -c)) * factor);
+  } else {
+    // 2^(z log2e - c') = 2^(z log2e - cg) / (S B); an ignored row has
+    // 1/(S B) = 0, so c' = +inf and every element 0; an invalid one NaN
+    const float cp = cg - log2_hw(rr.scale0);
+    auto phase_c = [&](auto unit) {
+      constexpr bool kUnit = decltype(unit)::value;
+      auto grad_of = [&](float x) {
+        const float g = exp2_hw(__builtin_fmaf(x, kLog2e, -cp));
+        return kUnit ? g : g * gmul;
+      };
+      const int len = opaque(own.len);
+      auto write_slot = [&](int k, u32x4 w) {
+        if (k * NT >= len) return;
+        float f[VE], g[VE];
+        E::unpack(w, f);
+#pragma unroll
+        for (int i = 0; i < VE; ++i) g[i] = grad_of(f[i]);
+        bstore128<kPolicyStream>(E::pack(g), rout, voff, (uint32_t)k * NT * 16u);
+      };
+#pragma unroll
+      for (int k = 0; k < NR; ++k) write_slot(k, v[k]);
+#pragma unroll
+      for (int p = 0; p < NLS; ++p) write_slot(NR + p, lds_slot(p));
+      if (xe >= 0) E::store1(gp + xe, xe == t ? rr.gt : grad_of(xs));
+    };
+    if (gmul == 1.0f)
+      phase_c(std::true_type{});
+    else
+      phase_c(std::false_type{});
   }
   // the target's gradient, over the value its vector store wrote there (the
   // same thread, the same address, later in program order)

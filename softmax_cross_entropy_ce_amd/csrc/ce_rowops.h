@@ -107,50 +107,82 @@ __device__ __forceinline__ float grad_mul(const RowArgs& rs) {
 }
 
 // Per-row epilogue shared by all kernels: from the row's (cg, Sx) and the
-// target logit, the gradient scale gmul/(S B), the target's gradient and
-// the per-row loss.
+// target logit, the gradient scale gmul/(S B) and the target's gradient.
+// The per-row value (the loss, or the softmax's log-sum-exp) is formed by
+// row_value only in the thread that stores it: its log1p is a long
+// instruction sequence that the other threads of a row need not run.
 struct RowResult {
   float scale;   // multiply 2^(z log2e - cg) by this to get the gradient
+  float scale0;  // the same without the upstream factor gmul: 1/(S B)
   float gt;      // gradient of the target element
-  float loss;    // per-row loss, already scaled by 1/B
+  float at, sx, invB;  // inputs of the per-row value (softmax: at = cg)
+  int state;     // 0: a result; 1: target out of range (NaN); 2: ignored (0)
 };
 
 __device__ __forceinline__ RowResult row_epilogue(float cg, float sx, float zt, bool valid,
                                                   float invB, float gmul) {
   RowResult r;
-  const float at = __builtin_fmaf(zt, kLog2e, -cg);
-  const float et = exp2_hw(at);
-  const float S = sx + et;
-  const float scale = invB / S * gmul;
-  float lossB;
-  if (at > -60.f)
-    lossB = log1pf(sx * exp2_hw(-at));
-  else
-    lossB = kLn2 * (log2_hw(S) - at);
+  r.at = __builtin_fmaf(zt, kLog2e, -cg);
+  const float S = sx + exp2_hw(r.at);
+  const float scale0 = invB / S;
   const float qnan = __builtin_nanf("");
-  r.scale = valid ? scale : qnan;
-  r.gt = valid ? -sx * scale : qnan;
-  r.loss = valid ? lossB * invB : qnan;
+  r.scale0 = valid ? scale0 : qnan;
+  r.scale = valid ? scale0 * gmul : qnan;
+  r.gt = valid ? -sx * r.scale : qnan;
+  r.sx = sx;
+  r.invB = invB;
+  r.state = valid ? 0 : 1;
   return r;
+}
+
+// The per-row loss of a CE row, already scaled by 1/B: ln(S / E_t), as
+// log1p(Sx / E_t) while E_t is not tiny (full relative accuracy when the
+// target holds almost all of the mass), else ln2 (log2 S - a_t).
+__device__ __forceinline__ float row_loss(const RowResult& r) {
+  if (r.state == 2) return 0.f;
+  if (r.state == 1) return __builtin_nanf("");
+  float lossB;
+  if (r.at > -60.f)
+    lossB = log1pf(r.sx * exp2_hw(-r.at));
+  else
+    lossB = kLn2 * (log2_hw(r.sx + exp2_hw(r.at)) - r.at);
+  return lossB * r.invB;
 }
 
 // The epilogue of each operation.  CE: row_epilogue, and an ignored row
 // gets scale, target gradient and loss 0.  Softmax: scale = 1 / S (the
-// target fields are unused, S = sx) and loss = lse = ln2 * (cg + log2 S).
-// Shard records need no epilogue.
+// target fields are unused, S = sx) and the per-row value is the
+// log-sum-exp ln2 * (cg + log2 S).  Shard records need no epilogue.
 template <int OP>
 __device__ __forceinline__ RowResult row_finish(float cg, float sx, float zt, bool valid,
                                                 bool ignored, float invB, float gmul) {
   if constexpr (OP == kOpCE) {
     RowResult r = row_epilogue(cg, sx, zt, valid, invB, gmul);
-    if (ignored) r.scale = r.gt = r.loss = 0.f;
+    if (ignored) {
+      r.scale = r.scale0 = r.gt = 0.f;
+      r.state = 2;
+    }
     return r;
   } else {
     RowResult r;
-    r.scale = OP == kOpSoftmax ? 1.0f / sx : 0.f;
+    r.scale = r.scale0 = OP == kOpSoftmax ? 1.0f / sx : 0.f;
     r.gt = 0.f;
-    r.loss = OP == kOpSoftmax ? kLn2 * (cg + log2_hw(sx)) : 0.f;
+    r.at = cg;
+    r.sx = sx;
+    r.invB = invB;
+    r.state = 0;
     return r;
+  }
+}
+
+// The per-row value of each operation, evaluated where it is stored: CE
+// the loss, softmax the log-sum-exp.
+template <int OP>
+__device__ __forceinline__ float row_value(const RowResult& r) {
+  if constexpr (OP == kOpCE) {
+    return row_loss(r);
+  } else {
+    return kLn2 * (r.at + log2_hw(r.sx));
   }
 }
 
@@ -161,9 +193,9 @@ template <int OP>
 __device__ __forceinline__ void store_row(float* out, int64_t row, const RowResult& rr, float cg,
                                           float sx, float zt, bool has_t) {
   if constexpr (OP == kOpCE) {
-    out[row] = rr.loss;
+    out[row] = row_value<OP>(rr);
   } else if constexpr (OP == kOpSoftmax) {
-    if (out != nullptr) out[row] = rr.loss;
+    if (out != nullptr) out[row] = row_value<OP>(rr);
   } else {
     const f32x4 rec = {cg, sx, has_t ? zt : 0.f, has_t ? 1.f : 0.f};
     *reinterpret_cast<f32x4*>(out + 4 * row) = rec;

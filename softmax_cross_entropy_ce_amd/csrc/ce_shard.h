@@ -32,7 +32,7 @@ struct ShardRow {
 __device__ __forceinline__ ShardRow shard_combine(const f32x4* __restrict__ recs, int nshards,
                                                   int64_t B, int64_t row) {
   ShardRow r{kLowest, 0.f, 0.f, 0.f};
-  for (int k = 0; k < nshards; ++k) r.c = __builtin_fmaxf(r.c, recs[(int64_t)k * B + row].x);
+  for (int k = 0; k < nshards; ++k) r.c = fmax2(r.c, recs[(int64_t)k * B + row].x);
   for (int k = 0; k < nshards; ++k) {
     const f32x4 q = recs[(int64_t)k * B + row];
     r.sx = r.sx + q.y * exp2_hw(q.x - r.c);
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kShardThreads) void ce_shard_grad_kernel(
   const int64_t tg = targets[row];
   const bool valid = tg >= 0 && tg < Ctot && sr.own == 1.f;
   const RowResult rr = row_epilogue(c, sr.sx, sr.zt, valid, rs.invB, grad_mul(rs));
-  if (loss_rows != nullptr && chunk == 0 && tid == 0) loss_rows[row] = rr.loss;
+  if (loss_rows != nullptr && chunk == 0 && tid == 0) loss_rows[row] = row_loss(rr);
 
   // the target's column in this shard, if it is here: body vector tvec
   // (element tj) or an edge element
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void ce_shard_grad_tiny_kernel(
   const int64_t tg = targets[row];
   const bool valid = tg >= 0 && tg < Ctot && sr.own == 1.f;
   const RowResult rr = row_epilogue(sr.c, sr.sx, sr.zt, valid, rs.invB, grad_mul(rs));
-  if (loss_rows != nullptr) loss_rows[row] = rr.loss;
+  if (loss_rows != nullptr) loss_rows[row] = row_loss(rr);
   const T* rp = logits + row * rs.ldz;
   T* gp = grad + row * rs.ldg;
   const int64_t tl = tg - col0;

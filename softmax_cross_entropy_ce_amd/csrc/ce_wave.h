@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kWaveThreads) void ce_wave_kernel(const T* __restri
       float f[VW];
       widen_vec<T, VB>(w[r][j], f);
       const float vm = max_of(f);
-      m = j * 64 + lane < nvec ? __builtin_fmaxf(m, vm) : m;
+      m = j * 64 + lane < nvec ? fmax2(m, vm) : m;
       if (j == ts[r]) {  // uniform
 #pragma unroll
         for (int k = 0; k < RV::kWords; ++k) zw = k == tj[r] / PER ? RV::word(w[r][j], k) : zw;
