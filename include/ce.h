@@ -18,7 +18,8 @@
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers owned by the caller.  The
  *    library allocates nothing and keeps no mutable state (apart from the
- *    test-only hooks at the end).
+ *    test-only hooks at the end, and the 4 KB per GPU that
+ *    ce_reduce_loss_noalloc holds).
  *  - Calls are asynchronous and ordered on `stream` (a hipStream_t passed as
  *    void*; NULL means the default stream).  No call synchronises the
  *    device or copies data to the host.
@@ -217,6 +218,34 @@ size_t ce_reduce_workspace_bytes(int64_t B);
  */
 int ce_reduce_loss(const float* loss_rows, int64_t B, float* loss_scalar_out,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Largest B that ce_reduce_loss_noalloc accepts. */
+#define CE_NOALLOC_MAX_ROWS ((int64_t)2147483647)
+
+/*
+ * ce_reduce_loss_noalloc - ce_reduce_loss without a workspace argument, for
+ * callers that cannot allocate device memory: code recorded under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ *   loss_rows, B, loss_scalar_out, stream   as ce_reduce_loss;
+ *                                            1 <= B <= CE_NOALLOC_MAX_ROWS.
+ *
+ * The first level's partial sums go to a scratch array of 1024 floats
+ * (4 KB) that the library holds in device memory, one copy per GPU, from
+ * its first use on that GPU until the process ends.  The call allocates
+ * nothing: the array's device address is looked up once per device (on
+ * the first call made with that device current) and cached.  The kernels
+ * and the tree are those of ce_reduce_loss, so the scalar is bitwise the
+ * same.  Every call on a GPU shares that GPU's array: calls whose
+ * executions overlap on one GPU (other streams, other host threads) race
+ * and may return wrong sums; calls ordered on one stream are safe.
+ *
+ * Returns CE_OK, CE_ERR_NULL, CE_ERR_SHAPE (B out of range), CE_ERR_ALIGN,
+ * or CE_ERR_LAUNCH (a failed launch, or the runtime could not give the
+ * scratch array's address).
+ */
+int ce_reduce_loss_noalloc(const float* loss_rows, int64_t B, float* loss_scalar_out,
+                           void* stream);
 
 /*
  * ce_softmax_fwd - row-wise softmax and log-sum-exp.

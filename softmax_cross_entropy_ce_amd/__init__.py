@@ -29,6 +29,7 @@ import os
 __all__ = [
     "CEError", "lib", "fwd_grad", "fwd_grad_into", "reduce_loss", "reduce_loss_into",
     "cross_entropy", "cross_entropy_loss", "fwd_grad_scaled_into", "scale_grad_",
+    "reduce_loss_noalloc_into",
     "fwd_loss", "fwd_loss_into", "fwd_grad_inplace_",
     "softmax_fwd", "softmax_fwd_into", "softmax_bwd", "softmax_bwd_into", "softmax",
     "shard_stats", "shard_stats_into", "shard_grad", "shard_grad_into",
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.ce_reduce_workspace_bytes.restype = sz
     L.ce_reduce_loss.argtypes = [vp, i64, vp, vp, sz, vp]
     L.ce_reduce_loss.restype = i32
+    L.ce_reduce_loss_noalloc.argtypes = [vp, i64, vp, vp]
+    L.ce_reduce_loss_noalloc.restype = i32
     L.ce_status_string.argtypes = [i32]
     L.ce_status_string.restype = ctypes.c_char_p
     L.ce_version.argtypes = []
@@ -413,6 +416,21 @@ def reduce_loss_into(loss_rows, out, workspace=None) -> None:
     st = lib().ce_reduce_loss(loss_rows.data_ptr(), B, out.data_ptr(), wptr, wbytes,
                               _stream_ptr(loss_rows.device))
     _check(st, "ce_reduce_loss")
+
+
+def reduce_loss_noalloc_into(loss_rows, out) -> None:
+    """ce_reduce_loss_noalloc: the sum into ``out`` with no workspace (the
+    library's per-GPU scratch holds the partial sums; calls that overlap on
+    one GPU race)."""
+    torch = _torch()
+    _check_cuda(loss_rows, out)
+    if loss_rows.dtype != torch.float32 or loss_rows.dim() != 1:
+        raise TypeError("loss_rows must be a float32 vector")
+    if out.dtype != torch.float32 or out.numel() != 1:
+        raise TypeError("out must be one float32")
+    st = lib().ce_reduce_loss_noalloc(loss_rows.data_ptr(), loss_rows.shape[0], out.data_ptr(),
+                                      _stream_ptr(loss_rows.device))
+    _check(st, "ce_reduce_loss_noalloc")
 
 
 def reduce_loss(loss_rows):

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <stdint.h>
 
 #include "ce.h"
@@ -607,6 +608,7 @@ bool overlaps(uintptr_t a, uintptr_t an, uintptr_t b, uintptr_t bn) {
 constexpr int64_t kReduceOneLaunch = 16384;
 constexpr int64_t kReduceMinChunk = 2048;
 constexpr int64_t kReduceMaxBlocks = 1024;
+constexpr int kMaxDevicesReduce = 64;
 
 int64_t reduce_chunk(int64_t B) {
   if (B <= kReduceOneLaunch) return kReduceOneLaunch;
@@ -617,6 +619,41 @@ int64_t reduce_chunk(int64_t B) {
 }
 
 int64_t reduce_blocks(int64_t B) { return (B + reduce_chunk(B) - 1) / reduce_chunk(B); }
+
+// Launch the reduction of B per-row values into *out: one workgroup up to
+// kReduceOneLaunch rows, else a first level of reduce_blocks(B) workgroups
+// writing their partial sums into part, then one workgroup over those.
+int launch_reduce(const float* rows, int64_t B, float* out, float* part, hipStream_t st);
+
+// Device scratch of ce_reduce_loss_noalloc: the first level's partial sums,
+// kReduceMaxBlocks floats (4 KB), one copy per GPU for the life of the
+// process.  Host code never uses the array's name as a device address: the
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and is cached here per device.
+__device__ __align__(256) float reduce_scratch[kReduceMaxBlocks];
+std::atomic<float*> g_reduce_scratch[kMaxDevicesReduce];
+std::mutex g_reduce_scratch_mu;
+
+// The current device's copy of reduce_scratch; CE_ERR_LAUNCH when the
+// runtime cannot give its address.
+int reduce_scratch_ptr(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevicesReduce) return CE_ERR_LAUNCH;
+  float* p = g_reduce_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_reduce_scratch_mu);
+    p = g_reduce_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(reduce_scratch)) != hipSuccess || addr == nullptr)
+        return CE_ERR_LAUNCH;
+      p = static_cast<float*>(addr);
+      g_reduce_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return CE_OK;
+}
 
 }  // namespace
 
@@ -1022,6 +1059,21 @@ int launch_shard_grad(const T* z, const int32_t* t, int64_t B, int64_t C, int64_
   return launched();
 }
 
+int launch_reduce(const float* rows, int64_t B, float* out, float* part, hipStream_t st) {
+  const int64_t blocks = reduce_blocks(B);
+  if (blocks == 1) {
+    hipLaunchKernelGGL(ce::ce_reduce_kernel, dim3(1), dim3(ce::kReduceThreads), 0, st, rows, B, B,
+                       out);
+    return launched();
+  }
+  hipLaunchKernelGGL(ce::ce_reduce_kernel, dim3((unsigned)blocks), dim3(ce::kReduceThreads), 0, st,
+                     rows, B, reduce_chunk(B), part);
+  if (launched() != CE_OK) return CE_ERR_LAUNCH;
+  hipLaunchKernelGGL(ce::ce_reduce_kernel, dim3(1), dim3(ce::kReduceThreads), 0, st,
+                     (const float*)part, blocks, blocks, out);
+  return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -1177,20 +1229,21 @@ int ce_reduce_loss(const float* loss_rows, int64_t B, float* loss_scalar_out, vo
   const size_t need = ce_reduce_workspace_bytes(B);
   if (need && (!workspace || workspace_bytes < need)) return CE_ERR_WORKSPACE;
   if (need && (uintptr_t)workspace % 4) return CE_ERR_ALIGN;
-  const hipStream_t st = as_stream(stream);
-  const int64_t blocks = reduce_blocks(B);
-  if (blocks == 1) {
-    hipLaunchKernelGGL(ce::ce_reduce_kernel, dim3(1), dim3(ce::kReduceThreads), 0, st, loss_rows,
-                       B, B, loss_scalar_out);
-    return launched();
+  return launch_reduce(loss_rows, B, loss_scalar_out, (float*)workspace, as_stream(stream));
+}
+
+int ce_reduce_loss_noalloc(const float* loss_rows, int64_t B, float* loss_scalar_out,
+                           void* stream) {
+  if (!loss_rows || !loss_scalar_out) return CE_ERR_NULL;
+  if (B <= 0 || B > CE_NOALLOC_MAX_ROWS) return CE_ERR_SHAPE;
+  if ((uintptr_t)loss_rows % 4 || (uintptr_t)loss_scalar_out % 4) return CE_ERR_ALIGN;
+  float* part = nullptr;
+  if (reduce_blocks(B) > 1) {
+    if (reduce_blocks(B) > kReduceMaxBlocks) return CE_ERR_SHAPE;
+    const int rc = reduce_scratch_ptr(&part);
+    if (rc != CE_OK) return rc;
   }
-  float* part = (float*)workspace;
-  hipLaunchKernelGGL(ce::ce_reduce_kernel, dim3((unsigned)blocks), dim3(ce::kReduceThreads), 0, st,
-                     loss_rows, B, reduce_chunk(B), part);
-  if (launched() != CE_OK) return CE_ERR_LAUNCH;
-  hipLaunchKernelGGL(ce::ce_reduce_kernel, dim3(1), dim3(ce::kReduceThreads), 0, st,
-                     (const float*)part, blocks, blocks, loss_scalar_out);
-  return launched();
+  return launch_reduce(loss_rows, B, loss_scalar_out, part, as_stream(stream));
 }
 
 const char* ce_status_string(int status) {

@@ -40,7 +40,8 @@ def test_library_exports_every_declared_function():
                             "ce_debug_part_counter", "ce_stream_copy",
                             "ce_fwd_grad_scaled", "ce_scale_grad", "ce_fwd_loss",
                             "ce_softmax_fwd", "ce_softmax_bwd", "ce_shard_stats",
-                            "ce_shard_grad", "ce_fwd_grad_ex", "ce_fwd_workspace_bytes"])
+                            "ce_shard_grad", "ce_fwd_grad_ex", "ce_fwd_workspace_bytes",
+                            "ce_reduce_loss_noalloc"])
     for n in names:
         assert hasattr(L_, n), n
 
@@ -115,6 +116,20 @@ def test_reduce_loss_validation():
     need = ce.reduce_workspace_bytes(1 << 20)
     assert red(B=1 << 20, ws=T, wsb=need - 1) == WORKSPACE  # too small
     assert red(B=1 << 20, ws=T + 2, wsb=need) == ALIGN
+
+
+def test_reduce_loss_noalloc_validation():
+    """Refusals happen on the host, before any HIP call (so they run here
+    without a GPU): NULL pointers, B outside [1, CE_NOALLOC_MAX_ROWS],
+    misaligned pointers."""
+    f = ce.lib().ce_reduce_loss_noalloc
+    assert f(None, 8, G, None) == NULL
+    assert f(L, 8, None, None) == NULL
+    assert f(L, 0, G, None) == SHAPE
+    assert f(L, -1, G, None) == SHAPE
+    assert f(L, (1 << 31), G, None) == SHAPE
+    assert f(L + 2, 8, G, None) == ALIGN
+    assert f(L, 8, G + 1, None) == ALIGN
 
 
 @pytest.mark.parametrize("name,C,dtype,path", [
