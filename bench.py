@@ -65,6 +65,102 @@ def traffic_for(workload: str):
     return None if w is None else w.get("hbm_bytes_per_launch")
 
 
+class HipEvents:
+    """HIP events created through the HIP runtime that the library and
+    torch share (resolved through the library's handle), for
+    ce_debug_time_next_launch: the library's next launch records them at
+    the kernel's own start and end, with no event packets between the
+    kernels of the timed loop."""
+
+    def __init__(self):
+        import ctypes
+        import softmax_cross_entropy_ce_amd as ce
+        self._c = ctypes
+        L = ce.lib()
+        self.L = L
+        L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        L.hipEventCreateWithFlags.restype = ctypes.c_int
+        L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        L.hipEventElapsedTime.restype = ctypes.c_int
+        L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        L.hipEventDestroy.restype = ctypes.c_int
+        self.events = []
+
+    def pairs(self, n: int):
+        out = []
+        for _ in range(n):
+            pair = []
+            for _ in range(2):
+                ev = self._c.c_void_p()
+                if self.L.hipEventCreateWithFlags(self._c.byref(ev), 0) != 0:
+                    raise RuntimeError("hipEventCreateWithFlags failed")
+                self.events.append(ev)
+                pair.append(ev)
+            out.append(tuple(pair))
+        return out
+
+    def arm(self, pair) -> None:
+        """The library's next launch on this thread records this pair."""
+        self.L.ce_debug_time_next_launch(pair[0], pair[1])
+
+    def ms(self, pair) -> float:
+        v = self._c.c_float()
+        if self.L.hipEventElapsedTime(self._c.byref(v), pair[0], pair[1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(v.value)
+
+    def close(self) -> None:
+        for ev in self.events:
+            self.L.hipEventDestroy(ev)
+        self.events = []
+
+
+# A timed kernel launch costs the step about 7 us (measured on lmhead128k:
+# 692 us per step without events, 699 us with a pair on every ce_fwd_grad,
+# whether recorded by torch around the call or attached to the launch): the
+# timestamps are taken after a system-scope release at the kernel's end.
+# The timed loop therefore attaches a pair to every EVENT_EVERY-th step.
+EVENT_EVERY = 5
+
+
+def time_steps(zd, td, grad, loss_rows, loss, ws, steps: int, warmup: int) -> dict:
+    """W untimed steps, then K steps timed by the wall clock between two
+    device synchronisations.  Every EVENT_EVERY-th timed ce_fwd_grad launch
+    (from the first) records a pair of HIP events at its kernel's own start
+    and end (ce_debug_time_next_launch) on the stream it runs on; those
+    give the kernel's duration."""
+    import torch
+    import softmax_cross_entropy_ce_amd as ce
+    hev = HipEvents()
+    timed = list(range(0, steps, EVENT_EVERY))
+    pairs = dict(zip(timed, hev.pairs(len(timed))))
+    for _ in range(warmup):
+        ce.fwd_grad_into(zd, td, grad, loss_rows)
+        ce.reduce_loss_into(loss_rows, loss, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        pr = pairs.get(i)
+        if pr is not None:
+            hev.arm(pr)
+        ce.fwd_grad_into(zd, td, grad, loss_rows)
+        ce.reduce_loss_into(loss_rows, loss, ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [hev.ms(pairs[i]) for i in timed]
+    # ce_reduce_loss alone, after the timed region, timed the same way
+    rpairs = hev.pairs(20)
+    for pr in rpairs:
+        hev.arm(pr)
+        ce.reduce_loss_into(loss_rows, loss, ws)
+    torch.cuda.synchronize()
+    red_ms = [hev.ms(pr) for pr in rpairs]
+    hev.close()
+    return {"ms_per_step": wall * 1e3 / steps, "fwd_ms": fwd_ms, "red_ms": red_ms,
+            "timed_region_s": wall, "timed_steps": timed}
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -102,7 +198,16 @@ def cpu_baseline(z, t, dtype: str, C: int, in_bytes: int, budget_s: float) -> di
         list(ex.map(lambda lh: oracle_ce(z[lh[0]:lh[1]], t[lh[0]:lh[1]], dtype)[0].sum(), blocks))
     dtn = time.perf_counter() - t0
     nbytes = rows * C * 2 * in_bytes
+    threads = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                               "MKL_NUM_THREADS", "NUMEXPR_NUM_THREADS")}
+    try:
+        from threadpoolctl import threadpool_info
+        threads["blas_pools"] = [{"api": i.get("internal_api"), "num_threads": i.get("num_threads")}
+                                 for i in threadpool_info()]
+    except Exception:  # threadpoolctl absent: the environment settings alone
+        pass
     return {"value": round(nbytes / dtn / 1e9, 4), "unit": "GB/s", "cores": workers,
+            "thread_settings": threads,
             "kind": "oracle", "rows_per_s": round(rows / dtn, 2),
             "one_core": {"value": round(nbytes / dt1 / 1e9, 4), "rows_per_s": round(rows / dt1, 2)},
             "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
@@ -319,7 +424,8 @@ def input_variants(zd, td, loss_rows, reps: int = 20) -> dict:
     return out
 
 
-def softmax_and_shards(zd, td, grad, loss_rows, reps: int = 20, nshards: int = 8) -> dict:
+def softmax_and_shards(zd, td, grad, loss_rows, reps: int = 20, nshards: int = 8,
+                       attention: bool = False) -> dict:
     """The row-wise softmax forward (y and the log-sum-exp) and backward on
     the workload's shape, and the cross-entropy of its vocabulary cut into
     nshards column shards: one shard's record pass (ce_shard_stats) and
@@ -352,6 +458,8 @@ def softmax_and_shards(zd, td, grad, loss_rows, reps: int = 20, nshards: int = 8
     out["shard_grad"] = _rate(2 * B * Cs * es + 4 * B + 16 * nshards * B + 4 * B, ms)
     out["shard"] = {"shards": nshards, "columns": Cs}
     del shards, recs, g0
+    if not attention:
+        return out
     # attention-shaped rows (the softmax of scaled dot products: batch 4 x
     # 32 heads x 2048 queries, 2048 keys), bf16, values from torch's device
     # generator (timing only)
@@ -367,6 +475,53 @@ def softmax_and_shards(zd, td, grad, loss_rows, reps: int = 20, nshards: int = 8
     ms = _event_median_ms(lambda: ce.softmax_bwd_into(ya, dya, dxa), stream, reps)
     att["softmax_bwd"] = _rate(3 * Ba * Ca * 2, ms)
     out["attention_rows"] = att
+    return out
+
+
+def second_workload(name: str, steps: int, warmup: int) -> dict:
+    """The other gated workload of the default run (the 4096 x 50257 fp32
+    LM head beside the 8192 x 128256 bf16 headline): the same step, W and
+    K, timed the same way in the same process, with the library's copy of
+    its own bytes beside it."""
+    import numpy as np
+    import torch
+    import softmax_cross_entropy_ce_amd as ce
+    import synth
+    w = synth.WORKLOADS[name]
+    B, C, es = w.B, w.C, w.in_bytes
+    dev = torch.device("cuda:0")
+    z, t = synth.make_workload(name)
+    if w.dtype == "f32":
+        zd = torch.from_numpy(z).to(dev)
+    else:
+        zd = torch.from_numpy(z.view(np.int16)).to(dev).view(torch.bfloat16)
+    td = torch.from_numpy(t).to(dev)
+    grad = torch.empty_like(zd)
+    loss_rows = torch.empty(B, dtype=torch.float32, device=dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(ce.reduce_workspace_bytes(B), 1), dtype=torch.uint8, device=dev)
+    res = time_steps(zd, td, grad, loss_rows, loss, ws, steps, warmup)
+    metric_bytes = B * C * 2 * es
+    fwd_bytes = metric_bytes + 8 * B
+    fwd_avg = statistics.fmean(res["fwd_ms"])
+    value = metric_bytes / (res["ms_per_step"] * 1e-3) / 1e9
+    achieved = fwd_bytes / (fwd_avg * 1e-3) / 1e9
+    cal = copy_calibration(zd, grad)
+    out = {"config": {**w.describe(), "path": ce.PATH_NAMES[ce.select_path(C, ce.F32 if w.dtype == "f32" else ce.BF16)]},
+           "steps": steps, "warmup": warmup,
+           "value": round(value, 2), "unit": "GB/s", "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+           "ms_per_step": round(res["ms_per_step"], 5),
+           "rows_per_s": round(B / (res["ms_per_step"] * 1e-3), 1),
+           "fwd_grad_ms": {"mean": round(fwd_avg, 5),
+                           "median": round(statistics.median(res["fwd_ms"]), 5),
+                           "min": round(min(res["fwd_ms"]), 5), "max": round(max(res["fwd_ms"]), 5)},
+           "roofline": {"bound": "hbm", "kernel": "ce_fwd_grad", "achieved": round(achieved, 2),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(achieved / PEAK_HBM_GBS, 4),
+                        "algorithmic_bytes_per_launch": fwd_bytes, "traffic": traffic_for(name)},
+           "copy_calibration": {**cal, "fwd_grad_pct_of_copy": round(100 * achieved / cal["GBps"], 2)}}
+    del zd, td, grad, loss_rows, ws
+    torch.cuda.empty_cache()
     return out
 
 
@@ -447,6 +602,10 @@ def main() -> None:
     ap.add_argument("--workload", default="lmhead128k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attention", action="store_true",
+                    help="also time the row softmax on attention-shaped rows (262144 x 2048 bf16)")
+    ap.add_argument("--no-second", action="store_true",
+                    help="skip the second gated workload (lmhead50k) of the default run")
     ap.add_argument("--mode", choices=["ce", "copy", "sweep"], default="ce")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--sweep-c", type=lambda v: tuple(int(x) for x in v.split(",")), default=None,
@@ -490,39 +649,9 @@ def main() -> None:
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     path = ce.select_path(C, ce.F32 if w.dtype == "f32" else ce.BF16)
 
-    def step():
-        ce.fwd_grad_into(zd, td, grad, loss_rows)
-        ce.reduce_loss_into(loss_rows, loss, ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    # Two events per step, around ce_fwd_grad only (each event adds a few
-    # microseconds between kernels); the step time is the wall time.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    log(f"[bench] path {ce.PATH_NAMES[path]}; timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record(stream)
-        ce.fwd_grad_into(zd, td, grad, loss_rows)
-        e1.record(stream)
-        ce.reduce_loss_into(loss_rows, loss, ws)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    fwd_ms = [a.elapsed_time(b) for a, b in evs]
-    ms_per_step = wall * 1e3 / args.steps
-    # ce_reduce_loss alone, after the timed region
-    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(20)]
-    for a, b in rev:
-        a.record(stream)
-        ce.reduce_loss_into(loss_rows, loss, ws)
-        b.record(stream)
-    torch.cuda.synchronize()
-    red_ms = [a.elapsed_time(b) for a, b in rev]
+    log(f"[bench] path {ce.PATH_NAMES[path]}; {args.warmup} warm-up steps, timing {args.steps}")
+    res = time_steps(zd, td, grad, loss_rows, loss, ws, args.steps, args.warmup)
+    fwd_ms, red_ms, ms_per_step = res["fwd_ms"], res["red_ms"], res["ms_per_step"]
     log(f"[bench] loss {loss.item():.6f}; fwd_grad median {statistics.median(fwd_ms):.4f} ms, "
         f"reduce median {statistics.median(red_ms):.4f} ms, step {ms_per_step:.4f} ms")
 
@@ -530,12 +659,11 @@ def main() -> None:
     fwd_bytes = metric_bytes + 8 * B             # + targets read + per-row loss written
     value = metric_bytes / (ms_per_step * 1e-3) / 1e9
     fwd_avg = statistics.fmean(fwd_ms)
-    qs = statistics.quantiles(fwd_ms, n=10)
     achieved = fwd_bytes / (fwd_avg * 1e-3) / 1e9
     cal = copy_calibration(zd, grad)
     bwd = backward_scale(zd, td, grad, loss_rows)
     variants = loss_only_and_in_place(zd, td, grad, loss_rows)
-    sm = softmax_and_shards(zd, td, grad, loss_rows)
+    sm = softmax_and_shards(zd, td, grad, loss_rows, attention=args.attention)
     cold = cold_fwd_grad(zd, td, grad, loss_rows)
     var = input_variants(zd, td, loss_rows)
     graph = graph_step(zd, td, grad, loss_rows, loss, ws)
@@ -559,8 +687,11 @@ def main() -> None:
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "rows_per_s": round(B / (ms_per_step * 1e-3), 1),
         "fwd_grad_ms": {"mean": round(fwd_avg, 5), "median": round(statistics.median(fwd_ms), 5),
-                        "p10": round(qs[0], 5), "p90": round(qs[8], 5),
-                        "min": round(min(fwd_ms), 5), "max": round(max(fwd_ms), 5)},
+                        "min": round(min(fwd_ms), 5), "max": round(max(fwd_ms), 5),
+                        "timed_steps": res["timed_steps"],
+                        "how": "HIP events attached to the kernel's launch "
+                               f"(every {EVENT_EVERY}th timed step)"},
+        "timed_region_s": round(res["timed_region_s"], 6),
         "reduce_ms": {"mean": round(statistics.fmean(red_ms), 5),
                       "median": round(statistics.median(red_ms), 5)},
         "roofline": {"bound": "hbm", "kernel": "ce_fwd_grad", "achieved": round(achieved, 2),
@@ -576,6 +707,9 @@ def main() -> None:
         "input_variants": var,
         "graph_step": graph,
     }
+    if w.name == "lmhead128k" and not args.no_second:
+        log("[bench] second gated workload lmhead50k (4096 x 50257 fp32)")
+        rec["lmhead50k"] = second_workload("lmhead50k", args.steps, args.warmup)
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f} s")
         rec["cpu_baseline"] = cpu_baseline(z, t, w.dtype, C, es, args.cpu_seconds)

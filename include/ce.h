@@ -446,6 +446,19 @@ int ce_debug_part_polls(int polls);
  */
 int ce_debug_part_counter(uint32_t* device_counter);
 
+/*
+ * Measurement hook: the next kernel launch that the library makes on the
+ * calling thread records start_event when that kernel starts and
+ * stop_event when it ends (hipExtLaunchKernel; either may be NULL), with
+ * no event packets of the caller's own between kernels on the stream.
+ * Both are hipEvent_t created by the caller (for example
+ * torch.cuda.Event(enable_timing=True).event_id... or hipEventCreate).
+ * One launch takes them: the first kernel of the next call (an entry point
+ * that launches several kernels times only its first).  Returns CE_OK.
+ * Per thread; not meant for production use.
+ */
+int ce_debug_time_next_launch(void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 }
 #endif

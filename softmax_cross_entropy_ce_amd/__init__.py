@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.ce_debug_part_polls.restype = i32
     L.ce_debug_part_counter.argtypes = [vp]
     L.ce_debug_part_counter.restype = i32
+    L.ce_debug_time_next_launch.argtypes = [vp, vp]
+    L.ce_debug_time_next_launch.restype = i32
     L.ce_stream_copy.argtypes = [vp, vp, i64, vp]
     L.ce_stream_copy.restype = i32
     L.ce_fwd_grad_scaled.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp, vp]

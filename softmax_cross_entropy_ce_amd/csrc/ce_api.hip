@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "ce.h"
+#include "ce_launch.h"
 #include "ce_parts.h"
 #include "ce_shard.h"
 #include "softmax_bwd.h"
@@ -14,6 +15,10 @@
 #include "ce_wave_host.h"
 
 namespace {
+
+// Events for the next launch on this thread (ce_debug_time_next_launch).
+thread_local hipEvent_t t_launch_start = nullptr;
+thread_local hipEvent_t t_launch_stop = nullptr;
 
 std::atomic<int> g_force_path{0};
 
@@ -146,7 +151,7 @@ int launch_short_cfg(const T* z, const int32_t* t, int64_t B, int C, ce::RowArgs
   constexpr int rpb = ce::kShortThreads / S * R;
   const int64_t blocks = (B + rpb - 1) / rpb;
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL((ce::ce_short_kernel<T, S, EPL, VW, GRAD, OP, R>), dim3((unsigned)blocks),
+  ce_host::launch((ce::ce_short_kernel<T, S, EPL, VW, GRAD, OP, R>), dim3((unsigned)blocks),
                      dim3(ce::kShortThreads), 0, st, z, t, B, C, rs, g, l);
   return launched();
 }
@@ -202,7 +207,7 @@ int launch_tiny_w(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArg
   const int64_t rows = (int64_t)ce::kTinyThreads * R;
   const int64_t chunks = (B + rows - 1) / rows;
   const int64_t grid = chunks < res ? chunks : res;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(ce::kTinyThreads), 0, st, z, t, B, (int)C, rs,
+  ce_host::launch(kern, dim3((unsigned)grid), dim3(ce::kTinyThreads), 0, st, z, t, B, (int)C, rs,
                      g, l);
   return launched();
 }
@@ -282,7 +287,7 @@ int launch_staged_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::Ro
   if (rows < 1 || C > S * EPL) return CE_ERR_PATH;  // a chunk pass and the slots hold a row
   const int64_t chunks = (B + rows - 1) / rows;
   const int64_t grid = chunks < res ? chunks : res;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(ce::kStagedThreads), 0, st, z, t, B, (int)C,
+  ce_host::launch(kern, dim3((unsigned)grid), dim3(ce::kStagedThreads), 0, st, z, t, B, (int)C,
                      rs, g, l);
   return launched();
 }
@@ -415,7 +420,7 @@ int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowAr
   const int res = resident_blocks(reinterpret_cast<const void*>(kern), NT, occupancy);
   if (res < 1) return CE_ERR_LAUNCH;
   const int64_t grid = B < res ? B : res;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), 0, st, z, t, B, (int)C, rs, g, l);
+  ce_host::launch(kern, dim3((unsigned)grid), dim3(NT), 0, st, z, t, B, (int)C, rs, g, l);
   return launched();
 }
 
@@ -431,7 +436,7 @@ int launch_row_lds(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowAr
   const int res = resident_blocks(reinterpret_cast<const void*>(kern), 1024, occupancy);
   if (res < 1) return CE_ERR_LAUNCH;
   const int64_t grid = B < res ? B : res;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(1024), 0, st, z, t, B, (int)C, rs, g, l);
+  ce_host::launch(kern, dim3((unsigned)grid), dim3(1024), 0, st, z, t, B, (int)C, rs, g, l);
   return launched();
 }
 
@@ -514,7 +519,7 @@ int launch_parts_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::Row
                      float* l, hipStream_t st) {
   const int64_t blocks = P * ((B + 7) / 8 * 8);
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL((ce::ce_part_kernel<T, P, NT, NR, NL, NXW, OP>), dim3((unsigned)blocks), dim3(NT),
+  ce_host::launch((ce::ce_part_kernel<T, P, NT, NR, NL, NXW, OP>), dim3((unsigned)blocks), dim3(NT),
                      0, st, z, t, B, (int)C, rs, g, l,
                      g_part_polls.load(std::memory_order_relaxed),
                      g_part_counter.load(std::memory_order_relaxed));
@@ -606,6 +611,7 @@ bool overlaps(uintptr_t a, uintptr_t an, uintptr_t b, uintptr_t bn) {
 // of at least kReduceMinChunk rows (2048: 8 per thread), so that the whole
 // GPU reads the rows, then one workgroup sums the partials.
 constexpr int64_t kReduceOneLaunch = 16384;
+static_assert(kReduceOneLaunch == ce::kReduceOneMax, "one launch sums what one workgroup holds");
 constexpr int64_t kReduceMinChunk = 2048;
 constexpr int64_t kReduceMaxBlocks = 1024;
 constexpr int kMaxDevicesReduce = 64;
@@ -656,6 +662,16 @@ int reduce_scratch_ptr(float** out) {
 }
 
 }  // namespace
+
+namespace ce_host {
+bool take_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (t_launch_start == nullptr && t_launch_stop == nullptr) return false;
+  *start = t_launch_start;
+  *stop = t_launch_stop;
+  t_launch_start = t_launch_stop = nullptr;
+  return true;
+}
+}  // namespace ce_host
 
 extern "C" {
 
@@ -778,10 +794,10 @@ int fwd_impl(const FwdArgs& a, void* stream) {
                  a.has_ignore ? 1 : 0};
   if (a.has_ignore) {
     uint32_t* kept = (uint32_t*)a.ws;
-    hipLaunchKernelGGL(ce::ce_set_u32_kernel, dim3(1), dim3(64), 0, st, kept, 0u);
+    ce_host::launch(ce::ce_set_u32_kernel, dim3(1), dim3(64), 0, st, kept, 0u);
     if (launched() != CE_OK) return CE_ERR_LAUNCH;
     const int64_t blocks = (B + ce::kCountThreads - 1) / ce::kCountThreads;
-    hipLaunchKernelGGL(ce::ce_count_kept_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)),
+    ce_host::launch(ce::ce_count_kept_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)),
                        dim3(ce::kCountThreads), 0, st, a.targets, B, a.ignore, kept);
     if (launched() != CE_OK) return CE_ERR_LAUNCH;
     rs.kept = kept;
@@ -824,7 +840,7 @@ int launch_scale(T* g, int64_t n, const float* scale, hipStream_t st) {
   const int64_t nb = n / (16 / (int64_t)sizeof(T)) + 1;
   const int64_t blocks = (nb + chunk - 1) / chunk;
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL(ce::ce_scale_kernel<T>, dim3((unsigned)blocks), dim3(ce::kScaleThreads), 0, st,
+  ce_host::launch(ce::ce_scale_kernel<T>, dim3((unsigned)blocks), dim3(ce::kScaleThreads), 0, st,
                      g, n, scale);
   return launched();
 }
@@ -842,7 +858,7 @@ int launch_bwd_short_cfg(const T* y, const T* dy, int64_t B, int C, T* dx, hipSt
   constexpr int rpb = ce::kShortThreads / S;
   const int64_t blocks = (B + rpb - 1) / rpb;
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL((ce::sm_bwd_short_kernel<T, S, EPL, VW>), dim3((unsigned)blocks),
+  ce_host::launch((ce::sm_bwd_short_kernel<T, S, EPL, VW>), dim3((unsigned)blocks),
                      dim3(ce::kShortThreads), 0, st, y, dy, B, C, dx);
   return launched();
 }
@@ -880,7 +896,7 @@ int launch_bwd_staged_cfg(const T* y, const T* dy, int64_t B, int64_t C, T* dx, 
   if (rows < 1 || C > S * EPL) return CE_ERR_PATH;
   const int64_t chunks = (B + rows - 1) / rows;
   const int64_t grid = chunks < res ? chunks : res;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(ce::kStagedThreads), 0, st, y, dy, B, (int)C,
+  ce_host::launch(kern, dim3((unsigned)grid), dim3(ce::kStagedThreads), 0, st, y, dy, B, (int)C,
                      dx);
   return launched();
 }
@@ -933,7 +949,7 @@ int launch_bwd_row_cfg(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hip
   const int res = resident_blocks(reinterpret_cast<const void*>(kern), NT, occupancy);
   if (res < 1) return CE_ERR_LAUNCH;
   const int64_t grid = B < res ? B : res;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), 0, st, y, dy, B, (int)C, dx);
+  ce_host::launch(kern, dim3((unsigned)grid), dim3(NT), 0, st, y, dy, B, (int)C, dx);
   return launched();
 }
 
@@ -981,7 +997,7 @@ template <typename T, int P>
 int launch_bwd_parts_p(const T* y, const T* dy, int64_t B, int64_t C, T* dx, hipStream_t st) {
   const int64_t blocks = P * ((B + 7) / 8 * 8);
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL((ce::sm_bwd_part_kernel<T, P, 1024, kBwdPartSlots>), dim3((unsigned)blocks),
+  ce_host::launch((ce::sm_bwd_part_kernel<T, P, 1024, kBwdPartSlots>), dim3((unsigned)blocks),
                      dim3(1024), 0, st, y, dy, B, (int)C, dx,
                      g_part_polls.load(std::memory_order_relaxed),
                      g_part_counter.load(std::memory_order_relaxed));
@@ -1036,7 +1052,7 @@ int launch_shard_grad(const T* z, const int32_t* t, int64_t B, int64_t C, int64_
   if (C <= ce::kShardTinyC) {
     const int64_t blocks = (B + 255) / 256;
     if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-    hipLaunchKernelGGL(ce::ce_shard_grad_tiny_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st,
+    ce_host::launch(ce::ce_shard_grad_tiny_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st,
                        z, t, B, (int)C, col0, Ctot, r4, nshards, rs, g, l);
     return launched();
   }
@@ -1049,11 +1065,11 @@ int launch_shard_grad(const T* z, const int32_t* t, int64_t B, int64_t C, int64_
   const int64_t blocks = (B * chunks + units - 1) / units;
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
   if (wave_units)
-    hipLaunchKernelGGL((ce::ce_shard_grad_kernel<T, 64>), dim3((unsigned)blocks),
+    ce_host::launch((ce::ce_shard_grad_kernel<T, 64>), dim3((unsigned)blocks),
                        dim3(ce::kShardThreads), 0, st, z, t, B, (int)C, col0, Ctot, r4, nshards, rs,
                        g, l, (int)chunks);
   else
-    hipLaunchKernelGGL((ce::ce_shard_grad_kernel<T, 256>), dim3((unsigned)blocks),
+    ce_host::launch((ce::ce_shard_grad_kernel<T, 256>), dim3((unsigned)blocks),
                        dim3(ce::kShardThreads), 0, st, z, t, B, (int)C, col0, Ctot, r4, nshards, rs,
                        g, l, (int)chunks);
   return launched();
@@ -1062,15 +1078,15 @@ int launch_shard_grad(const T* z, const int32_t* t, int64_t B, int64_t C, int64_
 int launch_reduce(const float* rows, int64_t B, float* out, float* part, hipStream_t st) {
   const int64_t blocks = reduce_blocks(B);
   if (blocks == 1) {
-    hipLaunchKernelGGL(ce::ce_reduce_kernel, dim3(1), dim3(ce::kReduceThreads), 0, st, rows, B, B,
-                       out);
+    ce_host::launch(ce::ce_reduce_one_kernel, dim3(1), dim3(ce::kReduceOneThreads), 0, st, rows,
+                    (int)B, out);
     return launched();
   }
-  hipLaunchKernelGGL(ce::ce_reduce_kernel, dim3((unsigned)blocks), dim3(ce::kReduceThreads), 0, st,
-                     rows, B, reduce_chunk(B), part);
+  ce_host::launch(ce::ce_reduce_kernel, dim3((unsigned)blocks), dim3(ce::kReduceThreads), 0, st,
+                  rows, B, reduce_chunk(B), part);
   if (launched() != CE_OK) return CE_ERR_LAUNCH;
-  hipLaunchKernelGGL(ce::ce_reduce_kernel, dim3(1), dim3(ce::kReduceThreads), 0, st,
-                     (const float*)part, blocks, blocks, out);
+  ce_host::launch(ce::ce_reduce_one_kernel, dim3(1), dim3(ce::kReduceOneThreads), 0, st,
+                  (const float*)part, (int)blocks, out);
   return launched();
 }
 
@@ -1270,7 +1286,7 @@ int ce_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
   if (overlaps((uintptr_t)src, (uintptr_t)bytes, (uintptr_t)dst, (uintptr_t)bytes)) return CE_ERR_ALIAS;
   const int64_t blocks = (bytes + ce::kCopyChunk - 1) / ce::kCopyChunk;
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL(ce::ce_copy_kernel, dim3((unsigned)blocks), dim3(ce::kCopyThreads), 0,
+  ce_host::launch(ce::ce_copy_kernel, dim3((unsigned)blocks), dim3(ce::kCopyThreads), 0,
                      as_stream(stream), (const char*)src, (char*)dst, bytes);
   return launched();
 }
@@ -1290,6 +1306,12 @@ int ce_debug_force_path(int path) {
 int ce_debug_part_polls(int polls) {
   if (polls < 0) return CE_ERR_PATH;
   return g_part_polls.exchange(polls);
+}
+
+int ce_debug_time_next_launch(void* start_event, void* stop_event) {
+  t_launch_start = static_cast<hipEvent_t>(start_event);
+  t_launch_stop = static_cast<hipEvent_t>(stop_event);
+  return CE_OK;
 }
 
 int ce_debug_part_counter(uint32_t* device_counter) {

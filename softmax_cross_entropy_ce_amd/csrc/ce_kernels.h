@@ -1054,6 +1054,44 @@ __global__ __launch_bounds__(kReduceThreads) void ce_reduce_kernel(const float* 
   if (threadIdx.x == 0) out[blockIdx.x] = tot;
 }
 
+// One workgroup of 1024 threads sums up to kReduceOneMax values with one
+// round of loads: thread i reads values i, i + 1024, ... (at most 16, all in
+// flight at once; the buffer's range returns 0 past n, and adding +0 leaves
+// a sum unchanged) and adds them in index order; the waves' sums are
+// combined across lanes in a fixed order and the 16 wave sums by a fixed
+// pairwise tree.  Used for the whole sum up to kReduceOneMax rows and for
+// the second level over the first level's partial sums.
+constexpr int kReduceOneThreads = 1024;
+constexpr int kReduceOneSlots = 16;
+constexpr int kReduceOneMax = kReduceOneThreads * kReduceOneSlots;
+
+__global__ __launch_bounds__(kReduceOneThreads) void ce_reduce_one_kernel(
+    const float* __restrict__ in, int n, float* __restrict__ out) {
+  __shared__ float part[kReduceOneThreads / 64];
+  const int tid = threadIdx.x;
+  const rsrc_t r = make_rsrc(in, (uint32_t)n * 4u);
+  float v[kReduceOneSlots];
+#pragma unroll
+  for (int k = 0; k < kReduceOneSlots; ++k) {
+    v[k] = 0.f;
+    if (k * kReduceOneThreads < n)  // uniform
+      v[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           r, (tid + k * kReduceOneThreads) * 4, 0, kPolicyDefault));
+  }
+  float a = v[0];
+#pragma unroll
+  for (int k = 1; k < kReduceOneSlots; ++k) a = a + v[k];
+  const float w = wave_allreduce(a, OpAdd{});
+  if ((tid & 63) == 0) part[tid >> 6] = w;
+  __syncthreads();
+  if (tid == 0) {
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[i] = part[i];
+    *out = tree_sum(t);
+  }
+}
+
 // ===========================================================================
 // Rows kept by ignore_index: the number of targets that differ from it,
 // added into *count with one integer atomic per wave (an integer total does

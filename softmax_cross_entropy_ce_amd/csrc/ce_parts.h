@@ -86,13 +86,41 @@ __device__ __forceinline__ void part_of_block(uint32_t g, int64_t& row, int& par
   part = (int)(local % P);
 }
 
+// Maximum over the 16 lanes of each row of a wave: four v_max_f32 steps
+// with their DPP operand (the compiler forms a max from a separate DPP move
+// and a v_maximum3_f32 per step).  Each step is preceded by the two wait
+// states a DPP read needs after a VALU write of its source.  v_max_f32
+// returns the other operand for a quiet NaN; the values reduced here are
+// finite, -inf or NaN from NaN inputs, whose sums are NaN regardless.
+__device__ __forceinline__ float row16_max(float v) {
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
+      : "+v"(v));
+  return v;
+}
+
+// The same over the whole wave; the result is wave-uniform.
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  v = fmax2(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                     kSwizzleXor16)));
+  const float lo = __builtin_bit_cast(float,
+                                      __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float hi = __builtin_bit_cast(float,
+                                      __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  return fmax2(lo, hi);
+}
+
 // Max / sum pair of the whole workgroup, from each thread's (c, s).  Every
 // thread gets the same result; the order of operations is fixed.  Contains
 // one barrier; the caller separates two uses by another.
 template <int NW>
 __device__ __forceinline__ void wg_pair(float c, float s, float* red_c, float* red_s, int lane,
                                         int wv, float& cg, float& sg) {
-  const float cw = wave_allreduce(c, OpMax{});
+  static_assert(NW <= 16, "one row of 16 lanes holds the waves' pairs");
+  const float cw = wave_max(c);
   const float sw = wave_allreduce(s * exp2_hw(c - cw), OpAdd{});
   if (lane == 0) {
     red_c[wv] = cw;
@@ -101,12 +129,26 @@ __device__ __forceinline__ void wg_pair(float c, float s, float* red_c, float* r
   __syncthreads();
   const float ci = lane < NW ? red_c[lane] : kLowest;
   const float si = lane < NW ? red_s[lane] : 0.f;
-  cg = wave_uniform(seg_allreduce<16>(ci, OpMax{}));
+  cg = wave_uniform(row16_max(ci));
   sg = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
 }
 
 // Vectors a part of ce_part_kernel<T, P, NT, NR, NL, NXW> holds.
 constexpr int part_capacity(int NT, int NR, int NL, int NXW) { return (NR + NL) * NT + NXW * 64; }
+
+// Waves per SIMD of a part kernel: eight (64 VGPRs, 32 waves per CU) for
+// up to eight register slots, four (128 VGPRs) for more.
+constexpr int part_waves(int NR) { return NR > 8 ? 4 : 8; }
+
+// Register slots whose fp32 terms a 16-bit part keeps in LDS: as many as
+// fit the CU's 160 KB shared by the workgroups that its waves allow, less
+// 2 KB each for the reductions (32 bytes per thread and slot).
+constexpr int part_lds_terms(int NT, int NR, int ES, int NL, int NXW) {
+  const int wgs = 4 * part_waves(NR) * 64 / NT;
+  const int budget = 160 * 1024 / wgs - 2048;
+  const int n = budget / (NT * 32);
+  return (ES != 2 || NL != 0 || NXW != 0) ? 0 : (n < NR ? n : NR);
+}
 
 // The max / sum pair of a part, in two passes over the data it holds:
 //  1. the thread's maximum over its elements (16-bit types on their bit
@@ -131,7 +173,7 @@ constexpr int part_capacity(int NT, int NR, int NL, int NXW) { return (NR + NL) 
 // before that happens (0: every part recomputes).  At most 64 VGPRs (eight
 // waves per SIMD), so 32 / (NT / 64) workgroups fit a CU by waves.
 template <typename T, int P, int NT, int NR, int NL, int NXW, int OP = kOpCE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(part_waves(NR))))
 void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B,
                     int C, RowArgs rs, T* __restrict__ grad, float* __restrict__ loss_rows,
                     int spin, uint32_t* __restrict__ fallbacks) {
@@ -144,7 +186,15 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   static_assert(P == 1 || P == 2 || P == 4 || P == 8, "one, two, four or eight parts per row");
   static_assert(NT % 64 == 0 && NW >= 1 && NW <= 16, "1 to 16 waves");
   static_assert(NXW >= 0 && NXW < NW, "partial LDS slot smaller than a slot");
+  // 16-bit parts held in registers alone keep the fp32 terms of their first
+  // kLdsTerms register slots in LDS (32 bytes per thread and slot: two
+  // slots, 64 KB, for 1024 threads, so two workgroups still fit a CU), so
+  // that the gradient of those slots is one multiply per element instead
+  // of an fma and an exponential.
+  constexpr int kLdsTerms = part_lds_terms(NT, NR, sizeof(T), NL, NXW);
+  static_assert(kLdsTerms <= NR, "kept slots are register slots");
   __shared__ u32x4 stage[NL * NT + NX > 0 ? NL * NT + NX : 1];
+  __shared__ f32x4 kept[kLdsTerms > 0 ? kLdsTerms * 2 * NT : 1];
   __shared__ float red_c[NW], red_s[NW];
   __shared__ float mail_c[P], mail_s[P];
   __shared__ int mail_ok[P];
@@ -231,14 +281,17 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   // stores.  Per part q: whether this wave holds the target's vector, and
   // the slot that holds it for the owning thread (-1 for the others).
   struct TargetIn {
-    bool wave;
-    int k;
+    bool wave;  // this wave holds the target's vector
+    int slot;   // the slot that holds it (the same for every thread), or -1
+    bool mine;  // this thread holds it
+    int k;      // slot for the owning thread, -1 for the others
     bool part;  // the part's body holds the target
   };
   auto target_in = [&](const PartRange& pr) -> TargetIn {
     const bool in = t_body && tvec >= pr.v0 && tvec < pr.v0 + pr.len;
     const bool mine = in && (tvec - pr.v0) % NT == tid;
-    return TargetIn{__builtin_amdgcn_ballot_w64(mine) != 0, mine ? (tvec - pr.v0) / NT : -1, in};
+    const int slot = in ? (tvec - pr.v0) / NT : -1;
+    return TargetIn{__builtin_amdgcn_ballot_w64(mine) != 0, slot, mine, mine ? slot : -1, in};
   };
   const TargetIn tin = target_in(own);
 
@@ -246,7 +299,9 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   // the part's end (last slot only; uniform test) set to -inf.  Slots wholly
   // past the end are skipped (uniform).
   auto slot_words = [&](const PartRange& pr, const TargetIn& ti, int k, u32x4 w) -> u32x4 {
-    if (ti.wave && ti.k == k) w = E::kill(w, tj);
+    if (ti.wave && ti.slot == k) {  // uniform: one wave, one slot
+      if (ti.mine) w = E::kill(w, tj);
+    }
     if (k * NT + NT > pr.len) {
       // a branch, not selects on every slot: only a part's last slot can
       // reach past its end
@@ -357,6 +412,12 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       float e[VE];
       s = s + slot_terms(v[k], c, e);
       if constexpr (kKeepTerms) v[k] = as_u32(f32x4{e[0], e[1], e[2], e[3]});
+      if constexpr (kLdsTerms > 0) {
+        if (k < kLdsTerms) {
+          kept[(2 * k) * NT + tid] = f32x4{e[0], e[1], e[2], e[3]};
+          kept[(2 * k + 1) * NT + tid] = f32x4{e[4], e[5], e[6], e[7]};
+        }
+      }
     }
 #pragma unroll
     for (int p = 0; p < NLS; ++p) {
@@ -526,8 +587,21 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
         for (int i = 0; i < VE; ++i) g[i] = grad_of(f[i]);
         bstore128<kPolicyStream>(E::pack(g), rout, voff, (uint32_t)k * NT * 16u);
       };
+      // slots whose terms 2^(z log2e - c) wait in LDS: times 2^(c - c')
+      // (and gmul), the same value up to the rounding of one multiply
+      if constexpr (kLdsTerms > 0) {
+        const float kfactor = kUnit ? exp2_hw(c - cp) : exp2_hw(c - cp) * gmul;
 #pragma unroll
-      for (int k = 0; k < NR; ++k) write_slot(k, v[k]);
+        for (int k = 0; k < kLdsTerms; ++k) {
+          if (k * NT >= len) continue;
+          const f32x4 a = kept[(2 * k) * NT + tid], b = kept[(2 * k + 1) * NT + tid];
+          const float g[VE] = {a.x * kfactor, a.y * kfactor, a.z * kfactor, a.w * kfactor,
+                               b.x * kfactor, b.y * kfactor, b.z * kfactor, b.w * kfactor};
+          bstore128<kPolicyStream>(E::pack(g), rout, voff, (uint32_t)k * NT * 16u);
+        }
+      }
+#pragma unroll
+      for (int k = kLdsTerms; k < NR; ++k) write_slot(k, v[k]);
 #pragma unroll
       for (int p = 0; p < NLS; ++p) write_slot(NR + p, lds_slot(p));
       if (xe >= 0) E::store1(gp + xe, xe == t ? rr.gt : grad_of(xs));

@@ -124,7 +124,9 @@ __device__ __forceinline__ RowResult row_epilogue(float cg, float sx, float zt, 
   RowResult r;
   r.at = __builtin_fmaf(zt, kLog2e, -cg);
   const float S = sx + exp2_hw(r.at);
-  const float scale0 = invB / S;
+  // one v_rcp_f32 (within an ulp) rather than a correctly rounded divide:
+  // S >= 1 and the gradient's bar is far wider than an fp32 ulp
+  const float scale0 = invB * __builtin_amdgcn_rcpf(S);
   const float qnan = __builtin_nanf("");
   r.scale0 = valid ? scale0 : qnan;
   r.scale = valid ? scale0 * gmul : qnan;

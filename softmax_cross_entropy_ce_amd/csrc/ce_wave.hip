@@ -3,6 +3,7 @@
 #include "ce_wave_host.h"
 
 #include "ce.h"
+#include "ce_launch.h"
 #include "ce_wave.h"
 
 namespace ce_wave {
@@ -16,7 +17,7 @@ int launch_cfg(const T* z, const int32_t* t, int64_t B, int C, const ce::RowArgs
   constexpr int64_t rows_per_block = (ce::kWaveThreads / 64) * R;
   const int64_t blocks = (B + rows_per_block - 1) / rows_per_block;
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL((ce::ce_wave_kernel<T, VB, LB, GRAD, OP>), dim3((unsigned)blocks),
+  ce_host::launch((ce::ce_wave_kernel<T, VB, LB, GRAD, OP>), dim3((unsigned)blocks),
                      dim3(ce::kWaveThreads), 0, st, z, t, B, C, rs, g, l);
   return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_LAUNCH;
 }
@@ -71,7 +72,7 @@ int launch_bwd_cfg(const void* y, const void* dy, int64_t B, int C, void* dx, hi
   constexpr int64_t rows_per_block = (ce::kWaveThreads / 64) * R;
   const int64_t blocks = (B + rows_per_block - 1) / rows_per_block;
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  hipLaunchKernelGGL((ce::sm_bwd_wave_kernel<T, VB, LB>), dim3((unsigned)blocks),
+  ce_host::launch((ce::sm_bwd_wave_kernel<T, VB, LB>), dim3((unsigned)blocks),
                      dim3(ce::kWaveThreads), 0, st, static_cast<const T*>(y),
                      static_cast<const T*>(dy), B, C, static_cast<T*>(dx));
   return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_LAUNCH;

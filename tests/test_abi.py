@@ -41,7 +41,7 @@ def test_library_exports_every_declared_function():
                             "ce_fwd_grad_scaled", "ce_scale_grad", "ce_fwd_loss",
                             "ce_softmax_fwd", "ce_softmax_bwd", "ce_shard_stats",
                             "ce_shard_grad", "ce_fwd_grad_ex", "ce_fwd_workspace_bytes",
-                            "ce_reduce_loss_noalloc"])
+                            "ce_reduce_loss_noalloc", "ce_debug_time_next_launch"])
     for n in names:
         assert hasattr(L_, n), n
 

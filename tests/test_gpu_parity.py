@@ -149,37 +149,34 @@ def test_parity_lmhead50k_workload():
     _log("lmhead50k", full_parity(z, t, "f32", block_elems=1 << 24, where="lmhead50k"))
 
 
-def test_parity_lmhead128k_workload_sampled():
+def test_parity_lmhead128k_workload():
     """8192 x 128256 bf16 at full size in the launch configuration the
-    benchmark times: 96 seeded-random rows plus the first and last rows are
-    compared with the oracle element by element; the scalar is compared with
-    the oracle's sum over all rows, computed in row blocks."""
-    import torch
+    benchmark times: every row's gradient compared with the oracle element
+    by element (1 bf16 ulp from RNE of the fp64 value) and every per-row
+    loss, in blocks of 64 rows on a pool of threads, and the scalar against
+    the oracle's sum over all rows."""
+    from concurrent.futures import ThreadPoolExecutor
     z, t = synth.make_workload("lmhead128k")
     B, C = z.shape
     z_dev, t_dev = to_device(z, t, "bf16")
     grad, loss_rows, loss = run_gpu(z_dev, t_dev)
-    rng = np.random.Generator(np.random.PCG64(123))
-    rows = np.unique(np.concatenate([[0, B - 1], rng.choice(B, 96, replace=False)]))
+    g_all = grad_to_host(grad, "bf16")
     lr = loss_rows.cpu().numpy()
-    idx = torch.from_numpy(rows).to(grad.device)
-    g = grad_to_host(grad.index_select(0, idx), "bf16")
-    worst, _ = compare_block(g, lr[rows], z[rows], t[rows], B, "bf16", where="lmhead128k")
-    from concurrent.futures import ThreadPoolExecutor
-    step = 128
+    del grad, z_dev
+    step = 64
 
     def block(lo):
-        zb = widen_rows(z[lo:lo + step], "bf16")
-        l, _ = ce_rows(zb, t[lo:lo + step], B)
-        return l, 1e-5 * (np.abs(zb.max(axis=1)) + math.log(C) + 1.0) / B
+        hi = min(B, lo + step)
+        return compare_block(g_all[lo:hi], lr[lo:hi], z[lo:hi], t[lo:hi], B, "bf16",
+                             where=f"lmhead128k rows {lo}:{hi}")
 
     with ThreadPoolExecutor(8) as ex:
         parts = list(ex.map(block, range(0, B, step)))
-    ora = np.concatenate([p[0] for p in parts])
-    tol = np.concatenate([p[1] for p in parts])
+    worst: dict = {}
+    for res, _ in parts:
+        for k, v in res.items():
+            worst[k] = max(worst.get(k, 0), v)
+    ora = np.concatenate([p[1] for p in parts])
     worst["loss_rel"] = compare_scalar(float(loss.item()), reduce_loss(ora), "bf16", "lmhead128k")
-    # every per-row loss, not just the sampled rows
-    err = np.abs(lr.astype(np.float64) - ora)
-    worst["loss_rows_all_abs"] = float(err.max())
-    assert (err <= tol).all(), f"row {int(np.argmax(err - tol))}"
-    _log("lmhead128k sampled", worst)
+    worst["rows_compared"] = B
+    _log("lmhead128k all rows", worst)

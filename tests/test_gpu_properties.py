@@ -90,9 +90,25 @@ def test_full_coverage_and_guard_bands(B, C, dtype, sigma, path):
 @pytest.mark.parametrize("B,C,dtype,sigma,path", CASES, ids=IDS)
 def test_shift_invariance(B, C, dtype, sigma, path):
     """Adding a constant to every logit of a row leaves loss and gradient
-    unchanged (within the parity bars).  Logits sit on a grid (fp32:
-    multiples of 2^-8 within +-64, shift 37; bf16: multiples of 2^-2 within
-    +-8, shift 4) so that the shifted inputs are exact."""
+    unchanged, to a bar derived from the kernels' arithmetic rather than bit
+    for bit.  Logits sit on a grid (fp32: multiples of 2^-8 within +-64,
+    shift 37; bf16: multiples of 2^-2 within +-8, shift 4) so that the
+    shifted inputs are exact.
+
+    Why not bitwise: every kernel forms an element's exponent as one fma,
+    z*log2e - c, with c = fl(m * log2e) for the row maximum m.  fl(m log2e)
+    and fl((m + k) log2e) differ from the exact products by different
+    rounding errors, and each fma result is rounded once more, so a shift
+    moves each exponent by at most ulp(c)/2 + ulp(c')/2 + ulp(x)/2 +
+    ulp(x')/2: with |c|, |c'|, |x| <= 185 on the fp32 grid that is below
+    3.5 * 2^-17 (log2 units), a relative change of each term, and of S, of
+    at most 2e-5.  The gradient (at most 1/B) therefore moves by at most
+    4e-5/B in fp32, inside 2 * F32_GRAD_ATOL; in bf16 the change is
+    a few 1e-6 before rounding, so a result can land on the other side of
+    a rounding boundary: at most 1 ulp (relative 2^-7).  The loss moves by
+    well under 2e-5 relative.  Forming the exponent as (z - m) * log2e,
+    exact on such grids, would cost a second instruction per element in
+    both passes over the row."""
     _force(path)
     if dtype == "f32":
         z = synth.grid_logits(B, C, 2.0 ** -8, 64.0, seed=9)
