@@ -113,24 +113,54 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmax2(lo, hi);
 }
 
-// Max / sum pair of the whole workgroup, from each thread's (c, s).  Every
-// thread gets the same result; the order of operations is fixed.  Contains
-// one barrier; the caller separates two uses by another.
-template <int NW>
-__device__ __forceinline__ void wg_pair(float c, float s, float* red_c, float* red_s, int lane,
-                                        int wv, float& cg, float& sg) {
-  static_assert(NW <= 16, "one row of 16 lanes holds the waves' pairs");
+// Each wave's max / sum pair, from each thread's (c, s), into red_c /
+// red_s[wv] (lane 0 writes).  The caller puts a barrier before the reads.
+__device__ __forceinline__ void wave_pair_to_lds(float c, float s, float* red_c, float* red_s,
+                                                 int lane, int wv) {
   const float cw = wave_max(c);
   const float sw = wave_allreduce(s * exp2_hw(c - cw), OpAdd{});
   if (lane == 0) {
     red_c[wv] = cw;
     red_s[wv] = sw;
   }
-  __syncthreads();
+}
+
+// The NW waves' pairs in LDS combined into one, in a fixed order, by the
+// calling wave (every lane gets the result).
+template <int NW>
+__device__ __forceinline__ void lds_pairs_combine(const float* red_c, const float* red_s, int lane,
+                                                  float& cg, float& sg) {
+  static_assert(NW <= 16, "one row of 16 lanes holds the waves' pairs");
   const float ci = lane < NW ? red_c[lane] : kLowest;
   const float si = lane < NW ? red_s[lane] : 0.f;
   cg = wave_uniform(row16_max(ci));
   sg = wave_uniform(seg_allreduce<16>(si * exp2_hw(ci - cg), OpAdd{}));
+}
+
+// The P parts' pairs combined in part order: cg = max c_q, then
+// sx = sum over q of s_q * 2^(c_q - cg) starting from part 0.
+template <int P>
+__device__ __forceinline__ void combine_pairs(const float* mail_c, const float* mail_s, float& cg,
+                                              float& sx) {
+  cg = mail_c[0];
+#pragma unroll
+  for (int q = 1; q < P; ++q) cg = fmax2(cg, mail_c[q]);
+  // the maxima are read from LDS again rather than kept in registers
+  if constexpr (P > 4) asm volatile("" ::: "memory");
+  sx = mail_s[0] * exp2_hw(mail_c[0] - cg);
+#pragma unroll
+  for (int q = 1; q < P; ++q) sx = sx + mail_s[q] * exp2_hw(mail_c[q] - cg);
+}
+
+// Max / sum pair of the whole workgroup, from each thread's (c, s).  Every
+// thread gets the same result; the order of operations is fixed.  Contains
+// one barrier; the caller separates two uses by another.
+template <int NW>
+__device__ __forceinline__ void wg_pair(float c, float s, float* red_c, float* red_s, int lane,
+                                        int wv, float& cg, float& sg) {
+  wave_pair_to_lds(c, s, red_c, red_s, lane, wv);
+  __syncthreads();
+  lds_pairs_combine<NW>(red_c, red_s, lane, cg, sg);
 }
 
 // Vectors a part of ce_part_kernel<T, P, NT, NR, NL, NXW> holds.
@@ -198,6 +228,11 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   __shared__ float red_c[NW], red_s[NW];
   __shared__ float mail_c[P], mail_s[P];
   __shared__ int mail_ok[P];
+  // The row's results, formed once by wave 0 when every partner's pair
+  // arrived (fin_ok) and read by every thread: cg, sx, 1/(S B), gmul/(S B),
+  // g_t.
+  __shared__ float fin[5];
+  __shared__ int fin_ok;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t voff = (uint32_t)tid * 16u;
@@ -349,12 +384,20 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       return m.f;
     }
   };
-  // c from the maximum over the slots, the edge element and (in the part
-  // holding it) the target
-  auto pair_c = [&](float m, int e, float x, bool has_t, float zt_) -> float {
+  // c from a maximum over slots and, where the thread has one, its edge
+  // element
+  auto pair_c = [&](float m, int e, float x) -> float {
     if (e >= 0) m = fmax2(m, x);
-    if (has_t) m = fmax2(m, zt_);
     return fmax2(m * kLog2e, kLowest);
+  };
+  // The part that holds the target folds z_t into its pair's maximum (the
+  // target stays out of the sum), so that the row's cg >= z_t log2 e.
+  auto fold_target = [&](bool has_t, float zt_, float& cp_, float& sp_) {
+    if (has_t) {
+      const float cn = fmax2(cp_, zt_ * kLog2e);
+      sp_ = sp_ * exp2_hw(cp_ - cn);
+      cp_ = cn;
+    }
   };
   // Pass 2 of one slot: its terms and their sum (the slot's words as from
   // slot_words).
@@ -371,7 +414,6 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
 
   // Phase B: this part's pair.
   constexpr bool kKeepTerms = sizeof(T) == 4 && P <= 4;
-  const float zt = t >= 0 ? zt_raw : 0.f;
   // Each phase tests the slots against its own opaque copy of the part's
   // length: conditions shared between phases would stay live in scalar
   // registers from pass 1 to the gradient, and the compiler spills them.
@@ -379,16 +421,29 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
     asm volatile("" : "+s"(x));
     return x;
   };
-  MaxState ms = max_init();
-  {
-    const int len = opaque(own.len);
-#pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      if (k * NT >= len) continue;
-      v[k] = slot_words(own, tin, k, v[k]);
-      max_add(ms, v[k]);
+  // 16-bit parts take c from their first slot alone and fold every slot
+  // as soon as its data is in, so that the exponentials of the first slots
+  // overlap the loads of the last; a thread whose sum overflows (an element
+  // more than 88 above its first slot's maximum) forms it again from its
+  // true maximum.  fp32 parts, which keep their terms in the register
+  // slots, take the maximum over all their slots first.
+  constexpr bool kFirstSlotC = sizeof(T) == 2;
+  auto keep_terms = [&](int k, const float (&e)[VE]) {
+    if constexpr (kKeepTerms) v[k] = as_u32(f32x4{e[0], e[1], e[2], e[3]});
+    if constexpr (kLdsTerms > 0) {
+      if (k < kLdsTerms) {
+        kept[(2 * k) * NT + tid] = f32x4{e[0], e[1], e[2], e[3]};
+        kept[(2 * k + 1) * NT + tid] = f32x4{e[4], e[5], e[6], e[7]};
+      }
     }
-    wait_vmcnt<0>();  // LDS slots (each thread reads its own wave's), edge and target loads
+  };
+  // the thread's maximum over all its slots (slot_words already applied to
+  // the register slots)
+  auto full_max = [&](int len) -> float {
+    MaxState ms = max_init();
+#pragma unroll
+    for (int k = 0; k < NR; ++k)
+      if (k * NT < len) max_add(ms, v[k]);
 #pragma unroll
     for (int p = 0; p < NLS; ++p)
       if ((NR + p) * NT < len) max_add(ms, slot_words(own, tin, NR + p, lds_slot(p)));
@@ -400,149 +455,241 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       for (int p = 0; p < NLS; ++p)
         if ((NR + p) * NT < len) max_add_neg(ms, slot_words(own, tin, NR + p, lds_slot(p)));
     }
-  }
-  const float xs = xe >= 0 ? xs_raw : kNegInf;
-  const float c = pair_c(max_value(ms), xe, xs, tin.part, zt);
-  float s = 0.f;
-  {
-    const int len = opaque(own.len);
+    return max_value(ms);
+  };
+  // the sum over all slots (and the edge element) with a given c
+  auto full_sum = [&](int len, float c_, float xs_) -> float {
+    float s_ = 0.f;
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       if (k * NT >= len) continue;
       float e[VE];
-      s = s + slot_terms(v[k], c, e);
-      if constexpr (kKeepTerms) v[k] = as_u32(f32x4{e[0], e[1], e[2], e[3]});
-      if constexpr (kLdsTerms > 0) {
-        if (k < kLdsTerms) {
-          kept[(2 * k) * NT + tid] = f32x4{e[0], e[1], e[2], e[3]};
-          kept[(2 * k + 1) * NT + tid] = f32x4{e[4], e[5], e[6], e[7]};
-        }
-      }
+      s_ = s_ + slot_terms(v[k], c_, e);
+      keep_terms(k, e);
     }
 #pragma unroll
     for (int p = 0; p < NLS; ++p) {
       if ((NR + p) * NT >= len) continue;
       float e[VE];
-      s = s + slot_terms(slot_words(own, tin, NR + p, lds_slot(p)), c, e);
+      s_ = s_ + slot_terms(slot_words(own, tin, NR + p, lds_slot(p)), c_, e);
     }
+    return s_ + edge_term(xe, xs_, c_);
+  };
+  float c, s;
+  float xs;
+  if constexpr (kFirstSlotC) {
+    const int len = opaque(own.len);
+    float c0 = kLowest;
+    if (0 < len) {
+      v[0] = slot_words(own, tin, 0, v[0]);
+      MaxState m0 = max_init();
+      max_add(m0, v[0]);
+      if (max_needs_neg(m0)) max_add_neg(m0, v[0]);
+      c0 = fmax2(max_value(m0) * kLog2e, kLowest);
+    }
+    s = 0.f;
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      if (k * NT >= len) continue;
+      if (k > 0) v[k] = slot_words(own, tin, k, v[k]);
+      float e[VE];
+      s = s + slot_terms(v[k], c0, e);
+      keep_terms(k, e);
+    }
+    wait_vmcnt<0>();  // LDS slots (each thread reads its own wave's), edge and target loads
+#pragma unroll
+    for (int p = 0; p < NLS; ++p) {
+      if ((NR + p) * NT >= len) continue;
+      float e[VE];
+      s = s + slot_terms(slot_words(own, tin, NR + p, lds_slot(p)), c0, e);
+    }
+    xs = xe >= 0 ? xs_raw : kNegInf;
+    s = s + edge_term(xe, xs, c0);
+    c = c0;
+    if (!(s < __builtin_inff())) {  // overflow (or NaN input): the true maximum
+      c = pair_c(full_max(len), xe, xs);
+      s = full_sum(len, c, xs);
+    }
+  } else {
+    const int len = opaque(own.len);
+#pragma unroll
+    for (int k = 0; k < NR; ++k)
+      if (k * NT < len) v[k] = slot_words(own, tin, k, v[k]);
+    wait_vmcnt<0>();  // LDS slots (each thread reads its own wave's), edge and target loads
+    xs = xe >= 0 ? xs_raw : kNegInf;
+    c = pair_c(full_max(len), xe, xs);
+    s = full_sum(opaque(own.len), c, xs);
   }
-  s = s + edge_term(xe, xs, c);
-  float c_own, s_own;
-  wg_pair<NW>(c, s, red_c, red_s, lane, wv, c_own, s_own);
-
+  const float zt = t >= 0 ? zt_raw : 0.f;
   // The pairs of all parts, in LDS: this part's own, the others' as
   // received, or recomputed where a partner's did not arrive in time.
-  float cg = c_own, sx = s_own;
-  if constexpr (P > 1) {
+  float cg, sx;
+  RowResult rr;
+  if constexpr (P == 1) {
+    wg_pair<NW>(c, s, red_c, red_s, lane, wv, cg, sx);
+    fold_target(tin.part, zt, cg, sx);
+    rr = row_finish<OP>(cg, sx, zt, valid, rt.ignored, invB, gmul);
+    if (tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
+  } else {
+    // Each wave's pair goes to LDS; wave 0 alone combines the 16, trades
+    // the part's pair with its partners (thread 0) and, when every pair
+    // has arrived, forms the row's results and leaves them in LDS (fin),
+    // so the other waves run none of that arithmetic.
+    wave_pair_to_lds(c, s, red_c, red_s, lane, wv);
+    __syncthreads();
     // Eight parts keep the loops over partners rolled (less code, and no
     // partner's address or pair held beyond its iteration: the kernel is
     // capped at 64 VGPRs).
     constexpr int kUnrollPartners = P <= 4 ? P : 1;
-    if (tid == 0) {
-      mail_c[part] = c_own;
-      mail_s[part] = s_own;
-      const uint64_t tag = (uint64_t)kMailTag << 32;
-      const uint64_t w0 = tag | __builtin_bit_cast(uint32_t, c_own);
-      const uint64_t w1 = tag | __builtin_bit_cast(uint32_t, s_own);
-      // The publishes are issued without waiting for their results, so the
-      // next poll follows them at once.
-      auto publish = [&] {
+    if (wv == 0) {
+      float c_own, s_own;
+      lds_pairs_combine<NW>(red_c, red_s, lane, c_own, s_own);
+      fold_target(tin.part, zt, c_own, s_own);
+      if (tid == 0) {
+        mail_c[part] = c_own;
+        mail_s[part] = s_own;
+        const uint64_t tag = (uint64_t)kMailTag << 32;
+        const uint64_t w0 = tag | __builtin_bit_cast(uint32_t, c_own);
+        const uint64_t w1 = tag | __builtin_bit_cast(uint32_t, s_own);
+        // The publishes are issued without waiting for their results, so
+        // the next poll follows them at once.
+        auto publish = [&] {
 #pragma unroll kUnrollPartners
-        for (int q = 0; q < P; ++q) {
-          if (q == part) continue;
-          uint64_t* m = mailbox(part_range(geo.nb, P, q)) + mail_index(part, q);
-          uint64_t e0 = kEmptyWord, e1 = kEmptyWord;
-          // a 64-bit compare-and-swap sends 16 bytes of data: the same
-          // wait states as a wide store follow it
-          __hip_atomic_compare_exchange_strong(&m[0], &e0, w0, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-          wide_store_guard();
-          __hip_atomic_compare_exchange_strong(&m[1], &e1, w1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-          wide_store_guard();
-        }
-      };
-      publish();
-      // a bit per part whose pair is here; received pairs go straight to LDS
-      constexpr unsigned kAll = (1u << P) - 1u;
-      unsigned got = 1u << part;
-      for (int it = 0; it < spin && got != kAll; ++it) {
+          for (int q = 0; q < P; ++q) {
+            if (q == part) continue;
+            uint64_t* m = mailbox(part_range(geo.nb, P, q)) + mail_index(part, q);
+            uint64_t e0 = kEmptyWord, e1 = kEmptyWord;
+            // a 64-bit compare-and-swap sends 16 bytes of data: the same
+            // wait states as a wide store follow it
+            __hip_atomic_compare_exchange_strong(&m[0], &e0, w0, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            wide_store_guard();
+            __hip_atomic_compare_exchange_strong(&m[1], &e1, w1, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            wide_store_guard();
+          }
+        };
+        publish();
+        // a bit per part whose pair is here; received pairs go straight to LDS
+        constexpr unsigned kAll = (1u << P) - 1u;
+        unsigned got = 1u << part;
+        for (int it = 0; it < spin && got != kAll; ++it) {
 #pragma unroll kUnrollPartners
-        for (int q = 0; q < P; ++q) {
-          if ((got >> q) & 1u) continue;
-          const uint64_t* m = mine + mail_index(q, part);
-          const uint64_t a = __hip_atomic_load(&m[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const uint64_t b = __hip_atomic_load(&m[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if ((uint32_t)(a >> 32) == kMailTag && (uint32_t)(b >> 32) == kMailTag) {
-            mail_c[q] = __builtin_bit_cast(float, (uint32_t)a);
-            mail_s[q] = __builtin_bit_cast(float, (uint32_t)b);
-            got |= 1u << q;
+          for (int q = 0; q < P; ++q) {
+            if ((got >> q) & 1u) continue;
+            const uint64_t* m = mine + mail_index(q, part);
+            const uint64_t a = __hip_atomic_load(&m[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t b = __hip_atomic_load(&m[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((uint32_t)(a >> 32) == kMailTag && (uint32_t)(b >> 32) == kMailTag) {
+              mail_c[q] = __builtin_bit_cast(float, (uint32_t)a);
+              mail_s[q] = __builtin_bit_cast(float, (uint32_t)b);
+              got |= 1u << q;
+            }
+          }
+          if (got != kAll) {
+            publish();
+            __builtin_amdgcn_s_sleep(8);
           }
         }
-        if (got != kAll) {
-          publish();
-          __builtin_amdgcn_s_sleep(8);
+#pragma unroll
+        for (int q = 0; q < P; ++q) mail_ok[q] = (int)((got >> q) & 1u);
+        fin_ok = got == kAll ? 1 : 0;
+        if (got != kAll && fallbacks != nullptr)
+          atomicAdd(fallbacks, (uint32_t)(P - __builtin_popcount(got)));
+      }
+      // wave 0 reads what its thread 0 wrote to LDS (in order, one wave)
+      if (fin_ok) {
+        combine_pairs<P>(mail_c, mail_s, cg, sx);
+        rr = row_finish<OP>(cg, sx, zt, valid, rt.ignored, invB, gmul);
+        if (part == 0 && tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
+        if (tid == 0) {
+          fin[0] = cg;
+          fin[1] = sx;
+          fin[2] = rr.scale0;
+          fin[3] = rr.scale;
+          fin[4] = rr.gt;
         }
       }
-#pragma unroll
-      for (int q = 0; q < P; ++q) mail_ok[q] = (int)((got >> q) & 1u);
-      if (got != kAll && fallbacks != nullptr)
-        atomicAdd(fallbacks, (uint32_t)(P - __builtin_popcount(got)));
     }
     __syncthreads();
+    if (fin_ok) {  // uniform (LDS, after the barrier): the common case
+      cg = fin[0];
+      sx = fin[1];
+      rr.scale0 = fin[2];
+      rr.scale = fin[3];
+      rr.gt = fin[4];
+    } else {
 #pragma unroll kUnrollPartners
-    for (int q = 0; q < P; ++q) {
-      if (q == part || mail_ok[q]) continue;  // uniform (LDS, after the barrier)
-      // Recompute part q's pair: the same slots, passes, edge and workgroup
-      // reduction as part q runs itself, reading its logits again for each
-      // pass.
-      const PartRange pq = part_range(geo.nb, P, q);
-      const rsrc_t rq = make_rsrc(rp + geo.h + pq.v0 * VE, (uint32_t)pq.len * 16u);
-      const TargetIn tq = target_in(pq);
-      auto load_q = [&](int k) {
-        return slot_words(pq, tq, k, bload128<kPolicyStream>(rq, voff, (uint32_t)k * NT * 16u));
-      };
-      // (rolled loops: one slot's load in flight at a time, beside the
-      // part's own slots held for its gradient)
-      const int nq = (pq.len + NT - 1) / NT;  // slots holding part q's vectors
-      MaxState mq = max_init();
+      for (int q = 0; q < P; ++q) {
+        if (q == part || mail_ok[q]) continue;  // uniform (LDS, after the barrier)
+        // Recompute part q's pair: the same slots, passes, edge and
+        // workgroup reduction as part q runs itself, reading its logits
+        // again for each pass.
+        const PartRange pq = part_range(geo.nb, P, q);
+        const rsrc_t rq = make_rsrc(rp + geo.h + pq.v0 * VE, (uint32_t)pq.len * 16u);
+        const TargetIn tq = target_in(pq);
+        auto load_q = [&](int k) {
+          return slot_words(pq, tq, k, bload128<kPolicyStream>(rq, voff, (uint32_t)k * NT * 16u));
+        };
+        // (rolled loops: one slot's load in flight at a time, beside the
+        // part's own slots held for its gradient)
+        const int nq = (pq.len + NT - 1) / NT;  // slots holding part q's vectors
+        const int xq = edge_elem(q);
+        const float xqv = bload_elem<T>(rrow, (uint32_t)(xq >= 0 ? xq : C) * ES);
+        const float xqs = xq >= 0 ? xqv : kNegInf;
+        auto max_q = [&]() -> float {
+          MaxState mq = max_init();
 #pragma unroll 1
-      for (int k = 0; k < nq; ++k) max_add(mq, load_q(k));
-      if (max_needs_neg(mq)) {
+          for (int k = 0; k < nq; ++k) max_add(mq, load_q(k));
+          if (max_needs_neg(mq)) {
 #pragma unroll 1
-        for (int k = 0; k < nq; ++k) max_add_neg(mq, load_q(k));
-      }
-      const int xq = edge_elem(q);
-      const float xqv = bload_elem<T>(rrow, (uint32_t)(xq >= 0 ? xq : C) * ES);
-      const float xqs = xq >= 0 ? xqv : kNegInf;
-      const float cq = pair_c(max_value(mq), xq, xqs, tq.part, zt);
-      float sq = 0.f;
+            for (int k = 0; k < nq; ++k) max_add_neg(mq, load_q(k));
+          }
+          return max_value(mq);
+        };
+        auto sum_q = [&](float c_) -> float {
+          float s_ = 0.f;
 #pragma unroll 1
-      for (int k = 0; k < nq; ++k) {
-        float e[VE];
-        sq = sq + slot_terms(load_q(k), cq, e);
+          for (int k = 0; k < nq; ++k) {
+            float e[VE];
+            s_ = s_ + slot_terms(load_q(k), c_, e);
+          }
+          return s_ + edge_term(xq, xqs, c_);
+        };
+        float cq, sq;
+        if constexpr (kFirstSlotC) {
+          float c0 = kLowest;
+          if (0 < pq.len) {
+            MaxState m0 = max_init();
+            const u32x4 w0 = load_q(0);
+            max_add(m0, w0);
+            if (max_needs_neg(m0)) max_add_neg(m0, w0);
+            c0 = fmax2(max_value(m0) * kLog2e, kLowest);
+          }
+          cq = c0;
+          sq = sum_q(c0);
+          if (!(sq < __builtin_inff())) {
+            cq = pair_c(max_q(), xq, xqs);
+            sq = sum_q(cq);
+          }
+        } else {
+          cq = pair_c(max_q(), xq, xqs);
+          sq = sum_q(cq);
+        }
+        float cr, sr;
+        wg_pair<NW>(cq, sq, red_c, red_s, lane, wv, cr, sr);
+        fold_target(tq.part, zt, cr, sr);
+        if (tid == 0) {
+          mail_c[q] = cr;
+          mail_s[q] = sr;
+        }
+        __syncthreads();  // the pair is in LDS; red_c / red_s may be used again
       }
-      sq = sq + edge_term(xq, xqs, cq);
-      float cr, sr;
-      wg_pair<NW>(cq, sq, red_c, red_s, lane, wv, cr, sr);
-      if (tid == 0) {
-        mail_c[q] = cr;
-        mail_s[q] = sr;
-      }
-      __syncthreads();  // the pair is in LDS; red_c / red_s may be used again
+      combine_pairs<P>(mail_c, mail_s, cg, sx);
+      rr = row_finish<OP>(cg, sx, zt, valid, rt.ignored, invB, gmul);
+      if (part == 0 && tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
     }
-    // Combine the parts' pairs in part order.
-    cg = mail_c[0];
-#pragma unroll
-    for (int q = 1; q < P; ++q) cg = fmax2(cg, mail_c[q]);
-    // the maxima are read from LDS again rather than kept in registers
-    if constexpr (P > 4) asm volatile("" ::: "memory");
-    sx = mail_s[0] * exp2_hw(mail_c[0] - cg);
-#pragma unroll
-    for (int q = 1; q < P; ++q) sx = sx + mail_s[q] * exp2_hw(mail_c[q] - cg);
   }
-  const RowResult rr = row_finish<OP>(cg, sx, zt, valid, rt.ignored, invB, gmul);
-  if (part == 0 && tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
 
   // Phase C: the gradient of this part from registers and LDS.
 #pragma unroll
@@ -590,14 +737,22 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       // slots whose terms 2^(z log2e - c) wait in LDS: times 2^(c - c')
       // (and gmul), the same value up to the rounding of one multiply
       if constexpr (kLdsTerms > 0) {
+        // The kept terms are relative to the thread's c (its first slot's
+        // maximum): where 2^(c - c') would lose precision below the normal
+        // range, those slots are formed again from their logits.
         const float kfactor = kUnit ? exp2_hw(c - cp) : exp2_hw(c - cp) * gmul;
+        const bool from_terms = c - cp >= -120.f;
 #pragma unroll
         for (int k = 0; k < kLdsTerms; ++k) {
           if (k * NT >= len) continue;
-          const f32x4 a = kept[(2 * k) * NT + tid], b = kept[(2 * k + 1) * NT + tid];
-          const float g[VE] = {a.x * kfactor, a.y * kfactor, a.z * kfactor, a.w * kfactor,
-                               b.x * kfactor, b.y * kfactor, b.z * kfactor, b.w * kfactor};
-          bstore128<kPolicyStream>(E::pack(g), rout, voff, (uint32_t)k * NT * 16u);
+          if (from_terms) {
+            const f32x4 a = kept[(2 * k) * NT + tid], b = kept[(2 * k + 1) * NT + tid];
+            const float g[VE] = {a.x * kfactor, a.y * kfactor, a.z * kfactor, a.w * kfactor,
+                                 b.x * kfactor, b.y * kfactor, b.z * kfactor, b.w * kfactor};
+            bstore128<kPolicyStream>(E::pack(g), rout, voff, (uint32_t)k * NT * 16u);
+          } else {
+            write_slot(k, v[k]);
+          }
         }
       }
 #pragma unroll
