@@ -120,20 +120,36 @@ class HipEvents:
 # 692 us per step without events, 699 us with a pair on every ce_fwd_grad,
 # whether recorded by torch around the call or attached to the launch): the
 # timestamps are taken after a system-scope release at the kernel's end.
-# The timed loop therefore attaches a pair to every EVENT_EVERY-th step.
+# The timed loop therefore attaches a pair to every EVENT_EVERY-th step,
+# from the fourth on: by then the host is ahead of the GPU, so the slower
+# host path of an armed launch does not leave the GPU idle; and never to
+# the last step, whose event completion would otherwise add its latency to
+# the wall clock (measured on 2,097,152 x 10 fp32 rows, 20 steps: 40.3 us
+# per step with pairs on steps 0, 5, 10 and 15, 38.7 us on 4, 9, 14 and 19,
+# 37.1 us with none).
 EVENT_EVERY = 5
+EVENT_OFFSET = 3
+
+
+def timed_step_indices(steps: int) -> list:
+    """The timed steps whose ce_fwd_grad launch carries an event pair:
+    EVENT_OFFSET, EVENT_OFFSET + EVENT_EVERY, ..., never the last of more
+    than one step, and at least one."""
+    last = steps - 1 if steps > 1 else steps
+    idx = list(range(min(EVENT_OFFSET, max(last - 1, 0)), last, EVENT_EVERY))
+    return idx or [0]
 
 
 def time_steps(zd, td, grad, loss_rows, loss, ws, steps: int, warmup: int) -> dict:
     """W untimed steps, then K steps timed by the wall clock between two
-    device synchronisations.  Every EVENT_EVERY-th timed ce_fwd_grad launch
-    (from the first) records a pair of HIP events at its kernel's own start
-    and end (ce_debug_time_next_launch) on the stream it runs on; those
-    give the kernel's duration."""
+    device synchronisations.  The ce_fwd_grad launches of the steps
+    timed_step_indices(K) record a pair of HIP events at their kernel's own
+    start and end (ce_debug_time_next_launch) on the stream they run on;
+    those give the kernel's duration."""
     import torch
     import softmax_cross_entropy_ce_amd as ce
     hev = HipEvents()
-    timed = list(range(0, steps, EVENT_EVERY))
+    timed = timed_step_indices(steps)
     pairs = dict(zip(timed, hev.pairs(len(timed))))
     for _ in range(warmup):
         ce.fwd_grad_into(zd, td, grad, loss_rows)
@@ -690,7 +706,8 @@ def main() -> None:
                         "min": round(min(fwd_ms), 5), "max": round(max(fwd_ms), 5),
                         "timed_steps": res["timed_steps"],
                         "how": "HIP events attached to the kernel's launch "
-                               f"(every {EVENT_EVERY}th timed step)"},
+                               f"(every {EVENT_EVERY}th timed step from step {EVENT_OFFSET}, "
+                               "never the last)"},
         "timed_region_s": round(res["timed_region_s"], 6),
         "reduce_ms": {"mean": round(statistics.fmean(red_ms), 5),
                       "median": round(statistics.median(red_ms), 5)},

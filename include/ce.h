@@ -207,7 +207,8 @@ size_t ce_reduce_workspace_bytes(int64_t B);
  * read back as 4 bytes only when the caller wants it).
  *
  *   loss_rows        [B] float32 (the loss_out of ce_fwd_grad).
- *   B                number of rows, >= 1.
+ *   B                number of rows, 1 <= B <= 2^39 (CE_ERR_SHAPE above:
+ *                    a first-level chunk's bytes must fit 32 bits).
  *   loss_scalar_out  [1] float32, overwritten with sum_b loss_rows[b].
  *   workspace        device scratch of at least ce_reduce_workspace_bytes(B)
  *                    bytes (may be NULL when that is 0); contents on entry

@@ -192,23 +192,19 @@ bool short_span_ok(int64_t C, int64_t ld, int es) {
 int resident_blocks(const void* kernel, int nt, std::atomic<int>& per_cu_cache);
 
 // Rows of at most 64 bytes, contiguous, in 16-byte aligned arrays: the
-// LDS-staged kernel, persistent over chunks of 256 * R rows (R rows per
-// thread, below).  Rows of more than 32 bytes take one per thread (two,
-// with half as many workgroups resident, measured slower on 40-byte rows).
+// LDS-staged kernel, one chunk of 64 * R rows per wave (R rows per lane,
+// below), four waves per workgroup.  Rows of more than 32 bytes take one
+// per lane.
 constexpr int kTinyRowsPerThread = 1;
 
 template <typename T, int CMAX, int R, int OP, bool GRAD, bool PAD>
 int launch_tiny_w(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
                   float* l, hipStream_t st) {
   auto kern = ce::ce_tiny_kernel<T, CMAX, R, GRAD, OP, PAD>;
-  static std::atomic<int> occupancy{0};
-  const int res = resident_blocks(reinterpret_cast<const void*>(kern), ce::kTinyThreads, occupancy);
-  if (res < 1) return CE_ERR_LAUNCH;
-  const int64_t rows = (int64_t)ce::kTinyThreads * R;
-  const int64_t chunks = (B + rows - 1) / rows;
-  const int64_t grid = chunks < res ? chunks : res;
+  const int64_t rows = (int64_t)ce::kTinyThreads * R;   // rows of one workgroup's four chunks
+  const int64_t grid = (B + rows - 1) / rows;            // B < 2^31: at most 2^23 workgroups
   ce_host::launch(kern, dim3((unsigned)grid), dim3(ce::kTinyThreads), 0, st, z, t, B, (int)C, rs,
-                     g, l);
+                  g, l);
   return launched();
 }
 
@@ -227,21 +223,23 @@ int launch_tiny_p(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArg
   return launch_tiny_w<T, CMAX, R, OP, GRAD, false>(z, t, B, C, rs, g, l, st);
 }
 
-// Rows per thread: rows of at most 8 bytes take four per thread and rows
-// of at most 32 bytes two, so that a chunk (and the loads in flight) is not
-// a few KB; longer rows one.  (Measured on rows filling 1 GiB: fp32 rows of
-// 6 and 8 elements went from 65 and 86 % of a copy's rate to 74 and 89 %,
-// 4-element bf16 rows from 30 to 35 %; four 16-byte rows per thread were
-// slower than two.)
+// Rows per lane: 16-bit rows of at most 8 elements take four per lane, other
+// rows of at most 32 bytes two, longer rows one, so that a wave's chunk
+// (and the loads in flight) is not a few hundred bytes.  Measured on rows
+// filling 256 MB, GB/s of logits and gradient for one, two and four rows
+// per lane: fp32 C = 2: 2033, 2520, 2329; fp32 C = 6: 4831, 5450, 4981;
+// fp32 C = 8: 5767, 5989, 5355; bf16 C = 4: 2052, 2467, 2744; bf16 C = 8:
+// 3612, 4172, 4367 (a copy of the same bytes: 6080-6180).
 template <typename T, int CMAX, int OP, bool GRAD>
 int launch_tiny_c(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
                   float* l, hipStream_t st) {
-  const int64_t rb = C * (int64_t)sizeof(T);
-  if constexpr (CMAX * sizeof(T) <= 32) {
-    if (rb <= 8) return launch_tiny_p<T, CMAX, 4, OP, GRAD>(z, t, B, C, rs, g, l, st);
-    if (rb <= 32) return launch_tiny_p<T, CMAX, 2, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  if constexpr (sizeof(T) == 2 && CMAX == 8) {
+    return launch_tiny_p<T, CMAX, 4, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  } else if constexpr (CMAX * sizeof(T) <= 32) {
+    return launch_tiny_p<T, CMAX, 2, OP, GRAD>(z, t, B, C, rs, g, l, st);
+  } else {
+    return launch_tiny_p<T, CMAX, kTinyRowsPerThread, OP, GRAD>(z, t, B, C, rs, g, l, st);
   }
-  return launch_tiny_p<T, CMAX, kTinyRowsPerThread, OP, GRAD>(z, t, B, C, rs, g, l, st);
 }
 
 template <typename T, int OP, bool GRAD>
@@ -608,20 +606,22 @@ bool overlaps(uintptr_t a, uintptr_t an, uintptr_t b, uintptr_t bn) {
 // ------------------------------------------------------------ reduction
 // Up to kReduceOneLaunch rows one workgroup sums them in a single launch.
 // Above, the first level has up to kReduceMaxBlocks workgroups with chunks
-// of at least kReduceMinChunk rows (2048: 8 per thread), so that the whole
-// GPU reads the rows, then one workgroup sums the partials.
+// of whole rounds of ce::kReduceRound rows (2048: eight per thread, all
+// loaded at once), so that the whole GPU reads the rows in as few rounds as
+// possible, then one workgroup sums the partials.
 constexpr int64_t kReduceOneLaunch = 16384;
 static_assert(kReduceOneLaunch == ce::kReduceOneMax, "one launch sums what one workgroup holds");
-constexpr int64_t kReduceMinChunk = 2048;
 constexpr int64_t kReduceMaxBlocks = 1024;
 constexpr int kMaxDevicesReduce = 64;
+// a first-level chunk's bytes must fit the 32-bit range of a buffer resource
+constexpr int64_t kReduceMaxChunk = (int64_t)1 << 29;
+constexpr int64_t kReduceMaxRows = kReduceMaxChunk * kReduceMaxBlocks;
 
 int64_t reduce_chunk(int64_t B) {
   if (B <= kReduceOneLaunch) return kReduceOneLaunch;
-  const int64_t step = 4 * ce::kReduceThreads;
-  int64_t chunk = (B + kReduceMaxBlocks - 1) / kReduceMaxBlocks;
-  chunk = (chunk + step - 1) / step * step;
-  return chunk < kReduceMinChunk ? kReduceMinChunk : chunk;
+  const int64_t step = ce::kReduceRound;
+  const int64_t chunk = (B + kReduceMaxBlocks - 1) / kReduceMaxBlocks;
+  return (chunk + step - 1) / step * step;
 }
 
 int64_t reduce_blocks(int64_t B) { return (B + reduce_chunk(B) - 1) / reduce_chunk(B); }
@@ -1232,7 +1232,7 @@ int ce_shard_grad(const void* logits, const int32_t* targets, int64_t B, int64_t
 }
 
 size_t ce_reduce_workspace_bytes(int64_t B) {
-  if (B <= 0) return 0;
+  if (B <= 0 || B > kReduceMaxRows) return 0;
   const int64_t blocks = reduce_blocks(B);
   return blocks > 1 ? (size_t)blocks * sizeof(float) : 0;
 }
@@ -1240,7 +1240,7 @@ size_t ce_reduce_workspace_bytes(int64_t B) {
 int ce_reduce_loss(const float* loss_rows, int64_t B, float* loss_scalar_out, void* workspace,
                    size_t workspace_bytes, void* stream) {
   if (!loss_rows || !loss_scalar_out) return CE_ERR_NULL;
-  if (B <= 0) return CE_ERR_SHAPE;
+  if (B <= 0 || B > kReduceMaxRows) return CE_ERR_SHAPE;
   if ((uintptr_t)loss_rows % 4 || (uintptr_t)loss_scalar_out % 4) return CE_ERR_ALIGN;
   const size_t need = ce_reduce_workspace_bytes(B);
   if (need && (!workspace || workspace_bytes < need)) return CE_ERR_WORKSPACE;
@@ -1254,6 +1254,7 @@ int ce_reduce_loss_noalloc(const float* loss_rows, int64_t B, float* loss_scalar
   if (B <= 0 || B > CE_NOALLOC_MAX_ROWS) return CE_ERR_SHAPE;
   if ((uintptr_t)loss_rows % 4 || (uintptr_t)loss_scalar_out % 4) return CE_ERR_ALIGN;
   float* part = nullptr;
+  static_assert(CE_NOALLOC_MAX_ROWS <= kReduceMaxRows, "noalloc range within the tree's");
   if (reduce_blocks(B) > 1) {
     if (reduce_blocks(B) > kReduceMaxBlocks) return CE_ERR_SHAPE;
     const int rc = reduce_scratch_ptr(&part);

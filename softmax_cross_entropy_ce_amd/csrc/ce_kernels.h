@@ -114,19 +114,30 @@ __global__ __launch_bounds__(kShortThreads) void ce_short_kernel(
 
 // ===========================================================================
 // Path 1, rows of at most 64 bytes (fp32 C <= 16, bf16/fp16 C <= 32) with
-// contiguous rows and 16-byte aligned arrays.  A chunk of 256 * R rows is
-// at most R * 16 KB and starts on a 16-byte boundary (256 * C * size is a
-// multiple of 16), so the workgroup reads it with whole 16-byte loads into
-// LDS; each thread reduces R rows from LDS without any cross-lane step and
-// writes their gradients back into LDS, and the chunk leaves with whole
-// 16-byte stores.  The workgroups are persistent and keep the loads of the
-// next two chunks in flight, in two register sets used in turn (each set
-// is refilled as soon as its chunk is in LDS, before this chunk's stores).
-// The last, partial chunk of a call is moved one element per thread
-// instead.
+// contiguous rows and 16-byte aligned arrays.  Each wave owns one chunk of
+// 64 * R rows: at most R * 4 KB, and a whole number of 16-byte vectors
+// (64 * C * size is a multiple of 16), so the wave reads it with whole
+// 16-byte loads into its own LDS slot; each lane reduces R rows from LDS
+// without any cross-lane step and writes their gradients back into the
+// slot, and the chunk leaves with whole 16-byte stores.  A wave touches no
+// other wave's slot, and one wave's LDS operations complete in issue
+// order, so no workgroup barrier is needed.  The grid has one wave per
+// chunk: the hardware dispatcher keeps every CU filled to the end (a
+// persistent grid over the same chunks left CUs idle at the tail, and its
+// barriers stalled all four waves of a workgroup on the slowest).  The
+// last, partial chunk of a call is moved one element per lane instead.
 // ===========================================================================
 constexpr int kTinyThreads = 256;
+constexpr int kTinyWaves = kTinyThreads / 64;
 constexpr int kTinyRowBytes = 64;   // largest row
+
+// Orders one wave's LDS accesses on either side (the hardware keeps them
+// in order; this keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <typename T>
 struct LdsElem;
@@ -158,8 +169,8 @@ struct LdsElem<_Float16> {
   }
 };
 
-// CMAX: the row length rounded up to 8, 16 or 32 elements (at most 64
-// bytes), the width of each thread's per-row arrays.  R: rows per thread.
+// CMAX: the row length rounded up to 8, 12, 16 or 32 elements (at most 64
+// bytes), the width of each lane's per-row arrays.  R: rows per lane.
 template <typename T, int CMAX, int R, bool GRAD, int OP = kOpCE, bool PAD = false>
 __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restrict__ logits,
                                                                const int32_t* __restrict__ targets,
@@ -167,24 +178,28 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
                                                                T* __restrict__ grad,
                                                                float* __restrict__ loss_rows) {
   using E = Elem<T>;
-  constexpr int ES = sizeof(T), NT = kTinyThreads, ROWS = NT * R;
-  constexpr int K = (ROWS * CMAX * ES + 16 * NT - 1) / (16 * NT);  // 16-byte loads per thread
+  constexpr int ES = sizeof(T), ROWS = 64 * R;                     // rows of a wave's chunk
+  constexpr int K = (ROWS * CMAX * ES + 16 * 64 - 1) / (16 * 64);  // 16-byte loads per lane
   static_assert(CMAX * ES <= kTinyRowBytes, "row width");
   // PAD: rows of whole 32-bit words (C * size a multiple of 4) sit in LDS at
-  // an odd stride of RS words, so that the threads of a wave, each reading
+  // an odd stride of RS words, so that the lanes of a wave, each reading
   // its own row, hit different banks (at the row's own stride of 4, 8, 12
   // or 16 words they would share a few).
   constexpr int EPW = 4 / ES;                 // elements per word
   constexpr int RDMAX = CMAX / EPW;           // words of the widest row
-  constexpr int STAGE = PAD ? (ROWS * (RDMAX | 1) + 3) / 4 : NT * K;
+  constexpr int SLOT = PAD ? (ROWS * (RDMAX | 1) + 3) / 4 : 64 * K;   // 16-byte units
   static_assert(!PAD || CMAX % EPW == 0, "whole words");
-  __shared__ u32x4 stage[STAGE];
+  __shared__ u32x4 slots[kTinyWaves][SLOT];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  u32x4* const stage = slots[wave];
   unsigned* const sw = reinterpret_cast<unsigned*>(stage);
   const float invB = row_invB(rs), gmul = grad_mul(rs);
-  const int tid = threadIdx.x;
-  const uint32_t voff = (uint32_t)tid * 16u;
-  const int64_t nchunks = (B + ROWS - 1) / ROWS;
-  const int64_t nfull = B / ROWS;             // chunks of exactly ROWS rows
+  const uint32_t voff = (uint32_t)lane * 16u;
+  const int64_t row0 = ((int64_t)blockIdx.x * kTinyWaves + wave) * ROWS;
+  if (row0 >= B) return;                      // wave-uniform
+  const bool full = row0 + ROWS <= B;
+  const int nrows = full ? ROWS : (int)(B - row0);
   const uint32_t full_bytes = (uint32_t)(ROWS * C * ES);
   const int nvec = (int)(full_bytes / 16);    // 16-byte vectors of a full chunk
   // PAD: words per row (4, 8, 12 or 16: the host pads rows of a multiple of
@@ -210,147 +225,114 @@ __global__ __launch_bounds__(kTinyThreads) void ce_tiny_kernel(const T* __restri
       return i;
     }
   };
-  int64_t chunk = blockIdx.x;
-  if (chunk >= nchunks) return;
 
-  // a chunk's loads: its data, and the targets of this thread's rows (so
-  // that no target load waits on the chunk's critical path)
-  auto load_full = [&](int64_t ch, u32x4 (&v)[K], int32_t (&tg)[R]) {
-    const rsrc_t r = make_rsrc(logits + ch * ROWS * C, full_bytes);
+  // the chunk's loads, and the targets of this lane's rows, all in flight
+  // before the first is used
+  u32x4 v[K];
+  int32_t tg[R];
+  if (full) {
+    const rsrc_t r = make_rsrc(logits + row0 * C, full_bytes);
 #pragma unroll
-    for (int k = 0; k < K; ++k) v[k] = bload128<kPolicyStream>(r, voff, (uint32_t)k * NT * 16u);
+    for (int k = 0; k < K; ++k) v[k] = bload128<kPolicyStream>(r, voff, (uint32_t)k * 64u * 16u);
     if constexpr (OP != kOpSoftmax) {
 #pragma unroll
-      for (int j = 0; j < R; ++j) tg[j] = targets[ch * ROWS + tid + j * NT];
+      for (int j = 0; j < R; ++j) tg[j] = targets[row0 + lane + j * 64];
     }
-  };
-  const int64_t G = gridDim.x;
-  // one chunk: into LDS from its register set, which is then refilled with
-  // the chunk two steps ahead, so two chunks' loads are in flight while
-  // this one is reduced and stored
-  auto step = [&](u32x4 (&r)[K], int32_t (&tg)[R], int64_t ch) {
-    const int64_t row0 = ch * ROWS;
-    const bool full = ch < nfull;
-    const int nrows = full ? ROWS : (int)(B - row0);
-    if (full) {
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const int gv = tid + k * NT;
-        if (gv >= nvec) continue;
-        if constexpr (PAD) {
-          sw[word_slot(4 * gv + 0)] = r[k].x;
-          sw[word_slot(4 * gv + 1)] = r[k].y;
-          sw[word_slot(4 * gv + 2)] = r[k].z;
-          sw[word_slot(4 * gv + 3)] = r[k].w;
-        } else {
-          stage[gv] = r[k];
+    for (int k = 0; k < K; ++k) {
+      const int gv = lane + k * 64;
+      if (gv >= nvec) continue;
+      if constexpr (PAD) {
+        sw[word_slot(4 * gv + 0)] = v[k].x;
+        sw[word_slot(4 * gv + 1)] = v[k].y;
+        sw[word_slot(4 * gv + 2)] = v[k].z;
+        sw[word_slot(4 * gv + 3)] = v[k].w;
+      } else {
+        stage[gv] = v[k];
+      }
+    }
+  } else {
+    for (int i = lane; i < nrows * C; i += 64)
+      LdsElem<T>::put(stage, elem_slot(i), E::load1(logits + row0 * C + i));
+  }
+  wave_lds_sync();
+
+  // rows lane, lane + 64, ... of the chunk
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int lr = lane + j * 64;
+    if (lr >= nrows) break;
+    const int64_t row = row0 + lr;
+    const RowTarget rt = full ? row_target_of<OP>(OP != kOpSoftmax ? tg[j] : -1, C, rs)
+                              : row_target<OP>(targets, row, C, rs);
+    const int t = rt.t;
+    float f[CMAX];
+    float m = kNegInf;
+    if constexpr (PAD) {
+#pragma unroll
+      for (int k = 0; k < RDMAX; ++k) {
+        const unsigned w = k < RD ? sw[lr * RS + k] : 0u;
+#pragma unroll
+        for (int q = 0; q < EPW; ++q) {
+          const int c = k * EPW + q;
+          f[c] = c < C ? widen_half<T>(w, q) : kNegInf;
         }
       }
     } else {
-      for (int i = tid; i < nrows * C; i += NT)
-        LdsElem<T>::put(stage, elem_slot(i), E::load1(logits + row0 * C + i));
-    }
-    // this chunk's targets, before the register set is refilled
-    RowTarget rts[R];
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const int lr = tid + j * NT;
-      rts[j] = !full && lr < nrows ? row_target<OP>(targets, row0 + lr, C, rs)
-                                   : row_target_of<OP>(full ? tg[j] : -1, C, rs);
+      for (int c = 0; c < CMAX; ++c) f[c] = c < C ? LdsElem<T>::get(stage, lr * C + c) : kNegInf;
     }
-    __syncthreads();
-    if (ch + 2 * G < nfull) load_full(ch + 2 * G, r, tg);
-
-    // rows tid, tid + NT, ... of the chunk
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const int lr = tid + j * NT;
-      if (lr >= nrows) break;
-      const int64_t row = row0 + lr;
-      const RowTarget rt = rts[j];
-      const int t = rt.t;
-      float f[CMAX];
-      float m = kNegInf;
+    for (int c = 0; c < CMAX; ++c) m = fmax2(m, f[c]);
+    const float cg = m * kLog2e;
+    float e[CMAX];
+    float zt = 0.f;
+#pragma unroll
+    for (int c = 0; c < CMAX; ++c) {
+      zt = (c == t) ? f[c] : zt;
+      e[c] = (c == t) ? 0.f : exp2_hw(__builtin_fmaf(f[c], kLog2e, -cg));
+    }
+    const float sx = tree_sum(e);
+    const RowResult rr = row_finish<OP>(cg, sx, zt, rt.valid, rt.ignored, invB, gmul);
+    store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
+    if constexpr (GRAD) {
+      // the terms of the sum are the unnormalised softmax: scaled, they
+      // are the gradient (the target's term was left out of the sum)
+      float g[CMAX];
+#pragma unroll
+      for (int c = 0; c < CMAX; ++c) g[c] = c == t ? rr.gt : e[c] * rr.scale;
       if constexpr (PAD) {
 #pragma unroll
-        for (int k = 0; k < RDMAX; ++k) {
-          const unsigned w = k < RD ? sw[lr * RS + k] : 0u;
-#pragma unroll
-          for (int q = 0; q < EPW; ++q) {
-            const int c = k * EPW + q;
-            f[c] = c < C ? widen_half<T>(w, q) : kNegInf;
-          }
-        }
+        for (int k = 0; k < RDMAX; ++k)
+          if (k < RD) sw[lr * RS + k] = pack_word<T>(&g[k * EPW]);
       } else {
 #pragma unroll
-        for (int c = 0; c < CMAX; ++c) f[c] = c < C ? LdsElem<T>::get(stage, lr * C + c) : kNegInf;
+        for (int c = 0; c < CMAX; ++c)
+          if (c < C) LdsElem<T>::put(stage, lr * C + c, g[c]);
       }
+    }
+  }
+  if constexpr (GRAD) {
+    wave_lds_sync();
+    if (full) {
+      const rsrc_t ro = make_rsrc(grad + row0 * C, full_bytes);
 #pragma unroll
-      for (int c = 0; c < CMAX; ++c) m = fmax2(m, f[c]);
-      const float cg = m * kLog2e;
-      float e[CMAX];
-      float zt = 0.f;
-#pragma unroll
-      for (int c = 0; c < CMAX; ++c) {
-        zt = (c == t) ? f[c] : zt;
-        e[c] = (c == t) ? 0.f : exp2_hw(__builtin_fmaf(f[c], kLog2e, -cg));
-      }
-      const float sx = tree_sum(e);
-      const RowResult rr = row_finish<OP>(cg, sx, zt, rt.valid, rt.ignored, invB, gmul);
-      store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
-      if constexpr (GRAD) {
-        // the terms of the sum are the unnormalised softmax: scaled, they
-        // are the gradient (the target's term was left out of the sum)
-        float g[CMAX];
-#pragma unroll
-        for (int c = 0; c < CMAX; ++c) g[c] = c == t ? rr.gt : e[c] * rr.scale;
+      for (int k = 0; k < K; ++k) {
+        const int gv = lane + k * 64;
+        if (gv >= nvec) continue;
+        u32x4 w;
         if constexpr (PAD) {
-#pragma unroll
-          for (int k = 0; k < RDMAX; ++k)
-            if (k < RD) sw[lr * RS + k] = pack_word<T>(&g[k * EPW]);
+          w = u32x4{sw[word_slot(4 * gv + 0)], sw[word_slot(4 * gv + 1)],
+                    sw[word_slot(4 * gv + 2)], sw[word_slot(4 * gv + 3)]};
         } else {
-#pragma unroll
-          for (int c = 0; c < CMAX; ++c)
-            if (c < C) LdsElem<T>::put(stage, lr * C + c, g[c]);
+          w = stage[gv];
         }
+        bstore128<kPolicyStream>(w, ro, voff, (uint32_t)k * 64u * 16u);
       }
+    } else {
+      for (int i = lane; i < nrows * C; i += 64)
+        E::store1(grad + row0 * C + i, LdsElem<T>::get(stage, elem_slot(i)));
     }
-    if constexpr (GRAD) {
-      __syncthreads();
-      if (full) {
-        const rsrc_t ro = make_rsrc(grad + row0 * C, full_bytes);
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const int gv = tid + k * NT;
-          if (gv >= nvec) continue;
-          u32x4 w;
-          if constexpr (PAD) {
-            w = u32x4{sw[word_slot(4 * gv + 0)], sw[word_slot(4 * gv + 1)],
-                      sw[word_slot(4 * gv + 2)], sw[word_slot(4 * gv + 3)]};
-          } else {
-            w = stage[gv];
-          }
-          bstore128<kPolicyStream>(w, ro, voff, (uint32_t)k * NT * 16u);
-        }
-      } else {
-        for (int i = tid; i < nrows * C; i += NT)
-          E::store1(grad + row0 * C + i, LdsElem<T>::get(stage, elem_slot(i)));
-      }
-    }
-    __syncthreads();  // the stage is refilled by the next step
-  };
-
-  u32x4 v[K], u[K];
-  int32_t tv[R], tu[R];
-  if (chunk < nfull) load_full(chunk, v, tv);
-  if (chunk + G < nfull) load_full(chunk + G, u, tu);
-  for (;;) {
-    step(v, tv, chunk);
-    chunk += G;
-    if (chunk >= nchunks) break;
-    step(u, tu, chunk);
-    chunk += G;
-    if (chunk >= nchunks) break;
   }
 }
 
@@ -1014,14 +996,20 @@ __global__ __launch_bounds__(1024) void ce_row_lds_kernel(const T* __restrict__ 
 
 // ===========================================================================
 // Loss reduction: a fixed two-level tree.  Workgroup g of the first level
-// sums the contiguous range [g*chunk, (g+1)*chunk) of the input; each
-// thread adds its elements i, i+256, ... in order into four interleaved
-// accumulators, and the workgroup combines its threads with DPP/ds_swizzle
-// and four LDS slots in a fixed order.  The second level is the same code
-// over the first level's partial sums.  Nothing depends on timing, so the
-// result is reproducible bit for bit.
+// sums the contiguous range [g*chunk, (g+1)*chunk) of the input (chunk a
+// multiple of kReduceRound); in each round of kReduceRound values, thread i
+// loads values i, i+256, ..., i+1792 of the round (eight 4-byte loads, all
+// in flight at once; values past the range read as 0 through the buffer
+// resource, and adding +0 leaves a sum unchanged) and adds each into its own
+// accumulator, so every accumulator takes its values in index order.  The
+// workgroup combines its threads with DPP/ds_swizzle and four LDS slots in
+// a fixed order.  The second level is ce_reduce_one_kernel over the first
+// level's partial sums.  Nothing depends on timing, so the result is
+// reproducible bit for bit.
 // ===========================================================================
 constexpr int kReduceThreads = 256;
+constexpr int kReduceLoads = 8;                               // per thread per round
+constexpr int kReduceRound = kReduceThreads * kReduceLoads;   // values per round
 
 __device__ __forceinline__ float block_sum_256(float v) {
   __shared__ float part[kReduceThreads / 64];
@@ -1035,22 +1023,24 @@ __global__ __launch_bounds__(kReduceThreads) void ce_reduce_kernel(const float* 
                                                                    int64_t n, int64_t chunk,
                                                                    float* __restrict__ out) {
   const int64_t lo = (int64_t)blockIdx.x * chunk;
-  const int64_t hi = (lo + chunk) < n ? (lo + chunk) : n;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  int64_t i = lo + threadIdx.x;
-  // unrolled so that 16 loads per thread are in flight; each accumulator
-  // still adds its elements in index order
-#pragma unroll 4
-  for (; i + 3 * kReduceThreads < hi; i += 4 * kReduceThreads) {
-    a0 += in[i];
-    a1 += in[i + kReduceThreads];
-    a2 += in[i + 2 * kReduceThreads];
-    a3 += in[i + 3 * kReduceThreads];
+  const int64_t len = (lo + chunk) < n ? chunk : n - lo;     // <= chunk < 2^30 (host check)
+  const rsrc_t r = make_rsrc(in + lo, (uint32_t)len * 4u);
+  const int rounds = (int)(chunk / kReduceRound);
+  const uint32_t voff = threadIdx.x * 4u;
+  float a[kReduceLoads];
+#pragma unroll
+  for (int k = 0; k < kReduceLoads; ++k) a[k] = 0.f;
+  for (int it = 0; it < rounds; ++it) {
+    float x[kReduceLoads];
+#pragma unroll
+    for (int k = 0; k < kReduceLoads; ++k)
+      x[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           r, (int)voff, (it * kReduceRound + k * kReduceThreads) * 4,
+                                           kPolicyDefault));
+#pragma unroll
+    for (int k = 0; k < kReduceLoads; ++k) a[k] = a[k] + x[k];
   }
-  if (i < hi) a0 += in[i];
-  if (i + kReduceThreads < hi) a1 += in[i + kReduceThreads];
-  if (i + 2 * kReduceThreads < hi) a2 += in[i + 2 * kReduceThreads];
-  const float tot = block_sum_256((a0 + a1) + (a2 + a3));
+  const float tot = block_sum_256(((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7])));
   if (threadIdx.x == 0) out[blockIdx.x] = tot;
 }
 

@@ -99,8 +99,12 @@ def test_reduce_workspace_sizes():
     # up to 16384 rows one workgroup sums them in a single launch
     assert f(1) == 0 and f(8) == 0 and f(2048) == 0 and f(16384) == 0
     assert f(16385) == 9 * 4                                # chunks of 2048 rows
-    # 2M rows: at most 1024 first-level partial sums
-    assert 0 < f(2_097_152) <= 1024 * 4
+    # 2M rows: 1024 first-level partial sums of one 2048-row round each
+    assert f(2_097_152) == 1024 * 4
+    # chunks are whole rounds of 2048 rows: 3M rows take chunks of 4096
+    assert f(3_000_001) == 733 * 4
+    # past 2^39 rows a chunk's bytes would not fit a buffer resource
+    assert f(1 << 39) == 1024 * 4 and f((1 << 39) + 1) == 0
 
 
 def red(x=L, B=8, out=G, ws=None, wsb=0):
@@ -111,6 +115,7 @@ def test_reduce_loss_validation():
     assert red(x=None) == NULL
     assert red(out=None) == NULL
     assert red(B=0) == SHAPE
+    assert red(B=(1 << 39) + 1) == SHAPE
     assert red(x=L + 2) == ALIGN
     assert red(B=1 << 20) == WORKSPACE                      # workspace needed, none given
     need = ce.reduce_workspace_bytes(1 << 20)
