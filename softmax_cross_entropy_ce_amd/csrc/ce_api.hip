@@ -599,6 +599,12 @@ int path_without_parts(int64_t C, int es, bool grad) {
   return need <= (int64_t)cap.nt * cap.nv ? kPathResident : kPathLong;
 }
 
+// Kept-row count of ignore_index: one workgroup for up to one round of
+// targets (a single launch, all loads in flight at once), else one
+// workgroup per round up to 256, after the zeroing launch.
+constexpr int64_t kCountOneRows = ce::kCountRound;
+constexpr int64_t kCountMaxBlocks = 256;
+
 bool overlaps(uintptr_t a, uintptr_t an, uintptr_t b, uintptr_t bn) {
   return a < b + bn && b < a + an;
 }
@@ -794,11 +800,17 @@ int fwd_impl(const FwdArgs& a, void* stream) {
                  a.has_ignore ? 1 : 0};
   if (a.has_ignore) {
     uint32_t* kept = (uint32_t*)a.ws;
-    ce_host::launch(ce::ce_set_u32_kernel, dim3(1), dim3(64), 0, st, kept, 0u);
-    if (launched() != CE_OK) return CE_ERR_LAUNCH;
-    const int64_t blocks = (B + ce::kCountThreads - 1) / ce::kCountThreads;
-    ce_host::launch(ce::ce_count_kept_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)),
-                       dim3(ce::kCountThreads), 0, st, a.targets, B, a.ignore, kept);
+    const int64_t rounds = (B + ce::kCountRound - 1) / ce::kCountRound;
+    if (B <= kCountOneRows) {
+      ce_host::launch(ce::ce_count_kept_kernel<true>, dim3(1), dim3(ce::kCountThreads), 0, st,
+                      a.targets, B, a.ignore, kept);
+    } else {
+      ce_host::launch(ce::ce_set_u32_kernel, dim3(1), dim3(64), 0, st, kept, 0u);
+      if (launched() != CE_OK) return CE_ERR_LAUNCH;
+      ce_host::launch(ce::ce_count_kept_kernel<false>,
+                      dim3((unsigned)(rounds < kCountMaxBlocks ? rounds : kCountMaxBlocks)),
+                      dim3(ce::kCountThreads), 0, st, a.targets, B, a.ignore, kept);
+    }
     if (launched() != CE_OK) return CE_ERR_LAUNCH;
     rs.kept = kept;
   }

@@ -1083,24 +1083,52 @@ __global__ __launch_bounds__(kReduceOneThreads) void ce_reduce_one_kernel(
 }
 
 // ===========================================================================
-// Rows kept by ignore_index: the number of targets that differ from it,
-// added into *count with one integer atomic per wave (an integer total does
-// not depend on the order of the additions).  The count is zeroed first by
-// ce_set_u32_kernel on the same stream.
+// Rows kept by ignore_index: the number of targets that differ from it.  A
+// workgroup of 1024 threads reads rounds of 16384 targets, each thread 16
+// of them at once (4-byte buffer loads, index-checked against B), and sums
+// its threads' counts in integers.  With ONE, a single workgroup covers all
+// B rows and stores the total; otherwise ce_set_u32_kernel zeroes the count
+// first on the same stream and every workgroup adds its total with one
+// integer atomic (an integer total does not depend on the order of the
+// additions).
 // ===========================================================================
-constexpr int kCountThreads = 256;
+constexpr int kCountThreads = 1024;
+constexpr int kCountLoads = 16;                              // per thread per round
+constexpr int kCountRound = kCountThreads * kCountLoads;     // targets per round
 
+template <bool ONE>
 __global__ __launch_bounds__(kCountThreads) void ce_count_kept_kernel(
     const int32_t* __restrict__ targets, int64_t B, int32_t ignore, uint32_t* __restrict__ count) {
+  __shared__ uint32_t part[kCountThreads / 64];
+  const int tid = threadIdx.x;
   uint32_t n = 0;
-  const int64_t stride = (int64_t)gridDim.x * kCountThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kCountThreads + threadIdx.x; i < B; i += stride)
-    n += targets[i] != ignore ? 1u : 0u;
-  // a wave's total is at most 64 * ceil(B / stride) < 2^24: exact in float32
-  const float w = wave_allreduce((float)n, OpAdd{});
-  if ((threadIdx.x & 63) == 0 && w != 0.f) atomicAdd(count, (uint32_t)w);
+  const int64_t stride = (int64_t)gridDim.x * kCountRound;
+  for (int64_t base = (int64_t)blockIdx.x * kCountRound; base < B; base += stride) {
+    const int len = B - base < kCountRound ? (int)(B - base) : kCountRound;
+    const rsrc_t r = make_rsrc(targets + base, (uint32_t)len * 4u);
+    int32_t x[kCountLoads];
+#pragma unroll
+    for (int k = 0; k < kCountLoads; ++k)
+      x[k] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r, tid * 4, k * kCountThreads * 4,
+                                                           kPolicyDefault);
+#pragma unroll
+    for (int k = 0; k < kCountLoads; ++k)
+      n += (tid + k * kCountThreads < len && x[k] != ignore) ? 1u : 0u;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) n += (uint32_t)__shfl_xor((int)n, m, 64);
+  if ((tid & 63) == 0) part[tid >> 6] = n;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t tot = 0;
+#pragma unroll
+    for (int i = 0; i < kCountThreads / 64; ++i) tot += part[i];
+    if constexpr (ONE)
+      *count = tot;
+    else if (tot != 0)
+      atomicAdd(count, tot);
+  }
 }
-
 __global__ __launch_bounds__(64) void ce_set_u32_kernel(uint32_t* __restrict__ p, uint32_t v) {
   if (threadIdx.x == 0) *p = v;
 }
