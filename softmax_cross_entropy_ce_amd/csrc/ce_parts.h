@@ -423,11 +423,16 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   };
   // 16-bit parts take c from their first slot alone and fold every slot
   // as soon as its data is in, so that the exponentials of the first slots
-  // overlap the loads of the last; a thread whose sum overflows (an element
-  // more than 88 above its first slot's maximum) forms it again from its
-  // true maximum.  fp32 parts, which keep their terms in the register
-  // slots, take the maximum over all their slots first.
+  // overlap the loads of the last.  A thread whose sum reaches 2^32 (an
+  // element about 22 or more above its first slot's maximum, or a NaN)
+  // forms it again from its true maximum.  Below that bound every element
+  // lies at most 32 above its thread's c in log2 units, and so above the
+  // row's cg: the row's Sx stays below C * 2^32 <= 2^60, and the loss's
+  // Sx * 2^(-a_t) (taken while a_t > -60) below 2^120, with no overflow
+  // anywhere after the sum.  fp32 parts, which keep their terms in the
+  // register slots, take the maximum over all their slots first.
   constexpr bool kFirstSlotC = sizeof(T) == 2;
+  constexpr float kFirstSlotSumMax = 0x1p32f;
   auto keep_terms = [&](int k, const float (&e)[VE]) {
     if constexpr (kKeepTerms) v[k] = as_u32(f32x4{e[0], e[1], e[2], e[3]});
     if constexpr (kLdsTerms > 0) {
@@ -506,7 +511,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
     xs = xe >= 0 ? xs_raw : kNegInf;
     s = s + edge_term(xe, xs, c0);
     c = c0;
-    if (!(s < __builtin_inff())) {  // overflow (or NaN input): the true maximum
+    if (!(s < kFirstSlotSumMax)) {  // an element far above c0 (or a NaN): the true maximum
       c = pair_c(full_max(len), xe, xs);
       s = full_sum(len, c, xs);
     }
@@ -668,7 +673,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
           }
           cq = c0;
           sq = sum_q(c0);
-          if (!(sq < __builtin_inff())) {
+          if (!(sq < kFirstSlotSumMax)) {
             cq = pair_c(max_q(), xq, xqs);
             sq = sum_q(cq);
           }

@@ -198,3 +198,47 @@ def test_eight_parts_full_grid_sampled(B, C, dtype, sigma):
     worst, _ = compare_block(g, loss_rows.cpu().numpy()[rows], z[rows], t[rows], B, dtype,
                              where=f"eight parts {B}x{C} {dtype}")
     print(f"[parts] {B}x{C} {dtype}: {worst}, recomputed pairs {n}", flush=True)
+
+
+# 16-bit parts take each thread's c from its first slot and fold the other
+# slots as they arrive; a thread whose sum overflows (an element more than
+# 128 ln 2 above that c) forms it again from its true maximum, and pass 1
+# takes maxima on the bit patterns (packed signed 16-bit max, packed min for
+# threads whose elements are all negative).  Rows that reach every branch:
+# spikes in later slots, spikes on the target, all-negative rows, rows
+# whose first slots are far below the rest, a row just past the overflow
+# margin, rows shifted far up, mixed signs around zero.
+@pytest.mark.parametrize("B,C,dtype", [(16, 128256, "bf16"), (16, 50257, "bf16"),
+                                       (12, 300001, "f16"), (16, 128256, "f16")],
+                         ids=["128256-bf16", "50257-bf16", "300001-f16", "128256-f16"])
+def test_16bit_part_max_edge_rows(B, C, dtype):
+    import torch
+    ce = _ce()
+    rng = np.random.Generator(np.random.PCG64(C + B))
+    z = (rng.standard_normal((B, C)) * 4).astype(np.float32)
+    t = rng.integers(0, C, B).astype(np.int32)
+    cols = rng.integers(0, C, (B, 2))
+    z[0, cols[0, 0]] = 1e4                      # spike in some later slot
+    z[1, t[1]] = 1e4                            # spike on the target
+    z[2] -= 200.0                               # every element negative
+    z[3] = -np.abs(z[3])                        # all negative, max near zero
+    z[3, cols[3, 0]] = -0.0
+    z[4, cols[4, 0]] = -1e4                     # one very negative element
+    z[5, cols[5]] = 1e4                         # spikes in two places (parts)
+    z[6] += 1000.0                              # far up, no overflow
+    # each thread's first slot far below its later slots: the first 8192
+    # vectors' elements (16-bit: 8 per vector) of the row
+    z[7, :8 * 1024] -= 1e4
+    z[8, cols[8, 0]] = z[8].max() + 95.0        # just past the overflow margin
+    z[9, cols[9, 0]] = z[9].max() + 80.0        # just inside it
+    z[10] = np.where(rng.random(C) < 0.5, -np.abs(z[10]), np.abs(z[10]))
+    z[11, :64] = 500.0                          # a run of equal maxima at the head
+    bits = synth.bf16_bits_from_f32(z) if dtype == "bf16" else synth.f16_bits_from_f32(z)
+    print(f"[part max rows] {B}x{C} {dtype}: {full_parity(bits, t, dtype, where=f'{C} {dtype}')}",
+          flush=True)
+    # the recompute gives the same bits
+    zd, td = to_device(bits, t, dtype)
+    g1, l1 = _run(zd, td)
+    ce.part_polls(0)
+    g0, l0 = _run(zd, td)
+    assert torch.equal(_bits(g0), _bits(g1)) and torch.equal(_bits(l0), _bits(l1))
