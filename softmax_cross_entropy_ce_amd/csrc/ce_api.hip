@@ -410,13 +410,25 @@ int resident_blocks(const void* kernel, int nt, std::atomic<int>& per_cu_cache) 
   return cus * per_cu;
 }
 
+// 16-bit rows read for their per-row value with 8 register slots (the
+// streaming read configurations): at most seven waves per SIMD.  At 63
+// VGPRs the kernel fits eight, and the extra workgroups slowed the streams
+// (measured: the loss alone on 8192 x 128256 bf16, 512 x 8, took 378 us
+// with four workgroups per CU against 333 us with three).
+constexpr int kReadWavesPerSimd = 7;
+
 template <typename T, int NT, int NV, int OP, bool GRAD>
 int launch_row_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
                    float* l, hipStream_t st) {
   auto kern = ce::ce_row_kernel<T, NT, NV, GRAD, OP>;
   static std::atomic<int> occupancy{0};
-  const int res = resident_blocks(reinterpret_cast<const void*>(kern), NT, occupancy);
+  int res = resident_blocks(reinterpret_cast<const void*>(kern), NT, occupancy);
   if (res < 1) return CE_ERR_LAUNCH;
+  if constexpr (!GRAD && sizeof(T) == 2 && NV == 8) {
+    constexpr int kPerCu = kReadWavesPerSimd * 4 / (NT / 64) > 0 ? kReadWavesPerSimd * 4 / (NT / 64) : 1;
+    const int cap = device_cus() * kPerCu;
+    if (cap > 0 && res > cap) res = cap;
+  }
   const int64_t grid = B < res ? B : res;
   ce_host::launch(kern, dim3((unsigned)grid), dim3(NT), 0, st, z, t, B, (int)C, rs, g, l);
   return launched();
