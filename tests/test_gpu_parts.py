@@ -178,8 +178,9 @@ def test_eight_parts_full_grid_sampled(B, C, dtype, sigma):
     """Eight parts per row on a grid of about 1 GB of logits, so that parts
     of one row may not all be resident at once (the bounded polls, then the
     recompute): 34 sampled rows, the first and last among them, against the
-    oracle element by element, and the device counter's recomputed pairs
-    reported."""
+    oracle element by element, the device counter's recomputed pairs
+    reported, and the whole gradient and every per-row loss bitwise equal to
+    a run in which every pair is recomputed (zero polls)."""
     import torch
     from _parity import compare_block, grad_to_host
     ce = _ce()
@@ -198,16 +199,21 @@ def test_eight_parts_full_grid_sampled(B, C, dtype, sigma):
     worst, _ = compare_block(g, loss_rows.cpu().numpy()[rows], z[rows], t[rows], B, dtype,
                              where=f"eight parts {B}x{C} {dtype}")
     print(f"[parts] {B}x{C} {dtype}: {worst}, recomputed pairs {n}", flush=True)
+    ce.part_counter(None)
+    ce.part_polls(0)
+    grad0, loss0 = _run(z_dev, t_dev)
+    assert torch.equal(_bits(grad0), _bits(grad)) and torch.equal(_bits(loss0), _bits(loss_rows))
 
 
 # 16-bit parts take each thread's c from its first slot and fold the other
-# slots as they arrive; a thread whose sum overflows (an element more than
-# 128 ln 2 above that c) forms it again from its true maximum, and pass 1
+# slots as they arrive; a thread whose sum reaches 2^32 (an element about 22
+# above that c) forms it again from its true maximum, and pass 1
 # takes maxima on the bit patterns (packed signed 16-bit max, packed min for
 # threads whose elements are all negative).  Rows that reach every branch:
 # spikes in later slots, spikes on the target, all-negative rows, rows
-# whose first slots are far below the rest, a row just past the overflow
-# margin, rows shifted far up, mixed signs around zero.
+# whose first slots are far below the rest, rows with one element 80 and 95
+# above the rest (past the bound: the first of them once gave an infinite
+# loss), rows shifted far up, mixed signs around zero.
 @pytest.mark.parametrize("B,C,dtype", [(16, 128256, "bf16"), (16, 50257, "bf16"),
                                        (12, 300001, "f16"), (16, 128256, "f16")],
                          ids=["128256-bf16", "50257-bf16", "300001-f16", "128256-f16"])
@@ -229,8 +235,8 @@ def test_16bit_part_max_edge_rows(B, C, dtype):
     # each thread's first slot far below its later slots: the first 8192
     # vectors' elements (16-bit: 8 per vector) of the row
     z[7, :8 * 1024] -= 1e4
-    z[8, cols[8, 0]] = z[8].max() + 95.0        # just past the overflow margin
-    z[9, cols[9, 0]] = z[9].max() + 80.0        # just inside it
+    z[8, cols[8, 0]] = z[8].max() + 95.0        # past the bound, and past fp32's exp range
+    z[9, cols[9, 0]] = z[9].max() + 80.0        # past the bound, inside fp32's exp range
     z[10] = np.where(rng.random(C) < 0.5, -np.abs(z[10]), np.abs(z[10]))
     z[11, :64] = 500.0                          # a run of equal maxima at the head
     bits = synth.bf16_bits_from_f32(z) if dtype == "bf16" else synth.f16_bits_from_f32(z)
