@@ -203,3 +203,17 @@ def test_stream_copy_is_exact(nbytes):
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
     assert (buf[:2048] == 0xA5).all() and (buf[2048 + nbytes:] == 0xA5).all()
+
+
+def test_stream_handle_is_torchs_current_stream():
+    """The binding passes the raw handle of torch's current stream, on the
+    default stream and inside a stream context."""
+    import torch
+    import softmax_cross_entropy_ce_amd as ce
+    dev = torch.device("cuda:0")
+    assert ce._stream_ptr(dev) == torch.cuda.current_stream(dev).cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert ce._stream_ptr(dev) == s.cuda_stream
+        assert ce._stream_ptr(torch.device("cuda")) == s.cuda_stream
+    assert ce._stream_ptr(dev) == torch.cuda.current_stream(dev).cuda_stream
