@@ -392,7 +392,7 @@ int ce_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
  *                   256-thread workgroup for rows up to 32 KB, else
  *                   1024-thread workgroups of up to 12 x 16 KB, two per
  *                   CU); each part is read once into registers and LDS and
- *                   reduced to an online max/sum-exp pair, the parts trade
+ *                   reduced to a max/sum-exp pair, the parts trade
  *                   their pairs and combine them in a fixed order, and each
  *                   writes its share of the gradient from on chip.  A part
  *                   that does not receive a partner's pair in time
