@@ -13,7 +13,14 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: full-size workloads (minutes of CPU)")
 
 
+@pytest.hookimpl(trylast=True)
 def pytest_collection_modifyitems(config, items):
+    # (after -m and -k have deselected) The host-sanitizer build takes
+    # minutes: start it now, so that it runs beside the other tests rather
+    # than after them.
+    if any(os.path.basename(str(it.fspath)) == "test_zy_host_sanitizers.py" for it in items):
+        from test_zy_host_sanitizers import start_build
+        start_build()
     # A GPU test on a machine without a GPU is skipped, not failed.
     try:
         import torch

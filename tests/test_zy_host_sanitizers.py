@@ -5,8 +5,10 @@ side only (the gfx950 code is built as usual), linked into a C++ client,
 and the client drives every entry point with invalid and extreme arguments
 (sizes up to INT64_MAX, strides that would overflow a span, misaligned and
 overlapping pointers).  Every call must be refused before any HIP call, with
-no sanitizer report.  The build takes about two minutes; it is cached under
-tests/.san_build by a digest of the sources, so later runs reuse it."""
+no sanitizer report.  The build takes about two and a half minutes; it
+starts in the background right after collection (tests/conftest.py), and
+is cached under tests/.san_build by a digest of the sources, so later runs
+reuse it."""
 
 from __future__ import annotations
 
@@ -142,9 +144,16 @@ def _digest() -> str:
     return h.hexdigest()[:16]
 
 
-def _build(out: str) -> str:
+_pending = None   # the two HIP compiles, when started early by start_build()
+
+
+def _have_compilers() -> bool:
+    return (os.path.exists(os.path.join(ROCM, "bin", "hipcc"))
+            and os.path.exists(os.path.join(ROCM, "llvm", "bin", "clang++")))
+
+
+def _hip_compiles(out: str):
     hipcc = os.path.join(ROCM, "bin", "hipcc")
-    clangxx = os.path.join(ROCM, "llvm", "bin", "clang++")
     os.makedirs(out, exist_ok=True)
     # sanitizers on the host side of the HIP translation units only
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
@@ -158,6 +167,31 @@ def _build(out: str) -> str:
         jobs.append((obj, subprocess.Popen([hipcc, *common, *san, "-c", os.path.join(CSRC, src),
                                             "-o", obj], stdout=subprocess.PIPE,
                                            stderr=subprocess.STDOUT, text=True)))
+    return jobs
+
+
+def start_build() -> None:
+    """Start the two HIP compiles in the background (called by conftest
+    after collection, so that they overlap the other CPU tests); the test
+    waits for them."""
+    global _pending
+    if _pending is not None or not _have_compilers():
+        return
+    out = os.path.join(CACHE, _digest())
+    if os.path.exists(os.path.join(out, "client")):
+        return
+    shutil.rmtree(CACHE, ignore_errors=True)
+    _pending = (out, _hip_compiles(out))
+
+
+def _build(out: str) -> str:
+    global _pending
+    clangxx = os.path.join(ROCM, "llvm", "bin", "clang++")
+    if _pending is not None and _pending[0] == out:
+        jobs = _pending[1]
+    else:
+        jobs = _hip_compiles(out)
+    _pending = None
     client_src = os.path.join(out, "client.cpp")
     with open(client_src, "w") as f:
         f.write(CLIENT)
@@ -181,13 +215,13 @@ def _build(out: str) -> str:
 
 @pytest.mark.timeout(900)
 def test_host_code_under_asan_and_ubsan():
-    if not (os.path.exists(os.path.join(ROCM, "bin", "hipcc"))
-            and os.path.exists(os.path.join(ROCM, "llvm", "bin", "clang++"))):
+    if not _have_compilers():
         pytest.skip("ROCm compilers not available")
     out = os.path.join(CACHE, _digest())
     exe = os.path.join(out, "client")
     if not os.path.exists(exe):
-        shutil.rmtree(CACHE, ignore_errors=True)
+        if _pending is None:
+            shutil.rmtree(CACHE, ignore_errors=True)
         exe = _build(out)
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0:halt_on_error=1",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
