@@ -1,13 +1,13 @@
-"""Path 1's tiny-row kernel (rows of at most 64 bytes, one row per thread
+"""Path 1's tiny-row kernel (rows of at most 64 bytes, one row per lane
 from LDS) on the GPU against the fp64 oracle, in every layout it has.
 
 Rows of a multiple of 16 bytes sit in LDS at a padded, odd stride of
-32-bit words; other rows keep the packed layout.  Rows of at most 8 bytes
-take four rows per thread and rows of at most 32 bytes two.  The kernel is
-persistent and keeps two chunks of 256 x R rows in flight per workgroup in
-two register sets used in turn, so the large cases give every workgroup
-several chunks (more rows than the resident grid holds), both register
-sets and a ragged last chunk; the small ones a single partial chunk.
+32-bit words; other rows keep the packed layout.  16-bit rows of at most 8
+elements take four rows per lane, other rows of at most 32 bytes two.  Each
+wave owns one chunk of 64 x R rows in its own LDS slot (four waves per
+workgroup), and the last, partial chunk moves element by element: the
+large cases have thousands of chunks and a ragged last one, the small ones
+put the call's end at every position of a chunk, a wave and a workgroup.
 """
 
 from __future__ import annotations
@@ -29,16 +29,21 @@ pytestmark = pytest.mark.gpu
 CASES = [
     (1_500_001, 16, "f32"),     # 64 B, padded, one row per thread
     (1_200_001, 8, "f32"),      # 32 B, padded, two rows per thread
-    (2_000_003, 2, "f32"),      # 8 B, packed, four rows per thread
+    (2_000_003, 2, "f32"),      # 8 B, packed, two rows per lane
     (700_001, 6, "f32"),        # 24 B, packed, two rows per thread
     (1_000_003, 32, "bf16"),    # 64 B, padded
     (999_999, 24, "bf16"),      # 48 B, padded
     (1_500_007, 12, "bf16"),    # 24 B, packed, two rows per thread
-    (3_000_001, 4, "bf16"),     # 8 B, packed, four rows per thread
+    (3_000_001, 4, "bf16"),     # 8 B, packed, four rows per lane
     (1_100_000, 9, "bf16"),     # 18 B, packed (rows not whole words), two per thread
     (257, 16, "f32"),           # one partial chunk, padded
     (1000, 4, "f32"),           # partial chunk, 16 B padded rows, two per thread
     (3, 32, "bf16"),
+    # the end of the call at the edges of a chunk (64 x R rows), of a wave's
+    # slot and of a workgroup's four waves
+    (63, 10, "f32"), (64, 10, "f32"), (65, 10, "f32"), (255, 10, "f32"), (256, 10, "f32"),
+    (257, 10, "f32"), (129, 6, "f32"), (511, 8, "bf16"), (513, 8, "bf16"), (1, 3, "f16"),
+    (4 * 64 * 3 + 64 + 17, 12, "bf16"), (1023, 7, "f16"), (640, 16, "bf16"),
 ]
 IDS = [f"{b}x{c}-{d}" for b, c, d in CASES]
 
