@@ -1080,20 +1080,21 @@ int launch_shard_grad(const T* z, const int32_t* t, int64_t B, int64_t C, int64_
                        z, t, B, (int)C, col0, Ctot, r4, nshards, rs, g, l);
     return launched();
   }
-  // units of one wave for rows of at most 512 vectors, else of four waves
+  // units of one wave x 8 slots for rows of at most 512 vectors, else of
+  // four waves x 2 slots
   const int64_t nb = body_vectors_max(C, sizeof(T));
-  const bool wave_units = nb <= 64 * ce::kShardSlots;
-  const int64_t chunk = (wave_units ? 64 : 256) * ce::kShardSlots;
+  const bool wave_units = nb <= 64 * 8;
+  const int64_t chunk = wave_units ? 64 * 8 : 256 * 2;
   const int64_t units = ce::kShardThreads / (wave_units ? 64 : 256);
   const int64_t chunks = nb > 0 ? (nb + chunk - 1) / chunk : 1;
   const int64_t blocks = (B * chunks + units - 1) / units;
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
   if (wave_units)
-    ce_host::launch((ce::ce_shard_grad_kernel<T, 64>), dim3((unsigned)blocks),
+    ce_host::launch((ce::ce_shard_grad_kernel<T, 64, 8>), dim3((unsigned)blocks),
                        dim3(ce::kShardThreads), 0, st, z, t, B, (int)C, col0, Ctot, r4, nshards, rs,
                        g, l, (int)chunks);
   else
-    ce_host::launch((ce::ce_shard_grad_kernel<T, 256>), dim3((unsigned)blocks),
+    ce_host::launch((ce::ce_shard_grad_kernel<T, 256, 2>), dim3((unsigned)blocks),
                        dim3(ce::kShardThreads), 0, st, z, t, B, (int)C, col0, Ctot, r4, nshards, rs,
                        g, l, (int)chunks);
   return launched();

@@ -42,13 +42,15 @@ __device__ __forceinline__ ShardRow shard_combine(const f32x4* __restrict__ recs
   return r;
 }
 
-// A unit of work is U threads x 8 slots: U * 8 body vectors of one row
-// (U = 256, or one wave for rows of at most 512 vectors).  1024 / U units
-// share a 1024-thread workgroup (large workgroups stream faster than small
-// ones on this GPU); they need no barrier, since every thread combines the
-// records of its row by itself.
+// A unit of work is U threads x S slots: U * S body vectors of one row.
+// Rows of at most 512 vectors take one wave x 8 slots; longer rows 256
+// threads x 2 slots (512 vectors, several units per row), which measured
+// 4-10 % faster than 256 x 8 on 8192 x 16032 and 8192 x 32064 bf16 and
+// 4096 x 6282 fp32 shards (at a copy's rate on the last two).  1024 / U
+// units share a 1024-thread workgroup (large workgroups stream faster than
+// small ones on this GPU); they need no barrier, since every thread
+// combines the records of its row by itself.
 constexpr int kShardThreads = 1024;
-constexpr int kShardSlots = 8;                              // 16-byte vectors per thread
 constexpr int kShardTinyC = 16;                             // rows one thread handles
 
 // Unit u (= 1024/U * workgroup + threadIdx.x / U) handles body vectors
@@ -58,14 +60,14 @@ constexpr int kShardTinyC = 16;                             // rows one thread h
 // records, shard-major.  A row whose target lies outside [0, Ctot), or is
 // held by other than exactly one shard's record, gets NaN loss and
 // gradient.
-template <typename T, int U>
+template <typename T, int U, int S>
 __global__ __launch_bounds__(kShardThreads) void ce_shard_grad_kernel(
     const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B, int C,
     int64_t col0, int64_t Ctot, const f32x4* __restrict__ recs, int nshards, RowArgs rs,
     T* __restrict__ grad, float* __restrict__ loss_rows, int chunks) {
   static_assert(U == 64 || U == 256, "a unit is one or four waves");
   constexpr int kUnits = kShardThreads / U;
-  constexpr int kChunk = U * kShardSlots;
+  constexpr int kChunk = U * S;
   using E = Elem<T>;
   constexpr int VE = E::VE, NT = U;
   // wave-uniform (a unit is whole waves): readfirstlane lets the compiler
@@ -86,9 +88,9 @@ __global__ __launch_bounds__(kShardThreads) void ce_shard_grad_kernel(
   const uint32_t bytes = nv > 0 ? (uint32_t)nv * 16u : 0u;
   const rsrc_t rin = make_rsrc(rp + geo.h + (int64_t)v0 * VE, bytes);
   const rsrc_t rout = make_rsrc(gp + geo.h + (int64_t)v0 * VE, bytes);
-  u32x4 v[kShardSlots];
+  u32x4 v[S];
 #pragma unroll
-  for (int k = 0; k < kShardSlots; ++k)
+  for (int k = 0; k < S; ++k)
     v[k] = bload128<kPolicyStream>(rin, voff, (uint32_t)k * NT * 16u);
   int xe = -1;  // chunk 0: this thread's edge element, if any
   if (chunk == 0) {
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(kShardThreads) void ce_shard_grad_kernel(
   const int tj = t_body ? tb % VE : 0;
 
 #pragma unroll
-  for (int k = 0; k < kShardSlots; ++k) {
+  for (int k = 0; k < S; ++k) {
     if (k * NT >= nv) break;  // uniform
     float f[VE], g[VE];
     E::unpack(v[k], f);
