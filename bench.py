@@ -85,7 +85,18 @@ class HipEvents:
         L.hipEventElapsedTime.restype = ctypes.c_int
         L.hipEventDestroy.argtypes = [ctypes.c_void_p]
         L.hipEventDestroy.restype = ctypes.c_int
+        L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventRecord.restype = ctypes.c_int
         self.events = []
+
+    # hipEventDisableSystemFence: the events time kernels and synchronise
+    # nothing (the host synchronises the device before reading them), so
+    # they skip the system-scope fence, a cache write-back and invalidate
+    # that otherwise follows each timed kernel.  Measured on lmhead128k, 20
+    # steps with 4 pairs: 702.0 us per step and 697.5 us for the kernel with
+    # default events, 699.5 and 694.4 us with these; lmhead50k 279.6 and
+    # 276.5 against 278.6 and 274.6 us.
+    FLAGS = 0x20000000
 
     def pairs(self, n: int):
         out = []
@@ -93,7 +104,7 @@ class HipEvents:
             pair = []
             for _ in range(2):
                 ev = self._c.c_void_p()
-                if self.L.hipEventCreateWithFlags(self._c.byref(ev), 0) != 0:
+                if self.L.hipEventCreateWithFlags(self._c.byref(ev), self.FLAGS) != 0:
                     raise RuntimeError("hipEventCreateWithFlags failed")
                 self.events.append(ev)
                 pair.append(ev)
@@ -103,6 +114,11 @@ class HipEvents:
     def arm(self, pair) -> None:
         """The library's next launch on this thread records this pair."""
         self.L.ce_debug_time_next_launch(pair[0], pair[1])
+
+    def record(self, ev, stream_handle: int) -> None:
+        """Record one event on a stream (a marker between launches)."""
+        if self.L.hipEventRecord(ev, stream_handle) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def ms(self, pair) -> float:
         v = self._c.c_float()
@@ -116,11 +132,12 @@ class HipEvents:
         self.events = []
 
 
-# A timed kernel launch costs the step about 7 us (measured on lmhead128k:
-# 692 us per step without events, 699 us with a pair on every ce_fwd_grad,
-# whether recorded by torch around the call or attached to the launch): the
-# timestamps are taken after a system-scope release at the kernel's end.
-# The timed loop therefore attaches a pair to every EVENT_EVERY-th step,
+# A timed kernel launch with default events cost the step about 7 us
+# (measured on lmhead128k: 692 us per step without events, 699 us with a
+# pair on every ce_fwd_grad, whether recorded by torch around the call or
+# attached to the launch): the timestamps were taken after a system-scope
+# release at the kernel's end, which HipEvents.FLAGS now skips.
+# The timed loop attaches a pair to every EVENT_EVERY-th step,
 # from the fourth on: by then the host is ahead of the GPU, so the slower
 # host path of an armed launch does not leave the GPU idle; and never to
 # the last step, whose event completion would otherwise add its latency to
@@ -240,23 +257,10 @@ def copy_calibration(zd, grad, reps: int = 20) -> dict:
     import softmax_cross_entropy_ce_amd as ce
     stream = torch.cuda.current_stream(zd.device)
     src, dst = zd.view(-1).view(torch.uint8), grad.view(-1).view(torch.uint8)
-
-    def timed(fn):
-        for _ in range(10):
-            fn()
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        for a, b in evs:
-            a.record(stream)
-            fn()
-            b.record(stream)
-        torch.cuda.synchronize()
-        return statistics.median([a.elapsed_time(b) for a, b in evs])
-
     nbytes = 2 * src.numel()
-    ms = timed(lambda: ce.stream_copy(src, dst))
-    ms_rt = timed(lambda: dst.copy_(src))
+    # timed as ce_fwd_grad is in the steps: events on the kernel's launch
+    ms = _event_median_ms(lambda: ce.stream_copy(src, dst), stream, reps, armed=True)
+    ms_rt = _event_median_ms(lambda: dst.copy_(src), stream, reps)
     return {"kernel": "ce_stream_copy (1024 threads x 8 slots of 16 B, non-temporal)",
             "ms": round(ms, 5), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 2),
             "runtime_copy_GBps": round(nbytes / (ms_rt * 1e-3) / 1e9, 2)}
@@ -274,17 +278,7 @@ def backward_scale(zd, td, grad, loss_rows, reps: int = 20) -> dict:
     one = torch.tensor([1.0], dtype=torch.float32, device=zd.device)
 
     def timed(fn):
-        for _ in range(10):
-            fn()
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        for a, b in evs:
-            a.record(stream)
-            fn()
-            b.record(stream)
-        torch.cuda.synchronize()
-        return statistics.median([a.elapsed_time(b) for a, b in evs])
+        return _event_median_ms(fn, stream, reps)
 
     nbytes = 2 * grad.numel() * grad.element_size()
     ms_half = timed(lambda: ce.scale_grad_(grad, half))
@@ -305,17 +299,7 @@ def loss_only_and_in_place(zd, td, grad, loss_rows, reps: int = 20) -> dict:
     stream = torch.cuda.current_stream(zd.device)
 
     def timed(fn):
-        for _ in range(10):
-            fn()
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        for a, b in evs:
-            a.record(stream)
-            fn()
-            b.record(stream)
-        torch.cuda.synchronize()
-        return statistics.median([a.elapsed_time(b) for a, b in evs])
+        return _event_median_ms(fn, stream, reps)
 
     in_bytes = zd.numel() * zd.element_size()
     ms_loss = timed(lambda: ce.fwd_loss_into(zd, td, loss_rows))
@@ -329,19 +313,31 @@ def loss_only_and_in_place(zd, td, grad, loss_rows, reps: int = 20) -> dict:
             "in_place_frac": round(gbs_inpl / PEAK_HBM_GBS, 4)}
 
 
-def _event_median_ms(fn, stream, reps: int, warm: int = 10) -> float:
+def _event_median_ms(fn, stream, reps: int, warm: int = 10, armed: bool = False) -> float:
+    """Median time of fn over reps calls, each between a pair of HipEvents
+    (no system fence, as in the timed steps): recorded on the stream around
+    the call, or with armed attached to the call's first library launch
+    (the kernel's own start and end, as for ce_fwd_grad in the timed
+    steps)."""
     import torch
+    hev = HipEvents()
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    for a, b in evs:
-        a.record(stream)
-        fn()
-        b.record(stream)
+    pairs = hev.pairs(reps)
+    handle = stream.cuda_stream
+    for a, b in pairs:
+        if armed:
+            hev.arm((a, b))
+            fn()
+        else:
+            hev.record(a, handle)
+            fn()
+            hev.record(b, handle)
     torch.cuda.synchronize()
-    return statistics.median([a.elapsed_time(b) for a, b in evs])
+    ms = statistics.median([hev.ms(pr) for pr in pairs])
+    hev.close()
+    return ms
 
 
 GATE_FRAC = 0.75   # the LM-head workloads' bar: 75 % of peak HBM bandwidth
@@ -407,18 +403,18 @@ def cold_fwd_grad(zd, td, grad, loss_rows, reps: int = 20) -> dict:
     import softmax_cross_entropy_ce_amd as ce
     stream = torch.cuda.current_stream(zd.device)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=zd.device)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
+    hev = HipEvents()
+    pairs = hev.pairs(reps)
     for _ in range(3):
         ce.fwd_grad_into(zd, td, grad, loss_rows)
-    for a, b in evs:
+    for pr in pairs:
         scratch.fill_(1)
-        a.record(stream)
+        hev.arm(pr)
         ce.fwd_grad_into(zd, td, grad, loss_rows)
-        b.record(stream)
     torch.cuda.synchronize()
     del scratch
-    ms = statistics.median([a.elapsed_time(b) for a, b in evs])
+    ms = statistics.median([hev.ms(pr) for pr in pairs])
+    hev.close()
     B, C = zd.shape
     return _rate(B * C * 2 * zd.element_size() + 8 * B, ms)
 
