@@ -291,9 +291,11 @@ def backward_scale(zd, td, grad, loss_rows, reps: int = 20) -> dict:
 
 
 def loss_only_and_in_place(zd, td, grad, loss_rows, reps: int = 20) -> dict:
-    """ce_fwd_loss (logits read once, per-row losses written) and
-    ce_fwd_grad in place of the logits (on a copy of them; each call then
-    reads the previous call's gradient, a valid input of the same size)."""
+    """ce_fwd_loss (logits read once, per-row losses written) and the
+    gradient in place of the logits (on a copy of them; each call then
+    reads the previous call's gradient, a valid input of the same size):
+    ce_fwd_grad_ex with the in-place workspace, so that rows of two parts
+    stay on path 4, and ce_fwd_grad, which has no workspace."""
     import torch
     import softmax_cross_entropy_ce_amd as ce
     stream = torch.cuda.current_stream(zd.device)
@@ -304,13 +306,18 @@ def loss_only_and_in_place(zd, td, grad, loss_rows, reps: int = 20) -> dict:
     in_bytes = zd.numel() * zd.element_size()
     ms_loss = timed(lambda: ce.fwd_loss_into(zd, td, loss_rows))
     grad.copy_(zd)
-    ms_inpl = timed(lambda: ce.fwd_grad_into(grad, td, grad, loss_rows))
+    ws = torch.zeros(ce.fwd_inplace_workspace_bytes(zd.shape[0]), dtype=torch.uint8,
+                     device=zd.device)
+    ms_inpl = timed(lambda: ce.fwd_grad_ex_into(grad, td, grad, loss_rows, workspace=ws))
+    ms_plain = timed(lambda: ce.fwd_grad_into(grad, td, grad, loss_rows))
     gbs_loss = (in_bytes + 8 * zd.shape[0]) / (ms_loss * 1e-3) / 1e9
     gbs_inpl = (2 * in_bytes + 8 * zd.shape[0]) / (ms_inpl * 1e-3) / 1e9
+    gbs_plain = (2 * in_bytes + 8 * zd.shape[0]) / (ms_plain * 1e-3) / 1e9
     return {"loss_only_ms": round(ms_loss, 5), "loss_only_GBps": round(gbs_loss, 2),
             "loss_only_frac": round(gbs_loss / PEAK_HBM_GBS, 4),
             "in_place_ms": round(ms_inpl, 5), "in_place_GBps": round(gbs_inpl, 2),
-            "in_place_frac": round(gbs_inpl / PEAK_HBM_GBS, 4)}
+            "in_place_frac": round(gbs_inpl / PEAK_HBM_GBS, 4),
+            "in_place_no_workspace_frac": round(gbs_plain / PEAK_HBM_GBS, 4)}
 
 
 def _event_median_ms(fn, stream, reps: int, warm: int = 10, armed: bool = False) -> float:

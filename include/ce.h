@@ -89,7 +89,8 @@ typedef enum {
  *             logits (every kernel holds a row's data on chip, or reads it
  *             again from the same thread, before writing it; rows that
  *             path 4 would cut into several parts run on path 2 or 3
- *             instead).
+ *             instead; with ce_fwd_grad_ex and an in-place workspace,
+ *             two-part rows run on path 4).
  *             Any other overlap with logits is refused.  Must be aligned
  *             to the element size, and (grad_out - logits) must be a
  *             multiple of 16 bytes (true for any two allocations from the
@@ -163,11 +164,43 @@ int ce_fwd_grad_scaled(const void* logits, const int32_t* targets, int64_t B, in
  *                 give NaN rows (and count in N).
  *   workspace     device scratch of ce_fwd_workspace_bytes(ignore_index)
  *                 bytes (4-byte aligned), or NULL when that is 0; it holds
- *                 the count N while the call's kernels run.
+ *                 the count N while the call's kernels run.  In place, rows
+ *                 that path 4 cuts into two parts run as two parts when the
+ *                 workspace also has ce_fwd_inplace_workspace_bytes(B)
+ *                 bytes, is 8-byte aligned and was zero-filled before its
+ *                 first use (each call leaves those bytes zero again, so a
+ *                 workspace serves any number of calls ordered on one
+ *                 stream; calls that may overlap need workspaces of their
+ *                 own); otherwise they run on path 2 or 3.
  *   other arguments and errors as ce_fwd_grad; CE_ERR_WORKSPACE when the
  *   workspace is missing or too small.
  */
 size_t ce_fwd_workspace_bytes(int32_t ignore_index);
+
+/*
+ * ce_fwd_inplace_workspace_bytes - the ce_fwd_grad_ex workspace with which
+ * the gradient in place of rows that path 4 cuts into two parts (bf16 and
+ * fp16 C of 81921 to 196608, fp32 C of 40961 to 98304, for rows starting on
+ * a 16-byte boundary) runs on path 4: 256 bytes (the ignore_index count in
+ * the first 4), then two 64-bit words a row, 256 + 16 B in all (0 for B
+ * outside [1, 2^31 - 1]).
+ *
+ * Defined by: as ce_fwd_grad (the gradient formed in the forward pass,
+ * here over the logits' own storage).
+ *
+ * The two parts of a row cannot trade their partial results through the
+ * gradient (it is the logits), and a part that stops waiting for its
+ * partner cannot read the partner's logits again (they may be gradient
+ * already).  So each row's parts meet at its two words: the first to
+ * arrive claims the first word with its pair; the second reads that pair,
+ * publishes its own in the second word and writes its half; the first
+ * polls the second word a bounded number of times and then either writes
+ * its half or marks the word and ends without writing, leaving its half
+ * as logits for the second part to write as well (the second finds the
+ * mark when it publishes).  No wait is unbounded, and each element's
+ * value does not depend on which part wrote it.
+ */
+size_t ce_fwd_inplace_workspace_bytes(int64_t B);
 
 int ce_fwd_grad_ex(const void* logits, int64_t ld_logits, const int32_t* targets, int64_t B,
                    int64_t C, int dtype, void* grad_out, int64_t ld_grad, float* loss_out,

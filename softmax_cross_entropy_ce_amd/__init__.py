@@ -36,7 +36,8 @@ __all__ = [
     "shard_stats", "shard_stats_into", "shard_grad", "shard_grad_into",
     "reduce_workspace_bytes", "select_path", "force_path", "part_polls", "part_counter",
     "stream_copy", "version", "PATH_NAMES", "F32", "BF16", "F16", "NO_IGNORE",
-    "fwd_grad_ex_into", "fwd_grad_ex", "fwd_workspace_bytes",
+    "fwd_grad_ex_into", "fwd_grad_ex", "fwd_workspace_bytes", "fwd_inplace_workspace_bytes",
+    "inplace_workspace",
 ]
 
 F32 = 0
@@ -114,6 +115,8 @@ def lib() -> ctypes.CDLL:
     L.ce_fwd_grad_ex.argtypes = [vp, i64, vp, i64, i64, i32, vp, i64, vp, vp, ctypes.c_int32, vp,
                                  sz, vp]
     L.ce_fwd_grad_ex.restype = i32
+    L.ce_fwd_inplace_workspace_bytes.argtypes = [i64]
+    L.ce_fwd_inplace_workspace_bytes.restype = sz
     _lib = L
     return L
 
@@ -293,10 +296,11 @@ def fwd_grad_into(logits, targets, grad, loss_rows) -> None:
 
 def fwd_grad_inplace_(logits, targets):
     """Overwrite logits with the gradient (softmax - onehot) / B and return
-    the per-row losses."""
+    the per-row losses (ce_fwd_grad_ex with the in-place workspace of
+    torch's current stream, so rows of two parts stay on path 4)."""
     torch = _torch()
     loss_rows = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device)
-    fwd_grad_into(logits, targets, logits, loss_rows)
+    fwd_grad_ex_into(logits, targets, logits, loss_rows)
     return loss_rows
 
 
@@ -350,6 +354,30 @@ def fwd_workspace_bytes(ignore_index=None) -> int:
     return int(lib().ce_fwd_workspace_bytes(NO_IGNORE if ignore_index is None else int(ignore_index)))
 
 
+def fwd_inplace_workspace_bytes(B: int) -> int:
+    return int(lib().ce_fwd_inplace_workspace_bytes(int(B)))
+
+
+# Zero-filled in-place workspaces of ce_fwd_grad_ex, one per (device,
+# stream): a call leaves its row words zero again, so one workspace serves
+# every call ordered on its stream; calls on other streams get their own.
+_inplace_ws = {}
+
+
+def inplace_workspace(device, B: int):
+    """The cached in-place workspace of torch's current stream on ``device``,
+    grown (zero-filled) to fit B rows."""
+    torch = _torch()
+    key = (device.index if device.index is not None else torch.cuda.current_device(),
+           _stream_ptr(device))
+    need = fwd_inplace_workspace_bytes(B)
+    ws = _inplace_ws.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
+        _inplace_ws[key] = ws
+    return ws
+
+
 def _rows_view(x, what: str):
     """A [B, C] device tensor whose rows are contiguous (column stride 1);
     returns its row stride in elements."""
@@ -385,7 +413,10 @@ def fwd_grad_ex_into(logits, targets, grad, loss_rows, grad_scale=None, ignore_i
         _check_scalar(grad_scale, "grad_scale")
     ii = NO_IGNORE if ignore_index is None else int(ignore_index)
     need = fwd_workspace_bytes(ignore_index)
-    if need and workspace is None:
+    in_place = grad is not None and grad.data_ptr() == logits.data_ptr() and ldg == ldz
+    if workspace is None and in_place:
+        workspace = inplace_workspace(logits.device, B)
+    elif need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
     st = lib().ce_fwd_grad_ex(
         logits.data_ptr(), ldz, targets.data_ptr(), B, C, _dtype_code(logits),

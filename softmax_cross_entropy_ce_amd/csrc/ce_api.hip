@@ -524,22 +524,31 @@ RowCfg read_cfg(int64_t need, int es) {
 }
 
 // ---------------------------------------------------------------- path 4
-template <typename T, int P, int NT, int NR, int NL, int NXW, int OP>
+template <typename T, int P, int NT, int NR, int NL, int NXW, int OP, bool IP = false>
 int launch_parts_cfg(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g,
-                     float* l, hipStream_t st) {
+                     float* l, hipStream_t st, uint64_t* in_place = nullptr) {
   const int64_t blocks = P * ((B + 7) / 8 * 8);
   if (blocks > 0x7fffffffLL) return CE_ERR_SHAPE;
-  ce_host::launch((ce::ce_part_kernel<T, P, NT, NR, NL, NXW, OP>), dim3((unsigned)blocks), dim3(NT),
-                     0, st, z, t, B, (int)C, rs, g, l,
-                     g_part_polls.load(std::memory_order_relaxed),
-                     g_part_counter.load(std::memory_order_relaxed));
+  ce_host::launch((ce::ce_part_kernel<T, P, NT, NR, NL, NXW, OP, IP>), dim3((unsigned)blocks),
+                  dim3(NT), 0, st, z, t, B, (int)C, rs, g, l,
+                  g_part_polls.load(std::memory_order_relaxed),
+                  g_part_counter.load(std::memory_order_relaxed), in_place);
   return launched();
 }
 
 template <typename T, int OP>
 int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g, float* l,
-                 hipStream_t st) {
+                 hipStream_t st, uint64_t* in_place = nullptr) {
   const int64_t nb = body_vectors_max(C, sizeof(T));
+  if (in_place != nullptr) {  // two-part rows in place (two_part_row)
+    if constexpr (OP == ce::kOpCE) {
+      if (nb > kPartsOne && nb <= kPartsTwoRegs)
+        return launch_parts_cfg<T, 2, 1024, 8, 0, 0, OP, true>(z, t, B, C, rs, g, l, st, in_place);
+      if (nb > kPartsTwoRegs && nb <= kPartsTwo)
+        return launch_parts_cfg<T, 2, 1024, 8, 4, 0, OP, true>(z, t, B, C, rs, g, l, st, in_place);
+    }
+    return CE_ERR_PATH;
+  }
   if (nb <= kPartsOneQuarter) return launch_parts_cfg<T, 1, 256, 8, 0, 0, OP>(z, t, B, C, rs, g, l, st);
   if (nb <= kPartsOneSmall) return launch_parts_cfg<T, 1, 1024, 4, 0, 0, OP>(z, t, B, C, rs, g, l, st);
   if (nb <= kPartsOne) return launch_parts_cfg<T, 1, 1024, 8, 2, 0, OP>(z, t, B, C, rs, g, l, st);
@@ -557,7 +566,7 @@ int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs
 // (nothing has to stay on chip for a gradient, so no row parts).
 template <typename T, int OP, bool GRAD>
 int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g, float* l,
-              ce::RowArgs rs, hipStream_t st) {
+              ce::RowArgs rs, hipStream_t st, uint64_t* in_place = nullptr) {
   constexpr int es = sizeof(T);
   const bool aligned = (uintptr_t)z % 16 == 0 && (rs.ldz * es) % 16 == 0 &&
                        (!GRAD || ((uintptr_t)g % 16 == 0 && (rs.ldg * es) % 16 == 0));
@@ -587,7 +596,7 @@ int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g
                                      B, C, rs, g, l, st);
     }
     case kPathParts:
-      if constexpr (GRAD) return launch_parts<T, OP>(z, t, B, C, rs, g, l, st);
+      if constexpr (GRAD) return launch_parts<T, OP>(z, t, B, C, rs, g, l, st, in_place);
       return CE_ERR_PATH;
     default:
       return CE_ERR_PATH;
@@ -598,6 +607,25 @@ int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g
 // other's logits (the recompute) and keep mailboxes in grad, so they cannot
 // run in place.
 bool multi_part_row(int64_t C, int es) { return body_vectors_max(C, es) > kPartsOne; }
+
+// Rows that path 4 cuts into exactly two parts: these run in place too, on
+// the in-place variant of the part kernel, when ce_fwd_grad_ex is given
+// the rows' words (ce_fwd_inplace_workspace_bytes).
+bool two_part_row(int64_t C, int es) {
+  const int64_t nb = body_vectors_max(C, es);
+  return nb > kPartsOne && nb <= kPartsTwo;
+}
+
+// The in-place rows' words in a ce_fwd_grad_ex workspace: two 64-bit words
+// a row from byte kInPlaceWordsOffset (the ignore_index count sits at byte
+// 0), or null when the workspace is missing, too small or not 8-byte
+// aligned.
+constexpr size_t kInPlaceWordsOffset = 256;
+uint64_t* in_place_words(void* ws, size_t ws_bytes, int64_t B) {
+  if (ws == nullptr || (uintptr_t)ws % 8 != 0) return nullptr;
+  if (ws_bytes < kInPlaceWordsOffset + (size_t)B * 16) return nullptr;
+  return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kInPlaceWordsOffset);
+}
 
 // Rows that do not run as row parts (the loss alone, rows of several parts
 // in place): path 5 where it has a configuration for contiguous rows (it falls
@@ -726,13 +754,13 @@ struct FwdArgs {
 
 template <typename T>
 int fwd_dispatch(int op, int path, const void* z, const int32_t* t, int64_t B, int64_t C, void* g,
-                 float* l, ce::RowArgs rs, hipStream_t st) {
+                 float* l, ce::RowArgs rs, hipStream_t st, uint64_t* in_place) {
   const T* zz = (const T*)z;
   T* gg = (T*)g;
   switch (op) {
     case ce::kOpCE:
       if (!g) return fwd_typed<T, ce::kOpCE, false>(path, zz, t, B, C, nullptr, l, rs, st);
-      return fwd_typed<T, ce::kOpCE, true>(path, zz, t, B, C, gg, l, rs, st);
+      return fwd_typed<T, ce::kOpCE, true>(path, zz, t, B, C, gg, l, rs, st, in_place);
     case ce::kOpSoftmax:
       return fwd_typed<T, ce::kOpSoftmax, true>(path, zz, t, B, C, gg, l, rs, st);
     case ce::kOpShard:
@@ -776,12 +804,18 @@ int fwd_impl(const FwdArgs& a, void* stream) {
 
   const int forced = g_force_path.load(std::memory_order_relaxed);
   int path = forced ? forced : auto_path(C, es);
+  // In place, two-part rows keep path 4 when the workspace holds their
+  // words (in_place_words).
+  const bool ip_parts = in_place && a.op == ce::kOpCE && two_part_row(C, es) &&
+                        in_place_words(a.ws, a.ws_bytes, B) != nullptr;
   if (!a.grad || in_place) {
-    if (path == kPathParts && (!a.grad || multi_part_row(C, es))) {
+    if (path == kPathParts && (!a.grad || (multi_part_row(C, es) && !ip_parts))) {
       if (forced) return CE_ERR_PATH;
       path = path_without_parts(C, es, a.grad != nullptr);
     }
   }
+  uint64_t* const ip_words =
+      ip_parts && path == kPathParts ? in_place_words(a.ws, a.ws_bytes, B) : nullptr;
   const bool short_ok = short_span_ok(C, a.ldz, es) && (!a.grad || short_span_ok(C, ldg, es));
   if (path == kPathShort && !forced && !short_ok) path = kPathResident;
   // path 5 loads vectors that every row start of both arrays is aligned to
@@ -831,11 +865,14 @@ int fwd_impl(const FwdArgs& a, void* stream) {
                            (int)C, rs, a.grad, a.loss, st);
   switch (a.dtype) {
     case CE_F32:
-      return fwd_dispatch<float>(a.op, path, a.logits, a.targets, B, C, a.grad, a.loss, rs, st);
+      return fwd_dispatch<float>(a.op, path, a.logits, a.targets, B, C, a.grad, a.loss, rs, st,
+                                 ip_words);
     case CE_BF16:
-      return fwd_dispatch<__bf16>(a.op, path, a.logits, a.targets, B, C, a.grad, a.loss, rs, st);
+      return fwd_dispatch<__bf16>(a.op, path, a.logits, a.targets, B, C, a.grad, a.loss, rs, st,
+                                  ip_words);
     default:
-      return fwd_dispatch<_Float16>(a.op, path, a.logits, a.targets, B, C, a.grad, a.loss, rs, st);
+      return fwd_dispatch<_Float16>(a.op, path, a.logits, a.targets, B, C, a.grad, a.loss, rs, st,
+                                    ip_words);
   }
 }
 
@@ -1140,6 +1177,11 @@ int ce_fwd_grad_scaled(const void* logits, const int32_t* targets, int64_t B, in
 
 size_t ce_fwd_workspace_bytes(int32_t ignore_index) {
   return ignore_index == CE_NO_IGNORE ? 0 : 4;
+}
+
+size_t ce_fwd_inplace_workspace_bytes(int64_t B) {
+  if (B <= 0 || B > 0x7fffffffLL) return 0;
+  return kInPlaceWordsOffset + (size_t)B * 16;
 }
 
 int ce_fwd_grad_ex(const void* logits, int64_t ld_logits, const int32_t* targets, int64_t B,

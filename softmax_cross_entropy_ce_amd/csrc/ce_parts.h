@@ -163,6 +163,37 @@ __device__ __forceinline__ void wg_pair(float c, float s, float* red_c, float* r
   lds_pairs_combine<NW>(red_c, red_s, lane, cg, sg);
 }
 
+// In place (IP): two-part rows whose gradient overwrites the logits.  A
+// part cannot keep a mailbox in its own logits, and a part that stops
+// waiting cannot recompute its partner's pair from the partner's logits,
+// which may already be gradient.  So the row has two 64-bit words in a
+// workspace (zero on entry and again on exit), each holding a pair as
+// the bitwise complement of (c bits, s bits), so that 0 means empty:
+//  - each part, with its pair, tries to claim word 0 by compare-and-swap
+//    from 0.  The part that claims it is the first; the other reads the
+//    first's pair from it.
+//  - the second publishes its pair into word 1 by compare-and-swap from 0
+//    and writes its own half.
+//  - the first polls word 1 a bounded number of times.  If the pair is
+//    there it writes its own half; if not, it claims word 1 with
+//    kInPlaceDeferred and ends without writing anything, so its half is
+//    still logits.  The second then finds word 1 taken, and writes both
+//    halves, reading the first's logits itself.
+//  - whoever reads the words last (the first when it found the pair, the
+//    second when the first deferred) sets both back to 0.
+// No wait is unbounded and no part reads logits that may have been
+// overwritten.  Every gradient element is 2^(z log2e - c') with the row's
+// c', whichever part writes it, so the bits do not depend on who writes.
+constexpr uint64_t kInPlaceDeferred = ~(((uint64_t)kMailTag << 32) | kMailTag);
+
+__device__ __forceinline__ uint64_t in_place_word(float c, float s) {
+  return ~(((uint64_t)__builtin_bit_cast(uint32_t, c) << 32) | __builtin_bit_cast(uint32_t, s));
+}
+__device__ __forceinline__ void in_place_pair(uint64_t w, float& c, float& s) {
+  c = __builtin_bit_cast(float, (uint32_t)(~w >> 32));
+  s = __builtin_bit_cast(float, (uint32_t)~w);
+}
+
 // Vectors a part of ce_part_kernel<T, P, NT, NR, NL, NXW> holds.
 constexpr int part_capacity(int NT, int NR, int NL, int NXW) { return (NR + NL) * NT + NXW * 64; }
 
@@ -202,11 +233,14 @@ constexpr int part_lds_terms(int NT, int NR, int ES, int NL, int NXW) {
 // that recomputed its partner's pair instead of receiving it.  spin: polls
 // before that happens (0: every part recomputes).  At most 64 VGPRs (eight
 // waves per SIMD), so 32 / (NT / 64) workgroups fit a CU by waves.
-template <typename T, int P, int NT, int NR, int NL, int NXW, int OP = kOpCE>
+//
+// IP: the gradient in place of the logits (two parts a row; in_place: the
+// rows' word pairs, see kInPlaceDeferred).
+template <typename T, int P, int NT, int NR, int NL, int NXW, int OP = kOpCE, bool IP = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(part_waves(NR))))
-void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ targets, int64_t B,
-                    int C, RowArgs rs, T* __restrict__ grad, float* __restrict__ loss_rows,
-                    int spin, uint32_t* __restrict__ fallbacks) {
+void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_t B, int C,
+                    RowArgs rs, T* grad, float* __restrict__ loss_rows, int spin,
+                    uint32_t* __restrict__ fallbacks, uint64_t* __restrict__ in_place) {
   const float invB = row_invB(rs), gmul = grad_mul(rs);
   using E = Elem<T>;
   constexpr int NW = NT / 64, VE = E::VE, ES = sizeof(T);
@@ -216,12 +250,13 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   static_assert(P == 1 || P == 2 || P == 4 || P == 8, "one, two, four or eight parts per row");
   static_assert(NT % 64 == 0 && NW >= 1 && NW <= 16, "1 to 16 waves");
   static_assert(NXW >= 0 && NXW < NW, "partial LDS slot smaller than a slot");
+  static_assert(!IP || (P == 2 && OP == kOpCE), "in place: two parts, the loss with a gradient");
   // 16-bit parts held in registers alone keep the fp32 terms of their first
   // kLdsTerms register slots in LDS (32 bytes per thread and slot: two
   // slots, 64 KB, for 1024 threads, so two workgroups still fit a CU), so
   // that the gradient of those slots is one multiply per element instead
   // of an fma and an exponential.
-  constexpr int kLdsTerms = part_lds_terms(NT, NR, sizeof(T), NL, NXW);
+  constexpr int kLdsTerms = IP ? 0 : part_lds_terms(NT, NR, sizeof(T), NL, NXW);
   static_assert(kLdsTerms <= NR, "kept slots are register slots");
   __shared__ u32x4 stage[NL * NT + NX > 0 ? NL * NT + NX : 1];
   __shared__ f32x4 kept[kLdsTerms > 0 ? kLdsTerms * 2 * NT : 1];
@@ -233,6 +268,9 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   // g_t.
   __shared__ float fin[5];
   __shared__ int fin_ok;
+  // in place: 0 each part writes its own half, 1 this part deferred (it
+  // writes nothing), 2 this part writes both halves
+  __shared__ int ip_mode;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t voff = (uint32_t)tid * 16u;
@@ -273,7 +311,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   auto mail_index = [](int from, int to) { return 2 * (from < to ? from : from - 1); };
   uint64_t* const mine = P > 1 ? mailbox(own) : nullptr;
   constexpr uint64_t kEmptyWord = (uint64_t)kMailEmpty << 32;
-  if constexpr (P > 1) {
+  if constexpr (P > 1 && !IP) {
     if (tid == 0) {
 #pragma unroll
       for (int w = 0; w < 2 * NM; ++w)
@@ -413,7 +451,7 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
   };
 
   // Phase B: this part's pair.
-  constexpr bool kKeepTerms = sizeof(T) == 4 && P <= 4;
+  constexpr bool kKeepTerms = sizeof(T) == 4 && P <= 4 && !IP;
   // Each phase tests the slots against its own opaque copy of the part's
   // length: conditions shared between phases would stay live in scalar
   // registers from pass 1 to the gradient, and the compiler spills them.
@@ -550,7 +588,48 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       float c_own, s_own;
       lds_pairs_combine<NW>(red_c, red_s, lane, c_own, s_own);
       fold_target(tin.part, zt, c_own, s_own);
-      if (tid == 0) {
+      if (IP && tid == 0) {
+        mail_c[part] = c_own;
+        mail_s[part] = s_own;
+        const int q = 1 - part;
+        const uint64_t mw = in_place_word(c_own, s_own);
+        uint64_t* const words = in_place + 2 * row;
+        uint64_t first = 0;
+        int mode = 0;
+        if (__hip_atomic_compare_exchange_strong(&words[0], &first, mw, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          // the first: the partner's pair comes to word 1
+          uint64_t o = 0;
+          for (int it = 0; it < spin; ++it) {
+            o = __hip_atomic_load(&words[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (o != 0) break;
+            __builtin_amdgcn_s_sleep(8);
+          }
+          if (o == 0 && __hip_atomic_compare_exchange_strong(&words[1], &o, kInPlaceDeferred,
+                                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT)) {
+            mode = 1;
+          } else {
+            in_place_pair(o, mail_c[q], mail_s[q]);
+            __hip_atomic_store(&words[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&words[1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        } else {
+          // the second: `first` holds the partner's pair
+          in_place_pair(first, mail_c[q], mail_s[q]);
+          uint64_t e = 0;
+          if (!__hip_atomic_compare_exchange_strong(&words[1], &e, mw, __ATOMIC_RELAXED,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            mode = 2;  // the partner deferred: both halves are this part's to write
+            __hip_atomic_store(&words[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&words[1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+        if (mode == 1 && fallbacks != nullptr) atomicAdd(fallbacks, 1u);
+        ip_mode = mode;
+        mail_ok[0] = mail_ok[1] = 1;
+        fin_ok = 1;
+      } else if (tid == 0) {
         mail_c[part] = c_own;
         mail_s[part] = s_own;
         const uint64_t tag = (uint64_t)kMailTag << 32;
@@ -606,7 +685,9 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       if (fin_ok) {
         combine_pairs<P>(mail_c, mail_s, cg, sx);
         rr = row_finish<OP>(cg, sx, zt, valid, rt.ignored, invB, gmul);
-        if (part == 0 && tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
+        // the loss goes with part 0's half (in place: with whoever writes it)
+        const bool stores = IP ? (ip_mode == 0 ? part == 0 : ip_mode == 2) : part == 0;
+        if (stores && tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
         if (tid == 0) {
           fin[0] = cg;
           fin[1] = sx;
@@ -617,6 +698,9 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
       }
     }
     __syncthreads();
+    if constexpr (IP) {
+      if (ip_mode == 1) return;  // uniform: deferred, the partner writes this half
+    }
     if (fin_ok) {  // uniform (LDS, after the barrier): the common case
       cg = fin[0];
       sx = fin[1];
@@ -765,6 +849,30 @@ void ce_part_kernel(const T* __restrict__ logits, const int32_t* __restrict__ ta
 #pragma unroll
       for (int p = 0; p < NLS; ++p) write_slot(NR + p, lds_slot(p));
       if (xe >= 0) E::store1(gp + xe, xe == t ? rr.gt : grad_of(xs));
+      if constexpr (IP) {
+        if (ip_mode == 2) {  // uniform: the partner deferred, its half is still logits
+          const int q = 1 - part;
+          const PartRange pq = part_range(geo.nb, P, q);
+          const rsrc_t rq = make_rsrc(rp + geo.h + pq.v0 * VE, (uint32_t)pq.len * 16u);
+          const rsrc_t rqo = make_rsrc(gp + geo.h + pq.v0 * VE, (uint32_t)pq.len * 16u);
+          const int nq = (pq.len + NT - 1) / NT;
+#pragma unroll 1
+          for (int k = 0; k < nq; ++k) {
+            float f[VE], g[VE];
+            E::unpack(bload128<kPolicyStream>(rq, voff, (uint32_t)k * NT * 16u), f);
+#pragma unroll
+            for (int i = 0; i < VE; ++i) g[i] = grad_of(f[i]);
+            bstore128<kPolicyStream>(E::pack(g), rqo, voff, (uint32_t)k * NT * 16u);
+          }
+          const int xq = edge_elem(q);
+          if (xq >= 0) {
+            const float x = bload_elem<T>(rrow, (uint32_t)xq * ES);
+            E::store1(gp + xq, xq == t ? rr.gt : grad_of(x));
+          }
+          const TargetIn tq = target_in(pq);
+          if (tq.k >= 0) E::store1(gp + geo.h + (int64_t)tvec * VE + tj, rr.gt);
+        }
+      }
     };
     if (gmul == 1.0f)
       phase_c(std::true_type{});

@@ -41,7 +41,8 @@ def test_library_exports_every_declared_function():
                             "ce_fwd_grad_scaled", "ce_scale_grad", "ce_fwd_loss",
                             "ce_softmax_fwd", "ce_softmax_bwd", "ce_shard_stats",
                             "ce_shard_grad", "ce_fwd_grad_ex", "ce_fwd_workspace_bytes",
-                            "ce_reduce_loss_noalloc", "ce_debug_time_next_launch"])
+                            "ce_reduce_loss_noalloc", "ce_debug_time_next_launch",
+                            "ce_fwd_inplace_workspace_bytes"])
     for n in names:
         assert hasattr(L_, n), n
 
@@ -352,6 +353,15 @@ def fex(z=Z, ldz=10, t=T, B=8, C=10, dtype=0, g=G, ldg=10, l=L, sc=None, ii=NO_I
 def test_fwd_workspace_bytes():
     assert ce.fwd_workspace_bytes() == 0 and ce.fwd_workspace_bytes(-100) == 4
     assert ce.fwd_workspace_bytes(0) == 4
+
+
+def test_fwd_inplace_workspace_bytes():
+    f = ce.fwd_inplace_workspace_bytes
+    # 256 bytes (the ignore_index count in the first 4), then two 64-bit
+    # words a row
+    assert f(1) == 256 + 16 and f(8192) == 256 + 16 * 8192
+    assert f((1 << 31) - 1) == 256 + 16 * ((1 << 31) - 1)
+    assert f(0) == 0 and f(-1) == 0 and f(1 << 31) == 0
 
 
 def test_fwd_grad_ex_validation():

@@ -37,6 +37,11 @@ def _ce():
     return ce
 
 
+def _bits(x):
+    import torch
+    return x.view(torch.int16 if x.element_size() == 2 else torch.int32)
+
+
 @pytest.fixture(autouse=True)
 def _reset_path():
     ce = _ce()
@@ -54,6 +59,13 @@ def _two_part(C, dtype):
     to 65536 16-byte vectors)."""
     nb = C // (4 if dtype == "f32" else 8)
     return 10 * 1024 < nb <= 64 * 1024
+
+
+def _exactly_two_parts(C, dtype):
+    """Rows that path 4 cuts into exactly two parts (10241 to 24576
+    vectors): in place with the in-place workspace they stay on path 4."""
+    nb = C // (4 if dtype == "f32" else 8)
+    return 10 * 1024 < nb <= 24 * 1024
 
 
 def _check_losses(lr_gpu, z, t, dtype, where, B=None):
@@ -130,16 +142,31 @@ def test_in_place_matches_oracle(B, C, dtype, sigma, path):
     zd, td = to_device(z, t, dtype)
     buf = zd.clone()
     if path == 4 and _two_part(C, dtype):
+        # without the in-place workspace (ce_fwd_grad), and with it for rows
+        # of four or eight parts, forcing path 4 in place is refused
         with pytest.raises(ce.CEError):
-            ce.fwd_grad_inplace_(buf, td)
-        return
+            ce.fwd_grad_into(buf, td, buf, torch.empty(B, dtype=torch.float32, device=zd.device))
+        if not _exactly_two_parts(C, dtype):
+            with pytest.raises(ce.CEError):
+                ce.fwd_grad_inplace_(buf, td)
+            return
     lr = ce.fwd_grad_inplace_(buf, td)
     torch.cuda.synchronize()
     g = grad_to_host(buf, dtype)
     worst, l_ora = compare_block(g, lr.cpu().numpy(), z, t, B, dtype, where=f"in place {B}x{C} p{path}")
     print(f"[in-place] {B}x{C} {dtype} p{path}: {worst}", flush=True)
-    # the same kernel out of place: the same bits (two-part rows run in
-    # place on the resident or long path)
+    if path in (0, 4) and _exactly_two_parts(C, dtype):
+        # the in-place part kernel: the same bits when every first part
+        # defers its half to its partner
+        prev = ce.part_polls(0)
+        buf2 = zd.clone()
+        lr2 = ce.fwd_grad_inplace_(buf2, td)
+        ce.part_polls(prev)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(buf2), _bits(buf)) and torch.equal(_bits(lr2), _bits(lr))
+        return
+    # the same kernel out of place: the same bits (rows of four or eight
+    # parts run in place on the resident or long path)
     if path != 0 or not _two_part(C, dtype):
         g0, l0 = ce.fwd_grad(zd, td)
     else:
@@ -152,7 +179,8 @@ def test_in_place_matches_oracle(B, C, dtype, sigma, path):
 
 
 def test_in_place_autograd_style_loop():
-    """Several in-place calls in a row on fresh logits: each matches the
+    """Several in-place calls in a row on fresh logits (ce_fwd_grad, no
+    workspace, so two-part rows run on path 2): each matches the
     out-of-place result of its kernel."""
     import torch
     ce = _ce()
@@ -160,7 +188,7 @@ def test_in_place_autograd_style_loop():
         z, t = synth.make_inputs(16, 128256, "bf16", 4.0, seed=100 + seed)
         zd, td = to_device(z, t, "bf16")
         buf = zd.clone()
-        ce.fwd_grad_inplace_(buf, td)
+        ce.fwd_grad_into(buf, td, buf, torch.empty(16, dtype=torch.float32, device=zd.device))
         ce.force_path(2)
         g0, _ = ce.fwd_grad(zd, td)
         ce.force_path(0)
