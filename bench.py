@@ -294,7 +294,7 @@ def loss_only_and_in_place(zd, td, grad, loss_rows, reps: int = 20) -> dict:
     """ce_fwd_loss (logits read once, per-row losses written) and the
     gradient in place of the logits (on a copy of them; each call then
     reads the previous call's gradient, a valid input of the same size):
-    ce_fwd_grad_ex with the in-place workspace, so that rows of two parts
+    ce_fwd_grad_ex with the in-place workspace, so that rows of several parts
     stay on path 4, and ce_fwd_grad, which has no workspace."""
     import torch
     import softmax_cross_entropy_ce_amd as ce

@@ -90,7 +90,7 @@ typedef enum {
  *             again from the same thread, before writing it; rows that
  *             path 4 would cut into several parts run on path 2 or 3
  *             instead; with ce_fwd_grad_ex and an in-place workspace,
- *             two-part rows run on path 4).
+ *             they run on path 4).
  *             Any other overlap with logits is refused.  Must be aligned
  *             to the element size, and (grad_out - logits) must be a
  *             multiple of 16 bytes (true for any two allocations from the
@@ -165,7 +165,7 @@ int ce_fwd_grad_scaled(const void* logits, const int32_t* targets, int64_t B, in
  *   workspace     device scratch of ce_fwd_workspace_bytes(ignore_index)
  *                 bytes (4-byte aligned), or NULL when that is 0; it holds
  *                 the count N while the call's kernels run.  In place, rows
- *                 that path 4 cuts into two parts run as two parts when the
+ *                 that path 4 cuts into several parts run as parts when the
  *                 workspace also has ce_fwd_inplace_workspace_bytes(B)
  *                 bytes, is 8-byte aligned and was zero-filled before its
  *                 first use (each call leaves those bytes zero again, so a
@@ -179,26 +179,33 @@ size_t ce_fwd_workspace_bytes(int32_t ignore_index);
 
 /*
  * ce_fwd_inplace_workspace_bytes - the ce_fwd_grad_ex workspace with which
- * the gradient in place of rows that path 4 cuts into two parts (bf16 and
- * fp16 C of 81921 to 196608, fp32 C of 40961 to 98304, for rows starting on
- * a 16-byte boundary) runs on path 4: 256 bytes (the ignore_index count in
- * the first 4), then two 64-bit words a row, 256 + 16 B in all (0 for B
- * outside [1, 2^31 - 1]).
+ * the gradient in place of rows that path 4 cuts into several parts (bf16
+ * and fp16 C of 81921 to 524288 in two, four or eight parts, fp32 C of
+ * 40961 to 262144, for rows starting on a 16-byte boundary) runs on path
+ * 4: 256 bytes (the ignore_index count in the first 4), then 18 64-bit
+ * words a row, 256 + 144 B in all (0 for B outside [1, 2^31 - 1]).
  *
  * Defined by: as ce_fwd_grad (the gradient formed in the forward pass,
  * here over the logits' own storage).
  *
- * The two parts of a row cannot trade their partial results through the
+ * The parts of a row cannot trade their partial results through the
  * gradient (it is the logits), and a part that stops waiting for its
- * partner cannot read the partner's logits again (they may be gradient
- * already).  So each row's parts meet at its two words: the first to
- * arrive claims the first word with its pair; the second reads that pair,
+ * partners cannot read their logits again (they may be gradient already).
+ * So each row's parts meet at its words.  Two parts: the first to arrive
+ * claims the first word with its pair; the second reads that pair,
  * publishes its own in the second word and writes its half; the first
  * polls the second word a bounded number of times and then either writes
  * its half or marks the word and ends without writing, leaving its half
  * as logits for the second part to write as well (the second finds the
- * mark when it publishes).  No wait is unbounded, and each element's
- * value does not depend on which part wrote it.
+ * mark when it publishes).  Four or eight parts: each part publishes its
+ * pair in a word of its own and counts its arrival; the last to arrive
+ * reads every pair and claims each other part's flag word, writing the
+ * gradient of any part whose flag it finds marked; any other part polls
+ * for the pairs a bounded number of times, then writes its own part, or
+ * marks its flag and ends without writing, or (when the last part has
+ * already claimed its flag, so every pair is on its way) reads the pairs
+ * and writes its own part.  No wait is on a part that has not published,
+ * and each element's value does not depend on which part wrote it.
  */
 size_t ce_fwd_inplace_workspace_bytes(int64_t B);
 

@@ -297,7 +297,7 @@ def fwd_grad_into(logits, targets, grad, loss_rows) -> None:
 def fwd_grad_inplace_(logits, targets):
     """Overwrite logits with the gradient (softmax - onehot) / B and return
     the per-row losses (ce_fwd_grad_ex with the in-place workspace of
-    torch's current stream, so rows of two parts stay on path 4)."""
+    torch's current stream, so rows of several parts stay on path 4)."""
     torch = _torch()
     loss_rows = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device)
     fwd_grad_ex_into(logits, targets, logits, loss_rows)

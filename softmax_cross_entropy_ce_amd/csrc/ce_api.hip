@@ -540,12 +540,21 @@ template <typename T, int OP>
 int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs rs, T* g, float* l,
                  hipStream_t st, uint64_t* in_place = nullptr) {
   const int64_t nb = body_vectors_max(C, sizeof(T));
-  if (in_place != nullptr) {  // two-part rows in place (two_part_row)
+  if (in_place != nullptr) {  // rows of several parts in place, the same parts as out of place
     if constexpr (OP == ce::kOpCE) {
-      if (nb > kPartsOne && nb <= kPartsTwoRegs)
+      if (nb <= kPartsOne) return CE_ERR_PATH;
+      if (nb <= kPartsTwoRegs)
         return launch_parts_cfg<T, 2, 1024, 8, 0, 0, OP, true>(z, t, B, C, rs, g, l, st, in_place);
-      if (nb > kPartsTwoRegs && nb <= kPartsTwo)
+      if (nb <= kPartsTwo)
         return launch_parts_cfg<T, 2, 1024, 8, 4, 0, OP, true>(z, t, B, C, rs, g, l, st, in_place);
+      if (nb <= kPartsFourRegs)
+        return launch_parts_cfg<T, 4, 1024, 8, 0, 0, OP, true>(z, t, B, C, rs, g, l, st, in_place);
+      if constexpr (sizeof(T) == 2) {
+        if (nb <= kPartsFour)
+          return launch_parts_cfg<T, 4, 1024, 8, 4, 0, OP, true>(z, t, B, C, rs, g, l, st, in_place);
+      }
+      if (nb <= kPartsEightRegs)
+        return launch_parts_cfg<T, 8, 1024, 8, 0, 0, OP, true>(z, t, B, C, rs, g, l, st, in_place);
     }
     return CE_ERR_PATH;
   }
@@ -604,26 +613,20 @@ int fwd_typed(int path, const T* z, const int32_t* t, int64_t B, int64_t C, T* g
 }
 
 // Rows that path 4 cuts into several parts: their parts may read each
-// other's logits (the recompute) and keep mailboxes in grad, so they cannot
-// run in place.
+// other's logits (the recompute) and keep mailboxes in grad, so in place
+// they run on the in-place variant of the part kernel, and only when
+// ce_fwd_grad_ex is given the rows' words (ce_fwd_inplace_workspace_bytes).
 bool multi_part_row(int64_t C, int es) { return body_vectors_max(C, es) > kPartsOne; }
 
-// Rows that path 4 cuts into exactly two parts: these run in place too, on
-// the in-place variant of the part kernel, when ce_fwd_grad_ex is given
-// the rows' words (ce_fwd_inplace_workspace_bytes).
-bool two_part_row(int64_t C, int es) {
-  const int64_t nb = body_vectors_max(C, es);
-  return nb > kPartsOne && nb <= kPartsTwo;
-}
-
-// The in-place rows' words in a ce_fwd_grad_ex workspace: two 64-bit words
-// a row from byte kInPlaceWordsOffset (the ignore_index count sits at byte
-// 0), or null when the workspace is missing, too small or not 8-byte
-// aligned.
+// The in-place rows' words in a ce_fwd_grad_ex workspace: a block of
+// ce::kInPlaceRowWords 64-bit words a row from byte kInPlaceWordsOffset (the
+// ignore_index count sits at byte 0), or null when the workspace is
+// missing, too small or not 8-byte aligned.
 constexpr size_t kInPlaceWordsOffset = 256;
+constexpr size_t kInPlaceRowBytes = 8 * (size_t)ce::kInPlaceRowWords;
 uint64_t* in_place_words(void* ws, size_t ws_bytes, int64_t B) {
   if (ws == nullptr || (uintptr_t)ws % 8 != 0) return nullptr;
-  if (ws_bytes < kInPlaceWordsOffset + (size_t)B * 16) return nullptr;
+  if (ws_bytes < kInPlaceWordsOffset + (size_t)B * kInPlaceRowBytes) return nullptr;
   return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kInPlaceWordsOffset);
 }
 
@@ -804,9 +807,9 @@ int fwd_impl(const FwdArgs& a, void* stream) {
 
   const int forced = g_force_path.load(std::memory_order_relaxed);
   int path = forced ? forced : auto_path(C, es);
-  // In place, two-part rows keep path 4 when the workspace holds their
-  // words (in_place_words).
-  const bool ip_parts = in_place && a.op == ce::kOpCE && two_part_row(C, es) &&
+  // In place, rows of several parts keep path 4 when the workspace holds
+  // their words (in_place_words).
+  const bool ip_parts = in_place && a.op == ce::kOpCE && multi_part_row(C, es) &&
                         in_place_words(a.ws, a.ws_bytes, B) != nullptr;
   if (!a.grad || in_place) {
     if (path == kPathParts && (!a.grad || (multi_part_row(C, es) && !ip_parts))) {
@@ -1181,7 +1184,7 @@ size_t ce_fwd_workspace_bytes(int32_t ignore_index) {
 
 size_t ce_fwd_inplace_workspace_bytes(int64_t B) {
   if (B <= 0 || B > 0x7fffffffLL) return 0;
-  return kInPlaceWordsOffset + (size_t)B * 16;
+  return kInPlaceWordsOffset + (size_t)B * kInPlaceRowBytes;
 }
 
 int ce_fwd_grad_ex(const void* logits, int64_t ld_logits, const int32_t* targets, int64_t B,

@@ -163,12 +163,17 @@ __device__ __forceinline__ void wg_pair(float c, float s, float* red_c, float* r
   lds_pairs_combine<NW>(red_c, red_s, lane, cg, sg);
 }
 
-// In place (IP): two-part rows whose gradient overwrites the logits.  A
-// part cannot keep a mailbox in its own logits, and a part that stops
-// waiting cannot recompute its partner's pair from the partner's logits,
-// which may already be gradient.  So the row has two 64-bit words in a
-// workspace (zero on entry and again on exit), each holding a pair as
-// the bitwise complement of (c bits, s bits), so that 0 means empty:
+// In place (IP): rows of several parts whose gradient overwrites the
+// logits.  A part cannot keep a mailbox in its own logits, and a part that
+// stops waiting cannot recompute a partner's pair from the partner's
+// logits, which may already be gradient.  So each row has a block of
+// kInPlaceRowWords 64-bit words in a workspace (zero on entry and again on
+// exit); a pair is stored as the bitwise complement of (c bits, s bits),
+// so that 0 means empty.  A part that gives up waiting always ends without
+// writing anything, so its logits are still there for the part that then
+// writes its gradient.
+//
+// Two parts, words 0 and 1:
 //  - each part, with its pair, tries to claim word 0 by compare-and-swap
 //    from 0.  The part that claims it is the first; the other reads the
 //    first's pair from it.
@@ -176,14 +181,39 @@ __device__ __forceinline__ void wg_pair(float c, float s, float* red_c, float* r
 //    and writes its own half.
 //  - the first polls word 1 a bounded number of times.  If the pair is
 //    there it writes its own half; if not, it claims word 1 with
-//    kInPlaceDeferred and ends without writing anything, so its half is
-//    still logits.  The second then finds word 1 taken, and writes both
-//    halves, reading the first's logits itself.
+//    kInPlaceDeferred and ends without writing anything.  The second then
+//    finds word 1 taken, and writes both halves.
 //  - whoever reads the words last (the first when it found the pair, the
 //    second when the first deferred) sets both back to 0.
-// No wait is unbounded and no part reads logits that may have been
-// overwritten.  Every gradient element is 2^(z log2e - c') with the row's
-// c', whichever part writes it, so the bits do not depend on who writes.
+//
+// Four or eight parts: pair words 0..P-1, flag words 8..8+P-1, an arrival
+// count (word 16) and a departure count (word 17), 32-bit counters that
+// wrap to 0 after P:
+//  - each part publishes its pair in its own word (an exchange whose
+//    result it waits for, so the word is written before anything after),
+//    then counts its arrival.  The part that arrives last is the closer:
+//    every other part has published, so the closer gathers all pairs
+//    (polling for words still on their way), then claims each other
+//    part's flag with kInPlaceChecked by compare-and-swap from 0; a flag
+//    that holds kInPlaceDeferred instead makes that part's gradient the
+//    closer's to write, besides its own.
+//  - any other part polls for all the pairs a bounded number of times.
+//    With all of them it writes its own part.  Without, it claims its own
+//    flag with kInPlaceDeferred: if that succeeds it ends without writing
+//    (the closer, still to come, will find the mark); if the flag already
+//    holds kInPlaceChecked, the closer has published, so the pairs are all
+//    on their way: it polls for them again and writes its own part.
+//  - every part counts its departure once its last access to the words has
+//    completed; the last to leave sets the pair and flag words back to 0.
+// No wait depends on a workgroup that has not started, and no part reads
+// logits that may have been overwritten.  Every gradient element is
+// 2^(z log2e - c') with the row's c', whichever part writes it, so the
+// bits do not depend on who writes.
+constexpr int kInPlaceRowWords = 18;
+constexpr int kInPlaceFlags = 8;      // word index of the first flag
+constexpr int kInPlaceCounts = 16;    // word index of the arrival count
+constexpr int kInPlaceLongPolls = 1 << 16;  // polls for pairs already on their way
+constexpr uint64_t kInPlaceChecked = 1;
 constexpr uint64_t kInPlaceDeferred = ~(((uint64_t)kMailTag << 32) | kMailTag);
 
 __device__ __forceinline__ uint64_t in_place_word(float c, float s) {
@@ -234,8 +264,8 @@ constexpr int part_lds_terms(int NT, int NR, int ES, int NL, int NXW) {
 // before that happens (0: every part recomputes).  At most 64 VGPRs (eight
 // waves per SIMD), so 32 / (NT / 64) workgroups fit a CU by waves.
 //
-// IP: the gradient in place of the logits (two parts a row; in_place: the
-// rows' word pairs, see kInPlaceDeferred).
+// IP: the gradient in place of the logits (in_place: the rows' word blocks,
+// see kInPlaceRowWords).
 template <typename T, int P, int NT, int NR, int NL, int NXW, int OP = kOpCE, bool IP = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(part_waves(NR))))
 void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_t B, int C,
@@ -250,7 +280,7 @@ void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_
   static_assert(P == 1 || P == 2 || P == 4 || P == 8, "one, two, four or eight parts per row");
   static_assert(NT % 64 == 0 && NW >= 1 && NW <= 16, "1 to 16 waves");
   static_assert(NXW >= 0 && NXW < NW, "partial LDS slot smaller than a slot");
-  static_assert(!IP || (P == 2 && OP == kOpCE), "in place: two parts, the loss with a gradient");
+  static_assert(!IP || (P >= 2 && OP == kOpCE), "in place: several parts, the loss with a gradient");
   // 16-bit parts held in registers alone keep the fp32 terms of their first
   // kLdsTerms register slots in LDS (32 bytes per thread and slot: two
   // slots, 64 KB, for 1024 threads, so two workgroups still fit a CU), so
@@ -268,9 +298,11 @@ void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_
   // g_t.
   __shared__ float fin[5];
   __shared__ int fin_ok;
-  // in place: 0 each part writes its own half, 1 this part deferred (it
-  // writes nothing), 2 this part writes both halves
-  __shared__ int ip_mode;
+  // in place: ip_deferred, this part ends without writing (its partner
+  // writes its gradient); ip_extra, a bit per other part whose gradient
+  // this part writes besides its own
+  __shared__ int ip_deferred;
+  __shared__ unsigned ip_extra;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t voff = (uint32_t)tid * 16u;
@@ -588,12 +620,12 @@ void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_
       float c_own, s_own;
       lds_pairs_combine<NW>(red_c, red_s, lane, c_own, s_own);
       fold_target(tin.part, zt, c_own, s_own);
-      if (IP && tid == 0) {
+      if (IP && P == 2 && tid == 0) {
         mail_c[part] = c_own;
         mail_s[part] = s_own;
         const int q = 1 - part;
         const uint64_t mw = in_place_word(c_own, s_own);
-        uint64_t* const words = in_place + 2 * row;
+        uint64_t* const words = in_place + row * kInPlaceRowWords;
         uint64_t first = 0;
         int mode = 0;
         if (__hip_atomic_compare_exchange_strong(&words[0], &first, mw, __ATOMIC_RELAXED,
@@ -626,8 +658,90 @@ void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_
           }
         }
         if (mode == 1 && fallbacks != nullptr) atomicAdd(fallbacks, 1u);
-        ip_mode = mode;
+        ip_deferred = mode == 1 ? 1 : 0;
+        ip_extra = mode == 2 ? 1u << q : 0u;
         mail_ok[0] = mail_ok[1] = 1;
+        fin_ok = 1;
+      } else if (IP && tid == 0) {
+        mail_c[part] = c_own;
+        mail_s[part] = s_own;
+        uint64_t* const words = in_place + row * kInPlaceRowWords;
+        uint64_t* const flags = words + kInPlaceFlags;
+        uint32_t* const arrived = reinterpret_cast<uint32_t*>(words + kInPlaceCounts);
+        uint32_t* const departed = reinterpret_cast<uint32_t*>(words + kInPlaceCounts + 1);
+        constexpr unsigned kAll = (1u << P) - 1u;
+        // publish, and wait until the word is written
+        const uint64_t prev = __hip_atomic_exchange(&words[part], in_place_word(c_own, s_own),
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("" ::"v"(prev) : "memory");
+        const uint32_t before =
+            __builtin_amdgcn_atomic_inc32(arrived, (uint32_t)(P - 1), __ATOMIC_RELAXED, "agent");
+        unsigned got = 1u << part;
+        // up to `polls` passes over the pair words (0: none)
+        auto gather = [&](int polls) {
+          for (int it = 0; it < polls; ++it) {
+#pragma unroll 1
+            for (int q = 0; q < P; ++q) {
+              if ((got >> q) & 1u) continue;
+              const uint64_t x =
+                  __hip_atomic_load(&words[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              if (x != 0) {
+                in_place_pair(x, mail_c[q], mail_s[q]);
+                got |= 1u << q;
+              }
+            }
+            if (got == kAll) break;
+            __builtin_amdgcn_s_sleep(8);
+          }
+        };
+        int deferred = 0;
+        unsigned extra = 0;
+        if (before == (uint32_t)(P - 1)) {
+          // the closer: every other part has published
+          gather(kInPlaceLongPolls);
+#pragma unroll 1
+          for (int q = 0; q < P; ++q) {
+            if (q == part) continue;
+            uint64_t e = 0;
+            if (!__hip_atomic_compare_exchange_strong(&flags[q], &e, kInPlaceChecked,
+                                                      __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT))
+              extra |= 1u << q;  // e == kInPlaceDeferred
+          }
+        } else {
+          gather(spin);
+          if (got != kAll) {
+            uint64_t e = 0;
+            if (__hip_atomic_compare_exchange_strong(&flags[part], &e, kInPlaceDeferred,
+                                                     __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT))
+              deferred = 1;
+            else
+              gather(kInPlaceLongPolls);  // e == kInPlaceChecked: the closer has published
+          }
+        }
+        if (!deferred && got != kAll) {
+#pragma unroll 1
+          for (int q = 0; q < P; ++q) {
+            if ((got >> q) & 1u) continue;
+            mail_c[q] = __builtin_nanf("");  // a pair that never came: the row is NaN
+            mail_s[q] = __builtin_nanf("");
+          }
+        }
+        wait_vmcnt<0>();  // every compare-and-swap above has taken effect
+        if (__builtin_amdgcn_atomic_inc32(departed, (uint32_t)(P - 1), __ATOMIC_RELAXED, "agent") ==
+            (uint32_t)(P - 1)) {
+#pragma unroll 1
+          for (int q = 0; q < P; ++q) {
+            __hip_atomic_store(&words[q], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&flags[q], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+        if (deferred && fallbacks != nullptr) atomicAdd(fallbacks, 1u);
+        ip_deferred = deferred;
+        ip_extra = extra;
+#pragma unroll
+        for (int q = 0; q < P; ++q) mail_ok[q] = 1;
         fin_ok = 1;
       } else if (tid == 0) {
         mail_c[part] = c_own;
@@ -686,7 +800,7 @@ void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_
         combine_pairs<P>(mail_c, mail_s, cg, sx);
         rr = row_finish<OP>(cg, sx, zt, valid, rt.ignored, invB, gmul);
         // the loss goes with part 0's half (in place: with whoever writes it)
-        const bool stores = IP ? (ip_mode == 0 ? part == 0 : ip_mode == 2) : part == 0;
+        const bool stores = IP ? (part == 0 ? !ip_deferred : (ip_extra & 1u) != 0) : part == 0;
         if (stores && tid == 0) store_row<OP>(loss_rows, row, rr, cg, sx, zt, t >= 0);
         if (tid == 0) {
           fin[0] = cg;
@@ -699,7 +813,7 @@ void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_
     }
     __syncthreads();
     if constexpr (IP) {
-      if (ip_mode == 1) return;  // uniform: deferred, the partner writes this half
+      if (ip_deferred) return;  // uniform: a partner writes this part's gradient
     }
     if (fin_ok) {  // uniform (LDS, after the barrier): the common case
       cg = fin[0];
@@ -850,8 +964,10 @@ void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_
       for (int p = 0; p < NLS; ++p) write_slot(NR + p, lds_slot(p));
       if (xe >= 0) E::store1(gp + xe, xe == t ? rr.gt : grad_of(xs));
       if constexpr (IP) {
-        if (ip_mode == 2) {  // uniform: the partner deferred, its half is still logits
-          const int q = 1 - part;
+        // parts that deferred to this one: their logits are still there
+#pragma unroll 1
+        for (int q = 0; q < P; ++q) {
+          if (!((ip_extra >> q) & 1u)) continue;  // uniform (LDS)
           const PartRange pq = part_range(geo.nb, P, q);
           const rsrc_t rq = make_rsrc(rp + geo.h + pq.v0 * VE, (uint32_t)pq.len * 16u);
           const rsrc_t rqo = make_rsrc(gp + geo.h + pq.v0 * VE, (uint32_t)pq.len * 16u);

@@ -357,10 +357,10 @@ def test_fwd_workspace_bytes():
 
 def test_fwd_inplace_workspace_bytes():
     f = ce.fwd_inplace_workspace_bytes
-    # 256 bytes (the ignore_index count in the first 4), then two 64-bit
+    # 256 bytes (the ignore_index count in the first 4), then 18 64-bit
     # words a row
-    assert f(1) == 256 + 16 and f(8192) == 256 + 16 * 8192
-    assert f((1 << 31) - 1) == 256 + 16 * ((1 << 31) - 1)
+    assert f(1) == 256 + 144 and f(8192) == 256 + 144 * 8192
+    assert f((1 << 31) - 1) == 256 + 144 * ((1 << 31) - 1)
     assert f(0) == 0 and f(-1) == 0 and f(1 << 31) == 0
 
 

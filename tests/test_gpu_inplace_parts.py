@@ -1,12 +1,13 @@
-"""The gradient in place of rows that path 4 cuts into two parts, on the
-in-place variant of the part kernel (ce_fwd_grad_ex with the in-place
-workspace): every row against the oracle; bitwise the same whether each
-part writes its own half or defers it to its partner (no polls makes
-nearly every first part defer, and the device counter sees the deferrals);
-the workspace's row words zero again after every call; with ignore_index
-and a gradient scale; captured in a HIP graph; and the 8192 x 128256 bf16
-workload at full size.  Without the workspace such rows still run off
-path 4 (and forcing path 4 is refused)."""
+"""The gradient in place of rows that path 4 cuts into two, four or eight
+parts, on the in-place variant of the part kernel (ce_fwd_grad_ex with the
+in-place workspace): every row against the oracle; bitwise the same
+whether each part writes its own gradient or defers it to a partner (no
+polls makes nearly every part but one defer, and the device counter sees
+the deferrals); the workspace's row words zero again after every call;
+with ignore_index and a gradient scale; captured in a HIP graph; the
+8192 x 128256 bf16 workload at full size and large batches of four- and
+eight-part rows.  Without the workspace such rows still run off path 4
+(and forcing path 4 is refused)."""
 
 from __future__ import annotations
 
@@ -60,14 +61,29 @@ def _in_place(zd, td, ws, **kw):
     return buf, lr
 
 
-# (B, C, dtype): register-only parts (bf16 and fp16 C up to 131072, fp32 up
-# to 65536) and parts with LDS slots beyond, the smallest and largest
-# two-part rows, one row, ragged batches
+# (B, C, dtype): two parts of register slots (bf16 and fp16 C up to 131072,
+# fp32 up to 65536) and of register and LDS slots beyond, four parts (bf16
+# and fp16 C up to 393216 with LDS slots past 262144, fp32 up to 131072),
+# eight parts (bf16 up to 524288, fp32 up to 262144); the smallest and
+# largest rows of each, one row, ragged batches
 SHAPES = [
     (1, 128256, "bf16"), (37, 128256, "bf16"), (6, 150000, "bf16"), (300, 81930, "bf16"),
     (5, 196608, "bf16"), (17, 100000, "f16"), (9, 50257, "f32"), (33, 70000, "f32"),
     (4, 98304, "f32"), (64, 40964, "f32"),
+    (3, 196616, "bf16"), (20, 262144, "bf16"), (7, 300000, "bf16"), (18, 256000, "f16"),
+    (2, 393216, "bf16"), (5, 393224, "bf16"), (16, 500000, "bf16"), (1, 524288, "bf16"),
+    (13, 128256, "f32"), (3, 98308, "f32"), (6, 200003, "f32"), (17, 262144, "f32"),
 ]
+
+
+def _parts(C, dtype):
+    """Parts per row of an aligned body (as path 4 cuts it)."""
+    nb = C // (4 if dtype == "f32" else 8)
+    if nb <= 10 * 1024:
+        return 1
+    if nb <= 24 * 1024:
+        return 2
+    return 4 if nb <= (32 if dtype == "f32" else 48) * 1024 else 8
 
 
 @pytest.mark.parametrize("B,C,dtype", SHAPES, ids=[f"{b}x{c}-{d}" for b, c, d in SHAPES])
@@ -75,10 +91,11 @@ def test_in_place_parts_match_oracle_and_defer_bitwise(B, C, dtype):
     import torch
     ce = _ce()
     assert ce.select_path(C, {"f32": 0, "bf16": 1, "f16": 2}[dtype]) == 4
+    assert _parts(C, dtype) > 1
     z, t = synth.make_inputs(B, C, dtype, 4.0, seed=B * 11 + C)
-    # targets on the row's first and last element and around its middle
-    # (where the parts meet)
-    for i, col in enumerate((0, C - 1, C // 2 - 1, C // 2, C // 2 + 1)):
+    # targets on the row's first and last element and around the middle and
+    # a quarter (where parts meet)
+    for i, col in enumerate((0, C - 1, C // 2 - 1, C // 2, C // 2 + 1, C // 4, C // 4 - 1)):
         if i < B:
             t[i] = col
     zd, td = to_device(z, t, dtype)
@@ -89,8 +106,8 @@ def test_in_place_parts_match_oracle_and_defer_bitwise(B, C, dtype):
     worst, _ = compare_block(grad_to_host(g, dtype), lr.cpu().numpy(), z, t, B, dtype,
                              where=f"in-place parts {B}x{C} {dtype}")
     print(f"[in-place parts] {B}x{C} {dtype}: {worst}", flush=True)
-    # (nearly) every first part defers: the second writes both halves, with the
-    # same bits
+    # (nearly) every part but one defers: a partner writes its gradient, with
+    # the same bits
     counter = torch.zeros(1, dtype=torch.int32, device=zd.device)
     ce.part_counter(counter)
     ce.part_polls(0)
@@ -101,19 +118,27 @@ def test_in_place_parts_match_oracle_and_defer_bitwise(B, C, dtype):
     assert _words_zero(ws)
     print(f"[in-place parts] {B}x{C} {dtype}: {int(counter.item())} of {B} rows deferred",
           flush=True)
-    # (with no polls a first part defers unless its partner published in the
-    # moment between the two compare-and-swaps: in batches of a few rows
-    # that can happen to every row)
+    # (with no polls a part defers unless its partners published before it
+    # looked: in batches of a few rows that can happen to every row)
     if B >= 16:
         assert int(counter.item()) >= 1
 
 
 def test_in_place_parts_ignore_index_and_scale():
     """A third of the rows ignored and a device gradient scale of 0.5, in
-    place on two-part rows: against the oracle, and bitwise with deferrals."""
+    place on rows of two and of eight parts: against the oracle, and
+    bitwise with deferrals."""
+    ce = _ce()
+    polls = ce.part_polls(0)
+    for C in (128256, 500000):
+        ce.part_polls(polls)
+        _ignore_and_scale(C)
+
+
+def _ignore_and_scale(C):
     import torch
     ce = _ce()
-    B, C, dtype = 48, 128256, "bf16"
+    B, dtype = 48, "bf16"
     z, t = synth.make_inputs(B, C, dtype, 4.0, seed=3)
     t[::3] = -100
     zd, td = to_device(z, t, dtype)
@@ -133,13 +158,14 @@ def test_in_place_parts_ignore_index_and_scale():
 
 
 def test_in_place_parts_workspace_reuse_and_smaller_batch():
-    """One workspace (zero-filled once) over calls of different B: each
-    call's result is its own (the same bits as on a fresh workspace) and the
-    words are zero after each."""
+    """One workspace (zero-filled once) over calls of different B and
+    parts per row: each call's result is its own (the same bits as on a
+    fresh workspace) and the words are zero after each."""
     import torch
     ws = _workspace(512)
-    for B, seed in ((512, 1), (7, 2), (512, 3), (100, 4)):
-        z, t = synth.make_inputs(B, 50257, "f32", 3.0, seed=seed)
+    for B, C, seed in ((512, 50257, 1), (7, 50257, 2), (512, 150000, 3), (100, 50257, 4),
+                       (64, 200003, 5), (300, 128256, 6)):
+        z, t = synth.make_inputs(B, C, "f32", 3.0, seed=seed)
         zd, td = to_device(z, t, "f32")
         g, lr = _in_place(zd, td, ws)
         g0, l0 = _in_place(zd, td, _workspace(B))
@@ -222,6 +248,33 @@ def test_in_place_parts_lmhead128k_full():
     rows = np.sort(np.random.Generator(np.random.PCG64(12)).choice(w.B, 64, replace=False))
     gh = grad_to_host(g[torch.from_numpy(rows).cuda()], "bf16")
     compare_block(gh, lr.cpu().numpy()[rows], z[rows], t[rows], w.B, "bf16", where="lmhead128k in place")
+    ce.part_polls(0)
+    g2, lr2 = _in_place(zd, td, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(g2), _bits(g)) and torch.equal(_bits(lr2), _bits(lr))
+    assert _words_zero(ws)
+
+
+@pytest.mark.parametrize("B,C,dtype", [(1024, 256000, "bf16"), (512, 500000, "bf16"),
+                                       (512, 262144, "f32")],
+                         ids=["1024x256000-bf16", "512x500000-bf16", "512x262144-f32"])
+def test_in_place_parts_large_batches(B, C, dtype):
+    """Large batches of four- and eight-part rows in place: 32 sampled rows
+    against the oracle, the whole gradient bitwise equal with (nearly)
+    every part but one deferring, and the words zero after both calls."""
+    import torch
+    ce = _ce()
+    assert _parts(C, dtype) in (4, 8)
+    z, t = synth.make_inputs(B, C, dtype, 4.0, seed=B + C)
+    zd, td = to_device(z, t, dtype)
+    ws = _workspace(B)
+    g, lr = _in_place(zd, td, ws)
+    torch.cuda.synchronize()
+    assert _words_zero(ws)
+    rows = np.sort(np.random.Generator(np.random.PCG64(C)).choice(B, 32, replace=False))
+    gh = grad_to_host(g[torch.from_numpy(rows).cuda()], dtype)
+    compare_block(gh, lr.cpu().numpy()[rows], z[rows], t[rows], B, dtype,
+                  where=f"in place {B}x{C} {dtype}")
     ce.part_polls(0)
     g2, lr2 = _in_place(zd, td, ws)
     torch.cuda.synchronize()

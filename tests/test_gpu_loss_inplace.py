@@ -54,18 +54,11 @@ def _legal(path, C, dtype):
     return path_takes(path, C, dtype)
 
 
-def _two_part(C, dtype):
+def _multi_part(C, dtype):
     """Rows that path 4 cuts into several parts (an aligned body of 10241
     to 65536 16-byte vectors)."""
     nb = C // (4 if dtype == "f32" else 8)
     return 10 * 1024 < nb <= 64 * 1024
-
-
-def _exactly_two_parts(C, dtype):
-    """Rows that path 4 cuts into exactly two parts (10241 to 24576
-    vectors): in place with the in-place workspace they stay on path 4."""
-    nb = C // (4 if dtype == "f32" else 8)
-    return 10 * 1024 < nb <= 24 * 1024
 
 
 def _check_losses(lr_gpu, z, t, dtype, where, B=None):
@@ -141,23 +134,19 @@ def test_in_place_matches_oracle(B, C, dtype, sigma, path):
     z, t = synth.make_inputs(B, C, dtype, sigma, seed=B * 5 + C)
     zd, td = to_device(z, t, dtype)
     buf = zd.clone()
-    if path == 4 and _two_part(C, dtype):
-        # without the in-place workspace (ce_fwd_grad), and with it for rows
-        # of four or eight parts, forcing path 4 in place is refused
+    if path == 4 and _multi_part(C, dtype):
+        # without the in-place workspace (ce_fwd_grad), forcing path 4 in
+        # place is refused
         with pytest.raises(ce.CEError):
             ce.fwd_grad_into(buf, td, buf, torch.empty(B, dtype=torch.float32, device=zd.device))
-        if not _exactly_two_parts(C, dtype):
-            with pytest.raises(ce.CEError):
-                ce.fwd_grad_inplace_(buf, td)
-            return
     lr = ce.fwd_grad_inplace_(buf, td)
     torch.cuda.synchronize()
     g = grad_to_host(buf, dtype)
     worst, l_ora = compare_block(g, lr.cpu().numpy(), z, t, B, dtype, where=f"in place {B}x{C} p{path}")
     print(f"[in-place] {B}x{C} {dtype} p{path}: {worst}", flush=True)
-    if path in (0, 4) and _exactly_two_parts(C, dtype):
-        # the in-place part kernel: the same bits when every first part
-        # defers its half to its partner
+    if path in (0, 4) and _multi_part(C, dtype):
+        # the in-place part kernel: the same bits when (nearly) every part
+        # but one defers its gradient to a partner
         prev = ce.part_polls(0)
         buf2 = zd.clone()
         lr2 = ce.fwd_grad_inplace_(buf2, td)
@@ -165,13 +154,8 @@ def test_in_place_matches_oracle(B, C, dtype, sigma, path):
         torch.cuda.synchronize()
         assert torch.equal(_bits(buf2), _bits(buf)) and torch.equal(_bits(lr2), _bits(lr))
         return
-    # the same kernel out of place: the same bits (rows of four or eight
-    # parts run in place on the resident or long path)
-    if path != 0 or not _two_part(C, dtype):
-        g0, l0 = ce.fwd_grad(zd, td)
-    else:
-        ce.force_path(2 if (C * (4 if dtype == "f32" else 2) + 15) // 16 + 1 <= 16384 else 3)
-        g0, l0 = ce.fwd_grad(zd, td)
+    # the same kernel out of place: the same bits
+    g0, l0 = ce.fwd_grad(zd, td)
     torch.cuda.synchronize()
     view = torch.int16 if dtype == "bf16" else torch.int32
     assert torch.equal(buf.view(view), g0.view(view))

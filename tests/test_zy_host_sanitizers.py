@@ -113,8 +113,8 @@ int main(void) {
   EQ(ce_fwd_inplace_workspace_bytes(0), 0u);
   EQ(ce_fwd_inplace_workspace_bytes(MINI), 0u);
   EQ(ce_fwd_inplace_workspace_bytes(MAXI), 0u);
-  EQ(ce_fwd_inplace_workspace_bytes(1), 272u);
-  EQ(ce_fwd_inplace_workspace_bytes(2147483647), (size_t)256 + (size_t)16 * 2147483647);
+  EQ(ce_fwd_inplace_workspace_bytes(1), 400u);
+  EQ(ce_fwd_inplace_workspace_bytes(2147483647), (size_t)256 + (size_t)144 * 2147483647);
   for (int64_t c = 1; c < ((int64_t)1 << 29); c = c * 3 + 1)
     for (int dt = 0; dt < 3; ++dt) (void)ce_select_path(c, dt);
   REFUSED(ce_select_path(0, CE_F32));
