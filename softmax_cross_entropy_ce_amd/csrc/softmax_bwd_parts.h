@@ -16,8 +16,11 @@
 //    body vectors in dx (four for eight parts); word q receives d_q as
 //    [kMailTag | bits(d_q)];
 //  - first thing, p sets its words to the empty tag; partners publish with
-//    compare-and-swap from the empty tag, repeat the publish on every poll
-//    of their own mailbox, and never wait for a publish's result;
+//    compare-and-swap from the empty tag, repeat the publish on every
+//    fourth poll of their own mailbox while partials are missing (eight
+//    parts also once more when the last one arrives, if a poll has skipped
+//    its publish since the one before), and never wait for a publish's
+//    result;
 //  - p polls a bounded number of times; a partial that has not arrived by
 //    then is recomputed from y and dy with the same slots, order and
 //    workgroup reduction as its part uses, so the bits do not depend on
@@ -140,6 +143,7 @@ void sm_bwd_part_kernel(const T* __restrict__ y, const T* __restrict__ dy, int64
     };
     publish();
     int have = 1;
+    bool behind = false;  // a pass has skipped its publish since the last one
     for (int it = 0; it < spin && have < P; ++it) {
 #pragma unroll kUnrollPartners
       for (int q = 0; q < P; ++q) {
@@ -151,10 +155,14 @@ void sm_bwd_part_kernel(const T* __restrict__ y, const T* __restrict__ dy, int64
           ++have;
         }
       }
-      if (have < P) {
+      const bool done = have == P;
+      if (done ? (P == 8 && behind) : (it & 3) == 3) {
         publish();
-        __builtin_amdgcn_s_sleep(8);
+        behind = false;
+      } else {
+        behind = !done;
       }
+      if (!done) __builtin_amdgcn_s_sleep(8);
     }
     if (fallbacks != nullptr && have < P) atomicAdd(fallbacks, (uint32_t)(P - have));
   }
