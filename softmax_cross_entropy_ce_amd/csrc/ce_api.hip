@@ -74,8 +74,9 @@ int64_t row_vectors(int64_t C, int es) { return (C * es + 15) / 16 + 1; }
 // register slots (eight such workgroups fit a CU); one part of 1024
 // threads and 4 register slots; one part of 8 register and 2 LDS slots;
 // two parts of 8 register slots; two parts of 8 register and 4 LDS slots;
-// four parts of 8 register slots; four parts of 8 register and 4 LDS slots;
-// eight parts of 8 register slots
+// four parts of 8 register slots; four parts of 8 register and 2 LDS
+// slots; four parts of 8 register and 4 LDS slots (16-bit types; float32
+// in place); eight parts of 8 register slots
 // (a 1024-thread slot is 1024 vectors, and a part of a P-part row is 1/P of
 // the body rounded up to 8 vectors).
 constexpr int64_t kPartsOneQuarter = 8 * 256;
@@ -84,12 +85,17 @@ constexpr int64_t kPartsOne = 10 * 1024;
 constexpr int64_t kPartsTwoRegs = 2 * 8 * 1024;
 constexpr int64_t kPartsTwo = 2 * 12 * 1024;
 constexpr int64_t kPartsFourRegs = 4 * 8 * 1024;
+constexpr int64_t kPartsFourLds2 = 4 * 10 * 1024;
 constexpr int64_t kPartsFour = 4 * 12 * 1024;
 constexpr int64_t kPartsEightRegs = 8 * 8 * 1024;
 // The largest body path 4 takes: eight register-only parts.  (Four parts
-// with LDS slots serve 16-bit rows up to kPartsFour; for float32, whose
-// register slots keep the terms of the sum, that configuration would exceed
-// 64 VGPRs, so fp32 rows go from four register-only parts to eight.)
+// with 2 LDS slots serve rows up to kPartsFourLds2, whose parts they fill
+// better than eight parts of 8 slots: fp32 rows of 151936 columns, 0.69 ->
+// 0.72 of 8 TB/s out of place and 0.64 -> 0.71 in place; four parts with 4
+// LDS slots serve 16-bit rows up to kPartsFour, and fp32 rows only in
+// place: out of place, 2048 x 180000 fp32 measured 0.706 that way against
+// 0.716 in eight parts, in place 0.70 against 0.66.  fp32 parts with LDS
+// slots do not keep their terms, which would exceed 64 VGPRs.)
 int64_t parts_max(int) { return kPartsEightRegs; }
 
 int64_t body_vectors_max(int64_t C, int es) { return C / (16 / es); }
@@ -549,10 +555,10 @@ int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs
         return launch_parts_cfg<T, 2, 1024, 8, 4, 0, OP, true>(z, t, B, C, rs, g, l, st, in_place);
       if (nb <= kPartsFourRegs)
         return launch_parts_cfg<T, 4, 1024, 8, 0, 0, OP, true>(z, t, B, C, rs, g, l, st, in_place);
-      if constexpr (sizeof(T) == 2) {
-        if (nb <= kPartsFour)
-          return launch_parts_cfg<T, 4, 1024, 8, 4, 0, OP, true>(z, t, B, C, rs, g, l, st, in_place);
-      }
+      if (nb <= kPartsFourLds2)
+        return launch_parts_cfg<T, 4, 1024, 8, 2, 0, OP, true>(z, t, B, C, rs, g, l, st, in_place);
+      if (nb <= kPartsFour)
+        return launch_parts_cfg<T, 4, 1024, 8, 4, 0, OP, true>(z, t, B, C, rs, g, l, st, in_place);
       if (nb <= kPartsEightRegs)
         return launch_parts_cfg<T, 8, 1024, 8, 0, 0, OP, true>(z, t, B, C, rs, g, l, st, in_place);
     }
@@ -564,6 +570,7 @@ int launch_parts(const T* z, const int32_t* t, int64_t B, int64_t C, ce::RowArgs
   if (nb <= kPartsTwoRegs) return launch_parts_cfg<T, 2, 1024, 8, 0, 0, OP>(z, t, B, C, rs, g, l, st);
   if (nb <= kPartsTwo) return launch_parts_cfg<T, 2, 1024, 8, 4, 0, OP>(z, t, B, C, rs, g, l, st);
   if (nb <= kPartsFourRegs) return launch_parts_cfg<T, 4, 1024, 8, 0, 0, OP>(z, t, B, C, rs, g, l, st);
+  if (nb <= kPartsFourLds2) return launch_parts_cfg<T, 4, 1024, 8, 2, 0, OP>(z, t, B, C, rs, g, l, st);
   if constexpr (sizeof(T) == 2) {
     if (nb <= kPartsFour) return launch_parts_cfg<T, 4, 1024, 8, 4, 0, OP>(z, t, B, C, rs, g, l, st);
   }

@@ -488,7 +488,7 @@ void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_
   };
 
   // Phase B: this part's pair.
-  constexpr bool kKeepTerms = sizeof(T) == 4 && P <= 4 && !IP;
+  constexpr bool kKeepTerms = sizeof(T) == 4 && !IP && (P <= 2 || (P == 4 && NL + NXW == 0));
   // Each phase tests the slots against its own opaque copy of the part's
   // length: conditions shared between phases would stay live in scalar
   // registers from pass 1 to the gradient, and the compiler spills them.

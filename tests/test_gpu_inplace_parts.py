@@ -63,9 +63,10 @@ def _in_place(zd, td, ws, **kw):
 
 # (B, C, dtype): two parts of register slots (bf16 and fp16 C up to 131072,
 # fp32 up to 65536) and of register and LDS slots beyond, four parts (bf16
-# and fp16 C up to 393216 with LDS slots past 262144, fp32 up to 131072),
-# eight parts (bf16 up to 524288, fp32 up to 262144); the smallest and
-# largest rows of each, one row, ragged batches
+# and fp16 C up to 393216, fp32 up to 196608, with 2 LDS slots past 262144
+# and 131072 and 4 past 327680 and 163840), eight parts (bf16 up to 524288,
+# fp32 up to 262144); the smallest and largest rows of each, one row,
+# ragged batches
 SHAPES = [
     (1, 128256, "bf16"), (37, 128256, "bf16"), (6, 150000, "bf16"), (300, 81930, "bf16"),
     (5, 196608, "bf16"), (17, 100000, "f16"), (9, 50257, "f32"), (33, 70000, "f32"),
@@ -73,17 +74,18 @@ SHAPES = [
     (3, 196616, "bf16"), (20, 262144, "bf16"), (7, 300000, "bf16"), (18, 256000, "f16"),
     (2, 393216, "bf16"), (5, 393224, "bf16"), (16, 500000, "bf16"), (1, 524288, "bf16"),
     (13, 128256, "f32"), (3, 98308, "f32"), (6, 200003, "f32"), (17, 262144, "f32"),
+    (9, 151936, "f32"), (5, 163844, "f32"), (4, 196608, "f32"), (3, 196612, "f32"),
 ]
 
 
 def _parts(C, dtype):
-    """Parts per row of an aligned body (as path 4 cuts it)."""
+    """Parts per row of an aligned body (as path 4 cuts it in place)."""
     nb = C // (4 if dtype == "f32" else 8)
     if nb <= 10 * 1024:
         return 1
     if nb <= 24 * 1024:
         return 2
-    return 4 if nb <= (32 if dtype == "f32" else 48) * 1024 else 8
+    return 4 if nb <= 48 * 1024 else 8
 
 
 @pytest.mark.parametrize("B,C,dtype", SHAPES, ids=[f"{b}x{c}-{d}" for b, c, d in SHAPES])
@@ -256,8 +258,9 @@ def test_in_place_parts_lmhead128k_full():
 
 
 @pytest.mark.parametrize("B,C,dtype", [(1024, 256000, "bf16"), (512, 500000, "bf16"),
-                                       (512, 262144, "f32")],
-                         ids=["1024x256000-bf16", "512x500000-bf16", "512x262144-f32"])
+                                       (512, 262144, "f32"), (1024, 151936, "f32")],
+                         ids=["1024x256000-bf16", "512x500000-bf16", "512x262144-f32",
+                              "1024x151936-f32"])
 def test_in_place_parts_large_batches(B, C, dtype):
     """Large batches of four- and eight-part rows in place: 32 sampled rows
     against the oracle, the whole gradient bitwise equal with (nearly)

@@ -23,7 +23,9 @@ pytestmark = pytest.mark.gpu
 
 # (B, C, dtype, sigma): two parts per row (aligned, 2-byte aligned, 4-byte
 # aligned fp32, every slot filled), four parts per row (registers only,
-# fp32 at its largest, 2-byte aligned with LDS slots, every slot filled),
+# fp32 register slots at their largest, 2-byte aligned with LDS slots, every
+# slot filled; 2 LDS slots: fp32 just past the register slots, a
+# 151936-wide fp32 row, both types at their largest, bf16 just past them),
 # eight parts per row (fp32 just past four parts, a 256000-wide fp32 row,
 # both types at their largest, 2-byte aligned bf16) and one one-part shape
 # as a control.
@@ -37,6 +39,12 @@ SHAPES = [
     (5, 300001, "bf16", 4.0),
     (3, 393216, "bf16", 4.0),
     (7, 131077, "f32", 3.0),
+    (13, 151936, "f32", 3.0),
+    (4, 163840, "f32", 3.0),
+    (6, 262152, "bf16", 4.0),
+    (3, 327680, "bf16", 4.0),
+    (5, 327688, "bf16", 4.0),
+    (5, 163844, "f32", 3.0),
     (9, 256000, "f32", 3.0),
     (3, 262144, "f32", 3.0),
     (3, 524288, "bf16", 4.0),
@@ -67,13 +75,13 @@ def _reset_hooks():
 
 def _parts(C, dtype):
     """Parts per row: one up to an aligned body of 10240 vectors, two up to
-    24576, four up to 49152 (16-bit) or 32768 (fp32), then eight."""
+    24576, four up to 49152 (16-bit) or 40960 (fp32), then eight."""
     nb = C // (4 if dtype == "f32" else 8)
     if nb <= 10 * 1024:
         return 1
     if nb <= 24 * 1024:
         return 2
-    return 4 if nb <= (32 if dtype == "f32" else 48) * 1024 else 8
+    return 4 if nb <= (40 if dtype == "f32" else 48) * 1024 else 8
 
 
 def _bits(x):
