@@ -45,6 +45,9 @@ FWD_SHAPES = [
     (9, 128256, "bf16", 4.0, None),
     (5, 70001, "bf16", 4.0, None),
     (3, 200_000, "bf16", 4.0, None),
+    (6, 151936, "f32", 3.0, None),
+    (3, 300_000, "bf16", 4.0, None),
+    (4, 180_000, "f32", 3.0, None),
 ]
 FWD_IDS = [f"{b}x{c}-{d}{'-spike' if s else ''}" for b, c, d, _, s in FWD_SHAPES]
 
