@@ -4,9 +4,9 @@ in-place workspace): every row against the oracle; bitwise the same
 whether each part writes its own gradient or defers it to a partner (no
 polls makes nearly every part but one defer, and the device counter sees
 the deferrals); the workspace's row words zero again after every call;
-with ignore_index and a gradient scale; captured in a HIP graph; the
-8192 x 128256 bf16 workload at full size and large batches of four- and
-eight-part rows.  Without the workspace such rows still run off path 4
+with ignore_index and a gradient scale; captured in a HIP graph; on two
+streams at once; the 8192 x 128256 bf16 workload at full size and large
+batches of four- and eight-part rows.  Without the workspace such rows still run off path 4
 (and forcing path 4 is refused)."""
 
 from __future__ import annotations
@@ -283,3 +283,32 @@ def test_in_place_parts_large_batches(B, C, dtype):
     torch.cuda.synchronize()
     assert torch.equal(_bits(g2), _bits(g)) and torch.equal(_bits(lr2), _bits(lr))
     assert _words_zero(ws)
+
+
+def test_in_place_parts_two_streams_at_once():
+    """In place on two streams at once, each call with the binding's
+    workspace for its own stream (rows of two, four and eight parts),
+    three calls a stream queued together: every result has the bits of the
+    call made alone."""
+    import torch
+    ce = _ce()
+    for B, C, dtype in ((48, 128256, "bf16"), (24, 300000, "bf16"), (12, 200003, "f32")):
+        z, t = synth.make_inputs(B, C, dtype, 4.0, seed=C)
+        zd, td = to_device(z, t, dtype)
+        g0, l0 = _in_place(zd, td, _workspace(B))
+        torch.cuda.synchronize()
+        outs = []
+        streams = (torch.cuda.Stream(), torch.cuda.Stream())
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream())
+        for s in streams:
+            with torch.cuda.stream(s):
+                buf = torch.empty_like(zd)
+                lr = torch.empty(B, dtype=torch.float32, device=zd.device)
+                for _ in range(3):
+                    buf.copy_(zd)
+                    ce.fwd_grad_ex_into(buf, td, buf, lr)
+                outs.append((buf, lr))
+        torch.cuda.synchronize()
+        for buf, lr in outs:
+            assert torch.equal(_bits(buf), _bits(g0)) and torch.equal(_bits(lr), _bits(l0)), (B, C)
