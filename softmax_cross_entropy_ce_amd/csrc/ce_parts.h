@@ -51,7 +51,7 @@
 // Workgroup g runs on XCD g % 8 (round-robin dispatch); the parts of a row
 // are given workgroups g, g + 8, ..., so they share an XCD and start next to
 // each other in its dispatch order, and each XCD takes a contiguous block of
-// rows (part_of_block_rows).  Rows are cut into one, two, four or
+// rows (part_of_block_rows; rows of one part are dealt to the XCDs in turn).  Rows are cut into one, two, four or
 // eight parts.
 #pragma once
 
@@ -94,12 +94,14 @@ __device__ __forceinline__ void part_of_block(uint32_t g, int64_t& row, int& par
 }
 
 // The same for B rows with each XCD a contiguous block of ceil(B / 8) rows,
-// taken in order: the cross-entropy row parts.  (Rows dealt in turn measured
-// slower there, fraction of 8 TB/s: 4096 x 50257 fp32 0.745 against 0.761,
-// bf16 4096 x 151936 0.707 against 0.739, 16384 x 65536 0.691 against
-// 0.738; 8192 x 128256 bf16 the same, 0.761.  The softmax backward's parts,
-// which read two arrays, measured 0.767 dealt in turn against 0.755 in
-// blocks on 8192 x 128256 bf16, and keep part_of_block.)
+// taken in order: the cross-entropy rows of two or more parts.  (Rows dealt
+// in turn measured slower there, fraction of 8 TB/s: 4096 x 50257 fp32
+// 0.745 against 0.761, bf16 4096 x 151936 0.707 against 0.739, 16384 x
+// 65536 0.691 against 0.738; 8192 x 128256 bf16 the same, 0.761.  Rows of
+// one part measured the other way, e.g. bf16 65536 x 8192 0.787 dealt in
+// turn against 0.717 in blocks and fp32 89472 x 3000 0.768 against 0.716,
+// and so did the softmax backward's parts, 0.767 against 0.755 on 8192 x
+// 128256 bf16: both keep part_of_block.)
 template <int P>
 __device__ __forceinline__ void part_of_block_rows(uint32_t g, int64_t B, int64_t& row,
                                                    int& part) {
@@ -330,7 +332,10 @@ void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_
   const uint32_t voff = (uint32_t)tid * 16u;
   int64_t row;
   int part;
-  part_of_block_rows<P>(blockIdx.x, B, row, part);
+  if constexpr (P == 1)
+    part_of_block<P>(blockIdx.x, row, part);
+  else
+    part_of_block_rows<P>(blockIdx.x, B, row, part);
   if (row >= B) return;  // whole workgroup (and every part of the row)
 
   const T* rp = logits + row * rs.ldz;
