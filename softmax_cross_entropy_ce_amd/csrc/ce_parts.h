@@ -51,8 +51,9 @@
 // Workgroup g runs on XCD g % 8 (round-robin dispatch); the parts of a row
 // are given workgroups g, g + 8, ..., so they share an XCD and start next to
 // each other in its dispatch order, and each XCD takes a contiguous block of
-// rows (part_of_block_rows; rows of one part are dealt to the XCDs in turn).  Rows are cut into one, two, four or
-// eight parts.
+// rows (part_of_block_rows; rows of one part, and rows of eight parts in
+// place, are dealt to the XCDs in turn).  Rows are cut into one, two, four
+// or eight parts.
 #pragma once
 
 #include <type_traits>
@@ -100,8 +101,10 @@ __device__ __forceinline__ void part_of_block(uint32_t g, int64_t& row, int& par
 // 65536 0.691 against 0.738; 8192 x 128256 bf16 the same, 0.761.  Rows of
 // one part measured the other way, e.g. bf16 65536 x 8192 0.787 dealt in
 // turn against 0.717 in blocks and fp32 89472 x 3000 0.768 against 0.716,
-// and so did the softmax backward's parts, 0.767 against 0.755 on 8192 x
-// 128256 bf16: both keep part_of_block.)
+// and so did rows of eight parts in place (bf16 2048 x 500000 0.695 against
+// 0.658, fp32 2048 x 200000 0.681 against 0.632) and the softmax backward's
+// parts (0.767 against 0.755 on 8192 x 128256 bf16): these keep
+// part_of_block.)
 template <int P>
 __device__ __forceinline__ void part_of_block_rows(uint32_t g, int64_t B, int64_t& row,
                                                    int& part) {
@@ -332,7 +335,7 @@ void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_
   const uint32_t voff = (uint32_t)tid * 16u;
   int64_t row;
   int part;
-  if constexpr (P == 1)
+  if constexpr (P == 1 || (IP && P == 8))
     part_of_block<P>(blockIdx.x, row, part);
   else
     part_of_block_rows<P>(blockIdx.x, B, row, part);
