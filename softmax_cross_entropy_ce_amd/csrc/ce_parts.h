@@ -232,6 +232,9 @@ __device__ __forceinline__ void wg_pair(float c, float s, float* red_c, float* r
 //    on their way: it polls for them again and writes its own part.
 //  - every part counts its departure once its last access to the words has
 //    completed; the last to leave sets the pair and flag words back to 0.
+// Wave 0 runs this with lane q looking after part q's pair word and flag,
+// so that a pass over the pairs or the flags is one access per lane (lane 0
+// publishes and counts).
 // No wait depends on a workgroup that has not started, and no part reads
 // logits that may have been overwritten.  Every gradient element is
 // 2^(z log2e - c') with the row's c', whichever part writes it, so the
@@ -692,35 +695,41 @@ void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_
         ip_extra = mode == 2 ? 1u << q : 0u;
         mail_ok[0] = mail_ok[1] = 1;
         fin_ok = 1;
-      } else if (IP && tid == 0) {
-        mail_c[part] = c_own;
-        mail_s[part] = s_own;
+      } else if (IP && P > 2) {
+        // Four or eight parts, on wave 0: lane q < P polls part q's pair
+        // word and claims part q's flag, so that each pass over the words is
+        // one access per lane; lane 0 publishes and counts.
         uint64_t* const words = in_place + row * kInPlaceRowWords;
         uint64_t* const flags = words + kInPlaceFlags;
         uint32_t* const arrived = reinterpret_cast<uint32_t*>(words + kInPlaceCounts);
         uint32_t* const departed = reinterpret_cast<uint32_t*>(words + kInPlaceCounts + 1);
-        constexpr unsigned kAll = (1u << P) - 1u;
-        // publish, and wait until the word is written
-        const uint64_t prev = __hip_atomic_exchange(&words[part], in_place_word(c_own, s_own),
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("" ::"v"(prev) : "memory");
-        const uint32_t before =
-            __builtin_amdgcn_atomic_inc32(arrived, (uint32_t)(P - 1), __ATOMIC_RELAXED, "agent");
-        unsigned got = 1u << part;
+        const bool watch = lane < P && lane != part;  // this lane waits for part `lane`'s pair
+        uint32_t before = 0;
+        if (lane == 0) {
+          mail_c[part] = c_own;
+          mail_s[part] = s_own;
+          // publish, and wait until the word is written, then count the
+          // arrival
+          const uint64_t prev = __hip_atomic_exchange(&words[part], in_place_word(c_own, s_own),
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          asm volatile("" ::"v"(prev) : "memory");
+          before = __builtin_amdgcn_atomic_inc32(arrived, (uint32_t)(P - 1), __ATOMIC_RELAXED,
+                                                 "agent");
+        }
+        before = __builtin_amdgcn_readfirstlane(before);
+        bool have = !watch;
         // up to `polls` passes over the pair words (0: none)
         auto gather = [&](int polls) {
           for (int it = 0; it < polls; ++it) {
-#pragma unroll 1
-            for (int q = 0; q < P; ++q) {
-              if ((got >> q) & 1u) continue;
+            if (!have) {
               const uint64_t x =
-                  __hip_atomic_load(&words[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  __hip_atomic_load(&words[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               if (x != 0) {
-                in_place_pair(x, mail_c[q], mail_s[q]);
-                got |= 1u << q;
+                in_place_pair(x, mail_c[lane], mail_s[lane]);
+                have = true;
               }
             }
-            if (got == kAll) break;
+            if (__builtin_amdgcn_ballot_w64(!have) == 0) break;
             __builtin_amdgcn_s_sleep(8);
           }
         };
@@ -729,50 +738,53 @@ void ce_part_kernel(const T* logits, const int32_t* __restrict__ targets, int64_
         if (before == (uint32_t)(P - 1)) {
           // the closer: every other part has published
           gather(kInPlaceLongPolls);
-#pragma unroll 1
-          for (int q = 0; q < P; ++q) {
-            if (q == part) continue;
+          bool ext = false;
+          if (watch) {
             uint64_t e = 0;
-            if (!__hip_atomic_compare_exchange_strong(&flags[q], &e, kInPlaceChecked,
-                                                      __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT))
-              extra |= 1u << q;  // e == kInPlaceDeferred
+            ext = !__hip_atomic_compare_exchange_strong(&flags[lane], &e, kInPlaceChecked,
+                                                        __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
           }
+          extra = (unsigned)__builtin_amdgcn_ballot_w64(ext);  // e == kInPlaceDeferred
         } else {
           gather(spin);
-          if (got != kAll) {
-            uint64_t e = 0;
-            if (__hip_atomic_compare_exchange_strong(&flags[part], &e, kInPlaceDeferred,
-                                                     __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT))
-              deferred = 1;
-            else
-              gather(kInPlaceLongPolls);  // e == kInPlaceChecked: the closer has published
+          if (__builtin_amdgcn_ballot_w64(!have) != 0) {
+            int d = 0;
+            if (lane == 0) {
+              uint64_t e = 0;
+              d = __hip_atomic_compare_exchange_strong(&flags[part], &e, kInPlaceDeferred,
+                                                       __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT)
+                      ? 1
+                      : 0;
+            }
+            deferred = __builtin_amdgcn_readfirstlane(d);
+            if (!deferred) gather(kInPlaceLongPolls);  // e == kInPlaceChecked: the closer has published
           }
         }
-        if (!deferred && got != kAll) {
+        if (!deferred && !have) {
+          mail_c[lane] = __builtin_nanf("");  // a pair that never came: the row is NaN
+          mail_s[lane] = __builtin_nanf("");
+        }
+        if (lane == 0) {
+          // every access to the words above (the wave's polls and
+          // compare-and-swaps) has completed before the departure counts
+          wait_vmcnt<0>();
+          if (__builtin_amdgcn_atomic_inc32(departed, (uint32_t)(P - 1), __ATOMIC_RELAXED, "agent") ==
+              (uint32_t)(P - 1)) {
 #pragma unroll 1
-          for (int q = 0; q < P; ++q) {
-            if ((got >> q) & 1u) continue;
-            mail_c[q] = __builtin_nanf("");  // a pair that never came: the row is NaN
-            mail_s[q] = __builtin_nanf("");
+            for (int q = 0; q < P; ++q) {
+              __hip_atomic_store(&words[q], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(&flags[q], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
-        }
-        wait_vmcnt<0>();  // every compare-and-swap above has taken effect
-        if (__builtin_amdgcn_atomic_inc32(departed, (uint32_t)(P - 1), __ATOMIC_RELAXED, "agent") ==
-            (uint32_t)(P - 1)) {
-#pragma unroll 1
-          for (int q = 0; q < P; ++q) {
-            __hip_atomic_store(&words[q], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&flags[q], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-        if (deferred && fallbacks != nullptr) atomicAdd(fallbacks, 1u);
-        ip_deferred = deferred;
-        ip_extra = extra;
+          if (deferred && fallbacks != nullptr) atomicAdd(fallbacks, 1u);
+          ip_deferred = deferred;
+          ip_extra = extra;
 #pragma unroll
-        for (int q = 0; q < P; ++q) mail_ok[q] = 1;
-        fin_ok = 1;
+          for (int q = 0; q < P; ++q) mail_ok[q] = 1;
+          fin_ok = 1;
+        }
       } else if (tid == 0) {
         mail_c[part] = c_own;
         mail_s[part] = s_own;
