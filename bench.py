@@ -159,7 +159,8 @@ def timed_step_indices(steps: int) -> list:
 
 def time_steps(zd, td, grad, loss_rows, loss, ws, steps: int, warmup: int) -> dict:
     """W untimed steps, then K steps timed by the wall clock between two
-    device synchronisations.  The ce_fwd_grad launches of the steps
+    device synchronisations; a step is one ce_fwd_grad_loss call (the
+    gradient and per-row losses, then their sum).  The ce_fwd_grad launches of the steps
     timed_step_indices(K) record a pair of HIP events at their kernel's own
     start and end (ce_debug_time_next_launch) on the stream they run on;
     those give the kernel's duration."""
@@ -169,16 +170,14 @@ def time_steps(zd, td, grad, loss_rows, loss, ws, steps: int, warmup: int) -> di
     timed = timed_step_indices(steps)
     pairs = dict(zip(timed, hev.pairs(len(timed))))
     for _ in range(warmup):
-        ce.fwd_grad_into(zd, td, grad, loss_rows)
-        ce.reduce_loss_into(loss_rows, loss, ws)
+        ce.fwd_grad_loss_into(zd, td, grad, loss_rows, loss, ws)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         pr = pairs.get(i)
         if pr is not None:
             hev.arm(pr)
-        ce.fwd_grad_into(zd, td, grad, loss_rows)
-        ce.reduce_loss_into(loss_rows, loss, ws)
+        ce.fwd_grad_loss_into(zd, td, grad, loss_rows, loss, ws)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     fwd_ms = [hev.ms(pairs[i]) for i in timed]

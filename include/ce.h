@@ -260,6 +260,29 @@ size_t ce_reduce_workspace_bytes(int64_t B);
 int ce_reduce_loss(const float* loss_rows, int64_t B, float* loss_scalar_out,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ce_fwd_grad_loss - the whole training step of the loss in one call:
+ * ce_fwd_grad, then ce_reduce_loss of its per-row losses, on the same
+ * stream (two kernel launches, one host call).
+ *
+ * Defined by: rumus 0.1.1 cross_entropy.wgsl, pass 1 (per-row loss and
+ * gradient) and pass 2 (the per-row losses summed into one scalar).
+ *
+ *   logits, targets, B, C, dtype, grad_out, stream  as ce_fwd_grad.
+ *   loss_rows_out    [B] float32, the per-row losses (loss_out of
+ *                    ce_fwd_grad), kept for the caller.
+ *   loss_scalar_out  [1] float32, the batch-mean loss (as ce_reduce_loss).
+ *   workspace        device scratch of ce_reduce_workspace_bytes(B) bytes
+ *                    (NULL when that is 0).
+ *
+ * Every argument, the reduction's included, is checked before anything is
+ * launched, so an error leaves all outputs untouched.  The results are
+ * bitwise those of the two calls made one after the other.
+ */
+int ce_fwd_grad_loss(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
+                     void* grad_out, float* loss_rows_out, float* loss_scalar_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Largest B that ce_reduce_loss_noalloc accepts. */
 #define CE_NOALLOC_MAX_ROWS ((int64_t)2147483647)
 

@@ -37,7 +37,7 @@ __all__ = [
     "reduce_workspace_bytes", "select_path", "force_path", "part_polls", "part_counter",
     "stream_copy", "version", "PATH_NAMES", "F32", "BF16", "F16", "NO_IGNORE",
     "fwd_grad_ex_into", "fwd_grad_ex", "fwd_workspace_bytes", "fwd_inplace_workspace_bytes",
-    "inplace_workspace",
+    "inplace_workspace", "fwd_grad_loss_into",
 ]
 
 F32 = 0
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.ce_reduce_loss.restype = i32
     L.ce_reduce_loss_noalloc.argtypes = [vp, i64, vp, vp]
     L.ce_reduce_loss_noalloc.restype = i32
+    L.ce_fwd_grad_loss.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp, vp, sz, vp]
+    L.ce_fwd_grad_loss.restype = i32
     L.ce_status_string.argtypes = [i32]
     L.ce_status_string.restype = ctypes.c_char_p
     L.ce_version.argtypes = []
@@ -292,6 +294,27 @@ def fwd_grad_into(logits, targets, grad, loss_rows) -> None:
     st = lib().ce_fwd_grad(logits.data_ptr(), targets.data_ptr(), B, C, _dtype_code(logits),
                            grad.data_ptr(), loss_rows.data_ptr(), _stream_ptr(logits.device))
     _check(st, "ce_fwd_grad")
+
+
+def fwd_grad_loss_into(logits, targets, grad, loss_rows, loss, workspace=None) -> None:
+    """The gradient, the per-row losses and the batch-mean loss (one float32
+    tensor ``loss``) in one library call (ce_fwd_grad_loss: ce_fwd_grad,
+    then ce_reduce_loss).  ``workspace``: device bytes of at least
+    reduce_workspace_bytes(B), or None to allocate them when needed."""
+    torch = _torch()
+    B, C = _check_fwd_args(logits, targets, grad, loss_rows)
+    _check_cuda(logits, loss)
+    if loss.dtype != torch.float32 or loss.numel() != 1:
+        raise TypeError("loss must be one float32")
+    need = reduce_workspace_bytes(B)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().ce_fwd_grad_loss(logits.data_ptr(), targets.data_ptr(), B, C, _dtype_code(logits),
+                                grad.data_ptr(), loss_rows.data_ptr(), loss.data_ptr(), wptr,
+                                wbytes, _stream_ptr(logits.device))
+    _check(st, "ce_fwd_grad_loss")
 
 
 def fwd_grad_inplace_(logits, targets):

@@ -1325,6 +1325,23 @@ int ce_reduce_loss(const float* loss_rows, int64_t B, float* loss_scalar_out, vo
   return launch_reduce(loss_rows, B, loss_scalar_out, (float*)workspace, as_stream(stream));
 }
 
+int ce_fwd_grad_loss(const void* logits, const int32_t* targets, int64_t B, int64_t C, int dtype,
+                     void* grad_out, float* loss_rows_out, float* loss_scalar_out,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  // the reduction's arguments first: ce_fwd_grad launches once its own
+  // arguments pass, and nothing may be launched when the call fails
+  if (!loss_scalar_out) return CE_ERR_NULL;
+  if ((uintptr_t)loss_scalar_out % 4) return CE_ERR_ALIGN;
+  if (B > 0 && B <= kReduceMaxRows) {
+    const size_t need = ce_reduce_workspace_bytes(B);
+    if (need && (!workspace || workspace_bytes < need)) return CE_ERR_WORKSPACE;
+    if (need && (uintptr_t)workspace % 4) return CE_ERR_ALIGN;
+  }
+  const int st = ce_fwd_grad(logits, targets, B, C, dtype, grad_out, loss_rows_out, stream);
+  if (st != CE_OK) return st;
+  return ce_reduce_loss(loss_rows_out, B, loss_scalar_out, workspace, workspace_bytes, stream);
+}
+
 int ce_reduce_loss_noalloc(const float* loss_rows, int64_t B, float* loss_scalar_out,
                            void* stream) {
   if (!loss_rows || !loss_scalar_out) return CE_ERR_NULL;

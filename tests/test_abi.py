@@ -42,7 +42,7 @@ def test_library_exports_every_declared_function():
                             "ce_softmax_fwd", "ce_softmax_bwd", "ce_shard_stats",
                             "ce_shard_grad", "ce_fwd_grad_ex", "ce_fwd_workspace_bytes",
                             "ce_reduce_loss_noalloc", "ce_debug_time_next_launch",
-                            "ce_fwd_inplace_workspace_bytes"])
+                            "ce_fwd_inplace_workspace_bytes", "ce_fwd_grad_loss"])
     for n in names:
         assert hasattr(L_, n), n
 
@@ -428,3 +428,20 @@ def test_header_builds_a_plain_client(tmp_path, compiler, std):
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, (run.returncode, run.stderr[-2000:])
     assert "gfx950" in run.stdout
+
+
+def test_fwd_grad_loss_refuses_before_launch():
+    """The whole-step call checks the reduction's arguments before it
+    launches anything (fake device addresses: every call here is refused)."""
+    f = ce.lib().ce_fwd_grad_loss
+    S = L + 65536
+    assert f(Z, T, 8, 10, 0, G, L, None, None, 0, None) == NULL           # no loss scalar
+    assert f(Z, T, 8, 10, 0, G, L, S + 2, None, 0, None) == ALIGN         # misaligned scalar
+    assert f(Z, T, 1 << 20, 10, 0, G, L, S, None, 0, None) == WORKSPACE   # reduction needs scratch
+    need = ce.reduce_workspace_bytes(1 << 20)
+    assert f(Z, T, 1 << 20, 10, 0, G, L, S, WS, need - 4, None) == WORKSPACE
+    assert f(Z, T, 1 << 20, 10, 0, G, L, S, WS + 2, need, None) == ALIGN
+    # then the forward's own checks
+    assert f(Z, T, 0, 10, 0, G, L, S, None, 0, None) == SHAPE
+    assert f(Z, T, 8, 10, 5, G, L, S, None, 0, None) == DTYPE
+    assert f(Z, T, 8, 10, 0, None, L, S, None, 0, None) == NULL

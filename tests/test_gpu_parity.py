@@ -180,3 +180,39 @@ def test_parity_lmhead128k_workload():
     worst["loss_rel"] = compare_scalar(float(loss.item()), reduce_loss(ora), "bf16", "lmhead128k")
     worst["rows_compared"] = B
     _log("lmhead128k all rows", worst)
+
+
+@pytest.mark.parametrize("B,C,dtype", [(8, 10, "f32"), (1024, 1000, "f32"), (37, 3000, "bf16"),
+                                       (64, 128256, "bf16"), (20000, 10, "f32"), (9, 50257, "f16")],
+                         ids=["8x10-f32", "1024x1000-f32", "37x3000-bf16", "64x128256-bf16",
+                              "20000x10-f32", "9x50257-f16"])
+def test_fwd_grad_loss_one_call(B, C, dtype):
+    """ce_fwd_grad_loss (the whole step in one call): the gradient, the
+    per-row losses and the batch loss bitwise those of ce_fwd_grad followed
+    by ce_reduce_loss, and the batch loss against the oracle's sum; past
+    16384 rows the reduction's workspace is required."""
+    import torch
+    import softmax_cross_entropy_ce_amd as ce
+    z, t = synth.make_inputs(B, C, dtype, 3.0, seed=B + C)
+    zd, td = to_device(z, t, dtype)
+    g0, l0 = ce.fwd_grad(zd, td)
+    s0 = torch.empty((), dtype=torch.float32, device=zd.device)
+    ce.reduce_loss_into(l0, s0)
+    g1 = torch.empty_like(zd)
+    l1 = torch.empty(B, dtype=torch.float32, device=zd.device)
+    s1 = torch.full((), float("nan"), dtype=torch.float32, device=zd.device)
+    ce.fwd_grad_loss_into(zd, td, g1, l1, s1)
+    torch.cuda.synchronize()
+    view = torch.int32 if dtype == "f32" else torch.int16
+    assert torch.equal(g1.view(view), g0.view(view))
+    assert torch.equal(l1.view(torch.int32), l0.view(torch.int32))
+    assert torch.equal(s1.view(torch.int32), s0.view(torch.int32))
+    l_ora, _ = ce_rows(widen_rows(z, dtype), t, B)
+    want = reduce_loss(l_ora)
+    assert abs(float(s1.item()) - want) <= 1e-5 * abs(want) + 1e-6
+    if ce.reduce_workspace_bytes(B) > 0:
+        lib = ce.lib()
+        st = lib.ce_fwd_grad_loss(zd.data_ptr(), td.data_ptr(), B, C, ce._dtype_code(zd),
+                                  g1.data_ptr(), l1.data_ptr(), s1.data_ptr(), None, 0,
+                                  ce._stream_ptr(zd.device))
+        assert st == -4  # CE_ERR_WORKSPACE, nothing launched

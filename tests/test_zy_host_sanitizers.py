@@ -60,6 +60,8 @@ int main(void) {
     for (int dt = 0; dt < 3; ++dt) {
       REFUSED(ce_fwd_grad(Z, T, Bs[i], 10, dt, G, L, 0));
       REFUSED(ce_fwd_grad(Z, T, 8, Cs[i], dt, G, L, 0));
+      REFUSED(ce_fwd_grad_loss(Z, T, Bs[i], 10, dt, G, L, L + 4096, 0, 0, 0));
+      REFUSED(ce_fwd_grad_loss(Z, T, 8, Cs[i], dt, G, L, L + 4096, 0, 0, 0));
       REFUSED(ce_fwd_loss(Z, T, Bs[i], 10, dt, L, 0));
       REFUSED(ce_fwd_loss(Z, T, 8, Cs[i], dt, L, 0));
       REFUSED(ce_fwd_grad_scaled(Z, T, 8, Cs[i], dt, G, L, L, 0));
@@ -104,6 +106,12 @@ int main(void) {
   REFUSED(ce_reduce_loss(L, 1 << 20, L + 4, 0, 0, 0));
   REFUSED(ce_reduce_loss(L, 1 << 20, L + 4, G, 3, 0));
   REFUSED(ce_reduce_loss(0, 8, L, 0, 0, 0));
+  /* the whole step: the reduction's arguments are refused before a launch */
+  REFUSED(ce_fwd_grad_loss(Z, T, 8, 10, 0, G, L, 0, 0, 0, 0));
+  REFUSED(ce_fwd_grad_loss(Z, T, 8, 10, 0, G, L, (float*)(Z + 2), 0, 0, 0));
+  REFUSED(ce_fwd_grad_loss(Z, T, 1 << 20, 10, 0, G, L, L + 4096, 0, 0, 0));
+  REFUSED(ce_fwd_grad_loss(Z, T, 1 << 20, 10, 0, G, L, L + 4096, G, 3, 0));
+  REFUSED(ce_fwd_grad_loss(Z, T, 1 << 20, 10, 0, G, L, L + 4096, Z + 2, 4096, 0));
   REFUSED(ce_reduce_loss_noalloc(L, MAXI, L + 4, 0));
   REFUSED(ce_reduce_loss_noalloc(L, 0, L + 4, 0));
   REFUSED(ce_reduce_loss_noalloc((float*)(Z + 2), 8, L, 0));
