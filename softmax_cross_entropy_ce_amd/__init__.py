@@ -512,11 +512,21 @@ def reduce_loss(loss_rows):
     return out
 
 
+def _fwd_grad_loss(logits, targets):
+    """``(loss, grad, loss_rows)`` in one library call (ce_fwd_grad_loss)."""
+    torch = _torch()
+    grad = _empty_congruent(logits)
+    loss_rows = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device)
+    loss = torch.empty((), dtype=torch.float32, device=logits.device)
+    fwd_grad_loss_into(logits, targets, grad, loss_rows, loss)
+    return loss, grad, loss_rows
+
+
 def cross_entropy(logits, targets):
     """Return ``(loss, grad)``: the batch-mean loss (0-d device tensor) and
     the gradient with respect to the logits."""
-    grad, loss_rows = fwd_grad(logits, targets)
-    return reduce_loss(loss_rows), grad
+    loss, grad, _ = _fwd_grad_loss(logits, targets)
+    return loss, grad
 
 
 _autograd_fn = None
@@ -530,16 +540,18 @@ def _function():
 
     class CrossEntropyFunction(torch.autograd.Function):
         """Forward: the batch-mean loss and, in the same pass, its gradient
-        (ce_fwd_grad + ce_reduce_loss).  Backward: that gradient scaled in
-        place by the upstream gradient (ce_scale_grad), a device scalar, so
-        there is no host synchronisation; one backward per forward."""
+        (ce_fwd_grad_loss; with ignore_index ce_fwd_grad_ex + ce_reduce_loss).
+        Backward: that gradient scaled in place by the upstream gradient
+        (ce_scale_grad), a device scalar, so there is no host
+        synchronisation; one backward per forward."""
 
         @staticmethod
         def forward(ctx, logits, targets, ignore_index=None):
             if ignore_index is None:
-                grad, loss_rows = fwd_grad(logits.detach(), targets)
-            else:
-                grad, loss_rows = fwd_grad_ex(logits.detach(), targets, ignore_index=ignore_index)
+                loss, grad, _ = _fwd_grad_loss(logits.detach(), targets)
+                ctx.grad = grad
+                return loss
+            grad, loss_rows = fwd_grad_ex(logits.detach(), targets, ignore_index=ignore_index)
             ctx.grad = grad
             return reduce_loss(loss_rows)
 
